@@ -1,0 +1,216 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) decode hot path for indexer-selected
+ * sparse attention over a block-scaled latent KV cache.
+ *
+ * One decode step of one layer is three calls:
+ *   mla_kv_append_quant   quantise the new entry (and indexer key) into the caches,
+ *                         write the window ring;
+ *   mla_indexer_topk      lightning-indexer scan over the indexer keys, causal mask,
+ *                         top-k -> int32 positions;
+ *   mla_sparse_decode     absorbed-MLA attention over the selected entries (plus the
+ *                         window), online softmax, logsumexp output.
+ * The cross-layer sharing modes of CSA2 are compositions of these calls over
+ * shared pointers (no mode enum): Full = append + topk + decode; Reindex = topk
+ * with its own indexer query over another layer's indexer cache + decode over
+ * the shared main cache; Reuse = decode with the shared indices.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [P1] "DeepSeek's Attention and KV Cache - From MLA to CSA2, From First Principles"
+ *  [P2] "From MLA to DSA to HCA/CSA: DeepSeek V3.2 and V4 Attention"
+ *  [P3] "DeepSeek-V4.1-Flash and the 890-byte KV cache"
+ *  [P4] "From First Principles: DeepSeek-V4.1-Flash Inference"
+ *
+ * Conventions common to every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state beyond a thread-local error string.
+ *  - `stream` is a hipStream_t passed as void*; calls only enqueue kernels on
+ *    it and never synchronise.  NULL means the default stream.
+ *  - Arguments are validated on the host before any launch; a call that
+ *    returns an error has enqueued nothing (except MLA_ERR_HIP, where a launch
+ *    itself failed).  mla_last_error() then holds a message.
+ *  - Byte strides are int64; rows are little-endian byte arrays.
+ *  - Non-finite inputs give unspecified (but memory-safe) results.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, bad stride, misalignment */
+    MLA_ERR_UNSUPPORTED = 2,   /* a format / shape combination with no kernel */
+    MLA_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+    MLA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} mla_status_t;
+
+/* Row formats of a cached entry.
+ *  MLA_FMT_F32       (dim+rope) fp32 values.
+ *  MLA_FMT_BF16      (dim+rope) bf16 values.
+ *  MLA_FMT_E4M3_S128 [dim E4M3 codes | dim/128 fp32 scales | rope bf16]; dim % 128 == 0.
+ *                    V3.2: 512 + 16 + 128 = 656 B main row, 128 + 4 = 132 B indexer
+ *                    key ([P1] "DeepSeek-V3.2", "What it costs and what it saves").
+ *                    Scale of a 128-channel block: amax/448 in fp32; code = E4M3
+ *                    round-to-nearest-even of x/scale (fp32 division), saturating.
+ *  MLA_FMT_E2M1_S16  [dim/2 bytes of E2M1 nibbles, channel 2i in the low nibble of
+ *                    byte i | dim/16 E4M3 scale bytes]; dim % 16 == 0, rope == 0.
+ *                    V4.1: 256 + 32 = 288 B main row ([P1] "DeepSeek-V4.1", "Four
+ *                    bits for the main KV"); 64 + 8 = 72 B indexer key ([P3] section 3).
+ *                    Scale of a 16-channel block: E4M3(amax / 6) (fp32 division,
+ *                    round-to-nearest-even, saturating); code = E2M1 nearest-even of
+ *                    x/scale; a zero scale gives zero codes.
+ * E4M3 is the OCP "fn" variant (max 448, no infinities); E2M1 magnitudes are
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 ([P1] "A Precision Primer"). */
+typedef enum {
+    MLA_FMT_F32 = 0,
+    MLA_FMT_BF16 = 1,
+    MLA_FMT_E4M3_S128 = 2,
+    MLA_FMT_E2M1_S16 = 3
+} mla_fmt_t;
+
+/* A row: `dim` quantised (or plain) channels followed by `rope_dim` RoPE channels.
+ * The attention key of a main row is all dim+rope channels ([c_KV ; k_R] of the
+ * absorbed form, [P1] "DeepSeek-V2", "Why RoPE breaks the trick"). */
+typedef struct {
+    int32_t dim;
+    int32_t rope_dim;
+    int32_t fmt;          /* an mla_fmt_t */
+} mla_row_t;
+
+/* Bytes of one row, or -1 if the format / shape is not supported. */
+int64_t mla_row_bytes(mla_row_t row);
+
+/* Static text of a status code. */
+const char* mla_status_str(int32_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int32_t mla_version(void);
+
+/*
+ * mla_kv_append_quant -- quantise-append of one decode step's entries.
+ *
+ * Writes, for each sequence b and each new entry i < n_new, the quantised main
+ * row of new_main[b, i, :] into main_cache at row slots[b, i], and the quantised
+ * indexer key of new_idx[b, i, :] into idx_cache at the same row.  The entry is
+ * quantised after RoPE, with no global scale ([P1] "DeepSeek-V4.1", "Four bits
+ * for the main KV"); the indexer key uses its own row format.  If new_win is
+ * given, the bf16 (round-to-nearest-even) window entry new_win[b, :] is written
+ * to ring slot win_pos[b] mod W ([P1] "Sliding Window Attention", "Definition and
+ * the bounded cache").
+ *
+ *  main_row, idx_row  row formats (idx_row.rope_dim must be 0)
+ *  new_main           fp32 [B, n_new, main.dim + main.rope_dim]; may be NULL iff main_cache is NULL
+ *  new_idx            fp32 [B, n_new, idx.dim]; may be NULL iff idx_cache is NULL
+ *  slots              int32 [B, n_new], each in [0, capacity); required if either cache is given
+ *  capacity           rows allocated per sequence (checked against slots on the device:
+ *                     out-of-range slots are skipped, not written)
+ *  main_cache         bytes, row r of sequence b at b*main_seq_stride + r*row_bytes; or NULL
+ *  idx_cache          likewise for indexer keys; or NULL
+ *  new_win            fp32 [B, Dw] or NULL (no window write)
+ *  win_pos            int32 [B] absolute positions (>= 0) of the window entries
+ *  win_ring           bf16 [B, W, Dw]
+ * Errors: MLA_ERR_INVALID_ARG for B < 0, n_new < 0, missing pointers, strides
+ * smaller than capacity * row_bytes, W <= 0 or Dw <= 0 with a window;
+ * MLA_ERR_UNSUPPORTED for an unsupported row format.
+ */
+mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
+                                 const float* new_main, const float* new_idx,
+                                 const int32_t* slots, int32_t B, int32_t n_new, int64_t capacity,
+                                 void* main_cache, int64_t main_seq_stride,
+                                 void* idx_cache, int64_t idx_seq_stride,
+                                 const float* new_win, const int32_t* win_pos,
+                                 void* win_ring, int32_t W, int32_t Dw,
+                                 void* stream);
+
+/*
+ * mla_indexer_topk -- lightning-indexer scan, causal mask and top-k.
+ *
+ * For every sequence b and cached row s < n_visible[b]:
+ *     I[b, s] = sum_j w[b, j] * ReLU(score_scale * q_idx[b, j, :] . k_idx[b, s, :])
+ * with one shared indexer key per row ([P1] "DeepSeek-V3.2", "The lightning
+ * indexer", eq. 1; [P2] Part 1, "The indexer"), accumulated in fp32.  Rows at or
+ * beyond n_visible[b] are masked ([P2] Part 2 "HCA": entry e is visible to query
+ * position p iff e < (p + 1) // m).  The k visible rows of largest score are
+ * returned as positions ([P1] eq. 2; ties at the k-th score go to the smaller
+ * position); slots past min(k, n_visible[b]) hold -1 ([P2] "CSA: two changes to
+ * HCA").  The returned positions are an unordered set.
+ *
+ *  idx_row      indexer-key row format (rope_dim 0)
+ *  q_idx        [B, H_I, idx_row.dim] bf16, or fp32 when idx_row.fmt == MLA_FMT_F32
+ *  w            fp32 [B, H_I], the per-head weights already scaled by the caller
+ *               (the V3.2 code multiplies them by H_I^-0.5)
+ *  score_scale  sigma > 0 applied inside the ReLU (d_I^-0.5 in the V3.2 code)
+ *  idx_cache    indexer rows, row s of sequence b at b*idx_seq_stride + s*row_bytes
+ *  capacity     rows allocated per sequence (the scan covers rows < n_visible[b] <= capacity)
+ *  n_visible    int32 [B] on the device, each in [0, capacity]
+ *  cand, n_cand must be NULL and 0 (candidate pools are not supported yet)
+ *  out_idx      int32 [B, k]
+ *  out_scores   optional fp32 [B, capacity]: the scores, -inf for masked rows
+ *  workspace    device scratch of at least mla_indexer_topk_workspace(B, capacity, k)
+ *               bytes, 256-byte aligned; its contents need no initialisation
+ * Errors: MLA_ERR_INVALID_ARG (pointers, B < 0, H_I < 1, k < 0, capacity < 0,
+ * score_scale <= 0, misalignment), MLA_ERR_UNSUPPORTED (format / H_I / dim with
+ * no kernel, or a candidate pool), MLA_ERR_WORKSPACE.
+ */
+size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k);
+
+mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w,
+                              float score_scale,
+                              const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                              const int32_t* n_visible,
+                              const int32_t* cand, int32_t n_cand,
+                              int32_t B, int32_t H_I, int32_t k,
+                              int32_t* out_idx, float* out_scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_sparse_decode -- absorbed MLA as shared-KV MQA over the selected entries.
+ *
+ * For each (b, h), over the multiset U = {rows idx[b, i] != -1} plus the window
+ * slots 0 .. win_len[b]-1 (concatenated, not de-duplicated: [P1] "DeepSeek-V4",
+ * "A window in every layer"):
+ *     z_u   = softmax_scale * q[b, h, :] . K_u          (K_u = all dim+rope channels)
+ *     lse   = logsumexp_u z_u                          (natural log)
+ *     out   = sum_u exp(z_u - lse) * K_u[0 : d_v]       (V = the leading d_v channels)
+ * This is the absorbed form ([P1] "DeepSeek-V2", "Check it in numpy"; [P2] Part 2,
+ * "What replaced MLA"): q is the query with W_UK already folded in, the output is
+ * the latent before W_UV.  Each selected row is read once for all heads ([P1]
+ * "DeepSeek-V3.2").  An empty U gives lse = -inf and out = 0.
+ *
+ *  main_row    main row format; d_v <= dim
+ *  q           [B, H, dim+rope] bf16 (fp32 when main_row.fmt == MLA_FMT_F32)
+ *  main_cache  rows as in mla_kv_append_quant; capacity rows per sequence
+ *  idx         int32 [B, k]: positions in [0, capacity) or -1 (skipped); duplicates
+ *              are attended twice
+ *  win_ring    optional bf16 [B, W, dim+rope] window entries (K = V), with
+ *  win_len     int32 [B] in [0, W], the number of valid ring slots (slots 0..len-1)
+ *  out         fp32 [B, H, d_v];  lse fp32 [B, H]
+ *  workspace   at least mla_sparse_decode_workspace(main_row, d_v, B, H, k, W) bytes,
+ *              256-byte aligned
+ * Positions outside [0, capacity) other than -1 are skipped.
+ * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE.
+ */
+size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H,
+                                   int32_t k, int32_t W);
+
+mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
+                               const void* main_cache, int64_t main_seq_stride, int64_t capacity,
+                               const int32_t* idx, int32_t k,
+                               const void* win_ring, const int32_t* win_len, int32_t W,
+                               float softmax_scale, int32_t B, int32_t H,
+                               float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

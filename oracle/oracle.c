@@ -294,12 +294,17 @@ int orc_append(int main_fmt, int main_dim, int main_rope, int idx_fmt, int idx_d
     int64_t mb = main_cache ? orc_row_bytes(main_fmt, main_dim, main_rope) : 0;
     int64_t ib = idx_cache ? orc_row_bytes(idx_fmt, idx_dim, 0) : 0;
     if (B < 0 || n_new < 0 || mb < 0 || ib < 0) return -1;
+    for (b = 0; b < B; b++)
+        for (i = 0; i < n_new; i++) {
+            int64_t slot = slots[(int64_t)b * n_new + i];
+            if ((main_cache || idx_cache) && (slot < 0 || slot >= capacity)) return -2;
+        }
     for (b = 0; b < B; b++) {
+#pragma omp parallel for schedule(static)
         for (i = 0; i < n_new; i++) {
             int64_t slot;
-            if (!main_cache && !idx_cache) break;
+            if (!main_cache && !idx_cache) continue;
             slot = slots[(int64_t)b * n_new + i];
-            if (slot < 0 || slot >= capacity) return -2;
             if (main_cache)
                 orc_quant_row(main_fmt, main_dim, main_rope,
                               new_main + ((int64_t)b * n_new + i) * (main_dim + main_rope),

@@ -1,0 +1,228 @@
+"""Python binding of the gfx950 decode hot path (libmla.so, C ABI in include/mla.h).
+
+Argument marshalling only: every function takes torch tensors on the GPU,
+checks their dtype / device / layout, and passes raw device pointers and the
+current HIP stream to the C entry point of the same name.  All arithmetic runs
+in the library's HIP kernels.  There is no fallback: if libmla.so is missing
+or fails to load, the functions raise.
+"""
+import ctypes as C
+import os
+from typing import NamedTuple, Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla.so")
+
+F32, BF16, E4M3_S128, E2M1_S16 = 0, 1, 2, 3
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
+
+
+class Row(NamedTuple):
+    """Row format of a cached entry: `dim` channels + `rope` RoPE channels."""
+    fmt: int
+    dim: int
+    rope: int = 0
+
+
+class _CRow(C.Structure):
+    _fields_ = [("dim", C.c_int32), ("rope_dim", C.c_int32), ("fmt", C.c_int32)]
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libmla.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python sparse_latent_attention_mla_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+        L.mla_row_bytes.argtypes, L.mla_row_bytes.restype = [_CRow], i64
+        L.mla_status_str.argtypes, L.mla_status_str.restype = [i32], C.c_char_p
+        L.mla_last_error.argtypes, L.mla_last_error.restype = [], C.c_char_p
+        L.mla_version.argtypes, L.mla_version.restype = [], i32
+        L.mla_kv_append_quant.argtypes = [_CRow, _CRow, P, P, P, i32, i32, i64, P, i64, P, i64,
+                                          P, P, P, i32, i32, P]
+        L.mla_kv_append_quant.restype = i32
+        L.mla_indexer_topk_workspace.argtypes, L.mla_indexer_topk_workspace.restype = [i32, i64, i32], sz
+        L.mla_indexer_topk.argtypes = [_CRow, P, P, f32, P, i64, i64, P, P, i32, i32, i32, i32,
+                                       P, P, P, sz, P]
+        L.mla_indexer_topk.restype = i32
+        L.mla_sparse_decode_workspace.argtypes = [_CRow, i32, i32, i32, i32, i32]
+        L.mla_sparse_decode_workspace.restype = sz
+        L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, f32, i32, i32,
+                                        P, P, P, sz, P]
+        L.mla_sparse_decode.restype = i32
+        _lib = L
+    return _lib
+
+
+def _crow(r: Row) -> _CRow:
+    return _CRow(r.dim, r.rope, r.fmt)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(status):
+    if status != 0:
+        raise MLAError(status, lib().mla_last_error().decode())
+
+
+def _need(t, name, dtype=None, ndim=None, contiguous=True):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def row_bytes(row: Row) -> int:
+    return int(lib().mla_row_bytes(_crow(row)))
+
+
+def version() -> int:
+    return int(lib().mla_version())
+
+
+def query_dtype(row: Row):
+    return torch.float32 if row.fmt == F32 else torch.bfloat16
+
+
+def _cache_stride(cache: Optional[torch.Tensor], name: str) -> int:
+    if cache is None:
+        return 0
+    _need(cache, name, torch.uint8, 3, contiguous=False)
+    if cache.stride(2) != 1 or cache.stride(1) != cache.shape[2]:
+        raise ValueError(f"{name}: rows must be contiguous [B, capacity, row_bytes]")
+    return cache.stride(0)
+
+
+def mla_kv_append_quant(main_row: Row, idx_row: Row, new_main, new_idx, slots,
+                        main_cache, idx_cache, new_win=None, win_pos=None, win_ring=None, stream=None):
+    """Quantise-append.  new_main fp32 [B, n, D], new_idx fp32 [B, n, d_I], slots int32 [B, n];
+    main_cache / idx_cache uint8 [B, capacity, row_bytes] (either may be None);
+    new_win fp32 [B, Dw], win_pos int32 [B], win_ring bf16 [B, W, Dw] (optional)."""
+    caches = [c for c in (main_cache, idx_cache) if c is not None]
+    capacity = caches[0].shape[1] if caches else 0
+    if len(caches) == 2 and main_cache.shape[1] != idx_cache.shape[1]:
+        raise ValueError("main and indexer caches must have the same capacity")
+    B = n_new = 0
+    if caches:
+        _need(slots, "slots", torch.int32, 2)
+        B, n_new = slots.shape
+    if main_cache is not None:
+        _need(new_main, "new_main", torch.float32, 3)
+        if tuple(new_main.shape) != (B, n_new, main_row.dim + main_row.rope) or main_cache.shape[0] != B:
+            raise ValueError("new_main must be [B, n_new, dim + rope] and main_cache [B, capacity, row_bytes]")
+        if main_cache.shape[2] != row_bytes(main_row):
+            raise ValueError("main_cache rows do not match the row format")
+    if idx_cache is not None:
+        _need(new_idx, "new_idx", torch.float32, 3)
+        if tuple(new_idx.shape) != (B, n_new, idx_row.dim) or idx_cache.shape[0] != B:
+            raise ValueError("new_idx must be [B, n_new, idx dim] and idx_cache [B, capacity, row_bytes]")
+        if idx_cache.shape[2] != row_bytes(idx_row):
+            raise ValueError("idx_cache rows do not match the row format")
+    W = Dw = 0
+    if new_win is not None:
+        _need(new_win, "new_win", torch.float32, 2)
+        _need(win_pos, "win_pos", torch.int32, 1)
+        _need(win_ring, "win_ring", torch.bfloat16, 3)
+        if caches and new_win.shape[0] != B:
+            raise ValueError("new_win batch differs from the caches'")
+        B = new_win.shape[0]
+        _, W, Dw = win_ring.shape
+        if win_ring.shape[0] != B or new_win.shape[1] != Dw or win_pos.shape[0] != B:
+            raise ValueError("window shapes: new_win [B, Dw], win_pos [B], win_ring [B, W, Dw]")
+    _check(lib().mla_kv_append_quant(
+        _crow(main_row), _crow(idx_row), _ptr(new_main), _ptr(new_idx), _ptr(slots), B, n_new, capacity,
+        _ptr(main_cache), _cache_stride(main_cache, "main_cache"),
+        _ptr(idx_cache), _cache_stride(idx_cache, "idx_cache"),
+        _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw, _stream(stream)))
+
+
+def mla_indexer_topk_workspace(B: int, capacity: int, k: int) -> int:
+    return int(lib().mla_indexer_topk_workspace(B, capacity, k))
+
+
+def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_visible, k: int,
+                     out_idx, workspace, out_scores=None, stream=None):
+    """Indexer scan + mask + top-k.  q_idx [B, H_I, d_I] (bf16; fp32 for F32 rows), w fp32 [B, H_I],
+    idx_cache uint8 [B, capacity, row_bytes], n_visible int32 [B], out_idx int32 [B, k],
+    workspace uint8 of mla_indexer_topk_workspace bytes, out_scores fp32 [B, capacity] (optional)."""
+    _need(q_idx, "q_idx", query_dtype(idx_row), 3)
+    _need(w, "w", torch.float32, 2)
+    _need(n_visible, "n_visible", torch.int32, 1)
+    _need(out_idx, "out_idx", torch.int32, 2)
+    _need(workspace, "workspace", torch.uint8)
+    stride = _cache_stride(idx_cache, "idx_cache")
+    B, H_I, dq = q_idx.shape
+    cap = idx_cache.shape[1]
+    if dq != idx_row.dim or idx_cache.shape[0] != B or idx_cache.shape[2] != row_bytes(idx_row):
+        raise ValueError("q_idx [B, H_I, dim] and idx_cache [B, capacity, row_bytes] must match the row format")
+    if tuple(w.shape) != (B, H_I) or tuple(n_visible.shape) != (B,) or tuple(out_idx.shape) != (B, k):
+        raise ValueError("w [B, H_I], n_visible [B], out_idx [B, k] expected")
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, 2)
+        if tuple(out_scores.shape) != (B, cap):
+            raise ValueError("out_scores must be [B, capacity]")
+    _check(lib().mla_indexer_topk(
+        _crow(idx_row), _ptr(q_idx), _ptr(w), float(score_scale), _ptr(idx_cache), stride,
+        idx_cache.shape[1], _ptr(n_visible), None, 0, B, H_I, k, _ptr(out_idx), _ptr(out_scores),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def mla_sparse_decode_workspace(main_row: Row, d_v: int, B: int, H: int, k: int, W: int = 0) -> int:
+    return int(lib().mla_sparse_decode_workspace(_crow(main_row), d_v, B, H, k, W))
+
+
+def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
+                      workspace=None, win_ring=None, win_len=None, stream=None):
+    """Sparse absorbed-MLA decode.  q [B, H, D] (bf16; fp32 for F32 rows), main_cache uint8
+    [B, capacity, row_bytes], idx int32 [B, k], out fp32 [B, H, d_v], lse fp32 [B, H];
+    win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch."""
+    _need(q, "q", query_dtype(main_row), 3)
+    _need(idx, "idx", torch.int32, 2)
+    _need(out, "out", torch.float32, 3)
+    _need(lse, "lse", torch.float32, 2)
+    stride = _cache_stride(main_cache, "main_cache")
+    B, H, D = q.shape
+    if D != main_row.dim + main_row.rope or main_cache.shape[0] != B or main_cache.shape[2] != row_bytes(main_row):
+        raise ValueError("q [B, H, dim + rope] and main_cache [B, capacity, row_bytes] must match the row format")
+    if idx.shape[0] != B or tuple(out.shape) != (B, H, d_v) or tuple(lse.shape) != (B, H):
+        raise ValueError("idx [B, k], out [B, H, d_v], lse [B, H] expected")
+    W = 0
+    if win_ring is not None:
+        _need(win_ring, "win_ring", torch.bfloat16, 3)
+        _need(win_len, "win_len", torch.int32, 1)
+        if win_ring.shape[0] != B or win_ring.shape[2] != D or tuple(win_len.shape) != (B,):
+            raise ValueError("win_ring [B, W, dim + rope] and win_len [B] expected")
+        W = win_ring.shape[1]
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    _check(lib().mla_sparse_decode(
+        _crow(main_row), d_v, _ptr(q), _ptr(main_cache), stride, main_cache.shape[1], _ptr(idx), idx.shape[1],
+        _ptr(win_ring), _ptr(win_len), W, float(softmax_scale), B, H, _ptr(out), _ptr(lse),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))

@@ -1,0 +1,280 @@
+// api.cpp -- the C ABI of include/mla.h: argument validation on the host,
+// workspace carving, dispatch to the gfx950 launchers, error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+#include "mla.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status_t fail(mla_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+mla_status_t ok() {
+    g_err[0] = '\0';
+    return MLA_OK;
+}
+
+mla_status_t hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return ok();
+    return fail(MLA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Minimum alignment of row starts for a format (the kernels use wide loads).
+size_t row_alignment(int fmt) { return fmt == MLA_FMT_F32 ? 4 : (fmt == MLA_FMT_BF16 ? 2 : 4); }
+
+mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int64_t stride, int64_t capacity,
+                        int B, int64_t* row_bytes) {
+    const int64_t rb = mla_row_bytes(row);
+    if (rb < 0)
+        return fail(MLA_ERR_UNSUPPORTED, "%s: unsupported row format (fmt %d, dim %d, rope %d)", what, row.fmt,
+                    row.dim, row.rope_dim);
+    *row_bytes = rb;
+    if (!cache) return ok();
+    if (capacity < 0) return fail(MLA_ERR_INVALID_ARG, "%s: capacity < 0", what);
+    if (B > 1 && stride < capacity * rb)
+        return fail(MLA_ERR_INVALID_ARG, "%s: sequence stride %lld < capacity * row bytes %lld", what,
+                    (long long)stride, (long long)(capacity * rb));
+    if (!aligned(cache, 16) || stride % 16 != 0)
+        return fail(MLA_ERR_INVALID_ARG, "%s: cache and sequence stride must be 16-byte aligned", what);
+    if (rb % (int64_t)row_alignment(row.fmt) != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "%s: row bytes %lld not a multiple of %zu", what, (long long)rb,
+                    row_alignment(row.fmt));
+    return ok();
+}
+
+struct TopkLayout {
+    size_t scores, hist, counters, cand, total;
+};
+
+TopkLayout topk_layout(int32_t B, int64_t capacity) {
+    TopkLayout L;
+    const size_t b = B > 0 ? (size_t)B : 0, cap = capacity > 0 ? (size_t)capacity : 0;
+    L.scores = 0;
+    L.hist = L.scores + round256(b * cap * sizeof(float));
+    L.counters = L.hist + round256(b * mla::kHistBinsHost * sizeof(uint32_t));
+    L.cand = L.counters + round256(b * 4 * sizeof(uint32_t));
+    L.total = L.cand + round256(b * cap * sizeof(uint64_t));
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mla_row_bytes(mla_row_t row) {
+    if (row.dim <= 0 || row.rope_dim < 0 || row.dim > 8192 || row.rope_dim > 8192) return -1;
+    switch (row.fmt) {
+    case MLA_FMT_F32: return 4LL * (row.dim + row.rope_dim);
+    case MLA_FMT_BF16: return 2LL * (row.dim + row.rope_dim);
+    case MLA_FMT_E4M3_S128:
+        if (row.dim % 128 != 0 || row.rope_dim % 2 != 0) return -1;
+        return (int64_t)row.dim + 4LL * (row.dim / 128) + 2LL * row.rope_dim;
+    case MLA_FMT_E2M1_S16:
+        if (row.dim % 16 != 0 || row.rope_dim != 0 || row.dim > 1024) return -1;
+        return (int64_t)row.dim / 2 + row.dim / 16;
+    default: return -1;
+    }
+}
+
+const char* mla_status_str(int32_t status) {
+    switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+int32_t mla_version(void) { return 100; }
+
+mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
+                                 const float* new_idx, const int32_t* slots, int32_t B, int32_t n_new,
+                                 int64_t capacity, void* main_cache, int64_t main_seq_stride, void* idx_cache,
+                                 int64_t idx_seq_stride, const float* new_win, const int32_t* win_pos,
+                                 void* win_ring, int32_t W, int32_t Dw, void* stream) {
+    if (B < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "append: B and n_new must be >= 0");
+    mla::AppendArgs a{};
+    if (main_cache) {
+        mla_status_t s = check_rows("append main", main_row, main_cache, main_seq_stride, capacity, B,
+                                    &a.main_row_bytes);
+        if (s != MLA_OK) return s;
+        if (main_row.dim + main_row.rope_dim > 4096)
+            return fail(MLA_ERR_UNSUPPORTED, "append: main row wider than 4096 channels");
+        if (!new_main) return fail(MLA_ERR_INVALID_ARG, "append: new_main is NULL");
+    }
+    if (idx_cache) {
+        if (idx_row.rope_dim != 0) return fail(MLA_ERR_INVALID_ARG, "append: indexer rows have no RoPE part");
+        mla_status_t s = check_rows("append indexer", idx_row, idx_cache, idx_seq_stride, capacity, B,
+                                    &a.idx_row_bytes);
+        if (s != MLA_OK) return s;
+        if (!new_idx) return fail(MLA_ERR_INVALID_ARG, "append: new_idx is NULL");
+    }
+    if ((main_cache || idx_cache) && n_new > 0 && B > 0 && !slots)
+        return fail(MLA_ERR_INVALID_ARG, "append: slots is NULL");
+    if (new_win) {
+        if (!win_pos || !win_ring) return fail(MLA_ERR_INVALID_ARG, "append: window needs win_pos and win_ring");
+        if (W <= 0 || Dw <= 0) return fail(MLA_ERR_INVALID_ARG, "append: window needs W > 0 and Dw > 0");
+        if (!aligned(win_ring, 2)) return fail(MLA_ERR_INVALID_ARG, "append: misaligned window ring");
+    }
+    a.main_fmt = main_row.fmt;
+    a.main_dim = main_row.dim;
+    a.main_rope = main_row.rope_dim;
+    a.idx_fmt = idx_row.fmt;
+    a.idx_dim = idx_row.dim;
+    a.new_main = new_main;
+    a.new_idx = new_idx;
+    a.slots = slots;
+    a.B = B;
+    a.n_new = n_new;
+    a.capacity = capacity;
+    a.main_cache = static_cast<uint8_t*>(main_cache);
+    a.main_stride = main_seq_stride;
+    a.idx_cache = static_cast<uint8_t*>(idx_cache);
+    a.idx_stride = idx_seq_stride;
+    a.new_win = new_win;
+    a.win_pos = win_pos;
+    a.win_ring = new_win ? static_cast<uint16_t*>(win_ring) : nullptr;
+    a.W = W;
+    a.Dw = Dw;
+    return hip_status(mla::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
+}
+
+size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
+    (void)k;
+    return topk_layout(B, capacity).total;
+}
+
+mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
+                              const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                              const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
+                              int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (B < 0 || k < 0 || H_I < 1 || capacity < 0)
+        return fail(MLA_ERR_INVALID_ARG, "indexer_topk: need B >= 0, k >= 0, H_I >= 1, capacity >= 0");
+    if (!(score_scale > 0.0f)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: score_scale must be > 0");
+    if (cand || n_cand) return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: candidate pools are not supported");
+    if (idx_row.rope_dim != 0) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: indexer rows have no RoPE part");
+    if (B == 0 || k == 0) return ok();
+    int64_t rb = 0;
+    mla_status_t s = check_rows("indexer_topk", idx_row, idx_cache, idx_seq_stride, capacity, B, &rb);
+    if (s != MLA_OK) return s;
+    if (!q_idx || !w || !idx_cache || !n_visible || !out_idx)
+        return fail(MLA_ERR_INVALID_ARG, "indexer_topk: a required pointer is NULL");
+    if (!aligned(q_idx, 16)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: q_idx must be 16-byte aligned");
+    if (!mla::scan_supported(idx_row.fmt, idx_row.dim, H_I))
+        return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: no kernel for fmt %d, dim %d, H_I %d", idx_row.fmt,
+                    idx_row.dim, H_I);
+    if (capacity > (int64_t)0x7FFFFFFF) return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: capacity over 2^31-1");
+    const TopkLayout L = topk_layout(B, capacity);
+    if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
+        return fail(MLA_ERR_WORKSPACE, "indexer_topk: workspace needs %zu bytes, 256-byte aligned", L.total);
+    if (out_scores && !aligned(out_scores, 4)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: misaligned out_scores");
+    char* ws = static_cast<char*>(workspace);
+    mla::TopkWorkspace T;
+    T.scores = out_scores ? out_scores : reinterpret_cast<float*>(ws + L.scores);
+    T.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    T.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
+    T.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_topk_clear(T, B, st);
+    if (e != hipSuccess) return hip_status(e, "indexer_topk clear");
+    mla::ScanArgs a{};
+    a.fmt = idx_row.fmt;
+    a.dim = idx_row.dim;
+    a.row_bytes = rb;
+    a.q_idx = q_idx;
+    a.w = w;
+    a.sigma = score_scale;
+    a.cache = static_cast<const uint8_t*>(idx_cache);
+    a.stride = idx_seq_stride;
+    a.capacity = capacity;
+    a.n_visible = n_visible;
+    a.B = B;
+    a.H_I = H_I;
+    a.k = k;
+    a.scores = T.scores;
+    a.hist = T.hist;
+    e = mla::launch_scan(a, st);
+    if (e != hipSuccess) return hip_status(e, "indexer scan");
+    e = mla::launch_select(T.scores, capacity, n_visible, B, k, T, out_idx, st);
+    return hip_status(e, "top-k select");
+}
+
+size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H, int32_t k, int32_t W) {
+    if (B <= 0 || H <= 0 || k < 0 || W < 0 || mla_row_bytes(main_row) < 0) return 0;
+    return mla::decode_workspace_bytes(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W);
+}
+
+mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
+                               int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
+                               const void* win_ring, const int32_t* win_len, int32_t W, float softmax_scale,
+                               int32_t B, int32_t H, float* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 1 || k < 0 || capacity < 0)
+        return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need B >= 0, H >= 1, k >= 0, capacity >= 0");
+    const int D = main_row.dim + main_row.rope_dim;
+    if (d_v <= 0 || d_v > main_row.dim) return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need 0 < d_v <= dim");
+    int64_t rb = 0;
+    mla_status_t s = check_rows("sparse_decode", main_row, main_cache, main_seq_stride, capacity, B, &rb);
+    if (s != MLA_OK) return s;
+    if (B == 0) return ok();
+    if (!q || !out || !lse || (k > 0 && (!idx || !main_cache)))
+        return fail(MLA_ERR_INVALID_ARG, "sparse_decode: a required pointer is NULL");
+    if (win_ring && (!win_len || W <= 0))
+        return fail(MLA_ERR_INVALID_ARG, "sparse_decode: window needs win_len and W > 0");
+    if (!aligned(q, 16) || !aligned(out, 16) || (win_ring && !aligned(win_ring, 16)))
+        return fail(MLA_ERR_INVALID_ARG, "sparse_decode: q, out and win_ring must be 16-byte aligned");
+    if (!mla::decode_supported(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, H))
+        return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: no kernel for this shape");
+    const size_t need = mla::decode_workspace_bytes(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k,
+                                                    win_ring ? W : 0);
+    if (need == 0 && (k + (win_ring ? W : 0) > 8192 || D > 1024))
+        return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: generic path limited to k + W <= 8192, width <= 1024");
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(MLA_ERR_WORKSPACE, "sparse_decode: workspace needs %zu bytes, 256-byte aligned", need);
+    mla::DecodeArgs a{};
+    a.fmt = main_row.fmt;
+    a.dim = main_row.dim;
+    a.rope = main_row.rope_dim;
+    a.d_v = d_v;
+    a.row_bytes = rb;
+    a.q = q;
+    a.cache = static_cast<const uint8_t*>(main_cache);
+    a.stride = main_seq_stride;
+    a.capacity = capacity;
+    a.idx = idx;
+    a.k = k;
+    a.win = win_ring ? static_cast<const uint16_t*>(win_ring) : nullptr;
+    a.win_len = win_len;
+    a.W = win_ring ? W : 0;
+    a.scale = softmax_scale;
+    a.B = B;
+    a.H = H;
+    a.out = out;
+    a.lse = lse;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    return hip_status(mla::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// common.hpp -- device helpers shared by the gfx950 kernels: vector types,
+// E4M3 / E2M1 / bf16 codecs, MFMA operand packing, wave reductions.
+//
+// Format definitions ([P1] "DeepSeek's Attention and KV Cache - From MLA to
+// CSA2", "A Precision Primer"): E4M3 "fn" (bias 7, no infinities, one NaN
+// pattern, max 448) and E2M1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "mla.h"
+
+namespace mla {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bit casts
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// ---------------------------------------------------------------- encoders
+// bf16 by round-to-nearest-even of the fp32 bit pattern (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    uint32_t u = f2u(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E4M3 code of x: round-to-nearest-even on the E4M3 grid, saturating to +-448.
+// Sign kept (so -0 -> 0x80).  Works on the fp32 bit pattern.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+    const uint32_t u = f2u(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a > 0x7F800000u) return 0x7Fu;                      // NaN
+    if (a >= 0x43E00000u) {                                 // >= 448
+        mag = 0x7Eu;
+    } else if (a < 0x3C800000u) {                           // < 2^-6: subnormal step 2^-9
+        mag = (uint32_t)__builtin_rintf(u2f(a) * 512.0f);    // exact scaling, RNE to 0..8
+    } else {
+        int e = (int)(a >> 23) - 127;                       // -6 .. 8
+        uint32_t m = a & 0x7FFFFFu;
+        uint32_t q = m >> 20;                               // top 3 mantissa bits
+        uint32_t rem = m & 0xFFFFFu;
+        if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+        if (q == 8u) { q = 0u; ++e; }
+        mag = ((uint32_t)(e + 7) << 3) | q;                 // a < 448 keeps mag <= 0x7E
+    }
+    return sign | mag;
+}
+
+// E2M1 nibble of y: nearest rung, ties to the even mantissa, saturating to +-6.
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+    const uint32_t u = f2u(y);
+    const uint32_t sign = (u >> 28) & 0x8u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a > 0x7F800000u) return 0x7u;
+    if (a >= 0x40C00000u) {                                 // >= 6
+        mag = 7u;
+    } else if (a < 0x3F800000u) {                           // < 1: step 0.5
+        mag = (uint32_t)__builtin_rintf(u2f(a) * 2.0f);      // 0, 1, 2 (2 == 1.0)
+    } else {
+        int e = (int)(a >> 23) - 127;                       // 0, 1, 2
+        uint32_t m = a & 0x7FFFFFu;
+        uint32_t q = m >> 22;                               // 1 mantissa bit
+        uint32_t rem = m & 0x3FFFFFu;
+        if (rem > 0x200000u || (rem == 0x200000u && (q & 1u))) ++q;
+        if (q == 2u) { q = 0u; ++e; }
+        mag = ((uint32_t)(e + 1) << 1) | q;
+        if (mag > 7u) mag = 7u;
+    }
+    return sign | mag;
+}
+
+// Exact value of an E4M3 scale byte as fp32 (scales are never NaN here).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+    f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false);
+    return v.x;
+}
+
+// ---------------------------------------------------------------- decoders
+// Four E4M3 codes (one dword) -> four exact fp32 values.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* o) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    o[0] = lo.x; o[1] = lo.y; o[2] = hi.x; o[3] = hi.y;
+}
+
+// Pack the bf16 of two fp32 values whose low 16 bits are zero (exact).
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
+    return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+}
+
+// Four E4M3 codes -> two dwords of bf16 (exact).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    u32x2 r;
+    r.x = pack_bf16_trunc(lo.x, lo.y);
+    r.y = pack_bf16_trunc(hi.x, hi.y);
+    return r;
+}
+
+// Byte `sel` (0..3) of w holds two E2M1 nibbles (low nibble = even channel):
+// return their values (exact fp32).
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// A caller-supplied count clamped to [0, limit] (keeps every access in bounds).
+__device__ __forceinline__ int64_t clamp_visible(int64_t v, int64_t limit) {
+    return v < 0 ? 0 : (v > limit ? limit : v);
+}
+
+// Order-preserving map of an fp32 score to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = f2u(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+    return u2f((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// MFMA wrappers (gfx950, 64-lane wave).  Operand layout, verified on the
+// device: A lane l holds row (l % 16), k-slots 8*(l/16) .. +7; B lane l holds
+// column (l % 16), the same k-slots; D lane l, element r holds row
+// 4*(l/16) + r, column l % 16.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Top-k histogram over the high bits of the score key.
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+static_assert(kHistBins == kHistBinsHost, "histogram size");
+
+}  // namespace mla

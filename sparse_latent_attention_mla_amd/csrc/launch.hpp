@@ -1,0 +1,83 @@
+// launch.hpp -- internal argument blocks and launchers of the gfx950 kernels.
+// Host-side validation lives in api.cpp; launchers assume valid arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Bins of the top-k score histogram (top 12 bits of the order-preserving key).
+constexpr int kHistBinsHost = 4096;
+
+struct AppendArgs {
+    int main_fmt, main_dim, main_rope;
+    int idx_fmt, idx_dim;
+    int64_t main_row_bytes, idx_row_bytes;
+    const float* new_main;
+    const float* new_idx;
+    const int32_t* slots;
+    int B, n_new;
+    int64_t capacity;
+    uint8_t* main_cache;
+    int64_t main_stride;
+    uint8_t* idx_cache;
+    int64_t idx_stride;
+    const float* new_win;
+    const int32_t* win_pos;
+    uint16_t* win_ring;
+    int W, Dw;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+// Workspace of the indexer + top-k, carved by the host (all 256-byte aligned).
+struct TopkWorkspace {
+    float* scores;          // [B, capacity] (used when the caller gives no score buffer)
+    uint32_t* hist;         // [B, kHistBins]
+    uint32_t* counters;     // [B, 4]: selected, candidates, -, -
+    uint64_t* cand;         // [B, capacity] (key << 32 | ~position)
+};
+
+struct ScanArgs {
+    int fmt, dim;           // indexer row format
+    int64_t row_bytes;
+    const void* q_idx;      // [B, H_I, dim] bf16 (fp32 for F32 rows)
+    const float* w;         // [B, H_I]
+    float sigma;
+    const uint8_t* cache;
+    int64_t stride;
+    int64_t capacity;
+    const int32_t* n_visible;
+    int B, H_I, k;
+    float* scores;          // [B, capacity]
+    uint32_t* hist;         // [B, bins]
+};
+hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+bool scan_supported(int fmt, int dim, int H_I);
+hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
+                         const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream);
+
+struct DecodeArgs {
+    int fmt, dim, rope, d_v;
+    int64_t row_bytes;
+    const void* q;          // [B, H, dim+rope] bf16 (fp32 for F32 rows)
+    const uint8_t* cache;
+    int64_t stride, capacity;
+    const int32_t* idx;
+    int k;
+    const uint16_t* win;    // [B, W, dim+rope] bf16 or null
+    const int32_t* win_len;
+    int W;
+    float scale;
+    int B, H;
+    float* out;             // [B, H, d_v]
+    float* lse;             // [B, H]
+    void* workspace;
+    size_t workspace_bytes;
+};
+bool decode_supported(int fmt, int dim, int rope, int d_v, int H);
+size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace mla

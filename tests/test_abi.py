@@ -1,0 +1,103 @@
+"""The C ABI library loads and exports every entry point include/mla.h declares,
+and host-side validation rejects bad arguments before any launch.  CPU only:
+no call here reaches the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def M():
+    import sparse_latent_attention_mla_amd as M
+    if not os.path.exists(M.LIB_PATH):
+        pytest.fail("libmla.so is not built (run __graft_entry__.build())")
+    return M
+
+
+def test_header_declares_the_three_path_calls():
+    names = declared_functions()
+    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(M):
+    lib = C.CDLL(M.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_row_bytes_and_status_strings(M):
+    R = M.Row
+    assert M.row_bytes(R(M.E4M3_S128, 512, 64)) == 656
+    assert M.row_bytes(R(M.E4M3_S128, 128)) == 132
+    assert M.row_bytes(R(M.E2M1_S16, 512)) == 288
+    assert M.row_bytes(R(M.E2M1_S16, 128)) == 72
+    assert M.row_bytes(R(M.BF16, 512, 64)) == 1152
+    assert M.row_bytes(R(M.F32, 64, 16)) == 320
+    assert M.row_bytes(R(M.E2M1_S16, 512, 64)) == -1          # no separate RoPE part in FP4 rows
+    assert M.row_bytes(R(M.E4M3_S128, 100)) == -1
+    assert M.row_bytes(R(7, 128)) == -1
+    assert M.lib().mla_status_str(3) == b"workspace missing or too small"
+    assert M.version() >= 100
+
+
+def _row(M, fmt, dim, rope=0):
+    return M._CRow(dim, rope, fmt)
+
+
+def test_host_validation_rejects_before_launch(M):
+    L = M.lib()
+    fake = C.c_void_p(0x1000)                  # never dereferenced: validation fails first
+    r_main, r_idx = _row(M, M.E4M3_S128, 512, 64), _row(M, M.E4M3_S128, 128)
+    # append: negative batch
+    assert L.mla_kv_append_quant(r_main, r_idx, fake, fake, fake, -1, 1, 10, fake, 6560, fake, 1320,
+                                 None, None, None, 0, 0, None) == 1
+    # append: unsupported row format
+    assert L.mla_kv_append_quant(_row(M, 9, 512), r_idx, fake, fake, fake, 1, 1, 10, fake, 6560, None, 0,
+                                 None, None, None, 0, 0, None) == 2
+    # append: window without a ring
+    assert L.mla_kv_append_quant(r_main, r_idx, None, None, None, 1, 0, 0, None, 0, None, 0,
+                                 fake, fake, None, 128, 512, None) == 1
+    # topk: score scale must be positive
+    assert L.mla_indexer_topk(r_idx, fake, fake, 0.0, fake, 1408, 10, fake, None, 0, 1, 64, 8,
+                              fake, None, fake, 1 << 20, None) == 1
+    # topk: candidate pools are not supported yet
+    assert L.mla_indexer_topk(r_idx, fake, fake, 0.1, fake, 1408, 10, fake, fake, 5, 1, 64, 8,
+                              fake, None, fake, 1 << 20, None) == 2
+    # topk: workspace too small
+    assert L.mla_indexer_topk(r_idx, fake, fake, 0.1, C.c_void_p(0x10000), 1408, 10, fake, None, 0, 1, 64, 8,
+                              fake, None, C.c_void_p(0x100000), 16, None) == 3
+    assert b"workspace" in L.mla_last_error()
+    # topk: no kernel for this shape (H_I * dim too large for the generic scan)
+    assert L.mla_indexer_topk(_row(M, M.F32, 512), C.c_void_p(0x10000), fake, 0.1, C.c_void_p(0x10000),
+                              20480, 10, fake, None, 0, 1, 64, 8, fake, None, C.c_void_p(0x100000),
+                              1 << 24, None) == 2
+    # decode: d_v larger than the latent
+    assert L.mla_sparse_decode(r_main, 600, fake, fake, 6560, 10, fake, 4, None, None, 0, 0.1, 1, 128,
+                               fake, fake, fake, 1 << 30, None) == 1
+    # decode: workspace too small for the MFMA path
+    assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
+                               None, None, 0, 0.1, 1, 128, C.c_void_p(0x10000), fake,
+                               C.c_void_p(0x100000), 64, None) == 3
+    # decode: misaligned query
+    assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10002), C.c_void_p(0x10000), 6560, 10, fake, 4,
+                               None, None, 0, 0.1, 1, 128, C.c_void_p(0x10000), fake,
+                               C.c_void_p(0x100000), 1 << 30, None) == 1
+
+
+def test_workspace_queries(M):
+    assert M.mla_indexer_topk_workspace(4, 131072, 2048) >= 4 * 131072 * (4 + 8)
+    r = M.Row(M.E4M3_S128, 512, 64)
+    assert M.mla_sparse_decode_workspace(r, 512, 4, 128, 2048, 0) >= 4 * 128 * 512 * 4
+    assert M.mla_sparse_decode_workspace(M.Row(M.F32, 64, 16), 64, 1, 16, 32, 0) == 0   # generic path

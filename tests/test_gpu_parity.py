@@ -1,0 +1,224 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars (written here, from the benchmark spec of the path):
+  * quantise-append and causal masking: bit-exact;
+  * indexer scores: |I_gpu - I_ref| <= 1e-4 * max(|I_ref|, rms of the row);
+  * top-k sets: exact, except positions whose oracle score lies within
+    1e-4 * max(|theta|, rms) of the oracle's k-th score theta;
+  * attention given identical dequantised rows and index sets: per (b, h),
+    max |o - o_ref| <= 2e-3 * max |o_ref| and |lse - lse_ref| <= 2e-3 * max(1, |lse_ref|).
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from tests import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+C = WL.CONFIGS
+SMALL = {
+    "c1": C["c1"],
+    "c2s": C["c2"].with_(name="c2s", cid=102, B=2, N=5003),
+    "c3s": C["c3"].with_(name="c3s", cid=103, B=2, N=6001),
+    "c4s": C["c4"].with_(name="c4s", cid=104, B=2, N=4099),
+    "c5s": C["c5"].with_(name="c5s", cid=105, B=1, N=3001),
+}
+FULL = {n: C[n] for n in ("c2", "c3", "c4", "c5")}
+
+
+def say(*a):
+    print("[gpu-parity]", *a, file=sys.stderr, flush=True)
+
+
+@functools.lru_cache(maxsize=2)
+def case_of(name):
+    cfg = SMALL.get(name) or FULL[name]
+    say("building", name, f"B={cfg.B} N={cfg.N} H={cfg.H} fmt={cfg.main_fmt}/{cfg.idx_fmt} W={cfg.W}")
+    return G.build_case(cfg)
+
+
+def indexer_layers(cfg):
+    """(layer, indexer query slot) of the layers that run the indexer."""
+    out, j = [], 0
+    for l, mode in enumerate(cfg.layers):
+        if mode in ("full", "reindex"):
+            out.append((l, j))
+            j += 1
+    return out
+
+
+def oracle_indices_per_layer(case):
+    """CSA2 composition on the oracle side: Full / Reindex layers select with
+    their own indexer query over the shared keys; Reuse layers take the latest."""
+    cfg = case.cfg
+    idx_of, latest, j = [], None, 0
+    for mode in cfg.layers:
+        if mode in ("full", "reindex"):
+            s = G.oracle_scores(case, j)
+            latest = G.O.topk(s, case.n_visible, cfg.k)
+            j += 1
+        idx_of.append(latest)
+    return idx_of
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_append_bitexact(name):
+    case = case_of(name)
+    say("append parity", name)
+    assert np.array_equal(case.g_main.cpu().numpy(), case.o_main), "main rows differ"
+    assert np.array_equal(case.g_idx.cpu().numpy(), case.o_idx), "indexer rows differ"
+    if case.cfg.W:
+        g = case.g_win.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(g, case.o_win), "window ring differs"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_indexer_scores_and_topk(name):
+    case = case_of(name)
+    cfg = case.cfg
+    for layer, j in indexer_layers(cfg):
+        say("indexer", name, "layer", layer)
+        got_idx, got_s = G.gpu_topk(case, j)
+        ref_s = G.oracle_scores(case, j)
+        G.check_scores(got_s, ref_s, case.n_visible)
+        G.check_topk(got_idx, ref_s, case.n_visible, cfg.k)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_given_oracle_indices(name):
+    case = case_of(name)
+    for layer, idx in enumerate(oracle_indices_per_layer(case)):
+        say("decode", name, "layer", layer, case.cfg.layers[layer])
+        ref_o, ref_l = G.oracle_attention(case, layer, idx)
+        got_o, got_l = G.gpu_decode(case, layer, idx)
+        G.check_attention(got_o, got_l, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_step_end_to_end(name):
+    """The GPU's own indices feed the GPU decode; the outputs are compared with
+    the oracle's step wherever the two selected sets coincide exactly."""
+    case = case_of(name)
+    cfg = case.cfg
+    ref_idx = oracle_indices_per_layer(case)
+    latest, j = None, 0
+    for layer, mode in enumerate(cfg.layers):
+        if mode in ("full", "reindex"):
+            latest, _ = G.gpu_topk(case, j, want_scores=False)
+            j += 1
+        say("step", name, "layer", layer, mode)
+        got_o, got_l = G.gpu_decode(case, layer, latest)
+        ref_o, ref_l = G.oracle_attention(case, layer, ref_idx[layer])
+        for b in range(cfg.B):
+            if set(latest[b].tolist()) == set(ref_idx[layer][b].tolist()):
+                G.check_attention(got_o[b:b + 1], got_l[b:b + 1], ref_o[b:b + 1], ref_l[b:b + 1])
+
+
+@pytest.mark.parametrize("name", ["c1", "c3s", "c4s"])
+def test_causal_mask_and_short_contexts(name):
+    case = case_of(name)
+    cfg = case.cfg
+    N, k = cfg.N, cfg.k
+    for nv in ([0] * cfg.B, [min(N, k // 2 + 3)] + [N] * (cfg.B - 1), [N - 1] + [1] * (cfg.B - 1),
+               [k] * cfg.B, [k + 1] * cfg.B):
+        nv = np.array([min(v, N) for v in nv], np.int32)
+        say("mask", name, nv.tolist())
+        got_idx, got_s = G.gpu_topk(case, 0, n_visible=nv)
+        ref_s = G.oracle_scores(case, 0, n_visible=nv)
+        G.check_scores(got_s, ref_s, nv)
+        G.check_topk(got_idx, ref_s, nv, k)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s"])
+def test_decode_edge_cases(name):
+    case = case_of(name)
+    cfg = case.cfg
+    rng = np.random.default_rng(7)
+    B, N = cfg.B, cfg.N
+    k = min(cfg.k, 300)
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(B)]).astype(np.int32)
+    variants = {
+        "ragged_minus_ones": np.where(rng.random((B, k)) < 0.3, -1, idx).astype(np.int32),
+        "duplicates": np.concatenate([idx[:, :k // 2], idx[:, :k - k // 2]], 1).astype(np.int32),
+        "all_minus_one": -np.ones((B, 37), np.int32),
+        "single": idx[:, :1].copy(),
+        "out_of_range_skipped": np.concatenate([idx[:, :50], np.full((B, 5), N + 7, np.int32)], 1),
+    }
+    for vname, v in variants.items():
+        say("decode edge", name, vname)
+        ref_v = np.where((v >= 0) & (v < N), v, -1).astype(np.int32)
+        ref_o, ref_l = G.oracle_attention(case, 0, ref_v)
+        got_o, got_l = G.gpu_decode(case, 0, v)
+        G.check_attention(got_o, got_l, ref_o, ref_l)
+    if cfg.W:
+        say("decode edge", name, "window only")
+        empty = np.zeros((B, 0), np.int32)
+        ref_o, ref_l = G.oracle_attention(case, 0, empty)
+        got_o, got_l = G.gpu_decode(case, 0, empty)
+        G.check_attention(got_o, got_l, ref_o, ref_l)
+
+
+def test_quantise_bitexact_over_magnitudes():
+    """Rows spanning 12 decades, exact zeros, signed zeros, tiny subnormal-range
+    values and block maxima sitting on format boundaries, in every format."""
+    rng = np.random.default_rng(11)
+    n = 4096
+    x = rng.standard_normal((1, n, 576)).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-8, 4, (1, n, 1))).astype(np.float32)
+    x[0, :16] = 0.0
+    x[0, 16:32] = -0.0
+    x[0, 32:48, ::3] = 448.0
+    x[0, 48:64, ::5] = 6.0
+    x[0, 64:80] *= np.float32(1e-30)
+    x[0, 80:96, :] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], (16, 576)).astype(np.float32)
+    for fmt, dim, rope in ((G.O.E4M3_S128, 512, 64), (G.O.E2M1_S16, 512, 0), (G.O.BF16, 512, 64),
+                           (G.O.E4M3_S128, 128, 0), (G.O.E2M1_S16, 128, 0), (G.O.F32, 64, 16)):
+        say("quantise", fmt, dim, rope)
+        D = dim + rope
+        src = np.ascontiguousarray(x[:, :, :D])
+        rb = G.O.row_bytes(fmt, dim, rope)
+        ref = np.zeros((1, n, rb), np.uint8)
+        slots = np.arange(n, dtype=np.int32)[None]
+        G.O.append((fmt, dim, rope), (fmt, dim, rope), src, None, slots, ref, None)
+        got = torch.zeros((1, n, rb), dtype=torch.uint8, device="cuda")
+        G.M.mla_kv_append_quant(G.M.Row(fmt, dim, rope), G.M.Row(fmt, dim, 0), G._t(src), None, G._t(slots),
+                                got, None)
+        torch.cuda.synchronize()
+        g = got.cpu().numpy()
+        bad = np.flatnonzero(np.any(g != ref, axis=(0, 2)))
+        assert bad.size == 0, f"fmt {fmt}: {bad.size} rows differ, first {bad[:5]}"
+
+
+# ---- full sizes (the configurations the benchmark times) -----------------
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size(name):
+    case = case_of(name)
+    cfg = case.cfg
+    say("full append parity", name)
+    assert np.array_equal(case.g_main.cpu().numpy(), case.o_main)
+    assert np.array_equal(case.g_idx.cpu().numpy(), case.o_idx)
+    ref_idx = oracle_indices_per_layer(case)
+    for layer, j in indexer_layers(cfg):
+        say("full indexer", name, "layer", layer)
+        got_idx, got_s = G.gpu_topk(case, j)
+        ref_s = G.oracle_scores(case, j)
+        G.check_scores(got_s, ref_s, case.n_visible)
+        ne = G.check_topk(got_idx, ref_s, case.n_visible, cfg.k)
+        say("  exempt boundary swaps:", ne)
+    for layer in range(len(cfg.layers)):
+        say("full decode", name, "layer", layer)
+        ref_o, ref_l = G.oracle_attention(case, layer, ref_idx[layer])
+        got_o, got_l = G.gpu_decode(case, layer, ref_idx[layer])
+        wo, wl = G.check_attention(got_o, got_l, ref_o, ref_l)
+        say(f"  worst rel err out {wo:.2e} lse {wl:.2e}")

@@ -28,7 +28,10 @@
  *  - Arguments are validated on the host before any launch; a call that
  *    returns an error has enqueued nothing (except MLA_ERR_HIP, where a launch
  *    itself failed).  mla_last_error() then holds a message.
- *  - Byte strides are int64; rows are little-endian byte arrays.
+ *  - Byte strides are int64; rows are little-endian byte arrays.  A cache's base
+ *    pointer must be 16-byte aligned and its sequence stride a multiple of the
+ *    row alignment (the largest power of two <= 16 dividing the row size:
+ *    16 for 656 / 288 / 256-byte rows, 8 for 72, 4 for 132).
  *  - Non-finite inputs give unspecified (but memory-safe) results.
  */
 #ifndef MLA_H

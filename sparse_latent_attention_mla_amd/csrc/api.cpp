@@ -35,8 +35,14 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Minimum alignment of row starts for a format (the kernels use wide loads).
-size_t row_alignment(int fmt) { return fmt == MLA_FMT_F32 ? 4 : (fmt == MLA_FMT_BF16 ? 2 : 4); }
+// Alignment every row start keeps when the cache base is 16-byte aligned and
+// the sequence stride is a multiple of it: the largest power of two <= 16
+// dividing the row size.  The kernels never load wider than this from a row.
+int64_t row_alignment(int64_t row_bytes) {
+    int64_t a = 16;
+    while (a > 1 && row_bytes % a != 0) a >>= 1;
+    return a;
+}
 
 mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int64_t stride, int64_t capacity,
                         int B, int64_t* row_bytes) {
@@ -50,11 +56,10 @@ mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int6
     if (B > 1 && stride < capacity * rb)
         return fail(MLA_ERR_INVALID_ARG, "%s: sequence stride %lld < capacity * row bytes %lld", what,
                     (long long)stride, (long long)(capacity * rb));
-    if (!aligned(cache, 16) || stride % 16 != 0)
-        return fail(MLA_ERR_INVALID_ARG, "%s: cache and sequence stride must be 16-byte aligned", what);
-    if (rb % (int64_t)row_alignment(row.fmt) != 0)
-        return fail(MLA_ERR_UNSUPPORTED, "%s: row bytes %lld not a multiple of %zu", what, (long long)rb,
-                    row_alignment(row.fmt));
+    const int64_t ra = row_alignment(rb);
+    if (!aligned(cache, 16) || stride % ra != 0)
+        return fail(MLA_ERR_INVALID_ARG, "%s: cache base must be 16-byte aligned and the sequence stride a "
+                    "multiple of %lld", what, (long long)ra);
     return ok();
 }
 

@@ -103,13 +103,12 @@ __device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
     return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
 }
 
-// Four E4M3 codes -> two dwords of bf16 (exact).
+// Four E4M3 codes -> two dwords of bf16 (exact: every E4M3 value is a bf16 value;
+// the converter's scale operand only contributes its exponent, here 2^0).
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
-    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
     u32x2 r;
-    r.x = pack_bf16_trunc(lo.x, lo.y);
-    r.y = pack_bf16_trunc(hi.x, hi.y);
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     return r;
 }
 

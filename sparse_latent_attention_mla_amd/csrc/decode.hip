@@ -25,6 +25,8 @@
 //   written as a partial; k_merge combines the partials by logsumexp.
 // Generic path (any other shape): one workgroup per (b, h), fp32 on the vector
 // ALUs, writes the final output directly.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -41,14 +43,22 @@ constexpr int kGenericMaxRows = 8192;
 
 enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2 };
 
+// Entries per split: fewer splits mean fewer fp32 partials to write and merge,
+// more splits mean more workgroups in flight.  MLA_DECODE_RPS (a multiple of
+// 32) overrides the default for tuning; the workspace query reads it too.
 int rows_per_split(int H, int k) {
     (void)k;
-    return H >= 128 ? 64 : 128;
+    if (const char* e = getenv("MLA_DECODE_RPS")) {
+        const int v = atoi(e);
+        if (v >= 32 && v % 32 == 0) return v;
+    }
+    return H >= 128 ? 256 : 128;
 }
 
 template <int DQK>
 struct Lds {
-    static constexpr int kKs = DQK + 8;                 // bf16 per K row (padded)
+    static constexpr int kKs = DQK + 8;                 // bf16 per K / q row (padded)
+    uint16_t qs[64 * kKs];                              // q of the workgroup's (up to) 64 heads
     uint16_t ks[kChunk * kKs];
     uint16_t vt[kDv * kVt];
     float rscale[kChunk][4];
@@ -56,33 +66,61 @@ struct Lds {
     uint32_t sref_bits[4];
 };
 
-// Dequantise segment `sg` (32 channels) of a source row into LDS row r.
+// Raw bytes of one gather item (32 channels of one row) held in registers
+// between its global load and its dequantising store into LDS.
+struct Slot {
+    u32x4 v[4];
+    uint32_t x;           // E4M3: the row's fp32 scale word; E2M1: the two scale bytes
+    int ok;
+};
+
+// Issue the global loads of segment `sg` (channels 32*sg .. +31) of a row.
 template <int SRC, int DQK>
-__device__ __forceinline__ void gather_segment(Lds<DQK>& L, const uint8_t* __restrict__ row, int r, int sg) {
+__device__ __forceinline__ void load_segment(Slot& sl, const uint8_t* __restrict__ row, int sg) {
+    if constexpr (SRC == SRC_BF16) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sl.v[i] = p[i];
+    } else if constexpr (SRC == SRC_E4M3) {
+        if (sg < 16) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 32);
+            sl.v[0] = p[0];
+            sl.v[1] = p[1];
+            sl.x = reinterpret_cast<const uint32_t*>(row + 512)[sg >> 2];
+        } else {  // bf16 RoPE channels 512 + 32 (sg - 16) ..
+            const u32x4* p = reinterpret_cast<const u32x4*>(row + 528 + (sg - 16) * 64);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sl.v[i] = p[i];
+        }
+    } else {  // SRC_FP4: 16 nibble bytes + 2 scale bytes per 32 channels
+        sl.v[0] = *reinterpret_cast<const u32x4*>(row + sg * 16);
+        sl.x = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * sg);
+    }
+}
+
+// Dequantise a loaded segment into LDS row r: K row-major in bf16 and, for the
+// value channels, V^T channel-major (fp16 for E4M3 / E2M1, bf16 for bf16 rows).
+template <int SRC, int DQK>
+__device__ __forceinline__ void store_segment(Lds<DQK>& L, const Slot& sl, int r, int sg) {
     uint16_t* kdst = L.ks + r * Lds<DQK>::kKs + sg * 32;
     const bool in_v = sg * 32 < kDv;
     if constexpr (SRC == SRC_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 64);
-        u32x4 v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = p[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = v[i];
+        for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = sl.v[i];
         if (in_v) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = v[i][e];
+                    const uint32_t w = sl.v[i][e];
                     L.vt[(sg * 32 + 8 * i + 2 * e) * kVt + r] = (uint16_t)(w & 0xFFFFu);
                     L.vt[(sg * 32 + 8 * i + 2 * e + 1) * kVt + r] = (uint16_t)(w >> 16);
                 }
         }
     } else if constexpr (SRC == SRC_E4M3) {
         if (sg < 16) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 32);
-            const u32x4 c0 = p[0], c1 = p[1];
-            const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const uint32_t w[8] = {sl.v[0].x, sl.v[0].y, sl.v[0].z, sl.v[0].w,
+                                   sl.v[1].x, sl.v[1].y, sl.v[1].z, sl.v[1].w};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float f[4];
@@ -93,17 +131,14 @@ __device__ __forceinline__ void gather_segment(Lds<DQK>& L, const uint8_t* __res
                 for (int e = 0; e < 4; ++e)
                     L.vt[(sg * 32 + 4 * i + e) * kVt + r] = __builtin_bit_cast(uint16_t, (_Float16)f[e]);
             }
-            if ((sg & 3) == 0) L.rscale[r][sg >> 2] = reinterpret_cast<const float*>(row + 512)[sg >> 2];
-        } else {  // bf16 RoPE channels 512 + 32 (sg - 16) ..
-            const u32x4* p = reinterpret_cast<const u32x4*>(row + 528 + (sg - 16) * 64);
+            if ((sg & 3) == 0) L.rscale[r][sg >> 2] = u2f(sl.x);
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = p[i];
+            for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = sl.v[i];
         }
-    } else {  // SRC_FP4: 16 nibble bytes + 2 scale bytes per 32 channels
-        const u32x4 nb = *reinterpret_cast<const u32x4*>(row + sg * 16);
-        const uint32_t sw = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * sg);
-        const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32(sw >> 8);
-        const uint32_t w[4] = {nb.x, nb.y, nb.z, nb.w};
+    } else {
+        const float s0 = e4m3_to_f32(sl.x & 0xFFu), s1 = e4m3_to_f32((sl.x >> 8) & 0xFFu);
+        const uint32_t w[4] = {sl.v[0].x, sl.v[0].y, sl.v[0].z, sl.v[0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float s = (i < 2) ? s0 : s1;
@@ -150,12 +185,6 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
     constexpr float kLog2e = 1.4426950408889634f;
     const float zscale = a.scale * kLog2e;
 
-    // q of this lane's head, k-slots (g, e) of k-step t = channel t*32 + g*8 + e
-    u32x4 qreg[NT];
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head) * DQK;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) qreg[t] = *reinterpret_cast<const u32x4*>(qp + t * 32 + g * 8);
-
     // source row of split entry u (nullptr if invalid)
     auto row_ptr = [&](int u) -> const uint8_t* {
         if (u >= n_rows) return nullptr;
@@ -164,6 +193,52 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
         if (s < 0 || s >= a.capacity) return nullptr;
         return a.cache + b * a.stride + (int64_t)s * a.row_bytes;
     };
+
+    // gather items of a chunk: (segment, row), segment-major; each thread owns NSLOT of them
+    constexpr int NTH = NHT * 64;
+    constexpr int NITEMS = kChunk * NSEG;
+    constexpr int NSLOT = (NITEMS + NTH - 1) / NTH;
+    auto load_chunk = [&](int c0, Slot* sl) {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int item = tid + i * NTH;
+            sl[i].ok = 0;
+            if (item < NITEMS) {
+                const uint8_t* rp = row_ptr(c0 + item % kChunk);
+                if (rp) {
+                    sl[i].ok = 1;
+                    load_segment<SRC, DQK>(sl[i], rp, item / kChunk);
+                }
+            }
+        }
+    };
+    auto store_chunk = [&](const Slot* sl) {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int item = tid + i * NTH;
+            if (item < NITEMS) {
+                const int sg = item / kChunk, r = item % kChunk;
+                if (sl[i].ok) store_segment<SRC, DQK>(L, sl[i], r, sg);
+                else zero_segment<DQK>(L, r, sg);
+                if (sg == 0) L.valid[r] = sl[i].ok;
+            }
+        }
+    };
+    Slot sl[NSLOT];
+    if (n_rows > 0) load_chunk(0, sl);
+
+    // q of the workgroup's heads into LDS (16-byte pieces); lane (j, g) later reads
+    // k-slots (g, e) of k-step t = channel t*32 + g*8 + e of head j of its tile
+    {
+        const int head0 = 16 * NHT * (int)blockIdx.z;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head0) * DQK;
+        for (int i = tid; i < 16 * NHT * (DQK / 8); i += NHT * 64) {
+            const int hh = i / (DQK / 8), c8 = i % (DQK / 8);
+            *reinterpret_cast<u32x4*>(L.qs + hh * Lds<DQK>::kKs + c8 * 8) =
+                *reinterpret_cast<const u32x4*>(qp + (int64_t)hh * DQK + c8 * 8);
+        }
+    }
+    const uint16_t* qrow = L.qs + (16 * w + j) * Lds<DQK>::kKs + g * 8;
 
     float inv_sref[4] = {1.f, 1.f, 1.f, 1.f};
     if constexpr (SRC == SRC_E4M3) {
@@ -193,15 +268,9 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
     float m_run = -__builtin_inff(), l_run = 0.0f;
 
     for (int c0 = 0; c0 < n_rows; c0 += kChunk) {
-        // ---- gather the chunk (items: segment-major, row-minor)
-        for (int item = tid; item < kChunk * NSEG; item += NHT * 64) {
-            const int sg = item / kChunk, r = item % kChunk;
-            const uint8_t* rp = row_ptr(c0 + r);
-            if (rp) gather_segment<SRC, DQK>(L, rp, r, sg);
-            else zero_segment<DQK>(L, r, sg);
-            if (sg == 0) L.valid[r] = rp != nullptr;
-        }
+        store_chunk(sl);
         __syncthreads();
+        if (c0 + kChunk < n_rows) load_chunk(c0 + kChunk, sl);   // in flight during the MFMAs
 
         // ---- S^T = K q^T for the chunk's two 16-row tiles
         float z[2][4];
@@ -215,22 +284,29 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
                     f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int t = 4 * b4; t < 4 * b4 + 4; ++t)
-                        t4 = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32), qreg[t], t4);
+                        t4 = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
+                                       *reinterpret_cast<const u32x4*>(qrow + t * 32), t4);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) s[r] += t4[r] * L.rscale[16 * rt + 4 * g + r][b4];
                 }
 #pragma unroll
-                for (int t = 16; t < NT; ++t) s = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32), qreg[t], s);
+                for (int t = 16; t < NT; ++t)
+                    s = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
+                                  *reinterpret_cast<const u32x4*>(qrow + t * 32), s);
             } else {
 #pragma unroll
-                for (int t = 0; t < NT; ++t) s = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32), qreg[t], s);
+                for (int t = 0; t < NT; ++t)
+                    s = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
+                                  *reinterpret_cast<const u32x4*>(qrow + t * 32), s);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 z[rt][r] = L.valid[16 * rt + 4 * g + r] ? s[r] * zscale : -__builtin_inff();
         }
 
-        // ---- online softmax (base 2), per head j; lanes j, j+16, j+32, j+48 share a head
+        // ---- online softmax (base 2), per head j; lanes j, j+16, j+32, j+48 share a head.
+        // The reference m_ref moves only when a chunk's max exceeds it by more than 8
+        // (p <= 2^8 keeps fp16 P finite), so the output tile is rarely rescaled.
         float zmax = -__builtin_inff();
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
@@ -238,30 +314,27 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
             for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, z[rt][r]);
         zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
         zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        const float m_new = fmaxf(m_run, zmax);
-        float p[2][4];
-        float psum = 0.0f, alpha = 1.0f;
-        if (m_new == -__builtin_inff()) {
+        const bool move = zmax > m_run + 8.0f;
+        if (__ballot(move)) {
+            const float m_new = move ? zmax : m_run;
+            const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[rt][r] = 0.0f;
-        } else {
-            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    p[rt][r] = __builtin_amdgcn_exp2f(z[rt][r] - m_new);
-                    psum += p[rt][r];
-                }
+            for (int i = 0; i < kDv / 16; ++i) oacc[i] *= alpha;
+            m_run = m_new;
         }
+        float p[2][4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[rt][r] = (z[rt][r] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[rt][r] - m_run);
+                psum += p[rt][r];
+            }
         psum += __shfl_xor(psum, 16, 64);
         psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < kDv / 16; ++i) oacc[i] *= alpha;
+        l_run += psum;
 
         // ---- O^T += V^T P^T.  k-slot (g, e): e < 4 -> row 4g+e, e >= 4 -> row 16+4g+e-4
         if constexpr (SRC == SRC_BF16) {

@@ -22,85 +22,213 @@ namespace mla {
 namespace {
 
 constexpr int kScanThreads = 256;         // 4 waves
-constexpr int kTilesPerWave = 8;          // 16-row tiles per wave
+constexpr int kTilesPerWave = 8;          // 16-row tiles per wave (direct-load path)
 constexpr int kRowsPerBlock = 4 * kTilesPerWave * 16;
+constexpr int kChunkRows = 64;            // rows a wave stages through LDS per step
+constexpr int kStagedBlocks = 512;        // target workgroups of the staged scan (2 per CU)
 
-// ------------------------------------------------------------------------
-// Load the 32 channels g*32 .. g*32+31 of one indexer row as four bf16 MFMA
-// B-operand chunks: kb[t] holds channels g*32 + t*8 .. +7.  Returns the
-// post-contraction multiplier of the row (its fp32 scale for E4M3, else 1).
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Dequantise the 32 channels g*32 .. g*32+31 of a row (given as raw words) into
+// four bf16 MFMA B-operand chunks kb[t] = channels g*32 + t*8 .. +7.
 template <int FMT>
-__device__ __forceinline__ float load_key_operand(const uint8_t* __restrict__ row, int g, u32x4 kb[4]) {
-    if constexpr (FMT == MLA_FMT_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + g * 64);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) kb[t] = __builtin_nontemporal_load(p + t);
-        return 1.0f;
-    } else if constexpr (FMT == MLA_FMT_E4M3_S128) {
-        // 132-byte rows: 4-byte aligned only
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(row + g * 32);
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = __builtin_nontemporal_load(p + i);
-        const float scale = __builtin_nontemporal_load(reinterpret_cast<const float*>(row + 128));
+__device__ __forceinline__ void dequant_key(const uint32_t* w, uint32_t sw, u32x4 kb[4]) {
+    if constexpr (FMT == MLA_FMT_E4M3_S128) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             u32x2 lo = e4m3x4_to_bf16(w[2 * t]);
             u32x2 hi = e4m3x4_to_bf16(w[2 * t + 1]);
             kb[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
-        return scale;
-    } else {  // MLA_FMT_E2M1_S16, 72-byte rows: 8-byte aligned
-        const u32x2* p = reinterpret_cast<const u32x2*>(row + g * 16);
-        const u32x2 n01 = __builtin_nontemporal_load(p);
-        const u32x2 n23 = __builtin_nontemporal_load(p + 1);
-        const uint32_t sw = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(row + 64 + 2 * g));
-        const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32(sw >> 8);
-        const uint32_t nib[4] = {n01.x, n01.y, n23.x, n23.y};
+    } else {  // E2M1 x E4M3 scale, exact in bf16
+        const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32((sw >> 8) & 0xFFu);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float s = (t < 2) ? s0 : s1;
-            const uint32_t w = nib[t];
-            f32x2 v0 = e2m1x2_to_f32<0>(w), v1 = e2m1x2_to_f32<1>(w);
-            f32x2 v2 = e2m1x2_to_f32<2>(w), v3 = e2m1x2_to_f32<3>(w);
+            f32x2 v0 = e2m1x2_to_f32<0>(w[t]), v1 = e2m1x2_to_f32<1>(w[t]);
+            f32x2 v2 = e2m1x2_to_f32<2>(w[t]), v3 = e2m1x2_to_f32<3>(w[t]);
             kb[t] = u32x4{pack_bf16_trunc(v0.x * s, v0.y * s), pack_bf16_trunc(v1.x * s, v1.y * s),
                           pack_bf16_trunc(v2.x * s, v2.y * s), pack_bf16_trunc(v3.x * s, v3.y * s)};
         }
-        return 1.0f;
     }
 }
 
-// MFMA scan for d_I = 128 and H_I = 16 * MT.  Block: 4 waves, kRowsPerBlock rows
-// of one sequence; a wave takes 16-row tiles.  Lane (col = l % 16, g = l / 16)
-// owns row col of the tile and channels g*32 .. g*32+31 (k-slot (g, e) of
+// ReLU on the bit pattern: a set sign bit is a negative int32 (also for -0),
+// so the signed integer max with 0 clears it; one instruction, no NaN canonicalisation.
+__device__ __forceinline__ float relu(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+template <int MT>
+struct ScanCtx {
+    u32x4 qa[MT][4];      // A operand: q_idx of heads 16m + col, channels g*32 + t*8 .. +7
+    float wv[MT][4];      // w * sigma of accumulator rows 4g + r of head tile m
+};
+
+// Contract one 16-row tile and emit its scores: lane (col, g) holds the B
+// operand of row `s` (= tile0 + col); `mult` is its post-contraction factor.
+template <int MT>
+__device__ __forceinline__ void tile_scores(const ScanCtx<MT>& C, const u32x4 kb[4], float mult, int64_t s,
+                                            bool valid, int g, float sigma, int64_t capacity, float* scores,
+                                            uint32_t* hist) {
+    f32x4 acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(C.qa[m][t], kb[t], acc[m]);
+    // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
+    float part = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += C.wv[m][r] * relu(acc[m][r]);
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    part *= mult;
+    if (g == 0 && s < capacity) {
+        scores[s] = valid ? part : -__builtin_inff();
+        if (valid) atomicAdd(&hist[score_key(part) >> (32 - kHistBits)], 1u);
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void load_ctx(ScanCtx<MT>& C, const ScanArgs& a, int b, int col, int g) {
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q_idx) + (int64_t)b * a.H_I * 128;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            C.qa[m][t] = *reinterpret_cast<const u32x4*>(qb + (16 * m + col) * 128 + g * 32 + t * 8);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) C.wv[m][r] = a.w[(int64_t)b * a.H_I + 16 * m + 4 * g + r] * a.sigma;
+}
+
+__device__ __forceinline__ void flush_hist(const uint32_t* hist, uint32_t* gh) {
+    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) {
+        const uint32_t v = hist[i];
+        if (v) atomicAdd(&gh[i], v);
+    }
+}
+
+// MFMA scan, rows that are not 16-byte multiples (E4M3 132 B, E2M1 72 B).
+// Each wave streams chunks of 64 contiguous rows: 16-byte coalesced global loads
+// into registers, then into a wave-private LDS stage, from which every lane
+// reads the bytes of its MFMA operand.  The next chunk's loads are in flight
+// while the current chunk is contracted.  Lane (col = l % 16, g = l / 16) owns
+// row col of a 16-row tile and channels g*32 .. g*32+31 (k-slot (g, e) of
 // k-step t is channel g*32 + t*8 + e, for A and B alike).
 template <int FMT, int MT>
-__global__ __launch_bounds__(kScanThreads) void k_scan_mfma(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int rows_per_block) {
+    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int kChunkBytes = kChunkRows * RB;
+    constexpr int kLoads = (kChunkBytes + 64 * 16 - 1) / (64 * 16);
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][kChunkBytes];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int64_t nvis = clamp_visible(a.n_visible[b], a.capacity);
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+    const int n_chunks = rows_per_block / (4 * kChunkRows);
+    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
+    ScanCtx<MT> C;
+    load_ctx<MT>(C, a, b, col, g);
+    __syncthreads();
+
+    const uint8_t* base = a.cache + b * a.stride;
+    float* scores = a.scores + b * a.capacity;
+    uint8_t* st = stage[wave];
+    u32x4 raw[kLoads];
+    // chunk c of this wave covers rows row0 + (c * 4 + wave) * 64 ..
+    auto issue = [&](int c) {
+        const int64_t r = row0 + (int64_t)(c * 4 + wave) * kChunkRows;
+        const int64_t avail = (a.capacity - r) * RB;          // bytes of this sequence from r on
+        const uint8_t* src = base + r * RB;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int off = (i * 64 + lane) * 16;
+            raw[i] = u32x4{0u, 0u, 0u, 0u};
+            if (off < kChunkBytes && off + 16 <= avail) {
+                raw[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load(
+                                                       reinterpret_cast<const u32x4_a4*>(src + off)));
+            } else if (off < kChunkBytes && off < avail) {
+                // the sequence ends inside this vector: its last 4, 8 or 12 bytes (rows and
+                // strides are multiples of 4 bytes)
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(src + off);
+                const int n = (int)((avail - off) >> 2);
+                raw[i].x = p[0];
+                if (n > 1) raw[i].y = p[1];
+                if (n > 2) raw[i].z = p[2];
+            }
+        }
+    };
+    const int64_t first_row = row0 + (int64_t)wave * kChunkRows;
+    if (first_row < nvis) issue(0);
+    for (int c = 0; c < n_chunks; ++c) {
+        const int64_t r = row0 + (int64_t)(c * 4 + wave) * kChunkRows;
+        if (r >= a.capacity) break;
+        if (r >= nvis) {                                       // whole chunk masked
+            for (int i = lane; i < kChunkRows; i += 64)
+                if (r + i < a.capacity) scores[r + i] = -__builtin_inff();
+            continue;
+        }
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int off = (i * 64 + lane) * 16;
+            if (off < kChunkBytes) *reinterpret_cast<u32x4*>(st + off) = raw[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t rn = r + 4 * kChunkRows;
+        if (c + 1 < n_chunks && rn < nvis) issue(c + 1);
+#pragma unroll
+        for (int tile = 0; tile < kChunkRows / 16; ++tile) {
+            const int rr = tile * 16 + col;
+            const int64_t s = r + rr;
+            const bool valid = s < nvis;
+            const uint8_t* rp = st + rr * RB;
+            uint32_t w[8];
+            uint32_t sw = 0;
+            float mult = 1.0f;
+            if constexpr (FMT == MLA_FMT_E4M3_S128) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 32)[i];
+                mult = *reinterpret_cast<const float*>(rp + 128);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 16)[i];
+                sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
+            }
+            u32x4 kb[4];
+            dequant_key<FMT>(w, sw, kb);
+            if (!valid) mult = 0.0f;
+            tile_scores<MT>(C, kb, mult, s, valid, g, a.sigma, a.capacity, scores, hist);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();
+    flush_hist(hist, a.hist + (int64_t)b * kHistBins);
+}
+
+// MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
+template <int MT>
+__global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
     __shared__ uint32_t hist[kHistBins];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
     const int64_t nvis = clamp_visible(a.n_visible[b], a.capacity);
     const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock;
-
     for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
-
-    // A operand: q_idx of heads 16m + col, channels g*32 + t*8 .. +7
-    u32x4 qa[MT][4];
-    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q_idx) + (int64_t)b * a.H_I * 128;
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            qa[m][t] = *reinterpret_cast<const u32x4*>(qb + (16 * m + col) * 128 + g * 32 + t * 8);
-    // head weights of the accumulator rows 4g + r of each head tile
-    float wv[MT][4];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wv[m][r] = a.w[(int64_t)b * a.H_I + 16 * m + 4 * g + r];
+    ScanCtx<MT> C;
+    load_ctx<MT>(C, a, b, col, g);
     __syncthreads();
-
     const uint8_t* base = a.cache + b * a.stride;
     float* scores = a.scores + b * a.capacity;
     for (int it = 0; it < kTilesPerWave; ++it) {
@@ -108,44 +236,23 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_mfma(ScanArgs a) {
         if (tile0 >= a.capacity) break;
         const int64_t s = tile0 + col;
         const bool valid = s < nvis;
-        if (tile0 >= nvis) {               // whole tile masked
+        if (tile0 >= nvis) {
             if (g == 0 && s < a.capacity) scores[s] = -__builtin_inff();
             continue;
         }
         u32x4 kb[4];
-        float mult = 0.0f;
         if (valid) {
-            mult = load_key_operand<FMT>(base + s * a.row_bytes, g, kb);
+            const u32x4* p = reinterpret_cast<const u32x4*>(base + s * 256 + g * 64);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) kb[t] = __builtin_nontemporal_load(p + t);
         } else {
 #pragma unroll
             for (int t = 0; t < 4; ++t) kb[t] = u32x4{0u, 0u, 0u, 0u};
         }
-        f32x4 acc[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(qa[m][t], kb[t], acc[m]);
-        const float c = a.sigma * mult;
-        float part = 0.0f;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) part += wv[m][r] * fmaxf(acc[m][r] * c, 0.0f);
-        part += __shfl_xor(part, 16, 64);
-        part += __shfl_xor(part, 32, 64);
-        if (g == 0 && s < a.capacity) {
-            scores[s] = valid ? part : -__builtin_inff();
-            if (valid) atomicAdd(&hist[score_key(part) >> (32 - kHistBits)], 1u);
-        }
+        tile_scores<MT>(C, kb, valid ? 1.0f : 0.0f, s, valid, g, a.sigma, a.capacity, scores, hist);
     }
     __syncthreads();
-    uint32_t* gh = a.hist + (int64_t)b * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) {
-        const uint32_t v = hist[i];
-        if (v) atomicAdd(&gh[i], v);
-    }
+    flush_hist(hist, a.hist + (int64_t)b * kHistBins);
 }
 
 // ------------------------------------------------------------------------
@@ -223,10 +330,18 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
                       a.dim == 128 && a.H_I % 16 == 0 && a.H_I <= 64;
     if (mfma) {
         const dim3 grid((unsigned)((a.capacity + kRowsPerBlock - 1) / kRowsPerBlock), a.B);
-#define MLA_SCAN_CASE(F, M)                                                              \
-    if (a.fmt == F && a.H_I == 16 * M) {                                                 \
-        hipLaunchKernelGGL((k_scan_mfma<F, M>), grid, dim3(kScanThreads), 0, stream, a); \
-        return hipGetLastError();                                                        \
+        // staged scan: ~kStagedBlocks long-lived workgroups, each wave streaming many chunks
+        const int64_t per_seq = (kStagedBlocks + a.B - 1) / a.B;
+        int64_t rpb = (a.capacity + per_seq - 1) / per_seq;
+        rpb = ((rpb + 4 * kChunkRows - 1) / (4 * kChunkRows)) * (4 * kChunkRows);
+        const dim3 sgrid((unsigned)((a.capacity + rpb - 1) / rpb), a.B);
+#define MLA_SCAN_CASE(F, M)                                                                    \
+    if (a.fmt == F && a.H_I == 16 * M) {                                                       \
+        if (F == MLA_FMT_BF16)                                                                 \
+            hipLaunchKernelGGL((k_scan_bf16<M>), grid, dim3(kScanThreads), 0, stream, a);      \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_scan_staged<F, M>), sgrid, dim3(kScanThreads), 0, stream, a, (int)rpb); \
+        return hipGetLastError();                                                              \
     }
         MLA_SCAN_CASE(MLA_FMT_BF16, 1) MLA_SCAN_CASE(MLA_FMT_BF16, 2)
         MLA_SCAN_CASE(MLA_FMT_BF16, 3) MLA_SCAN_CASE(MLA_FMT_BF16, 4)

@@ -117,8 +117,8 @@ def build_layers(cfg, n_layers, seed=0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py: the decode path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -1,5 +1,5 @@
 // decode.hip -- absorbed-MLA sparse decode: shared-KV MQA over the selected
-// latent entries plus the window, online softmax, logsumexp output.
+// latent entries plus the window, softmax, logsumexp output.
 //
 // For each (b, h), over U = {selected rows} + {window slots}:
 //   z_u = scale * q[b,h,:] . K_u,  lse = logsumexp z,  out = sum_u e^(z_u - lse) K_u[:d_v]
@@ -8,21 +8,26 @@
 // to HCA/CSA", Part 2 "What replaced MLA"; each selected latent is read once
 // for all heads, [P1] "DeepSeek-V3.2", "The lightning indexer").
 //
-// MFMA path (H = 16 * NHT, d_v = 512, K width 576 = 512 + 64 or 512):
-//   grid (splits, B, head groups); a split is `rps` consecutive entries of
-//   idx[b] (or of the window ring); workgroup = NHT <= 4 waves (one wave per
-//   SIMD: a wave keeps q and the fp32 output tile in registers), wave w owns
-//   heads 16 * (NHT * blockIdx.z + w) .. +15.
-//   Per 32-row chunk the workgroup gathers the rows once into LDS, dequantised
-//   exactly: K row-major in bf16 (E4M3 codes unscaled; E2M1 x scale), V
-//   channel-major in fp16 (E4M3 codes / E2M1 x scale, both exact in fp16) or
-//   bf16 (bf16 rows).  Each wave computes S^T = K q^T on bf16 MFMA (E4M3: one
-//   accumulator per 128-channel block, multiplied by the row's fp32 scale),
-//   runs the online softmax in registers and accumulates O^T = V^T P^T on
-//   MFMA: fp16 P (E4M3 rows: P times the row scale over the split's largest
-//   scale of that block, so P <= 1), or bf16 P split into a high and a low
-//   part when V is bf16.  The split's normalised output and its logsumexp are
-//   written as a partial; k_merge combines the partials by logsumexp.
+// MFMA path (H a multiple of 16 up to 128, d_v = 512, K width 576 = 512 + 64 or 512):
+//   grid (splits, B, head groups); a split is `rps` <= 128 consecutive entries of
+//   idx[b] (or of the window ring); workgroup = 4 waves that all gather, and the
+//   first NHT = min(4, H / 16) of them also contract: wave w owns heads
+//   16 * (NHT * blockIdx.z + w) .. +15, whose queries sit in LDS.
+//   Two phases over the split's 32-row chunks, the next chunk's row bytes always
+//   loaded into registers while the current one is contracted:
+//   * QK phase: the workgroup dequantises each chunk's rows exactly into a bf16
+//     row-major K tile (E4M3 codes unscaled, E2M1 x scale); each wave computes
+//     S^T = K q^T on bf16 MFMA (E4M3: one accumulator per 128-channel block times
+//     the row's fp32 scale) and keeps the split's scores in registers.  The exact
+//     per-head maximum and sum of exponentials follow, so no rescaling is ever
+//     needed and the fp32 output tile is only touched by the MFMA.
+//   * PV phase: the rows are read again (now from L2) into a channel-major V^T
+//     tile (fp16: E4M3 codes / E2M1 x scale are exact in fp16; bf16 for bf16
+//     rows), and O^T = V^T P^T accumulates on MFMA with fp16 P (E4M3: P times the
+//     row's scale over the split's largest scale of that block, <= 1) or bf16 P
+//     split into a high and a low part when V is bf16.
+//   The split's normalised output and logsumexp are written as a partial and
+//   k_merge combines the partials by logsumexp.
 // Generic path (any other shape): one workgroup per (b, h), fp32 on the vector
 // ALUs, writes the final output directly.
 #include <cstdlib>
@@ -35,48 +40,59 @@ namespace mla {
 namespace {
 
 constexpr int kChunk = 32;
-constexpr int kVt = 36;                  // halves per V^T channel row (32 rows + pad)
+constexpr int kMaxChunks = 4;             // rows per split <= 128
 constexpr int kDv = 512;
-constexpr int kMergeThreads = 256;
+constexpr int kVt = 36;                   // halves per V^T channel (32 rows + pad)
+constexpr int kVtGroupPad = 32;           // halves after every 32 channels: spreads LDS banks
+constexpr int kVtSize = kDv * kVt + (kDv / 32) * kVtGroupPad;
+constexpr int kMergeThreads = kDv / 4;
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxRows = 8192;
 
 enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2 };
 
-// Entries per split: fewer splits mean fewer fp32 partials to write and merge,
-// more splits mean more workgroups in flight.  MLA_DECODE_RPS (a multiple of
-// 32) overrides the default for tuning; the workspace query reads it too.
+__device__ __forceinline__ int vt_off(int c) { return c * kVt + (c >> 5) * kVtGroupPad; }
+
+// Entries per split (a multiple of 32, at most 128): fewer splits mean fewer
+// fp32 partials to write and merge, more splits more workgroups in flight.
+// MLA_DECODE_RPS overrides the default for tuning; the workspace query reads it too.
 int rows_per_split(int H, int k) {
-    (void)k;
     if (const char* e = getenv("MLA_DECODE_RPS")) {
         const int v = atoi(e);
-        if (v >= 32 && v % 32 == 0) return v;
+        if (v >= 32 && v <= 32 * kMaxChunks && v % 32 == 0) return v;
     }
-    return H >= 128 ? 256 : 128;
+    (void)H;
+    (void)k;
+    return 64;
 }
 
 template <int DQK>
 struct Lds {
-    static constexpr int kKs = DQK + 8;                 // bf16 per K / q row (padded)
-    uint16_t qs[64 * kKs];                              // q of the workgroup's (up to) 64 heads
-    uint16_t ks[kChunk * kKs];
-    uint16_t vt[kDv * kVt];
-    float rscale[kChunk][4];
+    static constexpr int kKs = DQK + 8;                  // bf16 per K / q row (padded)
+    static constexpr int kTile = (kChunk * kKs > kVtSize) ? kChunk * kKs : kVtSize;
+    uint16_t qs[64 * kKs];                               // queries of the workgroup's heads
+    uint16_t tile[kTile];                                // QK phase: K rows; PV phase: V^T
+    float fac[kChunk][4];                                // E4M3 row scales (QK) / scale over split max (PV)
     int32_t valid[kChunk];
-    uint32_t sref_bits[4];
+    uint32_t smax_bits[4];                               // E4M3: the split's largest row scale per block
+    float inv_smax[4];                                   // E4M3: 1 / smax (1 where the block has no row)
 };
 
-// Raw bytes of one gather item (32 channels of one row) held in registers
-// between its global load and its dequantising store into LDS.
-struct Slot {
+// Raw bytes of one QK-phase item (32 channels of one row).
+struct SlotA {
     u32x4 v[4];
-    uint32_t x;           // E4M3: the row's fp32 scale word; E2M1: the two scale bytes
+    uint32_t x;           // E4M3: the scale word of the segment's block; E2M1: two scale bytes
     int ok;
 };
+// Raw bytes of one PV-phase item (32 value channels of a pair of rows).
+struct SlotB {
+    u32x4 v[2][4];
+    uint32_t x[2];
+    int ok[2];
+};
 
-// Issue the global loads of segment `sg` (channels 32*sg .. +31) of a row.
-template <int SRC, int DQK>
-__device__ __forceinline__ void load_segment(Slot& sl, const uint8_t* __restrict__ row, int sg) {
+template <int SRC>
+__device__ __forceinline__ void load_a(SlotA& sl, const uint8_t* __restrict__ row, int sg) {
     if constexpr (SRC == SRC_BF16) {
         const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 64);
 #pragma unroll
@@ -98,72 +114,59 @@ __device__ __forceinline__ void load_segment(Slot& sl, const uint8_t* __restrict
     }
 }
 
-// Dequantise a loaded segment into LDS row r: K row-major in bf16 and, for the
-// value channels, V^T channel-major (fp16 for E4M3 / E2M1, bf16 for bf16 rows).
-template <int SRC, int DQK>
-__device__ __forceinline__ void store_segment(Lds<DQK>& L, const Slot& sl, int r, int sg) {
-    uint16_t* kdst = L.ks + r * Lds<DQK>::kKs + sg * 32;
-    const bool in_v = sg * 32 < kDv;
+template <int SRC>
+__device__ __forceinline__ void load_b(SlotB& sl, int h, const uint8_t* __restrict__ row, int sg) {
     if constexpr (SRC == SRC_BF16) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 64);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = sl.v[i];
-        if (in_v) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = sl.v[i][e];
-                    L.vt[(sg * 32 + 8 * i + 2 * e) * kVt + r] = (uint16_t)(w & 0xFFFFu);
-                    L.vt[(sg * 32 + 8 * i + 2 * e + 1) * kVt + r] = (uint16_t)(w >> 16);
-                }
-        }
+        for (int i = 0; i < 4; ++i) sl.v[h][i] = p[i];
     } else if constexpr (SRC == SRC_E4M3) {
-        if (sg < 16) {
-            const uint32_t w[8] = {sl.v[0].x, sl.v[0].y, sl.v[0].z, sl.v[0].w,
-                                   sl.v[1].x, sl.v[1].y, sl.v[1].z, sl.v[1].w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float f[4];
-                e4m3x4_to_f32(w[i], f);
-                reinterpret_cast<uint32_t*>(kdst)[2 * i] = pack_bf16_trunc(f[0], f[1]);
-                reinterpret_cast<uint32_t*>(kdst)[2 * i + 1] = pack_bf16_trunc(f[2], f[3]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    L.vt[(sg * 32 + 4 * i + e) * kVt + r] = __builtin_bit_cast(uint16_t, (_Float16)f[e]);
-            }
-            if ((sg & 3) == 0) L.rscale[r][sg >> 2] = u2f(sl.x);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = sl.v[i];
-        }
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 32);
+        sl.v[h][0] = p[0];
+        sl.v[h][1] = p[1];
+        sl.x[h] = reinterpret_cast<const uint32_t*>(row + 512)[sg >> 2];
     } else {
-        const float s0 = e4m3_to_f32(sl.x & 0xFFu), s1 = e4m3_to_f32((sl.x >> 8) & 0xFFu);
-        const uint32_t w[4] = {sl.v[0].x, sl.v[0].y, sl.v[0].z, sl.v[0].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float s = (i < 2) ? s0 : s1;
-            f32x2 v[4] = {e2m1x2_to_f32<0>(w[i]), e2m1x2_to_f32<1>(w[i]), e2m1x2_to_f32<2>(w[i]),
-                          e2m1x2_to_f32<3>(w[i])};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a = v[e].x * s, bb = v[e].y * s;
-                reinterpret_cast<uint32_t*>(kdst)[4 * i + e] = pack_bf16_trunc(a, bb);
-                L.vt[(sg * 32 + 8 * i + 2 * e) * kVt + r] = __builtin_bit_cast(uint16_t, (_Float16)a);
-                L.vt[(sg * 32 + 8 * i + 2 * e + 1) * kVt + r] = __builtin_bit_cast(uint16_t, (_Float16)bb);
-            }
-        }
+        sl.v[h][0] = *reinterpret_cast<const u32x4*>(row + sg * 16);
+        sl.x[h] = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * sg);
     }
 }
 
-template <int DQK>
-__device__ __forceinline__ void zero_segment(Lds<DQK>& L, int r, int sg) {
-    uint16_t* kdst = L.ks + r * Lds<DQK>::kKs + sg * 32;
+// 32 values of segment sg of a PV-phase item row: fp16 (E4M3 / E2M1, exact) or bf16 bits.
+template <int SRC>
+__device__ __forceinline__ void value_bits(const SlotB& sl, int h, uint16_t out[32]) {
+    if constexpr (SRC == SRC_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4*>(kdst)[i] = u32x4{0u, 0u, 0u, 0u};
-    if (sg * 32 < kDv)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 32; ++e) L.vt[(sg * 32 + e) * kVt + r] = 0;
-    if (sg < 4) L.rscale[r][sg] = 0.0f;      // invalid rows carry zero scales (never NaN)
+            for (int e = 0; e < 4; ++e) {
+                out[8 * i + 2 * e] = (uint16_t)(sl.v[h][i][e] & 0xFFFFu);
+                out[8 * i + 2 * e + 1] = (uint16_t)(sl.v[h][i][e] >> 16);
+            }
+    } else if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t w = sl.v[h][i >> 2][i & 3];
+            const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+            out[4 * i] = (uint16_t)(lo & 0xFFFFu);
+            out[4 * i + 1] = (uint16_t)(lo >> 16);
+            out[4 * i + 2] = (uint16_t)(hi & 0xFFFFu);
+            out[4 * i + 3] = (uint16_t)(hi >> 16);
+        }
+    } else {
+        const float s0 = e4m3_to_f32(sl.x[h] & 0xFFu), s1 = e4m3_to_f32((sl.x[h] >> 8) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sc = (i < 2) ? s0 : s1;
+            const uint32_t w = sl.v[h][0][i];
+            const f32x2 v[4] = {e2m1x2_to_f32<0>(w), e2m1x2_to_f32<1>(w), e2m1x2_to_f32<2>(w), e2m1x2_to_f32<3>(w)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                out[8 * i + 2 * e] = __builtin_bit_cast(uint16_t, (_Float16)(v[e].x * sc));
+                out[8 * i + 2 * e + 1] = __builtin_bit_cast(uint16_t, (_Float16)(v[e].y * sc));
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
@@ -171,21 +174,27 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// Process one split with source kind SRC.  Returns after writing the partial.
+// One split: QK phase, exact softmax statistics, PV phase, partial.
 template <int SRC, int DQK, int NHT>
 __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, int b, int split, int S,
                                              bool is_win, int64_t first, int n_rows, float* o_part,
                                              float* lse_part) {
-    constexpr int NT = DQK / 32;          // k-steps of QK
-    constexpr int NSEG = DQK / 32;        // 32-channel segments of a row
+    constexpr int NT = DQK / 32;           // k-steps of QK = 32-channel segments of a K row
+    constexpr int NTH = 256;               // every wave loads; waves w < NHT also contract
+    constexpr int NITEM_A = kChunk * NT;
+    constexpr int NSLOT_A = (NITEM_A + NTH - 1) / NTH;
+    constexpr int NITEM_B = (kChunk / 2) * (kDv / 32);   // (row pair, value segment)
+    constexpr int NSLOT_B = (NITEM_B + NTH - 1) / NTH;
+    constexpr int KS = Lds<DQK>::kKs;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
+    const bool mw = w < NHT;
     const int head = 16 * (NHT * (int)blockIdx.z + w) + j;
     constexpr float kLog2e = 1.4426950408889634f;
     const float zscale = a.scale * kLog2e;
+    const int nc = (n_rows + kChunk - 1) / kChunk;
 
-    // source row of split entry u (nullptr if invalid)
     auto row_ptr = [&](int u) -> const uint8_t* {
         if (u >= n_rows) return nullptr;
         if (is_win) return reinterpret_cast<const uint8_t*>(a.win + ((int64_t)b * a.W + first + u) * DQK);
@@ -193,91 +202,157 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
         if (s < 0 || s >= a.capacity) return nullptr;
         return a.cache + b * a.stride + (int64_t)s * a.row_bytes;
     };
-
-    // gather items of a chunk: (segment, row), segment-major; each thread owns NSLOT of them
-    constexpr int NTH = NHT * 64;
-    constexpr int NITEMS = kChunk * NSEG;
-    constexpr int NSLOT = (NITEMS + NTH - 1) / NTH;
-    auto load_chunk = [&](int c0, Slot* sl) {
+    auto load_chunk_a = [&](int c0, SlotA* sl) {
 #pragma unroll
-        for (int i = 0; i < NSLOT; ++i) {
+        for (int i = 0; i < NSLOT_A; ++i) {
             const int item = tid + i * NTH;
             sl[i].ok = 0;
-            if (item < NITEMS) {
+            if (item < NITEM_A) {
                 const uint8_t* rp = row_ptr(c0 + item % kChunk);
                 if (rp) {
                     sl[i].ok = 1;
-                    load_segment<SRC, DQK>(sl[i], rp, item / kChunk);
+                    load_a<SRC>(sl[i], rp, item / kChunk);
                 }
             }
         }
     };
-    auto store_chunk = [&](const Slot* sl) {
+    auto load_chunk_b = [&](int c0, SlotB* sl) {
 #pragma unroll
-        for (int i = 0; i < NSLOT; ++i) {
+        for (int i = 0; i < NSLOT_B; ++i) {
             const int item = tid + i * NTH;
-            if (item < NITEMS) {
-                const int sg = item / kChunk, r = item % kChunk;
-                if (sl[i].ok) store_segment<SRC, DQK>(L, sl[i], r, sg);
-                else zero_segment<DQK>(L, r, sg);
-                if (sg == 0) L.valid[r] = sl[i].ok;
+            sl[i].ok[0] = sl[i].ok[1] = 0;
+            if (item < NITEM_B) {
+                const int rp = item % (kChunk / 2), sg = item / (kChunk / 2);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint8_t* p = row_ptr(c0 + 2 * rp + h);
+                    if (p) {
+                        sl[i].ok[h] = 1;
+                        load_b<SRC>(sl[i], h, p, sg);
+                    }
+                }
             }
         }
     };
-    Slot sl[NSLOT];
-    if (n_rows > 0) load_chunk(0, sl);
-
-    // q of the workgroup's heads into LDS (16-byte pieces); lane (j, g) later reads
-    // k-slots (g, e) of k-step t = channel t*32 + g*8 + e of head j of its tile
-    {
-        const int head0 = 16 * NHT * (int)blockIdx.z;
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head0) * DQK;
-        for (int i = tid; i < 16 * NHT * (DQK / 8); i += NHT * 64) {
-            const int hh = i / (DQK / 8), c8 = i % (DQK / 8);
-            *reinterpret_cast<u32x4*>(L.qs + hh * Lds<DQK>::kKs + c8 * 8) =
-                *reinterpret_cast<const u32x4*>(qp + (int64_t)hh * DQK + c8 * 8);
+    auto store_chunk_a = [&](const SlotA* sl) {
+#pragma unroll
+        for (int i = 0; i < NSLOT_A; ++i) {
+            const int item = tid + i * NTH;
+            if (item >= NITEM_A) continue;
+            const int sg = item / kChunk, r = item % kChunk;
+            uint32_t* kd = reinterpret_cast<uint32_t*>(L.tile + r * KS + sg * 32);
+            if (!sl[i].ok) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(kd)[q] = u32x4{0u, 0u, 0u, 0u};
+                if (SRC == SRC_E4M3 && sg < 4) L.fac[r][sg] = 0.0f;
+            } else if constexpr (SRC == SRC_BF16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(kd)[q] = sl[i].v[q];
+            } else if constexpr (SRC == SRC_E4M3) {
+                if (sg < 16) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const u32x2 p0 = e4m3x4_to_bf16(sl[i].v[q].x), p1 = e4m3x4_to_bf16(sl[i].v[q].y);
+                        const u32x2 p2 = e4m3x4_to_bf16(sl[i].v[q].z), p3 = e4m3x4_to_bf16(sl[i].v[q].w);
+                        reinterpret_cast<u32x4*>(kd)[2 * q] = u32x4{p0.x, p0.y, p1.x, p1.y};
+                        reinterpret_cast<u32x4*>(kd)[2 * q + 1] = u32x4{p2.x, p2.y, p3.x, p3.y};
+                    }
+                    if ((sg & 3) == 0) {
+                        L.fac[r][sg >> 2] = u2f(sl[i].x);
+                        atomicMax(&L.smax_bits[sg >> 2], sl[i].x);     // positive fp32 orders as uint
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(kd)[q] = sl[i].v[q];
+                }
+            } else {  // E2M1 x E4M3 scale, exact in bf16
+                const float s0 = e4m3_to_f32(sl[i].x & 0xFFu), s1 = e4m3_to_f32((sl[i].x >> 8) & 0xFFu);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float sc = (q < 2) ? s0 : s1;
+                    const uint32_t wv = sl[i].v[0][q];
+                    const f32x2 v0 = e2m1x2_to_f32<0>(wv), v1 = e2m1x2_to_f32<1>(wv);
+                    const f32x2 v2 = e2m1x2_to_f32<2>(wv), v3 = e2m1x2_to_f32<3>(wv);
+                    reinterpret_cast<u32x4*>(kd)[q] =
+                        u32x4{pack_bf16_trunc(v0.x * sc, v0.y * sc), pack_bf16_trunc(v1.x * sc, v1.y * sc),
+                              pack_bf16_trunc(v2.x * sc, v2.y * sc), pack_bf16_trunc(v3.x * sc, v3.y * sc)};
+                }
+            }
+            if (sg == 0) L.valid[r] = sl[i].ok;
         }
-    }
-    const uint16_t* qrow = L.qs + (16 * w + j) * Lds<DQK>::kKs + g * 8;
-
-    float inv_sref[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (SRC == SRC_E4M3) {
-        if (tid < 4) L.sref_bits[tid] = 0u;
-        __syncthreads();
-        for (int u = tid; u < n_rows; u += NHT * 64) {
-            const uint8_t* rp = row_ptr(u);
-            if (rp) {
-                const float4 sc = *reinterpret_cast<const float4*>(rp + 512);
-                atomicMax(&L.sref_bits[0], f2u(sc.x));
-                atomicMax(&L.sref_bits[1], f2u(sc.y));
-                atomicMax(&L.sref_bits[2], f2u(sc.z));
-                atomicMax(&L.sref_bits[3], f2u(sc.w));
+    };
+    auto store_chunk_b = [&](const SlotB* sl) {
+#pragma unroll
+        for (int i = 0; i < NSLOT_B; ++i) {
+            const int item = tid + i * NTH;
+            if (item >= NITEM_B) continue;
+            const int rp = item % (kChunk / 2), sg = item / (kChunk / 2);
+            uint16_t v0[32], v1[32];
+            if (sl[i].ok[0]) value_bits<SRC>(sl[i], 0, v0);
+            else {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) v0[e] = 0;
+            }
+            if (sl[i].ok[1]) value_bits<SRC>(sl[i], 1, v1);
+            else {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) v1[e] = 0;
+            }
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+                *reinterpret_cast<uint32_t*>(L.tile + vt_off(sg * 32 + e) + 2 * rp) =
+                    (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
+            if (SRC == SRC_E4M3 && (sg & 3) == 0) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    L.fac[2 * rp + h][sg >> 2] = sl[i].ok[h] ? u2f(sl[i].x[h]) * L.inv_smax[sg >> 2] : 0.0f;
             }
         }
-        __syncthreads();
+    };
+
+    // ---- start the first chunk's loads, then stage the queries
+    SlotA sa[NSLOT_A];
+    SlotB sb[NSLOT_B];
+    if (nc > 0) load_chunk_a(0, sa);
+    {
+        constexpr int NQ = 16 * NHT * (DQK / 8);           // 16-byte pieces of the queries
+        constexpr int NQT = (NQ + NTH - 1) / NTH;
+        const int head0 = 16 * NHT * (int)blockIdx.z;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head0) * DQK;
+        u32x4 qv[NQT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float s = u2f(L.sref_bits[i]);
-            inv_sref[i] = (s > 0.0f) ? 1.0f / s : 1.0f;
+        for (int i = 0; i < NQT; ++i) {
+            const int e = tid + i * NTH;
+            if (e < NQ) qv[i] = *reinterpret_cast<const u32x4*>(qp + (int64_t)(e / (DQK / 8)) * DQK + (e % (DQK / 8)) * 8);
         }
-    }
-
-    f32x4 oacc[kDv / 16];
 #pragma unroll
-    for (int i = 0; i < kDv / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -__builtin_inff(), l_run = 0.0f;
+        for (int i = 0; i < NQT; ++i) {
+            const int e = tid + i * NTH;
+            if (e < NQ) *reinterpret_cast<u32x4*>(L.qs + (e / (DQK / 8)) * KS + (e % (DQK / 8)) * 8) = qv[i];
+        }
+        if (tid < 4) L.smax_bits[tid] = 0u;
+    }
+    const uint16_t* qrow = L.qs + (16 * w + j) * KS + g * 8;
 
-    for (int c0 = 0; c0 < n_rows; c0 += kChunk) {
-        store_chunk(sl);
+    // ---- QK phase: scores of all chunks into registers (base 2, scaled)
+    float z[kMaxChunks][2][4];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[c][rt][r] = -__builtin_inff();
+        if (c >= nc) continue;
+        __syncthreads();                                   // previous tile fully consumed (and q staged)
+        store_chunk_a(sa);
         __syncthreads();
-        if (c0 + kChunk < n_rows) load_chunk(c0 + kChunk, sl);   // in flight during the MFMAs
-
-        // ---- S^T = K q^T for the chunk's two 16-row tiles
-        float z[2][4];
+        if (c + 1 < nc) load_chunk_a((c + 1) * kChunk, sa);
+        else load_chunk_b(0, sb);                          // PV phase's first chunk, in flight now
+        if (!mw) continue;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            const uint16_t* ka = L.ks + (16 * rt + j) * Lds<DQK>::kKs + g * 8;
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint16_t* ka = L.tile + (16 * rt + j) * KS + g * 8;
+            f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (SRC == SRC_E4M3) {
 #pragma unroll
                 for (int b4 = 0; b4 < 4; ++b4) {
@@ -287,56 +362,76 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
                         t4 = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
                                        *reinterpret_cast<const u32x4*>(qrow + t * 32), t4);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) s[r] += t4[r] * L.rscale[16 * rt + 4 * g + r][b4];
+                    for (int r = 0; r < 4; ++r) sacc[r] += t4[r] * L.fac[16 * rt + 4 * g + r][b4];
                 }
 #pragma unroll
                 for (int t = 16; t < NT; ++t)
-                    s = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
-                                  *reinterpret_cast<const u32x4*>(qrow + t * 32), s);
+                    sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
+                                     *reinterpret_cast<const u32x4*>(qrow + t * 32), sacc);
             } else {
 #pragma unroll
                 for (int t = 0; t < NT; ++t)
-                    s = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
-                                  *reinterpret_cast<const u32x4*>(qrow + t * 32), s);
+                    sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
+                                     *reinterpret_cast<const u32x4*>(qrow + t * 32), sacc);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                z[rt][r] = L.valid[16 * rt + 4 * g + r] ? s[r] * zscale : -__builtin_inff();
+                if (L.valid[16 * rt + 4 * g + r]) z[c][rt][r] = sacc[r] * zscale;
         }
+    }
 
-        // ---- online softmax (base 2), per head j; lanes j, j+16, j+32, j+48 share a head.
-        // The reference m_ref moves only when a chunk's max exceeds it by more than 8
-        // (p <= 2^8 keeps fp16 P finite), so the output tile is rarely rescaled.
-        float zmax = -__builtin_inff();
+    // ---- exact softmax statistics of the split, per head (lanes j, j+16, j+32, j+48)
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) zmax = fmaxf(zmax, z[rt][r]);
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 16, 64));
-        zmax = fmaxf(zmax, __shfl_xor(zmax, 32, 64));
-        const bool move = zmax > m_run + 8.0f;
-        if (__ballot(move)) {
-            const float m_new = move ? zmax : m_run;
-            const float alpha = (m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, z[c][rt][r]);
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.0f;
+    if (m != -__builtin_inff()) {
 #pragma unroll
-            for (int i = 0; i < kDv / 16; ++i) oacc[i] *= alpha;
-            m_run = m_new;
+        for (int c = 0; c < kMaxChunks; ++c)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    z[c][rt][r] = __builtin_amdgcn_exp2f(z[c][rt][r] - m);     // exp2(-inf) = 0
+                    l += z[c][rt][r];
+                }
+    } else {                                               // no visible entry: P = 0, never -inf
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) z[c][rt][r] = 0.0f;
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if constexpr (SRC == SRC_E4M3) {
+        __syncthreads();                                   // every row's scale is in smax_bits
+        if (tid < 4) {                                     // read by the PV stores after their barrier
+            const float sm = u2f(L.smax_bits[tid]);
+            L.inv_smax[tid] = (sm > 0.0f) ? 1.0f / sm : 1.0f;
         }
-        float p[2][4];
-        float psum = 0.0f;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[rt][r] = (z[rt][r] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[rt][r] - m_run);
-                psum += p[rt][r];
-            }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run += psum;
+    }
 
-        // ---- O^T += V^T P^T.  k-slot (g, e): e < 4 -> row 4g+e, e >= 4 -> row 16+4g+e-4
+    // ---- PV phase: O^T += V^T P^T; k-slot (g, e): e < 4 -> row 4g+e, e >= 4 -> row 16+4g+e-4
+    f32x4 oacc[kDv / 16];
+#pragma unroll
+    for (int i = 0; i < kDv / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        if (c >= nc) continue;
+        __syncthreads();
+        store_chunk_b(sb);
+        __syncthreads();
+        if (c + 1 < nc) load_chunk_b((c + 1) * kChunk, sb);
+        if (!mw) continue;
+        const float (*p)[4] = z[c];
         if constexpr (SRC == SRC_BF16) {
             float hi[8], lo[8];
 #pragma unroll
@@ -351,10 +446,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
                                    bf16_rne(lo[4]) | (bf16_rne(lo[5]) << 16), bf16_rne(lo[6]) | (bf16_rne(lo[7]) << 16)};
 #pragma unroll
             for (int mt = 0; mt < kDv / 16; ++mt) {
-                const uint16_t* va = L.vt + (16 * mt + j) * kVt;
-                const u32x2 v0 = *reinterpret_cast<const u32x2*>(va + 4 * g);
-                const u32x2 v1 = *reinterpret_cast<const u32x2*>(va + 16 + 4 * g);
-                const u32x4 av = u32x4{v0.x, v0.y, v1.x, v1.y};
+                const uint16_t* va = L.tile + vt_off(16 * mt + j);
+                const u32x2 x0 = *reinterpret_cast<const u32x2*>(va + 4 * g);
+                const u32x2 x1 = *reinterpret_cast<const u32x2*>(va + 16 + 4 * g);
+                const u32x4 av = u32x4{x0.x, x0.y, x1.x, x1.y};
                 oacc[mt] = mfma_bf16(av, ph, oacc[mt]);
                 oacc[mt] = mfma_bf16(av, pl, oacc[mt]);
             }
@@ -367,7 +462,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int row = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
-                        q8[e] = p[e >> 2][e & 3] * (L.rscale[row][b4] * inv_sref[b4]);
+                        q8[e] = p[e >> 2][e & 3] * L.fac[row][b4];
                     }
                     pv[b4] = u32x4{pack_f16_rne(q8[0], q8[1]), pack_f16_rne(q8[2], q8[3]),
                                    pack_f16_rne(q8[4], q8[5]), pack_f16_rne(q8[6], q8[7])};
@@ -378,33 +473,32 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, i
             }
 #pragma unroll
             for (int mt = 0; mt < kDv / 16; ++mt) {
-                const uint16_t* va = L.vt + (16 * mt + j) * kVt;
-                const u32x2 v0 = *reinterpret_cast<const u32x2*>(va + 4 * g);
-                const u32x2 v1 = *reinterpret_cast<const u32x2*>(va + 16 + 4 * g);
-                const u32x4 av = u32x4{v0.x, v0.y, v1.x, v1.y};
+                const uint16_t* va = L.tile + vt_off(16 * mt + j);
+                const u32x2 x0 = *reinterpret_cast<const u32x2*>(va + 4 * g);
+                const u32x2 x1 = *reinterpret_cast<const u32x2*>(va + 16 + 4 * g);
+                const u32x4 av = u32x4{x0.x, x0.y, x1.x, x1.y};
                 oacc[mt] = mfma_f16(av, pv[(SRC == SRC_E4M3) ? (mt >> 3) : 0], oacc[mt]);
             }
         }
-        __syncthreads();
     }
 
     // ---- partial: normalised output and logsumexp (natural log) of the split
+    if (!mw) return;
     const int64_t prow = ((int64_t)b * S + split) * a.H + head;
-    const float inv_l = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    const float inv_l = (l > 0.0f) ? 1.0f / l : 0.0f;
 #pragma unroll
     for (int mt = 0; mt < kDv / 16; ++mt) {
         float f = inv_l;
-        if constexpr (SRC == SRC_E4M3) f *= u2f(L.sref_bits[mt >> 3]);
-        float4 v = make_float4(oacc[mt][0] * f, oacc[mt][1] * f, oacc[mt][2] * f, oacc[mt][3] * f);
-        *reinterpret_cast<float4*>(o_part + prow * kDv + 16 * mt + 4 * g) = v;
+        if constexpr (SRC == SRC_E4M3) f *= u2f(L.smax_bits[mt >> 3]);
+        *reinterpret_cast<float4*>(o_part + prow * kDv + 16 * mt + 4 * g) =
+            make_float4(oacc[mt][0] * f, oacc[mt][1] * f, oacc[mt][2] * f, oacc[mt][3] * f);
     }
     if (g == 0)
-        lse_part[prow] = (l_run > 0.0f) ? (m_run + __builtin_amdgcn_logf(l_run)) * 0.6931471805599453f
-                                        : -__builtin_inff();
+        lse_part[prow] = (l > 0.0f) ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
 }
 
 template <int SRC_MAIN, int DQK, int NHT>
-__global__ __launch_bounds__(NHT * 64) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps,
+__global__ __launch_bounds__(256) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps,
                                                           float* o_part, float* lse_part) {
     __shared__ Lds<DQK> L;
     const int b = blockIdx.y;
@@ -423,33 +517,38 @@ __global__ __launch_bounds__(NHT * 64) void k_decode_mfma(DecodeArgs a, int S_ma
     }
 }
 
+// Combine the splits of one (b, h) by their logsumexp; thread t owns channels 4t .. 4t+3.
 __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part, float* __restrict__ out,
                                                          float* __restrict__ lse) {
-    extern __shared__ float wts[];
     const int h = blockIdx.x, b = blockIdx.y;
+    const int t = threadIdx.x;
+    const float* lp = lse_part + (int64_t)b * S * H + h;
     float m = -__builtin_inff();
-    for (int s = 0; s < S; ++s) m = fmaxf(m, lse_part[((int64_t)b * S + s) * H + h]);
-    float* o = out + ((int64_t)b * H + h) * kDv;
+    for (int s = 0; s < S; ++s) m = fmaxf(m, lp[(int64_t)s * H]);
+    float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * kDv) + t;
     if (m == -__builtin_inff()) {
-        for (int c = threadIdx.x; c < kDv; c += kMergeThreads) o[c] = 0.0f;
-        if (threadIdx.x == 0) lse[(int64_t)b * H + h] = -__builtin_inff();
+        *o = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t == 0) lse[(int64_t)b * H + h] = -__builtin_inff();
         return;
     }
+    const float4* op = reinterpret_cast<const float4*>(o_part + ((int64_t)b * S * H + h) * kDv) + t;
+    const int64_t step = (int64_t)H * (kDv / 4);
     float tot = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
-        const float wv = __expf(lse_part[((int64_t)b * S + s) * H + h] - m);
-        if (threadIdx.x == 0) wts[s] = wv;
+        const float wv = __expf(lp[(int64_t)s * H] - m);
+        const float4 v = op[s * step];
         tot += wv;
+        acc.x += wv * v.x;
+        acc.y += wv * v.y;
+        acc.z += wv * v.z;
+        acc.w += wv * v.w;
     }
-    __syncthreads();
     const float inv = 1.0f / tot;
-    for (int c = threadIdx.x; c < kDv; c += kMergeThreads) {
-        float acc = 0.0f;
-        for (int s = 0; s < S; ++s) acc += wts[s] * o_part[(((int64_t)b * S + s) * H + h) * kDv + c];
-        o[c] = acc * inv;
-    }
-    if (threadIdx.x == 0) lse[(int64_t)b * H + h] = m + __logf(tot);
+    *o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (t == 0) lse[(int64_t)b * H + h] = m + __logf(tot);
 }
 
 // ------------------------------------------------------------------------
@@ -598,7 +697,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         const dim3 grid(S, a.B, a.H / (16 * NHT));
 #define MLA_DEC_CASE(SRC, DQK, N)                                                                      \
     if (NHT == N) {                                                                                    \
-        hipLaunchKernelGGL((k_decode_mfma<SRC, DQK, N>), grid, dim3(N * 64), 0, stream, a, S_main,     \
+        hipLaunchKernelGGL((k_decode_mfma<SRC, DQK, N>), grid, dim3(256), 0, stream, a, S_main,     \
                            S - S_main, rps, o_part, lse_part);                                         \
     }
 #define MLA_DEC_ALL_N(SRC, DQK) \
@@ -612,7 +711,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), S * sizeof(float), stream, S, a.H,
+    hipLaunchKernelGGL(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, S, a.H,
                        o_part, lse_part, a.out, a.lse);
     return hipGetLastError();
 }

@@ -186,9 +186,10 @@ __global__ __launch_bounds__(kFinalThreads) void k_select_final(const int32_t* _
     uint64_t prefix = radix ? (c[0] & kBinBits) : 0ull, mask = kBinBits;
     uint32_t rem = need;
     if (radix) {
-        constexpr int kShifts[7] = {44, 36, 28, 20, 12, 4, 0};
+        // digit windows 44..51, 36..43, .., 4..11, then 0..7 (bits 4..7 already fixed);
+        // computed, not tabled: a constant table would be read from the code object
         for (int p = 0; p < 7; ++p) {
-            const int shift = kShifts[p];
+            const int shift = (p < 6) ? 44 - 8 * p : 0;
             if (t < 256) h256[t] = 0u;
             __syncthreads();
             for (uint32_t i = t; i < ncand; i += kFinalThreads) {

@@ -1,6 +1,6 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
-Bars (written here, from the benchmark spec of the path):
+Bars (the tolerances the path is specified to):
   * quantise-append and causal masking: bit-exact;
   * indexer scores: |I_gpu - I_ref| <= 1e-4 * max(|I_ref|, rms of the row);
   * top-k sets: exact, except positions whose oracle score lies within
@@ -8,6 +8,7 @@ Bars (written here, from the benchmark spec of the path):
   * attention given identical dequantised rows and index sets: per (b, h),
     max |o - o_ref| <= 2e-3 * max |o_ref| and |lse - lse_ref| <= 2e-3 * max(1, |lse_ref|).
 """
+import dataclasses
 import functools
 import sys
 
@@ -167,6 +168,23 @@ def test_decode_edge_cases(name):
         ref_o, ref_l = G.oracle_attention(case, 0, empty)
         got_o, got_l = G.gpu_decode(case, 0, empty)
         G.check_attention(got_o, got_l, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("name,H", [("c2s", 16), ("c3s", 32), ("c3s", 16), ("c4s", 32), ("c5s", 16)])
+def test_decode_head_counts(name, H):
+    """Fewer than 64 heads: only one or two of a workgroup's waves contract while
+    all of them gather; the first H heads of the configuration's queries."""
+    case = case_of(name)
+    sub = dataclasses.replace(case, cfg=case.cfg.with_(H=H),
+                              inp=dataclasses.replace(case.inp, q=np.ascontiguousarray(case.inp.q[:, :, :H])))
+    rng = np.random.default_rng(H)
+    B, N, k = sub.cfg.B, sub.cfg.N, sub.cfg.k
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(B)]).astype(np.int32)
+    idx[:, -5:] = -1
+    say("decode heads", name, H)
+    ref_o, ref_l = G.oracle_attention(sub, 0, idx)
+    got_o, got_l = G.gpu_decode(sub, 0, idx)
+    G.check_attention(got_o, got_l, ref_o, ref_l)
 
 
 def test_quantise_bitexact_over_magnitudes():

@@ -25,9 +25,14 @@ FLAGS = [
 ]
 
 
+# Per-source extras. decode.hip: MFMA results in ordinary VGPRs, so the output
+# tile is never copied between accumulation and vector registers in the chunk loop.
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, verbose):
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -6,26 +6,28 @@
 // ([P1] "DeepSeek's Attention and KV Cache - From MLA to CSA2", "DeepSeek-V2",
 // "Why RoPE breaks the trick" and "Check it in numpy"; [P2] "From MLA to DSA
 // to HCA/CSA", Part 2 "What replaced MLA"; each selected latent is read once
-// for all heads, [P1] "DeepSeek-V3.2", "The lightning indexer").
+// per head group, [P1] "DeepSeek-V3.2", "The lightning indexer").
 //
 // MFMA path (H a multiple of 16 up to 128, d_v = 512, K width 576 = 512 + 64 or 512):
-//   grid (splits, B, head groups); a split is `rps` <= 128 consecutive entries of
-//   idx[b] (or of the window ring); workgroup = 4 waves that all gather, and the
-//   first NHT = min(4, H / 16) of them also contract: wave w owns heads
-//   16 * (NHT * blockIdx.z + w) .. +15, whose queries sit in LDS.
-//   Two phases over the split's 32-row chunks, the next chunk's row bytes always
-//   loaded into registers while the current one is contracted:
-//   * QK phase: the workgroup dequantises each chunk's rows exactly into a bf16
-//     row-major K tile (E4M3 codes unscaled, E2M1 x scale); each wave computes
-//     S^T = K q^T on bf16 MFMA (E4M3: one accumulator per 128-channel block times
-//     the row's fp32 scale) and keeps the split's scores in registers.  The exact
-//     per-head maximum and sum of exponentials follow, so no rescaling is ever
-//     needed and the fp32 output tile is only touched by the MFMA.
-//   * PV phase: the rows are read again (now from L2) into a channel-major V^T
-//     tile (fp16: E4M3 codes / E2M1 x scale are exact in fp16; bf16 for bf16
-//     rows), and O^T = V^T P^T accumulates on MFMA with fp16 P (E4M3: P times the
-//     row's scale over the split's largest scale of that block, <= 1) or bf16 P
-//     split into a high and a low part when V is bf16.
+//   one workgroup (4 waves) per (b, split, group of 16 * HT heads); a split is
+//   `rps` <= 256 consecutive entries of idx[b] (or of the window ring). Work items
+//   are laid out so that the head groups of one split run on the same XCD and
+//   share its L2. The split's rows stream through LDS in 32-row chunks:
+//   * E4M3 and bf16 rows are gathered straight from HBM into LDS
+//     (global_load_lds_dwordx4, two or three chunks in flight); E2M1 rows pass
+//     through registers and are staged dequantised to bf16 (exact).
+//   * QK: wave w takes rows 16 (w & 1) .. +15 of the chunk and either half of the
+//     K width (HT = 1) or head tile w >> 1 (HT = 2); K comes from the staged rows
+//     (E4M3 codes widened exactly to bf16, one accumulator per 128-channel block
+//     times the row's fp32 scale), queries sit in registers, bf16 MFMA.
+//   * Scores meet in LDS; every wave runs the same online softmax on them.
+//   * PV: wave w owns value channels 128 w .. +127 for all heads of the
+//     workgroup, so its fp32 output tile is 32 registers per head tile. V^T
+//     operands come from the staged rows through the transposing LDS reads
+//     (ds_read_b64_tr_b8 for E4M3 codes, ds_read_b64_tr_b16 for bf16). E4M3:
+//     fp16 MFMA with P times the row's block scale over the largest block scale
+//     seen so far (<= 1, rescaled when it grows); bf16: bf16 MFMA with P split
+//     into a high and a low part.
 //   The split's normalised output and logsumexp are written as a partial and
 //   k_merge combines the partials by logsumexp.
 // Generic path (any other shape): one workgroup per (b, h), fp32 on the vector
@@ -39,133 +41,109 @@ namespace mla {
 
 namespace {
 
-constexpr int kChunk = 32;
-constexpr int kMaxChunks = 4;             // rows per split <= 128
+#ifndef MLA_E4M3_BUFS
+#define MLA_E4M3_BUFS 3                    // E4M3 chunk buffers in LDS (2 or 3)
+#endif
+constexpr int kChunk = 32;                 // rows per pipeline step
 constexpr int kDv = 512;
-constexpr int kVt = 36;                   // halves per V^T channel (32 rows + pad)
-constexpr int kVtGroupPad = 32;           // halves after every 32 channels: spreads LDS banks
-constexpr int kVtSize = kDv * kVt + (kDv / 32) * kVtGroupPad;
+constexpr int kThreads = 256;
+constexpr int kMaxRps = 256;               // rows per split: one row index per thread
+constexpr int kZs = 36;                    // floats per (head) score row in LDS: 32 rows + pad
 constexpr int kMergeThreads = kDv / 4;
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxRows = 8192;
 
 enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2 };
 
-__device__ __forceinline__ int vt_off(int c) { return c * kVt + (c >> 5) * kVtGroupPad; }
-
-// Entries per split (a multiple of 32, at most 128): fewer splits mean fewer
-// fp32 partials to write and merge, more splits more workgroups in flight.
-// MLA_DECODE_RPS overrides the default for tuning; the workspace query reads it too.
-int rows_per_split(int H, int k) {
-    if (const char* e = getenv("MLA_DECODE_RPS")) {
-        const int v = atoi(e);
-        if (v >= 32 && v <= 32 * kMaxChunks && v % 32 == 0) return v;
-    }
-    (void)H;
-    (void)k;
-    return 64;
-}
-
-template <int DQK>
-struct Lds {
-    static constexpr int kKs = DQK + 8;                  // bf16 per K / q row (padded)
-    static constexpr int kTile = (kChunk * kKs > kVtSize) ? kChunk * kKs : kVtSize;
-    uint16_t qs[64 * kKs];                               // queries of the workgroup's heads
-    uint16_t tile[kTile];                                // QK phase: K rows; PV phase: V^T
-    float fac[kChunk][4];                                // E4M3 row scales (QK) / scale over split max (PV)
-    int32_t valid[kChunk];
-    uint32_t smax_bits[4];                               // E4M3: the split's largest row scale per block
-    float inv_smax[4];                                   // E4M3: 1 / smax (1 where the block has no row)
+// Geometry of one staged 32-row chunk. E4M3 rows are staged as stored
+// (512 codes | 4 fp32 scales | 64 bf16 RoPE = 656 B), bf16 rows as stored and
+// E2M1 rows dequantised to bf16; bf16 rows get 32 bytes of padding so that
+// consecutive rows start 8 LDS banks apart.
+template <int SRC, int DQK>
+struct Stage {
+    static constexpr int kRowBytes = SRC == SRC_E4M3 ? 656 : (SRC == SRC_FP4 ? 288 : 2 * DQK);
+    static constexpr int kStride = SRC == SRC_E4M3 ? 656 : 2 * (SRC == SRC_FP4 ? 512 : DQK) + 32;
+    static constexpr bool kDirect = SRC != SRC_FP4;
+    static constexpr int kPieces = kStride / 16;                  // 16-byte slots per staged row
+    static constexpr int kDataPieces = kRowBytes / 16;            // of which hold row bytes (direct)
+    static constexpr int kInstr = (kChunk * kPieces + 63) / 64;   // direct loads per chunk, 64 slots each
+    static constexpr int kHi = (kInstr + 3) / 4;                  // per-wave load count, waves w < kInstr % 4
+    static constexpr int kLo = kInstr / 4;                        // the other waves
+    static constexpr int kBytes = kDirect ? kInstr * 1024 : kChunk * kStride;
+    static constexpr int kBufs = SRC == SRC_E4M3 ? MLA_E4M3_BUFS : 2;  // chunk buffers
+    static constexpr int kLds = kBufs * kBytes;
 };
 
-// Raw bytes of one QK-phase item (32 channels of one row).
-struct SlotA {
-    u32x4 v[4];
-    uint32_t x;           // E4M3: the scale word of the segment's block; E2M1: two scale bytes
-    int ok;
-};
-// Raw bytes of one PV-phase item (32 value channels of a pair of rows).
-struct SlotB {
-    u32x4 v[2][4];
-    uint32_t x[2];
-    int ok[2];
-};
+// Dynamic LDS: row indices of the split | scores [2 parities][KH][16 HT heads][kZs] | chunk buffers.
+constexpr int kLdsIdx = 0;
+constexpr int kLdsZ = kMaxRps * 4;
+constexpr int kLdsZBytes = 2 * 2 * 16 * kZs * 4;            // KH * HT == 2 in both layouts
+constexpr int kLdsBuf = kLdsZ + kLdsZBytes;
 
-template <int SRC>
-__device__ __forceinline__ void load_a(SlotA& sl, const uint8_t* __restrict__ row, int sg) {
-    if constexpr (SRC == SRC_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sl.v[i] = p[i];
-    } else if constexpr (SRC == SRC_E4M3) {
-        if (sg < 16) {
-            const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 32);
-            sl.v[0] = p[0];
-            sl.v[1] = p[1];
-            sl.x = reinterpret_cast<const uint32_t*>(row + 512)[sg >> 2];
-        } else {  // bf16 RoPE channels 512 + 32 (sg - 16) ..
-            const u32x4* p = reinterpret_cast<const u32x4*>(row + 528 + (sg - 16) * 64);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sl.v[i] = p[i];
-        }
-    } else {  // SRC_FP4: 16 nibble bytes + 2 scale bytes per 32 channels
-        sl.v[0] = *reinterpret_cast<const u32x4*>(row + sg * 16);
-        sl.x = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * sg);
-    }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int SRC>
-__device__ __forceinline__ void load_b(SlotB& sl, int h, const uint8_t* __restrict__ row, int sg) {
-    if constexpr (SRC == SRC_BF16) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sl.v[h][i] = p[i];
-    } else if constexpr (SRC == SRC_E4M3) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + sg * 32);
-        sl.v[h][0] = p[0];
-        sl.v[h][1] = p[1];
-        sl.x[h] = reinterpret_cast<const uint32_t*>(row + 512)[sg >> 2];
-    } else {
-        sl.v[h][0] = *reinterpret_cast<const u32x4*>(row + sg * 16);
-        sl.x[h] = *reinterpret_cast<const uint16_t*>(row + 256 + 2 * sg);
-    }
+// 16 bytes from global memory to LDS address m0 + 16 * lane. Issued as inline
+// assembly so that the compiler does not wait for it at every barrier; the
+// kernel waits for these loads itself with vmcnt. The compiler reserves M0 and
+// warns about the clobber; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// 32 values of segment sg of a PV-phase item row: fp16 (E4M3 / E2M1, exact) or bf16 bits.
-template <int SRC>
-__device__ __forceinline__ void value_bits(const SlotB& sl, int h, uint16_t out[32]) {
-    if constexpr (SRC == SRC_BF16) {
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 ds_tr8(const uint8_t* p) {
+    const v2i_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i_t*)(
+        (__attribute__((address_space(3))) uint8_t*)(uintptr_t)lds_addr(p)));
+    return u32x2{(uint32_t)r.x, (uint32_t)r.y};
+}
+__device__ __forceinline__ u32x2 ds_tr16(const uint8_t* p) {
+    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(
+        (__attribute__((address_space(3))) uint8_t*)(uintptr_t)lds_addr(p)));
+    return u32x2{(uint32_t)(uint16_t)r.x | ((uint32_t)(uint16_t)r.y << 16),
+                 (uint32_t)(uint16_t)r.z | ((uint32_t)(uint16_t)r.w << 16)};
+}
+
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one head's rows), on the
+// VALU: each permlane swap hands every lane the value of its partner row / half.
+__device__ __forceinline__ float xmax4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    x = fmaxf(u2f(a[0]), u2f(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+__device__ __forceinline__ float xsum4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    x = u2f(a[0]) + u2f(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(b[0]) + u2f(b[1]);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (round to nearest even, hardware convert), low half first
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+// 8 floats -> bf16 high parts and bf16 residuals (p = hi + lo to about 16 bits)
+__device__ __forceinline__ void split_bf16x8(const float* p, u32x4& hi, u32x4& lo) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                out[8 * i + 2 * e] = (uint16_t)(sl.v[h][i][e] & 0xFFFFu);
-                out[8 * i + 2 * e + 1] = (uint16_t)(sl.v[h][i][e] >> 16);
-            }
-    } else if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t w = sl.v[h][i >> 2][i & 3];
-            const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-            const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-            out[4 * i] = (uint16_t)(lo & 0xFFFFu);
-            out[4 * i + 1] = (uint16_t)(lo >> 16);
-            out[4 * i + 2] = (uint16_t)(hi & 0xFFFFu);
-            out[4 * i + 3] = (uint16_t)(hi >> 16);
-        }
-    } else {
-        const float s0 = e4m3_to_f32(sl.x[h] & 0xFFu), s1 = e4m3_to_f32((sl.x[h] >> 8) & 0xFFu);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float sc = (i < 2) ? s0 : s1;
-            const uint32_t w = sl.v[h][0][i];
-            const f32x2 v[4] = {e2m1x2_to_f32<0>(w), e2m1x2_to_f32<1>(w), e2m1x2_to_f32<2>(w), e2m1x2_to_f32<3>(w)};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                out[8 * i + 2 * e] = __builtin_bit_cast(uint16_t, (_Float16)(v[e].x * sc));
-                out[8 * i + 2 * e + 1] = __builtin_bit_cast(uint16_t, (_Float16)(v[e].y * sc));
-            }
-        }
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h = pk_bf16(p[2 * i], p[2 * i + 1]);
+        hi[i] = h;
+        lo[i] = pk_bf16(p[2 * i] - u2f(h << 16), p[2 * i + 1] - u2f(h & 0xFFFF0000u));
     }
 }
 
@@ -174,346 +152,426 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// One split: QK phase, exact softmax statistics, PV phase, partial.
-template <int SRC, int DQK, int NHT>
-__device__ __forceinline__ void decode_split(const DecodeArgs& a, Lds<DQK>& L, int b, int split, int S,
-                                             bool is_win, int64_t first, int n_rows, float* o_part,
-                                             float* lse_part) {
-    constexpr int NT = DQK / 32;           // k-steps of QK = 32-channel segments of a K row
-    constexpr int NTH = 256;               // every wave loads; waves w < NHT also contract
-    constexpr int NITEM_A = kChunk * NT;
-    constexpr int NSLOT_A = (NITEM_A + NTH - 1) / NTH;
-    constexpr int NITEM_B = (kChunk / 2) * (kDv / 32);   // (row pair, value segment)
-    constexpr int NSLOT_B = (NITEM_B + NTH - 1) / NTH;
-    constexpr int KS = Lds<DQK>::kKs;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int j = lane & 15, g = lane >> 4;
-    const bool mw = w < NHT;
-    const int head = 16 * (NHT * (int)blockIdx.z + w) + j;
-    constexpr float kLog2e = 1.4426950408889634f;
-    const float zscale = a.scale * kLog2e;
-    const int nc = (n_rows + kChunk - 1) / kChunk;
-
-    auto row_ptr = [&](int u) -> const uint8_t* {
-        if (u >= n_rows) return nullptr;
-        if (is_win) return reinterpret_cast<const uint8_t*>(a.win + ((int64_t)b * a.W + first + u) * DQK);
-        const int32_t s = a.idx[(int64_t)b * a.k + first + u];
-        if (s < 0 || s >= a.capacity) return nullptr;
-        return a.cache + b * a.stride + (int64_t)s * a.row_bytes;
-    };
-    auto load_chunk_a = [&](int c0, SlotA* sl) {
-#pragma unroll
-        for (int i = 0; i < NSLOT_A; ++i) {
-            const int item = tid + i * NTH;
-            sl[i].ok = 0;
-            if (item < NITEM_A) {
-                const uint8_t* rp = row_ptr(c0 + item % kChunk);
-                if (rp) {
-                    sl[i].ok = 1;
-                    load_a<SRC>(sl[i], rp, item / kChunk);
-                }
-            }
-        }
-    };
-    auto load_chunk_b = [&](int c0, SlotB* sl) {
-#pragma unroll
-        for (int i = 0; i < NSLOT_B; ++i) {
-            const int item = tid + i * NTH;
-            sl[i].ok[0] = sl[i].ok[1] = 0;
-            if (item < NITEM_B) {
-                const int rp = item % (kChunk / 2), sg = item / (kChunk / 2);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint8_t* p = row_ptr(c0 + 2 * rp + h);
-                    if (p) {
-                        sl[i].ok[h] = 1;
-                        load_b<SRC>(sl[i], h, p, sg);
-                    }
-                }
-            }
-        }
-    };
-    auto store_chunk_a = [&](const SlotA* sl) {
-#pragma unroll
-        for (int i = 0; i < NSLOT_A; ++i) {
-            const int item = tid + i * NTH;
-            if (item >= NITEM_A) continue;
-            const int sg = item / kChunk, r = item % kChunk;
-            uint32_t* kd = reinterpret_cast<uint32_t*>(L.tile + r * KS + sg * 32);
-            if (!sl[i].ok) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(kd)[q] = u32x4{0u, 0u, 0u, 0u};
-                if (SRC == SRC_E4M3 && sg < 4) L.fac[r][sg] = 0.0f;
-            } else if constexpr (SRC == SRC_BF16) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(kd)[q] = sl[i].v[q];
-            } else if constexpr (SRC == SRC_E4M3) {
-                if (sg < 16) {
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const u32x2 p0 = e4m3x4_to_bf16(sl[i].v[q].x), p1 = e4m3x4_to_bf16(sl[i].v[q].y);
-                        const u32x2 p2 = e4m3x4_to_bf16(sl[i].v[q].z), p3 = e4m3x4_to_bf16(sl[i].v[q].w);
-                        reinterpret_cast<u32x4*>(kd)[2 * q] = u32x4{p0.x, p0.y, p1.x, p1.y};
-                        reinterpret_cast<u32x4*>(kd)[2 * q + 1] = u32x4{p2.x, p2.y, p3.x, p3.y};
-                    }
-                    if ((sg & 3) == 0) {
-                        L.fac[r][sg >> 2] = u2f(sl[i].x);
-                        atomicMax(&L.smax_bits[sg >> 2], sl[i].x);     // positive fp32 orders as uint
-                    }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) reinterpret_cast<u32x4*>(kd)[q] = sl[i].v[q];
-                }
-            } else {  // E2M1 x E4M3 scale, exact in bf16
-                const float s0 = e4m3_to_f32(sl[i].x & 0xFFu), s1 = e4m3_to_f32((sl[i].x >> 8) & 0xFFu);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float sc = (q < 2) ? s0 : s1;
-                    const uint32_t wv = sl[i].v[0][q];
-                    const f32x2 v0 = e2m1x2_to_f32<0>(wv), v1 = e2m1x2_to_f32<1>(wv);
-                    const f32x2 v2 = e2m1x2_to_f32<2>(wv), v3 = e2m1x2_to_f32<3>(wv);
-                    reinterpret_cast<u32x4*>(kd)[q] =
-                        u32x4{pack_bf16_trunc(v0.x * sc, v0.y * sc), pack_bf16_trunc(v1.x * sc, v1.y * sc),
-                              pack_bf16_trunc(v2.x * sc, v2.y * sc), pack_bf16_trunc(v3.x * sc, v3.y * sc)};
-                }
-            }
-            if (sg == 0) L.valid[r] = sl[i].ok;
-        }
-    };
-    auto store_chunk_b = [&](const SlotB* sl) {
-#pragma unroll
-        for (int i = 0; i < NSLOT_B; ++i) {
-            const int item = tid + i * NTH;
-            if (item >= NITEM_B) continue;
-            const int rp = item % (kChunk / 2), sg = item / (kChunk / 2);
-            uint16_t v0[32], v1[32];
-            if (sl[i].ok[0]) value_bits<SRC>(sl[i], 0, v0);
-            else {
-#pragma unroll
-                for (int e = 0; e < 32; ++e) v0[e] = 0;
-            }
-            if (sl[i].ok[1]) value_bits<SRC>(sl[i], 1, v1);
-            else {
-#pragma unroll
-                for (int e = 0; e < 32; ++e) v1[e] = 0;
-            }
-#pragma unroll
-            for (int e = 0; e < 32; ++e)
-                *reinterpret_cast<uint32_t*>(L.tile + vt_off(sg * 32 + e) + 2 * rp) =
-                    (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
-            if (SRC == SRC_E4M3 && (sg & 3) == 0) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    L.fac[2 * rp + h][sg >> 2] = sl[i].ok[h] ? u2f(sl[i].x[h]) * L.inv_smax[sg >> 2] : 0.0f;
-            }
-        }
-    };
-
-    // ---- start the first chunk's loads, then stage the queries
-    SlotA sa[NSLOT_A];
-    SlotB sb[NSLOT_B];
-    if (nc > 0) load_chunk_a(0, sa);
-    {
-        constexpr int NQ = 16 * NHT * (DQK / 8);           // 16-byte pieces of the queries
-        constexpr int NQT = (NQ + NTH - 1) / NTH;
-        const int head0 = 16 * NHT * (int)blockIdx.z;
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head0) * DQK;
-        u32x4 qv[NQT];
-#pragma unroll
-        for (int i = 0; i < NQT; ++i) {
-            const int e = tid + i * NTH;
-            if (e < NQ) qv[i] = *reinterpret_cast<const u32x4*>(qp + (int64_t)(e / (DQK / 8)) * DQK + (e % (DQK / 8)) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < NQT; ++i) {
-            const int e = tid + i * NTH;
-            if (e < NQ) *reinterpret_cast<u32x4*>(L.qs + (e / (DQK / 8)) * KS + (e % (DQK / 8)) * 8) = qv[i];
-        }
-        if (tid < 4) L.smax_bits[tid] = 0u;
-    }
-    const uint16_t* qrow = L.qs + (16 * w + j) * KS + g * 8;
-
-    // ---- QK phase: scores of all chunks into registers (base 2, scaled)
-    float z[kMaxChunks][2][4];
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) z[c][rt][r] = -__builtin_inff();
-        if (c >= nc) continue;
-        __syncthreads();                                   // previous tile fully consumed (and q staged)
-        store_chunk_a(sa);
-        __syncthreads();
-        if (c + 1 < nc) load_chunk_a((c + 1) * kChunk, sa);
-        else load_chunk_b(0, sb);                          // PV phase's first chunk, in flight now
-        if (!mw) continue;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const uint16_t* ka = L.tile + (16 * rt + j) * KS + g * 8;
-            f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-                for (int b4 = 0; b4 < 4; ++b4) {
-                    f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 4 * b4; t < 4 * b4 + 4; ++t)
-                        t4 = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
-                                       *reinterpret_cast<const u32x4*>(qrow + t * 32), t4);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) sacc[r] += t4[r] * L.fac[16 * rt + 4 * g + r][b4];
-                }
-#pragma unroll
-                for (int t = 16; t < NT; ++t)
-                    sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
-                                     *reinterpret_cast<const u32x4*>(qrow + t * 32), sacc);
-            } else {
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    sacc = mfma_bf16(*reinterpret_cast<const u32x4*>(ka + t * 32),
-                                     *reinterpret_cast<const u32x4*>(qrow + t * 32), sacc);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (L.valid[16 * rt + 4 * g + r]) z[c][rt][r] = sacc[r] * zscale;
-        }
-    }
-
-    // ---- exact softmax statistics of the split, per head (lanes j, j+16, j+32, j+48)
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) m = fmaxf(m, z[c][rt][r]);
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    float l = 0.0f;
-    if (m != -__builtin_inff()) {
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    z[c][rt][r] = __builtin_amdgcn_exp2f(z[c][rt][r] - m);     // exp2(-inf) = 0
-                    l += z[c][rt][r];
-                }
-    } else {                                               // no visible entry: P = 0, never -inf
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c)
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) z[c][rt][r] = 0.0f;
-    }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if constexpr (SRC == SRC_E4M3) {
-        __syncthreads();                                   // every row's scale is in smax_bits
-        if (tid < 4) {                                     // read by the PV stores after their barrier
-            const float sm = u2f(L.smax_bits[tid]);
-            L.inv_smax[tid] = (sm > 0.0f) ? 1.0f / sm : 1.0f;
-        }
-    }
-
-    // ---- PV phase: O^T += V^T P^T; k-slot (g, e): e < 4 -> row 4g+e, e >= 4 -> row 16+4g+e-4
-    f32x4 oacc[kDv / 16];
-#pragma unroll
-    for (int i = 0; i < kDv / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-        if (c >= nc) continue;
-        __syncthreads();
-        store_chunk_b(sb);
-        __syncthreads();
-        if (c + 1 < nc) load_chunk_b((c + 1) * kChunk, sb);
-        if (!mw) continue;
-        const float (*p)[4] = z[c];
-        if constexpr (SRC == SRC_BF16) {
-            float hi[8], lo[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = p[e >> 2][e & 3];
-                hi[e] = u2f(bf16_rne(v) << 16);
-                lo[e] = v - hi[e];
-            }
-            const u32x4 ph = u32x4{bf16_rne(hi[0]) | (bf16_rne(hi[1]) << 16), bf16_rne(hi[2]) | (bf16_rne(hi[3]) << 16),
-                                   bf16_rne(hi[4]) | (bf16_rne(hi[5]) << 16), bf16_rne(hi[6]) | (bf16_rne(hi[7]) << 16)};
-            const u32x4 pl = u32x4{bf16_rne(lo[0]) | (bf16_rne(lo[1]) << 16), bf16_rne(lo[2]) | (bf16_rne(lo[3]) << 16),
-                                   bf16_rne(lo[4]) | (bf16_rne(lo[5]) << 16), bf16_rne(lo[6]) | (bf16_rne(lo[7]) << 16)};
-#pragma unroll
-            for (int mt = 0; mt < kDv / 16; ++mt) {
-                const uint16_t* va = L.tile + vt_off(16 * mt + j);
-                const u32x2 x0 = *reinterpret_cast<const u32x2*>(va + 4 * g);
-                const u32x2 x1 = *reinterpret_cast<const u32x2*>(va + 16 + 4 * g);
-                const u32x4 av = u32x4{x0.x, x0.y, x1.x, x1.y};
-                oacc[mt] = mfma_bf16(av, ph, oacc[mt]);
-                oacc[mt] = mfma_bf16(av, pl, oacc[mt]);
-            }
-        } else {
-            u32x4 pv[4];
-            if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-                for (int b4 = 0; b4 < 4; ++b4) {
-                    float q8[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int row = (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4);
-                        q8[e] = p[e >> 2][e & 3] * L.fac[row][b4];
-                    }
-                    pv[b4] = u32x4{pack_f16_rne(q8[0], q8[1]), pack_f16_rne(q8[2], q8[3]),
-                                   pack_f16_rne(q8[4], q8[5]), pack_f16_rne(q8[6], q8[7])};
-                }
-            } else {
-                pv[0] = u32x4{pack_f16_rne(p[0][0], p[0][1]), pack_f16_rne(p[0][2], p[0][3]),
-                              pack_f16_rne(p[1][0], p[1][1]), pack_f16_rne(p[1][2], p[1][3])};
-            }
-#pragma unroll
-            for (int mt = 0; mt < kDv / 16; ++mt) {
-                const uint16_t* va = L.tile + vt_off(16 * mt + j);
-                const u32x2 x0 = *reinterpret_cast<const u32x2*>(va + 4 * g);
-                const u32x2 x1 = *reinterpret_cast<const u32x2*>(va + 16 + 4 * g);
-                const u32x4 av = u32x4{x0.x, x0.y, x1.x, x1.y};
-                oacc[mt] = mfma_f16(av, pv[(SRC == SRC_E4M3) ? (mt >> 3) : 0], oacc[mt]);
-            }
-        }
-    }
-
-    // ---- partial: normalised output and logsumexp (natural log) of the split
-    if (!mw) return;
-    const int64_t prow = ((int64_t)b * S + split) * a.H + head;
-    const float inv_l = (l > 0.0f) ? 1.0f / l : 0.0f;
-#pragma unroll
-    for (int mt = 0; mt < kDv / 16; ++mt) {
-        float f = inv_l;
-        if constexpr (SRC == SRC_E4M3) f *= u2f(L.smax_bits[mt >> 3]);
-        *reinterpret_cast<float4*>(o_part + prow * kDv + 16 * mt + 4 * g) =
-            make_float4(oacc[mt][0] * f, oacc[mt][1] * f, oacc[mt][2] * f, oacc[mt][3] * f);
-    }
-    if (g == 0)
-        lse_part[prow] = (l > 0.0f) ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
+// 8 E4M3 codes -> 8 exact bf16 / fp16 values (two per u32)
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 w) {
+    const u32x2 a = e4m3x4_to_bf16(w.x), b = e4m3x4_to_bf16(w.y);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 w) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true))};
 }
 
-template <int SRC_MAIN, int DQK, int NHT>
-__global__ __launch_bounds__(256) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps,
-                                                          float* o_part, float* lse_part) {
-    __shared__ Lds<DQK> L;
-    const int b = blockIdx.y;
-    const int split = blockIdx.x;
+// Entries per split and heads per workgroup. Fewer, longer splits write fewer
+// fp32 partials; more splits keep more workgroups in flight. MLA_DECODE_RPS
+// (32..256, multiple of 32) and MLA_DECODE_HT (1 or 2) override the choice for
+// tuning; the workspace query reads them too.
+struct Geometry {
+    int ht, rps, S_main, S_win, groups;
+};
+
+Geometry decode_geometry(int B, int H, int k, int W) {
+    Geometry g{};
+    g.ht = 1;
+    if (const char* e = getenv("MLA_DECODE_HT")) {
+        const int v = atoi(e);
+        if (v == 2 && H % 32 == 0) g.ht = 2;
+    }
+    g.groups = H / (16 * g.ht);
+    int rps = 0;
+    if (const char* e = getenv("MLA_DECODE_RPS")) {
+        const int v = atoi(e);
+        if (v >= kChunk && v <= kMaxRps && v % kChunk == 0) rps = v;
+    }
+    if (rps == 0) {
+        // the longest split that still gives every CU a workgroup; at least two chunks
+        constexpr int kTargetBlocks = 256;
+        constexpr int kMinRps = 2 * kChunk;
+        rps = kMinRps;
+        for (int r = kMaxRps; r >= kMinRps; r /= 2) {
+            const int64_t blocks = (int64_t)B * g.groups * ((k + r - 1) / r + (W + r - 1) / r);
+            if (blocks >= kTargetBlocks) { rps = r; break; }
+        }
+    }
+    g.rps = rps;
+    g.S_main = (k + rps - 1) / rps;
+    g.S_win = (W + rps - 1) / rps;
+    return g;
+}
+
+template <int SRC_MAIN, int DQK>
+constexpr int decode_lds_bytes(bool window) {
+    constexpr int m = Stage<SRC_MAIN, DQK>::kLds, w = Stage<SRC_BF16, DQK>::kLds;
+    return kLdsBuf + ((window && w > m) ? w : m);
+}
+
+// E2M1 rows through registers: 32 rows x 16 pieces (32 channels each) per chunk.
+struct Fp4Slot {
+    u32x4 v;
+    uint32_t sc;
+    int ok;
+};
+
+// One split of one workgroup. SRC is the kind of the rows (the window is bf16).
+template <int SRC, int DQK, int HT>
+__device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
+                                             bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
+    using G = Stage<SRC, DQK>;
+    constexpr int NB = G::kBufs;
+    constexpr int KH = (HT == 1) ? 2 : 1;                 // K halves split over waves
+    constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
+    constexpr int NMAIN_W = (HT == 1) ? 8 : 16;           // main k-steps per wave
+    constexpr int NROPE_W = (HT == 1) ? NROPE / 2 : NROPE;
+    constexpr int NQ = NMAIN_W + NROPE_W;
+    constexpr float kLazy = 8.0f;                         // P <= 2^8 before the reference max moves
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, g = lane >> 4;
+    const int rt = w & 1;                                   // QK row tile
+    const int kh = (HT == 1) ? (w >> 1) : 0;                // QK K half
+    const int qt = (HT == 1) ? 0 : (w >> 1);                // QK head tile
+    const int nc = (n + kChunk - 1) / kChunk;
+    int32_t* ridx = reinterpret_cast<int32_t*>(smem + kLdsIdx);
+    float* zs = reinterpret_cast<float*>(smem + kLdsZ);
+    uint8_t* bufs = smem + kLdsBuf;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float zscale = a.scale * kLog2e;
+
+    // ---- queries of the wave's QK head tile and K range: k-step t covers channels 32 t .. 32 t + 31
+    u32x4 qv[NQ];
+    {
+        const int head = 16 * (HT * hg + qt) + j;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head) * DQK + 8 * g;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
+            qv[i] = *reinterpret_cast<const u32x4*>(qp + 32 * t);
+        }
+    }
+    // ---- row indices of the split (-1: no row)
+    {
+        int32_t r = -1;
+        if (tid < n) {
+            if (is_win) r = (int32_t)(first + tid);
+            else {
+                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
+                if (s >= 0 && s < a.capacity) r = s;
+            }
+        }
+        ridx[tid] = r;
+    }
+    __syncthreads();
+
+    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
+                                     : a.cache + b * a.stride;
+    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;   // at most 2 KiB
+    const uint32_t buf_m0 = __builtin_amdgcn_readfirstlane(lds_addr(bufs));
+    // direct path: the lane's slots are the same in every chunk; slot (i) = 64 (w + 4 i) + lane
+    // row in chunk (kChunk: none), byte offset in the row, whether the slot holds row bytes
+    int slot_row[G::kHi];
+    uint32_t slot_off[G::kHi];
+    bool slot_data[G::kHi];
+#pragma unroll
+    for (int i = 0; i < G::kHi; ++i) {
+        const int s = 64 * (w + 4 * i) + lane;
+        const int u = s / G::kPieces, p = s - u * G::kPieces;
+        slot_row[i] = u < kChunk ? u : kChunk;
+        slot_off[i] = 16u * (uint32_t)p;
+        slot_data[i] = u < kChunk && p < G::kDataPieces;
+    }
+    // issue chunk c into buffer c % NB; returns the lane's slots whose row has no bytes (to be zeroed)
+    auto issue = [&](int c) -> uint32_t {
+        uint32_t zm = 0;
+        const uint32_t m0 = buf_m0 + (uint32_t)((c % NB) * G::kBytes);
+        int32_t rr[G::kHi];
+#pragma unroll
+        for (int i = 0; i < G::kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
+        const void* src[G::kHi];
+#pragma unroll
+        for (int i = 0; i < G::kHi; ++i) {
+            const bool row_ok = slot_row[i] < kChunk && rr[i] >= 0;
+            zm |= (slot_row[i] < kChunk && rr[i] < 0) ? (1u << i) : 0u;
+            // computed for every slot and selected without branching; slots without row
+            // bytes load a 16-byte-aligned stand-in (the queries)
+            const uint64_t row = reinterpret_cast<uint64_t>(row_base + slot_off[i]) +
+                                 (uint64_t)(uint32_t)(rr[i] < 0 ? 0 : rr[i]) * row_bytes;
+            const bool use = row_ok && slot_data[i];
+            src[i] = reinterpret_cast<const void*>(use ? row : reinterpret_cast<uint64_t>(a.q));
+        }
+#pragma unroll
+        for (int i = 0; i < G::kHi; ++i)
+            if (w + 4 * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(w + 4 * i));
+        return zm;
+    };
+    // register path (E2M1): 2 pieces of 32 channels per thread per chunk
+    Fp4Slot fs[2];
+    auto fp4_load = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int item = tid + kThreads * i;
+            const int u = item >> 4, p = item & 15;
+            const int32_t r = ridx[kChunk * c + u];
+            fs[i].ok = r >= 0;
+            if (r >= 0) {
+                const uint8_t* rp = row_base + (uint64_t)(uint32_t)r * row_bytes;
+                fs[i].v = *reinterpret_cast<const u32x4*>(rp + 16 * p);
+                fs[i].sc = *reinterpret_cast<const uint16_t*>(rp + 256 + 2 * p);
+            }
+        }
+    };
+    auto fp4_store = [&](int c) {
+        uint8_t* buf = bufs + (c % NB) * G::kBytes;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int item = tid + kThreads * i;
+            const int u = item >> 4, p = item & 15;
+            u32x4* d = reinterpret_cast<u32x4*>(buf + u * G::kStride + 64 * p);
+            const float s0 = fs[i].ok ? e4m3_to_f32(fs[i].sc & 0xFFu) : 0.0f;
+            const float s1 = fs[i].ok ? e4m3_to_f32((fs[i].sc >> 8) & 0xFFu) : 0.0f;
+            const u32x4 v = fs[i].ok ? fs[i].v : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float sc = (q < 2) ? s0 : s1;
+                const uint32_t wv = v[q];
+                const f32x2 v0 = e2m1x2_to_f32<0>(wv), v1 = e2m1x2_to_f32<1>(wv);
+                const f32x2 v2 = e2m1x2_to_f32<2>(wv), v3 = e2m1x2_to_f32<3>(wv);
+                d[q] = u32x4{pack_bf16_trunc(v0.x * sc, v0.y * sc), pack_bf16_trunc(v1.x * sc, v1.y * sc),
+                             pack_bf16_trunc(v2.x * sc, v2.y * sc), pack_bf16_trunc(v3.x * sc, v3.y * sc)};
+            }
+        }
+    };
+
+    // ---- running state: reference max (base 2, lazily raised), per-lane partial sums, output tile
+    f32x4 o[HT][8];
+#pragma unroll
+    for (int h = 0; h < HT; ++h)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[h][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref[HT], l_run[HT];
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+        m_ref[h] = -__builtin_inff();
+        l_run[h] = 0.0f;
+    }
+
+    uint32_t zm0 = 0, zm1 = 0;                              // zero masks of the chunks in flight
+    if constexpr (G::kDirect) {
+        if (nc > 0) zm0 = issue(0);
+        if (NB > 2 && nc > 1) zm1 = issue(1);
+    } else {
+        if (nc > 0) fp4_load(0);
+    }
+
+    for (int c = 0; c < nc; ++c) {
+        uint8_t* buf = bufs + (c % NB) * G::kBytes;
+        if constexpr (G::kDirect) {
+            // chunk c has landed once at most the later chunk's loads are outstanding
+            if ((NB > 2) && (c + 1 < nc)) {
+                if (w < (G::kInstr & 3) || (G::kInstr & 3) == 0) wait_vmcnt<G::kHi>();
+                else wait_vmcnt<G::kLo>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            // rows without bytes read as zeros (their P is 0; stand-in bytes could decode to NaN)
+            if (__builtin_amdgcn_ballot_w64(zm0 != 0u)) {
+#pragma unroll
+                for (int i = 0; i < G::kHi; ++i)
+                    if (zm0 & (1u << i))
+                        *reinterpret_cast<u32x4*>(buf + 16 * (64 * (w + 4 * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            fp4_store(c);
+        }
+        __syncthreads();                                    // chunk c staged; chunk c - 1 consumed
+        if constexpr (G::kDirect) {
+            zm0 = zm1;
+            zm1 = 0;
+            if (c + NB - 1 < nc) {
+                if (NB > 2) zm1 = issue(c + NB - 1);
+                else zm0 = issue(c + NB - 1);
+            }
+        } else {
+            if (c + 1 < nc) fp4_load(c + 1);
+        }
+
+        // ---- QK: rows 16 rt .. +15, K range of the wave, head tile qt
+        {
+            const uint8_t* krow = buf + (16 * rt + j) * G::kStride;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+                for (int bb = 0; bb < NMAIN_W / 4; ++bb) {
+                    const int blk = (NMAIN_W / 4) * kh + bb;
+                    f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int t = 4 * blk + s4;
+                        const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * t + 8 * g);
+                        t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[4 * bb + s4], t4);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[r] += t4[r] * *reinterpret_cast<const float*>(buf + (16 * rt + 4 * g + r) * G::kStride +
+                                                                        512 + 4 * blk);
+                }
+#pragma unroll
+                for (int i = 0; i < NROPE_W; ++i) {
+                    const int t = NROPE_W * kh + i;            // RoPE k-step within the 64 RoPE channels
+                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 528 + 2 * (32 * t + 8 * g)),
+                                    qv[NMAIN_W + i], acc);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
+                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * t + 8 * g)), qv[i], acc);
+                }
+            }
+            float* zd = zs + (((c & 1) * KH + kh) * 16 * HT + 16 * qt + j) * kZs + 16 * rt + 4 * g;
+            *reinterpret_cast<f32x4*>(zd) = acc;
+        }
+        __syncthreads();                                    // scores of chunk c complete
+
+        // ---- softmax on the chunk; lane (j, g) holds rows 8 g .. 8 g + 7 of head j
+        bool vld[8];
+        {
+            const int32_t* rp = ridx + kChunk * c + 8 * g;
+            const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp), r1 = *reinterpret_cast<const u32x4*>(rp + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vld[e] = (int32_t)r0[e] >= 0;
+                vld[4 + e] = (int32_t)r1[e] >= 0;
+            }
+        }
+        float sc[8];                                        // E4M3: the rows' scale of block w (0 for rows without bytes)
+        if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 + 4 * w);
+        }
+        float z[HT][8], alpha[HT];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < HT; ++h) {
+            const float* zr = zs + (((c & 1) * KH) * 16 * HT + 16 * h + j) * kZs + 8 * g;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(zr), a1 = *reinterpret_cast<const f32x4*>(zr + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[h][e] = a0[e];
+                z[h][4 + e] = a1[e];
+            }
+            if constexpr (KH == 2) {
+                const float* zr2 = zr + 16 * HT * kZs;
+                const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr2), b1 = *reinterpret_cast<const f32x4*>(zr2 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[h][e] += b0[e];
+                    z[h][4 + e] += b1[e];
+                }
+            }
+            float cm = -__builtin_inff();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                z[h][e] = vld[e] ? z[h][e] * zscale : -__builtin_inff();
+                cm = fmaxf(cm, z[h][e]);
+            }
+            cm = xmax4(cm);
+            // the reference moves only when the chunk exceeds it by more than 2^kLazy (and on
+            // the first chunk with a visible row, where the factor is exp2(-inf) = 0 on empty state)
+            const bool up = cm > m_ref[h] + kLazy;
+            alpha[h] = up ? __builtin_amdgcn_exp2f(m_ref[h] - cm) : 1.0f;
+            m_ref[h] = up ? cm : m_ref[h];
+            grow |= up;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int h = 0; h < HT; ++h) {
+                l_run[h] *= alpha[h];
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) o[h][mt] = o[h][mt] * alpha[h];
+            }
+        }
+        u32x4 pa[HT], pb[HT];                               // PV B operands: P (times the E4M3 scale) as bf16 hi, lo
+#pragma unroll
+        for (int h = 0; h < HT; ++h) {
+            float ls = 0.0f;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = (z[h][e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[h][e] - m_ref[h]);
+                ls += p[e];
+                if constexpr (SRC == SRC_E4M3) p[e] *= sc[e];
+            }
+            l_run[h] += ls;
+            split_bf16x8(p, pa[h], pb[h]);
+        }
+
+        // ---- PV: O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels 128 w .. +127
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const int c0 = 128 * w + 16 * mt;
+            u32x4 av;
+            if constexpr (SRC == SRC_E4M3) {
+                // lane (G, m) names row 8 G + m / 2, channels c0 + 8 (m & 1) ..; receives channel c0 + m of rows 8 G ..
+                av = e4m3x8_to_bf16(ds_tr8(buf + (8 * g + (j >> 1)) * G::kStride + c0 + 8 * (j & 1)));
+            } else {
+                // lane (G, m) names row 8 G + m / 4 (+4), channels c0 + 4 (m & 3) ..
+                const uint8_t* vp = buf + (8 * g + (j >> 2)) * G::kStride + 2 * (c0 + 4 * (j & 3));
+                const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * G::kStride);
+                av = u32x4{r0.x, r0.y, r1.x, r1.y};
+            }
+#pragma unroll
+            for (int h = 0; h < HT; ++h) {
+                o[h][mt] = mfma_bf16(av, pa[h], o[h][mt]);
+                o[h][mt] = mfma_bf16(av, pb[h], o[h][mt]);
+            }
+        }
+    }
+
+    // ---- partial: normalised output (channels 128 w ..) and logsumexp of the split
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+        const float l = xsum4(l_run[h]);
+        const int head = 16 * (HT * hg + h) + j;
+        const int64_t prow = ((int64_t)b * S + split) * a.H + head;
+        const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * w + 16 * mt + 4 * g) =
+                make_float4(o[h][mt][0] * f, o[h][mt][1] * f, o[h][mt][2] * f, o[h][mt][3] * f);
+        if (w == 0 && g == 0)
+            lse_part[prow] = (l > 0.0f) ? (m_ref[h] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
+                                        : -__builtin_inff();
+    }
+}
+
+// Work item order: consecutive items are the head groups of one split; items
+// [x * per, (x + 1) * per) run on XCD x (workgroups go to XCDs round-robin).
+template <int SRC_MAIN, int DQK, int HT>
+__global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps, int groups,
+                                                          int n_items, float* o_part, float* lse_part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int L = blockIdx.x;
+    const int per = gridDim.x >> 3;
+    const int item = (L & 7) * per + (L >> 3);
+    if (item >= n_items) return;
     const int S = S_main + S_win;
+    const int hg = item % groups;
+    const int rest = item / groups;
+    const int split = rest % S;
+    const int b = rest / S;
     if (split < S_main) {
         const int64_t first = (int64_t)split * rps;
         const int n = (int)((a.k - first < rps) ? a.k - first : rps);
-        decode_split<SRC_MAIN, DQK, NHT>(a, L, b, split, S, false, first, n, o_part, lse_part);
+        decode_split<SRC_MAIN, DQK, HT>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
     } else {
         const int64_t first = (int64_t)(split - S_main) * rps;
         const int wl = (int)clamp_visible(a.win_len[b], a.W);
         int n = (int)(wl - first);
         n = n < 0 ? 0 : (n > rps ? rps : n);
-        decode_split<SRC_BF16, DQK, NHT>(a, L, b, split, S, true, first, n, o_part, lse_part);
+        decode_split<SRC_BF16, DQK, HT>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
     }
 }
 
@@ -664,20 +722,34 @@ bool decode_supported(int fmt, int dim, int rope, int d_v, int H) {
     return dim + rope <= 1024 && d_v <= dim + rope && d_v > 0;
 }
 
-static void decode_geometry(int H, int k, int W, int* S_main, int* S_win, int* rps) {
-    *rps = rows_per_split(H, k);
-    *S_main = (k + *rps - 1) / *rps;
-    *S_win = (W + *rps - 1) / *rps;
-}
-
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W) {
     if (!mfma_shape(fmt, dim, rope, d_v, H)) return 0;
-    int S_main, S_win, rps;
-    decode_geometry(H, k, W, &S_main, &S_win, &rps);
-    const size_t S = (size_t)(S_main + S_win);
+    const Geometry g = decode_geometry(B, H, k, W);
+    const size_t S = (size_t)(g.S_main + g.S_win);
     const size_t o = (size_t)B * S * H * kDv * sizeof(float);
     const size_t l = (size_t)B * S * H * sizeof(float);
     return ((o + 255) & ~(size_t)255) + ((l + 255) & ~(size_t)255);
+}
+
+template <int SRC_MAIN, int DQK, int HT>
+static hipError_t launch_mfma(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
+                              hipStream_t stream) {
+    const int S = g.S_main + g.S_win;
+    const int n_items = a.B * S * g.groups;
+    const int grid = (n_items + 7) / 8 * 8;
+    const int lds = decode_lds_bytes<SRC_MAIN, DQK>(g.S_win > 0);
+    auto kern = k_decode_mfma<SRC_MAIN, DQK, HT>;
+    static bool attr_set = false;                          // dynamic LDS above 64 KiB, once per kernel
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 decode_lds_bytes<SRC_MAIN, DQK>(true));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, g.S_main, g.S_win, g.rps, g.groups, n_items,
+                       o_part, lse_part);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -686,33 +758,30 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, a);
         return hipGetLastError();
     }
-    int S_main, S_win, rps;
-    decode_geometry(a.H, a.k, a.win ? a.W : 0, &S_main, &S_win, &rps);
-    const int S = S_main + S_win;
+    const Geometry g = decode_geometry(a.B, a.H, a.k, a.win ? a.W : 0);
+    const int S = g.S_main + g.S_win;
     const size_t o_bytes = (((size_t)a.B * S * a.H * kDv * sizeof(float)) + 255) & ~(size_t)255;
     float* o_part = reinterpret_cast<float*>(a.workspace);
     float* lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + o_bytes);
     if (S > 0) {
-        const int NHT = a.H >= 64 ? 4 : a.H / 16;
-        const dim3 grid(S, a.B, a.H / (16 * NHT));
-#define MLA_DEC_CASE(SRC, DQK, N)                                                                      \
-    if (NHT == N) {                                                                                    \
-        hipLaunchKernelGGL((k_decode_mfma<SRC, DQK, N>), grid, dim3(256), 0, stream, a, S_main,     \
-                           S - S_main, rps, o_part, lse_part);                                         \
-    }
-#define MLA_DEC_ALL_N(SRC, DQK) \
-    MLA_DEC_CASE(SRC, DQK, 1) MLA_DEC_CASE(SRC, DQK, 2) MLA_DEC_CASE(SRC, DQK, 4)
-        if (a.fmt == MLA_FMT_E4M3_S128) { MLA_DEC_ALL_N(SRC_E4M3, 576) }
-        else if (a.fmt == MLA_FMT_E2M1_S16) { MLA_DEC_ALL_N(SRC_FP4, 512) }
-        else if (a.rope == 64) { MLA_DEC_ALL_N(SRC_BF16, 576) }
-        else { MLA_DEC_ALL_N(SRC_BF16, 512) }
-#undef MLA_DEC_ALL_N
-#undef MLA_DEC_CASE
-        hipError_t e = hipGetLastError();
+        hipError_t e = hipSuccess;
+        const bool two = g.ht == 2;
+        if (a.fmt == MLA_FMT_E4M3_S128)
+            e = two ? launch_mfma<SRC_E4M3, 576, 2>(a, g, o_part, lse_part, stream)
+                    : launch_mfma<SRC_E4M3, 576, 1>(a, g, o_part, lse_part, stream);
+        else if (a.fmt == MLA_FMT_E2M1_S16)
+            e = two ? launch_mfma<SRC_FP4, 512, 2>(a, g, o_part, lse_part, stream)
+                    : launch_mfma<SRC_FP4, 512, 1>(a, g, o_part, lse_part, stream);
+        else if (a.rope == 64)
+            e = two ? launch_mfma<SRC_BF16, 576, 2>(a, g, o_part, lse_part, stream)
+                    : launch_mfma<SRC_BF16, 576, 1>(a, g, o_part, lse_part, stream);
+        else
+            e = two ? launch_mfma<SRC_BF16, 512, 2>(a, g, o_part, lse_part, stream)
+                    : launch_mfma<SRC_BF16, 512, 1>(a, g, o_part, lse_part, stream);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, S, a.H,
-                       o_part, lse_part, a.out, a.lse);
+    hipLaunchKernelGGL(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, S, a.H, o_part, lse_part, a.out,
+                       a.lse);
     return hipGetLastError();
 }
 

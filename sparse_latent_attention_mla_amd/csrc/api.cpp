@@ -64,17 +64,20 @@ mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int6
 }
 
 struct TopkLayout {
-    size_t scores, hist, counters, cand, total;
+    size_t scores, hist, counts, sel, cand, cand2, total;
 };
 
 TopkLayout topk_layout(int32_t B, int64_t capacity) {
     TopkLayout L;
     const size_t b = B > 0 ? (size_t)B : 0, cap = capacity > 0 ? (size_t)capacity : 0;
+    const size_t groups = capacity > 0 ? (size_t)mla::select_groups(capacity) : 0;
     L.scores = 0;
     L.hist = L.scores + round256(b * cap * sizeof(float));
-    L.counters = L.hist + round256(b * mla::kHistBinsHost * sizeof(uint32_t));
-    L.cand = L.counters + round256(b * 4 * sizeof(uint32_t));
-    L.total = L.cand + round256(b * cap * sizeof(uint64_t));
+    L.counts = L.hist + round256(b * mla::kHistBinsHost * sizeof(uint32_t));
+    L.sel = L.counts + round256(b * groups * 2 * sizeof(uint32_t));
+    L.cand = L.sel + round256(b * cap * sizeof(int32_t));
+    L.cand2 = L.cand + round256(b * cap * sizeof(uint64_t));
+    L.total = L.cand2 + round256(b * cap * sizeof(uint64_t));
     return L;
 }
 
@@ -198,8 +201,10 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     mla::TopkWorkspace T;
     T.scores = out_scores ? out_scores : reinterpret_cast<float*>(ws + L.scores);
     T.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-    T.counters = reinterpret_cast<uint32_t*>(ws + L.counters);
+    T.counts = reinterpret_cast<uint32_t*>(ws + L.counts);
+    T.sel = reinterpret_cast<int32_t*>(ws + L.sel);
     T.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
+    T.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = mla::launch_topk_clear(T, B, st);
     if (e != hipSuccess) return hip_status(e, "indexer_topk clear");

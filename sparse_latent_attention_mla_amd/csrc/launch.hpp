@@ -34,9 +34,13 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 struct TopkWorkspace {
     float* scores;          // [B, capacity] (used when the caller gives no score buffer)
     uint32_t* hist;         // [B, kHistBins]
-    uint32_t* counters;     // [B, 4]: selected, candidates, -, -
-    uint64_t* cand;         // [B, capacity] (key << 32 | ~position)
+    uint32_t* counts;       // [B, select workgroups, 2]: each workgroup's selected / candidate count
+    int32_t* sel;           // [B, capacity]: workgroup i's selected positions at i * kSelRowsHost ..
+    uint64_t* cand;         // [B, capacity]: workgroup i's candidates (key << 32 | ~position) likewise
+    uint64_t* cand2;        // [B, capacity]: all candidates of a sequence, contiguous
 };
+constexpr int kSelRowsHost = 2048;      // rows per select workgroup
+inline int64_t select_groups(int64_t capacity) { return (capacity + kSelRowsHost - 1) / kSelRowsHost; }
 
 struct ScanArgs {
     int fmt, dim;           // indexer row format

@@ -9,13 +9,25 @@
 //   2. k_select (many workgroups per sequence) finds the bin T holding the
 //      k-th largest key, and each workgroup compacts, in LDS, the rows of its
 //      slice that lie above T (selected) and in T (candidates, as 64-bit
-//      key << 32 | ~position), then reserves space for both lists with one
-//      global atomic each and copies them out;
-//   3. k_select_final (one workgroup per sequence) radix-selects the missing
-//      count among the candidates (the 52 free bits of the 64-bit composite,
-//      most significant digit first, so the smaller position wins a tie) and
-//      pads with -1.
+//      key << 32 | ~position) and writes both lists and their counts to its
+//      own slots (no global atomics: across XCDs they serialise);
+//   3. k_select_final (one workgroup per sequence) prefix-sums the counts,
+//      gathers the selected positions into the output and the candidates
+//      into one list, then radix-selects the missing
+//      count among the candidates, most significant digit first: two 10-bit
+//      digits fix the exact threshold score (the bin fixed the top 12 of its 32
+//      bits); only when more rows share that score than are still needed do
+//      four 8-bit digits of the inverted position follow, so the smaller
+//      position wins a tie. It then pads with -1. (A separate launch: handing
+//      the lists over inside one kernel needs a device-scope fence in every
+//      workgroup, which costs more than the launch.)
+// Sequences of up to kRowPathMax rows take a shorter path: one workgroup per
+// sequence reads every score, finds T, compacts and radix-selects in LDS, with
+// no hand-over between workgroups. (Longer sequences outgrow one CU's vector
+// throughput: classifying 128K scores alone takes it several microseconds.)
 // Output positions form an unordered set.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -23,193 +35,130 @@ namespace mla {
 
 namespace {
 
-constexpr int kSelThreads = 256;
-constexpr int kSelRows = 2048;            // rows per k_select workgroup
-constexpr int kFinalThreads = 1024;
-constexpr int kFinalLds = 7168;           // candidates kept in LDS (56 KB)
+constexpr int kSelThreads = 256;          // multi-workgroup path
+constexpr int kSelRows = kSelRowsHost;    // rows per k_select workgroup
+constexpr int kRowThreads = 1024;         // one workgroup per sequence
+constexpr int64_t kRowPathMax = 16384;    // longest sequence on the one-workgroup path
+constexpr int kFinalLds = 6144;           // candidates kept in LDS (48 KB)
+constexpr int kMaxDigitBins = 1024;
 
 __global__ void k_topk_clear(TopkWorkspace ws, int B) {
     const int b = blockIdx.x;
     for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) ws.hist[(int64_t)b * kHistBins + i] = 0u;
-    if (threadIdx.x < 4) ws.counters[b * 4 + threadIdx.x] = 0u;
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Inclusive prefix sum over the lanes of a wave.
+// Inclusive prefix sum over the lanes of a wave, on DPP: shifts by 1, 2, 4, 8 within
+// each row of 16 lanes, then row 0's (row 1's) last lane added to rows 1, 3 (2, 3).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t u = __shfl_up(v, o, 64);
-        if (lane >= o) v += u;
-    }
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
     return v;
 }
 
-// Suffix search over `nb` (<= 4 * 64) counts held one per thread, thread t holding
-// the count of rank t in DESCENDING order (t = 0 is the largest bin).  Finds the
-// rank r with  sum_{t<r} c_t < need <= sum_{t<=r} c_t  and the sum before it.
-// All threads of the workgroup must call it; threads >= nb pass c = 0.
-// Result in *rank (-1 if the total is below need) and *before.
-__device__ void find_rank(uint32_t c, uint32_t need, int* rank, uint32_t* before, uint32_t* wsum) {
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    uint32_t incl = (t < 256) ? wave_incl_scan(c) : 0u;
-    if (t < 256 && lane == 63) wsum[wv] = incl;
-    if (t == 0) *rank = -1;
-    __syncthreads();
-    if (t < 256) {
-        uint32_t off = 0;
-        for (int i = 0; i < wv; ++i) off += wsum[i];
-        incl += off;
-        const uint32_t excl = incl - c;
-        if (excl < need && incl >= need) { *rank = t; *before = excl; }
-    }
-    __syncthreads();
-}
-
-// Threshold bin of sequence b: the bin T holding the k-th largest key and the
-// number of keys above it.  T = -1 when every visible row fits in k.
-__device__ void find_threshold(const uint32_t* __restrict__ hist, int k, int* T_out, uint32_t* above_out) {
-    __shared__ uint32_t wsum[4];
-    __shared__ int rank_s;
-    __shared__ uint32_t before_s;
-    __shared__ int T_s;
-    __shared__ uint32_t above_s;
-    const int t = threadIdx.x;                       // kSelThreads == 256
-    constexpr int per = kHistBins / kSelThreads;     // 16 bins per thread, top bins first
-    const int hi = kHistBins - 1 - t * per;
-    uint32_t cnt[per];
+// Digit search by one wave over counts h[0 .. nbins) (nbins a multiple of 64, at most
+// 4096; global or LDS): lane l sums the bins nbins-1-l*per .. nbins-(l+1)*per (largest
+// first). Finds d with sum_{e>d} h[e] < need <= sum_{e>=d} h[e]; found = false when the
+// total is below need. Results are uniform across the wave.
+struct DigitResult {
+    int digit;
+    uint32_t above, count;
+    bool found;
+};
+template <typename P>
+__device__ __forceinline__ DigitResult wave_find_digit(P h, int nbins, uint32_t need) {
+    const int lane = threadIdx.x & 63;
+    const int per = nbins >> 6;
+    const int lo = nbins - (lane + 1) * per;              // the lane's bins lo .. lo + per - 1
     uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) { cnt[i] = hist[hi - i]; sum += cnt[i]; }
-    find_rank(sum, (uint32_t)k, &rank_s, &before_s, wsum);
-    if (t == 0) { T_s = -1; above_s = 0; }
-    __syncthreads();
-    if (t == rank_s) {
-        uint32_t run = before_s;
-#pragma unroll
-        for (int i = 0; i < per; ++i) {
-            if (run + cnt[i] >= (uint32_t)k) { T_s = hi - i; above_s = run; break; }
-            run += cnt[i];
+    for (int i = 0; i < per; i += 4) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(&h[lo + i]);
+        sum += q.x + q.y + q.z + q.w;
+    }
+    const uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
+    const uint64_t hit = __ballot(excl < need && incl >= need);
+    DigitResult r{0, 0u, 0u, hit != 0};
+    if (!r.found) return r;
+    const int src = __builtin_ctzll(hit);
+    int d = 0;
+    uint32_t above = 0, cnt = 0;
+    if (lane == src) {
+        uint32_t run = excl;
+        for (int i = per - 1; i >= 0; --i) {
+            const uint32_t c = h[lo + i];
+            if (run + c >= need) { d = lo + i; above = run; cnt = c; break; }
+            run += c;
         }
     }
-    __syncthreads();
-    *T_out = T_s;
-    *above_out = above_s;
+    r.digit = __builtin_amdgcn_readlane(d, src);
+    r.above = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
+    r.count = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
+    return r;
 }
 
-__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores, int64_t capacity,
-                                                        const int32_t* __restrict__ n_visible, int k,
-                                                        TopkWorkspace ws, int32_t* __restrict__ out_idx) {
-    __shared__ int32_t sel[kSelRows];
-    __shared__ uint64_t cnd[kSelRows];
-    __shared__ uint32_t n_sel, n_cnd, base_sel, base_cnd;
-    const int b = blockIdx.y;
+// Among the candidates c[0 .. ncand) (64-bit key << 32 | ~position, all in one
+// top-12-bit bin), append the positions of the `need` largest to out from the LDS
+// cursor on (entries at or past `want` are not written). Two 10-bit digits fix the
+// exact threshold score; only when more candidates share it than are still
+// needed do four 8-bit digits of the inverted position follow. h: two LDS
+// histograms of kMaxDigitBins, the first zero on entry; res: 4 LDS words.
+template <int NT, typename P>
+__device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, int32_t* __restrict__ out,
+                           uint32_t* cursor, uint32_t (*h)[kMaxDigitBins], uint32_t* res) {
     const int t = threadIdx.x, lane = t & 63;
-    int T;
-    uint32_t above;
-    find_threshold(ws.hist + (int64_t)b * kHistBins, k, &T, &above);
-    const int64_t nvis = clamp_visible(n_visible[b], capacity);
-    const int64_t r0 = (int64_t)blockIdx.x * kSelRows;
-    if (t == 0) { n_sel = 0; n_cnd = 0; }
-    __syncthreads();
-    const float* sc = scores + b * capacity;
-    for (int i = 0; i < kSelRows / kSelThreads; ++i) {
-        const int64_t s = r0 + i * kSelThreads + t;
-        const bool in = s < nvis;
-        uint32_t key = 0, bin = 0;
-        if (in) {
-            key = score_key(sc[s]);
-            bin = key >> (32 - kHistBits);
-        }
-        const bool take = in && (T < 0 || (int)bin > T);
-        const bool maybe = in && T >= 0 && (int)bin == T;
-        const uint64_t mt = __ballot(take), mc = __ballot(maybe);
-        uint32_t bt = 0, bc = 0;
-        if (lane == 0) {
-            if (mt) bt = atomicAdd(&n_sel, (uint32_t)__popcll(mt));
-            if (mc) bc = atomicAdd(&n_cnd, (uint32_t)__popcll(mc));
-        }
-        bt = __shfl(bt, 0, 64);
-        bc = __shfl(bc, 0, 64);
-        if (take) sel[bt + lanes_below(mt)] = (int32_t)s;
-        if (maybe) cnd[bc + lanes_below(mc)] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)s);
-    }
-    __syncthreads();
-    if (t == 0) {
-        base_sel = n_sel ? atomicAdd(&ws.counters[b * 4 + 0], n_sel) : 0u;
-        base_cnd = n_cnd ? atomicAdd(&ws.counters[b * 4 + 1], n_cnd) : 0u;
-    }
-    __syncthreads();
-    int32_t* out = out_idx + (int64_t)b * k;
-    for (uint32_t i = t; i < n_sel; i += kSelThreads)
-        if (base_sel + i < (uint32_t)k) out[base_sel + i] = sel[i];
-    uint64_t* cand = ws.cand + b * capacity;
-    for (uint32_t i = t; i < n_cnd; i += kSelThreads)
-        if (base_cnd + i < (uint64_t)capacity) cand[base_cnd + i] = cnd[i];
-}
-
-// One workgroup per sequence.
-__global__ __launch_bounds__(kFinalThreads) void k_select_final(const int32_t* __restrict__ n_visible, int k,
-                                                               int64_t capacity, TopkWorkspace ws,
-                                                               int32_t* __restrict__ out_idx) {
-    __shared__ uint64_t lc[kFinalLds];
-    __shared__ uint32_t h256[256];
-    __shared__ uint32_t wsum[4];
-    __shared__ int rank_s;
-    __shared__ uint32_t before_s;
-    __shared__ uint32_t cursor;
-    const int b = blockIdx.x;
-    const int t = threadIdx.x, lane = t & 63;
-    const int64_t nvis = clamp_visible(n_visible[b], capacity);
-    const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    const uint32_t nsel = ws.counters[b * 4 + 0];
-    uint32_t ncand = ws.counters[b * 4 + 1];
-    if (ncand > (uint64_t)capacity) ncand = (uint32_t)capacity;
-    int32_t* out = out_idx + (int64_t)b * k;
-    const uint64_t* gcand = ws.cand + b * capacity;
-    const uint32_t need = (want > nsel) ? want - nsel : 0u;
-
-    const bool in_lds = ncand <= (uint32_t)kFinalLds;
-    if (in_lds)
-        for (uint32_t i = t; i < ncand; i += kFinalThreads) lc[i] = gcand[i];
-    if (t == 0) cursor = nsel;
-    __syncthreads();
-    const uint64_t* c = in_lds ? lc : gcand;
-
-    // the need-th largest 64-bit composite; bits 63..52 (the bin) are equal
     const bool radix = need > 0 && need < ncand;
-    constexpr uint64_t kBinBits = 0xFFFull << 52;    // shared by every candidate (the threshold bin)
-    uint64_t prefix = radix ? (c[0] & kBinBits) : 0ull, mask = kBinBits;
+    uint64_t prefix = radix ? (c[0] & (0xFFFull << 52)) : 0ull, mask = 0xFFFull << 52;
     uint32_t rem = need;
-    if (radix) {
-        // digit windows 44..51, 36..43, .., 4..11, then 0..7 (bits 4..7 already fixed);
-        // computed, not tabled: a constant table would be read from the code object
-        for (int p = 0; p < 7; ++p) {
-            const int shift = (p < 6) ? 44 - 8 * p : 0;
-            if (t < 256) h256[t] = 0u;
-            __syncthreads();
-            for (uint32_t i = t; i < ncand; i += kFinalThreads) {
-                const uint64_t v = c[i];
-                if ((v & mask) == prefix) atomicAdd(&h256[(v >> shift) & 255u], 1u);
+    int par = 0;
+    auto pass = [&](int shift, int bits) {
+        const int nb = 1 << bits;
+        uint32_t* hc = h[par];
+        for (uint32_t i = t; i < ncand; i += NT) {
+            const uint64_t v = c[i];
+            if ((v & mask) == prefix) atomicAdd(&hc[(v >> shift) & (uint64_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        if (t < 64) {                                    // one wave finds the digit
+            const DigitResult r = wave_find_digit(hc, nb, rem);
+            if (lane == 0) {
+                res[0] = (uint32_t)r.digit;
+                res[1] = r.above;
+                res[2] = r.count;
             }
-            __syncthreads();
-            // descending digit order: thread t holds digit 255 - t
-            find_rank(t < 256 ? h256[255 - t] : 0u, rem, &rank_s, &before_s, wsum);
-            const int d = 255 - (rank_s < 0 ? 0 : rank_s);
-            prefix |= (uint64_t)d << shift;
-            mask |= (uint64_t)255u << shift;
-            rem -= before_s;
+        } else {                                         // the others clear the next histogram
+            for (int i = t - 64; i < kMaxDigitBins; i += NT - 64) h[par ^ 1][i] = 0u;
+        }
+        __syncthreads();
+        const int d = (int)res[0];
+        prefix |= (uint64_t)d << shift;
+        mask |= (uint64_t)(nb - 1) << shift;
+        rem -= res[1];
+        par ^= 1;
+        return res[2];                                   // candidates sharing the prefix so far
+    };
+    if (radix) {
+        pass(42, 10);
+        const uint32_t eq = pass(32, 10);                // prefix now holds the exact threshold score
+        if (rem < eq) {                                  // ties at that score: smaller positions first
+            pass(24, 8);
+            pass(16, 8);
+            pass(8, 8);
+            pass(0, 8);
         }
     }
-    // composites are unique (positions are): "v >= the need-th largest" is exactly `need` of them
+    // "v >= prefix" takes exactly `need`: every candidate above the threshold score,
+    // and at it either all (score resolved, count fits) or those above the exact composite
     if (need > 0) {
-        const uint32_t n_iter = (ncand + kFinalThreads - 1) / kFinalThreads;
+        const uint32_t n_iter = (ncand + NT - 1) / NT;
         for (uint32_t it = 0; it < n_iter; ++it) {
-            const uint32_t i = it * kFinalThreads + t;
+            const uint32_t i = it * NT + t;
             bool take = false;
             int32_t pos = 0;
             if (i < ncand) {
@@ -219,7 +168,7 @@ __global__ __launch_bounds__(kFinalThreads) void k_select_final(const int32_t* _
             }
             const uint64_t m = __ballot(take);
             uint32_t base = 0;
-            if (lane == 0 && m) base = atomicAdd(&cursor, (uint32_t)__popcll(m));
+            if (lane == 0 && m) base = atomicAdd(cursor, (uint32_t)__popcll(m));
             base = __shfl(base, 0, 64);
             if (take) {
                 const uint32_t o = base + lanes_below(m);
@@ -227,8 +176,344 @@ __global__ __launch_bounds__(kFinalThreads) void k_select_final(const int32_t* _
             }
         }
     }
+}
+
+struct FinalLds {
+    uint64_t lc[kFinalLds];
+    uint32_t h[2][kMaxDigitBins];
+    uint32_t res[4];
+};
+
+// Radix-take over the candidates in LDS (the common case) or in the global list.
+template <int NT>
+__device__ __forceinline__ void radix_take_any(FinalLds& L, const uint64_t* gc2, uint32_t ncand, uint32_t need,
+                                               uint32_t want, int32_t* __restrict__ out, uint32_t* cursor) {
+    if (ncand <= (uint32_t)kFinalLds) radix_take<NT>(L.lc, ncand, need, want, out, cursor, L.h, L.res);
+    else radix_take<NT>(gc2, ncand, need, want, out, cursor, L.h, L.res);
+}
+
+// Classify one score: above the threshold bin T (take), in it (maybe).
+__device__ __forceinline__ void classify(float v, bool in, int T, uint32_t* key, bool* take, bool* maybe) {
+    uint32_t kk = 0, bin = 0;
+    if (in) {
+        kk = score_key(v);
+        bin = kk >> (32 - kHistBits);
+    }
+    *key = kk;
+    *take = in && (T < 0 || (int)bin > T);
+    *maybe = in && T >= 0 && (int)bin == T;
+}
+
+// ---- one workgroup per sequence ------------------------------------------
+__global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ scores, int64_t capacity,
+                                                          const int32_t* __restrict__ n_visible, int k,
+                                                          TopkWorkspace ws, int32_t* __restrict__ out_idx) {
+    __shared__ FinalLds L;
+    __shared__ uint32_t n_sel, n_cnd, cursor;
+    __shared__ int T_s;
+    constexpr int kR = 16;                               // scores per thread per round
+    constexpr int kRound = kRowThreads * kR;
+    const int b = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63;
+    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
+    int32_t* out = out_idx + (int64_t)b * k;
+    uint64_t* gc2 = ws.cand2 + b * capacity;
+    const float* __restrict__ sc = scores + b * capacity;
+    float v[kR];
+    auto load = [&](int64_t r0, float* d) {
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t s = r0 + u * kRowThreads + t;
+            d[u] = (s < nvis) ? sc[s] : 0.0f;
+        }
+    };
+    load(0, v);                                          // in flight during the threshold search
+    if (t < 64) {
+        const DigitResult r = wave_find_digit(ws.hist + (int64_t)b * kHistBins, kHistBins, (uint32_t)k);
+        if (t == 0) {
+            T_s = r.found ? r.digit : -1;                // -1: every visible row fits in k
+            n_sel = 0;
+            n_cnd = 0;
+        }
+    }
+    for (int i = t; i < kMaxDigitBins; i += kRowThreads) L.h[0][i] = 0u;
     __syncthreads();
-    for (uint32_t i = want + t; i < (uint32_t)k; i += kFinalThreads) out[i] = -1;
+    const int T = T_s;
+    for (int64_t r0 = 0; r0 < nvis; r0 += kRound) {
+        float vn[kR];
+        if (r0 + kRound < nvis) load(r0 + kRound, vn);
+        // classify the round, then one LDS reservation per wave and list
+        uint32_t key[kR];
+        uint64_t mt[kR], mc[kR];
+        uint32_t nt = 0, nc = 0;
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t s = r0 + u * kRowThreads + t;
+            bool take, maybe;
+            classify(v[u], s < nvis, T, &key[u], &take, &maybe);
+            mt[u] = __ballot(take);
+            mc[u] = __ballot(maybe);
+            nt += (uint32_t)__popcll(mt[u]);
+            nc += (uint32_t)__popcll(mc[u]);
+        }
+        if (nt | nc) {
+            uint32_t bt = 0, bc = 0;
+            if (lane == 0) {
+                if (nt) bt = atomicAdd(&n_sel, nt);
+                if (nc) bc = atomicAdd(&n_cnd, nc);
+            }
+            bt = __shfl(bt, 0, 64);
+            bc = __shfl(bc, 0, 64);
+#pragma unroll
+            for (int u = 0; u < kR; ++u) {
+                const int64_t s = r0 + u * kRowThreads + t;
+                if ((mt[u] >> lane) & 1u) {
+                    const uint32_t o = bt + lanes_below(mt[u]);
+                    if (o < (uint32_t)k) out[o] = (int32_t)s;
+                }
+                if ((mc[u] >> lane) & 1u) {
+                    const uint32_t o = bc + lanes_below(mc[u]);
+                    const uint64_t cv = ((uint64_t)key[u] << 32) | (uint64_t)(~(uint32_t)s);
+                    if (o < (uint32_t)kFinalLds) L.lc[o] = cv;
+                    else gc2[o] = cv;                    // o < capacity: one entry per row
+                }
+                bt += (uint32_t)__popcll(mt[u]);
+                bc += (uint32_t)__popcll(mc[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kR; ++u) v[u] = vn[u];
+    }
+    __syncthreads();
+    const uint32_t nsel = n_sel, ncand = n_cnd;
+    if (ncand > (uint32_t)kFinalLds)                     // the radix passes then read one contiguous list
+        for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kRowThreads) gc2[i] = L.lc[i];
+    __threadfence_block();
+    if (t == 0) cursor = nsel;
+    __syncthreads();
+    const uint32_t need = (want > nsel) ? want - nsel : 0u;
+    radix_take_any<kRowThreads>(L, gc2, ncand, need, want, out, &cursor);
+    __syncthreads();
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kRowThreads) out[i] = -1;
+}
+
+// ---- many workgroups per sequence ------------------------------------------
+__global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores, int64_t capacity,
+                                                        const int32_t* __restrict__ n_visible, int k,
+                                                        TopkWorkspace ws) {
+    __shared__ uint64_t cnd[kSelRows];
+    __shared__ int32_t sel[kSelRows];
+    __shared__ uint32_t n_sel, n_cnd;
+    __shared__ int T_s;
+    const int b = blockIdx.y;
+    const int t = threadIdx.x, lane = t & 63;
+    constexpr int kPer = kSelRows / kSelThreads;
+    // the slice's scores are loaded before the threshold search, so both latencies overlap
+    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const int64_t r0 = (int64_t)blockIdx.x * kSelRows;
+    const float* sc = scores + b * capacity;
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t s = r0 + i * kSelThreads + t;
+        v[i] = (s < nvis) ? sc[s] : 0.0f;
+    }
+    if (t < 64) {
+        const DigitResult r = wave_find_digit(ws.hist + (int64_t)b * kHistBins, kHistBins, (uint32_t)k);
+        if (t == 0) {
+            T_s = r.found ? r.digit : -1;
+            n_sel = 0;
+            n_cnd = 0;
+        }
+    }
+    __syncthreads();
+    const int T = T_s;
+    uint32_t key[kPer];
+    uint64_t mt[kPer], mc[kPer];
+    uint32_t nt = 0, nc = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t s = r0 + i * kSelThreads + t;
+        bool take, maybe;
+        classify(v[i], s < nvis, T, &key[i], &take, &maybe);
+        mt[i] = __ballot(take);
+        mc[i] = __ballot(maybe);
+        nt += (uint32_t)__popcll(mt[i]);
+        nc += (uint32_t)__popcll(mc[i]);
+    }
+    if (nt | nc) {                                       // one LDS reservation per wave and list
+        uint32_t bt = 0, bc = 0;
+        if (lane == 0) {
+            if (nt) bt = atomicAdd(&n_sel, nt);
+            if (nc) bc = atomicAdd(&n_cnd, nc);
+        }
+        bt = __shfl(bt, 0, 64);
+        bc = __shfl(bc, 0, 64);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int64_t s = r0 + i * kSelThreads + t;
+            if ((mt[i] >> lane) & 1u) sel[bt + lanes_below(mt[i])] = (int32_t)s;
+            if ((mc[i] >> lane) & 1u) cnd[bc + lanes_below(mc[i])] = ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)s);
+            bt += (uint32_t)__popcll(mt[i]);
+            bc += (uint32_t)__popcll(mc[i]);
+        }
+    }
+    __syncthreads();
+    // the workgroup's own slots: counts, then its lists at r0 (at most kSelRows rows each)
+    if (t == 0) {
+        uint32_t* cnt = ws.counts + ((int64_t)b * gridDim.x + blockIdx.x) * 2;
+        cnt[0] = n_sel;
+        cnt[1] = n_cnd;
+    }
+    int32_t* gsel = ws.sel + b * capacity + r0;
+    uint64_t* gcnd = ws.cand + b * capacity + r0;
+    for (uint32_t i = t; i < n_sel; i += kSelThreads) gsel[i] = sel[i];
+    for (uint32_t i = t; i < n_cnd; i += kSelThreads) gcnd[i] = cnd[i];
+}
+
+// Inclusive prefix sum over the kSelThreads threads of the workgroup (all call it).
+__device__ uint32_t block_incl_scan(uint32_t v, uint32_t* total) {
+    __shared__ uint32_t wsum[kSelThreads / 64];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    uint32_t incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+    for (int i = 0; i < kSelThreads / 64; ++i) {
+        off += (i < wv) ? wsum[i] : 0u;
+        tot += wsum[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return incl + off;
+}
+
+// One workgroup per sequence, after every k_select workgroup of it: prefix-sum the
+// counts, gather the selected positions into the output and the candidates into
+// one list, radix-select among the candidates, pad with -1.
+__global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __restrict__ n_visible, int k,
+                                                              int64_t capacity, int groups, TopkWorkspace ws,
+                                                              int32_t* __restrict__ out_idx) {
+    __shared__ FinalLds L;
+    __shared__ uint32_t cursor;
+    __shared__ uint32_t ex_s[kSelThreads], ex_c[kSelThreads], cnt_s[kSelThreads], cnt_c[kSelThreads];
+    const int b = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63;
+    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
+    int32_t* out = out_idx + (int64_t)b * k;
+    uint64_t* gc2 = ws.cand2 + b * capacity;
+
+    uint32_t nsel = 0, ncand = 0;
+    constexpr int kGU = 16;
+    const int wv = t >> 6;
+    for (int g0 = 0; g0 < groups; g0 += kSelThreads) {
+        const int gi = g0 + t;
+        const int nbatch = (groups - g0 < kSelThreads) ? groups - g0 : kSelThreads;
+        const int32_t* __restrict__ gsel = ws.sel + b * capacity + (int64_t)g0 * kSelRows;
+        const uint64_t* __restrict__ gcnd = ws.cand + b * capacity + (int64_t)g0 * kSelRows;
+        // the first 64 entries of 16 workgroups' lists per wave are loaded together with the
+        // counts (whatever the counts turn out to be: the slots exist, stale entries are dropped)
+        int32_t vs[kGU];
+        uint64_t vc[kGU];
+        const int64_t room = capacity - (int64_t)g0 * kSelRows;   // entries left in this batch's slots
+#pragma unroll
+        for (int u = 0; u < kGU; ++u) {
+            const int j = wv + 4 * u;
+            const int64_t off = (int64_t)j * kSelRows + lane;
+            const bool ok = j < nbatch && off < room;
+            vs[u] = ok ? gsel[off] : 0;
+            vc[u] = ok ? gcnd[off] : 0ull;
+        }
+        uint32_t cs = 0, cc = 0;
+        if (gi < groups) {
+            const uint32_t* cnt = ws.counts + ((int64_t)b * groups + gi) * 2;
+            cs = cnt[0];
+            cc = cnt[1];
+        }
+        uint32_t ts, tc;
+        const uint32_t is = block_incl_scan(cs, &ts);
+        const uint32_t ic = block_incl_scan(cc, &tc);
+        ex_s[t] = is - cs;
+        ex_c[t] = ic - cc;
+        cnt_s[t] = cs;
+        cnt_c[t] = cc;
+        __syncthreads();
+        // wave w places the lists of workgroups w, w + 4, ..: the first 64 entries of
+        // workgroups w .. w + 60 were loaded above, later rounds load theirs here
+        for (int jb = wv; jb < nbatch; jb += 4 * kGU) {
+            if (jb != wv) {
+#pragma unroll
+                for (int u = 0; u < kGU; ++u) {
+                    const int j = jb + 4 * u;
+                    const uint32_t ns = (j < nbatch) ? cnt_s[j] : 0u, nc = (j < nbatch) ? cnt_c[j] : 0u;
+                    vs[u] = ((uint32_t)lane < ns) ? gsel[(int64_t)j * kSelRows + lane] : 0;
+                    vc[u] = ((uint32_t)lane < nc) ? gcnd[(int64_t)j * kSelRows + lane] : 0ull;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kGU; ++u) {
+                const int j = jb + 4 * u;
+                if (j >= nbatch) break;
+                if ((uint32_t)lane < cnt_s[j]) {
+                    const uint32_t o = nsel + ex_s[j] + lane;
+                    if (o < (uint32_t)k) out[o] = vs[u];
+                }
+                if ((uint32_t)lane < cnt_c[j]) {
+                    const uint32_t o = ncand + ex_c[j] + lane;
+                    if (o < (uint32_t)kFinalLds) L.lc[o] = vc[u];
+                    else gc2[o] = vc[u];          // o < capacity: every row is in at most one list
+                }
+            }
+        }
+        // entries past the first 64 of a workgroup's list (concentrated selections)
+        const bool long_lists = __syncthreads_or(cs > 64u || cc > 64u);
+        for (int j = wv; long_lists && j < nbatch; j += 4) {
+            const uint32_t ns = cnt_s[j], nc = cnt_c[j];
+            for (uint32_t i0 = 64; i0 < ns; i0 += 64 * 8) {
+                int32_t vv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + 64 * u + lane;
+                    vv[u] = (i < ns) ? gsel[(int64_t)j * kSelRows + i] : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + 64 * u + lane, o = nsel + ex_s[j] + i;
+                    if (i < ns && o < (uint32_t)k) out[o] = vv[u];
+                }
+            }
+            for (uint32_t i0 = 64; i0 < nc; i0 += 64 * 8) {
+                uint64_t vv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + 64 * u + lane;
+                    vv[u] = (i < nc) ? gcnd[(int64_t)j * kSelRows + i] : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + 64 * u + lane, o = ncand + ex_c[j] + i;
+                    if (i >= nc) continue;
+                    if (o < (uint32_t)kFinalLds) L.lc[o] = vv[u];
+                    else gc2[o] = vv[u];
+                }
+            }
+        }
+        nsel += ts;
+        ncand += tc;
+        __syncthreads();
+    }
+    if (ncand > (uint32_t)kFinalLds)                     // the radix passes then read one contiguous list
+        for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kSelThreads) gc2[i] = L.lc[i];
+    __threadfence_block();
+    if (t == 0) cursor = nsel;
+    for (int i = t; i < kMaxDigitBins; i += kSelThreads) L.h[0][i] = 0u;
+    __syncthreads();
+    const uint32_t need = (want > nsel) ? want - nsel : 0u;
+    radix_take_any<kSelThreads>(L, gc2, ncand, need, want, out, &cursor);
+    __syncthreads();
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out[i] = -1;
 }
 
 }  // namespace
@@ -239,17 +524,25 @@ hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream)
     return hipGetLastError();
 }
 
+// MLA_TOPK_PATH=row|multi forces a path (for tuning).
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                          const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream) {
     if (B == 0 || k == 0) return hipSuccess;
+    bool row = capacity <= kRowPathMax;
+    if (const char* e = getenv("MLA_TOPK_PATH")) row = (e[0] == 'r');
+    if (row) {
+        hipLaunchKernelGGL(k_topk_row, dim3(B), dim3(kRowThreads), 0, stream, scores, capacity, n_visible, k, ws,
+                           out_idx);
+        return hipGetLastError();
+    }
     const unsigned nx = (unsigned)((capacity + kSelRows - 1) / kSelRows);
     if (nx > 0) {
         hipLaunchKernelGGL(k_select, dim3(nx, B), dim3(kSelThreads), 0, stream, scores, capacity, n_visible, k,
-                           ws, out_idx);
+                           ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_select_final, dim3(B), dim3(kFinalThreads), 0, stream, n_visible, k, capacity, ws,
+    hipLaunchKernelGGL(k_select_final, dim3(B), dim3(kSelThreads), 0, stream, n_visible, k, capacity, (int)nx, ws,
                        out_idx);
     return hipGetLastError();
 }

@@ -187,6 +187,53 @@ def test_decode_head_counts(name, H):
     G.check_attention(got_o, got_l, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("path", ["row", "multi"])
+@pytest.mark.parametrize("fmt", [G.O.E4M3_S128, G.O.E2M1_S16, G.O.BF16])
+@pytest.mark.parametrize("k", [1, 37, 2048])
+def test_topk_exact_ties(fmt, k, path, monkeypatch):
+    """Scores that are exact integers on both sides: integer queries and weights, and
+    rows whose values the format holds exactly with unit block scales (a 448 in each
+    E4M3 block of 128, a 6 in each E2M1 group of 16). Rows repeat, so many share a
+    score; the selected set must equal the oracle's exactly, the smaller position
+    winning each tie, and the scores must agree bit for bit. Both selection paths:
+    one workgroup per sequence, and many with a separate final step."""
+    monkeypatch.setenv("MLA_TOPK_PATH", path)
+    rng = np.random.default_rng(1000 + 10 * fmt + k)
+    B, N, d, H_I = 2, 5003, 128, 64
+    distinct = rng.choice(np.array([-3, -2, -1, 0, 1, 2, 3], np.float32), (B, 997, d))
+    if fmt == G.O.E4M3_S128:
+        distinct[:, :, 5] = 448.0
+    elif fmt == G.O.E2M1_S16:
+        distinct[:, :, ::16] = 6.0
+    rows = np.ascontiguousarray(distinct[:, np.arange(N) % 997])          # each row repeats ~5 times
+    q_idx = rng.choice(np.array([-1, 0, 1], np.float32), (B, H_I, d))
+    w = rng.choice(np.array([1, 2], np.float32), (B, H_I))
+    nv = np.array([N, N - 1234], np.int32)
+    row = (fmt, d, 0)
+    rb = G.O.row_bytes(fmt, d, 0)
+    slots = np.tile(np.arange(N, dtype=np.int32), (B, 1))
+    o_cache = np.zeros((B, N, rb), np.uint8)
+    G.O.append(row, row, None, rows, slots, None, o_cache)
+    ref_s = G.O.indexer_scores(row, q_idx, w, 1.0, o_cache, nv)
+    ref_i = G.O.topk(ref_s, nv, k)
+    g_cache = torch.zeros((B, N, rb), dtype=torch.uint8, device="cuda")
+    G.M.mla_kv_append_quant(G.M.Row(fmt, d, 0), G.M.Row(fmt, d, 0), None, G._t(rows), G._t(slots), None, g_cache)
+    out_idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out_s = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(G.M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device="cuda")
+    say("topk ties", fmt, k, path)
+    G.M.mla_indexer_topk(G.M.Row(fmt, d, 0), G._t(q_idx, torch.bfloat16), G._t(w), 1.0, g_cache, G._t(nv), k,
+                         out_idx, ws, out_scores=out_s)
+    torch.cuda.synchronize()
+    got_s, got_i = out_s.cpu().numpy(), out_idx.cpu().numpy()
+    for b in range(B):
+        n = int(nv[b])
+        assert np.array_equal(got_s[b, :n], ref_s[b, :n]), f"row {b}: scores differ"
+        assert np.all(np.isneginf(got_s[b, n:]))
+        assert len(np.unique(ref_s[b, :n])) < n // 4                 # the case really is full of ties
+        assert np.array_equal(np.sort(got_i[b]), np.sort(ref_i[b])), f"row {b}: selected sets differ"
+
+
 def test_quantise_bitexact_over_magnitudes():
     """Rows spanning 12 decades, exact zeros, signed zeros, tiny subnormal-range
     values and block maxima sitting on format boundaries, in every format."""

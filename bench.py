@@ -15,6 +15,7 @@ caches.
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -37,6 +38,8 @@ def parse():
     p.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--layers", type=int, default=8, help="distinct layer caches rotated")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="time only torch's device copy of a known size (scales HBM byte counters)")
     return p.parse_args()
 
 
@@ -114,12 +117,82 @@ def build_layers(cfg, n_layers, seed=0):
     return layers
 
 
+KERNELS = ("kv_append", "indexer_scan", "topk_select", "decode", "decode_merge")
+SCAN_SOURCES = ("csrc/indexer.hip", "csrc/common.hpp", "csrc/launch.hpp", "build.py")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_c3_hbm_traffic.md")
+
+
+def scan_source_digest():
+    """sha256 over the sources the indexer scan kernel is compiled from."""
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        with open(os.path.join(ROOT, "sparse_latent_attention_mla_amd", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def scan_traffic(cfg):
+    """HBM bytes per scan launch from the committed counter summary: FETCH_SIZE +
+    WRITE_SIZE per dispatch, each scaled by what the counter reads for a plain copy
+    of known size.  None when the summary is absent, is for another workload, or
+    was taken from a different version of the kernel's sources."""
+    if cfg.name != "c3" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("    ") and "=" in line:
+                key, val = line.strip().split("=", 1)
+                kv[key.strip()] = val.strip()
+    try:
+        if kv["scan_source_sha256"] != scan_source_digest():
+            return None
+        fetch = float(kv["scan_fetch_kib"]) * 1024 * float(kv["fetch_factor"])
+        write = float(kv["scan_write_kib"]) * 1024 * float(kv["write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+def calibrate_copy(args):
+    """Copies of a known size, for scaling the HBM byte counters: each launch must
+    read and write exactly COPY_BYTES.  Two kernels: the runtime's device-to-device
+    copy (what torch's copy_ issues) and torch's elementwise negation into another
+    buffer, a copy-shaped kernel of the ordinary kind."""
+    import torch
+    torch.cuda.set_device(0)
+    n = COPY_BYTES // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    res = {"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES}
+    for name, fn in (("copy_", lambda: dst.copy_(src)), ("neg", lambda: torch.neg(src, out=dst))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / args.steps
+        res[name] = {"avg_us": us, "gbps_read_plus_write": 2 * COPY_BYTES / (us * 1e-6) / 1e9}
+    print(json.dumps(res), flush=True)
+
+
+COPY_BYTES = 1 << 30
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: the decode path runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return
     import numpy as np
     import torch
 
@@ -151,63 +224,62 @@ def main():
                          device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(X, ev=None):
-        """One layer-step (or CSA2 group) on layer caches X.  ev: 4 events bracketing
-        append / indexer / decode of the first layer of the step."""
+    def step(X):
+        """One layer-step (or CSA2 group) on layer caches X."""
         j = 0
         latest = None
         for l, mode in enumerate(cfg.layers):
             first = l == 0
-            if ev is not None and first:
-                ev[0].record(stream)
             M.mla_kv_append_quant(mr, ir, X.new_main if first else None, X.new_idx if first else None,
                                   slots if first else None, X.main if first else None, X.idx if first else None,
                                   X.new_win[l] if cfg.W else None, win_pos if cfg.W else None,
                                   X.win[l] if cfg.W else None)
-            if ev is not None and first:
-                ev[1].record(stream)
             if mode in ("full", "reindex"):
                 latest = idx_out[j % 2]
                 M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk)
                 j += 1
-            if ev is not None and first:
-                ev[2].record(stream)
             M.mla_sparse_decode(mr, cfg.d_v, X.q[l], X.main, latest, cfg.softmax_scale, out, lse, ws_dec,
                                 X.win[l] if cfg.W else None, win_len if cfg.W else None)
-            if ev is not None and first:
-                ev[3].record(stream)
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(layers[i % n_layers])
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: exactly K steps.  The library records an event pair on the launch
+    # stream around each of its kernels (mla_profile_*), so the per-kernel times are
+    # those of the timed steps themselves.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    for name in KERNELS:
+        M.mla_profile_read(name)          # discard anything recorded before
+    M.mla_profile_enable(True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(layers[i % n_layers], evs[i])
+        step(layers[i % n_layers])
     t_end.record(stream)
     torch.cuda.synchronize()
+    M.mla_profile_enable(False)
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    per_call = {
-        "append": statistics.mean(e[0].elapsed_time(e[1]) for e in evs) * 1e3,
-        "indexer_topk": statistics.mean(e[1].elapsed_time(e[2]) for e in evs) * 1e3,
-        "sparse_decode": statistics.mean(e[2].elapsed_time(e[3]) for e in evs) * 1e3,
-    }
-    log(f"{ms_per_step * 1e3:.2f} us/step; per call (us): " + ", ".join(f"{k}={v:.2f}" for k, v in per_call.items()))
+    per_kernel = {}
+    for name in KERNELS:
+        n, ms = M.mla_profile_read(name)
+        if n:
+            per_kernel[name] = {"launches": n, "avg_us": ms * 1e3 / n, "us_per_step": ms * 1e3 / args.steps}
+    log(f"{ms_per_step * 1e3:.2f} us/step; per kernel (avg us): " +
+        ", ".join(f"{k}={v['avg_us']:.2f}" for k, v in per_kernel.items()))
 
     ab = WL.algorithmic_bytes(cfg)
     step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
-    # dominant call: the indexer (scan of every visible indexer row + top-k); for the
-    # CSA2 group the timed bracket covers its first (Full) layer
+    # dominant kernel: the indexer scan.  Per launch it must read every visible
+    # indexer row of the batch plus the indexer queries and head weights; the
+    # scores it writes for the selection are implementation traffic, not counted.
     n_idx_layers = WL.n_indexers(cfg)
-    idx_bytes = (ab["scan"] + ab["q_idx_w"]) // n_idx_layers + B * k * 4
-    idx_gbps = idx_bytes / (per_call["indexer_topk"] * 1e-6) / 1e9
+    scan_bytes = (ab["scan"] + ab["q_idx_w"]) // n_idx_layers
+    scan_us = per_kernel["indexer_scan"]["avg_us"]
+    scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,
@@ -229,22 +301,22 @@ def main():
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "mla_indexer_topk (indexer scan + top-k select)",
+            "kernel": "indexer scan (k_scan_staged)",
             "bound": "hbm",
-            "achieved": idx_gbps,
+            "achieved": scan_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": idx_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
-            "algorithmic_bytes_per_launch": idx_bytes,
-            "avg_launch_us": per_call["indexer_topk"],
+            "frac": scan_gbps / HBM_PEAK_GBPS,
+            "traffic": scan_traffic(cfg),
+            "algorithmic_bytes_per_launch": scan_bytes,
+            "avg_launch_us": scan_us,
         },
         "step_roofline": {
             "algorithmic_bytes_per_step": ab["total"],
             "achieved_gbps": step_gbps,
             "frac": step_gbps / HBM_PEAK_GBPS,
         },
-        "per_call_us": per_call,
+        "per_kernel": per_kernel,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)

@@ -98,6 +98,25 @@ const char* mla_last_error(void);
 int32_t mla_version(void);
 
 /*
+ * Measurement hooks (not part of the computation). mla_profile_enable(1) makes
+ * the library record a pair of HIP events on the caller's stream around every
+ * launch of the kernels named below; mla_profile_enable(0) stops it (the
+ * default: nothing is recorded). mla_profile_read waits for the recorded pairs
+ * of one kernel, returns how many there were and their summed duration in
+ * milliseconds, and starts a new count.
+ *   "kv_append"     the kernel of mla_kv_append_quant
+ *   "indexer_scan"  the indexer scan of mla_indexer_topk
+ *   "topk_select"   its top-k selection (one or two kernels)
+ *   "decode"        the split attention kernel of mla_sparse_decode
+ *   "decode_merge"  its logsumexp merge
+ * Events are created on first use and kept for reuse; recording is serialised
+ * by a lock. Errors: MLA_ERR_INVALID_ARG (unknown name, NULL pointer),
+ * MLA_ERR_HIP (an event query failed).
+ */
+mla_status_t mla_profile_enable(int32_t on);
+mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* total_ms);
+
+/*
  * mla_kv_append_quant -- quantise-append of one decode step's entries.
  *
  * Writes, for each sequence b and each new entry i < n_new, the quantised main

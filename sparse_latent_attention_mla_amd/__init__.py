@@ -52,6 +52,9 @@ def lib():
         L.mla_status_str.argtypes, L.mla_status_str.restype = [i32], C.c_char_p
         L.mla_last_error.argtypes, L.mla_last_error.restype = [], C.c_char_p
         L.mla_version.argtypes, L.mla_version.restype = [], i32
+        L.mla_profile_enable.argtypes, L.mla_profile_enable.restype = [i32], i32
+        L.mla_profile_read.argtypes = [C.c_char_p, C.POINTER(i32), C.POINTER(C.c_double)]
+        L.mla_profile_read.restype = i32
         L.mla_kv_append_quant.argtypes = [_CRow, _CRow, P, P, P, i32, i32, i64, P, i64, P, i64,
                                           P, P, P, i32, i32, P]
         L.mla_kv_append_quant.restype = i32
@@ -105,6 +108,22 @@ def row_bytes(row: Row) -> int:
 
 def version() -> int:
     return int(lib().mla_version())
+
+
+def mla_profile_enable(on: bool) -> None:
+    """Start (True) or stop (False) event timing of the library's main kernels."""
+    _check(lib().mla_profile_enable(1 if on else 0))
+
+
+def mla_profile_read(kernel: str):
+    """(launches, total_ms) of `kernel` since the previous read; waits for them to finish.
+
+    Names: "kv_append", "indexer_scan", "topk_select", "decode", "decode_merge".
+    """
+    n = C.c_int32(0)
+    ms = C.c_double(0.0)
+    _check(lib().mla_profile_read(kernel.encode(), C.byref(n), C.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 def query_dtype(row: Row):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "mla")
 LIB = os.path.join(HERE, "libmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "append.hip", "indexer.hip", "topk.hip", "decode.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "append.hip", "indexer.hip", "topk.hip", "decode.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -25,9 +25,11 @@ FLAGS = [
 ]
 
 
-# Per-source extras. decode.hip: MFMA results in ordinary VGPRs, so the output
-# tile is never copied between accumulation and vector registers in the chunk loop.
-EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extras: MFMA results in ordinary VGPRs, so accumulators are never
+# copied between accumulation and vector registers (decode: the output tile in
+# the chunk loop; indexer: the scores of every tile before ReLU).
+EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, verbose):

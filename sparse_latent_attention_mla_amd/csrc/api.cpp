@@ -113,6 +113,18 @@ const char* mla_status_str(int32_t status) {
 
 const char* mla_last_error(void) { return g_err; }
 
+mla_status_t mla_profile_enable(int32_t on) {
+    mla::prof_enable(on != 0);
+    return ok();
+}
+
+mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* total_ms) {
+    if (!kernel || !launches || !total_ms) return fail(MLA_ERR_INVALID_ARG, "mla_profile_read: NULL argument");
+    const int k = mla::prof_index(kernel);
+    if (k < 0) return fail(MLA_ERR_INVALID_ARG, "mla_profile_read: unknown kernel name '%s'", kernel);
+    return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
+}
+
 int32_t mla_version(void) { return 100; }
 
 mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
@@ -164,7 +176,11 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const fl
     a.win_ring = new_win ? static_cast<uint16_t*>(win_ring) : nullptr;
     a.W = W;
     a.Dw = Dw;
-    return hip_status(mla::launch_append(a, static_cast<hipStream_t>(stream)), "append launch");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    mla::prof_begin(mla::PROF_APPEND, st);
+    const hipError_t e = mla::launch_append(a, st);
+    mla::prof_end(mla::PROF_APPEND, st);
+    return hip_status(e, "append launch");
 }
 
 size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
@@ -224,9 +240,13 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     a.k = k;
     a.scores = T.scores;
     a.hist = T.hist;
+    mla::prof_begin(mla::PROF_SCAN, st);
     e = mla::launch_scan(a, st);
+    mla::prof_end(mla::PROF_SCAN, st);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
+    mla::prof_begin(mla::PROF_SELECT, st);
     e = mla::launch_select(T.scores, capacity, n_visible, B, k, T, out_idx, st);
+    mla::prof_end(mla::PROF_SELECT, st);
     return hip_status(e, "top-k select");
 }
 

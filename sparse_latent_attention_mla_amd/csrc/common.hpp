@@ -145,6 +145,21 @@ __device__ __forceinline__ float key_score(uint32_t k) {
     return u2f((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48, on the VALU: each
+// permlane swap hands every lane the value of its partner row (16 lanes) / half.
+__device__ __forceinline__ float xmax4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    x = fmaxf(u2f(a[0]), u2f(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+__device__ __forceinline__ float xsum4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    x = u2f(a[0]) + u2f(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(b[0]) + u2f(b[1]);
+}
+
 // MFMA wrappers (gfx950, 64-lane wave).  Operand layout, verified on the
 // device: A lane l holds row (l % 16), k-slots 8*(l/16) .. +7; B lane l holds
 // column (l % 16), the same k-slots; D lane l, element r holds row

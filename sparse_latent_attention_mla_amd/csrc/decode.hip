@@ -116,21 +116,6 @@ __device__ __forceinline__ u32x2 ds_tr16(const uint8_t* p) {
                  (uint32_t)(uint16_t)r.z | ((uint32_t)(uint16_t)r.w << 16)};
 }
 
-// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one head's rows), on the
-// VALU: each permlane swap hands every lane the value of its partner row / half.
-__device__ __forceinline__ float xmax4(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    x = fmaxf(u2f(a[0]), u2f(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return fmaxf(u2f(b[0]), u2f(b[1]));
-}
-__device__ __forceinline__ float xsum4(float x) {
-    const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
-    x = u2f(a[0]) + u2f(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
-    return u2f(b[0]) + u2f(b[1]);
-}
-
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // two floats -> two bf16 (round to nearest even, hardware convert), low half first
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
@@ -755,7 +740,9 @@ static hipError_t launch_mfma(const DecodeArgs& a, const Geometry& g, float* o_p
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     if (!mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H)) {
+        prof_begin(PROF_DECODE, stream);
         hipLaunchKernelGGL(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, a);
+        prof_end(PROF_DECODE, stream);
         return hipGetLastError();
     }
     const Geometry g = decode_geometry(a.B, a.H, a.k, a.win ? a.W : 0);
@@ -766,6 +753,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (S > 0) {
         hipError_t e = hipSuccess;
         const bool two = g.ht == 2;
+        prof_begin(PROF_DECODE, stream);
         if (a.fmt == MLA_FMT_E4M3_S128)
             e = two ? launch_mfma<SRC_E4M3, 576, 2>(a, g, o_part, lse_part, stream)
                     : launch_mfma<SRC_E4M3, 576, 1>(a, g, o_part, lse_part, stream);
@@ -778,10 +766,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         else
             e = two ? launch_mfma<SRC_BF16, 512, 2>(a, g, o_part, lse_part, stream)
                     : launch_mfma<SRC_BF16, 512, 1>(a, g, o_part, lse_part, stream);
+        prof_end(PROF_DECODE, stream);
         if (e != hipSuccess) return e;
     }
+    prof_begin(PROF_MERGE, stream);
     hipLaunchKernelGGL(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, S, a.H, o_part, lse_part, a.out,
                        a.lse);
+    prof_end(PROF_MERGE, stream);
     return hipGetLastError();
 }
 

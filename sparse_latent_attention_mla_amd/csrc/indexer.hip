@@ -79,14 +79,17 @@ __device__ __forceinline__ void tile_scores(const ScanCtx<MT>& C, const u32x4 kb
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(C.qa[m][t], kb[t], acc[m]);
     // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
-    float part = 0.0f;
+    float pm[MT];                                         // one partial sum per head tile: short chains
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
+        pm[m] = C.wv[m][0] * relu(acc[m][0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += C.wv[m][r] * relu(acc[m][r]);
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    part *= mult;
+        for (int r = 1; r < 4; ++r) pm[m] += C.wv[m][r] * relu(acc[m][r]);
+    }
+    float part = pm[0];
+#pragma unroll
+    for (int m = 1; m < MT; ++m) part += pm[m];
+    part = xsum4(part) * mult;
     if (g == 0 && s < capacity) {
         scores[s] = valid ? part : -__builtin_inff();
         if (valid) atomicAdd(&hist[score_key(part) >> (32 - kHistBits)], 1u);
@@ -142,12 +145,23 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
     const uint8_t* base = a.cache + b * a.stride;
     float* scores = a.scores + b * a.capacity;
     uint8_t* st = stage[wave];
-    u32x4 raw[kLoads];
-    // chunk c of this wave covers rows row0 + (c * 4 + wave) * 64 ..
-    auto issue = [&](int c) {
+    // chunk c of this wave covers rows row0 + (c * 4 + wave) * 64 ..; two chunks are
+    // in flight in two register buffers while the one before them is contracted
+    u32x4 rawA[kLoads], rawB[kLoads];
+    auto issue = [&](int c, u32x4* raw) {
         const int64_t r = row0 + (int64_t)(c * 4 + wave) * kChunkRows;
         const int64_t avail = (a.capacity - r) * RB;          // bytes of this sequence from r on
         const uint8_t* src = base + r * RB;
+        if (avail >= kChunkBytes) {                          // the whole chunk is in the sequence
+#pragma unroll
+            for (int i = 0; i < kLoads; ++i) {
+                const int off = (i * 64 + lane) * 16;
+                if (i + 1 < kLoads || off < kChunkBytes)
+                    raw[i] = __builtin_bit_cast(u32x4, __builtin_nontemporal_load(
+                                                           reinterpret_cast<const u32x4_a4*>(src + off)));
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             const int off = (i * 64 + lane) * 16;
@@ -166,15 +180,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
             }
         }
     };
-    const int64_t first_row = row0 + (int64_t)wave * kChunkRows;
-    if (first_row < nvis) issue(0);
-    for (int c = 0; c < n_chunks; ++c) {
-        const int64_t r = row0 + (int64_t)(c * 4 + wave) * kChunkRows;
-        if (r >= a.capacity) break;
+    auto chunk_row = [&](int c) { return row0 + (int64_t)(c * 4 + wave) * kChunkRows; };
+    // one chunk: stage its bytes, start the chunk two ahead into the same buffer, contract
+    auto step = [&](int c, u32x4* raw) -> bool {
+        const int64_t r = chunk_row(c);
+        if (r >= a.capacity) return false;
         if (r >= nvis) {                                       // whole chunk masked
             for (int i = lane; i < kChunkRows; i += 64)
                 if (r + i < a.capacity) scores[r + i] = -__builtin_inff();
-            continue;
+            return true;
         }
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
@@ -184,8 +198,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int64_t rn = r + 4 * kChunkRows;
-        if (c + 1 < n_chunks && rn < nvis) issue(c + 1);
+        if (c + 2 < n_chunks && chunk_row(c + 2) < nvis) issue(c + 2, raw);
 #pragma unroll
         for (int tile = 0; tile < kChunkRows / 16; ++tile) {
             const int rr = tile * 16 + col;
@@ -211,6 +224,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        return true;
+    };
+    if (chunk_row(0) < nvis) issue(0, rawA);
+    if (n_chunks > 1 && chunk_row(1) < nvis) issue(1, rawB);
+    for (int c = 0; c < n_chunks; c += 2) {
+        if (!step(c, rawA)) break;
+        if (c + 1 < n_chunks && !step(c + 1, rawB)) break;
     }
     __syncthreads();
     flush_hist(hist, a.hist + (int64_t)b * kHistBins);

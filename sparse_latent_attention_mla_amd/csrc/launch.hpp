@@ -81,6 +81,14 @@ struct DecodeArgs {
     size_t workspace_bytes;
 };
 bool decode_supported(int fmt, int dim, int rope, int d_v, int H);
+
+// Opt-in per-kernel event timing (profile.cpp): no-ops unless mla_profile_enable(1).
+enum ProfKernel { PROF_APPEND, PROF_SCAN, PROF_SELECT, PROF_DECODE, PROF_MERGE, PROF_KERNELS };
+void prof_begin(ProfKernel k, hipStream_t s);
+void prof_end(ProfKernel k, hipStream_t s);
+void prof_enable(bool on);
+int prof_index(const char* name);  // -1 for an unknown name
+hipError_t prof_read(int k, int32_t* launches, double* total_ms);
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

@@ -101,3 +101,15 @@ def test_workspace_queries(M):
     r = M.Row(M.E4M3_S128, 512, 64)
     assert M.mla_sparse_decode_workspace(r, 512, 4, 128, 2048, 0) >= 4 * 128 * 512 * 4
     assert M.mla_sparse_decode_workspace(M.Row(M.F32, 64, 16), 64, 1, 16, 32, 0) == 0   # generic path
+
+
+def test_profile_hooks_off_by_default_and_reject_unknown_names(M):
+    # nothing has been launched in this process, so every count is zero and no
+    # event is ever waited on
+    M.mla_profile_enable(False)
+    for name in ("kv_append", "indexer_scan", "topk_select", "decode", "decode_merge"):
+        assert M.mla_profile_read(name) == (0, 0.0)
+    with pytest.raises(M.MLAError, match="unknown kernel name"):
+        M.mla_profile_read("k_scan")
+    n, ms = C.c_int32(), C.c_double()
+    assert M.lib().mla_profile_read(None, C.byref(n), C.byref(ms)) == 1

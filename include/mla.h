@@ -98,22 +98,32 @@ const char* mla_last_error(void);
 int32_t mla_version(void);
 
 /*
- * Measurement hooks (not part of the computation). mla_profile_enable(1) makes
- * the library record a pair of HIP events on the caller's stream around every
- * launch of the kernels named below; mla_profile_enable(0) stops it (the
- * default: nothing is recorded). mla_profile_read waits for the recorded pairs
- * of one kernel, returns how many there were and their summed duration in
- * milliseconds, and starts a new count.
- *   "kv_append"     the kernel of mla_kv_append_quant
- *   "indexer_scan"  the indexer scan of mla_indexer_topk
- *   "topk_select"   its top-k selection (one or two kernels)
- *   "decode"        the split attention kernel of mla_sparse_decode
- *   "decode_merge"  its logsumexp merge
- * Events are created on first use and kept for reuse; recording is serialised
- * by a lock. Errors: MLA_ERR_INVALID_ARG (unknown name, NULL pointer),
- * MLA_ERR_HIP (an event query failed).
+ * Measurement hooks (not part of the computation). mla_profile_enable(mask)
+ * selects kernels to time; each later launch of a selected kernel takes a pair
+ * of HIP events that the runtime stamps from that kernel's own dispatch
+ * (hipExtLaunchKernel), on the caller's stream, so the pair measures exactly
+ * the kernel's execution. Timed launches cost more host time than plain ones.
+ * mask 0 (the default) times nothing; MLA_PROF_ALL times all of them.
+ * mla_profile_read waits for the recorded pairs of one kernel, returns how many
+ * there were and their summed duration in milliseconds, and starts a new count.
+ *   bit  name
+ *   0    "kv_append"     the kernel of mla_kv_append_quant
+ *   1    "indexer_scan"  the indexer scan of mla_indexer_topk
+ *   2    "topk_select"   its top-k selection (one kernel, or the first's start
+ *                        to the second's end)
+ *   3    "decode"        the split attention kernel of mla_sparse_decode
+ *   4    "decode_merge"  its logsumexp merge
+ * Events are created on first use and kept for reuse; taking them is
+ * serialised by a lock. Errors: MLA_ERR_INVALID_ARG (unknown name, NULL
+ * pointer), MLA_ERR_HIP (an event query failed).
  */
-mla_status_t mla_profile_enable(int32_t on);
+#define MLA_PROF_KV_APPEND 0x01
+#define MLA_PROF_INDEXER_SCAN 0x02
+#define MLA_PROF_TOPK_SELECT 0x04
+#define MLA_PROF_DECODE 0x08
+#define MLA_PROF_DECODE_MERGE 0x10
+#define MLA_PROF_ALL 0x1f
+mla_status_t mla_profile_enable(int32_t kernels);
 mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* total_ms);
 
 /*

@@ -110,9 +110,15 @@ def version() -> int:
     return int(lib().mla_version())
 
 
-def mla_profile_enable(on: bool) -> None:
-    """Start (True) or stop (False) event timing of the library's main kernels."""
-    _check(lib().mla_profile_enable(1 if on else 0))
+PROFILE_KERNELS = ("kv_append", "indexer_scan", "topk_select", "decode", "decode_merge")
+
+
+def mla_profile_enable(kernels=()) -> None:
+    """Time the named kernels (see PROFILE_KERNELS) from now on; () stops timing."""
+    mask = 0
+    for name in kernels:
+        mask |= 1 << PROFILE_KERNELS.index(name)
+    _check(lib().mla_profile_enable(mask))
 
 
 def mla_profile_read(kernel: str):

@@ -113,8 +113,8 @@ const char* mla_status_str(int32_t status) {
 
 const char* mla_last_error(void) { return g_err; }
 
-mla_status_t mla_profile_enable(int32_t on) {
-    mla::prof_enable(on != 0);
+mla_status_t mla_profile_enable(int32_t kernels) {
+    mla::prof_enable(static_cast<uint32_t>(kernels));
     return ok();
 }
 
@@ -177,10 +177,7 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const fl
     a.W = W;
     a.Dw = Dw;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    mla::prof_begin(mla::PROF_APPEND, st);
-    const hipError_t e = mla::launch_append(a, st);
-    mla::prof_end(mla::PROF_APPEND, st);
-    return hip_status(e, "append launch");
+    return hip_status(mla::launch_append(a, st), "append launch");
 }
 
 size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
@@ -240,13 +237,9 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     a.k = k;
     a.scores = T.scores;
     a.hist = T.hist;
-    mla::prof_begin(mla::PROF_SCAN, st);
     e = mla::launch_scan(a, st);
-    mla::prof_end(mla::PROF_SCAN, st);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
-    mla::prof_begin(mla::PROF_SELECT, st);
     e = mla::launch_select(T.scores, capacity, n_visible, B, k, T, out_idx, st);
-    mla::prof_end(mla::PROF_SELECT, st);
     return hip_status(e, "top-k select");
 }
 

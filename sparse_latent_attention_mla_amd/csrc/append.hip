@@ -99,8 +99,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
     int n_blocks_x = (a.main_cache || a.idx_cache) ? a.n_new : 0;
     if (a.win_ring && n_blocks_x < 1) n_blocks_x = 1;
     if (a.B == 0 || n_blocks_x == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_append, dim3(n_blocks_x, a.B), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    const ProfSlot p = prof_slot(PROF_APPEND);
+    return launch_kernel(k_append, dim3(n_blocks_x, a.B), dim3(kThreads), 0, stream, p.start, p.stop, a);
 }
 
 }  // namespace mla

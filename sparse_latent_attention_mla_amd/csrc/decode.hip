@@ -732,18 +732,16 @@ static hipError_t launch_mfma(const DecodeArgs& a, const Geometry& g, float* o_p
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, stream, a, g.S_main, g.S_win, g.rps, g.groups, n_items,
-                       o_part, lse_part);
-    return hipGetLastError();
+    const ProfSlot p = prof_slot(PROF_DECODE);
+    return launch_kernel(kern, dim3(grid), dim3(kThreads), lds, stream, p.start, p.stop, a, g.S_main, g.S_win, g.rps,
+                         g.groups, n_items, o_part, lse_part);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (a.B == 0) return hipSuccess;
     if (!mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H)) {
-        prof_begin(PROF_DECODE, stream);
-        hipLaunchKernelGGL(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, a);
-        prof_end(PROF_DECODE, stream);
-        return hipGetLastError();
+        const ProfSlot p = prof_slot(PROF_DECODE);
+        return launch_kernel(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, p.start, p.stop, a);
     }
     const Geometry g = decode_geometry(a.B, a.H, a.k, a.win ? a.W : 0);
     const int S = g.S_main + g.S_win;
@@ -753,7 +751,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     if (S > 0) {
         hipError_t e = hipSuccess;
         const bool two = g.ht == 2;
-        prof_begin(PROF_DECODE, stream);
         if (a.fmt == MLA_FMT_E4M3_S128)
             e = two ? launch_mfma<SRC_E4M3, 576, 2>(a, g, o_part, lse_part, stream)
                     : launch_mfma<SRC_E4M3, 576, 1>(a, g, o_part, lse_part, stream);
@@ -766,14 +763,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
         else
             e = two ? launch_mfma<SRC_BF16, 512, 2>(a, g, o_part, lse_part, stream)
                     : launch_mfma<SRC_BF16, 512, 1>(a, g, o_part, lse_part, stream);
-        prof_end(PROF_DECODE, stream);
         if (e != hipSuccess) return e;
     }
-    prof_begin(PROF_MERGE, stream);
-    hipLaunchKernelGGL(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, S, a.H, o_part, lse_part, a.out,
-                       a.lse);
-    prof_end(PROF_MERGE, stream);
-    return hipGetLastError();
+    const ProfSlot p = prof_slot(PROF_MERGE);
+    return launch_kernel(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, p.start, p.stop, S, a.H, o_part,
+                         lse_part, a.out, a.lse);
 }
 
 }  // namespace mla

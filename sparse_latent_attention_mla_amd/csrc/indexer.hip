@@ -357,11 +357,11 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         const dim3 sgrid((unsigned)((a.capacity + rpb - 1) / rpb), a.B);
 #define MLA_SCAN_CASE(F, M)                                                                    \
     if (a.fmt == F && a.H_I == 16 * M) {                                                       \
+        const ProfSlot p = prof_slot(PROF_SCAN);                                               \
         if (F == MLA_FMT_BF16)                                                                 \
-            hipLaunchKernelGGL((k_scan_bf16<M>), grid, dim3(kScanThreads), 0, stream, a);      \
-        else                                                                                   \
-            hipLaunchKernelGGL((k_scan_staged<F, M>), sgrid, dim3(kScanThreads), 0, stream, a, (int)rpb); \
-        return hipGetLastError();                                                              \
+            return launch_kernel(k_scan_bf16<M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a); \
+        return launch_kernel(k_scan_staged<F, M>, sgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, a, \
+                             (int)rpb);                                                        \
     }
         MLA_SCAN_CASE(MLA_FMT_BF16, 1) MLA_SCAN_CASE(MLA_FMT_BF16, 2)
         MLA_SCAN_CASE(MLA_FMT_BF16, 3) MLA_SCAN_CASE(MLA_FMT_BF16, 4)
@@ -373,8 +373,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         return hipErrorInvalidValue;
     }
     const dim3 grid((unsigned)((a.capacity + kScanThreads - 1) / kScanThreads), a.B);
-    hipLaunchKernelGGL(k_scan_generic, grid, dim3(kScanThreads), 0, stream, a);
-    return hipGetLastError();
+    const ProfSlot p = prof_slot(PROF_SCAN);
+    return launch_kernel(k_scan_generic, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a);
 }
 
 }  // namespace mla

@@ -2,7 +2,10 @@
 // Host-side validation lives in api.cpp; launchers assume valid arguments.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <tuple>
 #include <stdint.h>
 
 namespace mla {
@@ -82,13 +85,33 @@ struct DecodeArgs {
 };
 bool decode_supported(int fmt, int dim, int rope, int d_v, int H);
 
-// Opt-in per-kernel event timing (profile.cpp): no-ops unless mla_profile_enable(1).
+// Opt-in per-kernel event timing (profile.cpp), off unless mla_profile_enable(1).
 enum ProfKernel { PROF_APPEND, PROF_SCAN, PROF_SELECT, PROF_DECODE, PROF_MERGE, PROF_KERNELS };
-void prof_begin(ProfKernel k, hipStream_t s);
-void prof_end(ProfKernel k, hipStream_t s);
-void prof_enable(bool on);
+struct ProfSlot {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfSlot prof_slot(ProfKernel k);  // a fresh event pair for one launch; two nulls while timing is off
+void prof_enable(uint32_t mask);  // bit k times ProfKernel k
 int prof_index(const char* name);  // -1 for an unknown name
 hipError_t prof_read(int k, int32_t* launches, double* total_ms);
+
+// Launch `kernel`.  With events, through hipExtLaunchKernel: the runtime stamps
+// them from the kernel's own dispatch (start, end), so a pair brackets exactly
+// that kernel and no marker packet is added between kernels on the stream.
+template <typename... Params, typename... Args>
+hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                         hipEvent_t t0, hipEvent_t t1, Args... args) {
+    static_assert(sizeof...(Params) == sizeof...(Args), "argument count");
+    std::tuple<Params...> held{args...};
+    void* argv[sizeof...(Params)];
+    std::apply([&](auto&... x) {
+        int i = 0;
+        ((argv[i++] = static_cast<void*>(&x)), ...);
+    }, held);
+    const void* f = reinterpret_cast<const void*>(kernel);
+    if (t0 || t1) return hipExtLaunchKernel(f, grid, block, argv, lds, stream, t0, t1, 0);
+    return hipLaunchKernel(f, grid, block, argv, lds, stream);
+}
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 

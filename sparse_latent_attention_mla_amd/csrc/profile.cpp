@@ -1,9 +1,10 @@
 // profile.cpp -- opt-in per-kernel timing with HIP events on the caller's stream.
 //
-// When enabled, the launchers bracket the named kernels with a pair of events
-// recorded on the stream they launch on; mla_profile_read sums the elapsed
-// times of the pairs recorded since the previous read. Events are created on
-// first use and reused. Off by default: no event is ever recorded then.
+// When enabled, each launch of a timed kernel takes a fresh pair of events that
+// the runtime stamps from that kernel's own dispatch (launch_kernel);
+// mla_profile_read sums the elapsed times of the pairs taken since the previous
+// read. Events are created on first use and reused. Off by default: no event is
+// ever recorded then.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -22,7 +23,7 @@ struct Pairs {
     size_t used = 0;
 };
 
-std::atomic<bool> g_on{false};
+std::atomic<uint32_t> g_mask{0};      // bit k: time kernel k
 std::mutex g_mu;
 Pairs g_pairs[PROF_KERNELS];
 const char* const kNames[PROF_KERNELS] = {"kv_append", "indexer_scan", "topk_select", "decode",
@@ -30,31 +31,28 @@ const char* const kNames[PROF_KERNELS] = {"kv_append", "indexer_scan", "topk_sel
 
 }  // namespace
 
-void prof_begin(ProfKernel k, hipStream_t s) {
-    if (!g_on.load(std::memory_order_relaxed)) return;
+ProfSlot prof_slot(ProfKernel k) {
+    ProfSlot slot;
+    if (!(g_mask.load(std::memory_order_relaxed) >> k & 1u)) return slot;
     std::lock_guard<std::mutex> lock(g_mu);
     Pairs& p = g_pairs[k];
     if (p.used == p.start.size()) {
         hipEvent_t a, b;
-        if (hipEventCreate(&a) != hipSuccess) return;
-        if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+        if (hipEventCreate(&a) != hipSuccess) return slot;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return slot;
+        }
         p.start.push_back(a);
         p.stop.push_back(b);
     }
-    (void)hipEventRecord(p.start[p.used], s);
+    slot.start = p.start[p.used];
+    slot.stop = p.stop[p.used];
+    ++p.used;
+    return slot;
 }
 
-void prof_end(ProfKernel k, hipStream_t s) {
-    if (!g_on.load(std::memory_order_relaxed)) return;
-    std::lock_guard<std::mutex> lock(g_mu);
-    Pairs& p = g_pairs[k];
-    if (p.used < p.start.size()) {
-        (void)hipEventRecord(p.stop[p.used], s);
-        ++p.used;
-    }
-}
-
-void prof_enable(bool on) { g_on.store(on); }
+void prof_enable(uint32_t mask) { g_mask.store(mask & ((1u << PROF_KERNELS) - 1u)); }
 
 int prof_index(const char* name) {
     for (int i = 0; i < PROF_KERNELS; ++i)

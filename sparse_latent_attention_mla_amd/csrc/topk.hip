@@ -520,8 +520,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
 
 hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_topk_clear, dim3(B), dim3(256), 0, stream, ws, B);
-    return hipGetLastError();
+    return launch_kernel(k_topk_clear, dim3(B), dim3(256), 0, stream, nullptr, nullptr, ws, B);
 }
 
 // MLA_TOPK_PATH=row|multi forces a path (for tuning).
@@ -530,21 +529,18 @@ hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n
     if (B == 0 || k == 0) return hipSuccess;
     bool row = capacity <= kRowPathMax;
     if (const char* e = getenv("MLA_TOPK_PATH")) row = (e[0] == 'r');
-    if (row) {
-        hipLaunchKernelGGL(k_topk_row, dim3(B), dim3(kRowThreads), 0, stream, scores, capacity, n_visible, k, ws,
-                           out_idx);
-        return hipGetLastError();
-    }
+    const ProfSlot p = prof_slot(PROF_SELECT);      // spans both kernels of the two-kernel path
+    if (row)
+        return launch_kernel(k_topk_row, dim3(B), dim3(kRowThreads), 0, stream, p.start, p.stop, scores, capacity,
+                             n_visible, k, ws, out_idx);
     const unsigned nx = (unsigned)((capacity + kSelRows - 1) / kSelRows);
     if (nx > 0) {
-        hipLaunchKernelGGL(k_select, dim3(nx, B), dim3(kSelThreads), 0, stream, scores, capacity, n_visible, k,
-                           ws);
-        hipError_t e = hipGetLastError();
+        const hipError_t e = launch_kernel(k_select, dim3(nx, B), dim3(kSelThreads), 0, stream, p.start, nullptr,
+                                           scores, capacity, n_visible, k, ws);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_select_final, dim3(B), dim3(kSelThreads), 0, stream, n_visible, k, capacity, (int)nx, ws,
-                       out_idx);
-    return hipGetLastError();
+    return launch_kernel(k_select_final, dim3(B), dim3(kSelThreads), 0, stream, nx > 0 ? nullptr : p.start, p.stop,
+                         n_visible, k, capacity, (int)nx, ws, out_idx);
 }
 
 }  // namespace mla

@@ -106,9 +106,13 @@ def test_workspace_queries(M):
 def test_profile_hooks_off_by_default_and_reject_unknown_names(M):
     # nothing has been launched in this process, so every count is zero and no
     # event is ever waited on
-    M.mla_profile_enable(False)
-    for name in ("kv_append", "indexer_scan", "topk_select", "decode", "decode_merge"):
+    M.mla_profile_enable(())
+    for name in M.PROFILE_KERNELS:
         assert M.mla_profile_read(name) == (0, 0.0)
+    # the header's mask bits follow the binding's names
+    text = open(HEADER).read()
+    for bit, name in enumerate(M.PROFILE_KERNELS):
+        assert re.search(rf"#define MLA_PROF_{name.upper()} 0x{1 << bit:02x}\b", text), name
     with pytest.raises(M.MLAError, match="unknown kernel name"):
         M.mla_profile_read("k_scan")
     n, ms = C.c_int32(), C.c_double()

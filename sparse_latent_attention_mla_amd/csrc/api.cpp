@@ -73,7 +73,7 @@ TopkLayout topk_layout(int32_t B, int64_t capacity) {
     const size_t groups = capacity > 0 ? (size_t)mla::select_groups(capacity) : 0;
     L.scores = 0;
     L.hist = L.scores + round256(b * cap * sizeof(float));
-    L.counts = L.hist + round256(b * mla::kHistBinsHost * sizeof(uint32_t));
+    L.counts = L.hist + round256(b * (size_t)mla::kHistWordsHost * sizeof(uint32_t));
     L.sel = L.counts + round256(b * groups * 2 * sizeof(uint32_t));
     L.cand = L.sel + round256(b * cap * sizeof(int32_t));
     L.cand2 = L.cand + round256(b * cap * sizeof(uint64_t));

@@ -177,5 +177,81 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 static_assert(kHistBins == kHistBinsHost, "histogram size");
+constexpr int kHistCopies = kHistCopiesHost;
+constexpr int kCoarseBins = kCoarseBinsHost;
+constexpr int kFinePerCoarse = kHistBins / kCoarseBins;
+static_assert(kFinePerCoarse == 64, "one fine bin per lane of a wave within a coarse bin");
+
+// Histogram words of sequence b: coarse copy j at hb + 64 j, fine copy j at
+// hb + 64 * kHistCopies + 4096 j.
+__device__ __forceinline__ uint32_t* hist_coarse(uint32_t* hb, int j) { return hb + kCoarseBins * j; }
+__device__ __forceinline__ uint32_t* hist_fine(uint32_t* hb, int j) {
+    return hb + kCoarseBins * kHistCopies + kHistBins * j;
+}
+// The copy a workgroup adds into: the index of the XCD it runs on (hardware
+// register XCC_ID), so that every workgroup adding into one copy shares that
+// XCD's L2 and the adds can be L2-local atomics; the end of the kernel writes
+// the L2 back before any later kernel reads the copies.
+__device__ __forceinline__ int hist_copy_of_block() {
+    return (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (kHistCopies - 1));
+}
+__device__ __forceinline__ void l2_add(uint32_t* p, uint32_t v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Add a workgroup's counts into copy j of sequence b's histogram (L2-local
+// atomics, see hist_copy_of_block; zero counts skipped). count(i) gives fine bin i's count; the coarse
+// bins are the sums of 64 consecutive fine bins. Called by all threads of a
+// workgroup of `nthreads` (a multiple of 64) after its counts are final.
+template <typename F>
+__device__ __forceinline__ void flush_hist_copy(F count, uint32_t* hb, int j, int nthreads) {
+    uint32_t* fine = hist_fine(hb, j);
+    uint32_t* coarse = hist_coarse(hb, j);
+    // thread t covers fine bins 16 q .. 16 q + 15 for q = t, t + nthreads, ..; the 4
+    // lanes of a coarse bin (64 fine bins) are adjacent and meet in a shuffle sum
+    for (int q = threadIdx.x; q < kHistBins / 16; q += nthreads) {
+        uint32_t part = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t c = count(16 * q + i);
+            part += c;
+            if (c) l2_add(&fine[16 * q + i], c);
+        }
+        part += __shfl_xor(part, 1, 64);
+        part += __shfl_xor(part, 2, 64);
+        if ((q & 3) == 0 && part) l2_add(&coarse[q >> 2], part);
+    }
+}
+
+// ---------------------------------------------------------------- LDS DMA
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Global memory to LDS without passing through registers: every lane's 16 (4)
+// bytes land at LDS address m0 + 16 * lane (m0 + 4 * lane). Issued as inline
+// assembly so that the compiler neither waits for them at every barrier nor
+// reorders them; the kernels wait for them with vmcnt themselves. The compiler
+// reserves M0 and warns about the clobber; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+// wave-uniform base + per-lane 32-bit byte offset
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 }  // namespace mla

@@ -80,26 +80,6 @@ constexpr int kLdsZ = kMaxRps * 4;
 constexpr int kLdsZBytes = 2 * 2 * 16 * kZs * 4;            // KH * HT == 2 in both layouts
 constexpr int kLdsBuf = kLdsZ + kLdsZBytes;
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes from global memory to LDS address m0 + 16 * lane. Issued as inline
-// assembly so that the compiler does not wait for it at every barrier; the
-// kernel waits for these loads itself with vmcnt. The compiler reserves M0 and
-// warns about the clobber; nothing else in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));

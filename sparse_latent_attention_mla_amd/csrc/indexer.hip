@@ -14,6 +14,8 @@
 // applied to the accumulator.  ReLU, the head weights and the head sum run on
 // the accumulator in registers, and the top-k histogram of the score keys is
 // built in LDS, so the only outputs are the fp32 scores and the histogram.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -26,6 +28,13 @@ constexpr int kTilesPerWave = 8;          // 16-row tiles per wave (direct-load 
 constexpr int kRowsPerBlock = 4 * kTilesPerWave * 16;
 constexpr int kChunkRows = 64;            // rows a wave stages through LDS per step
 constexpr int kStagedBlocks = 512;        // target workgroups of the staged scan (2 per CU)
+constexpr int kDmaRows = 32;              // rows per chunk of the LDS-DMA scan
+constexpr int kDmaMaxRowsPerBlock = 1024;
+#ifndef MLA_SCAN_NBUF
+#define MLA_SCAN_NBUF 3                   // chunk buffers per wave in the LDS-DMA scan
+#endif
+constexpr int kDmaNbuf = MLA_SCAN_NBUF;
+constexpr int kDmaBlocksPerCu = (kDmaNbuf == 2) ? 3 : 2;   // what the LDS of one CU holds
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -65,12 +74,11 @@ struct ScanCtx {
     float wv[MT][4];      // w * sigma of accumulator rows 4g + r of head tile m
 };
 
-// Contract one 16-row tile and emit its scores: lane (col, g) holds the B
-// operand of row `s` (= tile0 + col); `mult` is its post-contraction factor.
+// Contract one 16-row tile: lane (col, g) holds the B operand of row col of
+// the tile; returns that row's score (every g holds it); `mult` is the row's
+// post-contraction factor.
 template <int MT>
-__device__ __forceinline__ void tile_scores(const ScanCtx<MT>& C, const u32x4 kb[4], float mult, int64_t s,
-                                            bool valid, int g, float sigma, int64_t capacity, float* scores,
-                                            uint32_t* hist) {
+__device__ __forceinline__ float tile_dot(const ScanCtx<MT>& C, const u32x4 kb[4], float mult) {
     f32x4 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -89,7 +97,15 @@ __device__ __forceinline__ void tile_scores(const ScanCtx<MT>& C, const u32x4 kb
     float part = pm[0];
 #pragma unroll
     for (int m = 1; m < MT; ++m) part += pm[m];
-    part = xsum4(part) * mult;
+    return xsum4(part) * mult;
+}
+
+// Contract one 16-row tile and emit its scores: row `s` (= tile0 + col).
+template <int MT>
+__device__ __forceinline__ void tile_scores(const ScanCtx<MT>& C, const u32x4 kb[4], float mult, int64_t s,
+                                            bool valid, int g, float sigma, int64_t capacity, float* scores,
+                                            uint32_t* hist) {
+    const float part = tile_dot<MT>(C, kb, mult);
     if (g == 0 && s < capacity) {
         scores[s] = valid ? part : -__builtin_inff();
         if (valid) atomicAdd(&hist[score_key(part) >> (32 - kHistBits)], 1u);
@@ -110,11 +126,9 @@ __device__ __forceinline__ void load_ctx(ScanCtx<MT>& C, const ScanArgs& a, int 
         for (int r = 0; r < 4; ++r) C.wv[m][r] = a.w[(int64_t)b * a.H_I + 16 * m + 4 * g + r] * a.sigma;
 }
 
-__device__ __forceinline__ void flush_hist(const uint32_t* hist, uint32_t* gh) {
-    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) {
-        const uint32_t v = hist[i];
-        if (v) atomicAdd(&gh[i], v);
-    }
+// A workgroup's LDS histogram (one word per bin) into its copy of the sequence's.
+__device__ __forceinline__ void flush_hist(const uint32_t* hist, uint32_t* hb) {
+    flush_hist_copy([&](int i) { return hist[i]; }, hb, hist_copy_of_block(), kScanThreads);
 }
 
 // MFMA scan, rows that are not 16-byte multiples (E4M3 132 B, E2M1 72 B).
@@ -233,7 +247,170 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
         if (c + 1 < n_chunks && !step(c + 1, rawB)) break;
     }
     __syncthreads();
-    flush_hist(hist, a.hist + (int64_t)b * kHistBins);
+    flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
+}
+
+// MFMA scan through LDS DMA, E4M3 (132 B) and E2M1 (72 B) rows, for caches
+// whose base and sequence stride are 16-byte aligned: a chunk of 32 rows is
+// then a 16-byte aligned run of 4224 or 2304 bytes. Each wave streams its own
+// chunks (rows row0 + (4 it + wave) * 32 ..) into a private ring of NBUF LDS
+// buffers with global_load_lds, without passing them through registers; it
+// waits for a chunk with an exact vector-memory count and contracts it as two
+// 16-row tiles (operand layout as in k_scan_staged) while the next chunks are
+// in flight. The queries and head weights arrive the same way (wave m fetches
+// head tile m into its last buffer before that buffer is first used). Scores
+// collect in LDS and leave in one coalesced pass; the histogram keeps two
+// 16-bit fine bins per word (a block has at most 1024 rows) plus the 64 coarse
+// bins, and is flushed by consecutive threads into consecutive bins.
+template <int FMT, int MT, int NBUF>
+__global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(ScanArgs a, int rows_per_block) {
+    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
+    constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
+    constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries + weights
+    static_assert(kBytes % 16 == 0, "chunk of 16-byte pieces");
+    static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+    __shared__ uint32_t hist2[kHistBins / 2];
+    __shared__ uint32_t coarse[kCoarseBins];
+    __shared__ __attribute__((aligned(16))) float sc[kDmaMaxRowsPerBlock];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][NBUF][kBuf];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, g = lane >> 4;
+    const int64_t cap = a.capacity;
+    const int64_t nvis = clamp_visible(a.n_visible[b], cap);
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+    const int n_it = rows_per_block / (4 * kDmaRows);
+    for (int i = threadIdx.x; i < kHistBins / 2; i += kScanThreads) hist2[i] = 0u;
+    if (threadIdx.x < kCoarseBins) coarse[threadIdx.x] = 0u;
+
+    const uint8_t* base = a.cache + b * a.stride;
+    auto chunk_row = [&](int it) { return row0 + (int64_t)(4 * it + wave) * kDmaRows; };
+    // number of this wave's chunks that start below `lim`
+    auto chunks_below = [&](int64_t lim) {
+        const int64_t d = lim - row0 - (int64_t)wave * kDmaRows;
+        if (d <= 0) return 0;
+        const int64_t n = (d + 4 * kDmaRows - 1) / (4 * kDmaRows);
+        return (int)(n < n_it ? n : n_it);
+    };
+    const int n_dma = chunks_below(nvis);                  // chunks with visible rows: read
+    const int n_cap = chunks_below(cap);                   // chunks inside the cache: scored
+    const uint32_t ring_m0 = __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][0][0]));
+    // KI DMA instructions per chunk, always all of them (the waits count them).
+    // Lanes past the chunk, or past the end of the sequence, re-read the
+    // chunk's first bytes (cached, never past the cache's end); the rows they
+    // stand for are masked.
+    auto issue = [&](int it) {
+        const int64_t r = chunk_row(it);
+        const uint8_t* src = base + r * RB;
+        const int64_t left = (cap - r) * RB;
+        const uint32_t m0 = ring_m0 + (uint32_t)((it % NBUF) * kBuf);
+#pragma unroll
+        for (int k = 0; k < KI; ++k) {
+            uint32_t off = (uint32_t)(1024 * k + 16 * lane);
+            if (off >= (uint32_t)kBytes || (int64_t)off + 16 > left) off = 0;
+            dma16_s(src, off, m0 + 1024u * (uint32_t)k);
+        }
+    };
+    // queries of head tile `wave` (16 heads x 128 bf16 = 4 KB) and, by wave 0, the
+    // head weights, into the wave's last buffer; then the first chunks
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q_idx) + ((int64_t)b * a.H_I + 16 * wave) * 256;
+    if (wave < MT) {
+        const uint32_t qm0 = ring_m0 + (uint32_t)((NBUF - 1) * kBuf);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dma16_s(qsrc, (uint32_t)(1024 * k + 16 * lane), qm0 + 1024u * (uint32_t)k);
+    }
+    const float* wstage = reinterpret_cast<const float*>(&ring[0][NBUF - 1][4096]);
+    if (wave == 0)
+        dma4_s(a.w + (int64_t)b * a.H_I, lane < a.H_I ? 4u * (uint32_t)lane : 0u, ring_m0 + (uint32_t)((NBUF - 1) * kBuf) + 4096u);
+    int issued = 0;
+    for (; issued < NBUF - 1 && issued < n_dma; ++issued) issue(issued);
+    if (NBUF == 3 && issued == 2) wait_vmcnt<2 * KI>();    // the queries have landed
+    else if (issued >= 1) wait_vmcnt<KI>();
+    else wait_vmcnt<0>();
+    __syncthreads();                                       // queries, weights staged; histograms cleared
+    ScanCtx<MT> C;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const uint8_t* qt = &ring[m][NBUF - 1][0];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) C.qa[m][t] = *reinterpret_cast<const u32x4*>(qt + col * 256 + (g * 32 + t * 8) * 2);
+        const f32x4 wv4 = *reinterpret_cast<const f32x4*>(&wstage[16 * m + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) C.wv[m][r] = wv4[r] * a.sigma;
+    }
+    __syncthreads();                                       // every wave holds them: the buffers are free
+
+    for (int it = 0; it < n_cap; ++it) {
+        const int lrow = (4 * it + wave) * kDmaRows;       // first row of the chunk within the block
+        if (it >= n_dma) {                                 // no visible row in the chunk
+            if (lane < kDmaRows) sc[lrow + lane] = -__builtin_inff();
+            continue;
+        }
+        // chunk it is complete once at most the chunks issued after it are in
+        // flight: it + 1 .. min(it + NBUF - 2, n_dma - 1)
+        if (NBUF == 3 && it + 1 < n_dma) wait_vmcnt<KI>();
+        else wait_vmcnt<0>();
+        // the buffer of chunk it - 1 (all of its reads consumed) takes chunk it + NBUF - 1
+        if (it + NBUF - 1 < n_dma) issue(it + NBUF - 1);
+        const int64_t r = chunk_row(it);
+        const uint8_t* buf = &ring[wave][it % NBUF][0];
+#pragma unroll
+        for (int tile = 0; tile < kDmaRows / 16; ++tile) {
+            const int rr = tile * 16 + col;
+            const bool valid = r + rr < nvis;
+            const uint8_t* rp = buf + rr * RB;
+            uint32_t w[8];
+            uint32_t sw = 0;
+            float mult = 1.0f;
+            if constexpr (FMT == MLA_FMT_E4M3_S128) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 32)[i];
+                mult = *reinterpret_cast<const float*>(rp + 128);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 16)[i];
+                sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
+            }
+            u32x4 kb[4];
+            dequant_key<FMT>(w, sw, kb);
+            const float score = tile_dot<MT>(C, kb, mult);
+            if (g == tile) {                               // one lane group per tile writes
+                sc[lrow + rr] = valid ? score : -__builtin_inff();
+                if (valid) {
+                    const uint32_t bin = score_key(score) >> (32 - kHistBits);
+                    atomicAdd(&hist2[bin >> 1], 1u << (16 * (bin & 1u)));
+                    atomicAdd(&coarse[bin / kFinePerCoarse], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    float* scores = a.scores + b * cap;
+    const int64_t nrows = min((int64_t)rows_per_block, cap - row0);
+    if (nrows == rows_per_block) {                         // scores + row0 is 512-byte aligned
+        for (int i = threadIdx.x; 4 * i < nrows; i += kScanThreads)
+            reinterpret_cast<f32x4*>(scores + row0)[i] = reinterpret_cast<const f32x4*>(sc)[i];
+    } else {
+        for (int i = threadIdx.x; i < nrows; i += kScanThreads) scores[row0 + i] = sc[i];
+    }
+    // histogram into this XCD's copy: thread t adds fine bins t + 256 i, so one
+    // instruction covers 64 consecutive bins
+    uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
+    const int copy = hist_copy_of_block();
+    uint32_t* fine = hist_fine(hb, copy);
+    uint32_t cnt[kHistBins / kScanThreads];
+#pragma unroll
+    for (int i = 0; i < kHistBins / kScanThreads; ++i) {
+        const int f = threadIdx.x + kScanThreads * i;
+        cnt[i] = (hist2[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
+    }
+#pragma unroll
+    for (int i = 0; i < kHistBins / kScanThreads; ++i)
+        if (cnt[i]) l2_add(&fine[threadIdx.x + kScanThreads * i], cnt[i]);
+    if (threadIdx.x < kCoarseBins && coarse[threadIdx.x])
+        l2_add(&hist_coarse(hb, copy)[threadIdx.x], coarse[threadIdx.x]);
 }
 
 // MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
@@ -272,7 +449,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
         tile_scores<MT>(C, kb, valid ? 1.0f : 0.0f, s, valid, g, a.sigma, a.capacity, scores, hist);
     }
     __syncthreads();
-    flush_hist(hist, a.hist + (int64_t)b * kHistBins);
+    flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
 }
 
 // ------------------------------------------------------------------------
@@ -327,11 +504,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_generic(ScanArgs a) {
         a.scores[b * a.capacity + s] = score;
     }
     __syncthreads();
-    uint32_t* gh = a.hist + (int64_t)b * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) {
-        const uint32_t v = hist[i];
-        if (v) atomicAdd(&gh[i], v);
-    }
+    flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
 }
 
 }  // namespace
@@ -355,13 +528,25 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         int64_t rpb = (a.capacity + per_seq - 1) / per_seq;
         rpb = ((rpb + 4 * kChunkRows - 1) / (4 * kChunkRows)) * (4 * kChunkRows);
         const dim3 sgrid((unsigned)((a.capacity + rpb - 1) / rpb), a.B);
+        // LDS-DMA scan: 16-byte aligned cache and stride; about kDmaBlocksPerCu blocks per CU
+        const bool dma = (reinterpret_cast<uintptr_t>(a.cache) % 16 == 0) && (a.stride % 16 == 0);
+        const int64_t dma_per_seq = (256 * kDmaBlocksPerCu + a.B - 1) / a.B;
+        int64_t drpb = (a.capacity + dma_per_seq - 1) / dma_per_seq;
+        drpb = ((drpb + 4 * kDmaRows - 1) / (4 * kDmaRows)) * (4 * kDmaRows);
+        drpb = std::min<int64_t>(std::max<int64_t>(drpb, 4 * kDmaRows), kDmaMaxRowsPerBlock);
+        const dim3 dgrid((unsigned)((a.capacity + drpb - 1) / drpb), a.B);
 #define MLA_SCAN_CASE(F, M)                                                                    \
     if (a.fmt == F && a.H_I == 16 * M) {                                                       \
         const ProfSlot p = prof_slot(PROF_SCAN);                                               \
-        if (F == MLA_FMT_BF16)                                                                 \
+        if constexpr (F == MLA_FMT_BF16) {                                                     \
             return launch_kernel(k_scan_bf16<M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a); \
-        return launch_kernel(k_scan_staged<F, M>, sgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, a, \
-                             (int)rpb);                                                        \
+        } else {                                                                               \
+            if (dma)                                                                           \
+                return launch_kernel(k_scan_dma<F, M, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, stream, \
+                                     p.start, p.stop, a, (int)drpb);                           \
+            return launch_kernel(k_scan_staged<F, M>, sgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, \
+                                 a, (int)rpb);                                                 \
+        }                                                                                      \
     }
         MLA_SCAN_CASE(MLA_FMT_BF16, 1) MLA_SCAN_CASE(MLA_FMT_BF16, 2)
         MLA_SCAN_CASE(MLA_FMT_BF16, 3) MLA_SCAN_CASE(MLA_FMT_BF16, 4)

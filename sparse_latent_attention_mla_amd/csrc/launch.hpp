@@ -11,7 +11,14 @@
 namespace mla {
 
 // Bins of the top-k score histogram (top 12 bits of the order-preserving key).
+// Every sequence has kHistCopiesHost copies of a 64-bin coarse level (top 6 bits)
+// followed by as many copies of the 4096-bin fine level; a scan workgroup adds
+// into the copy its block index selects, so that no bin takes atomics from every
+// workgroup of the sequence, and the selection sums the copies.
 constexpr int kHistBinsHost = 4096;
+constexpr int kHistCopiesHost = 8;
+constexpr int kCoarseBinsHost = 64;
+constexpr int64_t kHistWordsHost = (int64_t)kHistCopiesHost * (kCoarseBinsHost + kHistBinsHost);
 
 struct AppendArgs {
     int main_fmt, main_dim, main_rope;
@@ -36,7 +43,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // Workspace of the indexer + top-k, carved by the host (all 256-byte aligned).
 struct TopkWorkspace {
     float* scores;          // [B, capacity] (used when the caller gives no score buffer)
-    uint32_t* hist;         // [B, kHistBins]
+    uint32_t* hist;         // [B, kHistWordsHost]: coarse [copies][64], then fine [copies][4096]
     uint32_t* counts;       // [B, select workgroups, 2]: each workgroup's selected / candidate count
     int32_t* sel;           // [B, capacity]: workgroup i's selected positions at i * kSelRowsHost ..
     uint64_t* cand;         // [B, capacity]: workgroup i's candidates (key << 32 | ~position) likewise
@@ -57,7 +64,7 @@ struct ScanArgs {
     const int32_t* n_visible;
     int B, H_I, k;
     float* scores;          // [B, capacity]
-    uint32_t* hist;         // [B, bins]
+    uint32_t* hist;         // [B, kHistWordsHost] (see TopkWorkspace)
 };
 hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);

@@ -42,9 +42,12 @@ constexpr int64_t kRowPathMax = 16384;    // longest sequence on the one-workgro
 constexpr int kFinalLds = 6144;           // candidates kept in LDS (48 KB)
 constexpr int kMaxDigitBins = 1024;
 
+// grid (kHistCopies + 1, B): block j < kHistCopies clears fine copy j, the last the coarse copies
 __global__ void k_topk_clear(TopkWorkspace ws, int B) {
-    const int b = blockIdx.x;
-    for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) ws.hist[(int64_t)b * kHistBins + i] = 0u;
+    uint32_t* hb = ws.hist + (int64_t)blockIdx.y * kHistWordsHost;
+    u32x4* p = reinterpret_cast<u32x4*>(blockIdx.x < kHistCopies ? hist_fine(hb, blockIdx.x) : hb);
+    const int n = (blockIdx.x < kHistCopies ? kHistBins : kCoarseBins * kHistCopies) / 4;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
@@ -100,6 +103,35 @@ __device__ __forceinline__ DigitResult wave_find_digit(P h, int nbins, uint32_t 
     r.digit = __builtin_amdgcn_readlane(d, src);
     r.above = (uint32_t)__builtin_amdgcn_readlane((int)above, src);
     r.count = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
+    return r;
+}
+
+// The threshold bin of sequence b's histogram (fine bin d with sum_{e>d} < need
+// <= sum_{e>=d}; found = false when the total is below need), by one wave: lane l
+// sums the copies of coarse bin 63 - l, a prefix sum finds the coarse bin, then
+// the same over its 64 fine bins. Results are uniform across the wave.
+__device__ __forceinline__ DigitResult hist_find(uint32_t* hb, uint32_t need) {
+    const int lane = threadIdx.x & 63;
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kHistCopies; ++j) sum += hist_coarse(hb, j)[kCoarseBins - 1 - lane];
+    uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
+    uint64_t hit = __ballot(excl < need && incl >= need);
+    DigitResult r{0, 0u, 0u, hit != 0};
+    if (!r.found) return r;
+    int src = __builtin_ctzll(hit);
+    const int cb = kCoarseBins - 1 - src;
+    const uint32_t above_c = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+    sum = 0;
+#pragma unroll
+    for (int j = 0; j < kHistCopies; ++j) sum += hist_fine(hb, j)[cb * kFinePerCoarse + kFinePerCoarse - 1 - lane];
+    incl = wave_incl_scan(sum);
+    excl = incl - sum;
+    hit = __ballot(above_c + excl < need && above_c + incl >= need);
+    src = __builtin_ctzll(hit);                            // found: the coarse bin holds the need-th key
+    r.digit = cb * kFinePerCoarse + kFinePerCoarse - 1 - src;
+    r.above = above_c + (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+    r.count = (uint32_t)__builtin_amdgcn_readlane((int)sum, src);
     return r;
 }
 
@@ -230,7 +262,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     };
     load(0, v);                                          // in flight during the threshold search
     if (t < 64) {
-        const DigitResult r = wave_find_digit(ws.hist + (int64_t)b * kHistBins, kHistBins, (uint32_t)k);
+        const DigitResult r = hist_find(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);
         if (t == 0) {
             T_s = r.found ? r.digit : -1;                // -1: every visible row fits in k
             n_sel = 0;
@@ -320,7 +352,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
         v[i] = (s < nvis) ? sc[s] : 0.0f;
     }
     if (t < 64) {
-        const DigitResult r = wave_find_digit(ws.hist + (int64_t)b * kHistBins, kHistBins, (uint32_t)k);
+        const DigitResult r = hist_find(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);
         if (t == 0) {
             T_s = r.found ? r.digit : -1;
             n_sel = 0;
@@ -520,7 +552,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
 
 hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream) {
     if (B == 0) return hipSuccess;
-    return launch_kernel(k_topk_clear, dim3(B), dim3(256), 0, stream, nullptr, nullptr, ws, B);
+    return launch_kernel(k_topk_clear, dim3(kHistCopies + 1, B), dim3(256), 0, stream, nullptr, nullptr, ws, B);
 }
 
 // MLA_TOPK_PATH=row|multi forces a path (for tuning).

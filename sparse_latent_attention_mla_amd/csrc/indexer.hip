@@ -78,6 +78,8 @@ struct ScanCtx {
 // the tile; returns that row's score (every g holds it); `mult` is the row's
 // post-contraction factor.
 template <int MT>
+__device__ __forceinline__ float tile_epilogue(const ScanCtx<MT>& C, const f32x4 acc[MT], float mult);
+template <int MT>
 __device__ __forceinline__ float tile_dot(const ScanCtx<MT>& C, const u32x4 kb[4], float mult) {
     f32x4 acc[MT];
 #pragma unroll
@@ -86,6 +88,12 @@ __device__ __forceinline__ float tile_dot(const ScanCtx<MT>& C, const u32x4 kb[4
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(C.qa[m][t], kb[t], acc[m]);
+    return tile_epilogue<MT>(C, acc, mult);
+}
+
+// The row's score from its tile accumulators (every g holds it).
+template <int MT>
+__device__ __forceinline__ float tile_epilogue(const ScanCtx<MT>& C, const f32x4 acc[MT], float mult) {
     // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
     float pm[MT];                                         // one partial sum per head tile: short chains
 #pragma unroll
@@ -342,50 +350,66 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
     }
     __syncthreads();                                       // every wave holds them: the buffers are free
 
-    for (int it = 0; it < n_cap; ++it) {
-        const int lrow = (4 * it + wave) * kDmaRows;       // first row of the chunk within the block
-        if (it >= n_dma) {                                 // no visible row in the chunk
-            if (lane < kDmaRows) sc[lrow + lane] = -__builtin_inff();
-            continue;
+    // Software pipeline over the wave's 16-row tiles (two per chunk): the LDS
+    // reads and the dequantisation of tile n + 1 are issued between the MFMAs of
+    // tile n and its epilogue. Fetching the first tile of chunk c waits for that
+    // chunk (the chunks issued after it, c + 1 .. min(c + NBUF - 2, n_dma - 1),
+    // may still be in flight) and hands chunk c - 1's buffer, fully read by
+    // then, to chunk c + NBUF - 1.
+    struct TileIn {
+        u32x4 kb[4];
+        float mult;
+    };
+    auto fetch = [&](int c, int tile, TileIn& in) {
+        if (tile == 0) {
+            if (NBUF == 3 && c + 1 < n_dma) wait_vmcnt<KI>();
+            else wait_vmcnt<0>();
+            if (c + NBUF - 1 < n_dma) issue(c + NBUF - 1);
         }
-        // chunk it is complete once at most the chunks issued after it are in
-        // flight: it + 1 .. min(it + NBUF - 2, n_dma - 1)
-        if (NBUF == 3 && it + 1 < n_dma) wait_vmcnt<KI>();
-        else wait_vmcnt<0>();
-        // the buffer of chunk it - 1 (all of its reads consumed) takes chunk it + NBUF - 1
-        if (it + NBUF - 1 < n_dma) issue(it + NBUF - 1);
-        const int64_t r = chunk_row(it);
-        const uint8_t* buf = &ring[wave][it % NBUF][0];
+        const uint8_t* rp = &ring[wave][c % NBUF][0] + (tile * 16 + col) * RB;
+        uint32_t w[8];
+        uint32_t sw = 0;
+        in.mult = 1.0f;
+        if constexpr (FMT == MLA_FMT_E4M3_S128) {
 #pragma unroll
-        for (int tile = 0; tile < kDmaRows / 16; ++tile) {
-            const int rr = tile * 16 + col;
-            const bool valid = r + rr < nvis;
-            const uint8_t* rp = buf + rr * RB;
-            uint32_t w[8];
-            uint32_t sw = 0;
-            float mult = 1.0f;
-            if constexpr (FMT == MLA_FMT_E4M3_S128) {
+            for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 32)[i];
+            in.mult = *reinterpret_cast<const float*>(rp + 128);
+        } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 32)[i];
-                mult = *reinterpret_cast<const float*>(rp + 128);
-            } else {
+            for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 16)[i];
+            sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
+        }
+        dequant_key<FMT>(w, sw, in.kb);
+    };
+    const int n_tiles = 2 * n_dma;
+    TileIn cur;
+    if (n_tiles > 0) fetch(0, 0, cur);
+    for (int n = 0; n < n_tiles; ++n) {
+        const int c = n >> 1, tile = n & 1;
+        f32x4 acc[MT];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 16)[i];
-                sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
-            }
-            u32x4 kb[4];
-            dequant_key<FMT>(w, sw, kb);
-            const float score = tile_dot<MT>(C, kb, mult);
-            if (g == tile) {                               // one lane group per tile writes
-                sc[lrow + rr] = valid ? score : -__builtin_inff();
-                if (valid) {
-                    const uint32_t bin = score_key(score) >> (32 - kHistBits);
-                    atomicAdd(&hist2[bin >> 1], 1u << (16 * (bin & 1u)));
-                    atomicAdd(&coarse[bin / kFinePerCoarse], 1u);
-                }
+        for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(C.qa[m][t], cur.kb[t], acc[m]);
+        const float mult = cur.mult;
+        if (n + 1 < n_tiles) fetch((n + 1) >> 1, (n + 1) & 1, cur);
+        const float score = tile_epilogue<MT>(C, acc, mult);
+        const int rr = tile * 16 + col;
+        const int lrow = (4 * c + wave) * kDmaRows + rr;   // row within the block
+        if (g == tile) {                                   // one lane group per tile writes
+            const bool valid = row0 + lrow < nvis;
+            sc[lrow] = valid ? score : -__builtin_inff();
+            if (valid) {
+                const uint32_t bin = score_key(score) >> (32 - kHistBits);
+                atomicAdd(&hist2[bin >> 1], 1u << (16 * (bin & 1u)));
+                atomicAdd(&coarse[bin / kFinePerCoarse], 1u);
             }
         }
     }
+    for (int c = n_dma; c < n_cap; ++c)                     // chunks without a visible row
+        if (lane < kDmaRows) sc[(4 * c + wave) * kDmaRows + lane] = -__builtin_inff();
     __syncthreads();
     float* scores = a.scores + b * cap;
     const int64_t nrows = min((int64_t)rows_per_block, cap - row0);

@@ -153,6 +153,11 @@ __device__ __forceinline__ float xmax4(float x) {
     const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
     return fmaxf(u2f(b[0]), u2f(b[1]));
 }
+// Sum over lanes l and l ^ 32.
+__device__ __forceinline__ float xsum2(float x) {
+    const auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+    return u2f(b[0]) + u2f(b[1]);
+}
 __device__ __forceinline__ float xsum4(float x) {
     const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
     x = u2f(a[0]) + u2f(a[1]);
@@ -164,6 +169,13 @@ __device__ __forceinline__ float xsum4(float x) {
 // device: A lane l holds row (l % 16), k-slots 8*(l/16) .. +7; B lane l holds
 // column (l % 16), the same k-slots; D lane l, element r holds row
 // 4*(l/16) + r, column l % 16.
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+// 32x32x16 bf16: lane l holds A[l % 32][8 (l / 32) + e] and B[8 (l / 32) + e][l % 32];
+// register v of the result is D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

@@ -258,6 +258,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
     flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
 }
 
+// Histogram flush of the DMA scans: thread t holds the counts of fine bins
+// t + 256 i, so one instruction adds 64 consecutive bins; the coarse counts
+// (kept in LDS beside the fine ones) go by the first 64 threads.
+__device__ __forceinline__ void flush_fine_coarse(const uint32_t (&cnt)[kHistBins / kScanThreads],
+                                                  const uint32_t* coarse, uint32_t* hb, int copy) {
+    uint32_t* fine = hist_fine(hb, copy);
+#pragma unroll
+    for (int i = 0; i < kHistBins / kScanThreads; ++i)
+        if (cnt[i]) l2_add(&fine[threadIdx.x + kScanThreads * i], cnt[i]);
+    if (threadIdx.x < kCoarseBins && coarse[threadIdx.x]) l2_add(&hist_coarse(hb, copy)[threadIdx.x], coarse[threadIdx.x]);
+}
+
 // MFMA scan through LDS DMA, E4M3 (132 B) and E2M1 (72 B) rows, for caches
 // whose base and sequence stride are 16-byte aligned: a chunk of 32 rows is
 // then a 16-byte aligned run of 4224 or 2304 bytes. Each wave streams its own
@@ -430,11 +442,203 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
         const int f = threadIdx.x + kScanThreads * i;
         cnt[i] = (hist2[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
     }
+    flush_fine_coarse(cnt, coarse, hb, copy);
+}
+
+// The same scan with the 32x32x16 MFMA, for 32 or 64 indexer heads (MT2 head
+// tiles of 32). A 32-row chunk is one tile: lane l owns row l % 32 of the chunk
+// and channels 64 (l / 32) .. + 63 (k-step s of the lane is channels
+// 64 (l / 32) + 8 s + e, for queries and keys alike), so a row's score is the
+// sum over its lane's 16 heads per head tile plus the partner lane's (l ^ 32),
+// and the 32 scores of a chunk are written by lanes 0 .. 31 at once.
+template <int FMT, int MT2, int NBUF>
+__global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma32(ScanArgs a, int rows_per_block) {
+    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
+    constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
+    constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries + weights
+    static_assert(kBytes % 16 == 0, "chunk of 16-byte pieces");
+    static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
+    __shared__ uint32_t hist2[kHistBins / 2];
+    __shared__ uint32_t coarse[kCoarseBins];
+    __shared__ __attribute__((aligned(16))) float sc[kDmaMaxRowsPerBlock];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][NBUF][kBuf];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n32 = lane & 31, h = lane >> 5;
+    const int64_t cap = a.capacity;
+    const int64_t nvis = clamp_visible(a.n_visible[b], cap);
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+    const int n_it = rows_per_block / (4 * kDmaRows);
+    for (int i = threadIdx.x; i < kHistBins / 2; i += kScanThreads) hist2[i] = 0u;
+    if (threadIdx.x < kCoarseBins) coarse[threadIdx.x] = 0u;
+
+    const uint8_t* base = a.cache + b * a.stride;
+    auto chunk_row = [&](int it) { return row0 + (int64_t)(4 * it + wave) * kDmaRows; };
+    auto chunks_below = [&](int64_t lim) {
+        const int64_t d = lim - row0 - (int64_t)wave * kDmaRows;
+        if (d <= 0) return 0;
+        const int64_t n = (d + 4 * kDmaRows - 1) / (4 * kDmaRows);
+        return (int)(n < n_it ? n : n_it);
+    };
+    const int n_dma = chunks_below(nvis);
+    const int n_cap = chunks_below(cap);
+    const uint32_t ring_m0 = __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][0][0]));
+    // per-lane DMA offsets of a chunk that lies inside the sequence: the lanes
+    // past the chunk's bytes re-read its first 16
+    uint32_t full_off[KI];
 #pragma unroll
-    for (int i = 0; i < kHistBins / kScanThreads; ++i)
-        if (cnt[i]) l2_add(&fine[threadIdx.x + kScanThreads * i], cnt[i]);
-    if (threadIdx.x < kCoarseBins && coarse[threadIdx.x])
-        l2_add(&hist_coarse(hb, copy)[threadIdx.x], coarse[threadIdx.x]);
+    for (int k = 0; k < KI; ++k) {
+        const uint32_t o = (uint32_t)(1024 * k + 16 * lane);
+        full_off[k] = (o < (uint32_t)kBytes) ? o : 0u;
+    }
+    auto issue = [&](int it) {
+        const int64_t r = chunk_row(it);
+        const uint8_t* src = base + r * RB;
+        const int64_t left = (cap - r) * RB;
+        const uint32_t m0 = ring_m0 + (uint32_t)((it % NBUF) * kBuf);
+        if (left >= kBytes) {
+#pragma unroll
+            for (int k = 0; k < KI; ++k) dma16_s(src, full_off[k], m0 + 1024u * (uint32_t)k);
+        } else {                                           // the sequence ends inside the chunk
+#pragma unroll
+            for (int k = 0; k < KI; ++k) {
+                const uint32_t off = ((int64_t)full_off[k] + 16 > left) ? 0u : full_off[k];
+                dma16_s(src, off, m0 + 1024u * (uint32_t)k);
+            }
+        }
+    };
+    // queries of head tile `wave` (16 heads x 256 B) into the wave's last buffer
+    // with a 272-byte head stride (16-byte piece p of head hh at slot 17 hh + p),
+    // so that 16 lanes reading one piece of 16 heads hit distinct banks; the head
+    // weights (by wave 0) into the score buffer, unused until the chunks start
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q_idx) + ((int64_t)b * a.H_I + 16 * wave) * 256;
+    if (wave < 2 * MT2) {
+        const uint32_t qm0 = ring_m0 + (uint32_t)((NBUF - 1) * kBuf);
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const int j = 64 * k + lane, hh = j / 17, pc = j - 17 * hh;
+            const uint32_t off = (j < 272 && pc < 16) ? (uint32_t)(256 * hh + 16 * pc) : 0u;
+            dma16_s(qsrc, off, qm0 + 1024u * (uint32_t)k);
+        }
+    }
+    const float* wstage = sc;
+    if (wave == 0)
+        dma4_s(a.w + (int64_t)b * a.H_I, lane < a.H_I ? 4u * (uint32_t)lane : 0u,
+               __builtin_amdgcn_readfirstlane(lds_addr(sc)));
+    int issued = 0;
+    for (; issued < NBUF - 1 && issued < n_dma; ++issued) issue(issued);
+    if (NBUF == 3 && issued == 2) wait_vmcnt<2 * KI>();
+    else if (issued >= 1) wait_vmcnt<KI>();
+    else wait_vmcnt<0>();
+    __syncthreads();                                       // queries, weights staged; histograms cleared
+    u32x4 qa[MT2][8];                                      // head 32 mt + n32, channels 64 h + 8 s ..
+    float wv[MT2][16];                                     // w * sigma of result register v
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt) {
+        const int head = 32 * mt + n32;
+        const uint8_t* qt = &ring[head >> 4][NBUF - 1][0] + (head & 15) * 272 + 128 * h;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qt + 16 * s);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wstage[32 * mt + 8 * q + 4 * h]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[mt][4 * q + r] = w4[r] * a.sigma;
+        }
+    }
+    __syncthreads();                                       // every wave holds them: the buffers are free
+
+    // the codes of chunk c, dequantised: k-step s of this lane (waits for the
+    // chunk and hands chunk c - 1's buffer to chunk c + NBUF - 1 first)
+    struct ChunkIn {
+        u32x4 kb[8];
+        float mult;
+    };
+    auto fetch = [&](int c, ChunkIn& in) {
+        if (NBUF == 3 && c + 1 < n_dma) wait_vmcnt<KI>();
+        else wait_vmcnt<0>();
+        if (c + NBUF - 1 < n_dma) issue(c + NBUF - 1);
+        const uint8_t* rp = &ring[wave][c % NBUF][0] + n32 * RB;
+        in.mult = 1.0f;
+        if constexpr (FMT == MLA_FMT_E4M3_S128) {
+            uint32_t w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 64 * h)[i];
+            in.mult = *reinterpret_cast<const float*>(rp + 128);
+            dequant_key<FMT>(w, 0u, in.kb);
+            dequant_key<FMT>(w + 8, 0u, in.kb + 4);
+        } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 32 * h)[i];
+            const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
+            dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
+            dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+        }
+    };
+    ChunkIn cur;
+    if (n_dma > 0) fetch(0, cur);
+    for (int c = 0; c < n_dma; ++c) {
+        f32x16 acc[MT2];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT2; ++mt) acc[mt] = mfma32_bf16(qa[mt][s], cur.kb[s], acc[mt]);
+        const float mult = cur.mult;
+        if (c + 1 < n_dma) fetch(c + 1, cur);
+        // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
+        float pm[MT2][4];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                pm[mt][q] = wv[mt][4 * q] * relu(acc[mt][4 * q]);
+#pragma unroll
+                for (int r = 1; r < 4; ++r) pm[mt][q] += wv[mt][4 * q + r] * relu(acc[mt][4 * q + r]);
+            }
+        float part = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) part += (pm[mt][0] + pm[mt][1]) + (pm[mt][2] + pm[mt][3]);
+        const float score = xsum2(part) * mult;
+        const int lrow = (4 * c + wave) * kDmaRows + n32;  // row within the block
+        if (h == 0) {
+            const bool valid = row0 + lrow < nvis;
+            sc[lrow] = valid ? score : -__builtin_inff();
+            if (valid) {
+                const uint32_t bin = score_key(score) >> (32 - kHistBits);
+                atomicAdd(&hist2[bin >> 1], 1u << (16 * (bin & 1u)));
+                atomicAdd(&coarse[bin / kFinePerCoarse], 1u);
+            }
+        }
+    }
+    for (int c = n_dma; c < n_cap; ++c)                     // chunks without a visible row
+        if (lane < kDmaRows) sc[(4 * c + wave) * kDmaRows + lane] = -__builtin_inff();
+    __syncthreads();
+    float* scores = a.scores + b * cap;
+    const int64_t nrows = min((int64_t)rows_per_block, cap - row0);
+    if (nrows == rows_per_block) {
+        for (int i = threadIdx.x; 4 * i < nrows; i += kScanThreads)
+            reinterpret_cast<f32x4*>(scores + row0)[i] = reinterpret_cast<const f32x4*>(sc)[i];
+    } else {
+        for (int i = threadIdx.x; i < nrows; i += kScanThreads) scores[row0 + i] = sc[i];
+    }
+    uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
+    const int copy = hist_copy_of_block();
+    uint32_t* fine = hist_fine(hb, copy);
+    uint32_t cnt[kHistBins / kScanThreads];
+#pragma unroll
+    for (int i = 0; i < kHistBins / kScanThreads; ++i) {
+        const int f = threadIdx.x + kScanThreads * i;
+        cnt[i] = (hist2[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
+    }
+    flush_fine_coarse(cnt, coarse, hb, copy);
 }
 
 // MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
@@ -565,9 +769,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         if constexpr (F == MLA_FMT_BF16) {                                                     \
             return launch_kernel(k_scan_bf16<M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a); \
         } else {                                                                               \
-            if (dma)                                                                           \
-                return launch_kernel(k_scan_dma<F, M, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, stream, \
-                                     p.start, p.stop, a, (int)drpb);                           \
+            if (dma) {                                                                         \
+                if constexpr (M % 2 == 0)                                                      \
+                    return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, \
+                                         stream, p.start, p.stop, a, (int)drpb);               \
+                else                                                                           \
+                    return launch_kernel(k_scan_dma<F, M, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, \
+                                         stream, p.start, p.stop, a, (int)drpb);               \
+            }                                                                                  \
             return launch_kernel(k_scan_staged<F, M>, sgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, \
                                  a, (int)rpb);                                                 \
         }                                                                                      \

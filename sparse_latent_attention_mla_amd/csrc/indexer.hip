@@ -15,6 +15,7 @@
 // the accumulator in registers, and the top-k histogram of the score keys is
 // built in LDS, so the only outputs are the fp32 scores and the histogram.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -30,6 +31,11 @@ constexpr int kChunkRows = 64;            // rows a wave stages through LDS per 
 constexpr int kStagedBlocks = 512;        // target workgroups of the staged scan (2 per CU)
 constexpr int kDmaRows = 32;              // rows per chunk of the LDS-DMA scan
 constexpr int kDmaMaxRowsPerBlock = 1024;
+constexpr int kDmaRowsPerWave = 256;      // rows of a block per wave, at most (32x32 scan)
+#ifndef MLA_SCAN_WAVES
+#define MLA_SCAN_WAVES 4                  // waves per block of the 32x32 scan (4 or 8)
+#endif
+constexpr int kDma32Waves = MLA_SCAN_WAVES;
 #ifndef MLA_SCAN_NBUF
 #define MLA_SCAN_NBUF 3                   // chunk buffers per wave in the LDS-DMA scan
 #endif
@@ -261,12 +267,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
 // Histogram flush of the DMA scans: thread t holds the counts of fine bins
 // t + 256 i, so one instruction adds 64 consecutive bins; the coarse counts
 // (kept in LDS beside the fine ones) go by the first 64 threads.
-__device__ __forceinline__ void flush_fine_coarse(const uint32_t (&cnt)[kHistBins / kScanThreads],
-                                                  const uint32_t* coarse, uint32_t* hb, int copy) {
+template <int NT = kScanThreads>
+__device__ __forceinline__ void flush_fine_coarse(const uint32_t (&cnt)[kHistBins / NT], const uint32_t* coarse,
+                                                  uint32_t* hb, int copy) {
     uint32_t* fine = hist_fine(hb, copy);
 #pragma unroll
-    for (int i = 0; i < kHistBins / kScanThreads; ++i)
-        if (cnt[i]) l2_add(&fine[threadIdx.x + kScanThreads * i], cnt[i]);
+    for (int i = 0; i < kHistBins / NT; ++i)
+        if (cnt[i]) l2_add(&fine[threadIdx.x + NT * i], cnt[i]);
     if (threadIdx.x < kCoarseBins && coarse[threadIdx.x]) l2_add(&hist_coarse(hb, copy)[threadIdx.x], coarse[threadIdx.x]);
 }
 
@@ -451,8 +458,9 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
 // 64 (l / 32) + 8 s + e, for queries and keys alike), so a row's score is the
 // sum over its lane's 16 heads per head tile plus the partner lane's (l ^ 32),
 // and the 32 scores of a chunk are written by lanes 0 .. 31 at once.
-template <int FMT, int MT2, int NBUF>
-__global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma32(ScanArgs a, int rows_per_block) {
+template <int FMT, int MT2, int NBUF, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block) {
+    constexpr int NT = 64 * NW;                          // threads of the block
     constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
     constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
     constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
@@ -461,8 +469,8 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma32(Sc
     static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
     __shared__ uint32_t hist2[kHistBins / 2];
     __shared__ uint32_t coarse[kCoarseBins];
-    __shared__ __attribute__((aligned(16))) float sc[kDmaMaxRowsPerBlock];
-    __shared__ __attribute__((aligned(16))) uint8_t ring[4][NBUF][kBuf];
+    __shared__ __attribute__((aligned(16))) float sc[kDmaRowsPerWave * NW];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NBUF][kBuf];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -470,16 +478,16 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma32(Sc
     const int64_t cap = a.capacity;
     const int64_t nvis = clamp_visible(a.n_visible[b], cap);
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
-    const int n_it = rows_per_block / (4 * kDmaRows);
-    for (int i = threadIdx.x; i < kHistBins / 2; i += kScanThreads) hist2[i] = 0u;
+    const int n_it = rows_per_block / (NW * kDmaRows);
+    for (int i = threadIdx.x; i < kHistBins / 2; i += NT) hist2[i] = 0u;
     if (threadIdx.x < kCoarseBins) coarse[threadIdx.x] = 0u;
 
     const uint8_t* base = a.cache + b * a.stride;
-    auto chunk_row = [&](int it) { return row0 + (int64_t)(4 * it + wave) * kDmaRows; };
+    auto chunk_row = [&](int it) { return row0 + (int64_t)(NW * it + wave) * kDmaRows; };
     auto chunks_below = [&](int64_t lim) {
         const int64_t d = lim - row0 - (int64_t)wave * kDmaRows;
         if (d <= 0) return 0;
-        const int64_t n = (d + 4 * kDmaRows - 1) / (4 * kDmaRows);
+        const int64_t n = (d + NW * kDmaRows - 1) / (NW * kDmaRows);
         return (int)(n < n_it ? n : n_it);
     };
     const int n_dma = chunks_below(nvis);
@@ -607,7 +615,7 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma32(Sc
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt) part += (pm[mt][0] + pm[mt][1]) + (pm[mt][2] + pm[mt][3]);
         const float score = xsum2(part) * mult;
-        const int lrow = (4 * c + wave) * kDmaRows + n32;  // row within the block
+        const int lrow = (NW * c + wave) * kDmaRows + n32;  // row within the block
         if (h == 0) {
             const bool valid = row0 + lrow < nvis;
             sc[lrow] = valid ? score : -__builtin_inff();
@@ -619,26 +627,26 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma32(Sc
         }
     }
     for (int c = n_dma; c < n_cap; ++c)                     // chunks without a visible row
-        if (lane < kDmaRows) sc[(4 * c + wave) * kDmaRows + lane] = -__builtin_inff();
+        if (lane < kDmaRows) sc[(NW * c + wave) * kDmaRows + lane] = -__builtin_inff();
     __syncthreads();
     float* scores = a.scores + b * cap;
     const int64_t nrows = min((int64_t)rows_per_block, cap - row0);
     if (nrows == rows_per_block) {
-        for (int i = threadIdx.x; 4 * i < nrows; i += kScanThreads)
+        for (int i = threadIdx.x; 4 * i < nrows; i += NT)
             reinterpret_cast<f32x4*>(scores + row0)[i] = reinterpret_cast<const f32x4*>(sc)[i];
     } else {
-        for (int i = threadIdx.x; i < nrows; i += kScanThreads) scores[row0 + i] = sc[i];
+        for (int i = threadIdx.x; i < nrows; i += NT) scores[row0 + i] = sc[i];
     }
     uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
     const int copy = hist_copy_of_block();
     uint32_t* fine = hist_fine(hb, copy);
-    uint32_t cnt[kHistBins / kScanThreads];
+    uint32_t cnt[kHistBins / NT];
 #pragma unroll
-    for (int i = 0; i < kHistBins / kScanThreads; ++i) {
-        const int f = threadIdx.x + kScanThreads * i;
+    for (int i = 0; i < kHistBins / NT; ++i) {
+        const int f = threadIdx.x + NT * i;
         cnt[i] = (hist2[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
     }
-    flush_fine_coarse(cnt, coarse, hb, copy);
+    flush_fine_coarse<NT>(cnt, coarse, hb, copy);
 }
 
 // MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
@@ -758,11 +766,25 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         const dim3 sgrid((unsigned)((a.capacity + rpb - 1) / rpb), a.B);
         // LDS-DMA scan: 16-byte aligned cache and stride; about kDmaBlocksPerCu blocks per CU
         const bool dma = (reinterpret_cast<uintptr_t>(a.cache) % 16 == 0) && (a.stride % 16 == 0);
-        const int64_t dma_per_seq = (256 * kDmaBlocksPerCu + a.B - 1) / a.B;
+        // MLA_SCAN_BLOCKS overrides the target number of blocks (for tuning)
+        int64_t dma_target = 256 * kDmaBlocksPerCu;
+        if (const char* e = getenv("MLA_SCAN_BLOCKS")) {
+            const int64_t v = atoll(e);
+            if (v >= 1 && v <= 65536) dma_target = v;
+        }
+        const int64_t dma_per_seq = (dma_target + a.B - 1) / a.B;
         int64_t drpb = (a.capacity + dma_per_seq - 1) / dma_per_seq;
         drpb = ((drpb + 4 * kDmaRows - 1) / (4 * kDmaRows)) * (4 * kDmaRows);
         drpb = std::min<int64_t>(std::max<int64_t>(drpb, 4 * kDmaRows), kDmaMaxRowsPerBlock);
         const dim3 dgrid((unsigned)((a.capacity + drpb - 1) / drpb), a.B);
+        // the 32x32 scan: blocks of kDma32Waves waves, as many as the CUs hold at once
+        const int64_t blk32 = (int64_t)(dma_target * 4 / kDma32Waves);
+        const int64_t per_seq32 = (blk32 + a.B - 1) / a.B;
+        const int64_t unit32 = (int64_t)kDma32Waves * kDmaRows;
+        int64_t d32rpb = (a.capacity + per_seq32 - 1) / per_seq32;
+        d32rpb = ((d32rpb + unit32 - 1) / unit32) * unit32;
+        d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), (int64_t)kDmaRowsPerWave * kDma32Waves);
+        const dim3 d32grid((unsigned)((a.capacity + d32rpb - 1) / d32rpb), a.B);
 #define MLA_SCAN_CASE(F, M)                                                                    \
     if (a.fmt == F && a.H_I == 16 * M) {                                                       \
         const ProfSlot p = prof_slot(PROF_SCAN);                                               \
@@ -771,8 +793,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         } else {                                                                               \
             if (dma) {                                                                         \
                 if constexpr (M % 2 == 0)                                                      \
-                    return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, \
-                                         stream, p.start, p.stop, a, (int)drpb);               \
+                    return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves>, d32grid,     \
+                                         dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb); \
                 else                                                                           \
                     return launch_kernel(k_scan_dma<F, M, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, \
                                          stream, p.start, p.stop, a, (int)drpb);               \

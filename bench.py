@@ -219,7 +219,7 @@ def main():
     idx_out = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
     out = torch.empty((B, H, cfg.d_v), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    ws_topk = torch.empty(M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device=dev)
+    ws_topk = torch.zeros(M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(max(1, M.mla_sparse_decode_workspace(mr, cfg.d_v, B, H, k, cfg.W)), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()

@@ -196,7 +196,8 @@ def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_vi
                      out_idx, workspace, out_scores=None, stream=None):
     """Indexer scan + mask + top-k.  q_idx [B, H_I, d_I] (bf16; fp32 for F32 rows), w fp32 [B, H_I],
     idx_cache uint8 [B, capacity, row_bytes], n_visible int32 [B], out_idx int32 [B, k],
-    workspace uint8 of mla_indexer_topk_workspace bytes, out_scores fp32 [B, capacity] (optional)."""
+    workspace uint8 of mla_indexer_topk_workspace bytes, zeroed before its first use (every
+    successful call leaves it ready for the next), out_scores fp32 [B, capacity] (optional)."""
     _need(q_idx, "q_idx", query_dtype(idx_row), 3)
     _need(w, "w", torch.float32, 2)
     _need(n_visible, "n_visible", torch.int32, 1)

@@ -71,9 +71,11 @@ TopkLayout topk_layout(int32_t B, int64_t capacity) {
     TopkLayout L;
     const size_t b = B > 0 ? (size_t)B : 0, cap = capacity > 0 ? (size_t)capacity : 0;
     const size_t groups = capacity > 0 ? (size_t)mla::select_groups(capacity) : 0;
-    L.scores = 0;
-    L.hist = L.scores + round256(b * cap * sizeof(float));
-    L.counts = L.hist + round256(b * (size_t)mla::kHistWordsHost * sizeof(uint32_t));
+    // the histogram first, at a place that depends on nothing but the sequence, so
+    // that what a call leaves zeroed stays the histogram whatever the next call's sizes
+    L.hist = 0;
+    L.scores = L.hist + round256(b * (size_t)mla::kHistWordsHost * sizeof(uint32_t));
+    L.counts = L.scores + round256(b * cap * sizeof(float));
     L.sel = L.counts + round256(b * groups * 2 * sizeof(uint32_t));
     L.cand = L.sel + round256(b * cap * sizeof(int32_t));
     L.cand2 = L.cand + round256(b * cap * sizeof(uint64_t));
@@ -219,8 +221,6 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     T.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
     T.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = mla::launch_topk_clear(T, B, st);
-    if (e != hipSuccess) return hip_status(e, "indexer_topk clear");
     mla::ScanArgs a{};
     a.fmt = idx_row.fmt;
     a.dim = idx_row.dim;
@@ -237,7 +237,7 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     a.k = k;
     a.scores = T.scores;
     a.hist = T.hist;
-    e = mla::launch_scan(a, st);
+    hipError_t e = mla::launch_scan(a, st);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
     e = mla::launch_select(T.scores, capacity, n_visible, B, k, T, out_idx, st);
     return hip_status(e, "top-k select");

@@ -66,7 +66,6 @@ struct ScanArgs {
     float* scores;          // [B, capacity]
     uint32_t* hist;         // [B, kHistWordsHost] (see TopkWorkspace)
 };
-hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 bool scan_supported(int fmt, int dim, int H_I);
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,

@@ -42,14 +42,6 @@ constexpr int64_t kRowPathMax = 16384;    // longest sequence on the one-workgro
 constexpr int kFinalLds = 6144;           // candidates kept in LDS (48 KB)
 constexpr int kMaxDigitBins = 1024;
 
-// grid (kHistCopies + 1, B): block j < kHistCopies clears fine copy j, the last the coarse copies
-__global__ void k_topk_clear(TopkWorkspace ws, int B) {
-    uint32_t* hb = ws.hist + (int64_t)blockIdx.y * kHistWordsHost;
-    u32x4* p = reinterpret_cast<u32x4*>(blockIdx.x < kHistCopies ? hist_fine(hb, blockIdx.x) : hb);
-    const int n = (blockIdx.x < kHistCopies ? kHistBins : kCoarseBins * kHistCopies) / 4;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = u32x4{0u, 0u, 0u, 0u};
-}
-
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
@@ -64,6 +56,35 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);   // row_bcast:15
     v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);   // row_bcast:31
     return v;
+}
+
+// Zero sequence b's histogram (all copies) once its threshold has been read, so
+// that the next call's scan finds it cleared. Called by every thread of a block.
+__device__ __forceinline__ void zero_hist(uint32_t* hb) {
+    u32x4* p = reinterpret_cast<u32x4*>(hb);
+    for (int i = threadIdx.x; i < (int)(kHistWordsHost / 4); i += blockDim.x) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// What k_select leaves of the zeroing: the coarse level and, when there is a
+// threshold, the fine bins of its coarse bin (found again from the coarse level,
+// as the threshold search does). Called by every thread of a block of >= 128.
+__device__ __forceinline__ void zero_hist_rest(uint32_t* hb, uint32_t need) {
+    __shared__ int cb_s;
+    const int t = threadIdx.x, lane = t & 63;
+    if (t < 64) {
+        uint32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < kHistCopies; ++j) sum += hist_coarse(hb, j)[kCoarseBins - 1 - lane];
+        const uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
+        const uint64_t hit = __ballot(excl < need && incl >= need);
+        if (t == 0) cb_s = hit ? kCoarseBins - 1 - __builtin_ctzll(hit) : -1;
+    }
+    __syncthreads();
+    const int cb = cb_s;
+    if (cb >= 0 && t < kHistCopies * kFinePerCoarse / 4)       // 8 copies x 64 bins, 4 per thread
+        reinterpret_cast<u32x4*>(hist_fine(hb, t / (kFinePerCoarse / 4)) + cb * kFinePerCoarse)[t % (kFinePerCoarse / 4)] =
+            u32x4{0u, 0u, 0u, 0u};
+    if (t < kHistCopies * kCoarseBins / 4) reinterpret_cast<u32x4*>(hb)[t] = u32x4{0u, 0u, 0u, 0u};
 }
 
 // Digit search by one wave over counts h[0 .. nbins) (nbins a multiple of 64, at most
@@ -325,6 +346,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     if (t == 0) cursor = nsel;
     __syncthreads();
     const uint32_t need = (want > nsel) ? want - nsel : 0u;
+    zero_hist(ws.hist + (int64_t)b * kHistWordsHost);     // read above; the stores drain during the radix
     radix_take_any<kRowThreads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
     for (uint32_t i = want + t; i < (uint32_t)k; i += kRowThreads) out[i] = -1;
@@ -361,6 +383,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     }
     __syncthreads();
     const int T = T_s;
+    // this workgroup's share of zeroing the fine histogram for the next call: every
+    // workgroup of the sequence finds the same threshold, so only the 64 fine bins of
+    // the threshold's coarse bin (which the others may still be reading, and which
+    // k_select_final clears) are skipped
+    {
+        uint32_t* fine0 = hist_fine(ws.hist + (int64_t)b * kHistWordsHost, 0);
+        constexpr int kFineWords = kHistCopies * kHistBins;
+        const int per = (kFineWords / 4 + gridDim.x - 1) / gridDim.x;   // u32x4 per workgroup
+        const int cb = T >= 0 ? T / kFinePerCoarse : -1;
+        for (int i = blockIdx.x * per + t; i < (int)(blockIdx.x + 1) * per && i < kFineWords / 4; i += kSelThreads)
+            if (((4 * i) % kHistBins) / kFinePerCoarse != cb)
+                reinterpret_cast<u32x4*>(fine0)[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     uint32_t key[kPer];
     uint64_t mt[kPer], mc[kPer];
     uint32_t nt = 0, nc = 0;
@@ -543,17 +578,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
     for (int i = t; i < kMaxDigitBins; i += kSelThreads) L.h[0][i] = 0u;
     __syncthreads();
     const uint32_t need = (want > nsel) ? want - nsel : 0u;
+    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);   // the stores drain during the radix
     radix_take_any<kSelThreads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
     for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out[i] = -1;
 }
 
 }  // namespace
-
-hipError_t launch_topk_clear(const TopkWorkspace& ws, int B, hipStream_t stream) {
-    if (B == 0) return hipSuccess;
-    return launch_kernel(k_topk_clear, dim3(kHistCopies + 1, B), dim3(256), 0, stream, nullptr, nullptr, ws, B);
-}
 
 // MLA_TOPK_PATH=row|multi forces a path (for tuning).
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,

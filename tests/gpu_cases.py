@@ -132,14 +132,16 @@ def oracle_attention(case: Case, layer: int, idx: np.ndarray):
 
 
 # ---- GPU calls ------------------------------------------------------------
-def gpu_topk(case: Case, layer_idx: int = 0, n_visible=None, k=None, want_scores=True):
+def gpu_topk(case: Case, layer_idx: int = 0, n_visible=None, k=None, want_scores=True, ws=None):
+    """ws: a workspace to (re)use; by default a fresh zeroed one."""
     cfg = case.cfg
     k = cfg.k if k is None else k
     nv = case.n_visible if n_visible is None else n_visible
     B, N = cfg.B, cfg.N
     out_idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
     scores = torch.empty((B, N), dtype=torch.float32, device=DEV) if want_scores else None
-    ws = torch.empty(M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device=DEV)
+    if ws is None:
+        ws = torch.zeros(M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device=DEV)
     M.mla_indexer_topk(idx_row(cfg), _qi_gpu(cfg, case.inp.q_idx[layer_idx]), _t(case.inp.w[layer_idx]),
                        cfg.sigma, case.g_idx, _t(nv), k, out_idx, ws, out_scores=scores)
     torch.cuda.synchronize()

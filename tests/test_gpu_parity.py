@@ -36,7 +36,7 @@ def say(*a):
     print("[gpu-parity]", *a, file=sys.stderr, flush=True)
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=4)
 def case_of(name):
     cfg = SMALL.get(name) or FULL[name]
     say("building", name, f"B={cfg.B} N={cfg.N} H={cfg.H} fmt={cfg.main_fmt}/{cfg.idx_fmt} W={cfg.W}")
@@ -220,7 +220,7 @@ def test_topk_exact_ties(fmt, k, path, monkeypatch):
     G.M.mla_kv_append_quant(G.M.Row(fmt, d, 0), G.M.Row(fmt, d, 0), None, G._t(rows), G._t(slots), None, g_cache)
     out_idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     out_s = torch.empty((B, N), dtype=torch.float32, device="cuda")
-    ws = torch.empty(G.M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(G.M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device="cuda")
     say("topk ties", fmt, k, path)
     G.M.mla_indexer_topk(G.M.Row(fmt, d, 0), G._t(q_idx, torch.bfloat16), G._t(w), 1.0, g_cache, G._t(nv), k,
                          out_idx, ws, out_scores=out_s)
@@ -287,3 +287,20 @@ def test_full_size(name):
         got_o, got_l = G.gpu_decode(case, layer, ref_idx[layer])
         wo, wl = G.check_attention(got_o, got_l, ref_o, ref_l)
         say(f"  worst rel err out {wo:.2e} lse {wl:.2e}")
+
+
+def test_topk_workspace_reused_across_shapes(monkeypatch):
+    """One workspace, zeroed once, serves calls of different batch sizes,
+    capacities, formats and selection paths in a row: each call must leave the
+    histogram part zeroed for the next."""
+    cases = [case_of(n) for n in ("c3s", "c2s", "c4s")]
+    size = max(G.M.mla_indexer_topk_workspace(c.cfg.B, c.cfg.N, c.cfg.k) for c in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for name, path in (("c3s", "multi"), ("c2s", "row"), ("c3s", "row"), ("c4s", "multi"), ("c3s", "multi"),
+                       ("c2s", "multi")):
+        monkeypatch.setenv("MLA_TOPK_PATH", path)
+        case = case_of(name)
+        say("workspace reuse", name, path)
+        got_idx, _ = G.gpu_topk(case, 0, ws=ws, want_scores=False)
+        ref_s = G.oracle_scores(case, 0)
+        G.check_topk(got_idx, ref_s, case.n_visible, case.cfg.k)

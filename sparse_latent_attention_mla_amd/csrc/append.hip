@@ -65,30 +65,76 @@ __device__ void quant_row(int fmt, int dim, int rope, const float* __restrict__ 
     }
 }
 
+constexpr int kStageMain = 2048;           // rows up to these sizes are staged through LDS
+constexpr int kStageIdx = 1024;
+
+// Every global load of the block (slot, new rows, window entry) is issued at
+// entry, before any of them is used, so the block pays one memory round trip;
+// the rows then wait in LDS for the quantisers.
 __global__ __launch_bounds__(kThreads) void k_append(AppendArgs a) {
-    __shared__ uint32_t amax_bits[64];          // dim/16 <= 64 (dim <= 1024)
-    const int i = blockIdx.x, b = blockIdx.y;
-    if ((a.main_cache || a.idx_cache) && i < a.n_new) {
-        const int64_t slot = a.slots[(int64_t)b * a.n_new + i];
-        if (slot >= 0 && slot < a.capacity) {
-            if (a.main_cache) {
-                const int D = a.main_dim + a.main_rope;
-                quant_row(a.main_fmt, a.main_dim, a.main_rope, a.new_main + ((int64_t)b * a.n_new + i) * D,
-                          a.main_cache + b * a.main_stride + slot * a.main_row_bytes, amax_bits);
-                __syncthreads();
-            }
-            if (a.idx_cache) {
-                quant_row(a.idx_fmt, a.idx_dim, 0, a.new_idx + ((int64_t)b * a.n_new + i) * a.idx_dim,
-                          a.idx_cache + b * a.idx_stride + slot * a.idx_row_bytes, amax_bits);
-            }
+    __shared__ uint32_t amax_bits[64];          // dim/16 <= 64 (dim <= 1024), dim/128 <= 64
+    __shared__ float s_main[kStageMain];
+    __shared__ float s_idx[kStageIdx];
+    const int i = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const bool rows = (a.main_cache || a.idx_cache) && i < a.n_new;
+    const int D = a.main_dim + a.main_rope;
+    const int64_t e = (int64_t)b * a.n_new + i;
+    const float* gmain = (rows && a.main_cache) ? a.new_main + e * D : nullptr;
+    const float* gidx = (rows && a.idx_cache) ? a.new_idx + e * a.idx_dim : nullptr;
+    const bool stage = D <= kStageMain && a.idx_dim <= kStageIdx;
+    const int64_t slot = rows ? a.slots[e] : -1;
+    float vm[kStageMain / kThreads], vi[kStageIdx / kThreads];
+    if (stage) {
+#pragma unroll
+        for (int j = 0; j < kStageMain / kThreads; ++j) {
+            const int c = t + kThreads * j;
+            vm[j] = (gmain && c < D) ? gmain[c] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kStageIdx / kThreads; ++j) {
+            const int c = t + kThreads * j;
+            vi[j] = (gidx && c < a.idx_dim) ? gidx[c] : 0.0f;
         }
     }
-    if (a.win_ring && i == 0) {
-        const int pos = a.win_pos[b];
-        if (pos >= 0) {
-            uint16_t* dst = a.win_ring + ((int64_t)b * a.W + pos % a.W) * a.Dw;
-            const float* src = a.new_win + (int64_t)b * a.Dw;
-            for (int c = threadIdx.x; c < a.Dw; c += kThreads) dst[c] = (uint16_t)bf16_rne(src[c]);
+    const bool win = a.win_ring && i == 0;
+    const int pos = win ? a.win_pos[b] : -1;
+    const float* wsrc = a.new_win + (int64_t)b * a.Dw;
+    float vw[kStageMain / kThreads];
+    const bool wstage = win && a.Dw <= kStageMain;
+    if (wstage) {
+#pragma unroll
+        for (int j = 0; j < kStageMain / kThreads; ++j) {
+            const int c = t + kThreads * j;
+            vw[j] = (c < a.Dw) ? wsrc[c] : 0.0f;
+        }
+    }
+    if (stage) {
+#pragma unroll
+        for (int j = 0; j < kStageMain / kThreads; ++j) s_main[t + kThreads * j] = vm[j];
+#pragma unroll
+        for (int j = 0; j < kStageIdx / kThreads; ++j) s_idx[t + kThreads * j] = vi[j];
+        __syncthreads();
+    }
+    if (rows && slot >= 0 && slot < a.capacity) {
+        if (gmain) {
+            quant_row(a.main_fmt, a.main_dim, a.main_rope, stage ? s_main : gmain,
+                      a.main_cache + b * a.main_stride + slot * a.main_row_bytes, amax_bits);
+            __syncthreads();
+        }
+        if (gidx)
+            quant_row(a.idx_fmt, a.idx_dim, 0, stage ? s_idx : gidx,
+                      a.idx_cache + b * a.idx_stride + slot * a.idx_row_bytes, amax_bits);
+    }
+    if (win && pos >= 0) {
+        uint16_t* dst = a.win_ring + ((int64_t)b * a.W + pos % a.W) * a.Dw;
+        if (wstage) {
+#pragma unroll
+            for (int j = 0; j < kStageMain / kThreads; ++j) {
+                const int c = t + kThreads * j;
+                if (c < a.Dw) dst[c] = (uint16_t)bf16_rne(vw[j]);
+            }
+        } else {
+            for (int c = t; c < a.Dw; c += kThreads) dst[c] = (uint16_t)bf16_rne(wsrc[c]);
         }
     }
 }

@@ -46,7 +46,7 @@ namespace {
 #endif
 constexpr int kChunk = 32;                 // rows per pipeline step
 constexpr int kDv = 512;
-constexpr int kThreads = 256;
+constexpr int kMaxWaves = 8;             // waves of a workgroup: 4 or 8
 constexpr int kMaxRps = 256;               // rows per split: one row index per thread
 constexpr int kZs = 36;                    // floats per (head) score row in LDS: 32 rows + pad
 constexpr int kMergeThreads = kDv / 4;
@@ -67,18 +67,24 @@ struct Stage {
     static constexpr int kPieces = kStride / 16;                  // 16-byte slots per staged row
     static constexpr int kDataPieces = kRowBytes / 16;            // of which hold row bytes (direct)
     static constexpr int kInstr = (kChunk * kPieces + 63) / 64;   // direct loads per chunk, 64 slots each
-    static constexpr int kHi = (kInstr + 3) / 4;                  // per-wave load count, waves w < kInstr % 4
-    static constexpr int kLo = kInstr / 4;                        // the other waves
     static constexpr int kBytes = kDirect ? kInstr * 1024 : kChunk * kStride;
     static constexpr int kBufs = SRC == SRC_E4M3 ? MLA_E4M3_BUFS : 2;  // chunk buffers
     static constexpr int kLds = kBufs * kBytes;
 };
 
-// Dynamic LDS: row indices of the split | scores [2 parities][KH][16 HT heads][kZs] | chunk buffers.
+// Dynamic LDS: row indices of the split | scores [2 parities][KP][16 HT heads][kZs] | chunk buffers.
+// The waves of a workgroup are 2 row tiles x HT head tiles x KP parts of the K
+// width for QK, and NW slices of the 512 value channels for PV.
 constexpr int kLdsIdx = 0;
 constexpr int kLdsZ = kMaxRps * 4;
-constexpr int kLdsZBytes = 2 * 2 * 16 * kZs * 4;            // KH * HT == 2 in both layouts
-constexpr int kLdsBuf = kLdsZ + kLdsZBytes;
+template <int NW, int HT>
+struct Waves {
+    static constexpr int KP = NW / (2 * HT);               // K parts
+    static constexpr int kZBytes = 2 * KP * HT * 16 * kZs * 4;
+    static constexpr int kBuf = kLdsZ + kZBytes;            // offset of the chunk buffers
+    static constexpr int CPW = kDv / NW;                    // value channels per wave
+    static constexpr int MTW = CPW / 16;                    // 16-channel output tiles per wave
+};
 
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
@@ -134,7 +140,7 @@ __device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 w) {
 // (32..256, multiple of 32) and MLA_DECODE_HT (1 or 2) override the choice for
 // tuning; the workspace query reads them too.
 struct Geometry {
-    int ht, rps, S_main, S_win, groups;
+    int ht, nw, rps, S_main, S_win, groups;
 };
 
 Geometry decode_geometry(int B, int H, int k, int W) {
@@ -145,6 +151,13 @@ Geometry decode_geometry(int B, int H, int k, int W) {
         if (v == 2 && H % 32 == 0) g.ht = 2;
     }
     g.groups = H / (16 * g.ht);
+    // waves per workgroup: 8 (wave-specialised: half stage and score chunk c + 1 while
+    // the other half runs softmax and PV on chunk c) unless MLA_DECODE_NW=4; two head
+    // tiles per workgroup, and E2M1 rows (staged through registers), use 4
+    g.nw = 8;
+    if (const char* e = getenv("MLA_DECODE_NW"))
+        if (atoi(e) == 4) g.nw = 4;
+    if (g.ht == 2) g.nw = 4;
     int rps = 0;
     if (const char* e = getenv("MLA_DECODE_RPS")) {
         const int v = atoi(e);
@@ -166,10 +179,15 @@ Geometry decode_geometry(int B, int H, int k, int W) {
     return g;
 }
 
-template <int SRC_MAIN, int DQK>
+template <int SRC_MAIN, int DQK, int NW, int HT>
 constexpr int decode_lds_bytes(bool window) {
-    constexpr int m = Stage<SRC_MAIN, DQK>::kLds, w = Stage<SRC_BF16, DQK>::kLds;
-    return kLdsBuf + ((window && w > m) ? w : m);
+    if constexpr (NW == 8) {                               // wave-specialised: four chunk buffers
+        constexpr int m = 4 * Stage<SRC_MAIN, DQK>::kBytes, w = 4 * Stage<SRC_BF16, DQK>::kBytes;
+        return Waves<4, 1>::kBuf + ((window && w > m) ? w : m);
+    } else {
+        constexpr int m = Stage<SRC_MAIN, DQK>::kLds, w = Stage<SRC_BF16, DQK>::kLds;
+        return Waves<NW, HT>::kBuf + ((window && w > m) ? w : m);
+    }
 }
 
 // E2M1 rows through registers: 32 rows x 16 pieces (32 channels each) per chunk.
@@ -180,27 +198,34 @@ struct Fp4Slot {
 };
 
 // One split of one workgroup. SRC is the kind of the rows (the window is bf16).
-template <int SRC, int DQK, int HT>
+template <int SRC, int DQK, int NW, int HT>
 __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
                                              bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
     using G = Stage<SRC, DQK>;
+    using V = Waves<NW, HT>;
+    constexpr int NT = 64 * NW;
     constexpr int NB = G::kBufs;
-    constexpr int KH = (HT == 1) ? 2 : 1;                 // K halves split over waves
+    constexpr int KP = V::KP;                             // K parts split over waves
+    constexpr int kHi = (G::kInstr + NW - 1) / NW;        // per-wave load count, waves w < kInstr % NW
+    constexpr int kLo = G::kInstr / NW;                   // the other waves
     constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
-    constexpr int NMAIN_W = (HT == 1) ? 8 : 16;           // main k-steps per wave
-    constexpr int NROPE_W = (HT == 1) ? NROPE / 2 : NROPE;
+    constexpr int NMAIN_W = 16 / KP;                      // main k-steps per wave
+    // RoPE k-steps per wave: all of them with one K part, else step kp for the parts kp < NROPE
+    constexpr int NROPE_W = (KP == 1) ? NROPE : (NROPE > 0 ? 1 : 0);
     constexpr int NQ = NMAIN_W + NROPE_W;
+    static_assert(KP >= 1 && 16 % KP == 0 && (KP == 1 || NROPE <= KP), "wave layout");
     constexpr float kLazy = 8.0f;                         // P <= 2^8 before the reference max moves
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, g = lane >> 4;
     const int rt = w & 1;                                   // QK row tile
-    const int kh = (HT == 1) ? (w >> 1) : 0;                // QK K half
-    const int qt = (HT == 1) ? 0 : (w >> 1);                // QK head tile
+    const int kp = (w >> 1) % KP;                           // QK K part
+    const int qt = (w >> 1) / KP;                           // QK head tile
+    const bool rope_here = (KP == 1) || kp < NROPE;         // the wave's RoPE step exists
     const int nc = (n + kChunk - 1) / kChunk;
     int32_t* ridx = reinterpret_cast<int32_t*>(smem + kLdsIdx);
     float* zs = reinterpret_cast<float*>(smem + kLdsZ);
-    uint8_t* bufs = smem + kLdsBuf;
+    uint8_t* bufs = smem + V::kBuf;
     constexpr float kLog2e = 1.4426950408889634f;
     const float zscale = a.scale * kLog2e;
 
@@ -211,12 +236,13 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head) * DQK + 8 * g;
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
-            const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
+            const int rs = (KP == 1) ? (i - NMAIN_W) : kp;     // RoPE step of slot i >= NMAIN_W
+            const int t = (i < NMAIN_W) ? (NMAIN_W * kp + i) : (16 + (rope_here ? rs : 0));
             qv[i] = *reinterpret_cast<const u32x4*>(qp + 32 * t);
         }
     }
     // ---- row indices of the split (-1: no row)
-    {
+    if (tid < kMaxRps) {
         int32_t r = -1;
         if (tid < n) {
             if (is_win) r = (int32_t)(first + tid);
@@ -233,14 +259,14 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
                                      : a.cache + b * a.stride;
     const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;   // at most 2 KiB
     const uint32_t buf_m0 = __builtin_amdgcn_readfirstlane(lds_addr(bufs));
-    // direct path: the lane's slots are the same in every chunk; slot (i) = 64 (w + 4 i) + lane
+    // direct path: the lane's slots are the same in every chunk; slot (i) = 64 (w + NW i) + lane
     // row in chunk (kChunk: none), byte offset in the row, whether the slot holds row bytes
-    int slot_row[G::kHi];
-    uint32_t slot_off[G::kHi];
-    bool slot_data[G::kHi];
+    int slot_row[kHi];
+    uint32_t slot_off[kHi];
+    bool slot_data[kHi];
 #pragma unroll
-    for (int i = 0; i < G::kHi; ++i) {
-        const int s = 64 * (w + 4 * i) + lane;
+    for (int i = 0; i < kHi; ++i) {
+        const int s = 64 * (w + NW * i) + lane;
         const int u = s / G::kPieces, p = s - u * G::kPieces;
         slot_row[i] = u < kChunk ? u : kChunk;
         slot_off[i] = 16u * (uint32_t)p;
@@ -250,12 +276,12 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
     auto issue = [&](int c) -> uint32_t {
         uint32_t zm = 0;
         const uint32_t m0 = buf_m0 + (uint32_t)((c % NB) * G::kBytes);
-        int32_t rr[G::kHi];
+        int32_t rr[kHi];
 #pragma unroll
-        for (int i = 0; i < G::kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
-        const void* src[G::kHi];
+        for (int i = 0; i < kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
+        const void* src[kHi];
 #pragma unroll
-        for (int i = 0; i < G::kHi; ++i) {
+        for (int i = 0; i < kHi; ++i) {
             const bool row_ok = slot_row[i] < kChunk && rr[i] >= 0;
             zm |= (slot_row[i] < kChunk && rr[i] < 0) ? (1u << i) : 0u;
             // computed for every slot and selected without branching; slots without row
@@ -266,16 +292,17 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
             src[i] = reinterpret_cast<const void*>(use ? row : reinterpret_cast<uint64_t>(a.q));
         }
 #pragma unroll
-        for (int i = 0; i < G::kHi; ++i)
-            if (w + 4 * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(w + 4 * i));
+        for (int i = 0; i < kHi; ++i)
+            if (w + NW * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(w + NW * i));
         return zm;
     };
-    // register path (E2M1): 2 pieces of 32 channels per thread per chunk
-    Fp4Slot fs[2];
+    // register path (E2M1): 512 pieces of 32 channels per chunk, 512 / NT per thread
+    constexpr int kFp4Per = 512 / NT;
+    Fp4Slot fs[kFp4Per];
     auto fp4_load = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int item = tid + kThreads * i;
+        for (int i = 0; i < kFp4Per; ++i) {
+            const int item = tid + NT * i;
             const int u = item >> 4, p = item & 15;
             const int32_t r = ridx[kChunk * c + u];
             fs[i].ok = r >= 0;
@@ -289,8 +316,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
     auto fp4_store = [&](int c) {
         uint8_t* buf = bufs + (c % NB) * G::kBytes;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int item = tid + kThreads * i;
+        for (int i = 0; i < kFp4Per; ++i) {
+            const int item = tid + NT * i;
             const int u = item >> 4, p = item & 15;
             u32x4* d = reinterpret_cast<u32x4*>(buf + u * G::kStride + 64 * p);
             const float s0 = fs[i].ok ? e4m3_to_f32(fs[i].sc & 0xFFu) : 0.0f;
@@ -309,11 +336,11 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
     };
 
     // ---- running state: reference max (base 2, lazily raised), per-lane partial sums, output tile
-    f32x4 o[HT][8];
+    f32x4 o[HT][V::MTW];
 #pragma unroll
     for (int h = 0; h < HT; ++h)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[h][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < V::MTW; ++mt) o[h][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_ref[HT], l_run[HT];
 #pragma unroll
     for (int h = 0; h < HT; ++h) {
@@ -334,17 +361,17 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
         if constexpr (G::kDirect) {
             // chunk c has landed once at most the later chunk's loads are outstanding
             if ((NB > 2) && (c + 1 < nc)) {
-                if (w < (G::kInstr & 3) || (G::kInstr & 3) == 0) wait_vmcnt<G::kHi>();
-                else wait_vmcnt<G::kLo>();
+                if (w < (G::kInstr % NW) || (G::kInstr % NW) == 0) wait_vmcnt<kHi>();
+                else wait_vmcnt<kLo>();
             } else {
                 wait_vmcnt<0>();
             }
             // rows without bytes read as zeros (their P is 0; stand-in bytes could decode to NaN)
             if (__builtin_amdgcn_ballot_w64(zm0 != 0u)) {
 #pragma unroll
-                for (int i = 0; i < G::kHi; ++i)
+                for (int i = 0; i < kHi; ++i)
                     if (zm0 & (1u << i))
-                        *reinterpret_cast<u32x4*>(buf + 16 * (64 * (w + 4 * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
+                        *reinterpret_cast<u32x4*>(buf + 16 * (64 * (w + NW * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
             }
         } else {
             fp4_store(c);
@@ -368,7 +395,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
             if constexpr (SRC == SRC_E4M3) {
 #pragma unroll
                 for (int bb = 0; bb < NMAIN_W / 4; ++bb) {
-                    const int blk = (NMAIN_W / 4) * kh + bb;
+                    const int blk = (NMAIN_W / 4) * kp + bb;
                     f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4) {
@@ -383,18 +410,21 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
                 }
 #pragma unroll
                 for (int i = 0; i < NROPE_W; ++i) {
-                    const int t = NROPE_W * kh + i;            // RoPE k-step within the 64 RoPE channels
-                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 528 + 2 * (32 * t + 8 * g)),
-                                    qv[NMAIN_W + i], acc);
+                    const int t = (KP == 1) ? i : kp;          // RoPE k-step within the 64 RoPE channels
+                    if (rope_here)
+                        acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 528 + 2 * (32 * t + 8 * g)),
+                                        qv[NMAIN_W + i], acc);
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < NQ; ++i) {
-                    const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
-                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * t + 8 * g)), qv[i], acc);
+                    const int rs = (KP == 1) ? (i - NMAIN_W) : kp;
+                    const int t = (i < NMAIN_W) ? (NMAIN_W * kp + i) : (16 + rs);
+                    if (i < NMAIN_W || rope_here)
+                        acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * t + 8 * g)), qv[i], acc);
                 }
             }
-            float* zd = zs + (((c & 1) * KH + kh) * 16 * HT + 16 * qt + j) * kZs + 16 * rt + 4 * g;
+            float* zd = zs + (((c & 1) * KP + kp) * 16 * HT + 16 * qt + j) * kZs + 16 * rt + 4 * g;
             *reinterpret_cast<f32x4*>(zd) = acc;
         }
         __syncthreads();                                    // scores of chunk c complete
@@ -414,21 +444,23 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
         if constexpr (SRC == SRC_E4M3) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 + 4 * w);
+                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 +
+                                                        4 * ((V::CPW * w) / 128));
         }
         float z[HT][8], alpha[HT];
         bool grow = false;
 #pragma unroll
         for (int h = 0; h < HT; ++h) {
-            const float* zr = zs + (((c & 1) * KH) * 16 * HT + 16 * h + j) * kZs + 8 * g;
+            const float* zr = zs + (((c & 1) * KP) * 16 * HT + 16 * h + j) * kZs + 8 * g;
             const f32x4 a0 = *reinterpret_cast<const f32x4*>(zr), a1 = *reinterpret_cast<const f32x4*>(zr + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 z[h][e] = a0[e];
                 z[h][4 + e] = a1[e];
             }
-            if constexpr (KH == 2) {
-                const float* zr2 = zr + 16 * HT * kZs;
+#pragma unroll
+            for (int p = 1; p < KP; ++p) {                  // the other K parts' partial scores
+                const float* zr2 = zr + p * 16 * HT * kZs;
                 const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr2), b1 = *reinterpret_cast<const f32x4*>(zr2 + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -455,7 +487,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
             for (int h = 0; h < HT; ++h) {
                 l_run[h] *= alpha[h];
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) o[h][mt] = o[h][mt] * alpha[h];
+                for (int mt = 0; mt < V::MTW; ++mt) o[h][mt] = o[h][mt] * alpha[h];
             }
         }
         u32x4 pa[HT], pb[HT];                               // PV B operands: P (times the E4M3 scale) as bf16 hi, lo
@@ -473,10 +505,10 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
             split_bf16x8(p, pa[h], pb[h]);
         }
 
-        // ---- PV: O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels 128 w .. +127
+        // ---- PV: O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels CPW w .. + CPW - 1
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int c0 = 128 * w + 16 * mt;
+        for (int mt = 0; mt < V::MTW; ++mt) {
+            const int c0 = V::CPW * w + 16 * mt;
             u32x4 av;
             if constexpr (SRC == SRC_E4M3) {
                 // lane (G, m) names row 8 G + m / 2, channels c0 + 8 (m & 1) ..; receives channel c0 + m of rows 8 G ..
@@ -495,7 +527,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
         }
     }
 
-    // ---- partial: normalised output (channels 128 w ..) and logsumexp of the split
+    // ---- partial: normalised output (channels CPW w ..) and logsumexp of the split
 #pragma unroll
     for (int h = 0; h < HT; ++h) {
         const float l = xsum4(l_run[h]);
@@ -503,8 +535,8 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
         const int64_t prow = ((int64_t)b * S + split) * a.H + head;
         const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * w + 16 * mt + 4 * g) =
+        for (int mt = 0; mt < V::MTW; ++mt)
+            *reinterpret_cast<float4*>(o_part + prow * kDv + V::CPW * w + 16 * mt + 4 * g) =
                 make_float4(o[h][mt][0] * f, o[h][mt][1] * f, o[h][mt][2] * f, o[h][mt][3] * f);
         if (w == 0 && g == 0)
             lse_part[prow] = (l > 0.0f) ? (m_ref[h] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
@@ -512,11 +544,294 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
     }
 }
 
+// Wave-specialised split (8 waves, one head tile of 16, rows staged by LDS DMA):
+// waves 0 .. 3 stage the chunks and compute the scores of chunk c + 1 (2 row
+// tiles x 2 K halves) while waves 4 .. 7 run the softmax and the PV product of
+// chunk c (128 value channels each), so the two halves of a chunk's work
+// overlap and there is one barrier per chunk. Before that barrier the QK waves
+// wait for their own loads of chunk c + 2, which the barrier then makes visible
+// to all. Four chunk buffers: c (PV), c + 1 (QK), c + 2 (landed), c + 3 (in flight).
+template <int SRC, int DQK>
+__device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
+                                                bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
+    using G = Stage<SRC, DQK>;
+    using V = Waves<4, 1>;                                  // score layout of the 4 QK waves
+    static_assert(G::kDirect, "rows staged by DMA");
+    constexpr int NB = 4;
+    constexpr int kHi = (G::kInstr + 3) / 4;              // loads per QK wave, waves q < kInstr % 4
+    constexpr int kLo = G::kInstr / 4;
+    constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
+    constexpr int NMAIN_W = 8;                            // main k-steps per QK wave
+    constexpr int NROPE_W = NROPE / 2;
+    constexpr int NQ = NMAIN_W + NROPE_W;
+    constexpr float kLazy = 8.0f;                         // P <= 2^8 before the reference max moves
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool qk_role = w < 4;
+    const int q = w & 3;                                    // the wave's index within its role
+    const int j = lane & 15, g = lane >> 4;
+    const int rt = q & 1, kh = q >> 1;                      // QK row tile, K half
+    const int nc = (n + kChunk - 1) / kChunk;
+    int32_t* ridx = reinterpret_cast<int32_t*>(smem + kLdsIdx);
+    float* zs = reinterpret_cast<float*>(smem + kLdsZ);
+    uint8_t* bufs = smem + V::kBuf;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float zscale = a.scale * kLog2e;
+
+    // ---- QK waves: queries of their K half; k-step t covers channels 32 t .. 32 t + 31
+    u32x4 qv[NQ];
+    if (qk_role) {
+        const int head = 16 * hg + j;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head) * DQK + 8 * g;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
+            qv[i] = *reinterpret_cast<const u32x4*>(qp + 32 * t);
+        }
+    }
+    // ---- row indices of the split (-1: no row)
+    if (tid < kMaxRps) {
+        int32_t r = -1;
+        if (tid < n) {
+            if (is_win) r = (int32_t)(first + tid);
+            else {
+                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
+                if (s >= 0 && s < a.capacity) r = s;
+            }
+        }
+        ridx[tid] = r;
+    }
+    __syncthreads();
+
+    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
+                                     : a.cache + b * a.stride;
+    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;   // at most 2 KiB
+    const uint32_t buf_m0 = __builtin_amdgcn_readfirstlane(lds_addr(bufs));
+    // QK waves' DMA slots: slot (i) = 64 (q + 4 i) + lane, the same in every chunk
+    int slot_row[kHi];
+    uint32_t slot_off[kHi];
+    bool slot_data[kHi];
+#pragma unroll
+    for (int i = 0; i < kHi; ++i) {
+        const int s = 64 * (q + 4 * i) + lane;
+        const int u = s / G::kPieces, p = s - u * G::kPieces;
+        slot_row[i] = u < kChunk ? u : kChunk;
+        slot_off[i] = 16u * (uint32_t)p;
+        slot_data[i] = u < kChunk && p < G::kDataPieces;
+    }
+    auto issue = [&](int c) -> uint32_t {                   // returns the slots whose row has no bytes
+        uint32_t zm = 0;
+        const uint32_t m0 = buf_m0 + (uint32_t)((c % NB) * G::kBytes);
+        int32_t rr[kHi];
+#pragma unroll
+        for (int i = 0; i < kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
+        const void* src[kHi];
+#pragma unroll
+        for (int i = 0; i < kHi; ++i) {
+            const bool row_ok = slot_row[i] < kChunk && rr[i] >= 0;
+            zm |= (slot_row[i] < kChunk && rr[i] < 0) ? (1u << i) : 0u;
+            const uint64_t row = reinterpret_cast<uint64_t>(row_base + slot_off[i]) +
+                                 (uint64_t)(uint32_t)(rr[i] < 0 ? 0 : rr[i]) * row_bytes;
+            const bool use = row_ok && slot_data[i];
+            src[i] = reinterpret_cast<const void*>(use ? row : reinterpret_cast<uint64_t>(a.q));
+        }
+#pragma unroll
+        for (int i = 0; i < kHi; ++i)
+            if (q + 4 * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(q + 4 * i));
+        return zm;
+    };
+    // wait for chunk c (the `later` chunks issued after it, 0 .. 2, may stay in flight)
+    // and zero its slots without row bytes (their P is 0; stand-in bytes could decode to NaN)
+    auto land = [&](int c, int later, uint32_t zm) {
+        const bool hi = q < (G::kInstr & 3) || (G::kInstr & 3) == 0;
+        if (later >= 2) {
+            if (hi) wait_vmcnt<2 * kHi>();
+            else wait_vmcnt<2 * kLo>();
+        } else if (later == 1) {
+            if (hi) wait_vmcnt<kHi>();
+            else wait_vmcnt<kLo>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        if (__builtin_amdgcn_ballot_w64(zm != 0u)) {
+            uint8_t* buf = bufs + (c % NB) * G::kBytes;
+#pragma unroll
+            for (int i = 0; i < kHi; ++i)
+                if (zm & (1u << i))
+                    *reinterpret_cast<u32x4*>(buf + 16 * (64 * (q + 4 * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // scores of chunk c (rows 16 rt .. +15, the wave's K half) into parity c & 1
+    auto qk = [&](int c) {
+        const uint8_t* buf = bufs + (c % NB) * G::kBytes;
+        const uint8_t* krow = buf + (16 * rt + j) * G::kStride;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+            for (int bb = 0; bb < NMAIN_W / 4; ++bb) {
+                const int blk = (NMAIN_W / 4) * kh + bb;
+                f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int t = 4 * blk + s4;
+                    const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * t + 8 * g);
+                    t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[4 * bb + s4], t4);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[r] += t4[r] * *reinterpret_cast<const float*>(buf + (16 * rt + 4 * g + r) * G::kStride +
+                                                                    512 + 4 * blk);
+            }
+#pragma unroll
+            for (int i = 0; i < NROPE_W; ++i) {
+                const int t = NROPE_W * kh + i;
+                acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 528 + 2 * (32 * t + 8 * g)), qv[NMAIN_W + i],
+                                acc);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
+                acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * t + 8 * g)), qv[i], acc);
+            }
+        }
+        float* zd = zs + (((c & 1) * 2 + kh) * 16 + j) * kZs + 16 * rt + 4 * g;
+        *reinterpret_cast<f32x4*>(zd) = acc;
+    };
+
+    // ---- PV waves' running state: reference max (base 2, lazily raised), partial sums, output tile
+    f32x4 o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -__builtin_inff(), l_run = 0.0f;
+    auto pv = [&](int c) {
+        const uint8_t* buf = bufs + (c % NB) * G::kBytes;
+        // softmax on the chunk; lane (j, g) holds rows 8 g .. 8 g + 7 of head j
+        bool vld[8];
+        {
+            const int32_t* rp = ridx + kChunk * c + 8 * g;
+            const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp), r1 = *reinterpret_cast<const u32x4*>(rp + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vld[e] = (int32_t)r0[e] >= 0;
+                vld[4 + e] = (int32_t)r1[e] >= 0;
+            }
+        }
+        float sc[8];                                        // E4M3: the rows' scale of block q
+        if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 + 4 * q);
+        }
+        float z[8];
+        {
+            const float* zr = zs + (((c & 1) * 2) * 16 + j) * kZs + 8 * g;
+            const float* zr2 = zr + 16 * kZs;
+            const f32x4 a0 = *reinterpret_cast<const f32x4*>(zr), a1 = *reinterpret_cast<const f32x4*>(zr + 4);
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr2), b1 = *reinterpret_cast<const f32x4*>(zr2 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[e] = a0[e] + b0[e];
+                z[4 + e] = a1[e] + b1[e];
+            }
+        }
+        float cm = -__builtin_inff();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            z[e] = vld[e] ? z[e] * zscale : -__builtin_inff();
+            cm = fmaxf(cm, z[e]);
+        }
+        cm = xmax4(cm);
+        // the reference moves only when the chunk exceeds it by more than 2^kLazy (and on
+        // the first chunk with a visible row, where the factor is exp2(-inf) = 0 on empty state)
+        const bool up = cm > m_ref + kLazy;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - cm) : 1.0f;
+        m_ref = up ? cm : m_ref;
+        if (__builtin_amdgcn_ballot_w64(up)) {
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] = o[mt] * alpha;
+        }
+        u32x4 pa, pb;                                       // PV B operands: P (times the E4M3 scale), bf16 hi + lo
+        {
+            float ls = 0.0f;
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p[e] = (z[e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[e] - m_ref);
+                ls += p[e];
+                if constexpr (SRC == SRC_E4M3) p[e] *= sc[e];
+            }
+            l_run += ls;
+            split_bf16x8(p, pa, pb);
+        }
+        // O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels 128 q .. +127
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const int c0 = 128 * q + 16 * mt;
+            u32x4 av;
+            if constexpr (SRC == SRC_E4M3) {
+                av = e4m3x8_to_bf16(ds_tr8(buf + (8 * g + (j >> 1)) * G::kStride + c0 + 8 * (j & 1)));
+            } else {
+                const uint8_t* vp = buf + (8 * g + (j >> 2)) * G::kStride + 2 * (c0 + 4 * (j & 3));
+                const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * G::kStride);
+                av = u32x4{r0.x, r0.y, r1.x, r1.y};
+            }
+            o[mt] = mfma_bf16(av, pa, o[mt]);
+            o[mt] = mfma_bf16(av, pb, o[mt]);
+        }
+    };
+
+    // ---- prologue: chunks 0 .. 2 in flight, chunk 0 landed and scored, chunk 1 landed
+    uint32_t zm0 = 0, zm1 = 0, zm2 = 0;                     // zero masks of chunks c + 1, c + 2, c + 3
+    if (qk_role) {
+        uint32_t z0 = 0;
+        if (nc > 0) z0 = issue(0);
+        if (nc > 1) zm0 = issue(1);
+        if (nc > 2) zm1 = issue(2);
+        if (nc > 0) land(0, min(2, nc - 1), z0);
+    }
+    __syncthreads();
+    if (qk_role) {
+        if (nc > 0) qk(0);
+        if (nc > 1) land(1, nc > 2 ? 1 : 0, zm0);
+    }
+    __syncthreads();
+
+    for (int c = 0; c < nc; ++c) {
+        if (qk_role) {
+            if (c + 3 < nc) zm2 = issue(c + 3);            // into chunk c - 1's buffer (read before the barrier)
+            if (c + 1 < nc) qk(c + 1);
+            if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
+            zm1 = zm2;
+            zm2 = 0;
+        } else {
+            pv(c);
+        }
+        __syncthreads();
+    }
+
+    // ---- partial: normalised output (channels 128 q ..) and logsumexp of the split
+    if (!qk_role) {
+        const float l = xsum4(l_run);
+        const int head = 16 * hg + j;
+        const int64_t prow = ((int64_t)b * S + split) * a.H + head;
+        const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * q + 16 * mt + 4 * g) =
+                make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
+        if (q == 0 && g == 0)
+            lse_part[prow] = (l > 0.0f) ? (m_ref + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
+                                        : -__builtin_inff();
+    }
+}
+
 // Work item order: consecutive items are the head groups of one split; items
 // [x * per, (x + 1) * per) run on XCD x (workgroups go to XCDs round-robin).
-template <int SRC_MAIN, int DQK, int HT>
-__global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps, int groups,
-                                                          int n_items, float* o_part, float* lse_part) {
+template <int SRC_MAIN, int DQK, int NW, int HT>
+__global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps, int groups,
+                                                         int n_items, float* o_part, float* lse_part) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int L = blockIdx.x;
     const int per = gridDim.x >> 3;
@@ -530,13 +845,19 @@ __global__ __launch_bounds__(kThreads) void k_decode_mfma(DecodeArgs a, int S_ma
     if (split < S_main) {
         const int64_t first = (int64_t)split * rps;
         const int n = (int)((a.k - first < rps) ? a.k - first : rps);
-        decode_split<SRC_MAIN, DQK, HT>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
+        if constexpr (NW == 8)
+            decode_split_ws<SRC_MAIN, DQK>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
+        else
+            decode_split<SRC_MAIN, DQK, NW, HT>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
     } else {
         const int64_t first = (int64_t)(split - S_main) * rps;
         const int wl = (int)clamp_visible(a.win_len[b], a.W);
         int n = (int)(wl - first);
         n = n < 0 ? 0 : (n > rps ? rps : n);
-        decode_split<SRC_BF16, DQK, HT>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+        if constexpr (NW == 8)
+            decode_split_ws<SRC_BF16, DQK>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+        else
+            decode_split<SRC_BF16, DQK, NW, HT>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
     }
 }
 
@@ -696,25 +1017,34 @@ size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H,
     return ((o + 255) & ~(size_t)255) + ((l + 255) & ~(size_t)255);
 }
 
-template <int SRC_MAIN, int DQK, int HT>
+template <int SRC_MAIN, int DQK, int NW, int HT>
 static hipError_t launch_mfma(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
                               hipStream_t stream) {
     const int S = g.S_main + g.S_win;
     const int n_items = a.B * S * g.groups;
     const int grid = (n_items + 7) / 8 * 8;
-    const int lds = decode_lds_bytes<SRC_MAIN, DQK>(g.S_win > 0);
-    auto kern = k_decode_mfma<SRC_MAIN, DQK, HT>;
+    const int lds = decode_lds_bytes<SRC_MAIN, DQK, NW, HT>(g.S_win > 0);
+    auto kern = k_decode_mfma<SRC_MAIN, DQK, NW, HT>;
     static bool attr_set = false;                          // dynamic LDS above 64 KiB, once per kernel
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 decode_lds_bytes<SRC_MAIN, DQK>(true));
+                                                 decode_lds_bytes<SRC_MAIN, DQK, NW, HT>(true));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const ProfSlot p = prof_slot(PROF_DECODE);
-    return launch_kernel(kern, dim3(grid), dim3(kThreads), lds, stream, p.start, p.stop, a, g.S_main, g.S_win, g.rps,
-                         g.groups, n_items, o_part, lse_part);
+    return launch_kernel(kern, dim3(grid), dim3(64 * NW), lds, stream, p.start, p.stop, a, g.S_main, g.S_win,
+                         g.rps, g.groups, n_items, o_part, lse_part);
+}
+
+template <int SRC_MAIN, int DQK>
+static hipError_t launch_layout(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
+                                hipStream_t stream) {
+    if (g.ht == 2) return launch_mfma<SRC_MAIN, DQK, 4, 2>(a, g, o_part, lse_part, stream);
+    if constexpr (SRC_MAIN != SRC_FP4)                     // rows staged by DMA: wave-specialised
+        if (g.nw == 8) return launch_mfma<SRC_MAIN, DQK, 8, 1>(a, g, o_part, lse_part, stream);
+    return launch_mfma<SRC_MAIN, DQK, 4, 1>(a, g, o_part, lse_part, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -730,19 +1060,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     float* lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + o_bytes);
     if (S > 0) {
         hipError_t e = hipSuccess;
-        const bool two = g.ht == 2;
-        if (a.fmt == MLA_FMT_E4M3_S128)
-            e = two ? launch_mfma<SRC_E4M3, 576, 2>(a, g, o_part, lse_part, stream)
-                    : launch_mfma<SRC_E4M3, 576, 1>(a, g, o_part, lse_part, stream);
-        else if (a.fmt == MLA_FMT_E2M1_S16)
-            e = two ? launch_mfma<SRC_FP4, 512, 2>(a, g, o_part, lse_part, stream)
-                    : launch_mfma<SRC_FP4, 512, 1>(a, g, o_part, lse_part, stream);
-        else if (a.rope == 64)
-            e = two ? launch_mfma<SRC_BF16, 576, 2>(a, g, o_part, lse_part, stream)
-                    : launch_mfma<SRC_BF16, 576, 1>(a, g, o_part, lse_part, stream);
-        else
-            e = two ? launch_mfma<SRC_BF16, 512, 2>(a, g, o_part, lse_part, stream)
-                    : launch_mfma<SRC_BF16, 512, 1>(a, g, o_part, lse_part, stream);
+        if (a.fmt == MLA_FMT_E4M3_S128) e = launch_layout<SRC_E4M3, 576>(a, g, o_part, lse_part, stream);
+        else if (a.fmt == MLA_FMT_E2M1_S16) e = launch_layout<SRC_FP4, 512>(a, g, o_part, lse_part, stream);
+        else if (a.rope == 64) e = launch_layout<SRC_BF16, 576>(a, g, o_part, lse_part, stream);
+        else e = launch_layout<SRC_BF16, 512>(a, g, o_part, lse_part, stream);
         if (e != hipSuccess) return e;
     }
     const ProfSlot p = prof_slot(PROF_MERGE);

@@ -9,25 +9,27 @@
 // per head group, [P1] "DeepSeek-V3.2", "The lightning indexer").
 //
 // MFMA path (H a multiple of 16 up to 128, d_v = 512, K width 576 = 512 + 64 or 512):
-//   one workgroup (4 waves) per (b, split, group of 16 * HT heads); a split is
-//   `rps` <= 256 consecutive entries of idx[b] (or of the window ring). Work items
-//   are laid out so that the head groups of one split run on the same XCD and
-//   share its L2. The split's rows stream through LDS in 32-row chunks:
+//   one workgroup per (b, split, group of 16 heads); a split is `rps` <= 256
+//   consecutive entries of idx[b] (or of the window ring). Work items are laid
+//   out so that the head groups of one split run on the same XCD and share its
+//   L2. The split's rows stream through LDS in 32-row chunks:
 //   * E4M3 and bf16 rows are gathered straight from HBM into LDS
-//     (global_load_lds_dwordx4, two or three chunks in flight); E2M1 rows pass
+//     (global_load_lds_dwordx4, several chunks in flight); E2M1 rows pass
 //     through registers and are staged dequantised to bf16 (exact).
-//   * QK: wave w takes rows 16 (w & 1) .. +15 of the chunk and either half of the
-//     K width (HT = 1) or head tile w >> 1 (HT = 2); K comes from the staged rows
-//     (E4M3 codes widened exactly to bf16, one accumulator per 128-channel block
-//     times the row's fp32 scale), queries sit in registers, bf16 MFMA.
-//   * Scores meet in LDS; every wave runs the same online softmax on them.
-//   * PV: wave w owns value channels 128 w .. +127 for all heads of the
-//     workgroup, so its fp32 output tile is 32 registers per head tile. V^T
+//   * QK: a wave takes rows 16 rt .. +15 of the chunk and one part of the K
+//     width; K comes from the staged rows (E4M3 codes widened exactly to bf16,
+//     one accumulator per 128-channel block times the row's fp32 scale),
+//     queries sit in registers, bf16 MFMA. Partial scores meet in LDS.
+//   * Softmax: online, with a lazily raised reference maximum, on every PV wave.
+//   * PV: a wave owns a slice of the 512 value channels for all 16 heads. V^T
 //     operands come from the staged rows through the transposing LDS reads
-//     (ds_read_b64_tr_b8 for E4M3 codes, ds_read_b64_tr_b16 for bf16). E4M3:
-//     fp16 MFMA with P times the row's block scale over the largest block scale
-//     seen so far (<= 1, rescaled when it grows); bf16: bf16 MFMA with P split
-//     into a high and a low part.
+//     (ds_read_b64_tr_b8 for E4M3 codes, ds_read_b64_tr_b16 for bf16); bf16
+//     MFMA with P (times the row's block scale for E4M3) split into a high and
+//     a low bf16 part.
+//   Layouts: rows staged by DMA use 8 wave-specialised waves (decode_split_ws:
+//   4 waves stage and score chunk c + 1 while 4 run softmax and PV on chunk c,
+//   one barrier per chunk); E2M1 rows, two head tiles per workgroup or
+//   MLA_DECODE_NW=4 use 4 waves that take both roles in turn (decode_split).
 //   The split's normalised output and logsumexp are written as a partial and
 //   k_merge combines the partials by logsumexp.
 // Generic path (any other shape): one workgroup per (b, h), fp32 on the vector

@@ -482,6 +482,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
         const uint64_t* __restrict__ gcnd = ws.cand + b * capacity + (int64_t)g0 * kSelRows;
         // the first 64 entries of 16 workgroups' lists per wave are loaded together with the
         // counts (whatever the counts turn out to be: the slots exist, stale entries are dropped)
+        // the counts first: loads return in order, and the prefix sums need only them
+        uint32_t cs = 0, cc = 0;
+        if (gi < groups) {
+            const u32x2 cnt = *reinterpret_cast<const u32x2*>(ws.counts + ((int64_t)b * groups + gi) * 2);
+            cs = cnt.x;
+            cc = cnt.y;
+        }
         int32_t vs[kGU];
         uint64_t vc[kGU];
         const int64_t room = capacity - (int64_t)g0 * kSelRows;   // entries left in this batch's slots
@@ -492,12 +499,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
             const bool ok = j < nbatch && off < room;
             vs[u] = ok ? gsel[off] : 0;
             vc[u] = ok ? gcnd[off] : 0ull;
-        }
-        uint32_t cs = 0, cc = 0;
-        if (gi < groups) {
-            const uint32_t* cnt = ws.counts + ((int64_t)b * groups + gi) * 2;
-            cs = cnt[0];
-            cc = cnt[1];
         }
         uint32_t ts, tc;
         const uint32_t is = block_incl_scan(cs, &ts);
@@ -584,9 +585,117 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
     for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out[i] = -1;
 }
 
+// The same for up to kF2MaxGroups select workgroups, with 1024 threads: the
+// counts are loaded first and every wave's speculative list loads are straight
+// code, so the prefix sums (one DPP scan per wave, one LDS pass) start as soon as
+// the counts land; wave w places the lists of workgroups w, w + 16, ..
+constexpr int kF2Threads = 1024;
+constexpr int kF2Waves = kF2Threads / 64;
+constexpr int kF2MaxGroups = 1024;
+constexpr int kF2Spec = 4;                // workgroups per wave whose first 64 entries load early
+__global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __restrict__ n_visible, int k,
+                                                              int64_t capacity, int groups, TopkWorkspace ws,
+                                                              int32_t* __restrict__ out_idx) {
+    __shared__ FinalLds L;
+    __shared__ uint32_t cursor;
+    __shared__ uint32_t g_cnt[kF2MaxGroups][2], g_off[kF2MaxGroups][2];
+    __shared__ uint32_t wtot[kF2Waves][2];
+    const int b = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
+    int32_t* out = out_idx + (int64_t)b * k;
+    uint64_t* gc2 = ws.cand2 + b * capacity;
+    const int32_t* __restrict__ gsel = ws.sel + b * capacity;
+    const uint64_t* __restrict__ gcnd = ws.cand + b * capacity;
+
+    // every load unconditional, from a clamped in-bounds address, so that the waits
+    // for the counts (issued first) do not cover the list loads behind them
+    const bool has_cnt = t < groups;
+    const u32x2 c2 = *reinterpret_cast<const u32x2*>(ws.counts + ((int64_t)b * groups + (has_cnt ? t : 0)) * 2);
+    int32_t vs[kF2Spec];
+    uint64_t vc[kF2Spec];
+#pragma unroll
+    for (int u = 0; u < kF2Spec; ++u) {
+        const int j = wv + kF2Waves * u;
+        const int64_t off = (int64_t)j * kSelRows + lane;
+        const bool ok = j < groups && off < capacity;
+        vs[u] = gsel[ok ? off : 0];
+        vc[u] = gcnd[ok ? off : 0];
+        if (!ok) {
+            vs[u] = 0;
+            vc[u] = 0ull;
+        }
+    }
+    const uint32_t cs = has_cnt ? c2.x : 0u, cc = has_cnt ? c2.y : 0u;
+    // exclusive prefix sums of the counts over the workgroups
+    const uint32_t is = wave_incl_scan(cs), ic = wave_incl_scan(cc);
+    if (lane == 63) {
+        wtot[wv][0] = is;
+        wtot[wv][1] = ic;
+    }
+    __syncthreads();
+    uint32_t bs = 0, bc = 0, nsel = 0, ncand = 0;
+#pragma unroll
+    for (int i = 0; i < kF2Waves; ++i) {
+        const uint32_t s_ = wtot[i][0], c_ = wtot[i][1];
+        if (i < wv) {
+            bs += s_;
+            bc += c_;
+        }
+        nsel += s_;
+        ncand += c_;
+    }
+    if (t < groups) {
+        g_off[t][0] = bs + is - cs;
+        g_off[t][1] = bc + ic - cc;
+        g_cnt[t][0] = cs;
+        g_cnt[t][1] = cc;
+    }
+    __syncthreads();
+    // placement: entry i of workgroup j's lists goes to the output (selected) or to
+    // the candidate list (LDS, then cand2 past kFinalLds)
+    auto place_sel = [&](int j, uint32_t i, int32_t v) {
+        const uint32_t o = g_off[j][0] + i;
+        if (o < (uint32_t)k) out[o] = v;
+    };
+    auto place_cnd = [&](int j, uint32_t i, uint64_t v) {
+        const uint32_t o = g_off[j][1] + i;
+        if (o < (uint32_t)kFinalLds) L.lc[o] = v;
+        else gc2[o] = v;                                   // o < capacity: every row is in at most one list
+    };
+#pragma unroll
+    for (int u = 0; u < kF2Spec; ++u) {
+        const int j = wv + kF2Waves * u;
+        if (j < groups) {
+            if ((uint32_t)lane < g_cnt[j][0]) place_sel(j, lane, vs[u]);
+            if ((uint32_t)lane < g_cnt[j][1]) place_cnd(j, lane, vc[u]);
+        }
+    }
+    // the rest: workgroups past the speculated ones, and entries past the first 64
+    for (int j = wv; j < groups; j += kF2Waves) {
+        const uint32_t i0 = (j < wv + kF2Waves * kF2Spec) ? 64u : 0u;
+        const uint32_t ns = g_cnt[j][0], nc = g_cnt[j][1];
+        for (uint32_t i = i0 + lane; i < ns; i += 64) place_sel(j, i, gsel[(int64_t)j * kSelRows + i]);
+        for (uint32_t i = i0 + lane; i < nc; i += 64) place_cnd(j, i, gcnd[(int64_t)j * kSelRows + i]);
+    }
+    __syncthreads();
+    if (ncand > (uint32_t)kFinalLds)                     // the radix passes then read one contiguous list
+        for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kF2Threads) gc2[i] = L.lc[i];
+    __threadfence_block();
+    if (t == 0) cursor = nsel;
+    for (int i = t; i < kMaxDigitBins; i += kF2Threads) L.h[0][i] = 0u;
+    __syncthreads();
+    const uint32_t need = (want > nsel) ? want - nsel : 0u;
+    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);   // the stores drain during the radix
+    radix_take_any<kF2Threads>(L, gc2, ncand, need, want, out, &cursor);
+    __syncthreads();
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out[i] = -1;
+}
+
 }  // namespace
 
-// MLA_TOPK_PATH=row|multi forces a path (for tuning).
+// MLA_TOPK_PATH=row|multi forces a path, MLA_TOPK_FINAL1 the 256-thread final (for tuning).
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                          const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream) {
     if (B == 0 || k == 0) return hipSuccess;
@@ -602,6 +711,9 @@ hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n
                                            scores, capacity, n_visible, k, ws);
         if (e != hipSuccess) return e;
     }
+    if (nx <= (unsigned)kF2MaxGroups && !getenv("MLA_TOPK_FINAL1"))
+        return launch_kernel(k_select_final2, dim3(B), dim3(kF2Threads), 0, stream, nx > 0 ? nullptr : p.start,
+                             p.stop, n_visible, k, capacity, (int)nx, ws, out_idx);
     return launch_kernel(k_select_final, dim3(B), dim3(kSelThreads), 0, stream, nx > 0 ? nullptr : p.start, p.stop,
                          n_visible, k, capacity, (int)nx, ws, out_idx);
 }

@@ -864,12 +864,52 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
 }
 
 // Combine the splits of one (b, h) by their logsumexp; thread t owns channels 4t .. 4t+3.
+// Up to kMergeFast splits, every load (logsumexps and partials) is issued at
+// once, from clamped in-bounds addresses, so the block pays one memory round trip.
+constexpr int kMergeFast = 16;
 __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part, float* __restrict__ out,
                                                          float* __restrict__ lse) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int t = threadIdx.x;
     const float* lp = lse_part + (int64_t)b * S * H + h;
+    if (S <= kMergeFast) {
+        const float4* op = reinterpret_cast<const float4*>(o_part + ((int64_t)b * S * H + h) * kDv) + t;
+        const int64_t step = (int64_t)H * (kDv / 4);
+        float lv[kMergeFast];
+        float4 pv[kMergeFast];
+#pragma unroll
+        for (int s = 0; s < kMergeFast; ++s) {
+            const int sc = (s < S) ? s : 0;
+            lv[s] = lp[(int64_t)sc * H];
+            pv[s] = op[sc * step];
+        }
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int s = 0; s < kMergeFast; ++s)
+            if (s < S) m = fmaxf(m, lv[s]);
+        float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * kDv) + t;
+        if (m == -__builtin_inff()) {
+            *o = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t == 0) lse[(int64_t)b * H + h] = -__builtin_inff();
+            return;
+        }
+        float tot = 0.0f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int s = 0; s < kMergeFast; ++s) {
+            const float wv = (s < S) ? __expf(lv[s] - m) : 0.0f;
+            tot += wv;
+            acc.x += wv * pv[s].x;
+            acc.y += wv * pv[s].y;
+            acc.z += wv * pv[s].z;
+            acc.w += wv * pv[s].w;
+        }
+        const float inv = 1.0f / tot;
+        *o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        if (t == 0) lse[(int64_t)b * H + h] = m + __logf(tot);
+        return;
+    }
     float m = -__builtin_inff();
     for (int s = 0; s < S; ++s) m = fmaxf(m, lp[(int64_t)s * H]);
     float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * kDv) + t;

@@ -318,7 +318,7 @@ def main():
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "indexer scan (k_scan_staged)",
+            "kernel": "indexer scan (k_scan_dma32)",
             "bound": "hbm",
             "achieved": scan_gbps,
             "peak": HBM_PEAK_GBPS,

@@ -64,16 +64,18 @@ mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int6
 }
 
 struct TopkLayout {
-    size_t scores, hist, counts, sel, cand, cand2, total;
+    size_t queues, scores, hist, counts, sel, cand, cand2, total;
 };
 
 TopkLayout topk_layout(int32_t B, int64_t capacity) {
     TopkLayout L;
     const size_t b = B > 0 ? (size_t)B : 0, cap = capacity > 0 ? (size_t)capacity : 0;
     const size_t groups = capacity > 0 ? (size_t)mla::select_groups(capacity) : 0;
-    // the histogram first, at a place that depends on nothing but the sequence, so
-    // that what a call leaves zeroed stays the histogram whatever the next call's sizes
-    L.hist = 0;
+    // the scan's work queues and the histogram first, at places that depend on
+    // nothing but the sequence, so that what a call leaves zeroed stays the
+    // queues and the histogram whatever the next call's sizes
+    L.queues = 0;
+    L.hist = L.queues + (size_t)mla::kScanQueuesHost * mla::kQueueWordsHost * sizeof(uint32_t);
     L.scores = L.hist + round256(b * (size_t)mla::kHistWordsHost * sizeof(uint32_t));
     L.counts = L.scores + round256(b * cap * sizeof(float));
     L.sel = L.counts + round256(b * groups * 2 * sizeof(uint32_t));
@@ -237,6 +239,7 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     a.k = k;
     a.scores = T.scores;
     a.hist = T.hist;
+    a.queues = reinterpret_cast<uint32_t*>(ws + L.queues);
     hipError_t e = mla::launch_scan(a, st);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
     e = mla::launch_select(T.scores, capacity, n_visible, B, k, T, out_idx, st);

@@ -258,12 +258,43 @@ __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
 }
+// Device-scope atomic add of 1 by lane 0 alone, returning the old value into r
+// (lane 0) once the operation completes. Issued as inline assembly like the
+// loads above, so that it joins their in-order vmcnt count; r must not be read
+// before a wait_vmcnt_tie on it has covered the operation.
+__device__ __forceinline__ void ticket_issue(uint32_t& r, uint32_t* p) {
+    uint64_t save;
+    asm volatile(
+        "s_mov_b64 %1, exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "s_nop 1\n\t"
+        "global_atomic_add %0, %2, %3, off sc0\n\t"
+        "s_mov_b64 exec, %1"
+        : "=&v"(r), "=&s"(save)
+        : "v"(p), "v"(1u)
+        : "memory");
+}
+// Lane 0's value of a ticket register, read after the wait that covers its
+// atomic: volatile statements keep their order, so the read cannot move above
+// the wait the way an ordinary use of the register could
+__device__ __forceinline__ uint32_t ticket_read(uint32_t r) {
+    uint32_t t;
+    asm volatile("v_readfirstlane_b32 %0, %1" : "=s"(t) : "v"(r));
+    return t;
+}
 #pragma clang diagnostic pop
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// the same wait as a volatile statement, ordered with the other volatile asm
+// (ticket_issue, ticket_read) of a wave
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_asm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 }  // namespace mla

@@ -649,6 +649,251 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     flush_fine_coarse<NT>(cnt, coarse, hb, copy);
 }
 
+// The 32x32 scan with its chunks handed out at run time. Workgroup L serves
+// queue L mod nq (nq = gridDim.x / per_queue queues, `groups` per sequence);
+// queue (b, g) owns the 32-row chunks [g n / groups, (g + 1) n / groups) of
+// sequence b's n visible chunks. Each wave of the queue's W = per_queue * NW
+// waves takes two chunks by its index (wq and W + wq past the queue's first),
+// then one chunk per ticket drawn from the queue's counter: the ticket for the
+// wave's job j + 2 is drawn when job j is issued, two jobs ahead of its use, so
+// waves that are served early take more chunks and all finish together. The
+// tickets, the chunk loads and the score stores of a wave complete in issue
+// order, and every wait counts exactly the operations issued after the one it
+// needs. The last wave of a queue to finish returns its counters to zero.
+// The histogram is kept with one 32-bit word per fine bin (a workgroup may see
+// any number of rows); the scores of a chunk are stored by lanes 0 .. 31.
+template <int FMT, int MT2, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int groups, int per_queue) {
+    constexpr int NBUF = 3;
+    constexpr int NT = 64 * NW;
+    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
+    constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
+    constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries
+    static_assert(kBytes % 16 == 0, "chunk of 16-byte pieces");
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t coarse[kCoarseBins];
+    __shared__ __attribute__((aligned(16))) float wst[64];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NBUF][kBuf];
+    const int nq = gridDim.x / per_queue;
+    const int qi = blockIdx.x % nq, member = blockIdx.x / nq;
+    const int b = qi / groups, g = qi - b * groups;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n32 = lane & 31, h = lane >> 5;
+    const int64_t cap = a.capacity;
+    const int64_t nvis = clamp_visible(a.n_visible[b], cap);
+    const int64_t nch = (nvis + kDmaRows - 1) / kDmaRows;          // chunks holding visible rows
+    const int64_t c_lo = nch * g / groups, c_hi = nch * (g + 1) / groups;
+    const int64_t W = (int64_t)per_queue * NW;
+    const int64_t wq = (int64_t)member * NW + wave;
+    uint32_t* const qctr = a.queues + kQueueWordsHost * qi;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) hist[i] = 0u;
+    if (threadIdx.x < kCoarseBins) coarse[threadIdx.x] = 0u;
+
+    const uint8_t* base = a.cache + b * a.stride;
+    const uint32_t ring_m0 = __builtin_amdgcn_readfirstlane(lds_addr(&ring[wave][0][0]));
+    uint32_t full_off[KI];
+#pragma unroll
+    for (int k = 0; k < KI; ++k) {
+        const uint32_t o = (uint32_t)(1024 * k + 16 * lane);
+        full_off[k] = (o < (uint32_t)kBytes) ? o : 0u;
+    }
+    auto issue = [&](int64_t ch, int slot) {               // chunk ch into ring slot `slot`: KI loads
+        const int64_t r = ch * kDmaRows;
+        const uint8_t* src = base + r * RB;
+        const int64_t left = (cap - r) * RB;
+        const uint32_t m0 = ring_m0 + (uint32_t)(slot * kBuf);
+        if (left >= kBytes) {
+#pragma unroll
+            for (int k = 0; k < KI; ++k) dma16_s(src, full_off[k], m0 + 1024u * (uint32_t)k);
+        } else {                                           // the sequence ends inside the chunk
+#pragma unroll
+            for (int k = 0; k < KI; ++k) {
+                const uint32_t off = ((int64_t)full_off[k] + 16 > left) ? 0u : full_off[k];
+                dma16_s(src, off, m0 + 1024u * (uint32_t)k);
+            }
+        }
+    };
+    // wait until at most n operations are in flight (n: a count this kernel produces)
+    auto wait_upto = [&](int n) {
+        if (n >= KI + 3) wait_vmcnt_asm<KI + 3>();
+        else if (n == KI + 2) wait_vmcnt_asm<KI + 2>();
+        else if (n == KI + 1) wait_vmcnt_asm<KI + 1>();
+        else if (n >= 2) wait_vmcnt_asm<2>();
+        else if (n == 1) wait_vmcnt_asm<1>();
+        else wait_vmcnt_asm<0>();
+    };
+
+    // ---- prologue: ticket for job 2, queries and weights, job 0, ticket for job 3, job 1
+    const int64_t ch0 = c_lo + wq, ch1 = c_lo + W + wq;
+    const bool v0 = ch0 < c_hi, v1 = ch1 < c_hi;
+    uint32_t tA = 0u, tB = 0u;                             // tickets in flight: even jobs' in tA, odd in tB
+    if (v0) ticket_issue(tA, qctr);
+    const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q_idx) + ((int64_t)b * a.H_I + 16 * wave) * 256;
+    if (wave < 2 * MT2) {                                  // head tile `wave`, 272-byte head stride
+        const uint32_t qm0 = ring_m0 + (uint32_t)((NBUF - 1) * kBuf);
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const int j = 64 * k + lane, hh = j / 17, pc = j - 17 * hh;
+            const uint32_t off = (j < 272 && pc < 16) ? (uint32_t)(256 * hh + 16 * pc) : 0u;
+            dma16_s(qsrc, off, qm0 + 1024u * (uint32_t)k);
+        }
+    }
+    if (wave == 0)
+        dma4_s(a.w + (int64_t)b * a.H_I, lane < a.H_I ? 4u * (uint32_t)lane : 0u,
+               __builtin_amdgcn_readfirstlane(lds_addr(wst)));
+    if (v0) issue(ch0, 0);
+    if (v1) {
+        ticket_issue(tB, qctr);
+        issue(ch1, 1);
+    }
+    if (v1) wait_vmcnt_asm<KI + 1>();                       // all but job 1 and its ticket
+    else wait_vmcnt_asm<0>();
+    __syncthreads();                                       // queries, weights staged; histograms cleared
+    u32x4 qa[MT2][8];
+    float wv[MT2][16];
+#pragma unroll
+    for (int mt = 0; mt < MT2; ++mt) {
+        const int head = 32 * mt + n32;
+        const uint8_t* qt = &ring[head >> 4][NBUF - 1][0] + (head & 15) * 272 + 128 * h;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qt + 16 * s);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wst[32 * mt + 8 * q + 4 * h]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wv[mt][4 * q + r] = w4[r] * a.sigma;
+        }
+    }
+    __syncthreads();                                       // every wave holds them: the buffers are free
+
+    struct ChunkIn {
+        u32x4 kb[8];
+        float mult;
+    };
+    auto dequant = [&](int slot, ChunkIn& in) {
+        const uint8_t* rp = &ring[wave][slot][0] + n32 * RB;
+        in.mult = 1.0f;
+        if constexpr (FMT == MLA_FMT_E4M3_S128) {
+            uint32_t w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 64 * h)[i];
+            in.mult = *reinterpret_cast<const float*>(rp + 128);
+            dequant_key<FMT>(w, 0u, in.kb);
+            dequant_key<FMT>(w + 8, 0u, in.kb + 4);
+        } else {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 32 * h)[i];
+            const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
+            dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
+            dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+        }
+    };
+
+    // jobs: the current job j (chunk chj), then jobs j + 1 and j + 2 (chunk, valid)
+    ChunkIn cur;
+    int64_t chj = ch0, chn1 = ch1, chn2 = 0;
+    bool vn1 = v1, vn2 = false;
+    if (v0) {                                              // job 0 landed: issue job 2 from tA's ticket
+        const int64_t c2 = c_lo + 2 * W + (int64_t)ticket_read(tA);
+        vn2 = c2 < c_hi;
+        chn2 = c2;
+        if (vn2) {
+            ticket_issue(tA, qctr);                        // ticket for job 4
+            issue(c2, 2);
+        }
+        dequant(0, cur);
+    }
+    float* scores = a.scores + b * cap;
+    // job j on `cur`; treg holds the ticket drawn with job j + 1 (the one for job j + 3)
+    auto step = [&](int j, uint32_t& treg) -> bool {
+        f32x16 acc[MT2];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT2; ++mt) acc[mt] = mfma32_bf16(qa[mt][s], cur.kb[s], acc[mt]);
+        const float mult = cur.mult;
+        const int64_t row = chj * kDmaRows + n32;
+        const bool more = vn1;
+        if (vn1) {
+            // in flight after job j + 1's loads: the score store of job j - 2, job j + 2's
+            // ticket and loads, the score store of job j - 1
+            wait_upto((j >= 2 ? 1 : 0) + (vn2 ? KI + 1 : 0) + (j >= 1 ? 1 : 0));
+            const int64_t c3 = c_lo + 2 * W + (int64_t)ticket_read(treg);
+            const bool v3 = c3 < c_hi;
+            if (v3) {
+                ticket_issue(treg, qctr);                  // ticket for job j + 5
+                issue(c3, (j + 3) % 3);                    // into job j's slot, already read
+            }
+            dequant((j + 1) % 3, cur);
+            chj = chn1;
+            chn1 = chn2;
+            vn1 = vn2;
+            chn2 = c3;
+            vn2 = v3;
+        }
+        // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
+        float pm[MT2][4];
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                pm[mt][q] = wv[mt][4 * q] * relu(acc[mt][4 * q]);
+#pragma unroll
+                for (int r = 1; r < 4; ++r) pm[mt][q] += wv[mt][4 * q + r] * relu(acc[mt][4 * q + r]);
+            }
+        float part = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT2; ++mt) part += (pm[mt][0] + pm[mt][1]) + (pm[mt][2] + pm[mt][3]);
+        const float score = xsum2(part) * mult;
+        if (h == 0 && row < cap) {                         // row 0 of the chunk is visible: one store
+            const bool valid = row < nvis;
+            scores[row] = valid ? score : -__builtin_inff();
+            if (valid) {
+                const uint32_t bin = score_key(score) >> (32 - kHistBits);
+                atomicAdd(&hist[bin], 1u);
+                atomicAdd(&coarse[bin / kFinePerCoarse], 1u);
+            }
+        }
+        return more;
+    };
+    if (v0) {
+        for (int j = 0;; j += 2) {
+            if (!step(j, tB)) break;
+            if (!step(j + 1, tA)) break;
+        }
+    }
+    wait_vmcnt<0>();
+    // finished: count the wave out of its queue (the reply is read after the flush)
+    uint32_t fin = 0u;
+    if (lane == 0) fin = __hip_atomic_fetch_add(qctr + 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // rows past the visible chunks: -inf, a slice per workgroup of the sequence
+    {
+        const int64_t lo = nch * kDmaRows, n_wg = (int64_t)groups * per_queue;
+        const int64_t span = (cap - lo + n_wg - 1) / n_wg;
+        const int64_t r0 = lo + ((int64_t)g * per_queue + member) * span;
+        const int64_t r1 = min(r0 + span, cap);
+        for (int64_t r = r0 + threadIdx.x; r < r1; r += NT) scores[r] = -__builtin_inff();
+    }
+    __syncthreads();
+    uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
+    uint32_t cnt[kHistBins / NT];
+#pragma unroll
+    for (int i = 0; i < kHistBins / NT; ++i) cnt[i] = hist[threadIdx.x + NT * i];
+    flush_fine_coarse<NT>(cnt, coarse, hb, hist_copy_of_block());
+    if (lane == 0 && fin == (uint32_t)W - 1) {             // the queue's last wave: counters back to zero
+        __hip_atomic_store(qctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(qctr + 16, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
 template <int MT>
 __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
@@ -785,6 +1030,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         d32rpb = ((d32rpb + unit32 - 1) / unit32) * unit32;
         d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), (int64_t)kDmaRowsPerWave * kDma32Waves);
         const dim3 d32grid((unsigned)((a.capacity + d32rpb - 1) / d32rpb), a.B);
+        // the queue-fed 32x32 scan: about 64 queues (a sequence's rows split into
+        // `groups` ranges), 2 blocks per CU in all, about 4 chunks per wave at least
+        const bool dyn = a.queues != nullptr && a.B <= kScanQueuesHost && !getenv("MLA_SCAN_STATIC");
+        const int dyn_groups = std::max(1, 64 / a.B);
+        const int64_t dyn_nq = (int64_t)a.B * dyn_groups;
+        const int64_t dyn_chunks = (int64_t)a.B * ((a.capacity + kDmaRows - 1) / kDmaRows);
+        const int64_t dyn_per_queue = std::max<int64_t>(
+            1, std::min<int64_t>(blk32 / dyn_nq, dyn_chunks / (dyn_nq * kDma32Waves * 4)));
 #define MLA_SCAN_CASE(F, M)                                                                    \
     if (a.fmt == F && a.H_I == 16 * M) {                                                       \
         const ProfSlot p = prof_slot(PROF_SCAN);                                               \
@@ -792,9 +1045,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
             return launch_kernel(k_scan_bf16<M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a); \
         } else {                                                                               \
             if (dma) {                                                                         \
-                if constexpr (M % 2 == 0)                                                      \
+                if constexpr (M % 2 == 0) {                                                    \
+                    if (dyn)                                                                   \
+                        return launch_kernel(k_scan_dyn32<F, M / 2, kDma32Waves>,              \
+                                             dim3((unsigned)(dyn_nq * dyn_per_queue)), dim3(64 * kDma32Waves), \
+                                             0, stream, p.start, p.stop, a, dyn_groups, (int)dyn_per_queue); \
                     return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves>, d32grid,     \
                                          dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb); \
+                }                                                                              \
                 else                                                                           \
                     return launch_kernel(k_scan_dma<F, M, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, \
                                          stream, p.start, p.stop, a, (int)drpb);               \

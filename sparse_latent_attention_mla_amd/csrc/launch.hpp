@@ -19,6 +19,11 @@ constexpr int kHistBinsHost = 4096;
 constexpr int kHistCopiesHost = 8;
 constexpr int kCoarseBinsHost = 64;
 constexpr int64_t kHistWordsHost = (int64_t)kHistCopiesHost * (kCoarseBinsHost + kHistBinsHost);
+// Work queues of the dynamic indexer scan, at the start of the top-k workspace:
+// queue i's ticket counter is word kQueueWordsHost * i, its count of finished
+// waves the word 16 after it (one 128-byte line per queue). Zero between calls.
+constexpr int kScanQueuesHost = 512;
+constexpr int kQueueWordsHost = 32;
 
 struct AppendArgs {
     int main_fmt, main_dim, main_rope;
@@ -65,6 +70,7 @@ struct ScanArgs {
     int B, H_I, k;
     float* scores;          // [B, capacity]
     uint32_t* hist;         // [B, kHistWordsHost] (see TopkWorkspace)
+    uint32_t* queues;       // [kScanQueuesHost, kQueueWordsHost] work queues, zero on entry and on exit
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 bool scan_supported(int fmt, int dim, int H_I);

@@ -28,6 +28,9 @@ SMALL = {
     "c3s": C["c3"].with_(name="c3s", cid=103, B=2, N=6001),
     "c4s": C["c4"].with_(name="c4s", cid=104, B=2, N=4099),
     "c5s": C["c5"].with_(name="c5s", cid=105, B=1, N=3001),
+    # sizes at which every wave of the queue-fed scan draws several tickets
+    "c3m": C["c3"].with_(name="c3m", cid=113, B=3, N=40001),
+    "c4m": C["c4"].with_(name="c4m", cid=114, B=1, N=70001),
 }
 FULL = {n: C[n] for n in ("c2", "c3", "c4", "c5")}
 
@@ -304,3 +307,29 @@ def test_topk_workspace_reused_across_shapes(monkeypatch):
         got_idx, _ = G.gpu_topk(case, 0, ws=ws, want_scores=False)
         ref_s = G.oracle_scores(case, 0)
         G.check_topk(got_idx, ref_s, case.n_visible, case.cfg.k)
+
+
+@pytest.mark.parametrize("scan", ["queues", "static"])
+@pytest.mark.parametrize("name", ["c3m", "c4m"])
+def test_scan_work_queues(name, scan, monkeypatch):
+    """The queue-fed scan (chunks handed out by ticket at run time, 63 and 64
+    queues here, several tickets per wave) and the statically partitioned one,
+    on ragged visible lengths, with one workspace reused across the calls: the
+    scores, the selection, and the zeroed start of the workspace (the queues'
+    counters, then the histogram copies) after every call."""
+    if scan == "static":
+        monkeypatch.setenv("MLA_SCAN_STATIC", "1")
+    case = case_of(name)
+    cfg = case.cfg
+    B, N, k = cfg.B, cfg.N, cfg.k
+    ws = torch.zeros(G.M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device="cuda")
+    zero_part = 512 * 128 + B * 8 * (64 + 4096) * 4
+    rng = np.random.default_rng(cfg.cid)
+    for nv in ([N] * B, rng.integers(1, N + 1, B).tolist(), [N - 31] + [33] * (B - 1), [0] * B):
+        nv = np.array(nv, np.int32)
+        say("scan queues", name, scan, nv.tolist())
+        got_idx, got_s = G.gpu_topk(case, 0, n_visible=nv, ws=ws)
+        ref_s = G.oracle_scores(case, 0, n_visible=nv)
+        G.check_scores(got_s, ref_s, nv)
+        G.check_topk(got_idx, ref_s, nv, k)
+        assert not bool(ws[:zero_part].any()), "workspace start not zero after the call"

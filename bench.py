@@ -117,7 +117,7 @@ def build_layers(cfg, n_layers, seed=0):
     return layers
 
 
-SAMPLE_EVERY = 9
+SAMPLE_EVERY = 25
 SCAN_SOURCES = ("csrc/indexer.hip", "csrc/common.hpp", "csrc/launch.hpp", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_c3_hbm_traffic.md")
 

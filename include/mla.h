@@ -188,7 +188,8 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
  *  out_scores   optional fp32 [B, capacity]: the scores, -inf for masked rows
  *  workspace    device scratch of at least mla_indexer_topk_workspace(B, capacity, k)
  *               bytes, 256-byte aligned, ZEROED BEFORE ITS FIRST USE (e.g. hipMemset once
- *               after allocation). It holds the score histogram at its start; every call
+ *               after allocation). It holds the scan's work-queue counters and the score
+ *               histogram at its start; every call
  *               that returns MLA_OK leaves that part zeroed again, so one workspace serves
  *               any sequence of calls (any B, capacity, k within its size). A call that
  *               fails with MLA_ERR_HIP may leave it dirty: zero it again. Calls that

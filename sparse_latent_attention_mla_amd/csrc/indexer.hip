@@ -41,6 +41,10 @@ constexpr int kDma32Waves = MLA_SCAN_WAVES;
 #endif
 constexpr int kDmaNbuf = MLA_SCAN_NBUF;
 constexpr int kDmaBlocksPerCu = (kDmaNbuf == 2) ? 3 : 2;   // what the LDS of one CU holds
+#ifndef MLA_SCAN_STATIC_JOBS
+#define MLA_SCAN_STATIC_JOBS 4
+#endif
+constexpr int kScanStaticJobs = MLA_SCAN_STATIC_JOBS;      // queue-fed scan: chunks per wave by index
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -649,42 +653,50 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     flush_fine_coarse<NT>(cnt, coarse, hb, copy);
 }
 
-// The 32x32 scan with its chunks handed out at run time. Workgroup L serves
-// queue L mod nq (nq = gridDim.x / per_queue queues, `groups` per sequence);
+// The 32x32 scan with its chunks handed out at run time. Workgroup (x, y)
+// serves queue x as its member y (gridDim.x queues, 2^lg_groups per sequence,
+// gridDim.y workgroups each; workgroups go out x-fastest, one member of every
+// queue before the next); index arithmetic is shifts and masks only, so the
+// first loads leave at once.
 // queue (b, g) owns the 32-row chunks [g n / groups, (g + 1) n / groups) of
 // sequence b's n visible chunks. Each wave of the queue's W = per_queue * NW
-// waves takes two chunks by its index (wq and W + wq past the queue's first),
-// then one chunk per ticket drawn from the queue's counter: the ticket for the
-// wave's job j + 2 is drawn when job j is issued, two jobs ahead of its use, so
-// waves that are served early take more chunks and all finish together. The
+// waves takes its first kScanStaticJobs chunks by its index (x W + wq past the
+// queue's first, job x), then one chunk per ticket drawn from the queue's
+// counter: the ticket for the wave's job j + 2 is drawn when job j is issued,
+// two jobs ahead of its use, so waves that are served early take more chunks
+// and all finish together. No ticket is drawn before the wave's first chunks
+// have landed: at the start every wave would draw at once and the atomics on
+// one counter are served one after another. The
 // tickets, the chunk loads and the score stores of a wave complete in issue
 // order, and every wait counts exactly the operations issued after the one it
 // needs. The last wave of a queue to finish returns its counters to zero.
 // The histogram is kept with one 32-bit word per fine bin (a workgroup may see
 // any number of rows); the scores of a chunk are stored by lanes 0 .. 31.
 template <int FMT, int MT2, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int groups, int per_queue) {
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int lg_groups) {
     constexpr int NBUF = 3;
     constexpr int NT = 64 * NW;
     constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
     constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
     constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
     constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries
+    constexpr int S = kScanStaticJobs;
     static_assert(kBytes % 16 == 0, "chunk of 16-byte pieces");
+    static_assert(S >= 2 && S <= 4, "static jobs: a ticket is drawn with jobs S - 2 ..");
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t coarse[kCoarseBins];
     __shared__ __attribute__((aligned(16))) float wst[64];
     __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NBUF][kBuf];
-    const int nq = gridDim.x / per_queue;
-    const int qi = blockIdx.x % nq, member = blockIdx.x / nq;
-    const int b = qi / groups, g = qi - b * groups;
+    const int qi = blockIdx.x, member = blockIdx.y, per_queue = gridDim.y;
+    const int groups = 1 << lg_groups;
+    const int b = qi >> lg_groups, g = qi & (groups - 1);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n32 = lane & 31, h = lane >> 5;
     const int64_t cap = a.capacity;
     const int64_t nvis = clamp_visible(a.n_visible[b], cap);
-    const int64_t nch = (nvis + kDmaRows - 1) / kDmaRows;          // chunks holding visible rows
-    const int64_t c_lo = nch * g / groups, c_hi = nch * (g + 1) / groups;
+    const int64_t nch = (nvis + kDmaRows - 1) >> 5;                // chunks holding visible rows
+    const int64_t c_lo = (nch * g) >> lg_groups, c_hi = (nch * (g + 1)) >> lg_groups;
     const int64_t W = (int64_t)per_queue * NW;
     const int64_t wq = (int64_t)member * NW + wave;
     uint32_t* const qctr = a.queues + kQueueWordsHost * qi;
@@ -720,16 +732,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
         if (n >= KI + 3) wait_vmcnt_asm<KI + 3>();
         else if (n == KI + 2) wait_vmcnt_asm<KI + 2>();
         else if (n == KI + 1) wait_vmcnt_asm<KI + 1>();
+        else if (n == KI) wait_vmcnt_asm<KI>();
         else if (n >= 2) wait_vmcnt_asm<2>();
         else if (n == 1) wait_vmcnt_asm<1>();
         else wait_vmcnt_asm<0>();
     };
 
-    // ---- prologue: ticket for job 2, queries and weights, job 0, ticket for job 3, job 1
-    const int64_t ch0 = c_lo + wq, ch1 = c_lo + W + wq;
+    // job x: a static chunk for x < S, else the chunk of a ticket drawn with job x - 2
+    auto static_chunk = [&](int x) { return c_lo + (int64_t)x * W + wq; };
+    auto ticket_chunk = [&](uint32_t t) { return c_lo + (int64_t)S * W + (int64_t)t; };
+    // ---- prologue: queries and weights, job 0, job 1 (each with its ticket if S = 2, 3)
+    const int64_t ch0 = static_chunk(0), ch1 = static_chunk(1);
     const bool v0 = ch0 < c_hi, v1 = ch1 < c_hi;
-    uint32_t tA = 0u, tB = 0u;                             // tickets in flight: even jobs' in tA, odd in tB
-    if (v0) ticket_issue(tA, qctr);
+    uint32_t tA = 0u, tB = 0u;                             // tickets in flight: drawn with even jobs in tA, odd in tB
     const uint8_t* qsrc = reinterpret_cast<const uint8_t*>(a.q_idx) + ((int64_t)b * a.H_I + 16 * wave) * 256;
     if (wave < 2 * MT2) {                                  // head tile `wave`, 272-byte head stride
         const uint32_t qm0 = ring_m0 + (uint32_t)((NBUF - 1) * kBuf);
@@ -743,13 +758,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
     if (wave == 0)
         dma4_s(a.w + (int64_t)b * a.H_I, lane < a.H_I ? 4u * (uint32_t)lane : 0u,
                __builtin_amdgcn_readfirstlane(lds_addr(wst)));
-    if (v0) issue(ch0, 0);
+    if (v0) {
+        if (S <= 2) ticket_issue(tA, qctr);
+        issue(ch0, 0);
+    }
     if (v1) {
-        ticket_issue(tB, qctr);
+        if (S <= 3) ticket_issue(tB, qctr);
         issue(ch1, 1);
     }
-    if (v1) wait_vmcnt_asm<KI + 1>();                       // all but job 1 and its ticket
-    else wait_vmcnt_asm<0>();
+    if (v1) {                                              // all but job 1 (and its ticket)
+        if (S <= 3) wait_vmcnt_asm<KI + 1>();
+        else wait_vmcnt_asm<KI>();
+    } else {
+        wait_vmcnt_asm<0>();
+    }
     __syncthreads();                                       // queries, weights staged; histograms cleared
     u32x4 qa[MT2][8];
     float wv[MT2][16];
@@ -796,8 +818,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
     ChunkIn cur;
     int64_t chj = ch0, chn1 = ch1, chn2 = 0;
     bool vn1 = v1, vn2 = false;
-    if (v0) {                                              // job 0 landed: issue job 2 from tA's ticket
-        const int64_t c2 = c_lo + 2 * W + (int64_t)ticket_read(tA);
+    if (v0) {                                              // job 0 landed: issue job 2
+        const int64_t c2 = (S > 2) ? static_chunk(2) : ticket_chunk(ticket_read(tA));
         vn2 = c2 < c_hi;
         chn2 = c2;
         if (vn2) {
@@ -824,9 +846,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
         const bool more = vn1;
         if (vn1) {
             // in flight after job j + 1's loads: the score store of job j - 2, job j + 2's
-            // ticket and loads, the score store of job j - 1
-            wait_upto((j >= 2 ? 1 : 0) + (vn2 ? KI + 1 : 0) + (j >= 1 ? 1 : 0));
-            const int64_t c3 = c_lo + 2 * W + (int64_t)ticket_read(treg);
+            // ticket (drawn from job S - 2 on) and loads, the score store of job j - 1
+            wait_upto((j >= 2 ? 1 : 0) + (vn2 ? KI + (j + 2 >= S - 2 ? 1 : 0) : 0) + (j >= 1 ? 1 : 0));
+            const int64_t c3 = (j + 3 < S) ? static_chunk(j + 3) : ticket_chunk(ticket_read(treg));
             const bool v3 = c3 < c_hi;
             if (v3) {
                 ticket_issue(treg, qctr);                  // ticket for job j + 5
@@ -874,13 +896,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
     // finished: count the wave out of its queue (the reply is read after the flush)
     uint32_t fin = 0u;
     if (lane == 0) fin = __hip_atomic_fetch_add(qctr + 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // rows past the visible chunks: -inf, a slice per workgroup of the sequence
+    // rows past the visible chunks: -inf, strided over the workgroups of the sequence
     {
-        const int64_t lo = nch * kDmaRows, n_wg = (int64_t)groups * per_queue;
-        const int64_t span = (cap - lo + n_wg - 1) / n_wg;
-        const int64_t r0 = lo + ((int64_t)g * per_queue + member) * span;
-        const int64_t r1 = min(r0 + span, cap);
-        for (int64_t r = r0 + threadIdx.x; r < r1; r += NT) scores[r] = -__builtin_inff();
+        const int64_t stride = (int64_t)groups * per_queue * NT;
+        for (int64_t r = nch * kDmaRows + ((int64_t)g * per_queue + member) * NT + threadIdx.x; r < cap; r += stride)
+            scores[r] = -__builtin_inff();
     }
     __syncthreads();
     uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
@@ -1030,11 +1050,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
         d32rpb = ((d32rpb + unit32 - 1) / unit32) * unit32;
         d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), (int64_t)kDmaRowsPerWave * kDma32Waves);
         const dim3 d32grid((unsigned)((a.capacity + d32rpb - 1) / d32rpb), a.B);
-        // the queue-fed 32x32 scan: about 64 queues (a sequence's rows split into
-        // `groups` ranges), 2 blocks per CU in all, about 4 chunks per wave at least
-        const bool dyn = a.queues != nullptr && a.B <= kScanQueuesHost && !getenv("MLA_SCAN_STATIC");
-        const int dyn_groups = std::max(1, 64 / a.B);
-        const int64_t dyn_nq = (int64_t)a.B * dyn_groups;
+        // the queue-fed 32x32 scan (MLA_SCAN_QUEUES; at the T = 128K shape it is
+        // slower than the static partition): about 64 queues (a sequence's rows
+        // split into `groups` ranges), 2 blocks per CU in all, at least about 4
+        // chunks per wave
+        const bool dyn = a.queues != nullptr && a.B <= kScanQueuesHost && getenv("MLA_SCAN_QUEUES") != nullptr;
+        int dyn_lg = 0;
+        while (a.B << (dyn_lg + 1) <= 64) ++dyn_lg;            // 2^lg queues per sequence, B 2^lg <= 64
+        const int64_t dyn_nq = (int64_t)a.B << dyn_lg;
         const int64_t dyn_chunks = (int64_t)a.B * ((a.capacity + kDmaRows - 1) / kDmaRows);
         const int64_t dyn_per_queue = std::max<int64_t>(
             1, std::min<int64_t>(blk32 / dyn_nq, dyn_chunks / (dyn_nq * kDma32Waves * 4)));
@@ -1048,8 +1071,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
                 if constexpr (M % 2 == 0) {                                                    \
                     if (dyn)                                                                   \
                         return launch_kernel(k_scan_dyn32<F, M / 2, kDma32Waves>,              \
-                                             dim3((unsigned)(dyn_nq * dyn_per_queue)), dim3(64 * kDma32Waves), \
-                                             0, stream, p.start, p.stop, a, dyn_groups, (int)dyn_per_queue); \
+                                             dim3((unsigned)dyn_nq, (unsigned)dyn_per_queue), dim3(64 * kDma32Waves), \
+                                             0, stream, p.start, p.stop, a, dyn_lg);   \
                     return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves>, d32grid,     \
                                          dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb); \
                 }                                                                              \

@@ -312,13 +312,13 @@ def test_topk_workspace_reused_across_shapes(monkeypatch):
 @pytest.mark.parametrize("scan", ["queues", "static"])
 @pytest.mark.parametrize("name", ["c3m", "c4m"])
 def test_scan_work_queues(name, scan, monkeypatch):
-    """The queue-fed scan (chunks handed out by ticket at run time, 63 and 64
+    """The queue-fed scan (chunks handed out by ticket at run time, 48 and 64
     queues here, several tickets per wave) and the statically partitioned one,
     on ragged visible lengths, with one workspace reused across the calls: the
     scores, the selection, and the zeroed start of the workspace (the queues'
     counters, then the histogram copies) after every call."""
-    if scan == "static":
-        monkeypatch.setenv("MLA_SCAN_STATIC", "1")
+    if scan == "queues":
+        monkeypatch.setenv("MLA_SCAN_QUEUES", "1")
     case = case_of(name)
     cfg = case.cfg
     B, N, k = cfg.B, cfg.N, cfg.k

@@ -800,17 +800,22 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
     }
     __syncthreads();
 
-    for (int c = 0; c < nc; ++c) {
-        if (qk_role) {
+    // each role in a loop of its own, one barrier per chunk in both (the output tile
+    // then lives in the PV loop alone; a shared loop made the compiler copy it per chunk)
+    if (qk_role) {
+        for (int c = 0; c < nc; ++c) {
             if (c + 3 < nc) zm2 = issue(c + 3);            // into chunk c - 1's buffer (read before the barrier)
             if (c + 1 < nc) qk(c + 1);
             if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
             zm1 = zm2;
             zm2 = 0;
-        } else {
-            pv(c);
+            __syncthreads();
         }
-        __syncthreads();
+    } else {
+        for (int c = 0; c < nc; ++c) {
+            pv(c);
+            __syncthreads();
+        }
     }
 
     // ---- partial: normalised output (channels 128 q ..) and logsumexp of the split

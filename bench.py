@@ -1,8 +1,9 @@
 """Decode hot-path benchmark on one MI355X.
 
 One step = one decode layer-step of the whole batch: quantise-append of the
-new entry and indexer key, lightning-indexer scan + causal mask + top-k, and
-sparse absorbed-MLA decode (+ window branch).  The CSA2 group configuration
+new entry and indexer key, lightning-indexer scan + causal mask + top-k (the
+append carried in the scan's launch), and sparse absorbed-MLA decode (+ window
+branch).  The CSA2 group configuration
 counts one group (Full + Reindex + 4 Reuse layers) as a step.
 
 Default workload: the V3.2-shaped long-context configuration (B = 4,
@@ -225,19 +226,30 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(X):
-        """One layer-step (or CSA2 group) on layer caches X."""
+        """One layer-step (or CSA2 group) on layer caches X: the first layer appends the
+        step's entry (main row, indexer key) and every layer its window entry; Full and
+        Reindex layers select, every layer attends. The first layer's append rides
+        with its indexer scan (mla_append_indexer_topk)."""
         j = 0
         latest = None
         for l, mode in enumerate(cfg.layers):
             first = l == 0
-            M.mla_kv_append_quant(mr, ir, X.new_main if first else None, X.new_idx if first else None,
-                                  slots if first else None, X.main if first else None, X.idx if first else None,
-                                  X.new_win[l] if cfg.W else None, win_pos if cfg.W else None,
-                                  X.win[l] if cfg.W else None)
-            if mode in ("full", "reindex"):
+            win = (X.new_win[l], win_pos, X.win[l]) if cfg.W else (None, None, None)
+            selects = mode in ("full", "reindex")
+            if first and selects:
                 latest = idx_out[j % 2]
-                M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk)
+                M.mla_append_indexer_topk(mr, ir, X.new_main, X.new_idx, slots, X.main, X.idx, X.q_idx[j],
+                                          X.w[j], cfg.sigma, nvis, k, latest, ws_topk,
+                                          new_win=win[0], win_pos=win[1], win_ring=win[2])
                 j += 1
+            else:
+                M.mla_kv_append_quant(mr, ir, X.new_main if first else None, X.new_idx if first else None,
+                                      slots if first else None, X.main if first else None,
+                                      X.idx if first else None, *win)
+                if selects:
+                    latest = idx_out[j % 2]
+                    M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk)
+                    j += 1
             M.mla_sparse_decode(mr, cfg.d_v, X.q[l], X.main, latest, cfg.softmax_scale, out, lse, ws_dec,
                                 X.win[l] if cfg.W else None, win_len if cfg.W else None)
 

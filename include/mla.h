@@ -9,6 +9,8 @@
  *                         top-k -> int32 positions;
  *   mla_sparse_decode     absorbed-MLA attention over the selected entries (plus the
  *                         window), online softmax, logsumexp output.
+ * mla_append_indexer_topk is the first two in one call (the append then rides in
+ * the scan's launch where the scan kernel can carry it).
  * The cross-layer sharing modes of CSA2 are compositions of these calls over
  * shared pointers (no mode enum): Full = append + topk + decode; Reindex = topk
  * with its own indexer query over another layer's indexer cache + decode over
@@ -208,6 +210,37 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
                               int32_t B, int32_t H_I, int32_t k,
                               int32_t* out_idx, float* out_scores,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_append_indexer_topk -- one step's quantise-append followed by its indexer
+ * top-k, in one call.
+ *
+ * Exactly mla_kv_append_quant(main_row, idx_row, new_main, new_idx, slots, B,
+ * n_new, capacity, main_cache, main_seq_stride, idx_cache, idx_seq_stride,
+ * new_win, win_pos, win_ring, W, Dw) and then mla_indexer_topk(idx_row, q_idx,
+ * w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, NULL, 0, B,
+ * H_I, k, out_idx, out_scores, workspace, workspace_bytes) on the same stream:
+ * same arguments, same results and the same errors, the new indexer keys scored
+ * from the bytes the append writes ([P1] "DeepSeek-V3.2", "The lightning
+ * indexer": the step's own entry is among the keys its query ranks). Where
+ * the scan kernel can carry it (E4M3 or E2M1 indexer rows of 128 channels, 32
+ * or 64 indexer heads, 16-byte aligned cache, 1 <= n_new <= 4) the append runs
+ * inside the scan's launch, which saves a launch and its memory round trip;
+ * otherwise it is launched first, as its own kernel. idx_cache must not be
+ * NULL; main_cache may be (indexer key and window only). The slots of one
+ * sequence must be distinct.
+ */
+mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
+                                     const float* new_main, const float* new_idx,
+                                     const int32_t* slots, int32_t n_new,
+                                     void* main_cache, int64_t main_seq_stride,
+                                     void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                     const float* new_win, const int32_t* win_pos,
+                                     void* win_ring, int32_t W, int32_t Dw,
+                                     const void* q_idx, const float* w, float score_scale,
+                                     const int32_t* n_visible, int32_t B, int32_t H_I, int32_t k,
+                                     int32_t* out_idx, float* out_scores,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mla_sparse_decode -- absorbed MLA as shared-KV MQA over the selected entries.

@@ -62,6 +62,9 @@ def lib():
         L.mla_indexer_topk.argtypes = [_CRow, P, P, f32, P, i64, i64, P, P, i32, i32, i32, i32,
                                        P, P, P, sz, P]
         L.mla_indexer_topk.restype = i32
+        L.mla_append_indexer_topk.argtypes = [_CRow, _CRow, P, P, P, i32, P, i64, P, i64, i64, P, P, P,
+                                              i32, i32, P, P, f32, P, i32, i32, i32, P, P, P, sz, P]
+        L.mla_append_indexer_topk.restype = i32
         L.mla_sparse_decode_workspace.argtypes = [_CRow, i32, i32, i32, i32, i32]
         L.mla_sparse_decode_workspace.restype = sz
         L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, f32, i32, i32,
@@ -217,6 +220,57 @@ def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_vi
     _check(lib().mla_indexer_topk(
         _crow(idx_row), _ptr(q_idx), _ptr(w), float(score_scale), _ptr(idx_cache), stride,
         idx_cache.shape[1], _ptr(n_visible), None, 0, B, H_I, k, _ptr(out_idx), _ptr(out_scores),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def mla_append_indexer_topk(main_row: Row, idx_row: Row, new_main, new_idx, slots, main_cache, idx_cache,
+                            q_idx, w, score_scale: float, n_visible, k: int, out_idx, workspace,
+                            new_win=None, win_pos=None, win_ring=None, out_scores=None, stream=None):
+    """mla_kv_append_quant then mla_indexer_topk in one call (the append rides in the
+    scan's launch where the scan kernel can carry it).  Arguments as for those two;
+    idx_cache is required, main_cache may be None."""
+    if idx_cache is None:
+        raise ValueError("idx_cache is required")
+    _need(slots, "slots", torch.int32, 2)
+    B, n_new = slots.shape
+    cap = idx_cache.shape[1]
+    if main_cache is not None:
+        _need(new_main, "new_main", torch.float32, 3)
+        if tuple(new_main.shape) != (B, n_new, main_row.dim + main_row.rope) or tuple(main_cache.shape[:2]) != (B, cap):
+            raise ValueError("new_main must be [B, n_new, dim + rope] and main_cache [B, capacity, row_bytes]")
+        if main_cache.shape[2] != row_bytes(main_row):
+            raise ValueError("main_cache rows do not match the row format")
+    _need(new_idx, "new_idx", torch.float32, 3)
+    if tuple(new_idx.shape) != (B, n_new, idx_row.dim) or idx_cache.shape[0] != B:
+        raise ValueError("new_idx must be [B, n_new, idx dim] and idx_cache [B, capacity, row_bytes]")
+    W = Dw = 0
+    if new_win is not None:
+        _need(new_win, "new_win", torch.float32, 2)
+        _need(win_pos, "win_pos", torch.int32, 1)
+        _need(win_ring, "win_ring", torch.bfloat16, 3)
+        _, W, Dw = win_ring.shape
+        if win_ring.shape[0] != B or tuple(new_win.shape) != (B, Dw) or win_pos.shape[0] != B:
+            raise ValueError("window shapes: new_win [B, Dw], win_pos [B], win_ring [B, W, Dw]")
+    _need(q_idx, "q_idx", query_dtype(idx_row), 3)
+    _need(w, "w", torch.float32, 2)
+    _need(n_visible, "n_visible", torch.int32, 1)
+    _need(out_idx, "out_idx", torch.int32, 2)
+    _need(workspace, "workspace", torch.uint8)
+    _, H_I, dq = q_idx.shape
+    if dq != idx_row.dim or q_idx.shape[0] != B or idx_cache.shape[2] != row_bytes(idx_row):
+        raise ValueError("q_idx [B, H_I, dim] and idx_cache [B, capacity, row_bytes] must match the row format")
+    if tuple(w.shape) != (B, H_I) or tuple(n_visible.shape) != (B,) or tuple(out_idx.shape) != (B, k):
+        raise ValueError("w [B, H_I], n_visible [B], out_idx [B, k] expected")
+    if out_scores is not None:
+        _need(out_scores, "out_scores", torch.float32, 2)
+        if tuple(out_scores.shape) != (B, cap):
+            raise ValueError("out_scores must be [B, capacity]")
+    _check(lib().mla_append_indexer_topk(
+        _crow(main_row), _crow(idx_row), _ptr(new_main), _ptr(new_idx), _ptr(slots), n_new,
+        _ptr(main_cache), _cache_stride(main_cache, "main_cache"),
+        _ptr(idx_cache), _cache_stride(idx_cache, "idx_cache"), cap,
+        _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw,
+        _ptr(q_idx), _ptr(w), float(score_scale), _ptr(n_visible), B, H_I, k, _ptr(out_idx), _ptr(out_scores),
         _ptr(workspace), workspace.numel(), _stream(stream)))
 
 

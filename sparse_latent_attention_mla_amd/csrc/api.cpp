@@ -85,57 +85,11 @@ TopkLayout topk_layout(int32_t B, int64_t capacity) {
     return L;
 }
 
-}  // namespace
-
-extern "C" {
-
-int64_t mla_row_bytes(mla_row_t row) {
-    if (row.dim <= 0 || row.rope_dim < 0 || row.dim > 8192 || row.rope_dim > 8192) return -1;
-    switch (row.fmt) {
-    case MLA_FMT_F32: return 4LL * (row.dim + row.rope_dim);
-    case MLA_FMT_BF16: return 2LL * (row.dim + row.rope_dim);
-    case MLA_FMT_E4M3_S128:
-        if (row.dim % 128 != 0 || row.rope_dim % 2 != 0) return -1;
-        return (int64_t)row.dim + 4LL * (row.dim / 128) + 2LL * row.rope_dim;
-    case MLA_FMT_E2M1_S16:
-        if (row.dim % 16 != 0 || row.rope_dim != 0 || row.dim > 1024) return -1;
-        return (int64_t)row.dim / 2 + row.dim / 16;
-    default: return -1;
-    }
-}
-
-const char* mla_status_str(int32_t status) {
-    switch (status) {
-    case MLA_OK: return "ok";
-    case MLA_ERR_INVALID_ARG: return "invalid argument";
-    case MLA_ERR_UNSUPPORTED: return "unsupported format or shape";
-    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
-    case MLA_ERR_HIP: return "HIP error";
-    default: return "unknown status";
-    }
-}
-
-const char* mla_last_error(void) { return g_err; }
-
-mla_status_t mla_profile_enable(int32_t kernels) {
-    mla::prof_enable(static_cast<uint32_t>(kernels));
-    return ok();
-}
-
-mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* total_ms) {
-    if (!kernel || !launches || !total_ms) return fail(MLA_ERR_INVALID_ARG, "mla_profile_read: NULL argument");
-    const int k = mla::prof_index(kernel);
-    if (k < 0) return fail(MLA_ERR_INVALID_ARG, "mla_profile_read: unknown kernel name '%s'", kernel);
-    return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
-}
-
-int32_t mla_version(void) { return 100; }
-
-mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
-                                 const float* new_idx, const int32_t* slots, int32_t B, int32_t n_new,
-                                 int64_t capacity, void* main_cache, int64_t main_seq_stride, void* idx_cache,
-                                 int64_t idx_seq_stride, const float* new_win, const int32_t* win_pos,
-                                 void* win_ring, int32_t W, int32_t Dw, void* stream) {
+// Validated argument block of the quantise-append.
+mla_status_t append_args(mla_row_t main_row, mla_row_t idx_row, const float* new_main, const float* new_idx,
+                         const int32_t* slots, int32_t B, int32_t n_new, int64_t capacity, void* main_cache,
+                         int64_t main_seq_stride, void* idx_cache, int64_t idx_seq_stride, const float* new_win,
+                         const int32_t* win_pos, void* win_ring, int32_t W, int32_t Dw, mla::AppendArgs* out) {
     if (B < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "append: B and n_new must be >= 0");
     mla::AppendArgs a{};
     if (main_cache) {
@@ -180,26 +134,30 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const fl
     a.win_ring = new_win ? static_cast<uint16_t*>(win_ring) : nullptr;
     a.W = W;
     a.Dw = Dw;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    return hip_status(mla::launch_append(a, st), "append launch");
+    *out = a;
+    return ok();
 }
 
-size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
-    (void)k;
-    return topk_layout(B, capacity).total;
-}
+// Validated scan and selection of one top-k call (empty: nothing to compute).
+struct TopkCall {
+    bool empty = false;
+    mla::ScanArgs scan{};
+    mla::TopkWorkspace ws{};
+    int32_t* out_idx = nullptr;
+};
 
-mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
-                              const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
-                              const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
-                              int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
+                       const void* idx_cache, int64_t idx_seq_stride, int64_t capacity, const int32_t* n_visible,
+                       int32_t B, int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
+                       size_t workspace_bytes, TopkCall* out) {
     if (B < 0 || k < 0 || H_I < 1 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "indexer_topk: need B >= 0, k >= 0, H_I >= 1, capacity >= 0");
     if (!(score_scale > 0.0f)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: score_scale must be > 0");
-    if (cand || n_cand) return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: candidate pools are not supported");
     if (idx_row.rope_dim != 0) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: indexer rows have no RoPE part");
-    if (B == 0 || k == 0) return ok();
+    if (B == 0 || k == 0) {
+        out->empty = true;
+        return ok();
+    }
     int64_t rb = 0;
     mla_status_t s = check_rows("indexer_topk", idx_row, idx_cache, idx_seq_stride, capacity, B, &rb);
     if (s != MLA_OK) return s;
@@ -215,15 +173,14 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
         return fail(MLA_ERR_WORKSPACE, "indexer_topk: workspace needs %zu bytes, 256-byte aligned", L.total);
     if (out_scores && !aligned(out_scores, 4)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: misaligned out_scores");
     char* ws = static_cast<char*>(workspace);
-    mla::TopkWorkspace T;
+    mla::TopkWorkspace& T = out->ws;
     T.scores = out_scores ? out_scores : reinterpret_cast<float*>(ws + L.scores);
     T.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     T.counts = reinterpret_cast<uint32_t*>(ws + L.counts);
     T.sel = reinterpret_cast<int32_t*>(ws + L.sel);
     T.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
     T.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    mla::ScanArgs a{};
+    mla::ScanArgs& a = out->scan;
     a.fmt = idx_row.fmt;
     a.dim = idx_row.dim;
     a.row_bytes = rb;
@@ -240,10 +197,121 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
     a.scores = T.scores;
     a.hist = T.hist;
     a.queues = reinterpret_cast<uint32_t*>(ws + L.queues);
-    hipError_t e = mla::launch_scan(a, st);
+    out->out_idx = out_idx;
+    return ok();
+}
+
+// The scan (carrying `append` when given) and the selection.
+mla_status_t topk_launch(const TopkCall& c, const mla::AppendArgs* append, hipStream_t st) {
+    hipError_t e = mla::launch_scan(c.scan, st, append);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
-    e = mla::launch_select(T.scores, capacity, n_visible, B, k, T, out_idx, st);
+    e = mla::launch_select(c.scan.scores, c.scan.capacity, c.scan.n_visible, c.scan.B, c.scan.k, c.ws, c.out_idx, st);
     return hip_status(e, "top-k select");
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mla_row_bytes(mla_row_t row) {
+    if (row.dim <= 0 || row.rope_dim < 0 || row.dim > 8192 || row.rope_dim > 8192) return -1;
+    switch (row.fmt) {
+    case MLA_FMT_F32: return 4LL * (row.dim + row.rope_dim);
+    case MLA_FMT_BF16: return 2LL * (row.dim + row.rope_dim);
+    case MLA_FMT_E4M3_S128:
+        if (row.dim % 128 != 0 || row.rope_dim % 2 != 0) return -1;
+        return (int64_t)row.dim + 4LL * (row.dim / 128) + 2LL * row.rope_dim;
+    case MLA_FMT_E2M1_S16:
+        if (row.dim % 16 != 0 || row.rope_dim != 0 || row.dim > 1024) return -1;
+        return (int64_t)row.dim / 2 + row.dim / 16;
+    default: return -1;
+    }
+}
+
+const char* mla_status_str(int32_t status) {
+    switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char* mla_last_error(void) { return g_err; }
+
+mla_status_t mla_profile_enable(int32_t kernels) {
+    mla::prof_enable(static_cast<uint32_t>(kernels));
+    return ok();
+}
+
+mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* total_ms) {
+    if (!kernel || !launches || !total_ms) return fail(MLA_ERR_INVALID_ARG, "mla_profile_read: NULL argument");
+    const int k = mla::prof_index(kernel);
+    if (k < 0) return fail(MLA_ERR_INVALID_ARG, "mla_profile_read: unknown kernel name '%s'", kernel);
+    return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
+}
+
+int32_t mla_version(void) { return 101; }
+
+mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
+                                 const float* new_idx, const int32_t* slots, int32_t B, int32_t n_new,
+                                 int64_t capacity, void* main_cache, int64_t main_seq_stride, void* idx_cache,
+                                 int64_t idx_seq_stride, const float* new_win, const int32_t* win_pos,
+                                 void* win_ring, int32_t W, int32_t Dw, void* stream) {
+    mla::AppendArgs a{};
+    const mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
+                                       main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W,
+                                       Dw, &a);
+    if (s != MLA_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(mla::launch_append(a, st), "append launch");
+}
+
+size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
+    (void)k;
+    return topk_layout(B, capacity).total;
+}
+
+mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
+                              const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                              const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
+                              int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (cand || n_cand) return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: candidate pools are not supported");
+    TopkCall c;
+    const mla_status_t s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
+                                     B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
+    if (s != MLA_OK || c.empty) return s;
+    return topk_launch(c, nullptr, static_cast<hipStream_t>(stream));
+}
+
+mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
+                                     const float* new_idx, const int32_t* slots, int32_t n_new, void* main_cache,
+                                     int64_t main_seq_stride, void* idx_cache, int64_t idx_seq_stride,
+                                     int64_t capacity, const float* new_win, const int32_t* win_pos,
+                                     void* win_ring, int32_t W, int32_t Dw, const void* q_idx, const float* w,
+                                     float score_scale, const int32_t* n_visible, int32_t B, int32_t H_I,
+                                     int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (!idx_cache) return fail(MLA_ERR_INVALID_ARG, "append_indexer_topk: idx_cache is NULL");
+    mla::AppendArgs ap{};
+    mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
+                                 main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W, Dw, &ap);
+    if (s != MLA_OK) return s;
+    TopkCall c;
+    s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, B, H_I, k,
+                  out_idx, out_scores, workspace, workspace_bytes, &c);
+    if (s != MLA_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c.empty) return hip_status(mla::launch_append(ap, st), "append launch");
+    if (n_new == 0) {                                      // at most a window entry: nothing to carry
+        const mla_status_t sa = hip_status(mla::launch_append(ap, st), "append launch");
+        if (sa != MLA_OK) return sa;
+        return topk_launch(c, nullptr, st);
+    }
+    return topk_launch(c, &ap, st);
 }
 
 size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H, int32_t k, int32_t W) {

@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <cstdlib>
 
+#include "append.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -462,8 +463,19 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
 // 64 (l / 32) + 8 s + e, for queries and keys alike), so a row's score is the
 // sum over its lane's 16 heads per head tile plus the partner lane's (l ^ 32),
 // and the 32 scores of a chunk are written by lanes 0 .. 31 at once.
-template <int FMT, int MT2, int NBUF, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block) {
+//
+// With FUSE the kernel also carries its step's quantise-append (ap, n_new <=
+// kFuseMaxNew entries), cut into pieces of at most 128 channels (piece_load /
+// piece_store): wave w of block (x, 0) carries piece 4x + w, loading it as it
+// starts, while memory is quiet, and quantising and storing it in registers
+// once its own chunks are scored (no LDS, no barrier; extra blocks would
+// outgrow the two per CU that run at once), and the wave whose chunk holds a
+// new slot stages that entry's fp32 key with
+// the queries, quantises it (quant128_wave, byte for byte quant_row's) and
+// writes the bytes over the chunk's row in LDS before it dequantises the chunk,
+// so the row is scored from the bytes the append writes, whatever the load saw.
+template <int FMT, int MT2, int NBUF, int NW, bool FUSE>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block, AppendArgs ap) {
     constexpr int NT = 64 * NW;                          // threads of the block
     constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
     constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
@@ -475,13 +487,42 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     __shared__ uint32_t coarse[kCoarseBins];
     __shared__ __attribute__((aligned(16))) float sc[kDmaRowsPerWave * NW];
     __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NBUF][kBuf];
+    __shared__ __attribute__((aligned(16))) float fuse_src[FUSE ? kFuseMaxNew : 1][128];
+    __shared__ __attribute__((aligned(16))) uint8_t fuse_row[FUSE ? kFuseMaxNew : 1][144];
+    static_assert(NW * NBUF * kBuf >= kAppendLdsBytes, "append scratch in the ring");
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Piece pc;                                              // the carried piece, in registers meanwhile
+    if constexpr (FUSE) {
+        pc.kind = 0;
+        if (blockIdx.y == 0) piece_load(ap, (int64_t)blockIdx.x * NW + wave, pc);
+    }
     const int n32 = lane & 31, h = lane >> 5;
     const int64_t cap = a.capacity;
     const int64_t nvis = clamp_visible(a.n_visible[b], cap);
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+    // new entries whose slot lies in one of this wave's chunks: own_it[e] is that
+    // chunk's iteration (-1: not this wave's), own_r[e] the row in the chunk
+    int own_it[FUSE ? kFuseMaxNew : 1], own_r[FUSE ? kFuseMaxNew : 1];
+    if constexpr (FUSE) {
+#pragma unroll
+        for (int e = 0; e < kFuseMaxNew; ++e) {
+            own_it[e] = -1;
+            own_r[e] = 0;
+            if (e < ap.n_new) {
+                const int64_t sl = ap.slots[(int64_t)b * ap.n_new + e];
+                const int64_t local = sl - row0;
+                if (sl >= 0 && sl < cap && local >= 0 && local < rows_per_block) {
+                    const int ci = (int)(local >> 5);
+                    if (ci % NW == wave) {
+                        own_it[e] = ci / NW;
+                        own_r[e] = (int)(local & 31);
+                    }
+                }
+            }
+        }
+    }
     const int n_it = rows_per_block / (NW * kDmaRows);
     for (int i = threadIdx.x; i < kHistBins / 2; i += NT) hist2[i] = 0u;
     if (threadIdx.x < kCoarseBins) coarse[threadIdx.x] = 0u;
@@ -539,12 +580,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     if (wave == 0)
         dma4_s(a.w + (int64_t)b * a.H_I, lane < a.H_I ? 4u * (uint32_t)lane : 0u,
                __builtin_amdgcn_readfirstlane(lds_addr(sc)));
+    if constexpr (FUSE) {                                  // the owned entries' fp32 keys, 128 channels
+#pragma unroll
+        for (int e = 0; e < kFuseMaxNew; ++e)
+            if (own_it[e] >= 0) {
+                const float* src = ap.new_idx + ((int64_t)b * ap.n_new + e) * 128;
+                const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(&fuse_src[e][0]));
+                dma4_s(src, 4u * (uint32_t)lane, m0);
+                dma4_s(src, 256u + 4u * (uint32_t)lane, m0 + 256u);
+            }
+    }
     int issued = 0;
     for (; issued < NBUF - 1 && issued < n_dma; ++issued) issue(issued);
     if (NBUF == 3 && issued == 2) wait_vmcnt<2 * KI>();
     else if (issued >= 1) wait_vmcnt<KI>();
     else wait_vmcnt<0>();
     __syncthreads();                                       // queries, weights staged; histograms cleared
+    if constexpr (FUSE) {
+#pragma unroll
+        for (int e = 0; e < kFuseMaxNew; ++e)
+            if (own_it[e] >= 0)
+                quant128_wave<FMT>(fuse_src[e][2 * lane], fuse_src[e][2 * lane + 1], &fuse_row[e][0],
+                                   &fuse_row[e][FMT == MLA_FMT_E4M3_S128 ? 128 : 64]);
+    }
     u32x4 qa[MT2][8];                                      // head 32 mt + n32, channels 64 h + 8 s ..
     float wv[MT2][16];                                     // w * sigma of result register v
 #pragma unroll
@@ -572,6 +630,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
         if (NBUF == 3 && c + 1 < n_dma) wait_vmcnt<KI>();
         else wait_vmcnt<0>();
         if (c + NBUF - 1 < n_dma) issue(c + NBUF - 1);
+        if constexpr (FUSE) {                              // a new entry's row: its bytes over the stale ones
+#pragma unroll
+            for (int e = 0; e < kFuseMaxNew; ++e)
+                if (own_it[e] == c && lane < RB / 4)
+                    reinterpret_cast<uint32_t*>(&ring[wave][c % NBUF][0] + own_r[e] * RB)[lane] =
+                        reinterpret_cast<const uint32_t*>(&fuse_row[e][0])[lane];
+        }
         const uint8_t* rp = &ring[wave][c % NBUF][0] + n32 * RB;
         in.mult = 1.0f;
         if constexpr (FMT == MLA_FMT_E4M3_S128) {
@@ -630,6 +695,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
             }
         }
     }
+    if constexpr (FUSE) piece_store(ap, pc);               // every load of the wave has landed
     for (int c = n_dma; c < n_cap; ++c)                     // chunks without a visible row
         if (lane < kDmaRows) sc[(NW * c + wave) * kDmaRows + lane] = -__builtin_inff();
     __syncthreads();
@@ -651,6 +717,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
         cnt[i] = (hist2[f >> 1] >> (16 * (f & 1))) & 0xFFFFu;
     }
     flush_fine_coarse<NT>(cnt, coarse, hb, copy);
+
 }
 
 // The 32x32 scan with its chunks handed out at run time. Workgroup (x, y)
@@ -1018,8 +1085,19 @@ bool scan_supported(int fmt, int dim, int H_I) {
     return H_I * dim <= 8192;
 }
 
-hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
-    if (a.B == 0 || a.capacity == 0) return hipSuccess;
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* append) {
+    // the step's append rides in the 32x32 scan's launch when that kernel runs and the
+    // append writes the scanned cache; otherwise it is launched on its own, first
+    const bool carry = append && append->n_new >= 1 && append->n_new <= kFuseMaxNew && append->B == a.B &&
+                       append->idx_cache == a.cache && append->idx_stride == a.stride && a.dim == 128;
+    auto unfused = [&]() -> hipError_t {
+        if (append) {
+            const hipError_t e = launch_append(*append, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    };
+    if (a.B == 0 || a.capacity == 0) return unfused();
     const bool mfma = (a.fmt == MLA_FMT_BF16 || a.fmt == MLA_FMT_E4M3_S128 || a.fmt == MLA_FMT_E2M1_S16) &&
                       a.dim == 128 && a.H_I % 16 == 0 && a.H_I <= 64;
     if (mfma) {
@@ -1063,23 +1141,35 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
             1, std::min<int64_t>(blk32 / dyn_nq, dyn_chunks / (dyn_nq * kDma32Waves * 4)));
 #define MLA_SCAN_CASE(F, M)                                                                    \
     if (a.fmt == F && a.H_I == 16 * M) {                                                       \
-        const ProfSlot p = prof_slot(PROF_SCAN);                                               \
         if constexpr (F == MLA_FMT_BF16) {                                                     \
+            if (const hipError_t e = unfused(); e != hipSuccess) return e;                     \
+            const ProfSlot p = prof_slot(PROF_SCAN);                                           \
             return launch_kernel(k_scan_bf16<M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a); \
         } else {                                                                               \
+            const ProfSlot p = prof_slot(PROF_SCAN);                                           \
             if (dma) {                                                                         \
                 if constexpr (M % 2 == 0) {                                                    \
+                    if (!dyn && carry && pieces_supported(*append) &&                          \
+                        piece_count(*append) <= (int64_t)d32grid.x * kDma32Waves)              \
+                        return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves, true>,    \
+                                             d32grid, dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, \
+                                             a, (int)d32rpb, *append);                         \
+                    if (const hipError_t e = unfused(); e != hipSuccess) return e;             \
                     if (dyn)                                                                   \
                         return launch_kernel(k_scan_dyn32<F, M / 2, kDma32Waves>,              \
                                              dim3((unsigned)dyn_nq, (unsigned)dyn_per_queue), dim3(64 * kDma32Waves), \
                                              0, stream, p.start, p.stop, a, dyn_lg);   \
-                    return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves>, d32grid,     \
-                                         dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb); \
+                    return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves, false>, d32grid,     \
+                                         dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb, \
+                                         AppendArgs{});                                        \
                 }                                                                              \
-                else                                                                           \
+                else {                                                                         \
+                    if (const hipError_t e = unfused(); e != hipSuccess) return e;             \
                     return launch_kernel(k_scan_dma<F, M, kDmaNbuf>, dgrid, dim3(kScanThreads), 0, \
                                          stream, p.start, p.stop, a, (int)drpb);               \
+                }                                                                              \
             }                                                                                  \
+            if (const hipError_t e = unfused(); e != hipSuccess) return e;                     \
             return launch_kernel(k_scan_staged<F, M>, sgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, \
                                  a, (int)rpb);                                                 \
         }                                                                                      \
@@ -1093,6 +1183,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
 #undef MLA_SCAN_CASE
         return hipErrorInvalidValue;
     }
+    if (const hipError_t e = unfused(); e != hipSuccess) return e;
     const dim3 grid((unsigned)((a.capacity + kScanThreads - 1) / kScanThreads), a.B);
     const ProfSlot p = prof_slot(PROF_SCAN);
     return launch_kernel(k_scan_generic, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a);

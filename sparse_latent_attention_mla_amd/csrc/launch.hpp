@@ -72,7 +72,12 @@ struct ScanArgs {
     uint32_t* hist;         // [B, kHistWordsHost] (see TopkWorkspace)
     uint32_t* queues;       // [kScanQueuesHost, kQueueWordsHost] work queues, zero on entry and on exit
 };
-hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+// Entries of a step's append that the indexer scan can carry in the same launch.
+constexpr int kFuseMaxNew = 4;
+// The scan; with `append` (its cache the scan's, 1 <= n_new <= kFuseMaxNew), the
+// quantise-append of the same step first, in the scan's launch where the scan
+// kernel can carry it, else as its own launch before it.
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* append = nullptr);
 bool scan_supported(int fmt, int dim, int H_I);
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                          const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream);

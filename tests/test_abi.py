@@ -27,7 +27,7 @@ def M():
 
 def test_header_declares_the_three_path_calls():
     names = declared_functions()
-    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode"):
+    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode", "mla_append_indexer_topk"):
         assert n in names
 
 
@@ -83,6 +83,18 @@ def test_host_validation_rejects_before_launch(M):
     assert L.mla_indexer_topk(_row(M, M.F32, 512), C.c_void_p(0x10000), fake, 0.1, C.c_void_p(0x10000),
                               20480, 10, fake, None, 0, 1, 64, 8, fake, None, C.c_void_p(0x100000),
                               1 << 24, None) == 2
+    # append + topk: the indexer cache is required
+    assert L.mla_append_indexer_topk(r_main, r_idx, fake, fake, fake, 1, fake, 6560, None, 0, 10,
+                                     None, None, None, 0, 0, fake, fake, 0.1, fake, 1, 64, 8,
+                                     fake, None, fake, 1 << 20, None) == 1
+    # append + topk: the append half is validated too (unsupported main row format)
+    assert L.mla_append_indexer_topk(_row(M, 9, 512), r_idx, fake, fake, fake, 1, fake, 6560, fake, 1408, 10,
+                                     None, None, None, 0, 0, fake, fake, 0.1, fake, 1, 64, 8,
+                                     fake, None, fake, 1 << 20, None) == 2
+    # append + topk: and the top-k half (workspace too small)
+    assert L.mla_append_indexer_topk(r_main, r_idx, fake, fake, fake, 1, C.c_void_p(0x10000), 6560,
+                                     C.c_void_p(0x10000), 1408, 10, None, None, None, 0, 0, fake, fake, 0.1,
+                                     fake, 1, 64, 8, fake, None, C.c_void_p(0x100000), 16, None) == 3
     # decode: d_v larger than the latent
     assert L.mla_sparse_decode(r_main, 600, fake, fake, 6560, 10, fake, 4, None, None, 0, 0.1, 1, 128,
                                fake, fake, fake, 1 << 30, None) == 1

@@ -333,3 +333,70 @@ def test_scan_work_queues(name, scan, monkeypatch):
         G.check_scores(got_s, ref_s, nv)
         G.check_topk(got_idx, ref_s, nv, k)
         assert not bool(ws[:zero_part].any()), "workspace start not zero after the call"
+
+
+@pytest.mark.parametrize("slots_kind", ["step", "spread"])
+@pytest.mark.parametrize("name", ["c3s", "c4s", "c3m", "c2s", "c1"])
+def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
+    """mla_append_indexer_topk against mla_kv_append_quant then mla_indexer_topk on
+    copies of the same caches whose new slots hold stale bytes: the caches and the
+    window ring byte for byte, the scores bit for bit, the selected sets equal; and
+    against the oracle (the entries re-appended are the ones the caches were built
+    from, so the expected bytes are the case's own). Entries: the step's one (slot
+    N - 1), or four spread over the sequence so that several scan workgroups and
+    waves each own one; visible lengths that include and that exclude slot N - 1.
+    E4M3 and E2M1 indexer rows take the fused kernel, bf16 and fp32 the fallback."""
+    case = case_of(name)
+    cfg = case.cfg
+    B, N, k = cfg.B, cfg.N, cfg.k
+    mr, ir = G.main_row(cfg), G.idx_row(cfg)
+    slots = [N - 1] if slots_kind == "step" else sorted({N - 1, 5 % N, N // 2, (37 * N) // 41})
+    sl = np.tile(np.array(slots, np.int32), (B, 1))
+    new_main = G._t(case.inp.main[:, slots])
+    new_idx = G._t(case.inp.idx[:, slots])
+    p = cfg.tokens - 1
+    posv = G._t(np.full(B, p, np.int32))
+    wl0 = G._t(case.inp.win[0, :, cfg.W - 1]) if cfg.W else None
+
+    def stale():
+        m, i = case.g_main.clone(), case.g_idx.clone()
+        m[:, slots] = 0xA7
+        i[:, slots] = 0x5B
+        wr = None
+        if cfg.W:
+            wr = case.g_win[0].clone()
+            wr[:, p % cfg.W] = 7.0
+        return m, i, wr
+
+    for nv in ([N] * B, [N - 1] + [N] * (B - 1)):
+        nv = np.array(nv, np.int32)
+        say("append+topk", name, slots_kind, slots, nv.tolist())
+        m_a, i_a, w_a = stale()
+        m_b, i_b, w_b = stale()
+        out_a = torch.empty((B, k), dtype=torch.int32, device="cuda")
+        out_b = torch.empty_like(out_a)
+        s_a = torch.empty((B, N), dtype=torch.float32, device="cuda")
+        s_b = torch.empty_like(s_a)
+        ws_a = torch.zeros(G.M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device="cuda")
+        ws_b = torch.zeros_like(ws_a)
+        qi, w = G._qi_gpu(cfg, case.inp.q_idx[0]), G._t(case.inp.w[0])
+        G.M.mla_kv_append_quant(mr, ir, new_main, new_idx, G._t(sl), m_a, i_a,
+                                wl0, posv if cfg.W else None, w_a)
+        G.M.mla_indexer_topk(ir, qi, w, cfg.sigma, i_a, G._t(nv), k, out_a, ws_a, out_scores=s_a)
+        G.M.mla_append_indexer_topk(mr, ir, new_main, new_idx, G._t(sl), m_b, i_b, qi, w, cfg.sigma, G._t(nv),
+                                    k, out_b, ws_b, new_win=wl0, win_pos=posv if cfg.W else None, win_ring=w_b,
+                                    out_scores=s_b)
+        torch.cuda.synchronize()
+        assert torch.equal(m_a, m_b) and torch.equal(i_a, i_b), "caches differ between the paths"
+        assert torch.equal(i_b, case.g_idx) and torch.equal(m_b, case.g_main), "caches differ from the case's"
+        if cfg.W:
+            assert torch.equal(w_a.view(torch.int16), w_b.view(torch.int16))
+            assert torch.equal(w_b.view(torch.int16), case.g_win[0].view(torch.int16))
+        ga, gb = s_a.cpu().numpy(), s_b.cpu().numpy()
+        assert np.array_equal(ga.view(np.uint32), gb.view(np.uint32)), "scores differ bit-wise"
+        oa, ob = out_a.cpu().numpy(), out_b.cpu().numpy()
+        for bb in range(B):
+            assert set(oa[bb].tolist()) == set(ob[bb].tolist())
+        ref_s = G.oracle_scores(case, 0, n_visible=nv)
+        G.check_scores(gb, ref_s, nv)
+        G.check_topk(ob, ref_s, nv, k)

@@ -119,7 +119,7 @@ def build_layers(cfg, n_layers, seed=0):
 
 
 SAMPLE_EVERY = 25
-SCAN_SOURCES = ("csrc/indexer.hip", "csrc/common.hpp", "csrc/launch.hpp", "build.py")
+SCAN_SOURCES = ("csrc/indexer.hip", "csrc/append.hpp", "csrc/common.hpp", "csrc/launch.hpp", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_c3_hbm_traffic.md")
 
 
@@ -303,11 +303,16 @@ def main():
 
     ab = WL.algorithmic_bytes(cfg)
     step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
-    # dominant kernel: the indexer scan.  Per launch it must read every visible
-    # indexer row of the batch plus the indexer queries and head weights; the
-    # scores it writes for the selection are implementation traffic, not counted.
+    # dominant kernel: the indexer scan, which also carries the first layer's
+    # quantise-append.  Per launch it must read every visible indexer row of the
+    # batch plus the indexer queries and head weights, and read the new entries
+    # and write their rows (the step's one entry per sequence: fp32 inputs in,
+    # quantised main row and indexer key out, and the first layer's bf16 window
+    # entry); the scores it writes for the selection are implementation traffic,
+    # not counted.
     n_idx_layers = WL.n_indexers(cfg)
-    scan_bytes = (ab["scan"] + ab["q_idx_w"]) // n_idx_layers
+    carried = B * (M.row_bytes(mr) + M.row_bytes(ir) + 4 * (cfg.D + cfg.d_I)) + (B * cfg.D * 6 if cfg.W else 0)
+    scan_bytes = (ab["scan"] + ab["q_idx_w"]) // n_idx_layers + carried
     scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
@@ -330,7 +335,7 @@ def main():
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "indexer scan (k_scan_dma32)",
+            "kernel": "indexer scan carrying the step's append (k_scan_dma32)",
             "bound": "hbm",
             "achieved": scan_gbps,
             "peak": HBM_PEAK_GBPS,

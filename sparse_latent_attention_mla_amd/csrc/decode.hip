@@ -104,6 +104,27 @@ __device__ __forceinline__ u32x2 ds_tr16(const uint8_t* p) {
                  (uint32_t)(uint16_t)r.z | ((uint32_t)(uint16_t)r.w << 16)};
 }
 
+// One DPP lane permutation of a float (compile-time control word).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xf, 0xf, false));
+}
+// Max / sum over each row of 16 lanes, on the VALU: swaps within pairs and quads
+// (quad_perm 1,0,3,2 and 2,3,0,1), then the two quads of each half row
+// (row_half_mirror) and the two halves (row_mirror).
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    return v + dpp_f<0x140>(v);
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // two floats -> two bf16 (round to nearest even, hardware convert), low half first
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
@@ -183,8 +204,10 @@ Geometry decode_geometry(int B, int H, int k, int W) {
 
 template <int SRC_MAIN, int DQK, int NW, int HT>
 constexpr int decode_lds_bytes(bool window) {
-    if constexpr (NW == 8) {                               // wave-specialised: four chunk buffers
-        constexpr int m = 4 * Stage<SRC_MAIN, DQK>::kBytes, w = 4 * Stage<SRC_BF16, DQK>::kBytes;
+    if constexpr (NW == 8) {                               // wave-specialised: four chunk buffers (E4M3: five + P)
+        constexpr int m = SRC_MAIN == SRC_E4M3 ? 5 * Stage<SRC_MAIN, DQK>::kBytes + (2 * 16 * kZs + 4 * 16) * 4
+                                               : 4 * Stage<SRC_MAIN, DQK>::kBytes;
+        constexpr int w = 4 * Stage<SRC_BF16, DQK>::kBytes;
         return Waves<4, 1>::kBuf + ((window && w > m) ? w : m);
     } else {
         constexpr int m = Stage<SRC_MAIN, DQK>::kLds, w = Stage<SRC_BF16, DQK>::kLds;
@@ -553,13 +576,22 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
 // overlap and there is one barrier per chunk. Before that barrier the QK waves
 // wait for their own loads of chunk c + 2, which the barrier then makes visible
 // to all. Four chunk buffers: c (PV), c + 1 (QK), c + 2 (landed), c + 3 (in flight).
-template <int SRC, int DQK>
+// With SMQK (E4M3 rows) the softmax moves to the QK waves and runs once per
+// chunk instead of once in every PV wave, and the PV waves take over the row
+// gathers: in step c the QK waves score chunk c + 1 and turn chunk c's scores
+// into P (wave q: heads 4q .. 4q + 3, two rows per lane, the lazy reference
+// per head), writing P and the reference's factor to LDS, while the PV waves
+// issue chunk c + 3, rescale and accumulate chunk c - 1 and wait for their
+// loads of chunk c + 2; five chunk buffers (c - 1 for PV, c idle, c + 1 .. c + 3),
+// one barrier per step.
+template <int SRC, int DQK, bool SMQK>
 __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
                                                 bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
     using G = Stage<SRC, DQK>;
     using V = Waves<4, 1>;                                  // score layout of the 4 QK waves
     static_assert(G::kDirect, "rows staged by DMA");
-    constexpr int NB = 4;
+    constexpr int NB = SMQK ? 5 : 4;
+    static_assert(!SMQK || SRC == SRC_E4M3, "P in LDS: E4M3 rows");
     constexpr int kHi = (G::kInstr + 3) / 4;              // loads per QK wave, waves q < kInstr % 4
     constexpr int kLo = G::kInstr / 4;
     constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
@@ -701,6 +733,31 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
         *reinterpret_cast<f32x4*>(zd) = acc;
     };
 
+    // ---- SMQK: P [2 parities][16 heads][kZs], the reference's factor [2][16], final l, m [2][16]
+    float* pbuf = reinterpret_cast<float*>(bufs + NB * G::kBytes);
+    float* abuf = pbuf + 2 * 16 * kZs;
+    float* lmbuf = abuf + 2 * 16;
+    float m_q = -__builtin_inff(), l_q = 0.0f;              // QK lane's head 4q + lane / 16
+    auto softmax_qk = [&](int c) {
+        const int hh = 4 * q + (lane >> 4), r0 = 2 * (lane & 15);
+        const f32x2 za = *reinterpret_cast<const f32x2*>(zs + (((c & 1) * 2) * 16 + hh) * kZs + r0);
+        const f32x2 zb = *reinterpret_cast<const f32x2*>(zs + (((c & 1) * 2 + 1) * 16 + hh) * kZs + r0);
+        const u32x2 iv = *reinterpret_cast<const u32x2*>(ridx + kChunk * c + r0);
+        const float z0 = ((int32_t)iv.x >= 0) ? (za.x + zb.x) * zscale : -__builtin_inff();
+        const float z1 = ((int32_t)iv.y >= 0) ? (za.y + zb.y) * zscale : -__builtin_inff();
+        const float cm = row16_max(fmaxf(z0, z1));        // the head's 16 lanes
+        // the reference moves only when the chunk exceeds it by more than 2^kLazy (and on
+        // the first chunk with a visible row, where the factor is exp2(-inf) = 0 on empty state)
+        const bool up = cm > m_q + kLazy;
+        const float alpha = up ? __builtin_amdgcn_exp2f(m_q - cm) : 1.0f;
+        m_q = up ? cm : m_q;
+        const float p0 = (z0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z0 - m_q);
+        const float p1 = (z1 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z1 - m_q);
+        l_q = l_q * alpha + (p0 + p1);
+        *reinterpret_cast<f32x2*>(pbuf + ((c & 1) * 16 + hh) * kZs + r0) = f32x2{p0, p1};
+        if ((lane & 15) == 0) abuf[(c & 1) * 16 + hh] = alpha;
+    };
+
     // ---- PV waves' running state: reference max (base 2, lazily raised), partial sums, output tile
     f32x4 o[8];
 #pragma unroll
@@ -708,6 +765,27 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
     float m_ref = -__builtin_inff(), l_run = 0.0f;
     auto pv = [&](int c) {
         const uint8_t* buf = bufs + (c % NB) * G::kBytes;
+        u32x4 pa, pb;                                       // PV B operands: P (times the E4M3 scale), bf16 hi + lo
+        if constexpr (SMQK) {
+            float sc[8];                                    // the rows' scale of block q
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 + 4 * q);
+            const float alpha = abuf[(c & 1) * 16 + j];
+            const float* pr = pbuf + ((c & 1) * 16 + j) * kZs + 8 * g;
+            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) o[mt] = o[mt] * alpha;
+            }
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = p0[e] * sc[e];
+                p[4 + e] = p1[e] * sc[4 + e];
+            }
+            split_bf16x8(p, pa, pb);
+        } else {
         // softmax on the chunk; lane (j, g) holds rows 8 g .. 8 g + 7 of head j
         bool vld[8];
         {
@@ -754,7 +832,6 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) o[mt] = o[mt] * alpha;
         }
-        u32x4 pa, pb;                                       // PV B operands: P (times the E4M3 scale), bf16 hi + lo
         {
             float ls = 0.0f;
             float p[8];
@@ -766,6 +843,7 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
             }
             l_run += ls;
             split_bf16x8(p, pa, pb);
+        }
         }
         // O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels 128 q .. +127
 #pragma unroll
@@ -786,7 +864,16 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
 
     // ---- prologue: chunks 0 .. 2 in flight, chunk 0 landed and scored, chunk 1 landed
     uint32_t zm0 = 0, zm1 = 0, zm2 = 0;                     // zero masks of chunks c + 1, c + 2, c + 3
-    if (qk_role) {
+    if (SMQK) {                                            // QK waves gather chunks 0, 1; PV waves from 2 on
+        if (qk_role) {
+            uint32_t z0 = 0;
+            if (nc > 0) z0 = issue(0);
+            if (nc > 1) zm0 = issue(1);
+            if (nc > 0) land(0, nc > 1 ? 1 : 0, z0);
+        } else if (nc > 2) {
+            zm1 = issue(2);
+        }
+    } else if (qk_role) {
         uint32_t z0 = 0;
         if (nc > 0) z0 = issue(0);
         if (nc > 1) zm0 = issue(1);
@@ -796,13 +883,36 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
     __syncthreads();
     if (qk_role) {
         if (nc > 0) qk(0);
-        if (nc > 1) land(1, nc > 2 ? 1 : 0, zm0);
+        if (nc > 1) land(1, (!SMQK && nc > 2) ? 1 : 0, zm0);   // with SMQK chunk 2 is the PV waves' load
     }
     __syncthreads();
 
     // each role in a loop of its own, one barrier per chunk in both (the output tile
     // then lives in the PV loop alone; a shared loop made the compiler copy it per chunk)
-    if (qk_role) {
+    if constexpr (SMQK) {                                  // step c: scores c + 1, P of c, PV of c - 1
+        if (qk_role) {
+            for (int c = 0; c <= nc; ++c) {
+                if (c + 1 < nc) qk(c + 1);
+                if (c < nc) softmax_qk(c);
+                __syncthreads();
+            }
+            const float l = row16_sum(l_q);                // the head's sum over its 16 lanes
+            if ((lane & 15) == 0) {
+                lmbuf[4 * q + (lane >> 4)] = l;
+                lmbuf[16 + 4 * q + (lane >> 4)] = m_q;
+            }
+        } else {
+            for (int c = 0; c <= nc; ++c) {
+                if (c + 3 < nc) zm2 = issue(c + 3);        // into chunk c - 2's buffer (read before the barrier)
+                if (c >= 1) pv(c - 1);
+                if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
+                zm1 = zm2;
+                zm2 = 0;
+                __syncthreads();
+            }
+        }
+        __syncthreads();                                   // l and the reference of every head
+    } else if (qk_role) {
         for (int c = 0; c < nc; ++c) {
             if (c + 3 < nc) zm2 = issue(c + 3);            // into chunk c - 1's buffer (read before the barrier)
             if (c + 1 < nc) qk(c + 1);
@@ -820,7 +930,8 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
 
     // ---- partial: normalised output (channels 128 q ..) and logsumexp of the split
     if (!qk_role) {
-        const float l = xsum4(l_run);
+        const float l = SMQK ? lmbuf[j] : xsum4(l_run);
+        const float mref = SMQK ? lmbuf[16 + j] : m_ref;
         const int head = 16 * hg + j;
         const int64_t prow = ((int64_t)b * S + split) * a.H + head;
         const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
@@ -829,7 +940,7 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
             *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * q + 16 * mt + 4 * g) =
                 make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
         if (q == 0 && g == 0)
-            lse_part[prow] = (l > 0.0f) ? (m_ref + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
+            lse_part[prow] = (l > 0.0f) ? (mref + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
                                         : -__builtin_inff();
     }
 }
@@ -853,7 +964,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
         const int64_t first = (int64_t)split * rps;
         const int n = (int)((a.k - first < rps) ? a.k - first : rps);
         if constexpr (NW == 8)
-            decode_split_ws<SRC_MAIN, DQK>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
+            decode_split_ws<SRC_MAIN, DQK, SRC_MAIN == SRC_E4M3>(a, smem, b, split, S, hg, false, first, n, o_part,
+                                                                  lse_part);
         else
             decode_split<SRC_MAIN, DQK, NW, HT>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
     } else {
@@ -862,7 +974,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
         int n = (int)(wl - first);
         n = n < 0 ? 0 : (n > rps ? rps : n);
         if constexpr (NW == 8)
-            decode_split_ws<SRC_BF16, DQK>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+            decode_split_ws<SRC_BF16, DQK, false>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
         else
             decode_split<SRC_BF16, DQK, NW, HT>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
     }

@@ -65,16 +65,24 @@ __device__ __forceinline__ void zero_hist(uint32_t* hb) {
     for (int i = threadIdx.x; i < (int)(kHistWordsHost / 4); i += blockDim.x) p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// The sum over the copies of coarse bin 63 - lane (the first wave of a block;
+// loaded early, used by zero_hist_rest).
+__device__ __forceinline__ uint32_t coarse_sum_of_lane(const uint32_t* hb) {
+    const int lane = threadIdx.x & 63;
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kHistCopies; ++j) sum += hist_coarse(const_cast<uint32_t*>(hb), j)[kCoarseBins - 1 - lane];
+    return sum;
+}
+
 // What k_select leaves of the zeroing: the coarse level and, when there is a
 // threshold, the fine bins of its coarse bin (found again from the coarse level,
-// as the threshold search does). Called by every thread of a block of >= 128.
-__device__ __forceinline__ void zero_hist_rest(uint32_t* hb, uint32_t need) {
+// as the threshold search does; `sum`: coarse_sum_of_lane, for the first wave).
+// Called by every thread of a block of >= 128.
+__device__ __forceinline__ void zero_hist_rest(uint32_t* hb, uint32_t need, uint32_t sum) {
     __shared__ int cb_s;
     const int t = threadIdx.x, lane = t & 63;
     if (t < 64) {
-        uint32_t sum = 0;
-#pragma unroll
-        for (int j = 0; j < kHistCopies; ++j) sum += hist_coarse(hb, j)[kCoarseBins - 1 - lane];
         const uint32_t incl = wave_incl_scan(sum), excl = incl - sum;
         const uint64_t hit = __ballot(excl < need && incl >= need);
         if (t == 0) cb_s = hit ? kCoarseBins - 1 - __builtin_ctzll(hit) : -1;
@@ -579,7 +587,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
     for (int i = t; i < kMaxDigitBins; i += kSelThreads) L.h[0][i] = 0u;
     __syncthreads();
     const uint32_t need = (want > nsel) ? want - nsel : 0u;
-    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);   // the stores drain during the radix
+    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k,
+                   threadIdx.x < 64 ? coarse_sum_of_lane(ws.hist + (int64_t)b * kHistWordsHost) : 0u);   // the stores drain during the radix
     radix_take_any<kSelThreads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
     for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out[i] = -1;
@@ -611,6 +620,8 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
 
     // every load unconditional, from a clamped in-bounds address, so that the waits
     // for the counts (issued first) do not cover the list loads behind them
+    // wave 0 also loads the coarse histogram sums the zeroing needs at the end
+    const uint32_t csum = (t < 64) ? coarse_sum_of_lane(ws.hist + (int64_t)b * kHistWordsHost) : 0u;
     const bool has_cnt = t < groups;
     const u32x2 c2 = *reinterpret_cast<const u32x2*>(ws.counts + ((int64_t)b * groups + (has_cnt ? t : 0)) * 2);
     int32_t vs[kF2Spec];
@@ -680,14 +691,15 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
         for (uint32_t i = i0 + lane; i < nc; i += 64) place_cnd(j, i, gcnd[(int64_t)j * kSelRows + i]);
     }
     __syncthreads();
-    if (ncand > (uint32_t)kFinalLds)                     // the radix passes then read one contiguous list
+    if (ncand > (uint32_t)kFinalLds) {                   // the radix passes then read one contiguous list
         for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kF2Threads) gc2[i] = L.lc[i];
-    __threadfence_block();
+        __threadfence_block();                             // (only then: it waits for every store)
+    }
     if (t == 0) cursor = nsel;
     for (int i = t; i < kMaxDigitBins; i += kF2Threads) L.h[0][i] = 0u;
     __syncthreads();
     const uint32_t need = (want > nsel) ? want - nsel : 0u;
-    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);   // the stores drain during the radix
+    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k, csum);   // the stores drain during the radix
     radix_take_any<kF2Threads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
     for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out[i] = -1;

@@ -38,7 +38,7 @@ constexpr int kDmaRowsPerWave = 256;      // rows of a block per wave, at most (
 #endif
 constexpr int kDma32Waves = MLA_SCAN_WAVES;
 #ifndef MLA_SCAN_NBUF
-#define MLA_SCAN_NBUF 3                   // chunk buffers per wave in the LDS-DMA scan
+#define MLA_SCAN_NBUF 2                   // chunk buffers per wave in the LDS-DMA scan
 #endif
 constexpr int kDmaNbuf = MLA_SCAN_NBUF;
 constexpr int kDmaBlocksPerCu = (kDmaNbuf == 2) ? 3 : 2;   // what the LDS of one CU holds
@@ -1121,7 +1121,12 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         drpb = std::min<int64_t>(std::max<int64_t>(drpb, 4 * kDmaRows), kDmaMaxRowsPerBlock);
         const dim3 dgrid((unsigned)((a.capacity + drpb - 1) / drpb), a.B);
         // the 32x32 scan: blocks of kDma32Waves waves, as many as the CUs hold at once
-        const int64_t blk32 = (int64_t)(dma_target * 4 / kDma32Waves);
+        // (two 4-wave blocks per CU, whatever the ring depth)
+        int64_t blk32 = 256 * (8 / kDma32Waves);
+        if (const char* e = getenv("MLA_SCAN_BLOCKS")) {
+            const int64_t v = atoll(e);
+            if (v >= 1 && v <= 65536) blk32 = v * 4 / kDma32Waves;
+        }
         const int64_t per_seq32 = (blk32 + a.B - 1) / a.B;
         const int64_t unit32 = (int64_t)kDma32Waves * kDmaRows;
         int64_t d32rpb = (a.capacity + per_seq32 - 1) / per_seq32;

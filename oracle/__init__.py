@@ -44,6 +44,7 @@ def lib():
         L.orc_indexer_scores.argtypes = [i32, i32, P, P, f32, P, i64, P, P, i32, i32, i32, i64, P]
         L.orc_indexer_scores.restype = i32
         L.orc_topk.argtypes, L.orc_topk.restype = [P, i64, P, P, i32, i32, i32, P], i32
+        L.orc_pool.argtypes, L.orc_pool.restype = [P, i64, P, i32, i32, i32, P], i32
         L.orc_attention.argtypes = [i32, i32, i32, i32, P, P, i64, i64, P, i32, P, P, i32,
                                     f32, i32, i32, P, P]
         L.orc_attention.restype = i32
@@ -193,6 +194,26 @@ def topk(scores, n_visible, k, n_rows=None, cand=None):
                         0 if cand is None else cand_a.shape[1], B, k, _p(out))
     _check(rc, "topk")
     return out
+
+
+def pool(scores, n_visible, n_blocks, block=8):
+    """Candidate pool of the hierarchical sparse indexer: the block indices
+    [B, n_blocks] of the n_blocks blocks (of `block` consecutive positions) with
+    the largest maximum visible score, -1 padded."""
+    scores = _c(scores, np.float32)
+    B, n_rows = scores.shape
+    out = np.empty((B, n_blocks), dtype=np.int32)
+    rc = lib().orc_pool(_p(scores), n_rows, _p(_c(n_visible, np.int32)), B, block, n_blocks, _p(out))
+    _check(rc, "pool")
+    return out
+
+
+def pool_positions(blocks, block=8):
+    """The positions [B, block * n_blocks] of a pool's blocks (-1 for -1)."""
+    blocks = np.asarray(blocks, np.int64)
+    pos = blocks[:, :, None] * block + np.arange(block)[None, None, :]
+    pos = np.where(blocks[:, :, None] < 0, -1, pos)
+    return pos.reshape(blocks.shape[0], -1).astype(np.int32)
 
 
 def attention(main_row, d_v, q, main_cache, idx, softmax_scale, win_ring=None, win_len=None):

@@ -419,6 +419,54 @@ int orc_topk(const float* scores, int64_t n_rows, const int32_t* n_visible,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Candidate pool of the hierarchical sparse indexer ([P4] "The Hierarchical
+ * Sparse Indexer: bounded sweeps"; [P3] "The hierarchical indexer"): the
+ * positions of one layer's scores are grouped into blocks of `block`
+ * consecutive positions (block i = positions block*i .. block*i + block - 1),
+ * each block is scored by the largest score among its visible positions
+ * (blocks with none are left out), and the n_blocks best blocks are kept,
+ * ordered by that score descending, then block index ascending (the same
+ * order as the top-k).  out_blocks[b, :] holds their block indices, -1 past
+ * the number of blocks with a visible position.
+ * Pins: block 1 reduces to the top-k; enough blocks keep every block with a
+ * visible position; the pool holds every position of the layer's own top-k
+ * for k <= n_blocks (a block holding the j-th best position scores at least
+ * as much, and at most j - 1 other blocks score more); ties go to the smaller
+ * block; hand fixtures. */
+int orc_pool(const float* scores, int64_t n_rows, const int32_t* n_visible, int B, int block, int n_blocks,
+             int32_t* out_blocks) {
+    int b;
+    if (B < 0 || block <= 0 || n_blocks < 0 || n_rows < 0) return -1;
+    for (b = 0; b < B; b++) {
+        int64_t nb = (n_rows + block - 1) / block, n = 0, i;
+        orc_pair* v = (orc_pair*)malloc(sizeof(orc_pair) * (size_t)(nb > 0 ? nb : 1));
+        if (n_visible[b] < 0 || n_visible[b] > n_rows) {
+            free(v);
+            return -2;
+        }
+        for (i = 0; i < nb; i++) {
+            int64_t s, lo = i * block, hi = lo + block;
+            int any = 0;
+            float m = 0.0f;
+            if (hi > n_visible[b]) hi = n_visible[b];
+            for (s = lo; s < hi; s++) {
+                float x = scores[b * n_rows + s];
+                if (!any || x > m) m = x;
+                any = 1;
+            }
+            if (!any) continue;
+            v[n].score = m;
+            v[n].pos = (int32_t)i;
+            n++;
+        }
+        qsort(v, (size_t)n, sizeof(orc_pair), cmp_pair);
+        for (i = 0; i < n_blocks; i++) out_blocks[(int64_t)b * n_blocks + i] = (i < n) ? v[i].pos : -1;
+        free(v);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Sparse attention in the absorbed (MQA) form ([P1] "DeepSeek-V2", "Why RoPE
  * breaks the trick" and "Check it in numpy"; [P2] Part 2 "What replaced MLA";
  * [P1] "DeepSeek-V3.2": each selected latent is shared by all query heads).

@@ -151,6 +151,50 @@ def test_topk_with_candidate_pool_returns_positions():
     assert list(got[0]) == [int(cand[0, i]) for i in best]
 
 
+# ---- candidate pool (hierarchical sparse indexer) -------------------------
+def test_pool_hand_fixture():
+    """Blocks of 4 over 14 positions, 11 visible: block 0 scores 9, block 1
+    scores 7, block 2 scores 8 (positions 8 .. 10; the 12s lie past n_visible),
+    block 3 has no visible position; so the pool is 0, 2, 1, then -1."""
+    s = np.array([[1, 9, 2, 3, 0, 5, 7, 6, 8, -1, 4, 12, 12, 3]], np.float32)
+    nv = np.array([11], np.int32)
+    assert O.pool(s, nv, 3, block=4).tolist() == [[0, 2, 1]]
+    assert O.pool(s, nv, 5, block=4).tolist() == [[0, 2, 1, -1, -1]]
+    assert O.pool(s, nv, 2, block=4).tolist() == [[0, 2]]
+    # equal maxima: the smaller block first
+    t = np.array([[5, 1, 2, 5, 0, 0]], np.float32)
+    assert O.pool(t, np.array([6], np.int32), 3, block=2).tolist() == [[0, 1, 2]]
+    assert O.pool(t, np.array([6], np.int32), 1, block=3).tolist() == [[0]]
+
+
+def test_pool_of_block_one_is_the_topk():
+    rng = np.random.default_rng(21)
+    s = rng.standard_normal((3, 300)).astype(np.float32)
+    s[1, 10:20] = 0.5                                   # ties
+    nv = np.array([300, 123, 7], np.int32)
+    for n in (1, 40, 300):
+        assert np.array_equal(O.pool(s, nv, n, block=1), O.topk(s, nv, n))
+
+
+def test_pool_keeps_every_visible_block_and_contains_the_topk():
+    rng = np.random.default_rng(22)
+    B, N, blk = 4, 1000, 8
+    s = rng.standard_normal((B, N)).astype(np.float32)
+    nv = np.array([1000, 997, 9, 0], np.int32)
+    everything = O.pool(s, nv, N // blk + 5, block=blk)
+    for b in range(B):
+        vis_blocks = (int(nv[b]) + blk - 1) // blk
+        got = everything[b]
+        assert sorted(got[got >= 0].tolist()) == list(range(vis_blocks))
+        assert np.all(got[vis_blocks:] == -1)
+    for n_blocks, k in ((20, 20), (20, 7), (64, 64)):
+        pool = O.pool(s, nv, n_blocks, block=blk)
+        top = O.topk(s, nv, k)
+        for b in range(B):
+            members = {int(p) for p in O.pool_positions(pool[b:b + 1], blk)[0] if p >= 0}
+            assert {int(p) for p in top[b] if p >= 0} <= members
+
+
 # ---- attention -------------------------------------------------------------
 def test_absorbed_attention_equals_naive_mla_pages_example(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "absorption_worked_example.json")))

@@ -10,7 +10,9 @@
  *   mla_sparse_decode     absorbed-MLA attention over the selected entries (plus the
  *                         window), online softmax, logsumexp output.
  * mla_append_indexer_topk is the first two in one call (the append then rides in
- * the scan's launch where the scan kernel can carry it).
+ * the scan's launch where the scan kernel can carry it).  mla_indexer_pool turns
+ * one layer's scores into the candidate pool of the hierarchical sparse indexer,
+ * which deeper layers' mla_indexer_topk calls then score instead of every row.
  * The cross-layer sharing modes of CSA2 are compositions of these calls over
  * shared pointers (no mode enum): Full = append + topk + decode; Reindex = topk
  * with its own indexer query over another layer's indexer cache + decode over
@@ -185,11 +187,22 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
  *  idx_cache    indexer rows, row s of sequence b at b*idx_seq_stride + s*row_bytes
  *  capacity     rows allocated per sequence (the scan covers rows < n_visible[b] <= capacity)
  *  n_visible    int32 [B] on the device, each in [0, capacity]
- *  cand, n_cand must be NULL and 0 (candidate pools are not supported yet)
+ *  cand, n_cand NULL and 0: every row is a candidate.  Otherwise a candidate pool
+ *               ([P4] "The Hierarchical Sparse Indexer: bounded sweeps"; [P1]
+ *               "DeepSeek-V4.1", "The hierarchical indexer": a Reindex layer scores
+ *               only the positions a Full layer published, e.g. by
+ *               mla_indexer_pool): int32 [B, n_cand] positions, n_cand >= 0, on the
+ *               device.  Only the pool's positions are scored; an entry that is
+ *               negative or not below n_visible[b] is never selected (its score is
+ *               -inf).  The positions of one sequence's pool must be distinct.
+ *               The selection is over the pool's visible positions with the same
+ *               order and tie rule, and out_idx holds positions as without a pool.
  *  out_idx      int32 [B, k]
- *  out_scores   optional fp32 [B, capacity]: the scores, -inf for masked rows
- *  workspace    device scratch of at least mla_indexer_topk_workspace(B, capacity, k)
- *               bytes, 256-byte aligned, ZEROED BEFORE ITS FIRST USE (e.g. hipMemset once
+ *  out_scores   optional fp32 [B, capacity], or [B, n_cand] with a pool (entry i =
+ *               the score of position cand[b, i]): the scores, -inf for masked rows
+ *  workspace    device scratch of at least mla_indexer_topk_workspace(B, R, k) bytes,
+ *               R = capacity (with a pool: the larger of capacity and n_cand),
+ *               256-byte aligned, ZEROED BEFORE ITS FIRST USE (e.g. hipMemset once
  *               after allocation). It holds the scan's work-queue counters and the score
  *               histogram at its start; every call
  *               that returns MLA_OK leaves that part zeroed again, so one workspace serves
@@ -197,8 +210,8 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
  *               fails with MLA_ERR_HIP may leave it dirty: zero it again. Calls that
  *               share a workspace must not overlap in time (one stream, or ordered).
  * Errors: MLA_ERR_INVALID_ARG (pointers, B < 0, H_I < 1, k < 0, capacity < 0,
- * score_scale <= 0, misalignment), MLA_ERR_UNSUPPORTED (format / H_I / dim with
- * no kernel, or a candidate pool), MLA_ERR_WORKSPACE.
+ * n_cand < 0 or n_cand > 0 without cand, score_scale <= 0, misalignment),
+ * MLA_ERR_UNSUPPORTED (format / H_I / dim with no kernel), MLA_ERR_WORKSPACE.
  */
 size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k);
 
@@ -209,6 +222,42 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
                               const int32_t* cand, int32_t n_cand,
                               int32_t B, int32_t H_I, int32_t k,
                               int32_t* out_idx, float* out_scores,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_indexer_pool -- the candidate pool of the hierarchical sparse indexer.
+ *
+ * From one layer's indexer scores ([P4] "The Hierarchical Sparse Indexer:
+ * bounded sweeps"; [P1] "DeepSeek-V4.1", "The hierarchical indexer"): the positions of
+ * sequence b are grouped into blocks of `block` consecutive positions (block i =
+ * positions block*i .. block*i + block - 1), each block holding a visible position
+ * is scored by the largest score among its visible positions, and the n_blocks
+ * best blocks are kept (order by block score descending, ties to the smaller
+ * block index, as in mla_indexer_topk).  out_pos[b] receives the positions of the
+ * kept blocks, block*i + j for j < block in slots block*m .. block*m + block - 1 of
+ * the m-th kept block (the order of the blocks is unspecified); the block slots
+ * past min(n_blocks, blocks with a visible position) hold -1.  A kept partial last
+ * block also lists its positions at or past n_visible[b]: mla_indexer_topk never
+ * selects them.  V4.1 publishes 2,048 blocks of 8 (16,384 positions).
+ *
+ *  scores     fp32 [B, capacity] on the device, e.g. the out_scores of the layer's
+ *             own mla_indexer_topk call; entries at or past n_visible[b] are not read
+ *  n_visible  int32 [B], each in [0, capacity]
+ *  block      a power of two, 1 .. 64 (block 1 gives the top-n_blocks positions)
+ *  n_blocks   blocks kept per sequence (>= 0)
+ *  out_pos    int32 [B, n_blocks * block]
+ *  workspace  at least mla_indexer_pool_workspace(B, capacity, block) bytes,
+ *             256-byte aligned, under the same zeroing contract as the workspace
+ *             of mla_indexer_topk (the two may share one buffer that is large
+ *             enough for both, used by one call at a time)
+ * Errors: MLA_ERR_INVALID_ARG (pointers, B < 0, capacity < 0, n_blocks < 0,
+ * misalignment), MLA_ERR_UNSUPPORTED (block not a power of two <= 64, sizes at or
+ * over 2^31), MLA_ERR_WORKSPACE.
+ */
+size_t mla_indexer_pool_workspace(int32_t B, int64_t capacity, int32_t block);
+
+mla_status_t mla_indexer_pool(const float* scores, int64_t capacity, const int32_t* n_visible,
+                              int32_t B, int32_t block, int32_t n_blocks, int32_t* out_pos,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*

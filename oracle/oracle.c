@@ -420,7 +420,8 @@ int orc_topk(const float* scores, int64_t n_rows, const int32_t* n_visible,
 
 /* ------------------------------------------------------------------------- */
 /* Candidate pool of the hierarchical sparse indexer ([P4] "The Hierarchical
- * Sparse Indexer: bounded sweeps"; [P3] "The hierarchical indexer"): the
+ * Sparse Indexer: bounded sweeps"; [P1] "DeepSeek-V4.1", "The hierarchical
+ * indexer"): the
  * positions of one layer's scores are grouped into blocks of `block`
  * consecutive positions (block i = positions block*i .. block*i + block - 1),
  * each block is scored by the largest score among its visible positions

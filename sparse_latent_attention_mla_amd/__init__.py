@@ -65,6 +65,9 @@ def lib():
         L.mla_append_indexer_topk.argtypes = [_CRow, _CRow, P, P, P, i32, P, i64, P, i64, i64, P, P, P,
                                               i32, i32, P, P, f32, P, i32, i32, i32, P, P, P, sz, P]
         L.mla_append_indexer_topk.restype = i32
+        L.mla_indexer_pool_workspace.argtypes, L.mla_indexer_pool_workspace.restype = [i32, i64, i32], sz
+        L.mla_indexer_pool.argtypes = [P, i64, P, i32, i32, i32, P, P, sz, P]
+        L.mla_indexer_pool.restype = i32
         L.mla_sparse_decode_workspace.argtypes = [_CRow, i32, i32, i32, i32, i32]
         L.mla_sparse_decode_workspace.restype = sz
         L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, f32, i32, i32,
@@ -196,11 +199,13 @@ def mla_indexer_topk_workspace(B: int, capacity: int, k: int) -> int:
 
 
 def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_visible, k: int,
-                     out_idx, workspace, out_scores=None, stream=None):
+                     out_idx, workspace, out_scores=None, stream=None, cand=None):
     """Indexer scan + mask + top-k.  q_idx [B, H_I, d_I] (bf16; fp32 for F32 rows), w fp32 [B, H_I],
     idx_cache uint8 [B, capacity, row_bytes], n_visible int32 [B], out_idx int32 [B, k],
     workspace uint8 of mla_indexer_topk_workspace bytes, zeroed before its first use (every
-    successful call leaves it ready for the next), out_scores fp32 [B, capacity] (optional)."""
+    successful call leaves it ready for the next), out_scores fp32 [B, capacity] (optional).
+    cand: optional int32 [B, n_cand] candidate pool (positions); only those are scored, and
+    out_scores is then [B, n_cand]."""
     _need(q_idx, "q_idx", query_dtype(idx_row), 3)
     _need(w, "w", torch.float32, 2)
     _need(n_visible, "n_visible", torch.int32, 1)
@@ -213,14 +218,43 @@ def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_vi
         raise ValueError("q_idx [B, H_I, dim] and idx_cache [B, capacity, row_bytes] must match the row format")
     if tuple(w.shape) != (B, H_I) or tuple(n_visible.shape) != (B,) or tuple(out_idx.shape) != (B, k):
         raise ValueError("w [B, H_I], n_visible [B], out_idx [B, k] expected")
+    n_cand = 0
+    if cand is not None:
+        _need(cand, "cand", torch.int32, 2)
+        if cand.shape[0] != B:
+            raise ValueError("cand must be [B, n_cand]")
+        n_cand = cand.shape[1]
     if out_scores is not None:
         _need(out_scores, "out_scores", torch.float32, 2)
-        if tuple(out_scores.shape) != (B, cap):
-            raise ValueError("out_scores must be [B, capacity]")
+        if tuple(out_scores.shape) != (B, cap if cand is None else n_cand):
+            raise ValueError("out_scores must be [B, capacity] ([B, n_cand] with a pool)")
+    # an empty pool is still a pool: the C ABI takes it as a non-NULL cand with n_cand 0
+    # (never read), so an empty tensor's null data pointer is replaced by out_idx's
+    cand_p = None if cand is None else (_ptr(cand) if n_cand > 0 else _ptr(out_idx))
     _check(lib().mla_indexer_topk(
         _crow(idx_row), _ptr(q_idx), _ptr(w), float(score_scale), _ptr(idx_cache), stride,
-        idx_cache.shape[1], _ptr(n_visible), None, 0, B, H_I, k, _ptr(out_idx), _ptr(out_scores),
+        idx_cache.shape[1], _ptr(n_visible), cand_p, n_cand, B, H_I, k, _ptr(out_idx), _ptr(out_scores),
         _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def mla_indexer_pool_workspace(B: int, capacity: int, block: int = 8) -> int:
+    return int(lib().mla_indexer_pool_workspace(B, capacity, block))
+
+
+def mla_indexer_pool(scores, n_visible, n_blocks: int, out_pos, workspace, block: int = 8, stream=None):
+    """Candidate pool of the hierarchical sparse indexer from one layer's scores fp32 [B, capacity]:
+    the positions int32 [B, n_blocks * block] of the n_blocks blocks (of `block` consecutive
+    positions) with the largest maximum visible score, -1 padded.  workspace: uint8 of
+    mla_indexer_pool_workspace bytes, under the zeroing contract of mla_indexer_topk's."""
+    _need(scores, "scores", torch.float32, 2)
+    _need(n_visible, "n_visible", torch.int32, 1)
+    _need(out_pos, "out_pos", torch.int32, 2)
+    _need(workspace, "workspace", torch.uint8)
+    B, cap = scores.shape
+    if tuple(n_visible.shape) != (B,) or tuple(out_pos.shape) != (B, n_blocks * block):
+        raise ValueError("n_visible [B] and out_pos [B, n_blocks * block] expected")
+    _check(lib().mla_indexer_pool(_ptr(scores), cap, _ptr(n_visible), B, block, n_blocks, _ptr(out_pos),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def mla_append_indexer_topk(main_row: Row, idx_row: Row, new_main, new_idx, slots, main_cache, idx_cache,

@@ -2,6 +2,7 @@
 // workspace carving, dispatch to the gfx950 launchers, error reporting.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -148,10 +149,12 @@ struct TopkCall {
 
 mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
                        const void* idx_cache, int64_t idx_seq_stride, int64_t capacity, const int32_t* n_visible,
-                       int32_t B, int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
-                       size_t workspace_bytes, TopkCall* out) {
+                       const int32_t* cand, int32_t n_cand, int32_t B, int32_t H_I, int32_t k, int32_t* out_idx,
+                       float* out_scores, void* workspace, size_t workspace_bytes, TopkCall* out) {
     if (B < 0 || k < 0 || H_I < 1 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "indexer_topk: need B >= 0, k >= 0, H_I >= 1, capacity >= 0");
+    if (n_cand < 0 || (!cand && n_cand != 0))
+        return fail(MLA_ERR_INVALID_ARG, "indexer_topk: a candidate pool needs cand != NULL and n_cand >= 0");
     if (!(score_scale > 0.0f)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: score_scale must be > 0");
     if (idx_row.rope_dim != 0) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: indexer rows have no RoPE part");
     if (B == 0 || k == 0) {
@@ -168,7 +171,9 @@ mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, flo
         return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: no kernel for fmt %d, dim %d, H_I %d", idx_row.fmt,
                     idx_row.dim, H_I);
     if (capacity > (int64_t)0x7FFFFFFF) return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: capacity over 2^31-1");
-    const TopkLayout L = topk_layout(B, capacity);
+    // with a pool the scores and the selection's lists have n_cand entries per sequence
+    const int64_t rows = cand ? std::max<int64_t>(capacity, n_cand) : capacity;
+    const TopkLayout L = topk_layout(B, rows);
     if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256))
         return fail(MLA_ERR_WORKSPACE, "indexer_topk: workspace needs %zu bytes, 256-byte aligned", L.total);
     if (out_scores && !aligned(out_scores, 4)) return fail(MLA_ERR_INVALID_ARG, "indexer_topk: misaligned out_scores");
@@ -197,6 +202,8 @@ mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, flo
     a.scores = T.scores;
     a.hist = T.hist;
     a.queues = reinterpret_cast<uint32_t*>(ws + L.queues);
+    a.cand = cand;
+    a.n_cand = cand ? n_cand : 0;
     out->out_idx = out_idx;
     return ok();
 }
@@ -205,7 +212,16 @@ mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, flo
 mla_status_t topk_launch(const TopkCall& c, const mla::AppendArgs* append, hipStream_t st) {
     hipError_t e = mla::launch_scan(c.scan, st, append);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
-    e = mla::launch_select(c.scan.scores, c.scan.capacity, c.scan.n_visible, c.scan.B, c.scan.k, c.ws, c.out_idx, st);
+    const mla::ScanArgs& a = c.scan;
+    if (a.cand) {       // the pool's n_cand entries, reported as their positions
+        mla::SelectMap map;
+        map.cand = a.cand;
+        map.n_visible = a.n_visible;
+        map.limit = a.capacity;
+        e = mla::launch_select(a.scores, a.n_cand, nullptr, a.B, a.k, c.ws, c.out_idx, st, map);
+    } else {
+        e = mla::launch_select(a.scores, a.capacity, a.n_visible, a.B, a.k, c.ws, c.out_idx, st);
+    }
     return hip_status(e, "top-k select");
 }
 
@@ -253,7 +269,7 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
     return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
 }
 
-int32_t mla_version(void) { return 101; }
+int32_t mla_version(void) { return 102; }
 
 mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
                                  const float* new_idx, const int32_t* slots, int32_t B, int32_t n_new,
@@ -279,10 +295,9 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
                               const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
                               int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
                               size_t workspace_bytes, void* stream) {
-    if (cand || n_cand) return fail(MLA_ERR_UNSUPPORTED, "indexer_topk: candidate pools are not supported");
     TopkCall c;
     const mla_status_t s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
-                                     B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
+                                     cand, n_cand, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
     if (s != MLA_OK || c.empty) return s;
     return topk_launch(c, nullptr, static_cast<hipStream_t>(stream));
 }
@@ -301,8 +316,8 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, cons
                                  main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W, Dw, &ap);
     if (s != MLA_OK) return s;
     TopkCall c;
-    s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, B, H_I, k,
-                  out_idx, out_scores, workspace, workspace_bytes, &c);
+    s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, nullptr, 0, B,
+                  H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
     if (s != MLA_OK) return s;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (c.empty) return hip_status(mla::launch_append(ap, st), "append launch");
@@ -312,6 +327,48 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, cons
         return topk_launch(c, nullptr, st);
     }
     return topk_launch(c, &ap, st);
+}
+
+size_t mla_indexer_pool_workspace(int32_t B, int64_t capacity, int32_t block) {
+    if (B < 0 || capacity < 0 || block < 1) return 0;
+    const int64_t nb = (capacity + block - 1) / block;
+    return topk_layout(B, nb).total + round256((size_t)B * sizeof(int32_t));
+}
+
+mla_status_t mla_indexer_pool(const float* scores, int64_t capacity, const int32_t* n_visible, int32_t B,
+                              int32_t block, int32_t n_blocks, int32_t* out_pos, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (B < 0 || capacity < 0 || n_blocks < 0)
+        return fail(MLA_ERR_INVALID_ARG, "indexer_pool: need B >= 0, capacity >= 0, n_blocks >= 0");
+    if (block < 1 || block > 64 || (block & (block - 1)) != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "indexer_pool: block must be a power of two <= 64");
+    if (capacity > (int64_t)0x7FFFFFFF || (int64_t)n_blocks * block > (int64_t)0x7FFFFFFF)
+        return fail(MLA_ERR_UNSUPPORTED, "indexer_pool: capacity and n_blocks * block must be below 2^31");
+    if (B == 0 || n_blocks == 0) return ok();
+    if (!scores || !n_visible || !out_pos) return fail(MLA_ERR_INVALID_ARG, "indexer_pool: a required pointer is NULL");
+    if (!aligned(scores, 4) || !aligned(out_pos, 4))
+        return fail(MLA_ERR_INVALID_ARG, "indexer_pool: misaligned scores or out_pos");
+    const int64_t nb = (capacity + block - 1) / block;
+    const TopkLayout L = topk_layout(B, nb);
+    const size_t need = mla_indexer_pool_workspace(B, capacity, block);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(MLA_ERR_WORKSPACE, "indexer_pool: workspace needs %zu bytes, 256-byte aligned", need);
+    char* ws = static_cast<char*>(workspace);
+    mla::TopkWorkspace T;
+    T.scores = reinterpret_cast<float*>(ws + L.scores);          // the block scores
+    T.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    T.counts = reinterpret_cast<uint32_t*>(ws + L.counts);
+    T.sel = reinterpret_cast<int32_t*>(ws + L.sel);
+    T.cand = reinterpret_cast<uint64_t*>(ws + L.cand);
+    T.cand2 = reinterpret_cast<uint64_t*>(ws + L.cand2);
+    int32_t* nvb = reinterpret_cast<int32_t*>(ws + L.total);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = mla::launch_block_max(scores, capacity, n_visible, B, block, T.scores, nvb, T.hist, st);
+    if (e != hipSuccess) return hip_status(e, "pool block maxima");
+    mla::SelectMap map;
+    map.expand = block;
+    e = mla::launch_select(T.scores, nb, nvb, B, n_blocks, T, out_pos, st, map);
+    return hip_status(e, "pool select");
 }
 
 size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H, int32_t k, int32_t W) {

@@ -1020,6 +1020,100 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
     flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
 }
 
+// MFMA scan of a candidate pool ([P4] "The Hierarchical Sparse
+// Indexer: bounded sweeps"; [P1] "DeepSeek-V4.1", "The hierarchical indexer": a Reindex layer scores only the positions a
+// Full layer published). Entry i of sequence b is the row at position
+// cand[b, i]; its score goes to scores[b, i] (-inf when the position is
+// negative or not visible) and every entry, -inf ones included, is counted in
+// the histogram, so that the selection can treat the pool as n_cand visible
+// entries. The pool is small (16384 rows of 72 B at V4.1's sizes), so the
+// kernel is built for latency: each lane loads the bytes of its own MFMA
+// operand straight from the row (rows of a pool are scattered, and only
+// 4-byte (E4M3), 8-byte (E2M1) or 16-byte (bf16) aligned), all of a wave's
+// loads are issued before the first contraction, and each workgroup takes
+// kCandTiles 16-entry tiles per wave. Lane (col, g) owns entry col of a tile
+// and channels g*32 .. g*32+31, as in the streaming scans.
+constexpr int kCandTiles = 2;
+template <int FMT, int MT>
+__global__ __launch_bounds__(kScanThreads) void k_scan_cand(ScanArgs a) {
+    __shared__ uint32_t hist[kHistBins];
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int64_t nvis = clamp_visible(a.n_visible[b], a.capacity);
+    const int64_t n = a.n_cand;
+    const int32_t* cand = a.cand + b * n;
+    const uint8_t* base = a.cache + b * a.stride;
+    float* scores = a.scores + b * n;
+    int64_t ent[kCandTiles];
+    bool valid[kCandTiles];
+    int32_t pos[kCandTiles];
+#pragma unroll
+    for (int t = 0; t < kCandTiles; ++t) {
+        ent[t] = ((int64_t)blockIdx.x * 4 * kCandTiles + t * 4 + wave) * 16 + col;
+        pos[t] = ent[t] < n ? cand[ent[t]] : -1;
+    }
+    // the row loads: E4M3 8 words of codes + the fp32 scale, E2M1 4 words of
+    // nibbles + the two scale bytes of the lane's channels, bf16 four 16-byte vectors
+    constexpr int NW = (FMT == MLA_FMT_E4M3_S128) ? 8 : (FMT == MLA_FMT_E2M1_S16 ? 4 : 16);
+    uint32_t w[kCandTiles][NW];
+    uint32_t sw[kCandTiles];
+#pragma unroll
+    for (int t = 0; t < kCandTiles; ++t) {
+        valid[t] = pos[t] >= 0 && pos[t] < nvis;
+        const uint8_t* row = base + (int64_t)(valid[t] ? pos[t] : 0) * a.row_bytes;
+        if constexpr (FMT == MLA_FMT_E4M3_S128) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(row + g * 32);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[t][i] = valid[t] ? p[i] : 0u;
+            sw[t] = valid[t] ? *reinterpret_cast<const uint32_t*>(row + 128) : 0u;
+        } else if constexpr (FMT == MLA_FMT_E2M1_S16) {
+            const u32x2* p = reinterpret_cast<const u32x2*>(row + g * 16);
+            const u32x2 lo = valid[t] ? p[0] : u32x2{0u, 0u}, hi = valid[t] ? p[1] : u32x2{0u, 0u};
+            w[t][0] = lo.x;
+            w[t][1] = lo.y;
+            w[t][2] = hi.x;
+            w[t][3] = hi.y;
+            sw[t] = valid[t] ? *reinterpret_cast<const uint16_t*>(row + 64 + 2 * g) : 0u;
+        } else {
+            const u32x4* p = reinterpret_cast<const u32x4*>(row + g * 64);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 x = valid[t] ? p[i] : u32x4{0u, 0u, 0u, 0u};
+                w[t][4 * i] = x.x;
+                w[t][4 * i + 1] = x.y;
+                w[t][4 * i + 2] = x.z;
+                w[t][4 * i + 3] = x.w;
+            }
+            sw[t] = 0u;
+        }
+    }
+    ScanCtx<MT> C;
+    load_ctx<MT>(C, a, b, col, g);
+    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kCandTiles; ++t) {
+        u32x4 kb[4];
+        float mult = valid[t] ? 1.0f : 0.0f;
+        if constexpr (FMT == MLA_FMT_BF16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kb[i] = u32x4{w[t][4 * i], w[t][4 * i + 1], w[t][4 * i + 2], w[t][4 * i + 3]};
+        } else {
+            dequant_key<FMT>(w[t], sw[t], kb);
+            if constexpr (FMT == MLA_FMT_E4M3_S128) mult = valid[t] ? __builtin_bit_cast(float, sw[t]) : 0.0f;
+        }
+        const float part = tile_dot<MT>(C, kb, mult);
+        if (g == 0 && ent[t] < n) {
+            const float sc = valid[t] ? part : -__builtin_inff();
+            scores[ent[t]] = sc;
+            atomicAdd(&hist[score_key(sc) >> (32 - kHistBits)], 1u);
+        }
+    }
+    __syncthreads();
+    flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
+}
+
 // ------------------------------------------------------------------------
 // Generic scan (any row format, any d_I, H_I * d_I <= 8192): one row per
 // thread, fp32 FMA on the vector ALUs.  Used for shapes outside the MFMA
@@ -1055,21 +1149,25 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_generic(ScanArgs a) {
     }
     for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
     __syncthreads();
+    // entry s: row s, or with a candidate pool the row at position cand[b, s]
+    // (every pool entry is counted in the histogram, -inf ones included)
+    const int64_t n_out = a.cand ? a.n_cand : a.capacity;
     const int64_t s = (int64_t)blockIdx.x * kScanThreads + threadIdx.x;
     const int64_t nvis = clamp_visible(a.n_visible[b], a.capacity);
-    if (s < a.capacity) {
+    if (s < n_out) {
+        const int64_t pos = a.cand ? (int64_t)a.cand[b * n_out + s] : s;
         float score = -__builtin_inff();
-        if (s < nvis) {
-            const uint8_t* row = a.cache + b * a.stride + s * a.row_bytes;
+        if (pos >= 0 && pos < nvis) {
+            const uint8_t* row = a.cache + b * a.stride + pos * a.row_bytes;
             score = 0.0f;
             for (int j = 0; j < a.H_I; ++j) {
                 float d = 0.0f;
                 for (int c = 0; c < a.dim; ++c) d += qs[j * a.dim + c] * key_elem(a.fmt, a.dim, row, c);
                 score += a.w[(int64_t)b * a.H_I + j] * fmaxf(a.sigma * d, 0.0f);
             }
-            atomicAdd(&hist[score_key(score) >> (32 - kHistBits)], 1u);
         }
-        a.scores[b * a.capacity + s] = score;
+        if (a.cand || pos < nvis) atomicAdd(&hist[score_key(score) >> (32 - kHistBits)], 1u);
+        a.scores[b * n_out + s] = score;
     }
     __syncthreads();
     flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
@@ -1097,9 +1195,30 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         }
         return hipSuccess;
     };
-    if (a.B == 0 || a.capacity == 0) return unfused();
     const bool mfma = (a.fmt == MLA_FMT_BF16 || a.fmt == MLA_FMT_E4M3_S128 || a.fmt == MLA_FMT_E2M1_S16) &&
                       a.dim == 128 && a.H_I % 16 == 0 && a.H_I <= 64;
+    if (a.cand) {                                              // a candidate pool: n_cand entries per sequence
+        if (const hipError_t e = unfused(); e != hipSuccess) return e;
+        if (a.B == 0 || a.n_cand == 0) return hipSuccess;
+        const ProfSlot p = prof_slot(PROF_SCAN);
+        if (mfma) {
+            const dim3 grid((unsigned)((a.n_cand + 64 * kCandTiles - 1) / (64 * kCandTiles)), a.B);
+#define MLA_CAND_CASE(F, M)                                                                    \
+    if (a.fmt == F && a.H_I == 16 * M)                                                         \
+        return launch_kernel(k_scan_cand<F, M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a);
+            MLA_CAND_CASE(MLA_FMT_BF16, 1) MLA_CAND_CASE(MLA_FMT_BF16, 2)
+            MLA_CAND_CASE(MLA_FMT_BF16, 3) MLA_CAND_CASE(MLA_FMT_BF16, 4)
+            MLA_CAND_CASE(MLA_FMT_E4M3_S128, 1) MLA_CAND_CASE(MLA_FMT_E4M3_S128, 2)
+            MLA_CAND_CASE(MLA_FMT_E4M3_S128, 3) MLA_CAND_CASE(MLA_FMT_E4M3_S128, 4)
+            MLA_CAND_CASE(MLA_FMT_E2M1_S16, 1) MLA_CAND_CASE(MLA_FMT_E2M1_S16, 2)
+            MLA_CAND_CASE(MLA_FMT_E2M1_S16, 3) MLA_CAND_CASE(MLA_FMT_E2M1_S16, 4)
+#undef MLA_CAND_CASE
+            return hipErrorInvalidValue;
+        }
+        const dim3 grid((unsigned)((a.n_cand + kScanThreads - 1) / kScanThreads), a.B);
+        return launch_kernel(k_scan_generic, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a);
+    }
+    if (a.B == 0 || a.capacity == 0) return unfused();
     if (mfma) {
         const dim3 grid((unsigned)((a.capacity + kRowsPerBlock - 1) / kRowsPerBlock), a.B);
         // staged scan: ~kStagedBlocks long-lived workgroups, each wave streaming many chunks

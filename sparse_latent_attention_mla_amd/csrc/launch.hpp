@@ -71,6 +71,9 @@ struct ScanArgs {
     float* scores;          // [B, capacity]
     uint32_t* hist;         // [B, kHistWordsHost] (see TopkWorkspace)
     uint32_t* queues;       // [kScanQueuesHost, kQueueWordsHost] work queues, zero on entry and on exit
+    const int32_t* cand;    // [B, n_cand] positions of a candidate pool, or null: every row
+    int64_t n_cand;         // pool entries per sequence; with a pool the scores are [B, n_cand] and
+                            // the histogram counts every entry (those not visible as -inf)
 };
 // Entries of a step's append that the indexer scan can carry in the same launch.
 constexpr int kFuseMaxNew = 4;
@@ -79,8 +82,28 @@ constexpr int kFuseMaxNew = 4;
 // kernel can carry it, else as its own launch before it.
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* append = nullptr);
 bool scan_supported(int fmt, int dim, int H_I);
+// How the selection reports entry s of a sequence's scores: as s, or, with a
+// candidate pool, as its position cand[b, s] (-1 when that is negative or not
+// below min(n_visible[b], limit)); a reported value v is written as `expand`
+// outputs v * expand + j (j < expand; -1 as -1s), so that a selection of blocks
+// reports their positions.
+struct SelectMap {
+    const int32_t* cand = nullptr;      // [B, capacity]
+    const int32_t* n_visible = nullptr;
+    int64_t limit = 0;
+    int expand = 1;
+};
+// The k largest of scores[b, 0 .. n_visible[b]) (every one of the capacity
+// entries when n_visible is null) into out_idx [B, k * map.expand].
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
-                         const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream);
+                         const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream,
+                         const SelectMap& map = SelectMap{});
+// Block maxima of a layer's scores ([B, capacity]): bmax[b, i] = the largest
+// score among the visible positions block*i .. block*i + block - 1, the
+// histogram of their keys into hist (as the scan builds it), and nvb[b] = the
+// number of blocks holding a visible position.
+hipError_t launch_block_max(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int block,
+                            float* bmax, int32_t* nvb, uint32_t* hist, hipStream_t stream);
 
 struct DecodeArgs {
     int fmt, dim, rope, d_v;

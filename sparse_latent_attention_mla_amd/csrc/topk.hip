@@ -26,6 +26,11 @@
 // no hand-over between workgroups. (Longer sequences outgrow one CU's vector
 // throughput: classifying 128K scores alone takes it several microseconds.)
 // Output positions form an unordered set.
+// The same kernels select over a candidate pool (the entries of a Reindex
+// layer's pool: each selected entry is reported as its position, entries that
+// name no visible position as -1, ties going to the smaller position) and over
+// block scores (the pool of the hierarchical indexer: each selected block is
+// written as its positions); see SelectMap.
 #include <cstdlib>
 
 #include "common.hpp"
@@ -164,6 +169,41 @@ __device__ __forceinline__ DigitResult hist_find(uint32_t* hb, uint32_t need) {
     return r;
 }
 
+// One sequence's output row: reported value v goes to slot o as v itself, or,
+// expanding blocks of `expand` positions, as v * expand + j in slots
+// o * expand + j (-1 as -1s).
+struct OutRow {
+    int32_t* out;
+    int expand;
+    __device__ __forceinline__ void put(uint32_t o, int32_t v) const {
+        if (expand == 1) {
+            out[o] = v;
+            return;
+        }
+        for (int j = 0; j < expand; ++j) out[(int64_t)o * expand + j] = v < 0 ? -1 : v * expand + j;
+    }
+};
+__device__ __forceinline__ OutRow out_row(int32_t* out_idx, int b, int k, const SelectMap& m) {
+    return OutRow{out_idx + (int64_t)b * k * m.expand, m.expand};
+}
+
+// Sequence b's view of a SelectMap: the position entry s reports, given the
+// pool entry cv = cand[b, s] (loaded with the score; unused without a pool).
+struct PosMap {
+    bool pool;
+    int64_t lim;
+    __device__ __forceinline__ int32_t operator()(int64_t s, int32_t cv) const {
+        if (!pool) return (int32_t)s;
+        return (cv >= 0 && cv < lim) ? cv : -1;
+    }
+};
+__device__ __forceinline__ PosMap pos_map(const SelectMap& m, int b) {
+    return m.cand ? PosMap{true, clamp_visible(m.n_visible[b], m.limit)} : PosMap{false, 0};
+}
+__device__ __forceinline__ int64_t visible_of(const int32_t* n_visible, int b, int64_t capacity) {
+    return n_visible ? clamp_visible(n_visible[b], capacity) : capacity;
+}
+
 // Among the candidates c[0 .. ncand) (64-bit key << 32 | ~position, all in one
 // top-12-bit bin), append the positions of the `need` largest to out from the LDS
 // cursor on (entries at or past `want` are not written). Two 10-bit digits fix the
@@ -171,7 +211,7 @@ __device__ __forceinline__ DigitResult hist_find(uint32_t* hb, uint32_t need) {
 // needed do four 8-bit digits of the inverted position follow. h: two LDS
 // histograms of kMaxDigitBins, the first zero on entry; res: 4 LDS words.
 template <int NT, typename P>
-__device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, int32_t* __restrict__ out,
+__device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, OutRow out,
                            uint32_t* cursor, uint32_t (*h)[kMaxDigitBins], uint32_t* res) {
     const int t = threadIdx.x, lane = t & 63;
     const bool radix = need > 0 && need < ncand;
@@ -233,7 +273,7 @@ __device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, in
             base = __shfl(base, 0, 64);
             if (take) {
                 const uint32_t o = base + lanes_below(m);
-                if (o < want) out[o] = pos;
+                if (o < want) out.put(o, pos);
             }
         }
     }
@@ -248,7 +288,7 @@ struct FinalLds {
 // Radix-take over the candidates in LDS (the common case) or in the global list.
 template <int NT>
 __device__ __forceinline__ void radix_take_any(FinalLds& L, const uint64_t* gc2, uint32_t ncand, uint32_t need,
-                                               uint32_t want, int32_t* __restrict__ out, uint32_t* cursor) {
+                                               uint32_t want, OutRow out, uint32_t* cursor) {
     if (ncand <= (uint32_t)kFinalLds) radix_take<NT>(L.lc, ncand, need, want, out, cursor, L.h, L.res);
     else radix_take<NT>(gc2, ncand, need, want, out, cursor, L.h, L.res);
 }
@@ -268,7 +308,8 @@ __device__ __forceinline__ void classify(float v, bool in, int T, uint32_t* key,
 // ---- one workgroup per sequence ------------------------------------------
 __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ scores, int64_t capacity,
                                                           const int32_t* __restrict__ n_visible, int k,
-                                                          TopkWorkspace ws, int32_t* __restrict__ out_idx) {
+                                                          TopkWorkspace ws, int32_t* __restrict__ out_idx,
+                                                          SelectMap map) {
     __shared__ FinalLds L;
     __shared__ uint32_t n_sel, n_cnd, cursor;
     __shared__ int T_s;
@@ -276,20 +317,24 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     constexpr int kRound = kRowThreads * kR;
     const int b = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63;
-    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const int64_t nvis = visible_of(n_visible, b, capacity);
     const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    int32_t* out = out_idx + (int64_t)b * k;
+    const OutRow out = out_row(out_idx, b, k, map);
+    const PosMap pmap = pos_map(map, b);
+    const int32_t* __restrict__ cb = map.cand ? map.cand + b * capacity : nullptr;
     uint64_t* gc2 = ws.cand2 + b * capacity;
     const float* __restrict__ sc = scores + b * capacity;
     float v[kR];
-    auto load = [&](int64_t r0, float* d) {
+    int32_t cv[kR];                                      // pool entries (with a pool)
+    auto load = [&](int64_t r0, float* d, int32_t* e) {
 #pragma unroll
         for (int u = 0; u < kR; ++u) {
             const int64_t s = r0 + u * kRowThreads + t;
             d[u] = (s < nvis) ? sc[s] : 0.0f;
+            e[u] = (cb && s < nvis) ? cb[s] : 0;
         }
     };
-    load(0, v);                                          // in flight during the threshold search
+    load(0, v, cv);                                      // in flight during the threshold search
     if (t < 64) {
         const DigitResult r = hist_find(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);
         if (t == 0) {
@@ -303,7 +348,8 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     const int T = T_s;
     for (int64_t r0 = 0; r0 < nvis; r0 += kRound) {
         float vn[kR];
-        if (r0 + kRound < nvis) load(r0 + kRound, vn);
+        int32_t cn[kR];
+        if (r0 + kRound < nvis) load(r0 + kRound, vn, cn);
         // classify the round, then one LDS reservation per wave and list
         uint32_t key[kR];
         uint64_t mt[kR], mc[kR];
@@ -331,20 +377,23 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
                 const int64_t s = r0 + u * kRowThreads + t;
                 if ((mt[u] >> lane) & 1u) {
                     const uint32_t o = bt + lanes_below(mt[u]);
-                    if (o < (uint32_t)k) out[o] = (int32_t)s;
+                    if (o < (uint32_t)k) out.put(o, pmap(s, cv[u]));
                 }
                 if ((mc[u] >> lane) & 1u) {
                     const uint32_t o = bc + lanes_below(mc[u]);
-                    const uint64_t cv = ((uint64_t)key[u] << 32) | (uint64_t)(~(uint32_t)s);
-                    if (o < (uint32_t)kFinalLds) L.lc[o] = cv;
-                    else gc2[o] = cv;                    // o < capacity: one entry per row
+                    const uint64_t c = ((uint64_t)key[u] << 32) | (uint64_t)(~(uint32_t)pmap(s, cv[u]));
+                    if (o < (uint32_t)kFinalLds) L.lc[o] = c;
+                    else gc2[o] = c;                     // o < capacity: one entry per row
                 }
                 bt += (uint32_t)__popcll(mt[u]);
                 bc += (uint32_t)__popcll(mc[u]);
             }
         }
 #pragma unroll
-        for (int u = 0; u < kR; ++u) v[u] = vn[u];
+        for (int u = 0; u < kR; ++u) {
+            v[u] = vn[u];
+            cv[u] = cn[u];
+        }
     }
     __syncthreads();
     const uint32_t nsel = n_sel, ncand = n_cnd;
@@ -357,13 +406,13 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     zero_hist(ws.hist + (int64_t)b * kHistWordsHost);     // read above; the stores drain during the radix
     radix_take_any<kRowThreads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
-    for (uint32_t i = want + t; i < (uint32_t)k; i += kRowThreads) out[i] = -1;
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kRowThreads) out.put(i, -1);
 }
 
 // ---- many workgroups per sequence ------------------------------------------
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores, int64_t capacity,
                                                         const int32_t* __restrict__ n_visible, int k,
-                                                        TopkWorkspace ws) {
+                                                        TopkWorkspace ws, SelectMap map) {
     __shared__ uint64_t cnd[kSelRows];
     __shared__ int32_t sel[kSelRows];
     __shared__ uint32_t n_sel, n_cnd;
@@ -372,14 +421,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     const int t = threadIdx.x, lane = t & 63;
     constexpr int kPer = kSelRows / kSelThreads;
     // the slice's scores are loaded before the threshold search, so both latencies overlap
-    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const int64_t nvis = visible_of(n_visible, b, capacity);
     const int64_t r0 = (int64_t)blockIdx.x * kSelRows;
     const float* sc = scores + b * capacity;
+    const PosMap pmap = pos_map(map, b);
+    const int32_t* __restrict__ cb = map.cand ? map.cand + b * capacity : nullptr;
     float v[kPer];
+    int32_t cv[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int64_t s = r0 + i * kSelThreads + t;
         v[i] = (s < nvis) ? sc[s] : 0.0f;
+        cv[i] = (cb && s < nvis) ? cb[s] : 0;
     }
     if (t < 64) {
         const DigitResult r = hist_find(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);
@@ -428,8 +481,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int64_t s = r0 + i * kSelThreads + t;
-            if ((mt[i] >> lane) & 1u) sel[bt + lanes_below(mt[i])] = (int32_t)s;
-            if ((mc[i] >> lane) & 1u) cnd[bc + lanes_below(mc[i])] = ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)s);
+            if ((mt[i] >> lane) & 1u) sel[bt + lanes_below(mt[i])] = pmap(s, cv[i]);
+            if ((mc[i] >> lane) & 1u)
+                cnd[bc + lanes_below(mc[i])] = ((uint64_t)key[i] << 32) | (uint64_t)(~(uint32_t)pmap(s, cv[i]));
             bt += (uint32_t)__popcll(mt[i]);
             bc += (uint32_t)__popcll(mc[i]);
         }
@@ -469,15 +523,15 @@ __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* total) {
 // one list, radix-select among the candidates, pad with -1.
 __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __restrict__ n_visible, int k,
                                                               int64_t capacity, int groups, TopkWorkspace ws,
-                                                              int32_t* __restrict__ out_idx) {
+                                                              int32_t* __restrict__ out_idx, SelectMap map) {
     __shared__ FinalLds L;
     __shared__ uint32_t cursor;
     __shared__ uint32_t ex_s[kSelThreads], ex_c[kSelThreads], cnt_s[kSelThreads], cnt_c[kSelThreads];
     const int b = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63;
-    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const int64_t nvis = visible_of(n_visible, b, capacity);
     const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    int32_t* out = out_idx + (int64_t)b * k;
+    const OutRow out = out_row(out_idx, b, k, map);
     uint64_t* gc2 = ws.cand2 + b * capacity;
 
     uint32_t nsel = 0, ncand = 0;
@@ -534,7 +588,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
                 if (j >= nbatch) break;
                 if ((uint32_t)lane < cnt_s[j]) {
                     const uint32_t o = nsel + ex_s[j] + lane;
-                    if (o < (uint32_t)k) out[o] = vs[u];
+                    if (o < (uint32_t)k) out.put(o, vs[u]);
                 }
                 if ((uint32_t)lane < cnt_c[j]) {
                     const uint32_t o = ncand + ex_c[j] + lane;
@@ -557,7 +611,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const uint32_t i = i0 + 64 * u + lane, o = nsel + ex_s[j] + i;
-                    if (i < ns && o < (uint32_t)k) out[o] = vv[u];
+                    if (i < ns && o < (uint32_t)k) out.put(o, vv[u]);
                 }
             }
             for (uint32_t i0 = 64; i0 < nc; i0 += 64 * 8) {
@@ -591,7 +645,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
                    threadIdx.x < 64 ? coarse_sum_of_lane(ws.hist + (int64_t)b * kHistWordsHost) : 0u);   // the stores drain during the radix
     radix_take_any<kSelThreads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
-    for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out[i] = -1;
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out.put(i, -1);
 }
 
 // The same for up to kF2MaxGroups select workgroups, with 1024 threads: the
@@ -604,16 +658,16 @@ constexpr int kF2MaxGroups = 1024;
 constexpr int kF2Spec = 4;                // workgroups per wave whose first 64 entries load early
 __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __restrict__ n_visible, int k,
                                                               int64_t capacity, int groups, TopkWorkspace ws,
-                                                              int32_t* __restrict__ out_idx) {
+                                                              int32_t* __restrict__ out_idx, SelectMap map) {
     __shared__ FinalLds L;
     __shared__ uint32_t cursor;
     __shared__ uint32_t g_cnt[kF2MaxGroups][2], g_off[kF2MaxGroups][2];
     __shared__ uint32_t wtot[kF2Waves][2];
     const int b = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const int64_t nvis = clamp_visible(n_visible[b], capacity);
+    const int64_t nvis = visible_of(n_visible, b, capacity);
     const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    int32_t* out = out_idx + (int64_t)b * k;
+    const OutRow out = out_row(out_idx, b, k, map);
     uint64_t* gc2 = ws.cand2 + b * capacity;
     const int32_t* __restrict__ gsel = ws.sel + b * capacity;
     const uint64_t* __restrict__ gcnd = ws.cand + b * capacity;
@@ -668,7 +722,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     // the candidate list (LDS, then cand2 past kFinalLds)
     auto place_sel = [&](int j, uint32_t i, int32_t v) {
         const uint32_t o = g_off[j][0] + i;
-        if (o < (uint32_t)k) out[o] = v;
+        if (o < (uint32_t)k) out.put(o, v);
     };
     auto place_cnd = [&](int j, uint32_t i, uint64_t v) {
         const uint32_t o = g_off[j][1] + i;
@@ -702,32 +756,32 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k, csum);   // the stores drain during the radix
     radix_take_any<kF2Threads>(L, gc2, ncand, need, want, out, &cursor);
     __syncthreads();
-    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out[i] = -1;
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);
 }
 
 }  // namespace
 
 // MLA_TOPK_PATH=row|multi forces a path, MLA_TOPK_FINAL1 the 256-thread final (for tuning).
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
-                         const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream) {
+                         const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream, const SelectMap& map) {
     if (B == 0 || k == 0) return hipSuccess;
     bool row = capacity <= kRowPathMax;
     if (const char* e = getenv("MLA_TOPK_PATH")) row = (e[0] == 'r');
     const ProfSlot p = prof_slot(PROF_SELECT);      // spans both kernels of the two-kernel path
     if (row)
         return launch_kernel(k_topk_row, dim3(B), dim3(kRowThreads), 0, stream, p.start, p.stop, scores, capacity,
-                             n_visible, k, ws, out_idx);
+                             n_visible, k, ws, out_idx, map);
     const unsigned nx = (unsigned)((capacity + kSelRows - 1) / kSelRows);
     if (nx > 0) {
         const hipError_t e = launch_kernel(k_select, dim3(nx, B), dim3(kSelThreads), 0, stream, p.start, nullptr,
-                                           scores, capacity, n_visible, k, ws);
+                                           scores, capacity, n_visible, k, ws, map);
         if (e != hipSuccess) return e;
     }
     if (nx <= (unsigned)kF2MaxGroups && !getenv("MLA_TOPK_FINAL1"))
         return launch_kernel(k_select_final2, dim3(B), dim3(kF2Threads), 0, stream, nx > 0 ? nullptr : p.start,
-                             p.stop, n_visible, k, capacity, (int)nx, ws, out_idx);
+                             p.stop, n_visible, k, capacity, (int)nx, ws, out_idx, map);
     return launch_kernel(k_select_final, dim3(B), dim3(kSelThreads), 0, stream, nx > 0 ? nullptr : p.start, p.stop,
-                         n_visible, k, capacity, (int)nx, ws, out_idx);
+                         n_visible, k, capacity, (int)nx, ws, out_idx, map);
 }
 
 }  // namespace mla

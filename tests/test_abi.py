@@ -27,7 +27,8 @@ def M():
 
 def test_header_declares_the_three_path_calls():
     names = declared_functions()
-    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode", "mla_append_indexer_topk"):
+    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode", "mla_append_indexer_topk",
+              "mla_indexer_pool"):
         assert n in names
 
 
@@ -72,9 +73,27 @@ def test_host_validation_rejects_before_launch(M):
     # topk: score scale must be positive
     assert L.mla_indexer_topk(r_idx, fake, fake, 0.0, fake, 1408, 10, fake, None, 0, 1, 64, 8,
                               fake, None, fake, 1 << 20, None) == 1
-    # topk: candidate pools are not supported yet
-    assert L.mla_indexer_topk(r_idx, fake, fake, 0.1, fake, 1408, 10, fake, fake, 5, 1, 64, 8,
-                              fake, None, fake, 1 << 20, None) == 2
+    # topk: a pool size without a pool, and a negative pool size
+    assert L.mla_indexer_topk(r_idx, fake, fake, 0.1, fake, 1408, 10, fake, None, 5, 1, 64, 8,
+                              fake, None, fake, 1 << 20, None) == 1
+    assert L.mla_indexer_topk(r_idx, fake, fake, 0.1, fake, 1408, 10, fake, fake, -1, 1, 64, 8,
+                              fake, None, fake, 1 << 20, None) == 1
+    # topk: a pool larger than the capacity sizes the workspace
+    need = L.mla_indexer_topk_workspace(1, 100000, 8)
+    assert need > L.mla_indexer_topk_workspace(1, 10, 8)
+    assert L.mla_indexer_topk(r_idx, C.c_void_p(0x10000), fake, 0.1, C.c_void_p(0x10000), 1408, 10, fake,
+                              fake, 100000, 1, 64, 8, fake, None, C.c_void_p(0x100000), need - 256, None) == 3
+    # pool: block not a power of two, or over 64
+    assert L.mla_indexer_pool(fake, 1000, fake, 1, 3, 16, fake, fake, 1 << 24, None) == 2
+    assert L.mla_indexer_pool(fake, 1000, fake, 1, 128, 16, fake, fake, 1 << 24, None) == 2
+    # pool: negative sizes, missing pointers, workspace too small
+    assert L.mla_indexer_pool(fake, 1000, fake, 1, 8, -1, fake, fake, 1 << 24, None) == 1
+    assert L.mla_indexer_pool(fake, -5, fake, 1, 8, 16, fake, fake, 1 << 24, None) == 1
+    assert L.mla_indexer_pool(None, 1000, fake, 1, 8, 16, fake, fake, 1 << 24, None) == 1
+    assert L.mla_indexer_pool(fake, 1000, fake, 1, 8, 16, fake, C.c_void_p(0x100000), 64, None) == 3
+    # pool: nothing to select is a successful no-op (no launch)
+    assert L.mla_indexer_pool(None, 1000, None, 1, 8, 0, None, None, 0, None) == 0
+    assert L.mla_indexer_pool(None, 1000, None, 0, 8, 16, None, None, 0, None) == 0
     # topk: workspace too small
     assert L.mla_indexer_topk(r_idx, fake, fake, 0.1, C.c_void_p(0x10000), 1408, 10, fake, None, 0, 1, 64, 8,
                               fake, None, C.c_void_p(0x100000), 16, None) == 3
@@ -110,6 +129,9 @@ def test_host_validation_rejects_before_launch(M):
 
 def test_workspace_queries(M):
     assert M.mla_indexer_topk_workspace(4, 131072, 2048) >= 4 * 131072 * (4 + 8)
+    # the pool's selection runs over capacity / block block scores
+    assert M.mla_indexer_pool_workspace(1, 524288, 8) >= M.mla_indexer_topk_workspace(1, 65536, 2048)
+    assert M.mla_indexer_pool_workspace(1, 524288, 8) < M.mla_indexer_topk_workspace(1, 524288, 2048)
     r = M.Row(M.E4M3_S128, 512, 64)
     assert M.mla_sparse_decode_workspace(r, 512, 4, 128, 2048, 0) >= 4 * 128 * 512 * 4
     assert M.mla_sparse_decode_workspace(M.Row(M.F32, 64, 16), 64, 1, 16, 32, 0) == 0   # generic path

@@ -38,7 +38,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--layers", type=int, default=8, help="distinct layer caches rotated")
+    p.add_argument("--pool", type=int, default=0,
+                   help="CSA2 group: the Full layer publishes a candidate pool of this many 8-position "
+                        "blocks and the Reindex layer scores only the pool (hierarchical sparse indexer)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each rotated layer's step from a HIP graph captured once (the stamped steps "
+                        "still run eagerly); default: every step's kernels are launched from the host")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="time only torch's device copy of a known size (scales HBM byte counters)")
     return p.parse_args()
@@ -220,16 +226,25 @@ def main():
     idx_out = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
     out = torch.empty((B, H, cfg.d_v), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    ws_topk = torch.zeros(M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device=dev)
+    pool = args.pool if WL.n_indexers(cfg) > 1 else 0
+    POOL_BLOCK = 8
+    ws_size = M.mla_indexer_topk_workspace(B, N, k)
+    if pool:
+        ws_size = max(ws_size, M.mla_indexer_pool_workspace(B, N, POOL_BLOCK))
+        full_scores = torch.empty((B, N), dtype=torch.float32, device=dev)
+        pool_pos = torch.empty((B, pool * POOL_BLOCK), dtype=torch.int32, device=dev)
+    ws_topk = torch.zeros(ws_size, dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(max(1, M.mla_sparse_decode_workspace(mr, cfg.d_v, B, H, k, cfg.W)), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(X):
+    def step(X, stamp=False):
         """One layer-step (or CSA2 group) on layer caches X: the first layer appends the
         step's entry (main row, indexer key) and every layer its window entry; Full and
         Reindex layers select, every layer attends. The first layer's append rides
-        with its indexer scan (mla_append_indexer_topk)."""
+        with its indexer scan (mla_append_indexer_topk). With a pool, the Full layer
+        also publishes the candidate pool and the Reindex layer scores only the pool.
+        stamp: time the first layer's scan (the full scan carrying the append)."""
         j = 0
         latest = None
         for l, mode in enumerate(cfg.layers):
@@ -238,9 +253,16 @@ def main():
             selects = mode in ("full", "reindex")
             if first and selects:
                 latest = idx_out[j % 2]
+                if stamp:
+                    M.mla_profile_enable(("indexer_scan",))
                 M.mla_append_indexer_topk(mr, ir, X.new_main, X.new_idx, slots, X.main, X.idx, X.q_idx[j],
                                           X.w[j], cfg.sigma, nvis, k, latest, ws_topk,
-                                          new_win=win[0], win_pos=win[1], win_ring=win[2])
+                                          new_win=win[0], win_pos=win[1], win_ring=win[2],
+                                          out_scores=full_scores if pool else None)
+                if stamp:
+                    M.mla_profile_enable(())
+                if pool:
+                    M.mla_indexer_pool(full_scores, nvis, pool, pool_pos, ws_topk, block=POOL_BLOCK)
                 j += 1
             else:
                 M.mla_kv_append_quant(mr, ir, X.new_main if first else None, X.new_idx if first else None,
@@ -248,7 +270,8 @@ def main():
                                       X.idx if first else None, *win)
                 if selects:
                     latest = idx_out[j % 2]
-                    M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk)
+                    M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk,
+                                       cand=pool_pos if pool else None)
                     j += 1
             M.mla_sparse_decode(mr, cfg.d_v, X.q[l], X.main, latest, cfg.softmax_scale, out, lse, ws_dec,
                                 X.win[l] if cfg.W else None, win_len if cfg.W else None)
@@ -257,6 +280,40 @@ def main():
     for i in range(args.warmup):
         step(layers[i % n_layers])
     torch.cuda.synchronize()
+
+    # one HIP graph per rotated layer cache, captured from the same calls (the
+    # library only enqueues kernels: no allocation, no memset, no host sync)
+    graphs = None
+    if args.graph:
+        graphs = []
+        for l in range(n_layers):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(layers[l])
+            graphs.append(g)
+        torch.cuda.synchronize()
+        # replays must reproduce the eager step, also with eager work between them
+        for rep_i in range(2):
+            step(layers[1 % n_layers])
+            torch.cuda.synchronize()
+            ref = (out.clone(), lse.clone(), [x.clone() for x in idx_out])
+            step(layers[0])
+            graphs[1 % n_layers].replay()
+            torch.cuda.synchronize()
+            same_idx = all(torch.equal(torch.sort(a, dim=1)[0], torch.sort(b, dim=1)[0])
+                           for a, b in zip(idx_out, ref[2]))
+            # (the order of the selected positions may differ, and with it the
+            # decode's summation order: outputs agree to rounding)
+            close = lambda a, r: float((a - r).abs().max()) <= 1e-4 * float(r.abs().max())
+            if not (same_idx and close(out, ref[0]) and close(lse, ref[1])):
+                raise RuntimeError("graph replay differs from the eager step")
+        log(f"captured {n_layers} step graphs; replays match the eager step")
+
+    def run_step(i, stamp=False):
+        if graphs is None or stamp:
+            step(layers[i % n_layers], stamp=stamp)
+        else:
+            graphs[i % n_layers].replay()
 
     # timed region: exactly K steps.  On every SAMPLE_EVERY-th step the library
     # stamps a pair of events from the scan kernel's own dispatch on the launch
@@ -271,18 +328,25 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        stamped = i % SAMPLE_EVERY == 0
-        if stamped:
-            M.mla_profile_enable(("indexer_scan",))
-        step(layers[i % n_layers])
-        if stamped:
-            M.mla_profile_enable(())
+        run_step(i, stamp=i % SAMPLE_EVERY == 0)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     n_scan, scan_ms = M.mla_profile_read("indexer_scan")
     scan_us = scan_ms * 1e3 / n_scan
+
+    # the same K steps all launched from the host, for comparison (not the result)
+    eager_ms = None
+    if graphs is not None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(layers[i % n_layers])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / args.steps
 
     # per-kernel breakdown: a separate, untimed pass with every kernel stamped
     # (stamped launches cost host time, so this pass is not the step time)
@@ -297,13 +361,14 @@ def main():
         n, ms = M.mla_profile_read(name)
         if n:
             per_kernel[name] = {"launches": n, "avg_us": ms * 1e3 / n}
-    log(f"{ms_per_step * 1e3:.2f} us/step; scan {scan_us:.2f} us live ({n_scan} stamped launches); "
+    log(f"{ms_per_step * 1e3:.2f} us/step" + (f" (eager {eager_ms * 1e3:.2f})" if eager_ms else "") +
+        f"; scan {scan_us:.2f} us live ({n_scan} stamped launches); "
         "breakdown pass (avg us): " +
         ", ".join(f"{k}={v['avg_us']:.2f}" for k, v in per_kernel.items()))
 
-    ab = WL.algorithmic_bytes(cfg)
+    ab = WL.algorithmic_bytes(cfg, pool)
     step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
-    # dominant kernel: the indexer scan, which also carries the first layer's
+    # dominant kernel: the first layer's indexer scan, which also carries its
     # quantise-append.  Per launch it must read every visible indexer row of the
     # batch plus the indexer queries and head weights, and read the new entries
     # and write their rows (the step's one entry per sequence: fp32 inputs in,
@@ -312,7 +377,7 @@ def main():
     # not counted.
     n_idx_layers = WL.n_indexers(cfg)
     carried = B * (M.row_bytes(mr) + M.row_bytes(ir) + 4 * (cfg.D + cfg.d_I)) + (B * cfg.D * 6 if cfg.W else 0)
-    scan_bytes = (ab["scan"] + ab["q_idx_w"]) // n_idx_layers + carried
+    scan_bytes = B * N * M.row_bytes(ir) + ab["q_idx_w"] // n_idx_layers + carried
     scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
     result = {
         "metric": METRIC,
@@ -322,6 +387,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "launch": "eager" if graphs is None else "HIP graph per layer cache (every 25th step eager, scan-stamped)",
+        "ms_per_step_eager": eager_ms if graphs is not None else ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -333,6 +400,8 @@ def main():
             "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "window": cfg.W, "layers_per_step": len(cfg.layers),
             "main_row_bytes": M.row_bytes(mr), "indexer_row_bytes": M.row_bytes(ir),
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
+            "candidate_pool": (f"{pool} blocks of {POOL_BLOCK} published by the Full layer, scored by the "
+                               "Reindex layer") if pool else None,
         },
         "roofline": {
             "kernel": "indexer scan carrying the step's append (k_scan_dma32)",

@@ -136,6 +136,15 @@ __device__ __forceinline__ int64_t clamp_visible(int64_t v, int64_t limit) {
     return v < 0 ? 0 : (v > limit ? limit : v);
 }
 
+// Workgroup barrier that orders LDS only: the waves' outstanding global stores
+// are not waited for (a plain __syncthreads waits for every vector memory
+// operation of the wave, stores included, before the barrier).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Order-preserving map of an fp32 score to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t score_key(float s) {
     uint32_t u = f2u(s);

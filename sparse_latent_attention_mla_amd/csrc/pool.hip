@@ -19,50 +19,58 @@ namespace mla {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kPoolIters = 16;            // 64-position strips per wave
-constexpr int kPoolRows = kPoolThreads * kPoolIters;   // positions per workgroup
+constexpr int kPoolPer = 2;               // blocks per thread
+constexpr int kPoolBlocks = kPoolThreads * kPoolPer;   // blocks per workgroup
 
-// Lanes read consecutive scores (one coalesced load per 64 positions), and the
-// `block` lanes of a block (block a power of two <= 64) meet in a butterfly
-// maximum; invisible positions enter as -inf.  The block score is canonicalised
-// (+0 for a zero maximum) so that its key orders like the float comparison.
+// Each thread scores whole blocks (consecutive threads, consecutive blocks):
+// it loads the block's scores (16-byte vectors when the rows allow), takes their
+// maximum over the visible positions (invisible ones enter as -inf) and adds the
+// block score's key to the workgroup's LDS histogram. The block score is
+// canonicalised (+0 for a zero maximum) so that its key orders like the float
+// comparison.
+template <bool VEC4>
 __global__ __launch_bounds__(kPoolThreads) void k_block_max(const float* __restrict__ scores, int64_t capacity,
                                                             const int32_t* __restrict__ n_visible, int block,
                                                             int lg_block, float* __restrict__ bmax,
                                                             int32_t* __restrict__ nvb, uint32_t* __restrict__ hist_all) {
     __shared__ uint32_t hist[kHistBins];
     const int b = blockIdx.y;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x;
     const int64_t nvis = clamp_visible(n_visible[b], capacity);
     const int64_t nb_cap = (capacity + block - 1) >> lg_block;
     const int64_t n_vb = (nvis + block - 1) >> lg_block;
-    const int64_t r0 = (int64_t)blockIdx.x * kPoolRows + (int64_t)wave * 64 * kPoolIters;
     const float* sc = scores + b * capacity;
-    float v[kPoolIters];
+    float m[kPoolPer];
 #pragma unroll
-    for (int i = 0; i < kPoolIters; ++i) {
-        const int64_t s = r0 + 64 * i + lane;
-        v[i] = (s < nvis) ? sc[s] : -__builtin_inff();
+    for (int u = 0; u < kPoolPer; ++u) {
+        const int64_t blk = (int64_t)blockIdx.x * kPoolBlocks + u * kPoolThreads + t;
+        const int64_t s0 = blk << lg_block;
+        float x = -__builtin_inff();
+        if (blk < n_vb) {
+            if constexpr (VEC4) {
+                for (int j = 0; j < block && s0 + j < nvis; j += 4) {   // (then all 4 lie below capacity)
+                    const f32x4 q = *reinterpret_cast<const f32x4*>(sc + s0 + j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (s0 + j + e < nvis && q[e] > x) x = q[e];
+                }
+            } else {
+                for (int j = 0; j < block; ++j)
+                    if (s0 + j < nvis && sc[s0 + j] > x) x = sc[s0 + j];
+            }
+        }
+        m[u] = x + 0.0f;                                    // -0 -> +0
     }
     for (int i = t; i < kHistBins; i += kPoolThreads) hist[i] = 0u;
     if (blockIdx.x == 0 && t == 0) nvb[b] = (int32_t)n_vb;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
-    for (int i = 0; i < kPoolIters; ++i) {
-        float m = v[i];
-        for (int w = 1; w < block; w <<= 1) {
-            const float o = __shfl_xor(m, w, 64);
-            m = (o > m) ? o : m;
-        }
-        const int64_t s = r0 + 64 * i + lane;
-        const int64_t blk = s >> lg_block;
-        if ((lane & (block - 1)) == 0 && blk < nb_cap) {
-            m = m + 0.0f;                                   // -0 -> +0
-            bmax[b * nb_cap + blk] = m;
-            if (blk < n_vb) atomicAdd(&hist[score_key(m) >> (32 - kHistBits)], 1u);
-        }
+    for (int u = 0; u < kPoolPer; ++u) {
+        const int64_t blk = (int64_t)blockIdx.x * kPoolBlocks + u * kPoolThreads + t;
+        if (blk < nb_cap) bmax[b * nb_cap + blk] = m[u];
+        if (blk < n_vb) atomicAdd(&hist[score_key(m[u]) >> (32 - kHistBits)], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     flush_hist_copy([&](int i) { return hist[i]; }, hist_all + (int64_t)b * kHistWordsHost, hist_copy_of_block(),
                     kPoolThreads);
 }
@@ -75,8 +83,14 @@ hipError_t launch_block_max(const float* scores, int64_t capacity, const int32_t
     int lg = 0;
     while ((1 << lg) < block) ++lg;
     if ((1 << lg) != block || block > 64) return hipErrorInvalidValue;
-    const unsigned gx = (unsigned)std::max<int64_t>(1, (capacity + kPoolRows - 1) / kPoolRows);
-    return launch_kernel(k_block_max, dim3(gx, B), dim3(kPoolThreads), 0, stream, nullptr, nullptr, scores,
+    const int64_t nb = (capacity + block - 1) >> lg;
+    const unsigned gx = (unsigned)std::max<int64_t>(1, (nb + kPoolBlocks - 1) / kPoolBlocks);
+    // 16-byte loads when every block starts 16-byte aligned
+    const bool vec4 = block % 4 == 0 && capacity % 4 == 0 && reinterpret_cast<uintptr_t>(scores) % 16 == 0;
+    if (vec4)
+        return launch_kernel(k_block_max<true>, dim3(gx, B), dim3(kPoolThreads), 0, stream, nullptr, nullptr,
+                             scores, capacity, n_visible, block, lg, bmax, nvb, hist);
+    return launch_kernel(k_block_max<false>, dim3(gx, B), dim3(kPoolThreads), 0, stream, nullptr, nullptr, scores,
                          capacity, n_visible, block, lg, bmax, nvb, hist);
 }
 

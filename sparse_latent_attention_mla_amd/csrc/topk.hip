@@ -22,9 +22,13 @@
 //      the lists over inside one kernel needs a device-scope fence in every
 //      workgroup, which costs more than the launch.)
 // Sequences of up to kRowPathMax rows take a shorter path: one workgroup per
-// sequence reads every score, finds T, compacts and radix-selects in LDS, with
-// no hand-over between workgroups. (Longer sequences outgrow one CU's vector
-// throughput: classifying 128K scores alone takes it several microseconds.)
+// sequence reads every score, finds T, appends every row of bin T or above to
+// one LDS list (one compare and one ballot per score) and radix-selects in it,
+// the rows above T first, with no hand-over between workgroups. (Longer
+// sequences outgrow one CU's vector throughput: 64K scores already take it
+// longer than the two-kernel path.) The final kernel for more than 64 select
+// workgroups, or for selections of blocks, gathers the lists flat
+// (k_select_final2_flat).
 // Output positions form an unordered set.
 // The same kernels select over a candidate pool (the entries of a Reindex
 // layer's pool: each selected entry is reported as its position, entries that
@@ -92,7 +96,7 @@ __device__ __forceinline__ void zero_hist_rest(uint32_t* hb, uint32_t need, uint
         const uint64_t hit = __ballot(excl < need && incl >= need);
         if (t == 0) cb_s = hit ? kCoarseBins - 1 - __builtin_ctzll(hit) : -1;
     }
-    __syncthreads();
+    lds_barrier();
     const int cb = cb_s;
     if (cb >= 0 && t < kHistCopies * kFinePerCoarse / 4)       // 8 copies x 64 bins, 4 per thread
         reinterpret_cast<u32x4*>(hist_fine(hb, t / (kFinePerCoarse / 4)) + cb * kFinePerCoarse)[t % (kFinePerCoarse / 4)] =
@@ -172,50 +176,55 @@ __device__ __forceinline__ DigitResult hist_find(uint32_t* hb, uint32_t need) {
 // One sequence's output row: reported value v goes to slot o as v itself, or,
 // expanding blocks of `expand` positions, as v * expand + j in slots
 // o * expand + j (-1 as -1s).
+// (EXPAND false: expand is 1, and the kernels compile to plain stores.)
+template <bool EXPAND>
 struct OutRow {
     int32_t* out;
     int expand;
     __device__ __forceinline__ void put(uint32_t o, int32_t v) const {
-        if (expand == 1) {
+        if constexpr (!EXPAND) {
             out[o] = v;
-            return;
+        } else {
+            for (int j = 0; j < expand; ++j) out[(int64_t)o * expand + j] = v < 0 ? -1 : v * expand + j;
         }
-        for (int j = 0; j < expand; ++j) out[(int64_t)o * expand + j] = v < 0 ? -1 : v * expand + j;
     }
 };
-__device__ __forceinline__ OutRow out_row(int32_t* out_idx, int b, int k, const SelectMap& m) {
-    return OutRow{out_idx + (int64_t)b * k * m.expand, m.expand};
+template <bool EXPAND>
+__device__ __forceinline__ OutRow<EXPAND> out_row(int32_t* out_idx, int b, int k, const SelectMap& m) {
+    return OutRow<EXPAND>{out_idx + (int64_t)b * k * (EXPAND ? m.expand : 1), EXPAND ? m.expand : 1};
 }
 
 // Sequence b's view of a SelectMap: the position entry s reports, given the
 // pool entry cv = cand[b, s] (loaded with the score; unused without a pool).
+template <bool POOL>
 struct PosMap {
-    bool pool;
     int64_t lim;
     __device__ __forceinline__ int32_t operator()(int64_t s, int32_t cv) const {
-        if (!pool) return (int32_t)s;
-        return (cv >= 0 && cv < lim) ? cv : -1;
+        if constexpr (!POOL) return (int32_t)s;
+        else return (cv >= 0 && cv < lim) ? cv : -1;
     }
 };
-__device__ __forceinline__ PosMap pos_map(const SelectMap& m, int b) {
-    return m.cand ? PosMap{true, clamp_visible(m.n_visible[b], m.limit)} : PosMap{false, 0};
+template <bool POOL>
+__device__ __forceinline__ PosMap<POOL> pos_map(const SelectMap& m, int b) {
+    return PosMap<POOL>{POOL ? clamp_visible(m.n_visible[b], m.limit) : 0};
 }
 __device__ __forceinline__ int64_t visible_of(const int32_t* n_visible, int b, int64_t capacity) {
     return n_visible ? clamp_visible(n_visible[b], capacity) : capacity;
 }
 
-// Among the candidates c[0 .. ncand) (64-bit key << 32 | ~position, all in one
-// top-12-bit bin), append the positions of the `need` largest to out from the LDS
-// cursor on (entries at or past `want` are not written). Two 10-bit digits fix the
-// exact threshold score; only when more candidates share it than are still
-// needed do four 8-bit digits of the inverted position follow. h: two LDS
-// histograms of kMaxDigitBins, the first zero on entry; res: 4 LDS words.
-template <int NT, typename P>
-__device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, OutRow out,
-                           uint32_t* cursor, uint32_t (*h)[kMaxDigitBins], uint32_t* res) {
+// The list c[0 .. ncand) (64-bit key << 32 | ~position) holds entries whose
+// top-12-bit bin is T (nT of them) or, when `above` is set, above T. Append to
+// out from the LDS cursor on every entry above bin T and the positions of the
+// `need` largest of bin T (entries at or past `want` are not written). Two
+// 10-bit digits fix the exact threshold score; only when more entries share it
+// than are still needed do four 8-bit digits of the inverted position follow.
+// h: two LDS histograms of kMaxDigitBins, the first zero on entry; res: 4 LDS words.
+template <int NT, typename P, typename OUT>
+__device__ void radix_take_bins(P c, uint32_t ncand, int T, uint32_t nT, bool above, uint32_t need, uint32_t want,
+                                OUT out, uint32_t* cursor, uint32_t (*h)[kMaxDigitBins], uint32_t* res) {
     const int t = threadIdx.x, lane = t & 63;
-    const bool radix = need > 0 && need < ncand;
-    uint64_t prefix = radix ? (c[0] & (0xFFFull << 52)) : 0ull, mask = 0xFFFull << 52;
+    const bool radix = need > 0 && need < nT;
+    uint64_t prefix = (uint64_t)(uint32_t)T << 52, mask = 0xFFFull << 52;
     uint32_t rem = need;
     int par = 0;
     auto pass = [&](int shift, int bits) {
@@ -225,7 +234,7 @@ __device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, Ou
             const uint64_t v = c[i];
             if ((v & mask) == prefix) atomicAdd(&hc[(v >> shift) & (uint64_t)(nb - 1)], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         if (t < 64) {                                    // one wave finds the digit
             const DigitResult r = wave_find_digit(hc, nb, rem);
             if (lane == 0) {
@@ -236,13 +245,13 @@ __device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, Ou
         } else {                                         // the others clear the next histogram
             for (int i = t - 64; i < kMaxDigitBins; i += NT - 64) h[par ^ 1][i] = 0u;
         }
-        __syncthreads();
+        lds_barrier();
         const int d = (int)res[0];
         prefix |= (uint64_t)d << shift;
         mask |= (uint64_t)(nb - 1) << shift;
         rem -= res[1];
         par ^= 1;
-        return res[2];                                   // candidates sharing the prefix so far
+        return res[2];                                   // entries sharing the prefix so far
     };
     if (radix) {
         pass(42, 10);
@@ -254,17 +263,21 @@ __device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, Ou
             pass(0, 8);
         }
     }
-    // "v >= prefix" takes exactly `need`: every candidate above the threshold score,
-    // and at it either all (score resolved, count fits) or those above the exact composite
-    if (need > 0) {
-        const uint32_t n_iter = (ncand + NT - 1) / NT;
+    // the entries above bin T first, then those of bin T at or above the prefix:
+    // exactly `need` of them, above the threshold score and at it either all (score
+    // resolved, count fits) or those above the exact composite (need == nT: all).
+    // (Equal composites, which only entries reported as -1 share, may exceed `need`;
+    // the excess lands past `want` and is dropped, after every entry above bin T.)
+    const uint64_t binT = (uint64_t)(uint32_t)T;
+    const uint32_t n_iter = (ncand + NT - 1) / NT;
+    auto take_pass = [&](bool of_t) {
         for (uint32_t it = 0; it < n_iter; ++it) {
             const uint32_t i = it * NT + t;
             bool take = false;
             int32_t pos = 0;
             if (i < ncand) {
                 const uint64_t v = c[i];
-                take = !radix || v >= prefix;
+                take = of_t ? ((v >> 52) == binT && v >= prefix) : (v >> 52) > binT;
                 pos = (int32_t)(~(uint32_t)(v & 0xFFFFFFFFull));
             }
             const uint64_t m = __ballot(take);
@@ -276,7 +289,21 @@ __device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, Ou
                 if (o < want) out.put(o, pos);
             }
         }
+    };
+    if (above) {
+        take_pass(false);
+        lds_barrier();                                   // (the cursor)
     }
+    if (need > 0) take_pass(true);
+}
+
+// Among the candidates c[0 .. ncand), all in one top-12-bit bin, append the
+// positions of the `need` largest to out from the LDS cursor on.
+template <int NT, typename P, typename OUT>
+__device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, OUT out,
+                           uint32_t* cursor, uint32_t (*h)[kMaxDigitBins], uint32_t* res) {
+    if (ncand == 0 || need == 0) return;
+    radix_take_bins<NT>(c, ncand, (int)(c[0] >> 52), ncand, false, need, want, out, cursor, h, res);
 }
 
 struct FinalLds {
@@ -286,9 +313,9 @@ struct FinalLds {
 };
 
 // Radix-take over the candidates in LDS (the common case) or in the global list.
-template <int NT>
+template <int NT, typename OUT>
 __device__ __forceinline__ void radix_take_any(FinalLds& L, const uint64_t* gc2, uint32_t ncand, uint32_t need,
-                                               uint32_t want, OutRow out, uint32_t* cursor) {
+                                               uint32_t want, OUT out, uint32_t* cursor) {
     if (ncand <= (uint32_t)kFinalLds) radix_take<NT>(L.lc, ncand, need, want, out, cursor, L.h, L.res);
     else radix_take<NT>(gc2, ncand, need, want, out, cursor, L.h, L.res);
 }
@@ -306,12 +333,13 @@ __device__ __forceinline__ void classify(float v, bool in, int T, uint32_t* key,
 }
 
 // ---- one workgroup per sequence ------------------------------------------
+template <bool POOL, bool EXPAND>
 __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ scores, int64_t capacity,
                                                           const int32_t* __restrict__ n_visible, int k,
                                                           TopkWorkspace ws, int32_t* __restrict__ out_idx,
                                                           SelectMap map) {
     __shared__ FinalLds L;
-    __shared__ uint32_t n_sel, n_cnd, cursor;
+    __shared__ uint32_t n_hit, cursor, above_s, in_t_s;
     __shared__ int T_s;
     constexpr int kR = 16;                               // scores per thread per round
     constexpr int kRound = kRowThreads * kR;
@@ -319,97 +347,104 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     const int t = threadIdx.x, lane = t & 63;
     const int64_t nvis = visible_of(n_visible, b, capacity);
     const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    const OutRow out = out_row(out_idx, b, k, map);
-    const PosMap pmap = pos_map(map, b);
-    const int32_t* __restrict__ cb = map.cand ? map.cand + b * capacity : nullptr;
+    const auto out = out_row<EXPAND>(out_idx, b, k, map);
+    const auto pmap = pos_map<POOL>(map, b);
+    const int32_t* __restrict__ cb = POOL ? map.cand + b * capacity : nullptr;
     uint64_t* gc2 = ws.cand2 + b * capacity;
+    uint32_t* hb = ws.hist + (int64_t)b * kHistWordsHost;
     const float* __restrict__ sc = scores + b * capacity;
     float v[kR];
     int32_t cv[kR];                                      // pool entries (with a pool)
-    auto load = [&](int64_t r0, float* d, int32_t* e) {
+    auto load = [&](int64_t r0) {
 #pragma unroll
         for (int u = 0; u < kR; ++u) {
             const int64_t s = r0 + u * kRowThreads + t;
-            d[u] = (s < nvis) ? sc[s] : 0.0f;
-            e[u] = (cb && s < nvis) ? cb[s] : 0;
+            v[u] = (s < nvis) ? sc[s] : 0.0f;
+            if constexpr (POOL) cv[u] = (s < nvis) ? cb[s] : 0;
+            else cv[u] = 0;
         }
     };
-    load(0, v, cv);                                      // in flight during the threshold search
+    load(0);                                             // in flight during the threshold search
     if (t < 64) {
-        const DigitResult r = hist_find(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);
+        const DigitResult r = hist_find(hb, (uint32_t)k);
         if (t == 0) {
             T_s = r.found ? r.digit : -1;                // -1: every visible row fits in k
-            n_sel = 0;
-            n_cnd = 0;
+            above_s = r.above;
+            in_t_s = r.count;
+            n_hit = 0;
+            cursor = 0;
         }
     }
     for (int i = t; i < kMaxDigitBins; i += kRowThreads) L.h[0][i] = 0u;
-    __syncthreads();
+    lds_barrier();
     const int T = T_s;
-    for (int64_t r0 = 0; r0 < nvis; r0 += kRound) {
-        float vn[kR];
-        int32_t cn[kR];
-        if (r0 + kRound < nvis) load(r0 + kRound, vn, cn);
-        // classify the round, then one LDS reservation per wave and list
-        uint32_t key[kR];
-        uint64_t mt[kR], mc[kR];
-        uint32_t nt = 0, nc = 0;
-#pragma unroll
-        for (int u = 0; u < kR; ++u) {
-            const int64_t s = r0 + u * kRowThreads + t;
-            bool take, maybe;
-            classify(v[u], s < nvis, T, &key[u], &take, &maybe);
-            mt[u] = __ballot(take);
-            mc[u] = __ballot(maybe);
-            nt += (uint32_t)__popcll(mt[u]);
-            nc += (uint32_t)__popcll(mc[u]);
-        }
-        if (nt | nc) {
-            uint32_t bt = 0, bc = 0;
-            if (lane == 0) {
-                if (nt) bt = atomicAdd(&n_sel, nt);
-                if (nc) bc = atomicAdd(&n_cnd, nc);
-            }
-            bt = __shfl(bt, 0, 64);
-            bc = __shfl(bc, 0, 64);
+    if (T < 0) {                                         // every visible entry, in place
+        for (int64_t r0 = 0; r0 < nvis; r0 += kRound) {
+            if (r0 > 0) load(r0);
 #pragma unroll
             for (int u = 0; u < kR; ++u) {
                 const int64_t s = r0 + u * kRowThreads + t;
-                if ((mt[u] >> lane) & 1u) {
-                    const uint32_t o = bt + lanes_below(mt[u]);
-                    if (o < (uint32_t)k) out.put(o, pmap(s, cv[u]));
-                }
-                if ((mc[u] >> lane) & 1u) {
-                    const uint32_t o = bc + lanes_below(mc[u]);
+                if (s < nvis) out.put((uint32_t)s, pmap(s, cv[u]));
+            }
+        }
+        zero_hist(hb);
+        for (uint32_t i = want + t; i < (uint32_t)k; i += kRowThreads) out.put(i, -1);
+        return;
+    }
+    // the hits: every entry in bin T or above, appended to one list (key << 32 |
+    // ~position), one LDS reservation per wave and round
+    const uint32_t lo = (uint32_t)T << (32 - kHistBits);
+    for (int64_t r0 = 0; r0 < nvis; r0 += kRound) {
+        if (r0 > 0) load(r0);
+        uint32_t key[kR];
+        uint64_t m[kR];
+        uint32_t bits = 0, nh = 0;
+#pragma unroll
+        for (int u = 0; u < kR; ++u) {
+            const int64_t s = r0 + u * kRowThreads + t;
+            key[u] = score_key(v[u]);
+            const bool hit = s < nvis && key[u] >= lo;
+            bits |= (uint32_t)hit << u;
+            m[u] = __ballot(hit);
+            nh += (uint32_t)__popcll(m[u]);
+        }
+        if (nh) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&n_hit, nh);
+            base = __shfl(base, 0, 64);
+#pragma unroll
+            for (int u = 0; u < kR; ++u) {
+                if ((bits >> u) & 1u) {
+                    const int64_t s = r0 + u * kRowThreads + t;
+                    const uint32_t o = base + lanes_below(m[u]);
                     const uint64_t c = ((uint64_t)key[u] << 32) | (uint64_t)(~(uint32_t)pmap(s, cv[u]));
                     if (o < (uint32_t)kFinalLds) L.lc[o] = c;
                     else gc2[o] = c;                     // o < capacity: one entry per row
                 }
-                bt += (uint32_t)__popcll(mt[u]);
-                bc += (uint32_t)__popcll(mc[u]);
+                base += (uint32_t)__popcll(m[u]);
             }
         }
-#pragma unroll
-        for (int u = 0; u < kR; ++u) {
-            v[u] = vn[u];
-            cv[u] = cn[u];
-        }
     }
-    __syncthreads();
-    const uint32_t nsel = n_sel, ncand = n_cnd;
-    if (ncand > (uint32_t)kFinalLds)                     // the radix passes then read one contiguous list
+    lds_barrier();
+    const uint32_t nh = n_hit;
+    if (nh > (uint32_t)kFinalLds) {                      // the radix passes then read one contiguous list
         for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kRowThreads) gc2[i] = L.lc[i];
-    __threadfence_block();
-    if (t == 0) cursor = nsel;
-    __syncthreads();
-    const uint32_t need = (want > nsel) ? want - nsel : 0u;
-    zero_hist(ws.hist + (int64_t)b * kHistWordsHost);     // read above; the stores drain during the radix
-    radix_take_any<kRowThreads>(L, gc2, ncand, need, want, out, &cursor);
+        __threadfence_block();                             // (only then: it waits for every store)
+        __syncthreads();
+    }
+    zero_hist(hb);                                       // read above; the stores drain during the radix
+    // every hit above bin T, and the need = want - above largest of bin T
+    const uint32_t above = above_s, need = want > above ? want - above : 0u;
+    if (nh <= (uint32_t)kFinalLds)
+        radix_take_bins<kRowThreads>(L.lc, nh, T, in_t_s, true, need, want, out, &cursor, L.h, L.res);
+    else
+        radix_take_bins<kRowThreads>(gc2, nh, T, in_t_s, true, need, want, out, &cursor, L.h, L.res);
     __syncthreads();
     for (uint32_t i = want + t; i < (uint32_t)k; i += kRowThreads) out.put(i, -1);
 }
 
 // ---- many workgroups per sequence ------------------------------------------
+template <bool POOL>
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict__ scores, int64_t capacity,
                                                         const int32_t* __restrict__ n_visible, int k,
                                                         TopkWorkspace ws, SelectMap map) {
@@ -424,15 +459,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     const int64_t nvis = visible_of(n_visible, b, capacity);
     const int64_t r0 = (int64_t)blockIdx.x * kSelRows;
     const float* sc = scores + b * capacity;
-    const PosMap pmap = pos_map(map, b);
-    const int32_t* __restrict__ cb = map.cand ? map.cand + b * capacity : nullptr;
+    const auto pmap = pos_map<POOL>(map, b);
+    const int32_t* __restrict__ cb = POOL ? map.cand + b * capacity : nullptr;
     float v[kPer];
     int32_t cv[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int64_t s = r0 + i * kSelThreads + t;
         v[i] = (s < nvis) ? sc[s] : 0.0f;
-        cv[i] = (cb && s < nvis) ? cb[s] : 0;
+        if constexpr (POOL) cv[i] = (s < nvis) ? cb[s] : 0;
+        else cv[i] = 0;
     }
     if (t < 64) {
         const DigitResult r = hist_find(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k);
@@ -442,7 +478,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
             n_cnd = 0;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int T = T_s;
     // this workgroup's share of zeroing the fine histogram for the next call: every
     // workgroup of the sequence finds the same threshold, so only the 64 fine bins of
@@ -488,7 +524,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
             bc += (uint32_t)__popcll(mc[i]);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // the workgroup's own slots: counts, then its lists at r0 (at most kSelRows rows each)
     if (t == 0) {
         uint32_t* cnt = ws.counts + ((int64_t)b * gridDim.x + blockIdx.x) * 2;
@@ -521,6 +557,7 @@ __device__ uint32_t block_incl_scan(uint32_t v, uint32_t* total) {
 // One workgroup per sequence, after every k_select workgroup of it: prefix-sum the
 // counts, gather the selected positions into the output and the candidates into
 // one list, radix-select among the candidates, pad with -1.
+template <bool EXPAND>
 __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __restrict__ n_visible, int k,
                                                               int64_t capacity, int groups, TopkWorkspace ws,
                                                               int32_t* __restrict__ out_idx, SelectMap map) {
@@ -531,7 +568,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
     const int t = threadIdx.x, lane = t & 63;
     const int64_t nvis = visible_of(n_visible, b, capacity);
     const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    const OutRow out = out_row(out_idx, b, k, map);
+    const auto out = out_row<EXPAND>(out_idx, b, k, map);
     uint64_t* gc2 = ws.cand2 + b * capacity;
 
     uint32_t nsel = 0, ncand = 0;
@@ -648,14 +685,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
     for (uint32_t i = want + t; i < (uint32_t)k; i += kSelThreads) out.put(i, -1);
 }
 
-// The same for up to kF2MaxGroups select workgroups, with 1024 threads: the
-// counts are loaded first and every wave's speculative list loads are straight
-// code, so the prefix sums (one DPP scan per wave, one LDS pass) start as soon as
-// the counts land; wave w places the lists of workgroups w, w + 16, ..
 constexpr int kF2Threads = 1024;
 constexpr int kF2Waves = kF2Threads / 64;
 constexpr int kF2MaxGroups = 1024;
 constexpr int kF2Spec = 4;                // workgroups per wave whose first 64 entries load early
+constexpr int kF2Flat = 4;                // rest entries per thread per batch
+constexpr int kSpecGroups = kF2Waves * kF2Spec;
+// The final for up to kSpecGroups (64) select workgroups, where every list's
+// first 64 entries are loaded speculatively: wave w places the lists of
+// workgroups w, w + 16, w + 32, w + 48 (the counts are loaded first, and the
+// prefix sums wait only for them); entries past the first 64 of a list, which
+// the selections here rarely have, are placed afterwards, 64 at a time.
+template <bool EXPAND>
 __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __restrict__ n_visible, int k,
                                                               int64_t capacity, int groups, TopkWorkspace ws,
                                                               int32_t* __restrict__ out_idx, SelectMap map) {
@@ -667,7 +708,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t nvis = visible_of(n_visible, b, capacity);
     const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
-    const OutRow out = out_row(out_idx, b, k, map);
+    const auto out = out_row<EXPAND>(out_idx, b, k, map);
     uint64_t* gc2 = ws.cand2 + b * capacity;
     const int32_t* __restrict__ gsel = ws.sel + b * capacity;
     const uint64_t* __restrict__ gcnd = ws.cand + b * capacity;
@@ -759,29 +800,203 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);
 }
 
+
+// The same for up to kF2MaxGroups select workgroups (and for selections of
+// blocks, whose lists run longer), with 1024 threads. The counts are loaded first, then (from clamped in-bounds addresses, branch-free,
+// so that the waits for the counts do not cover them) the first 64 entries of
+// the lists of workgroups w, w + 16, w + 32, w + 48 by wave w, speculatively.
+// Prefix sums of the counts (one DPP scan per wave, one LDS pass) give every
+// workgroup's offsets in the output and in the candidate list, and prefix sums
+// of what the speculative loads did not cover (entries past the first 64, and
+// the lists of workgroups past the first 64) place "the rest" in one flat
+// index space: rest entry r belongs to the last workgroup whose rest offset is
+// <= r (a binary search in LDS). Each thread issues the loads of its rest
+// entries before it stores anything (a load issued behind a store waits for
+// that store: the vector memory counter counts both), so the rest costs one
+// load latency however the entries spread over the workgroups.
+template <bool EXPAND>
+__global__ __launch_bounds__(kF2Threads) void k_select_final2_flat(const int32_t* __restrict__ n_visible, int k,
+                                                              int64_t capacity, int groups, TopkWorkspace ws,
+                                                              int32_t* __restrict__ out_idx, SelectMap map) {
+    __shared__ FinalLds L;
+    __shared__ uint32_t cursor;
+    __shared__ uint32_t g_off[2][kF2MaxGroups], g_cnt[2][kF2MaxGroups], r_off[2][kF2MaxGroups];
+    __shared__ uint32_t wtot[kF2Waves][4];
+    const int b = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int64_t nvis = visible_of(n_visible, b, capacity);
+    const uint32_t want = (uint32_t)((nvis < k) ? nvis : k);
+    const auto out = out_row<EXPAND>(out_idx, b, k, map);
+    uint64_t* gc2 = ws.cand2 + b * capacity;
+    const int32_t* __restrict__ gsel = ws.sel + b * capacity;
+    const uint64_t* __restrict__ gcnd = ws.cand + b * capacity;
+
+    // wave 0 also loads the coarse histogram sums the zeroing needs at the end
+    const uint32_t csum = (t < 64) ? coarse_sum_of_lane(ws.hist + (int64_t)b * kHistWordsHost) : 0u;
+    const bool has_cnt = t < groups;
+    const u32x2 c2 = *reinterpret_cast<const u32x2*>(ws.counts + ((int64_t)b * groups + (has_cnt ? t : 0)) * 2);
+    int32_t vs[kF2Spec];
+    uint64_t vc[kF2Spec];
+#pragma unroll
+    for (int u = 0; u < kF2Spec; ++u) {
+        const int j = wv + kF2Waves * u;
+        const int64_t off = (int64_t)j * kSelRows + lane;
+        const bool ok = j < groups && off < capacity;
+        vs[u] = gsel[ok ? off : 0];
+        vc[u] = gcnd[ok ? off : 0];
+        if (!ok) {
+            vs[u] = 0;
+            vc[u] = 0ull;
+        }
+    }
+    const uint32_t cs = has_cnt ? c2.x : 0u, cc = has_cnt ? c2.y : 0u;
+    const bool spec = t < kSpecGroups;
+    const uint32_t rs = spec ? cs - min(cs, 64u) : cs, rc = spec ? cc - min(cc, 64u) : cc;
+    // exclusive prefix sums over the workgroups: offsets, and offsets of the rest
+    const uint32_t is = wave_incl_scan(cs), ic = wave_incl_scan(cc);
+    const uint32_t irs = wave_incl_scan(rs), irc = wave_incl_scan(rc);
+    if (lane == 63) {
+        wtot[wv][0] = is;
+        wtot[wv][1] = ic;
+        wtot[wv][2] = irs;
+        wtot[wv][3] = irc;
+    }
+    lds_barrier();
+    uint32_t bs = 0, bc = 0, brs = 0, brc = 0, nsel = 0, ncand = 0, nrs = 0, nrc = 0;
+#pragma unroll
+    for (int i = 0; i < kF2Waves; ++i) {
+        const uint32_t s_ = wtot[i][0], c_ = wtot[i][1], rs_ = wtot[i][2], rc_ = wtot[i][3];
+        if (i < wv) {
+            bs += s_;
+            bc += c_;
+            brs += rs_;
+            brc += rc_;
+        }
+        nsel += s_;
+        ncand += c_;
+        nrs += rs_;
+        nrc += rc_;
+    }
+    if (t < groups) {
+        g_off[0][t] = bs + is - cs;
+        g_off[1][t] = bc + ic - cc;
+        g_cnt[0][t] = cs;
+        g_cnt[1][t] = cc;
+        r_off[0][t] = brs + irs - rs;
+        r_off[1][t] = brc + irc - rc;
+    }
+    lds_barrier();
+    // placement: entry i of workgroup j's lists goes to the output (selected) or to
+    // the candidate list (LDS, then cand2 past kFinalLds)
+    auto place = [&](int w, int j, uint32_t i, uint64_t v) {
+        const uint32_t o = g_off[w][j] + i;
+        if (w == 0) {
+            if (o < (uint32_t)k) out.put(o, (int32_t)(uint32_t)v);
+        } else {
+            if (o < (uint32_t)kFinalLds) L.lc[o] = v;
+            else gc2[o] = v;                               // o < capacity: every row is in at most one list
+        }
+    };
+    // the workgroup holding rest entry r of list w: the last one whose rest offset is <= r
+    auto owner = [&](int w, uint32_t r) -> int {
+        int lo = 0, hi = groups - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (r_off[w][mid] <= r) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    const uint32_t n_rest = nrs + nrc;
+    bool spec_placed = false;
+    for (uint32_t base = 0; base == 0 || base < n_rest; base += kF2Flat * kF2Threads) {
+        uint64_t rv[kF2Flat];
+        int rj[kF2Flat];
+        uint32_t ri[kF2Flat];
+#pragma unroll
+        for (int u = 0; u < kF2Flat; ++u) {
+            const uint32_t r = base + u * kF2Threads + t;
+            rj[u] = -1;
+            if (r < nrs) {
+                const int j = owner(0, r);
+                const uint32_t i = (j < kSpecGroups ? 64u : 0u) + (r - r_off[0][j]);
+                rj[u] = j;
+                ri[u] = i;
+                rv[u] = (uint64_t)(uint32_t)gsel[(int64_t)j * kSelRows + i];
+            } else if (r < n_rest) {
+                const uint32_t rr = r - nrs;
+                const int j = owner(1, rr);
+                const uint32_t i = (j < kSpecGroups ? 64u : 0u) + (rr - r_off[1][j]);
+                rj[u] = j + kF2MaxGroups;                  // (list 1)
+                ri[u] = i;
+                rv[u] = gcnd[(int64_t)j * kSelRows + i];
+            }
+        }
+        if (!spec_placed) {                                // the speculated entries, behind the first rest loads
+            spec_placed = true;
+#pragma unroll
+            for (int u = 0; u < kF2Spec; ++u) {
+                const int j = wv + kF2Waves * u;
+                if (j < groups) {
+                    if ((uint32_t)lane < g_cnt[0][j]) place(0, j, lane, (uint64_t)(uint32_t)vs[u]);
+                    if ((uint32_t)lane < g_cnt[1][j]) place(1, j, lane, vc[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kF2Flat; ++u) {
+            if (rj[u] >= kF2MaxGroups) place(1, rj[u] - kF2MaxGroups, ri[u], rv[u]);
+            else if (rj[u] >= 0) place(0, rj[u], ri[u], rv[u]);
+        }
+    }
+    lds_barrier();
+    if (ncand > (uint32_t)kFinalLds) {                   // the radix passes then read one contiguous list
+        for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kF2Threads) gc2[i] = L.lc[i];
+        __threadfence_block();                             // (only then: it waits for every store)
+        __syncthreads();
+    }
+    if (t == 0) cursor = nsel;
+    for (int i = t; i < kMaxDigitBins; i += kF2Threads) L.h[0][i] = 0u;
+    lds_barrier();
+    const uint32_t need = (want > nsel) ? want - nsel : 0u;
+    zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k, csum);   // the stores drain during the radix
+    radix_take_any<kF2Threads>(L, gc2, ncand, need, want, out, &cursor);
+    __syncthreads();
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);
+}
+
 }  // namespace
 
 // MLA_TOPK_PATH=row|multi forces a path, MLA_TOPK_FINAL1 the 256-thread final (for tuning).
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                          const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream, const SelectMap& map) {
     if (B == 0 || k == 0) return hipSuccess;
+    const bool pool = map.cand != nullptr, expand = map.expand != 1;
     bool row = capacity <= kRowPathMax;
     if (const char* e = getenv("MLA_TOPK_PATH")) row = (e[0] == 'r');
     const ProfSlot p = prof_slot(PROF_SELECT);      // spans both kernels of the two-kernel path
-    if (row)
-        return launch_kernel(k_topk_row, dim3(B), dim3(kRowThreads), 0, stream, p.start, p.stop, scores, capacity,
+    if (row) {
+        auto kr = pool ? (expand ? k_topk_row<true, true> : k_topk_row<true, false>)
+                       : (expand ? k_topk_row<false, true> : k_topk_row<false, false>);
+        return launch_kernel(kr, dim3(B), dim3(kRowThreads), 0, stream, p.start, p.stop, scores, capacity,
                              n_visible, k, ws, out_idx, map);
+    }
     const unsigned nx = (unsigned)((capacity + kSelRows - 1) / kSelRows);
     if (nx > 0) {
-        const hipError_t e = launch_kernel(k_select, dim3(nx, B), dim3(kSelThreads), 0, stream, p.start, nullptr,
+        const hipError_t e = launch_kernel(pool ? k_select<true> : k_select<false>, dim3(nx, B),
+                                           dim3(kSelThreads), 0, stream, p.start, nullptr,
                                            scores, capacity, n_visible, k, ws, map);
         if (e != hipSuccess) return e;
     }
     if (nx <= (unsigned)kF2MaxGroups && !getenv("MLA_TOPK_FINAL1"))
-        return launch_kernel(k_select_final2, dim3(B), dim3(kF2Threads), 0, stream, nx > 0 ? nullptr : p.start,
+        return launch_kernel(expand ? k_select_final2_flat<true>
+                                    : (nx > (unsigned)kSpecGroups ? k_select_final2_flat<false>
+                                                                  : k_select_final2<false>),
+                             dim3(B), dim3(kF2Threads), 0, stream, nx > 0 ? nullptr : p.start,
                              p.stop, n_visible, k, capacity, (int)nx, ws, out_idx, map);
-    return launch_kernel(k_select_final, dim3(B), dim3(kSelThreads), 0, stream, nx > 0 ? nullptr : p.start, p.stop,
-                         n_visible, k, capacity, (int)nx, ws, out_idx, map);
+    return launch_kernel(expand ? k_select_final<true> : k_select_final<false>, dim3(B), dim3(kSelThreads), 0,
+                         stream, nx > 0 ? nullptr : p.start, p.stop, n_visible, k, capacity, (int)nx, ws, out_idx,
+                         map);
 }
 
 }  // namespace mla

@@ -204,17 +204,21 @@ def step_inputs(cfg: Config, seed: int = 0) -> StepInputs:
     return StepInputs(cfg, main, idx, q, q_idx, w.astype(np.float32), win)
 
 
-def algorithmic_bytes(cfg: Config) -> dict:
+def algorithmic_bytes(cfg: Config, pool_blocks: int = 0, block: int = 8) -> dict:
     """Bytes one decode step (layer group) must move, by part.  Materialised
-    scores and split-K partials are excluded: they are implementation traffic."""
-    from math import prod  # noqa: F401
+    scores and split-K partials are excluded: they are implementation traffic.
+    With pool_blocks > 0 the first indexer layer publishes a candidate pool of
+    that many blocks (hierarchical sparse indexer): the later indexer layers
+    read only the pool's rows, and the pool's positions are written once and
+    read by each of them."""
     rb_main = _row_bytes(cfg.main_fmt, cfg.dim, cfg.rope)
     rb_idx = _row_bytes(cfg.idx_fmt, cfg.d_I, 0)
     qb = 4 if cfg.main_fmt == F32 else 2
     B, L, LI = cfg.B, len(cfg.layers), n_indexers(cfg)
     k_eff = min(cfg.k, cfg.N)
+    pool_rows = min(pool_blocks * block, cfg.N) if pool_blocks else cfg.N
     parts = {
-        "scan": LI * B * cfg.N * rb_idx,
+        "scan": B * cfg.N * rb_idx + (LI - 1) * B * pool_rows * rb_idx,
         "q_idx_w": LI * B * cfg.H_I * (cfg.d_I * qb + 4),
         "indices": LI * B * cfg.k * 4 + L * B * cfg.k * 4,
         "gather": L * B * k_eff * rb_main,
@@ -223,6 +227,8 @@ def algorithmic_bytes(cfg: Config) -> dict:
         "out": L * B * cfg.H * (cfg.d_v + 1) * 4,
         "append": B * (rb_main + rb_idx + 4 * (cfg.D + cfg.d_I)) + L * B * cfg.D * (4 + 2) * (cfg.W > 0),
     }
+    if pool_blocks and LI > 1:
+        parts["pool"] = B * pool_blocks * block * 4 * LI
     parts["total"] = sum(parts.values())
     return parts
 

@@ -14,7 +14,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, E4M3_S128, E2M1_S16 = 0, 1, 2, 3
+F32, BF16, E4M3_S128, E2M1_S16, MXFP4 = 0, 1, 2, 3, 4
 
 _lib = None
 
@@ -28,6 +28,8 @@ def lib():
         P = C.c_void_p
         i32, i64, f32 = C.c_int32, C.c_int64, C.c_float
         L.orc_e4m3_value.argtypes, L.orc_e4m3_value.restype = [C.c_uint32], C.c_double
+        L.orc_e8m0_value.argtypes, L.orc_e8m0_value.restype = [C.c_uint32], C.c_double
+        L.orc_mx_scale.argtypes, L.orc_mx_scale.restype = [C.c_float], C.c_uint32
         L.orc_e4m3_encode.argtypes, L.orc_e4m3_encode.restype = [f32], C.c_uint32
         L.orc_e2m1_value.argtypes, L.orc_e2m1_value.restype = [C.c_uint32], C.c_double
         L.orc_e2m1_encode.argtypes, L.orc_e2m1_encode.restype = [f32], C.c_uint32
@@ -74,6 +76,16 @@ def num_threads() -> int:
 def e4m3_value(codes):
     codes = np.asarray(codes, dtype=np.uint32)
     return np.array([lib().orc_e4m3_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e8m0_value(codes):
+    codes = np.asarray(codes, dtype=np.uint32)
+    return np.array([lib().orc_e8m0_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def mx_scale(amax):
+    """The E8M0 code of an MXFP4 block whose largest magnitude is amax (fp32)."""
+    return int(lib().orc_mx_scale(float(np.float32(amax))))
 
 
 def e2m1_value(nibs):

@@ -155,6 +155,34 @@ static void put_u16(uint8_t* p, uint32_t h) { p[0] = (uint8_t)(h & 0xFF); p[1] =
 static uint32_t get_u16(const uint8_t* p) { return (uint32_t)p[0] | ((uint32_t)p[1] << 8); }
 
 /* ------------------------------------------------------------------------- */
+/* E8M0 and the MXFP4 block scale ([P1] "DeepSeek-V4", "The indexer in four
+ * bits" and [P4] "FP4 main KV: smaller cells": V4's indexer keys and queries
+ * use the OCP MXFP4 format, 128 four-bit values plus four E8M0 scales = 68 B).
+ * An E8M0 code e is the power of two 2^(e - 127); 0xFF is NaN.  The pages do
+ * not state how the shared scale is chosen; the reading taken is the OCP
+ * microscaling rule: X = 2^(floor(log2(amax)) - 2), 2 being the exponent of
+ * E2M1's largest value 6, clamped to the codes 0 .. 254; a block of zeros
+ * takes code 0.  Elements are E2M1(x / X), round-to-nearest-even on the
+ * ladder, saturating at 6 (amax / X lies in [4, 8), so values over 6X clamp).
+ * Pins: codes 127 -> 1, 128 -> 2, 0 -> 2^-127, 254 -> 2^127; amax 6 -> X = 1,
+ * amax 1 -> X = 1/4; blocks on the grid round-trip; |x - x^| <= X below 6X. */
+double orc_e8m0_value(uint32_t code) {
+    code &= 0xFFu;
+    if (code == 0xFFu) return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+uint32_t orc_mx_scale(float amax) {
+    int e;
+    if (!(amax > 0.0f)) return 0u;
+    (void)frexpf(amax, &e);                 /* amax = m * 2^e, m in [0.5, 1): floor(log2) = e - 1 */
+    e = (e - 1) - 2 + 127;
+    if (e < 0) e = 0;
+    if (e > 254) e = 254;
+    return (uint32_t)e;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Row layouts.
  *  F32        : (dim+rope) fp32                                   c1: 320 / 128 B
  *  BF16       : (dim+rope) bf16                                   c2: 1152 / 256 B
@@ -167,7 +195,11 @@ static uint32_t get_u16(const uint8_t* p) { return (uint32_t)p[0] | ((uint32_t)p
  *               ([P1] "DeepSeek-V4.1", "Four bits for the main KV": 256 + 32 =
  *               288 B; [P3] section 3: the indexer key in the same format is
  *               72 B)
- * Pins: 656 / 132 / 288 / 72; 61 x (656 + 132) = 48,068 ([P1] "DeepSeek-V3.2").
+ *  MXFP4      : dim/2 bytes of nibbles (as E2M1_S16) | dim/32 E8M0 scale bytes;
+ *               no RoPE part ([P1] "DeepSeek-V4", "The indexer in four bits":
+ *               64 + 4 = 68 B for the 128-channel indexer key)
+ * Pins: 656 / 132 / 288 / 72 / 68; 61 x (656 + 132) = 48,068 ([P1]
+ * "DeepSeek-V3.2"); 2.5 x (288 + 68) = 890 ([P3], [P4]).
  */
 int64_t orc_row_bytes(int fmt, int dim, int rope) {
     if (dim <= 0 || rope < 0) return -1;
@@ -180,6 +212,9 @@ int64_t orc_row_bytes(int fmt, int dim, int rope) {
     case ORC_E2M1_S16:
         if (dim % 16 || rope != 0) return -1;
         return (int64_t)dim / 2 + dim / 16;
+    case ORC_MXFP4:
+        if (dim % 32 || rope != 0) return -1;
+        return (int64_t)dim / 2 + dim / 32;
     default: return -1;
     }
 }
@@ -242,6 +277,24 @@ int orc_quant_row(int fmt, int dim, int rope, const float* x, uint8_t* row) {
             }
         }
         return 0;
+    case ORC_MXFP4:
+        memset(row, 0, (size_t)nb);
+        for (b = 0; b < dim / 32; b++) {
+            float a = 0.0f, X;
+            uint32_t sc;
+            for (c = 32 * b; c < 32 * (b + 1); c++) {
+                float m = fabsf(x[c]);
+                if (m > a) a = m;
+            }
+            sc = orc_mx_scale(a);
+            X = ldexpf(1.0f, (int)sc - 127);         /* exact, 2^-127 as an fp32 subnormal */
+            row[dim / 2 + b] = (uint8_t)sc;
+            for (c = 32 * b; c < 32 * (b + 1); c++) {
+                uint32_t nib = (a == 0.0f) ? 0u : orc_e2m1_encode(x[c] / X);
+                row[c / 2] |= (uint8_t)((c & 1) ? (nib << 4) : nib);
+            }
+        }
+        return 0;
     }
     return -1;
 }
@@ -269,6 +322,12 @@ int orc_dequant_row(int fmt, int dim, int rope, const uint8_t* row, double* out)
         for (c = 0; c < dim; c++) {
             uint32_t nib = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 0xF);
             out[c] = orc_e2m1_value(nib) * orc_e4m3_value(row[dim / 2 + c / 16]);
+        }
+        return 0;
+    case ORC_MXFP4:
+        for (c = 0; c < dim; c++) {
+            uint32_t nib = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 0xF);
+            out[c] = orc_e2m1_value(nib) * orc_e8m0_value(row[dim / 2 + c / 32]);
         }
         return 0;
     }
@@ -336,7 +395,10 @@ int orc_append(int main_fmt, int main_dim, int main_rope, int idx_fmt, int idx_d
  * With a candidate pool (cand != NULL, [P4] "The Hierarchical Sparse
  * Indexer"), score i of row b is that of position cand[b,i] (-inf when the
  * position is negative or not visible) and scores is [B, n_cand].
- * q_idx holds the exact values of the bf16 queries, [B, H_I, idx_dim].
+ * q_idx holds the exact values of the bf16 queries, [B, H_I, idx_dim].  With
+ * MXFP4 keys the query is quantised the same way first (each head's vector as
+ * an MXFP4 row): V4 caches, loads and multiplies the indexer's query-key path
+ * entirely in FP4 ([P1] "DeepSeek-V4", "The indexer in four bits").
  * Pins: single-head and one-hot-weight cases reduce to a dot product;
  * I(q) - I(-q) is the plain bilinear form sum_j w_j sigma q_j.k; ReLU votes
  * are non-negative; brute force on the tiny case. */
@@ -350,7 +412,24 @@ int orc_indexer_scores(int idx_fmt, int idx_dim, const float* q_idx, const float
     if (rb < 0 || B < 0 || H_I <= 0 || n_rows < 0) return -1;
     for (b = 0; b < B; b++) {
         int64_t i;
-        if (n_visible[b] < 0 || n_visible[b] > n_rows) return -2;
+        int j0;
+        double* qd = (double*)malloc(sizeof(double) * (size_t)H_I * idx_dim);
+        if (n_visible[b] < 0 || n_visible[b] > n_rows) {
+            free(qd);
+            return -2;
+        }
+        for (j0 = 0; j0 < H_I; j0++) {                 /* the queries the scores use */
+            const float* qj = q_idx + ((int64_t)b * H_I + j0) * idx_dim;
+            int c;
+            if (idx_fmt == ORC_MXFP4) {
+                uint8_t* qrow = (uint8_t*)malloc((size_t)rb);
+                orc_quant_row(ORC_MXFP4, idx_dim, 0, qj, qrow);
+                orc_dequant_row(ORC_MXFP4, idx_dim, 0, qrow, qd + (int64_t)j0 * idx_dim);
+                free(qrow);
+            } else {
+                for (c = 0; c < idx_dim; c++) qd[(int64_t)j0 * idx_dim + c] = (double)qj[c];
+            }
+        }
 #pragma omp parallel for schedule(static)
         for (i = 0; i < n_out; i++) {
             double* k = (double*)malloc(sizeof(double) * idx_dim);
@@ -364,9 +443,9 @@ int orc_indexer_scores(int idx_fmt, int idx_dim, const float* q_idx, const float
             }
             orc_dequant_row(idx_fmt, idx_dim, 0, idx_cache + b * idx_seq_stride + s * rb, k);
             for (j = 0; j < H_I; j++) {
-                const float* qj = q_idx + ((int64_t)b * H_I + j) * idx_dim;
+                const double* qj = qd + (int64_t)j * idx_dim;
                 double d = 0.0, v;
-                for (c = 0; c < idx_dim; c++) d += (double)qj[c] * k[c];
+                for (c = 0; c < idx_dim; c++) d += qj[c] * k[c];
                 v = (double)sigma * d;
                 if (v < 0.0) v = 0.0;                          /* ReLU */
                 acc += (double)w[(int64_t)b * H_I + j] * v;
@@ -374,6 +453,7 @@ int orc_indexer_scores(int idx_fmt, int idx_dim, const float* q_idx, const float
             scores[b * n_out + i] = (float)acc;
             free(k);
         }
+        free(qd);
     }
     return 0;
 }

@@ -20,7 +20,7 @@ extern "C" {
 #endif
 
 /* Row formats (value of the `fmt` arguments). */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3_S128 = 2, ORC_E2M1_S16 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3_S128 = 2, ORC_E2M1_S16 = 3, ORC_MXFP4 = 4 };
 
 /* Scalar codecs. */
 double   orc_e4m3_value(uint32_t code);   /* NaN for 0x7F / 0xFF */
@@ -28,6 +28,8 @@ uint32_t orc_e4m3_encode(float x);        /* RNE, saturating at +-448 */
 double   orc_e2m1_value(uint32_t nib);
 uint32_t orc_e2m1_encode(float y);        /* RNE on the ladder, saturating at +-6 */
 uint32_t orc_bf16_encode(float x);        /* RNE */
+double   orc_e8m0_value(uint32_t code);   /* 2^(code - 127); NaN for 0xFF */
+uint32_t orc_mx_scale(float amax);        /* shared exponent code of an MXFP4 block */
 float    orc_bf16_value(uint32_t h);
 
 /* Rows. */

@@ -121,8 +121,12 @@ def test_row_sizes_match_the_pages(golden_dir):
     assert abs(900 - 890) / 890 < 0.012                              # "within about one per cent"
     assert O.row_bytes(O.BF16, 512, 64) == 1152 and O.row_bytes(O.BF16, 128, 0) == 256
     assert O.row_bytes(O.F32, 64, 16) == 320 and O.row_bytes(O.F32, 32, 0) == 128
+    # the MXFP4 indexer key: 128 nibbles + four E8M0 scales, the 68 B the pages' total needs
+    assert O.row_bytes(O.MXFP4, 128, 0) == v41["indexer_row_mxfp4"] == 68
+    assert v41["entries_per_token"] * (288 + O.row_bytes(O.MXFP4, 128, 0)) == 890
     # unsupported shapes are refused
     assert O.row_bytes(O.E4M3_S128, 100, 0) < 0 and O.row_bytes(O.E2M1_S16, 512, 64) < 0
+    assert O.row_bytes(O.MXFP4, 48, 0) < 0 and O.row_bytes(O.MXFP4, 128, 2) < 0
 
 
 def test_fp4_row_reproduces_the_pages_worked_example(golden_dir):
@@ -225,3 +229,45 @@ def test_append_writes_only_its_slots_and_the_window_ring():
     with pytest.raises(ValueError):
         O.append((O.E2M1_S16, 512, 0), (O.E2M1_S16, 128, 0), new_main, new_idx,
                  np.array([[0, 40]] * 3, np.int32), main, idx)
+
+
+# ---- MXFP4 (E2M1 elements, one E8M0 power-of-two scale per 32 channels) ----
+def test_e8m0_values_and_the_mx_scale_rule():
+    assert list(O.e8m0_value([127, 128, 126, 0, 254])) == [1.0, 2.0, 0.5, 2.0 ** -127, 2.0 ** 127]
+    assert np.isnan(O.e8m0_value([255])[0])
+    # X = 2^(floor(log2 amax) - 2): the block maximum lands in [4, 8) scale units
+    assert O.mx_scale(6.0) == 127 and O.mx_scale(4.0) == 127 and O.mx_scale(7.99) == 127
+    assert O.mx_scale(1.0) == 125 and O.mx_scale(3.99) == 126 and O.mx_scale(8.0) == 128
+    assert O.mx_scale(0.0) == 0 and O.mx_scale(2.0 ** -140) == 0          # clamped at the smallest code
+    assert O.mx_scale(3.0e38) == 127 + 127 - 2                           # floor(log2 3e38) = 127
+    rng = np.random.default_rng(11)
+    a = (rng.uniform(0.5, 1.0, 500) * 2.0 ** rng.integers(-60, 60, 500)).astype(np.float32)
+    X = O.e8m0_value([O.mx_scale(v) for v in a])
+    assert np.all((a / X >= 4) & (a / X < 8))
+
+
+def test_mxfp4_row_roundtrip_error_bound_and_layout():
+    rng = np.random.default_rng(12)
+    # blocks on the grid (a rung of 4 or 6 present, so the block maximum picks the scale) round-trip
+    nib = rng.integers(0, 16, (40, 128)).astype(np.uint32)
+    nib[:, ::32] = rng.choice([0x6, 0x7, 0xE, 0xF], (40, 4))              # +-4 or +-6 in every block
+    e = rng.integers(100, 150, (40, 4))
+    x = (O.e2m1_value(nib) * np.repeat(2.0 ** (e - 127), 32, axis=1)).astype(np.float32)
+    r = O.quant_rows(O.MXFP4, 128, 0, x)
+    assert np.array_equal(O.dequant_rows(O.MXFP4, 128, 0, r), x)
+    assert np.array_equal(r[:, 64:], e.astype(np.uint8))
+    # low nibble = even channel
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    assert np.array_equal(r[:, :64], packed)
+    # general inputs: nearest rung below 6X (largest gap 2X), saturation above
+    y = (rng.standard_normal((64, 128)) * rng.uniform(1e-3, 1e3, (64, 1))).astype(np.float32)
+    ry = O.quant_rows(O.MXFP4, 128, 0, y)
+    d = O.dequant_rows(O.MXFP4, 128, 0, ry)
+    Xs = np.repeat(O.e8m0_value(ry[:, 64:]), 32, axis=1)
+    small = np.abs(y) <= 6 * Xs
+    assert np.all(np.abs(d - y)[small] <= Xs[small])
+    assert np.all(np.abs(d[~small]) == 6 * Xs[~small])
+    assert np.all(np.isin(np.abs(d / Xs), E2M1_LADDER))
+    # a block of zeros: scale code 0, codes 0
+    z = np.zeros((1, 128), np.float32)
+    assert not O.quant_rows(O.MXFP4, 128, 0, z).any()

@@ -33,10 +33,18 @@ def _exact_fp4_keys(rng, n, dim):
     return x.astype(np.float32)
 
 
+def _exact_mx_keys(rng, n, dim):
+    lad = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    x = rng.choice(lad, (n, dim)) * rng.choice([-1, 1], (n, dim))
+    x[:, ::32] = 6.0                                             # E8M0 scale 2^0
+    return x.astype(np.float32)
+
+
 KEY_MAKERS = {
     O.F32: lambda rng, n, d: rng.standard_normal((n, d)).astype(np.float32),
     O.E4M3_S128: _exact_e4m3_keys,
     O.E2M1_S16: _exact_fp4_keys,
+    O.MXFP4: _exact_mx_keys,
 }
 
 
@@ -55,6 +63,36 @@ def test_indexer_single_head_reduces_to_relu_of_dot(fmt, dim):
         got = O.indexer_scores((fmt, dim, 0), q, w, sigma, rows, [N])[0]
         ref = np.maximum(sigma * (keys.astype(np.float64) @ q[0, j].astype(np.float64)), 0)
         np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_mxfp4_indexer_quantises_the_query_too():
+    """With MXFP4 keys the query-key product runs in FP4: a query on the MXFP4
+    grid scores as ReLU(sigma q.k) exactly (np.dot), and any query scores as its
+    own MXFP4 rounding (which differs from the unrounded query's score)."""
+    rng = np.random.default_rng(13)
+    N, H_I, dim = 200, 3, 128
+    keys = _exact_fp4_keys(rng, N, dim)                  # on both grids (a 6 in every 16 channels)
+    rows = O.quant_rows(O.MXFP4, dim, 0, keys)[None]
+    assert np.array_equal(O.dequant_rows(O.MXFP4, dim, 0, rows)[0], keys)
+    sigma = dim ** -0.5
+    q_grid = (_exact_mx_keys(rng, H_I, dim) * np.float32(0.25))[None]       # scale 2^-2, still on the grid
+    for j in range(H_I):
+        w = np.zeros((1, H_I), np.float32)
+        w[0, j] = 1.0
+        got = O.indexer_scores((O.MXFP4, dim, 0), q_grid, w, sigma, rows, [N])[0]
+        ref = np.maximum(sigma * (keys.astype(np.float64) @ q_grid[0, j].astype(np.float64)), 0)
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+    q = rng.standard_normal((1, H_I, dim)).astype(np.float32)
+    q_hat = O.dequant_rows(O.MXFP4, dim, 0, O.quant_rows(O.MXFP4, dim, 0, q[0]))[None].astype(np.float32)
+    w = rng.standard_normal((1, H_I)).astype(np.float32)
+    s_q = O.indexer_scores((O.MXFP4, dim, 0), q, w, sigma, rows, [N])
+    assert np.array_equal(s_q, O.indexer_scores((O.MXFP4, dim, 0), q_hat, w, sigma, rows, [N]))
+    # the unrounded query through the E2M1 format (which leaves queries alone) scores differently
+    rows16 = O.quant_rows(O.E2M1_S16, dim, 0, keys)[None]
+    assert np.array_equal(O.dequant_rows(O.E2M1_S16, dim, 0, rows16)[0], keys)
+    assert not np.array_equal(s_q, O.indexer_scores((O.E2M1_S16, dim, 0), q, w, sigma, rows16, [N]))
+    np.testing.assert_allclose(s_q, O.indexer_scores((O.E2M1_S16, dim, 0), q_hat, w, sigma, rows16, [N]),
+                               rtol=1e-6, atol=1e-7)
 
 
 def test_indexer_relu_difference_is_the_bilinear_form():

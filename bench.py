@@ -36,7 +36,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c4x", "c5"])
     p.add_argument("--layers", type=int, default=8, help="distinct layer caches rotated")
     p.add_argument("--pool", type=int, default=0,
                    help="CSA2 group: the Full layer publishes a candidate pool of this many 8-position "

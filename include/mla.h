@@ -71,13 +71,23 @@ typedef enum {
  *                    Scale of a 16-channel block: E4M3(amax / 6) (fp32 division,
  *                    round-to-nearest-even, saturating); code = E2M1 nearest-even of
  *                    x/scale; a zero scale gives zero codes.
+ *  MLA_FMT_MXFP4     [dim/2 bytes of E2M1 nibbles as above | dim/32 E8M0 scale bytes];
+ *                    dim % 32 == 0, rope == 0. V4's indexer keys: 64 + 4 = 68 B
+ *                    ([P1] "DeepSeek-V4", "The indexer in four bits"; [P4] "FP4 main
+ *                    KV: smaller cells"). The OCP microscaling rule: the E8M0 code of a
+ *                    32-channel block is floor(log2 amax) - 2 + 127, clamped to 0..254
+ *                    (0 for a block of zeros), its scale X = 2^(code - 127); code =
+ *                    E2M1 nearest-even of x/X, saturating at 6. As an indexer format it
+ *                    makes the query-key product FP4 on both sides: mla_indexer_topk
+ *                    rounds each head's query to MXFP4 the same way before scoring.
  * E4M3 is the OCP "fn" variant (max 448, no infinities); E2M1 magnitudes are
- * 0, 0.5, 1, 1.5, 2, 3, 4, 6 ([P1] "A Precision Primer"). */
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 ([P1] "A Precision Primer"); an E8M0 code e is 2^(e - 127). */
 typedef enum {
     MLA_FMT_F32 = 0,
     MLA_FMT_BF16 = 1,
     MLA_FMT_E4M3_S128 = 2,
-    MLA_FMT_E2M1_S16 = 3
+    MLA_FMT_E2M1_S16 = 3,
+    MLA_FMT_MXFP4 = 4
 } mla_fmt_t;
 
 /* A row: `dim` quantised (or plain) channels followed by `rope_dim` RoPE channels.

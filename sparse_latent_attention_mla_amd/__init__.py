@@ -15,7 +15,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-F32, BF16, E4M3_S128, E2M1_S16 = 0, 1, 2, 3
+F32, BF16, E4M3_S128, E2M1_S16, MXFP4 = 0, 1, 2, 3, 4
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
 

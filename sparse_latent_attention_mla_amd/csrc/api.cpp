@@ -240,6 +240,9 @@ int64_t mla_row_bytes(mla_row_t row) {
     case MLA_FMT_E2M1_S16:
         if (row.dim % 16 != 0 || row.rope_dim != 0 || row.dim > 1024) return -1;
         return (int64_t)row.dim / 2 + row.dim / 16;
+    case MLA_FMT_MXFP4:
+        if (row.dim % 32 != 0 || row.rope_dim != 0 || row.dim > 1024) return -1;
+        return (int64_t)row.dim / 2 + row.dim / 32;
     default: return -1;
     }
 }

@@ -33,7 +33,7 @@ __device__ void quant_row(int fmt, int dim, int rope, const float* __restrict__ 
         for (int c = t; c < dim + rope; c += NT) reinterpret_cast<uint16_t*>(dst)[c] = (uint16_t)bf16_rne(src[c]);
         return;
     }
-    const int blk = (fmt == MLA_FMT_E4M3_S128) ? 128 : 16;
+    const int blk = (fmt == MLA_FMT_E4M3_S128) ? 128 : (fmt == MLA_FMT_MXFP4 ? 32 : 16);
     const int nblk = dim / blk;
     for (int j = t; j < nblk; j += NT) amax_bits[j] = 0u;
     __syncthreads();
@@ -49,6 +49,13 @@ __device__ void quant_row(int fmt, int dim, int rope, const float* __restrict__ 
         for (int j = t; j < nblk; j += NT) scales[j] = u2f(amax_bits[j]) / 448.0f;
         uint16_t* ropep = reinterpret_cast<uint16_t*>(dst + dim + 4 * nblk);
         for (int r = t; r < rope; r += NT) ropep[r] = (uint16_t)bf16_rne(src[dim + r]);
+    } else if (fmt == MLA_FMT_MXFP4) {
+        for (int p = t; p < dim / 2; p += NT) {
+            const int c = 2 * p;
+            const uint32_t ab = amax_bits[c / 32], code = mx_code(ab);
+            dst[p] = (uint8_t)(mx_encode(src[c], ab, code) | (mx_encode(src[c + 1], ab, code) << 4));
+        }
+        for (int j = t; j < nblk; j += NT) dst[dim / 2 + j] = (uint8_t)mx_code(amax_bits[j]);
     } else {  // MLA_FMT_E2M1_S16
         for (int p = t; p < dim / 2; p += NT) {
             const int c = 2 * p;
@@ -65,13 +72,14 @@ __device__ void quant_row(int fmt, int dim, int rope, const float* __restrict__ 
     }
 }
 
-// The same quantisation of 128 channels (one E4M3 block, or 8 E2M1 blocks of
-// 16) by one wave, in registers: lane l holds channels 2l and 2l + 1 (v0, v1)
-// and writes their codes (E4M3: codes[2l .. 2l + 1]; E2M1: the byte codes[l]);
-// the block scale goes to `scales` (E4M3: one fp32; E2M1: 8 E4M3 bytes). Block
-// maxima are wave (E4M3) or 8-lane (E2M1) maxima of the same fp32 bit patterns
-// quant_row takes, so every byte equals quant_row's. Pointers may be global or
-// LDS; E4M3 `scales` must be 4-byte aligned.
+// The same quantisation of 128 channels (one E4M3 block, 8 E2M1 blocks of 16
+// or 4 MXFP4 blocks of 32) by one wave, in registers: lane l holds channels 2l
+// and 2l + 1 (v0, v1) and writes their codes (E4M3: codes[2l .. 2l + 1]; E2M1
+// and MXFP4: the byte codes[l]); the block scale goes to `scales` (E4M3: one
+// fp32; E2M1: 8 E4M3 bytes; MXFP4: 4 E8M0 bytes). Block maxima are wave,
+// 8-lane or 16-lane maxima of the same fp32 bit patterns quant_row takes, so
+// every byte equals quant_row's. Pointers may be global or LDS; E4M3 `scales`
+// must be 4-byte aligned.
 template <int FMT>
 __device__ __forceinline__ void quant128_wave(float v0, float v1, uint8_t* codes, uint8_t* scales) {
     const int l = threadIdx.x & 63;
@@ -98,6 +106,16 @@ __device__ __forceinline__ void quant128_wave(float v0, float v1, uint8_t* codes
         codes[l] = (uint8_t)(lo | (hi << 4));
         if ((l & 7) == 0) scales[l >> 3] = (uint8_t)sc;
     }
+}
+template <>
+__device__ __forceinline__ void quant128_wave<MLA_FMT_MXFP4>(float v0, float v1, uint8_t* codes, uint8_t* scales) {
+    const int l = threadIdx.x & 63;
+    uint32_t m = max(f2u(fabsf(v0)), f2u(fabsf(v1)));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    const uint32_t code = mx_code(m);
+    codes[l] = (uint8_t)(mx_encode(v0, m, code) | (mx_encode(v1, m, code) << 4));
+    if ((l & 15) == 0) scales[l >> 4] = (uint8_t)code;
 }
 
 // An entry cut into pieces of at most 128 channels that one wave each
@@ -127,7 +145,8 @@ __host__ inline bool pieces_supported(const AppendArgs& a) {
                           (a.main_fmt == MLA_FMT_E2M1_S16 && a.main_rope == 0)))
         return false;
     if (a.main_cache && a.main_dim % 128 != 0) return false;
-    if (a.idx_cache && !((a.idx_fmt == MLA_FMT_E4M3_S128 || a.idx_fmt == MLA_FMT_E2M1_S16) && a.idx_dim == 128))
+    if (a.idx_cache && !((a.idx_fmt == MLA_FMT_E4M3_S128 || a.idx_fmt == MLA_FMT_E2M1_S16 ||
+                          a.idx_fmt == MLA_FMT_MXFP4) && a.idx_dim == 128))
         return false;
     return reinterpret_cast<uintptr_t>(a.new_main) % 8 == 0 && reinterpret_cast<uintptr_t>(a.new_idx) % 8 == 0 &&
            reinterpret_cast<uintptr_t>(a.new_win) % 8 == 0 && (a.main_dim + a.main_rope) % 2 == 0 &&
@@ -193,6 +212,7 @@ __device__ __forceinline__ void piece_store(const AppendArgs& a, const Piece& pc
     if (pc.kind == 3) {                                    // indexer key
         uint8_t* row = a.idx_cache + pc.b * a.idx_stride + pc.slot * a.idx_row_bytes;
         if (a.idx_fmt == MLA_FMT_E4M3_S128) quant128_wave<MLA_FMT_E4M3_S128>(pc.v0, pc.v1, row, row + 128);
+        else if (a.idx_fmt == MLA_FMT_MXFP4) quant128_wave<MLA_FMT_MXFP4>(pc.v0, pc.v1, row, row + 64);
         else quant128_wave<MLA_FMT_E2M1_S16>(pc.v0, pc.v1, row, row + 64);
         return;
     }

@@ -85,6 +85,23 @@ __device__ __forceinline__ uint32_t e2m1_encode(float y) {
 }
 
 // Exact value of an E4M3 scale byte as fp32 (scales are never NaN here).
+// MXFP4 (OCP microscaling): the E8M0 code of a block whose largest magnitude
+// has the fp32 bit pattern `amax_bits` (sign clear): floor(log2 amax) - 2 + 127
+// (E2M1's largest value is 1.5 x 2^2), clamped to 0 .. 254, 0 for zeros and
+// subnormals; the scale it encodes is 2^(code - 127).
+__device__ __forceinline__ uint32_t mx_code(uint32_t amax_bits) {
+    const uint32_t e = amax_bits >> 23;
+    return e >= 2u ? min(e - 2u, 254u) : 0u;
+}
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+    return code ? u2f(code << 23) : u2f(0x00400000u);     // code 0: 2^-127, an fp32 subnormal
+}
+// The E2M1 code of x in an MXFP4 block of code `code` (x / 2^(code - 127), exact
+// scaling, then round-to-nearest-even, saturating); zero for a block of zeros.
+__device__ __forceinline__ uint32_t mx_encode(float x, uint32_t amax_bits, uint32_t code) {
+    return amax_bits ? e2m1_encode(__builtin_ldexpf(x, 127 - (int)code)) : 0u;
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
     f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false);
     return v.x;

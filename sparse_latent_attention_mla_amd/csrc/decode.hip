@@ -1069,6 +1069,10 @@ __device__ __forceinline__ float row_elem(int fmt, int dim, const uint8_t* row, 
     case MLA_FMT_E4M3_S128:
         if (c < dim) return e4m3_to_f32(row[c]) * reinterpret_cast<const float*>(row + dim)[c / 128];
         return u2f((uint32_t)reinterpret_cast<const uint16_t*>(row + dim + 4 * (dim / 128))[c - dim] << 16);
+    case MLA_FMT_MXFP4: {
+        const uint32_t byte = row[c / 2];
+        return e2m1_val((c & 1) ? (byte >> 4) : (byte & 15u)) * e8m0_to_f32(row[dim / 2 + c / 32]);
+    }
     default: {
         const uint32_t byte = row[c / 2];
         return e2m1_val((c & 1) ? (byte >> 4) : (byte & 15u)) * e4m3_to_f32(row[dim / 2 + c / 16]);

@@ -60,8 +60,9 @@ __device__ __forceinline__ void dequant_key(const uint32_t* w, uint32_t sw, u32x
             u32x2 hi = e4m3x4_to_bf16(w[2 * t + 1]);
             kb[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
-    } else {  // E2M1 x E4M3 scale, exact in bf16
-        const float s0 = e4m3_to_f32(sw & 0xFFu), s1 = e4m3_to_f32((sw >> 8) & 0xFFu);
+    } else {  // E2M1 x E4M3 scale (x E8M0 scale for MXFP4: one per 32 channels), exact in bf16
+        const float s0 = FMT == MLA_FMT_MXFP4 ? e8m0_to_f32(sw & 0xFFu) : e4m3_to_f32(sw & 0xFFu);
+        const float s1 = FMT == MLA_FMT_MXFP4 ? s0 : e4m3_to_f32((sw >> 8) & 0xFFu);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float s = (t < 2) ? s0 : s1;
@@ -71,6 +72,41 @@ __device__ __forceinline__ void dequant_key(const uint32_t* w, uint32_t sw, u32x
                           pack_bf16_trunc(v2.x * s, v2.y * s), pack_bf16_trunc(v3.x * s, v3.y * s)};
         }
     }
+}
+
+// Bytes of a 128-channel indexer row of format FMT.
+template <int FMT>
+constexpr int idx_rb() {
+    return FMT == MLA_FMT_E4M3_S128 ? 132 : (FMT == MLA_FMT_MXFP4 ? 68 : 72);
+}
+
+// The MXFP4 rounding of one query block of 32 channels, held as four vectors
+// of 8 bf16 values, in place: the block's E8M0 code from its largest magnitude,
+// E2M1 elements, values back in bf16 (exact: a rung times a power of two). With
+// MXFP4 keys the query-key product is FP4 on both sides ([P1] "DeepSeek-V4",
+// "The indexer in four bits"). Round-to-nearest-even on the E2M1 ladder is
+// rint on its grid of the binade: steps of 1/2 below 2, of 1 below 4, of 2
+// above (saturating at 6) -- the nearest rung, ties to the even code.
+__device__ __forceinline__ void mx_round_query(u32x4* q) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, max((q[i][e] << 16) & 0x7FFFFFFFu, q[i][e] & 0x7FFF0000u));
+    const uint32_t code = mx_code(m);
+    const float X = e8m0_to_f32(code);
+    const int sh = 127 - (int)code;
+    auto round1 = [&](uint32_t bits) -> uint32_t {            // fp32 bits of a bf16 value -> rounded bf16
+        const float a = __builtin_ldexpf(u2f(bits & 0x7FFFFFFFu), sh);     // |x| / X, exact, < 8
+        const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+        const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+        const float r = fminf(__builtin_rintf(a * inv) * step, 6.0f);
+        return ((f2u(r * X) >> 16) & 0x7FFFu) | ((bits >> 16) & 0x8000u);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[i][e] = round1(q[i][e] << 16) | (round1(q[i][e] & 0xFFFF0000u) << 16);
 }
 
 // ReLU on the bit pattern: a set sign bit is a negative int32 (also for -0),
@@ -139,6 +175,9 @@ __device__ __forceinline__ void load_ctx(ScanCtx<MT>& C, const ScanArgs& a, int 
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             C.qa[m][t] = *reinterpret_cast<const u32x4*>(qb + (16 * m + col) * 128 + g * 32 + t * 8);
+    if (a.fmt == MLA_FMT_MXFP4)                              // the lane holds one 32-channel block per head
+#pragma unroll
+        for (int m = 0; m < MT; ++m) mx_round_query(C.qa[m]);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -159,7 +198,7 @@ __device__ __forceinline__ void flush_hist(const uint32_t* hist, uint32_t* hb) {
 // k-step t is channel g*32 + t*8 + e, for A and B alike).
 template <int FMT, int MT>
 __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int rows_per_block) {
-    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int RB = idx_rb<FMT>();
     constexpr int kChunkBytes = kChunkRows * RB;
     constexpr int kLoads = (kChunkBytes + 64 * 16 - 1) / (64 * 16);
     __shared__ uint32_t hist[kHistBins];
@@ -248,7 +287,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 16)[i];
-                sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
+                sw = FMT == MLA_FMT_MXFP4 ? (uint32_t)rp[64 + g] : *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
             }
             u32x4 kb[4];
             dequant_key<FMT>(w, sw, kb);
@@ -296,7 +335,7 @@ __device__ __forceinline__ void flush_fine_coarse(const uint32_t (&cnt)[kHistBin
 // bins, and is flushed by consecutive threads into consecutive bins.
 template <int FMT, int MT, int NBUF>
 __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(ScanArgs a, int rows_per_block) {
-    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int RB = idx_rb<FMT>();
     constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
     constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
     constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries + weights
@@ -361,6 +400,17 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
     if (NBUF == 3 && issued == 2) wait_vmcnt<2 * KI>();    // the queries have landed
     else if (issued >= 1) wait_vmcnt<KI>();
     else wait_vmcnt<0>();
+    if constexpr (FMT == MLA_FMT_MXFP4) {                  // FP4 queries: each wave rounds its staged head tile
+        if (wave < MT) {                                   // (lane: head lane / 4, 32-channel block lane % 4)
+            uint8_t* hq = &ring[wave][NBUF - 1][0] + (lane >> 2) * 256 + (lane & 3) * 64;
+            u32x4 qb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const u32x4*>(hq + 16 * i);
+            mx_round_query(qb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(hq + 16 * i) = qb[i];
+        }
+    }
     __syncthreads();                                       // queries, weights staged; histograms cleared
     ScanCtx<MT> C;
 #pragma unroll
@@ -401,7 +451,7 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + g * 16)[i];
-            sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
+            sw = FMT == MLA_FMT_MXFP4 ? (uint32_t)rp[64 + g] : *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * g);
         }
         dequant_key<FMT>(w, sw, in.kb);
     };
@@ -477,7 +527,7 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
 template <int FMT, int MT2, int NBUF, int NW, bool FUSE>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block, AppendArgs ap) {
     constexpr int NT = 64 * NW;                          // threads of the block
-    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int RB = idx_rb<FMT>();
     constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
     constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
     constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries + weights
@@ -595,6 +645,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     if (NBUF == 3 && issued == 2) wait_vmcnt<2 * KI>();
     else if (issued >= 1) wait_vmcnt<KI>();
     else wait_vmcnt<0>();
+    if constexpr (FMT == MLA_FMT_MXFP4) {                  // FP4 queries: each wave rounds its staged head tile
+        if (wave < 2 * MT2) {                              // (lane: head lane / 4, 32-channel block lane % 4)
+            uint8_t* hq = &ring[wave][NBUF - 1][0] + (lane >> 2) * 272 + (lane & 3) * 64;
+            u32x4 qb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const u32x4*>(hq + 16 * i);
+            mx_round_query(qb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(hq + 16 * i) = qb[i];
+        }
+    }
     __syncthreads();                                       // queries, weights staged; histograms cleared
     if constexpr (FUSE) {
 #pragma unroll
@@ -650,9 +711,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
             uint32_t w[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 32 * h)[i];
-            const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
-            dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
-            dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+            if constexpr (FMT == MLA_FMT_MXFP4) {               // one E8M0 byte per 32 channels
+                const uint32_t sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * h);
+                dequant_key<FMT>(w, sw & 0xFFu, in.kb);
+                dequant_key<FMT>(w + 4, sw >> 8, in.kb + 4);
+            } else {
+                const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
+                dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
+                dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+            }
         }
     };
     ChunkIn cur;
@@ -743,7 +810,7 @@ template <int FMT, int MT2, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int lg_groups) {
     constexpr int NBUF = 3;
     constexpr int NT = 64 * NW;
-    constexpr int RB = (FMT == MLA_FMT_E4M3_S128) ? 132 : 72;
+    constexpr int RB = idx_rb<FMT>();
     constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
     constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
     constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries
@@ -839,6 +906,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
     } else {
         wait_vmcnt_asm<0>();
     }
+    if constexpr (FMT == MLA_FMT_MXFP4) {                  // FP4 queries: each wave rounds its staged head tile
+        if (wave < 2 * MT2) {                              // (lane: head lane / 4, 32-channel block lane % 4)
+            uint8_t* hq = &ring[wave][NBUF - 1][0] + (lane >> 2) * 272 + (lane & 3) * 64;
+            u32x4 qb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const u32x4*>(hq + 16 * i);
+            mx_round_query(qb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(hq + 16 * i) = qb[i];
+        }
+    }
     __syncthreads();                                       // queries, weights staged; histograms cleared
     u32x4 qa[MT2][8];
     float wv[MT2][16];
@@ -875,9 +953,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
             uint32_t w[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 32 * h)[i];
-            const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
-            dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
-            dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+            if constexpr (FMT == MLA_FMT_MXFP4) {
+                const uint32_t sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * h);
+                dequant_key<FMT>(w, sw & 0xFFu, in.kb);
+                dequant_key<FMT>(w + 4, sw >> 8, in.kb + 4);
+            } else {
+                const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
+                dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
+                dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+            }
         }
     };
 
@@ -1054,8 +1138,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_cand(ScanArgs a) {
         pos[t] = ent[t] < n ? cand[ent[t]] : -1;
     }
     // the row loads: E4M3 8 words of codes + the fp32 scale, E2M1 4 words of
-    // nibbles + the two scale bytes of the lane's channels, bf16 four 16-byte vectors
-    constexpr int NW = (FMT == MLA_FMT_E4M3_S128) ? 8 : (FMT == MLA_FMT_E2M1_S16 ? 4 : 16);
+    // nibbles + the two scale bytes of the lane's channels (MXFP4: one byte),
+    // bf16 four 16-byte vectors
+    constexpr int NW = (FMT == MLA_FMT_E4M3_S128) ? 8 : (FMT == MLA_FMT_BF16 ? 16 : 4);
     uint32_t w[kCandTiles][NW];
     uint32_t sw[kCandTiles];
 #pragma unroll
@@ -1075,6 +1160,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_cand(ScanArgs a) {
             w[t][2] = hi.x;
             w[t][3] = hi.y;
             sw[t] = valid[t] ? *reinterpret_cast<const uint16_t*>(row + 64 + 2 * g) : 0u;
+        } else if constexpr (FMT == MLA_FMT_MXFP4) {          // 68-byte rows: 4-byte aligned
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(row + g * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[t][i] = valid[t] ? p[i] : 0u;
+            sw[t] = valid[t] ? (uint32_t)row[64 + g] : 0u;
         } else {
             const u32x4* p = reinterpret_cast<const u32x4*>(row + g * 64);
 #pragma unroll
@@ -1130,6 +1220,10 @@ __device__ __forceinline__ float key_elem(int fmt, int dim, const uint8_t* row, 
     case MLA_FMT_BF16: return u2f((uint32_t)reinterpret_cast<const uint16_t*>(row)[c] << 16);
     case MLA_FMT_E4M3_S128:
         return e4m3_to_f32(row[c]) * reinterpret_cast<const float*>(row + dim)[c / 128];
+    case MLA_FMT_MXFP4: {
+        const uint32_t byte = row[c / 2];
+        return e2m1_value((c & 1) ? (byte >> 4) : (byte & 15u)) * e8m0_to_f32(row[dim / 2 + c / 32]);
+    }
     default: {
         const uint32_t byte = row[c / 2];
         return e2m1_value((c & 1) ? (byte >> 4) : (byte & 15u)) * e4m3_to_f32(row[dim / 2 + c / 16]);
@@ -1146,6 +1240,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_generic(ScanArgs a) {
         qs[i] = (a.fmt == MLA_FMT_F32)
                     ? reinterpret_cast<const float*>(a.q_idx)[(int64_t)b * n + i]
                     : u2f((uint32_t)reinterpret_cast<const uint16_t*>(a.q_idx)[(int64_t)b * n + i] << 16);
+    }
+    if (a.fmt == MLA_FMT_MXFP4) {                             // FP4 queries: each 32-channel block rounded
+        __syncthreads();
+        for (int blk = threadIdx.x; blk < n / 32; blk += kScanThreads) {
+            uint32_t m = 0;
+            for (int c = 0; c < 32; ++c) m = max(m, f2u(fabsf(qs[32 * blk + c])));
+            const uint32_t code = mx_code(m);
+            for (int c = 0; c < 32; ++c) {
+                const uint32_t nib = mx_encode(qs[32 * blk + c], m, code);
+                qs[32 * blk + c] = e2m1_value(nib) * e8m0_to_f32(code);
+            }
+        }
     }
     for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
     __syncthreads();
@@ -1177,7 +1283,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_generic(ScanArgs a) {
 
 bool scan_supported(int fmt, int dim, int H_I) {
     if (H_I <= 0) return false;
-    if ((fmt == MLA_FMT_BF16 || fmt == MLA_FMT_E4M3_S128 || fmt == MLA_FMT_E2M1_S16) && dim == 128 &&
+    if ((fmt == MLA_FMT_BF16 || fmt == MLA_FMT_E4M3_S128 || fmt == MLA_FMT_E2M1_S16 || fmt == MLA_FMT_MXFP4) &&
+        dim == 128 &&
         H_I % 16 == 0 && H_I <= 64)
         return true;
     return H_I * dim <= 8192;
@@ -1195,7 +1302,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         }
         return hipSuccess;
     };
-    const bool mfma = (a.fmt == MLA_FMT_BF16 || a.fmt == MLA_FMT_E4M3_S128 || a.fmt == MLA_FMT_E2M1_S16) &&
+    const bool mfma = (a.fmt == MLA_FMT_BF16 || a.fmt == MLA_FMT_E4M3_S128 || a.fmt == MLA_FMT_E2M1_S16 ||
+                       a.fmt == MLA_FMT_MXFP4) &&
                       a.dim == 128 && a.H_I % 16 == 0 && a.H_I <= 64;
     if (a.cand) {                                              // a candidate pool: n_cand entries per sequence
         if (const hipError_t e = unfused(); e != hipSuccess) return e;
@@ -1212,6 +1320,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
             MLA_CAND_CASE(MLA_FMT_E4M3_S128, 3) MLA_CAND_CASE(MLA_FMT_E4M3_S128, 4)
             MLA_CAND_CASE(MLA_FMT_E2M1_S16, 1) MLA_CAND_CASE(MLA_FMT_E2M1_S16, 2)
             MLA_CAND_CASE(MLA_FMT_E2M1_S16, 3) MLA_CAND_CASE(MLA_FMT_E2M1_S16, 4)
+            MLA_CAND_CASE(MLA_FMT_MXFP4, 1) MLA_CAND_CASE(MLA_FMT_MXFP4, 2)
+            MLA_CAND_CASE(MLA_FMT_MXFP4, 3) MLA_CAND_CASE(MLA_FMT_MXFP4, 4)
 #undef MLA_CAND_CASE
             return hipErrorInvalidValue;
         }
@@ -1304,6 +1414,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         MLA_SCAN_CASE(MLA_FMT_E4M3_S128, 3) MLA_SCAN_CASE(MLA_FMT_E4M3_S128, 4)
         MLA_SCAN_CASE(MLA_FMT_E2M1_S16, 1) MLA_SCAN_CASE(MLA_FMT_E2M1_S16, 2)
         MLA_SCAN_CASE(MLA_FMT_E2M1_S16, 3) MLA_SCAN_CASE(MLA_FMT_E2M1_S16, 4)
+        MLA_SCAN_CASE(MLA_FMT_MXFP4, 1) MLA_SCAN_CASE(MLA_FMT_MXFP4, 2)
+        MLA_SCAN_CASE(MLA_FMT_MXFP4, 3) MLA_SCAN_CASE(MLA_FMT_MXFP4, 4)
 #undef MLA_SCAN_CASE
         return hipErrorInvalidValue;
     }

@@ -44,6 +44,7 @@ def test_row_bytes_and_status_strings(M):
     assert M.row_bytes(R(M.E4M3_S128, 128)) == 132
     assert M.row_bytes(R(M.E2M1_S16, 512)) == 288
     assert M.row_bytes(R(M.E2M1_S16, 128)) == 72
+    assert M.row_bytes(R(M.MXFP4, 128)) == 68 and M.row_bytes(R(M.MXFP4, 48)) == -1
     assert M.row_bytes(R(M.BF16, 512, 64)) == 1152
     assert M.row_bytes(R(M.F32, 64, 16)) == 320
     assert M.row_bytes(R(M.E2M1_S16, 512, 64)) == -1          # no separate RoPE part in FP4 rows

@@ -27,12 +27,13 @@ SMALL = {
     "c2s": C["c2"].with_(name="c2s", cid=102, B=2, N=5003),
     "c3s": C["c3"].with_(name="c3s", cid=103, B=2, N=6001),
     "c4s": C["c4"].with_(name="c4s", cid=104, B=2, N=4099),
+    "c4xs": C["c4x"].with_(name="c4xs", cid=106, B=2, N=5021),
     "c5s": C["c5"].with_(name="c5s", cid=105, B=1, N=3001),
     # sizes at which every wave of the queue-fed scan draws several tickets
     "c3m": C["c3"].with_(name="c3m", cid=113, B=3, N=40001),
     "c4m": C["c4"].with_(name="c4m", cid=114, B=1, N=70001),
 }
-FULL = {n: C[n] for n in ("c2", "c3", "c4", "c5")}
+FULL = {n: C[n] for n in ("c2", "c3", "c4", "c4x", "c5")}
 
 
 def say(*a):
@@ -129,7 +130,7 @@ def test_step_end_to_end(name):
                 G.check_attention(got_o[b:b + 1], got_l[b:b + 1], ref_o[b:b + 1], ref_l[b:b + 1])
 
 
-@pytest.mark.parametrize("name", ["c1", "c3s", "c4s"])
+@pytest.mark.parametrize("name", ["c1", "c3s", "c4s", "c4xs"])
 def test_causal_mask_and_short_contexts(name):
     case = case_of(name)
     cfg = case.cfg
@@ -191,7 +192,7 @@ def test_decode_head_counts(name, H):
 
 
 @pytest.mark.parametrize("path", ["row", "multi"])
-@pytest.mark.parametrize("fmt", [G.O.E4M3_S128, G.O.E2M1_S16, G.O.BF16])
+@pytest.mark.parametrize("fmt", [G.O.E4M3_S128, G.O.E2M1_S16, G.O.MXFP4, G.O.BF16])
 @pytest.mark.parametrize("k", [1, 37, 2048])
 def test_topk_exact_ties(fmt, k, path, monkeypatch):
     """Scores that are exact integers on both sides: integer queries and weights, and
@@ -206,7 +207,7 @@ def test_topk_exact_ties(fmt, k, path, monkeypatch):
     distinct = rng.choice(np.array([-3, -2, -1, 0, 1, 2, 3], np.float32), (B, 997, d))
     if fmt == G.O.E4M3_S128:
         distinct[:, :, 5] = 448.0
-    elif fmt == G.O.E2M1_S16:
+    elif fmt in (G.O.E2M1_S16, G.O.MXFP4):                          # (MXFP4: queries of +-1 stay exact)
         distinct[:, :, ::16] = 6.0
     rows = np.ascontiguousarray(distinct[:, np.arange(N) % 997])          # each row repeats ~5 times
     q_idx = rng.choice(np.array([-1, 0, 1], np.float32), (B, H_I, d))
@@ -251,7 +252,8 @@ def test_quantise_bitexact_over_magnitudes():
     x[0, 64:80] *= np.float32(1e-30)
     x[0, 80:96, :] = rng.choice([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], (16, 576)).astype(np.float32)
     for fmt, dim, rope in ((G.O.E4M3_S128, 512, 64), (G.O.E2M1_S16, 512, 0), (G.O.BF16, 512, 64),
-                           (G.O.E4M3_S128, 128, 0), (G.O.E2M1_S16, 128, 0), (G.O.F32, 64, 16)):
+                           (G.O.E4M3_S128, 128, 0), (G.O.E2M1_S16, 128, 0), (G.O.MXFP4, 128, 0),
+                           (G.O.MXFP4, 512, 0), (G.O.F32, 64, 16)):
         say("quantise", fmt, dim, rope)
         D = dim + rope
         src = np.ascontiguousarray(x[:, :, :D])
@@ -336,7 +338,7 @@ def test_scan_work_queues(name, scan, monkeypatch):
 
 
 @pytest.mark.parametrize("slots_kind", ["step", "spread"])
-@pytest.mark.parametrize("name", ["c3s", "c4s", "c3m", "c2s", "c1"])
+@pytest.mark.parametrize("name", ["c3s", "c4s", "c4xs", "c3m", "c2s", "c1"])
 def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
     """mla_append_indexer_topk against mla_kv_append_quant then mla_indexer_topk on
     copies of the same caches whose new slots hold stale bytes: the caches and the

@@ -248,7 +248,7 @@ def test_reindex_over_the_full_layers_pool(name):
         check_pool_topk(idx_p, ref_p, pos, nv, k)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c4xs"])
 def test_topk_over_arbitrary_pools(name):
     """Pools that are not block runs: shuffled distinct positions mixed with
     -1, other negatives, positions past n_visible and past the capacity; sizes

@@ -31,7 +31,7 @@ LIB = os.path.join(HERE, "libsynth.so")
 T_MAIN, T_IDX, T_Q, T_QIDX, T_W, T_WIN = 1, 2, 3, 4, 5, 6
 
 # row formats (numbering used by the library and the oracle alike)
-F32, BF16, E4M3_S128, E2M1_S16 = 0, 1, 2, 3
+F32, BF16, E4M3_S128, E2M1_S16, MXFP4 = 0, 1, 2, 3, 4
 
 
 def build(verbose=False):
@@ -142,6 +142,11 @@ CONFIGS = {
                  k=512, main_fmt=E2M1_S16, idx_fmt=E2M1_S16, W=128, softmax_scale=512 ** -0.5,
                  desc="V4.1-Flash format, one Full layer: B=4, T=262144, FP4 rows (288 B / 72 B), "
                       "64 heads x 512, indexer 64x128, top-512, 128-entry bf16 window"),
+    "c4x": Config("c4x", 6, B=4, N=262144, H=64, dim=512, rope=0, d_v=512, H_I=64, d_I=128,
+                  k=512, main_fmt=E2M1_S16, idx_fmt=MXFP4, W=128, softmax_scale=512 ** -0.5,
+                  desc="c4 with V4's MXFP4 indexer: B=4, T=262144, FP4 main rows (288 B), MXFP4 "
+                       "indexer keys (68 B) and FP4 query-key products, 64 heads x 512, indexer 64x128, "
+                       "top-512, 128-entry bf16 window"),
     "c5": Config("c5", 5, B=1, N=524288, H=64, dim=512, rope=0, d_v=512, H_I=64, d_I=128,
                  k=512, main_fmt=E2M1_S16, idx_fmt=E2M1_S16, W=128, m=2,
                  layers=("full", "reindex", "reuse", "reuse", "reuse", "reuse"),
@@ -242,4 +247,6 @@ def _row_bytes(fmt, dim, rope):
         return dim + 4 * (dim // 128) + 2 * rope
     if fmt == E2M1_S16:
         return dim // 2 + dim // 16
+    if fmt == MXFP4:
+        return dim // 2 + dim // 32
     raise ValueError(fmt)

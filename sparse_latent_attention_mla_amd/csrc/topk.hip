@@ -297,13 +297,77 @@ __device__ void radix_take_bins(P c, uint32_t ncand, int T, uint32_t nT, bool ab
     if (need > 0) take_pass(true);
 }
 
-// Among the candidates c[0 .. ncand), all in one top-12-bit bin, append the
-// positions of the `need` largest to out from the LDS cursor on.
+// Among the candidates c[0 .. ncand) (all in one top-12-bit bin), append the
+// positions of the `need` largest to out from the LDS cursor on: the same radix
+// passes over a list that holds bin T only (a separate function: folding it into
+// radix_take_bins cost the two-kernel selection 1.5 us per call, measured).
 template <int NT, typename P, typename OUT>
 __device__ void radix_take(P c, uint32_t ncand, uint32_t need, uint32_t want, OUT out,
                            uint32_t* cursor, uint32_t (*h)[kMaxDigitBins], uint32_t* res) {
-    if (ncand == 0 || need == 0) return;
-    radix_take_bins<NT>(c, ncand, (int)(c[0] >> 52), ncand, false, need, want, out, cursor, h, res);
+    const int t = threadIdx.x, lane = t & 63;
+    const bool radix = need > 0 && need < ncand;
+    uint64_t prefix = radix ? (c[0] & (0xFFFull << 52)) : 0ull, mask = 0xFFFull << 52;
+    uint32_t rem = need;
+    int par = 0;
+    auto pass = [&](int shift, int bits) {
+        const int nb = 1 << bits;
+        uint32_t* hc = h[par];
+        for (uint32_t i = t; i < ncand; i += NT) {
+            const uint64_t v = c[i];
+            if ((v & mask) == prefix) atomicAdd(&hc[(v >> shift) & (uint64_t)(nb - 1)], 1u);
+        }
+        lds_barrier();
+        if (t < 64) {                                    // one wave finds the digit
+            const DigitResult r = wave_find_digit(hc, nb, rem);
+            if (lane == 0) {
+                res[0] = (uint32_t)r.digit;
+                res[1] = r.above;
+                res[2] = r.count;
+            }
+        } else {                                         // the others clear the next histogram
+            for (int i = t - 64; i < kMaxDigitBins; i += NT - 64) h[par ^ 1][i] = 0u;
+        }
+        lds_barrier();
+        const int d = (int)res[0];
+        prefix |= (uint64_t)d << shift;
+        mask |= (uint64_t)(nb - 1) << shift;
+        rem -= res[1];
+        par ^= 1;
+        return res[2];                                   // candidates sharing the prefix so far
+    };
+    if (radix) {
+        pass(42, 10);
+        const uint32_t eq = pass(32, 10);                // prefix now holds the exact threshold score
+        if (rem < eq) {                                  // ties at that score: smaller positions first
+            pass(24, 8);
+            pass(16, 8);
+            pass(8, 8);
+            pass(0, 8);
+        }
+    }
+    // "v >= prefix" takes exactly `need`: every candidate above the threshold score,
+    // and at it either all (score resolved, count fits) or those above the exact composite
+    if (need > 0) {
+        const uint32_t n_iter = (ncand + NT - 1) / NT;
+        for (uint32_t it = 0; it < n_iter; ++it) {
+            const uint32_t i = it * NT + t;
+            bool take = false;
+            int32_t pos = 0;
+            if (i < ncand) {
+                const uint64_t v = c[i];
+                take = !radix || v >= prefix;
+                pos = (int32_t)(~(uint32_t)(v & 0xFFFFFFFFull));
+            }
+            const uint64_t m = __ballot(take);
+            uint32_t base = 0;
+            if (lane == 0 && m) base = atomicAdd(cursor, (uint32_t)__popcll(m));
+            base = __shfl(base, 0, 64);
+            if (take) {
+                const uint32_t o = base + lanes_below(m);
+                if (o < want) out.put(o, pos);
+            }
+        }
+    }
 }
 
 struct FinalLds {

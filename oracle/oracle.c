@@ -559,6 +559,13 @@ int orc_pool(const float* scores, int64_t n_rows, const int32_t* n_visible, int 
  *   o[c] = sum_u exp(z_u - lse) * K_u[c],  c < d_v  (V = the leading d_v channels:
  *          the 512 latent channels for V3.2, the whole row when K = V)
  * An empty U gives lse = -inf and o = 0.
+ * With attention sinks ([P2] Part 2 "The sliding window", "Attention sinks":
+ * one learned scalar per head is appended to each row of scaled scores as an
+ * extra column before the softmax and dropped after it; the column has no
+ * value vector), sinks[h] joins the normaliser only:
+ *   lse  = log(sum_u exp(z_u) + exp(sinks[h])),  o[c] = sum_u exp(z_u - lse) * K_u[c]
+ * so the weights of U sum to 1 - p_sink; an empty U gives lse = sinks[h], o = 0.
+ * sinks == NULL (or -inf) is the plain softmax.
  * Window rows are bf16, [B, W, dim+rope].
  * Pins: absorbed = naive MLA with explicit up-projections; k >= visible rows
  * equals dense softmax attention; LSE merge of any partition equals the whole;
@@ -567,7 +574,7 @@ int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                   const float* q, const uint8_t* main_cache, int64_t main_seq_stride, int64_t capacity,
                   const int32_t* idx, int k,
                   const uint16_t* win_ring, const int32_t* win_len, int W,
-                  float softmax_scale, int B, int H, float* out, float* lse) {
+                  float softmax_scale, const float* sinks, int B, int H, float* out, float* lse) {
     int D = main_dim + main_rope;
     int64_t rb = orc_row_bytes(main_fmt, main_dim, main_rope);
     int b;
@@ -606,6 +613,7 @@ int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                 const float* qh = q + ((int64_t)b * H + h) * D;
                 double* z = (double*)malloc(sizeof(double) * (size_t)(nu > 0 ? nu : 1));
                 double m = -INFINITY, sum = 0.0, l;
+                double sk = sinks ? (double)sinks[h] : -INFINITY;   /* the sink column's logit */
                 int uu, c;
                 for (uu = 0; uu < nu; uu++) {
                     double d = 0.0;
@@ -613,13 +621,15 @@ int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                     z[uu] = (double)softmax_scale * d;
                     if (z[uu] > m) m = z[uu];
                 }
-                if (nu == 0) {
+                if (sk > m) m = sk;
+                if (m == -INFINITY) {
                     lse[(int64_t)b * H + h] = -INFINITY;
                     for (c = 0; c < d_v; c++) out[((int64_t)b * H + h) * d_v + c] = 0.0f;
                     free(z);
                     continue;
                 }
                 for (uu = 0; uu < nu; uu++) sum += exp(z[uu] - m);
+                if (sk > -INFINITY) sum += exp(sk - m);
                 l = m + log(sum);
                 lse[(int64_t)b * H + h] = (float)l;
                 for (c = 0; c < d_v; c++) {

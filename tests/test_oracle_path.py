@@ -371,3 +371,33 @@ def test_window_branch_and_empty_set():
     # empty set: lse -inf, o = 0
     o3, l3 = O.attention((O.E2M1_S16, 512, 0), 512, q, rows, none, 0.05, ring, np.zeros(B, np.int32))
     assert np.all(np.isneginf(l3)) and np.all(o3 == 0)
+
+
+def test_attention_sinks_follow_the_pages_formulation():
+    """Attention sinks: one logit per head appended to the scaled scores as an
+    extra column before the softmax and dropped after it (the pages' concat /
+    softmax / slice), brute force with the library softmax; a -inf sink is the
+    plain softmax; the relation to the sink-free result; an empty set keeps all
+    mass on the sink (lse = sink, out = 0)."""
+    rng = np.random.default_rng(29)
+    B, H, N, k, scale = 1, 5, 60, 25, 0.09
+    x = rng.standard_normal((B, N, 64)).astype(np.float32)
+    rows = O.quant_rows(O.F32, 64, 0, x)                         # exact rows
+    q = rng.standard_normal((B, H, 64)).astype(np.float32)
+    idx = rng.permutation(N)[:k].astype(np.int32)[None]
+    sinks = np.array([-1.5, 0.0, 2.0, 30.0, -np.inf], np.float32)
+    o, l = O.attention((O.F32, 64, 0), 64, q, rows, idx, scale, sinks=sinks)
+    K = x[0, idx[0]].astype(np.float64)
+    for h in range(H):
+        z = scale * (K @ q[0, h].astype(np.float64))
+        p = softmax(np.concatenate([z, [float(sinks[h])]]))[:-1]
+        np.testing.assert_allclose(o[0, h], p @ K, rtol=1e-5, atol=1e-7)
+        np.testing.assert_allclose(l[0, h], logsumexp(np.concatenate([z, [float(sinks[h])]])), rtol=1e-6)
+    o0, l0 = O.attention((O.F32, 64, 0), 64, q, rows, idx, scale)
+    assert np.array_equal(o[0, 4], o0[0, 4]) and l[0, 4] == l0[0, 4]          # -inf sink = none
+    ls = np.logaddexp(l0.astype(np.float64), sinks.astype(np.float64)[None])
+    np.testing.assert_allclose(l, ls, rtol=1e-6)
+    np.testing.assert_allclose(o, o0 * np.exp(l0 - ls)[..., None], rtol=1e-5, atol=1e-7)
+    assert np.abs(o[0, 3]).max() < 1e-6 * np.abs(o0[0, 3]).max()               # a dominant sink
+    oe, le = O.attention((O.F32, 64, 0), 64, q, rows, -np.ones((1, 4), np.int32), scale, sinks=sinks)
+    assert np.all(oe == 0) and np.array_equal(le[0], sinks)

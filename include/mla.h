@@ -322,6 +322,12 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
  *              are attended twice
  *  win_ring    optional bf16 [B, W, dim+rope] window entries (K = V), with
  *  win_len     int32 [B] in [0, W], the number of valid ring slots (slots 0..len-1)
+ *  sinks       optional fp32 [H] attention-sink logits, one per head, shared by the batch
+ *              ([P2] Part 2 "The sliding window", "Attention sinks": an extra score column
+ *              with no value vector), in the units of the scaled scores z; NULL = none.
+ *              With sinks, lse = log(sum_u exp(z_u) + exp(sinks[h])) and out = sum_u exp(z_u - lse)
+ *              K_u[0 : d_v] (the weights of U sum to 1 - p_sink); an empty U gives lse =
+ *              sinks[h] and out = 0.
  *  out         fp32 [B, H, d_v];  lse fp32 [B, H]
  *  workspace   at least mla_sparse_decode_workspace(main_row, d_v, B, H, k, W) bytes,
  *              256-byte aligned
@@ -335,7 +341,7 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
                                const void* main_cache, int64_t main_seq_stride, int64_t capacity,
                                const int32_t* idx, int32_t k,
                                const void* win_ring, const int32_t* win_len, int32_t W,
-                               float softmax_scale, int32_t B, int32_t H,
+                               float softmax_scale, const float* sinks, int32_t B, int32_t H,
                                float* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 

@@ -70,7 +70,7 @@ def lib():
         L.mla_indexer_pool.restype = i32
         L.mla_sparse_decode_workspace.argtypes = [_CRow, i32, i32, i32, i32, i32]
         L.mla_sparse_decode_workspace.restype = sz
-        L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, f32, i32, i32,
+        L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, f32, P, i32, i32,
                                         P, P, P, sz, P]
         L.mla_sparse_decode.restype = i32
         _lib = L
@@ -313,10 +313,11 @@ def mla_sparse_decode_workspace(main_row: Row, d_v: int, B: int, H: int, k: int,
 
 
 def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
-                      workspace=None, win_ring=None, win_len=None, stream=None):
+                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None):
     """Sparse absorbed-MLA decode.  q [B, H, D] (bf16; fp32 for F32 rows), main_cache uint8
     [B, capacity, row_bytes], idx int32 [B, k], out fp32 [B, H, d_v], lse fp32 [B, H];
-    win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch."""
+    win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch; sinks fp32 [H]
+    attention-sink logits (optional)."""
     _need(q, "q", query_dtype(main_row), 3)
     _need(idx, "idx", torch.int32, 2)
     _need(out, "out", torch.float32, 3)
@@ -336,7 +337,11 @@ def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale
         W = win_ring.shape[1]
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
+    if sinks is not None:
+        _need(sinks, "sinks", torch.float32, 1)
+        if tuple(sinks.shape) != (H,):
+            raise ValueError("sinks [H] expected")
     _check(lib().mla_sparse_decode(
         _crow(main_row), d_v, _ptr(q), _ptr(main_cache), stride, main_cache.shape[1], _ptr(idx), idx.shape[1],
-        _ptr(win_ring), _ptr(win_len), W, float(softmax_scale), B, H, _ptr(out), _ptr(lse),
+        _ptr(win_ring), _ptr(win_len), W, float(softmax_scale), _ptr(sinks), B, H, _ptr(out), _ptr(lse),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))

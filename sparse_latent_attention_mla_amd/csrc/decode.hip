@@ -984,12 +984,32 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
 // Up to kMergeFast splits, every load (logsumexps and partials) is issued at
 // once, from clamped in-bounds addresses, so the block pays one memory round trip.
 constexpr int kMergeFast = 16;
+// With attention sinks the head's sink logit joins the normaliser (no value
+// vector): out scales by exp(lse_U - lse) and lse = logaddexp(lse_U, sink).
+__device__ __forceinline__ void merge_finish(float m, float tot, float4 acc, const float* sinks, int h, float4* o,
+                                            float* lse_out, int t) {
+    if (sinks) {
+        const float sk = sinks[h];
+        if (sk > -__builtin_inff()) {
+            const float M = fmaxf(m, sk), f = __expf(m - M);
+            tot = tot * f + __expf(sk - M);
+            acc = make_float4(acc.x * f, acc.y * f, acc.z * f, acc.w * f);
+            m = M;
+        }
+    }
+    const float inv = 1.0f / tot;
+    *o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (t == 0) *lse_out = m + __logf(tot);
+}
+
 __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part, float* __restrict__ out,
-                                                         float* __restrict__ lse) {
+                                                         float* __restrict__ lse, const float* __restrict__ sinks) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int t = threadIdx.x;
     const float* lp = lse_part + (int64_t)b * S * H + h;
+    // an empty set: all mass on the sink (lse = the sink's logit, -inf without one)
+    const float empty_lse = sinks ? sinks[h] : -__builtin_inff();
     if (S <= kMergeFast) {
         const float4* op = reinterpret_cast<const float4*>(o_part + ((int64_t)b * S * H + h) * kDv) + t;
         const int64_t step = (int64_t)H * (kDv / 4);
@@ -1008,7 +1028,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
         float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * kDv) + t;
         if (m == -__builtin_inff()) {
             *o = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t == 0) lse[(int64_t)b * H + h] = -__builtin_inff();
+            if (t == 0) lse[(int64_t)b * H + h] = empty_lse;
             return;
         }
         float tot = 0.0f;
@@ -1022,9 +1042,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
             acc.z += wv * pv[s].z;
             acc.w += wv * pv[s].w;
         }
-        const float inv = 1.0f / tot;
-        *o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-        if (t == 0) lse[(int64_t)b * H + h] = m + __logf(tot);
+        merge_finish(m, tot, acc, sinks, h, o, &lse[(int64_t)b * H + h], t);
         return;
     }
     float m = -__builtin_inff();
@@ -1032,7 +1050,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
     float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * kDv) + t;
     if (m == -__builtin_inff()) {
         *o = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (t == 0) lse[(int64_t)b * H + h] = -__builtin_inff();
+        if (t == 0) lse[(int64_t)b * H + h] = empty_lse;
         return;
     }
     const float4* op = reinterpret_cast<const float4*>(o_part + ((int64_t)b * S * H + h) * kDv) + t;
@@ -1049,9 +1067,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
         acc.z += wv * v.z;
         acc.w += wv * v.w;
     }
-    const float inv = 1.0f / tot;
-    *o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (t == 0) lse[(int64_t)b * H + h] = m + __logf(tot);
+    merge_finish(m, tot, acc, sinks, h, o, &lse[(int64_t)b * H + h], t);
 }
 
 // ------------------------------------------------------------------------
@@ -1123,6 +1139,8 @@ __global__ __launch_bounds__(kGenericThreads) void k_decode_generic(DecodeArgs a
     __syncthreads();
     mx = red[0];
     for (int i = 1; i < kGenericThreads / 64; ++i) mx = fmaxf(mx, red[i]);
+    const float sink = a.sinks ? a.sinks[h] : -__builtin_inff();   // the sink column's logit
+    mx = fmaxf(mx, sink);
     __syncthreads();
     float* o = a.out + ((int64_t)b * a.H + h) * a.d_v;
     if (mx == -__builtin_inff()) {
@@ -1141,6 +1159,7 @@ __global__ __launch_bounds__(kGenericThreads) void k_decode_generic(DecodeArgs a
     __syncthreads();
     sum = 0.0f;
     for (int i = 0; i < kGenericThreads / 64; ++i) sum += red[i];
+    if (sink > -__builtin_inff()) sum += __expf(sink - mx);
     for (int c = t; c < a.d_v; c += kGenericThreads) {
         float acc = 0.0f;
         for (int u = 0; u < n; ++u) {
@@ -1231,7 +1250,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     const ProfSlot p = prof_slot(PROF_MERGE);
     return launch_kernel(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, p.start, p.stop, S, a.H, o_part,
-                         lse_part, a.out, a.lse);
+                         lse_part, a.out, a.lse, a.sinks);
 }
 
 }  // namespace mla

@@ -117,6 +117,7 @@ struct DecodeArgs {
     const int32_t* win_len;
     int W;
     float scale;
+    const float* sinks;     // [H] attention-sink logits, or null
     int B, H;
     float* out;             // [B, H, d_v]
     float* lse;             // [B, H]

@@ -124,11 +124,12 @@ def oracle_scores(case: Case, layer_idx: int = 0, n_visible=None, cand=None):
                             cfg.sigma, case.o_idx, nv, cand=cand)
 
 
-def oracle_attention(case: Case, layer: int, idx: np.ndarray):
+def oracle_attention(case: Case, layer: int, idx: np.ndarray, sinks=None, with_window=True):
     cfg = case.cfg
-    win = case.o_win[layer] if cfg.W else None
+    use_w = with_window and cfg.W > 0
+    win = case.o_win[layer] if use_w else None
     return O.attention((cfg.main_fmt, cfg.dim, cfg.rope), cfg.d_v, case.inp.q[layer], case.o_main, idx,
-                       cfg.softmax_scale, win, case.win_len if cfg.W else None)
+                       cfg.softmax_scale, win, case.win_len if use_w else None, sinks=sinks)
 
 
 # ---- GPU calls ------------------------------------------------------------
@@ -148,7 +149,7 @@ def gpu_topk(case: Case, layer_idx: int = 0, n_visible=None, k=None, want_scores
     return out_idx.cpu().numpy(), (scores.cpu().numpy() if want_scores else None)
 
 
-def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True):
+def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True, sinks=None):
     cfg = case.cfg
     B, H = cfg.B, cfg.H
     k = idx.shape[1]
@@ -159,7 +160,8 @@ def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True):
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=DEV)
     M.mla_sparse_decode(main_row(cfg), cfg.d_v, _q_gpu(cfg, case.inp.q[layer]), case.g_main, _t(idx),
                         cfg.softmax_scale, out, lse, ws,
-                        case.g_win[layer] if use_w else None, _t(case.win_len) if use_w else None)
+                        case.g_win[layer] if use_w else None, _t(case.win_len) if use_w else None,
+                        sinks=None if sinks is None else _t(np.asarray(sinks, np.float32)))
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
 

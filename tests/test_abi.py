@@ -116,15 +116,19 @@ def test_host_validation_rejects_before_launch(M):
                                      C.c_void_p(0x10000), 1408, 10, None, None, None, 0, 0, fake, fake, 0.1,
                                      fake, 1, 64, 8, fake, None, C.c_void_p(0x100000), 16, None) == 3
     # decode: d_v larger than the latent
-    assert L.mla_sparse_decode(r_main, 600, fake, fake, 6560, 10, fake, 4, None, None, 0, 0.1, 1, 128,
+    assert L.mla_sparse_decode(r_main, 600, fake, fake, 6560, 10, fake, 4, None, None, 0, 0.1, None, 1, 128,
                                fake, fake, fake, 1 << 30, None) == 1
     # decode: workspace too small for the MFMA path
     assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
-                               None, None, 0, 0.1, 1, 128, C.c_void_p(0x10000), fake,
+                               None, None, 0, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
                                C.c_void_p(0x100000), 64, None) == 3
     # decode: misaligned query
     assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10002), C.c_void_p(0x10000), 6560, 10, fake, 4,
-                               None, None, 0, 0.1, 1, 128, C.c_void_p(0x10000), fake,
+                               None, None, 0, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
+                               C.c_void_p(0x100000), 1 << 30, None) == 1
+    # decode: misaligned sinks
+    assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
+                               None, None, 0, 0.1, C.c_void_p(0x10002), 1, 128, C.c_void_p(0x10000), fake,
                                C.c_void_p(0x100000), 1 << 30, None) == 1
 
 

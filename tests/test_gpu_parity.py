@@ -174,6 +174,28 @@ def test_decode_edge_cases(name):
         G.check_attention(got_o, got_l, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s"])
+def test_decode_with_attention_sinks(name):
+    """Attention sinks (one logit per head in the softmax normaliser, no value
+    vector): ordinary, dominant (+40: the output nearly vanishes) and absent
+    (-inf) sinks, with and without the window; an empty set puts all mass on
+    the sink (lse = sink, out = 0)."""
+    case = case_of(name)
+    cfg = case.cfg
+    rng = np.random.default_rng(cfg.cid + 7)
+    idx = oracle_indices_per_layer(case)[0]
+    sinks = (rng.standard_normal(cfg.H) * 3).astype(np.float32)
+    sinks[0], sinks[1] = 40.0, -np.inf
+    for with_window in ((True, False) if cfg.W else (True,)):
+        say("sinks", name, "window", with_window)
+        ref_o, ref_l = G.oracle_attention(case, 0, idx, sinks=sinks, with_window=with_window)
+        got_o, got_l = G.gpu_decode(case, 0, idx, with_window=with_window, sinks=sinks)
+        G.check_attention(got_o, got_l, ref_o, ref_l)
+    empty = -np.ones((cfg.B, 4), np.int32)
+    got_o, got_l = G.gpu_decode(case, 0, empty, with_window=False, sinks=sinks)
+    assert np.all(got_o == 0) and np.array_equal(got_l, np.tile(sinks, (cfg.B, 1)))
+
+
 @pytest.mark.parametrize("name,H", [("c2s", 16), ("c3s", 32), ("c3s", 16), ("c4s", 32), ("c5s", 16)])
 def test_decode_head_counts(name, H):
     """Fewer than 64 heads: only one or two of a workgroup's waves contract while

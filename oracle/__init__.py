@@ -48,7 +48,7 @@ def lib():
         L.orc_topk.argtypes, L.orc_topk.restype = [P, i64, P, P, i32, i32, i32, P], i32
         L.orc_pool.argtypes, L.orc_pool.restype = [P, i64, P, i32, i32, i32, P], i32
         L.orc_attention.argtypes = [i32, i32, i32, i32, P, P, i64, i64, P, i32, P, P, i32,
-                                    f32, P, i32, i32, P, P]
+                                    f32, P, i32, P, i32, i32, P, P]
         L.orc_attention.restype = i32
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i32
         _lib = L
@@ -228,10 +228,12 @@ def pool_positions(blocks, block=8):
     return pos.reshape(blocks.shape[0], -1).astype(np.int32)
 
 
-def attention(main_row, d_v, q, main_cache, idx, softmax_scale, win_ring=None, win_len=None, sinks=None):
+def attention(main_row, d_v, q, main_cache, idx, softmax_scale, win_ring=None, win_len=None, sinks=None,
+              rope_cs=None):
     """q: [B, H, dim+rope] (exact values of the bf16 inputs); main_cache uint8
     [B, capacity, row_bytes]; idx int32 [B, k]; win_ring uint16 [B, W, dim+rope];
-    sinks: optional fp32 [H] attention-sink logits.  Returns (out fp32 [B, H, d_v], lse fp32 [B, H])."""
+    sinks: optional fp32 [H] attention-sink logits; rope_cs: optional fp32 [B, r/2, 2]
+    (cos, sin) un-rotating the trailing r output channels.  Returns (out fp32 [B, H, d_v], lse fp32 [B, H])."""
     fmt, dim, rope = main_row
     q = _c(q, np.float32)
     B, H, D = q.shape
@@ -248,7 +250,8 @@ def attention(main_row, d_v, q, main_cache, idx, softmax_scale, win_ring=None, w
     lse = np.empty((B, H), dtype=np.float32)
     rc = lib().orc_attention(fmt, dim, rope, d_v, _p(q), _p(main_cache), main_cache.strides[0],
                              main_cache.shape[1], _p(idx), k, _p(win_ring),
-                             _p(_c(win_len, np.int32)), W, float(softmax_scale), _p(_c(sinks, np.float32)), B, H,
-                             _p(out), _p(lse))
+                             _p(_c(win_len, np.int32)), W, float(softmax_scale), _p(_c(sinks, np.float32)),
+                             0 if rope_cs is None else 2 * np.asarray(rope_cs).shape[1],
+                             _p(_c(rope_cs, np.float32)), B, H, _p(out), _p(lse))
     _check(rc, "attention")
     return out, lse

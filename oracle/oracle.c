@@ -566,6 +566,13 @@ int orc_pool(const float* scores, int64_t n_rows, const int32_t* n_visible, int 
  *   lse  = log(sum_u exp(z_u) + exp(sinks[h])),  o[c] = sum_u exp(z_u - lse) * K_u[c]
  * so the weights of U sum to 1 - p_sink; an empty U gives lse = sinks[h], o = 0.
  * sinks == NULL (or -inf) is the plain softmax.
+ * O-RoPE ([P2] Part 2 "What replaced MLA", "Partial RoPE, and its inverse on
+ * the output": K = V carries the rotation of its trailing RoPE channels, and
+ * V4 undoes it on the output at the query position, apply_rotary_pos_emb(o,
+ * cos, -sin)): with rope_dim > 0 the trailing rope_dim output channels, as
+ * halves x1 = o[d_v - rope_dim .. d_v - rope_dim/2), x2 = the rest (the
+ * rotate-half pairing of that function), become x1 cos + x2 sin and
+ * x2 cos - x1 sin, with (cos, sin) = rope_cs[b, i] for pair i.
  * Window rows are bf16, [B, W, dim+rope].
  * Pins: absorbed = naive MLA with explicit up-projections; k >= visible rows
  * equals dense softmax attention; LSE merge of any partition equals the whole;
@@ -574,11 +581,13 @@ int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                   const float* q, const uint8_t* main_cache, int64_t main_seq_stride, int64_t capacity,
                   const int32_t* idx, int k,
                   const uint16_t* win_ring, const int32_t* win_len, int W,
-                  float softmax_scale, const float* sinks, int B, int H, float* out, float* lse) {
+                  float softmax_scale, const float* sinks, int rope_dim, const float* rope_cs,
+                  int B, int H, float* out, float* lse) {
     int D = main_dim + main_rope;
     int64_t rb = orc_row_bytes(main_fmt, main_dim, main_rope);
     int b;
     if (rb < 0 || d_v <= 0 || d_v > D || B < 0 || H <= 0 || k < 0) return -1;
+    if (rope_dim < 0 || rope_dim % 2 || rope_dim > d_v || (rope_dim > 0 && !rope_cs)) return -1;
     for (b = 0; b < B; b++) {
         int i, nw = 0, nu = 0;
         for (i = 0; i < k; i++) {
@@ -632,10 +641,22 @@ int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                 if (sk > -INFINITY) sum += exp(sk - m);
                 l = m + log(sum);
                 lse[(int64_t)b * H + h] = (float)l;
-                for (c = 0; c < d_v; c++) {
-                    double o = 0.0;
-                    for (uu = 0; uu < nu; uu++) o += exp(z[uu] - l) * rows[(int64_t)uu * D + c];
-                    out[((int64_t)b * H + h) * d_v + c] = (float)o;
+                {
+                    double* ov = (double*)malloc(sizeof(double) * (size_t)d_v);
+                    int hr = rope_dim / 2, ii;
+                    for (c = 0; c < d_v; c++) {
+                        double o = 0.0;
+                        for (uu = 0; uu < nu; uu++) o += exp(z[uu] - l) * rows[(int64_t)uu * D + c];
+                        ov[c] = o;
+                    }
+                    for (ii = 0; ii < hr; ii++) {            /* un-rotate pair ii at the query position */
+                        double cs = rope_cs[((int64_t)b * hr + ii) * 2], sn = rope_cs[((int64_t)b * hr + ii) * 2 + 1];
+                        double x1 = ov[d_v - rope_dim + ii], x2 = ov[d_v - hr + ii];
+                        ov[d_v - rope_dim + ii] = x1 * cs + x2 * sn;
+                        ov[d_v - hr + ii] = x2 * cs - x1 * sn;
+                    }
+                    for (c = 0; c < d_v; c++) out[((int64_t)b * H + h) * d_v + c] = (float)ov[c];
+                    free(ov);
                 }
                 free(z);
             }

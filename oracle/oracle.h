@@ -61,7 +61,8 @@ int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                   const float* q, const uint8_t* main_cache, int64_t main_seq_stride, int64_t capacity,
                   const int32_t* idx, int k,
                   const uint16_t* win_ring, const int32_t* win_len, int W,
-                  float softmax_scale, const float* sinks, int B, int H, float* out, float* lse);
+                  float softmax_scale, const float* sinks, int rope_dim, const float* rope_cs,
+                  int B, int H, float* out, float* lse);
 
 int orc_num_threads(void);
 

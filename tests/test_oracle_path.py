@@ -401,3 +401,54 @@ def test_attention_sinks_follow_the_pages_formulation():
     assert np.abs(o[0, 3]).max() < 1e-6 * np.abs(o0[0, 3]).max()               # a dominant sink
     oe, le = O.attention((O.F32, 64, 0), 64, q, rows, -np.ones((1, 4), np.int32), scale, sinks=sinks)
     assert np.all(oe == 0) and np.array_equal(le[0], sinks)
+
+
+def test_output_rope_undoes_the_rotation_at_the_query_position():
+    """O-RoPE: the trailing r output channels are rotated by the negative query
+    angle (rotate-half pairing). A zero angle is the identity; a rotation
+    preserves each pair's norm; rotating the result forward again by the same
+    angles (the forward formula x cos + rotate_half(x) sin) gives back the
+    plain output; and when every value row's rope part is its own rotation
+    R_s(v) and the query sits at t, the output only sees s - t: shifting all
+    positions by a constant changes nothing."""
+    rng = np.random.default_rng(31)
+    B, H, N, k, r, D = 2, 3, 40, 16, 16, 64
+    x = rng.standard_normal((B, N, D)).astype(np.float32)
+    rows = O.quant_rows(O.F32, D, 0, x)
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(B)]).astype(np.int32)
+    o0, l0 = O.attention((O.F32, D, 0), D, q, rows, idx, 0.1)
+    ang = rng.uniform(-np.pi, np.pi, (B, r // 2))
+    cs = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    o1, l1 = O.attention((O.F32, D, 0), D, q, rows, idx, 0.1, rope_cs=cs)
+    assert np.array_equal(l0, l1) and np.array_equal(o0[..., :D - r], o1[..., :D - r])
+    ident = np.stack([np.ones((B, r // 2)), np.zeros((B, r // 2))], -1).astype(np.float32)
+    assert np.array_equal(O.attention((O.F32, D, 0), D, q, rows, idx, 0.1, rope_cs=ident)[0], o0)
+    a0, b0 = o0[..., D - r:D - r // 2], o0[..., D - r // 2:]
+    a1, b1 = o1[..., D - r:D - r // 2], o1[..., D - r // 2:]
+    np.testing.assert_allclose(a1 ** 2 + b1 ** 2, a0 ** 2 + b0 ** 2, rtol=1e-5, atol=1e-7)
+    c, s = cs[:, None, :, 0].astype(np.float64), cs[:, None, :, 1].astype(np.float64)
+    fwd = np.concatenate([a1 * c - b1 * s, b1 * c + a1 * s], -1)       # x cos + rotate_half(x) sin
+    np.testing.assert_allclose(fwd, o0[..., D - r:], rtol=1e-5, atol=1e-6)
+    # relative positions only: value rows whose rope part is rotated by their own position s
+    freqs = 10000.0 ** (-np.arange(r // 2) / (r // 2))
+
+    def rot(v, pos):                                                  # forward rotation at `pos`
+        th = pos[..., None] * freqs
+        v1, v2 = v[..., :r // 2], v[..., r // 2:]
+        return np.concatenate([v1 * np.cos(th) - v2 * np.sin(th), v2 * np.cos(th) + v1 * np.sin(th)], -1)
+
+    base = rng.standard_normal((B, N, D))
+    qz = q.copy()
+    qz[..., D - r:] = 0.0                                             # scores independent of the positions
+    outs = []
+    for shift in (0.0, 37.0):
+        pos = np.arange(N, dtype=np.float64)[None].repeat(B, 0) + shift
+        xr = base.copy()
+        xr[..., D - r:] = rot(base[..., D - r:], pos)
+        t = pos[:, -1] + 1.0
+        th = t[:, None] * freqs
+        cst = np.stack([np.cos(th), np.sin(th)], -1).astype(np.float32)
+        outs.append(O.attention((O.F32, D, 0), D, qz, O.quant_rows(O.F32, D, 0, xr.astype(np.float32)), idx, 0.1,
+                                rope_cs=cst)[0])
+    np.testing.assert_allclose(outs[0], outs[1], rtol=1e-4, atol=1e-5)

@@ -322,18 +322,31 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
  *              are attended twice
  *  win_ring    optional bf16 [B, W, dim+rope] window entries (K = V), with
  *  win_len     int32 [B] in [0, W], the number of valid ring slots (slots 0..len-1)
- *  sinks       optional fp32 [H] attention-sink logits, one per head, shared by the batch
+ *  epilogue    optional (NULL = none):
+ *              sinks: fp32 [H] attention-sink logits, one per head, shared by the batch
  *              ([P2] Part 2 "The sliding window", "Attention sinks": an extra score column
- *              with no value vector), in the units of the scaled scores z; NULL = none.
- *              With sinks, lse = log(sum_u exp(z_u) + exp(sinks[h])) and out = sum_u exp(z_u - lse)
+ *              with no value vector), in the units of the scaled scores z. With sinks,
+ *              lse = log(sum_u exp(z_u) + exp(sinks[h])) and out = sum_u exp(z_u - lse)
  *              K_u[0 : d_v] (the weights of U sum to 1 - p_sink); an empty U gives lse =
  *              sinks[h] and out = 0.
+ *              rope_dim, rope_cs: the output's RoPE inverse ([P2] Part 2 "What replaced
+ *              MLA", "Partial RoPE, and its inverse on the output": K = V carries the
+ *              rotation, which V4 undoes at the query position): with halves x1 =
+ *              out[d_v - r .. d_v - r/2) and x2 = out[d_v - r/2 .. d_v), pair i becomes
+ *              (x1 cos + x2 sin, x2 cos - x1 sin) with (cos, sin) = rope_cs[b, i].
  *  out         fp32 [B, H, d_v];  lse fp32 [B, H]
  *  workspace   at least mla_sparse_decode_workspace(main_row, d_v, B, H, k, W) bytes,
  *              256-byte aligned
  * Positions outside [0, capacity) other than -1 are skipped.
  * Errors: MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE.
  */
+/* Optional epilogue of mla_sparse_decode: the V4 output path. */
+typedef struct {
+    const float* sinks;     /* [H] attention-sink logits (see mla_sparse_decode), or NULL */
+    int32_t rope_dim;       /* 0, or r trailing output channels to un-rotate (r % 8 == 0, r <= min(d_v, 256)) */
+    const float* rope_cs;   /* [B, r / 2, 2]: (cos, sin) of each sequence's query position, per RoPE pair */
+} mla_decode_epilogue_t;
+
 size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H,
                                    int32_t k, int32_t W);
 
@@ -341,7 +354,7 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
                                const void* main_cache, int64_t main_seq_stride, int64_t capacity,
                                const int32_t* idx, int32_t k,
                                const void* win_ring, const int32_t* win_len, int32_t W,
-                               float softmax_scale, const float* sinks, int32_t B, int32_t H,
+                               float softmax_scale, const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H,
                                float* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 

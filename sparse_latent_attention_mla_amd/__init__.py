@@ -312,12 +312,17 @@ def mla_sparse_decode_workspace(main_row: Row, d_v: int, B: int, H: int, k: int,
     return int(lib().mla_sparse_decode_workspace(_crow(main_row), d_v, B, H, k, W))
 
 
+class _CEpilogue(C.Structure):
+    _fields_ = [("sinks", C.c_void_p), ("rope_dim", C.c_int32), ("rope_cs", C.c_void_p)]
+
+
 def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
-                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None):
+                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None, rope_cs=None):
     """Sparse absorbed-MLA decode.  q [B, H, D] (bf16; fp32 for F32 rows), main_cache uint8
     [B, capacity, row_bytes], idx int32 [B, k], out fp32 [B, H, d_v], lse fp32 [B, H];
     win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch; sinks fp32 [H]
-    attention-sink logits (optional)."""
+    attention-sink logits (optional); rope_cs fp32 [B, r/2, 2] (cos, sin) un-rotating the
+    trailing r output channels (optional)."""
     _need(q, "q", query_dtype(main_row), 3)
     _need(idx, "idx", torch.int32, 2)
     _need(out, "out", torch.float32, 3)
@@ -337,11 +342,22 @@ def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale
         W = win_ring.shape[1]
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    if sinks is not None:
-        _need(sinks, "sinks", torch.float32, 1)
-        if tuple(sinks.shape) != (H,):
-            raise ValueError("sinks [H] expected")
+    epi = None
+    if sinks is not None or rope_cs is not None:
+        if sinks is not None:
+            _need(sinks, "sinks", torch.float32, 1)
+            if tuple(sinks.shape) != (H,):
+                raise ValueError("sinks [H] expected")
+        r = 0
+        if rope_cs is not None:
+            _need(rope_cs, "rope_cs", torch.float32, 3)
+            if rope_cs.shape[0] != B or rope_cs.shape[2] != 2:
+                raise ValueError("rope_cs [B, r/2, 2] expected")
+            r = 2 * rope_cs.shape[1]
+        epi_s = _CEpilogue(None if sinks is None else sinks.data_ptr(), r,
+                           None if rope_cs is None else rope_cs.data_ptr())
+        epi = C.c_void_p(C.addressof(epi_s))             # (epi_s stays alive through the call)
     _check(lib().mla_sparse_decode(
         _crow(main_row), d_v, _ptr(q), _ptr(main_cache), stride, main_cache.shape[1], _ptr(idx), idx.shape[1],
-        _ptr(win_ring), _ptr(win_len), W, float(softmax_scale), _ptr(sinks), B, H, _ptr(out), _ptr(lse),
+        _ptr(win_ring), _ptr(win_len), W, float(softmax_scale), epi, B, H, _ptr(out), _ptr(lse),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))

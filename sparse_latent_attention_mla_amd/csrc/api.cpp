@@ -382,7 +382,8 @@ size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, i
 mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
                                int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
                                const void* win_ring, const int32_t* win_len, int32_t W, float softmax_scale,
-                               const float* sinks, int32_t B, int32_t H, float* out, float* lse, void* workspace,
+                               const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
+                               void* workspace,
                                size_t workspace_bytes, void* stream) {
     if (B < 0 || H < 1 || k < 0 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need B >= 0, H >= 1, k >= 0, capacity >= 0");
@@ -396,7 +397,14 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: a required pointer is NULL");
     if (win_ring && (!win_len || W <= 0))
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: window needs win_len and W > 0");
+    const float* sinks = epilogue ? epilogue->sinks : nullptr;
+    const int32_t rope_dim = epilogue ? epilogue->rope_dim : 0;
+    const float* rope_cs = epilogue ? epilogue->rope_cs : nullptr;
     if (sinks && !aligned(sinks, 4)) return fail(MLA_ERR_INVALID_ARG, "sparse_decode: misaligned sinks");
+    if (rope_dim < 0 || (rope_dim > 0 && (!rope_cs || !aligned(rope_cs, 4))))
+        return fail(MLA_ERR_INVALID_ARG, "sparse_decode: output RoPE needs rope_dim >= 0 and aligned rope_cs");
+    if (rope_dim % 8 != 0 || rope_dim > d_v || rope_dim > 256)
+        return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: output RoPE needs rope_dim % 8 == 0, <= min(d_v, 256)");
     if (!aligned(q, 16) || !aligned(out, 16) || (win_ring && !aligned(win_ring, 16)))
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: q, out and win_ring must be 16-byte aligned");
     if (!mla::decode_supported(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, H))
@@ -424,6 +432,8 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
     a.W = win_ring ? W : 0;
     a.scale = softmax_scale;
     a.sinks = sinks;
+    a.rope_dim = rope_dim;
+    a.rope_cs = rope_cs;
     a.B = B;
     a.H = H;
     a.out = out;

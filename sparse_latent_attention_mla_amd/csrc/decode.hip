@@ -986,8 +986,39 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
 constexpr int kMergeFast = 16;
 // With attention sinks the head's sink logit joins the normaliser (no value
 // vector): out scales by exp(lse_U - lse) and lse = logaddexp(lse_U, sink).
+// The output's RoPE inverse on thread t's four channels 4t .. 4t + 3 (the
+// trailing r channels: halves x1, x2 of r / 2 each, pair i = (x1[i], x2[i])
+// becomes (x1 cos + x2 sin, x2 cos - x1 sin)); the partner channel sits r / 8
+// lanes away in the same wave (r <= 256 keeps the trailing channels in the
+// last wave of the 128 threads). Every lane of the wave takes part in the shuffle.
+__device__ __forceinline__ float4 unrotate4(float4 v, int t, int r, const float* cs) {
+    const int c0 = 4 * t, base = kDv - r, half = r / 2;
+    const bool in = r > 0 && c0 >= base;
+    const bool first = c0 < base + half;
+    const int lane = t & 63, dl = half / 4;
+    const int src = in ? (first ? lane + dl : lane - dl) : lane;
+    float4 p;
+    p.x = __shfl(v.x, src, 64);
+    p.y = __shfl(v.y, src, 64);
+    p.z = __shfl(v.z, src, 64);
+    p.w = __shfl(v.w, src, 64);
+    if (!in) return v;
+    const int i0 = (c0 - base) % half;                    // pair of the first channel
+    float c[4], s[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        c[e] = cs[2 * (i0 + e)];
+        s[e] = cs[2 * (i0 + e) + 1];
+    }
+    if (first)
+        return make_float4(v.x * c[0] + p.x * s[0], v.y * c[1] + p.y * s[1], v.z * c[2] + p.z * s[2],
+                           v.w * c[3] + p.w * s[3]);
+    return make_float4(v.x * c[0] - p.x * s[0], v.y * c[1] - p.y * s[1], v.z * c[2] - p.z * s[2],
+                       v.w * c[3] - p.w * s[3]);
+}
+
 __device__ __forceinline__ void merge_finish(float m, float tot, float4 acc, const float* sinks, int h, float4* o,
-                                            float* lse_out, int t) {
+                                            float* lse_out, int t, int r, const float* cs) {
     if (sinks) {
         const float sk = sinks[h];
         if (sk > -__builtin_inff()) {
@@ -998,18 +1029,22 @@ __device__ __forceinline__ void merge_finish(float m, float tot, float4 acc, con
         }
     }
     const float inv = 1.0f / tot;
-    *o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    float4 v = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (r > 0) v = unrotate4(v, t, r, cs);
+    *o = v;
     if (t == 0) *lse_out = m + __logf(tot);
 }
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part, float* __restrict__ out,
-                                                         float* __restrict__ lse, const float* __restrict__ sinks) {
+                                                         float* __restrict__ lse, const float* __restrict__ sinks,
+                                                         int rope_dim, const float* __restrict__ rope_cs) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int t = threadIdx.x;
     const float* lp = lse_part + (int64_t)b * S * H + h;
     // an empty set: all mass on the sink (lse = the sink's logit, -inf without one)
     const float empty_lse = sinks ? sinks[h] : -__builtin_inff();
+    const float* cs = rope_dim > 0 ? rope_cs + (int64_t)b * rope_dim : nullptr;   // [r / 2][2] of sequence b
     if (S <= kMergeFast) {
         const float4* op = reinterpret_cast<const float4*>(o_part + ((int64_t)b * S * H + h) * kDv) + t;
         const int64_t step = (int64_t)H * (kDv / 4);
@@ -1042,7 +1077,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
             acc.z += wv * pv[s].z;
             acc.w += wv * pv[s].w;
         }
-        merge_finish(m, tot, acc, sinks, h, o, &lse[(int64_t)b * H + h], t);
+        merge_finish(m, tot, acc, sinks, h, o, &lse[(int64_t)b * H + h], t, rope_dim, cs);
         return;
     }
     float m = -__builtin_inff();
@@ -1067,7 +1102,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
         acc.z += wv * v.z;
         acc.w += wv * v.w;
     }
-    merge_finish(m, tot, acc, sinks, h, o, &lse[(int64_t)b * H + h], t);
+    merge_finish(m, tot, acc, sinks, h, o, &lse[(int64_t)b * H + h], t, rope_dim, cs);
 }
 
 // ------------------------------------------------------------------------
@@ -1099,6 +1134,7 @@ __device__ __forceinline__ float row_elem(int fmt, int dim, const uint8_t* row, 
 __global__ __launch_bounds__(kGenericThreads) void k_decode_generic(DecodeArgs a) {
     __shared__ float zs[kGenericMaxRows];
     __shared__ float qs[1024];
+    __shared__ float os[1024];
     __shared__ float red[kGenericThreads / 64];
     const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int D = a.dim + a.rope;
@@ -1170,7 +1206,21 @@ __global__ __launch_bounds__(kGenericThreads) void k_decode_generic(DecodeArgs a
             acc += p * (win ? u2f((uint32_t)reinterpret_cast<const uint16_t*>(r)[c] << 16)
                             : row_elem(a.fmt, a.dim, r, c));
         }
-        o[c] = acc / sum;
+        os[c] = acc / sum;
+    }
+    __syncthreads();
+    // the output's RoPE inverse on the trailing rope_dim channels (pair i: x1 = os[base + i],
+    // x2 = os[base + r/2 + i] -> x1 cos + x2 sin, x2 cos - x1 sin)
+    const int r = a.rope_dim, base = a.d_v - r, half = r / 2;
+    const float* cs = r > 0 ? a.rope_cs + (int64_t)b * r : nullptr;
+    for (int c = t; c < a.d_v; c += kGenericThreads) {
+        float v = os[c];
+        if (r > 0 && c >= base) {
+            const int i = (c - base) % half;
+            const float cv = cs[2 * i], sv = cs[2 * i + 1];
+            v = (c < base + half) ? os[c] * cv + os[c + half] * sv : os[c] * cv - os[c - half] * sv;
+        }
+        o[c] = v;
     }
     if (t == 0) a.lse[(int64_t)b * a.H + h] = mx + __logf(sum);
 }
@@ -1250,7 +1300,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     const ProfSlot p = prof_slot(PROF_MERGE);
     return launch_kernel(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, p.start, p.stop, S, a.H, o_part,
-                         lse_part, a.out, a.lse, a.sinks);
+                         lse_part, a.out, a.lse, a.sinks, a.rope_dim, a.rope_cs);
 }
 
 }  // namespace mla

@@ -118,6 +118,8 @@ struct DecodeArgs {
     int W;
     float scale;
     const float* sinks;     // [H] attention-sink logits, or null
+    int rope_dim;           // trailing output channels un-rotated (0: none)
+    const float* rope_cs;   // [B, rope_dim / 2, 2] (cos, sin)
     int B, H;
     float* out;             // [B, H, d_v]
     float* lse;             // [B, H]

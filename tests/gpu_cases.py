@@ -124,12 +124,12 @@ def oracle_scores(case: Case, layer_idx: int = 0, n_visible=None, cand=None):
                             cfg.sigma, case.o_idx, nv, cand=cand)
 
 
-def oracle_attention(case: Case, layer: int, idx: np.ndarray, sinks=None, with_window=True):
+def oracle_attention(case: Case, layer: int, idx: np.ndarray, sinks=None, with_window=True, rope_cs=None):
     cfg = case.cfg
     use_w = with_window and cfg.W > 0
     win = case.o_win[layer] if use_w else None
     return O.attention((cfg.main_fmt, cfg.dim, cfg.rope), cfg.d_v, case.inp.q[layer], case.o_main, idx,
-                       cfg.softmax_scale, win, case.win_len if use_w else None, sinks=sinks)
+                       cfg.softmax_scale, win, case.win_len if use_w else None, sinks=sinks, rope_cs=rope_cs)
 
 
 # ---- GPU calls ------------------------------------------------------------
@@ -149,7 +149,7 @@ def gpu_topk(case: Case, layer_idx: int = 0, n_visible=None, k=None, want_scores
     return out_idx.cpu().numpy(), (scores.cpu().numpy() if want_scores else None)
 
 
-def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True, sinks=None):
+def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True, sinks=None, rope_cs=None):
     cfg = case.cfg
     B, H = cfg.B, cfg.H
     k = idx.shape[1]
@@ -161,7 +161,8 @@ def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True, sinks=
     M.mla_sparse_decode(main_row(cfg), cfg.d_v, _q_gpu(cfg, case.inp.q[layer]), case.g_main, _t(idx),
                         cfg.softmax_scale, out, lse, ws,
                         case.g_win[layer] if use_w else None, _t(case.win_len) if use_w else None,
-                        sinks=None if sinks is None else _t(np.asarray(sinks, np.float32)))
+                        sinks=None if sinks is None else _t(np.asarray(sinks, np.float32)),
+                        rope_cs=None if rope_cs is None else _t(np.asarray(rope_cs, np.float32)))
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
 

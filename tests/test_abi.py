@@ -126,10 +126,16 @@ def test_host_validation_rejects_before_launch(M):
     assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10002), C.c_void_p(0x10000), 6560, 10, fake, 4,
                                None, None, 0, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
                                C.c_void_p(0x100000), 1 << 30, None) == 1
-    # decode: misaligned sinks
-    assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
-                               None, None, 0, 0.1, C.c_void_p(0x10002), 1, 128, C.c_void_p(0x10000), fake,
-                               C.c_void_p(0x100000), 1 << 30, None) == 1
+    # decode epilogue: misaligned sinks; output RoPE without its table, or of an unsupported width
+    def epi(sinks, r, cs):
+        e = M._CEpilogue(sinks, r, cs)
+        return e, C.c_void_p(C.addressof(e))
+    for (sk, r, cs), want in (((0x10002, 0, None), 1), ((None, 64, None), 1), ((None, -8, 0x20000), 1),
+                              ((None, 12, 0x20000), 2), ((None, 512, 0x20000), 2)):
+        keep, ep = epi(sk, r, cs)
+        assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
+                                   None, None, 0, 0.1, ep, 1, 128, C.c_void_p(0x10000), fake,
+                                   C.c_void_p(0x100000), 1 << 30, None) == want, (sk, r, cs)
 
 
 def test_workspace_queries(M):

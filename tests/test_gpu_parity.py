@@ -196,6 +196,27 @@ def test_decode_with_attention_sinks(name):
     assert np.all(got_o == 0) and np.array_equal(got_l, np.tile(sinks, (cfg.B, 1)))
 
 
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s"])
+def test_decode_output_rope_inverse(name):
+    """The output's RoPE inverse (the trailing r channels rotated back at each
+    sequence's query position, rotate-half pairing), alone and with sinks, with
+    and without the window."""
+    case = case_of(name)
+    cfg = case.cfg
+    rng = np.random.default_rng(cfg.cid + 11)
+    idx = oracle_indices_per_layer(case)[0]
+    r = 16 if cfg.d_v < 128 else 64
+    ang = rng.uniform(-np.pi, np.pi, (cfg.B, r // 2))
+    cs = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    sinks = (rng.standard_normal(cfg.H) * 2).astype(np.float32)
+    for with_window in ((True, False) if cfg.W else (True,)):
+        for sk in (None, sinks):
+            say("output rope", name, "window", with_window, "sinks", sk is not None)
+            ref_o, ref_l = G.oracle_attention(case, 0, idx, sinks=sk, with_window=with_window, rope_cs=cs)
+            got_o, got_l = G.gpu_decode(case, 0, idx, with_window=with_window, sinks=sk, rope_cs=cs)
+            G.check_attention(got_o, got_l, ref_o, ref_l)
+
+
 @pytest.mark.parametrize("name,H", [("c2s", 16), ("c3s", 32), ("c3s", 16), ("c4s", 32), ("c5s", 16)])
 def test_decode_head_counts(name, H):
     """Fewer than 64 heads: only one or two of a workgroup's waves contract while

@@ -33,6 +33,16 @@ constexpr int kStagedBlocks = 512;        // target workgroups of the staged sca
 constexpr int kDmaRows = 32;              // rows per chunk of the LDS-DMA scan
 constexpr int kDmaMaxRowsPerBlock = 1024;
 constexpr int kDmaRowsPerWave = 256;      // rows of a block per wave, at most (32x32 scan)
+#ifndef MLA_SCAN_RPW4
+#define MLA_SCAN_RPW4 512
+#endif
+constexpr int kDmaRowsPerWave4 = MLA_SCAN_RPW4;   // the same for the four-bit keys (68 and 72 B rows)
+#ifndef MLA_SCAN_NBUF4
+#define MLA_SCAN_NBUF4 2
+#endif
+constexpr int kDmaNbuf4 = MLA_SCAN_NBUF4;          // ring depth of the 32x32 scan for the four-bit keys
+template <int FMT>
+constexpr int dma32_rows_per_wave() { return FMT == MLA_FMT_E4M3_S128 ? kDmaRowsPerWave : kDmaRowsPerWave4; }
 #ifndef MLA_SCAN_WAVES
 #define MLA_SCAN_WAVES 4                  // waves per block of the 32x32 scan (4 or 8)
 #endif
@@ -74,6 +84,36 @@ __device__ __forceinline__ void dequant_key(const uint32_t* w, uint32_t sw, u32x
     }
 }
 
+// The same 32 channels of an E2M1 x E4M3-scale row widened to fp16 for the
+// f16 MFMA: every product of an E2M1 value (at most 2 significant bits, 0.5 .. 6)
+// and an E4M3 scale (at most 4 bits, 2^-9 .. 448) lies in fp16's normal range
+// with at most 5 significant bits, so the packed fp16 multiply is exact.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+__device__ __forceinline__ void dequant_e2m1_f16(const uint32_t* w, uint32_t sw, u32x4 kb[4]) {
+    const _Float16 s0 = (_Float16)e4m3_to_f32(sw & 0xFFu), s1 = (_Float16)e4m3_to_f32((sw >> 8) & 0xFFu);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const f16x2 s = (t < 2) ? f16x2{s0, s0} : f16x2{s1, s1};
+        kb[t] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[t], 1.0f, 0) * s),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[t], 1.0f, 1) * s),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[t], 1.0f, 2) * s),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[t], 1.0f, 3) * s)};
+    }
+}
+
+// A query head held as bf16 pairs (u32x4 of 8 values) moved to fp16 after
+// scaling by 2^k: exact for every value within 2^32 of the head's largest
+// (k puts that largest in [2^14, 2^15)); smaller ones round to fp16's grid.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 q, float p) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const f16x2 v = {(_Float16)(u2f(q[e] << 16) * p), (_Float16)(u2f(q[e] & 0xFFFF0000u) * p)};
+        r[e] = __builtin_bit_cast(uint32_t, v);
+    }
+    return r;
+}
+
 // Bytes of a 128-channel indexer row of format FMT.
 template <int FMT>
 constexpr int idx_rb() {
@@ -107,6 +147,37 @@ __device__ __forceinline__ void mx_round_query(u32x4* q) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) q[i][e] = round1(q[i][e] << 16) | (round1(q[i][e] & 0xFFFF0000u) << 16);
+}
+
+// The same rounding of one query block kept as MX codes for the FP4 MFMA: the
+// 32 E2M1 codes (channel 2i in the low nibble of byte i; the rung r is code
+// 2r below 2, r + 2 below 4, r / 2 + 4 above, the sign in bit 3) into `codes`,
+// the block's E8M0 code returned.
+__device__ __forceinline__ uint32_t mx_encode_query(const u32x4* q, u32x4& codes) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, max((q[i][e] << 16) & 0x7FFFFFFFu, q[i][e] & 0x7FFF0000u));
+    const uint32_t code = mx_code(m);
+    const int sh = 127 - (int)code;
+    auto enc1 = [&](uint32_t bits) -> uint32_t {              // fp32 bits of a bf16 value -> E2M1 code
+        const float a = __builtin_ldexpf(u2f(bits & 0x7FFFFFFFu), sh);
+        const float step = a < 2.0f ? 0.5f : (a < 4.0f ? 1.0f : 2.0f);
+        const float inv = a < 2.0f ? 2.0f : (a < 4.0f ? 1.0f : 0.5f);
+        const float r = fminf(__builtin_rintf(a * inv) * step, 6.0f);
+        const uint32_t c = r < 2.0f ? (uint32_t)(2.0f * r) : (r < 4.0f ? (uint32_t)r + 2u : (uint32_t)(0.5f * r) + 4u);
+        return c | ((bits >> 28) & 8u);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w |= (enc1(q[i][e] << 16) | (enc1(q[i][e] & 0xFFFF0000u) << 4)) << (8 * e);
+        codes[i] = w;
+    }
+    return code;
 }
 
 // ReLU on the bit pattern: a set sign bit is a negative int32 (also for -0),
@@ -535,7 +606,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     static_assert(NBUF >= 2 && NBUF <= 3, "ring depth");
     __shared__ uint32_t hist2[kHistBins / 2];
     __shared__ uint32_t coarse[kCoarseBins];
-    __shared__ __attribute__((aligned(16))) float sc[kDmaRowsPerWave * NW];
+    __shared__ __attribute__((aligned(16))) float sc[dma32_rows_per_wave<FMT>() * NW];
     __shared__ __attribute__((aligned(16))) uint8_t ring[NW][NBUF][kBuf];
     __shared__ __attribute__((aligned(16))) float fuse_src[FUSE ? kFuseMaxNew : 1][128];
     __shared__ __attribute__((aligned(16))) uint8_t fuse_row[FUSE ? kFuseMaxNew : 1][144];
@@ -645,15 +716,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     if (NBUF == 3 && issued == 2) wait_vmcnt<2 * KI>();
     else if (issued >= 1) wait_vmcnt<KI>();
     else wait_vmcnt<0>();
-    if constexpr (FMT == MLA_FMT_MXFP4) {                  // FP4 queries: each wave rounds its staged head tile
+    if constexpr (FMT == MLA_FMT_MXFP4) {                  // FP4 queries: each wave encodes its staged head tile
         if (wave < 2 * MT2) {                              // (lane: head lane / 4, 32-channel block lane % 4)
             uint8_t* hq = &ring[wave][NBUF - 1][0] + (lane >> 2) * 272 + (lane & 3) * 64;
-            u32x4 qb[4];
-#pragma unroll
+            u32x4 qb[4], codes;                            // (the block's 16 code bytes, then its scale
+#pragma unroll                                             // byte, over the start of its own 64 bytes)
             for (int i = 0; i < 4; ++i) qb[i] = *reinterpret_cast<const u32x4*>(hq + 16 * i);
-            mx_round_query(qb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(hq + 16 * i) = qb[i];
+            const uint32_t e8 = mx_encode_query(qb, codes);
+            *reinterpret_cast<u32x4*>(hq) = codes;
+            *reinterpret_cast<uint32_t*>(hq + 16) = e8;
         }
     }
     __syncthreads();                                       // queries, weights staged; histograms cleared
@@ -665,18 +736,43 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
                                    &fuse_row[e][FMT == MLA_FMT_E4M3_S128 ? 128 : 64]);
     }
     u32x4 qa[MT2][8];                                      // head 32 mt + n32, channels 64 h + 8 s ..
+    uint32_t qsc[MT2];                                     // MXFP4: scales of blocks 2h, 2h + 1; E2M1: the head's k
     float wv[MT2][16];                                     // w * sigma of result register v
 #pragma unroll
     for (int mt = 0; mt < MT2; ++mt) {
         const int head = 32 * mt + n32;
         const uint8_t* qt = &ring[head >> 4][NBUF - 1][0] + (head & 15) * 272 + 128 * h;
+        if constexpr (FMT == MLA_FMT_MXFP4) {
+            qa[mt][0] = *reinterpret_cast<const u32x4*>(qt);
+            qa[mt][1] = *reinterpret_cast<const u32x4*>(qt + 64);
+            qsc[mt] = (*reinterpret_cast<const uint32_t*>(qt + 16) & 0xFFu) |
+                      ((*reinterpret_cast<const uint32_t*>(qt + 80) & 0xFFu) << 8);
+        } else {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qt + 16 * s);
+            for (int s = 0; s < 8; ++s) qa[mt][s] = *reinterpret_cast<const u32x4*>(qt + 16 * s);
+        }
+        if constexpr (FMT == MLA_FMT_E2M1_S16) {           // fp16 operands: the head scaled by 2^k into range
+            uint32_t m = 0;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    m = max(m, max((qa[mt][s][e] << 16) & 0x7FFFFFFFu, qa[mt][s][e] & 0x7FFF0000u));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+            const int k = min(max(14 - ((int)(m >> 23) - 127), -120), 120);
+            qsc[mt] = (uint32_t)k;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) qa[mt][s] = bf16x8_to_f16x8_scaled(qa[mt][s], u2f((uint32_t)(k + 127) << 23));
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const f32x4 w4 = *reinterpret_cast<const f32x4*>(&wstage[32 * mt + 8 * q + 4 * h]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wv[mt][4 * q + r] = w4[r] * a.sigma;
+            for (int r = 0; r < 4; ++r) {
+                wv[mt][4 * q + r] = w4[r] * a.sigma;
+                if constexpr (FMT == MLA_FMT_E2M1_S16)      // the row's head was scaled by 2^k: undo it
+                    wv[mt][4 * q + r] *= u2f((uint32_t)(127 - __shfl((int)qsc[mt], 8 * q + 4 * h + r, 64)) << 23);
+            }
         }
     }
     __syncthreads();                                       // every wave holds them: the buffers are free
@@ -686,6 +782,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     struct ChunkIn {
         u32x4 kb[8];
         float mult;
+        uint32_t ks;                                       // MXFP4: the E8M0 codes of blocks 2h, 2h + 1
     };
     auto fetch = [&](int c, ChunkIn& in) {
         if (NBUF == 3 && c + 1 < n_dma) wait_vmcnt<KI>();
@@ -711,14 +808,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
             uint32_t w[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) w[i] = reinterpret_cast<const uint32_t*>(rp + 32 * h)[i];
-            if constexpr (FMT == MLA_FMT_MXFP4) {               // one E8M0 byte per 32 channels
-                const uint32_t sw = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * h);
-                dequant_key<FMT>(w, sw & 0xFFu, in.kb);
-                dequant_key<FMT>(w + 4, sw >> 8, in.kb + 4);
+            if constexpr (FMT == MLA_FMT_MXFP4) {               // the codes as they are, for the FP4 MFMA
+                in.kb[0] = u32x4{w[0], w[1], w[2], w[3]};
+                in.kb[1] = u32x4{w[4], w[5], w[6], w[7]};
+                in.ks = *reinterpret_cast<const uint16_t*>(rp + 64 + 2 * h);
             } else {
                 const uint32_t sw = *reinterpret_cast<const uint32_t*>(rp + 64 + 4 * h);
-                dequant_key<FMT>(w, sw & 0xFFFFu, in.kb);
-                dequant_key<FMT>(w + 4, sw >> 16, in.kb + 4);
+                dequant_e2m1_f16(w, sw & 0xFFFFu, in.kb);
+                dequant_e2m1_f16(w + 4, sw >> 16, in.kb + 4);
             }
         }
     };
@@ -731,10 +828,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[mt][v] = 0.0f;
         }
+        if constexpr (FMT == MLA_FMT_MXFP4) {              // FP4 x FP4 with the blocks' E8M0 scales
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
+            for (int mt = 0; mt < MT2; ++mt) {
+                acc[mt] = mfma32_fp4(qa[mt][0], cur.kb[0], acc[mt], qsc[mt] & 0xFFu, cur.ks & 0xFFu);
+                acc[mt] = mfma32_fp4(qa[mt][1], cur.kb[1], acc[mt], qsc[mt] >> 8, cur.ks >> 8);
+            }
+        } else {
 #pragma unroll
-            for (int mt = 0; mt < MT2; ++mt) acc[mt] = mfma32_bf16(qa[mt][s], cur.kb[s], acc[mt]);
+            for (int s = 0; s < 8; ++s)
+#pragma unroll
+                for (int mt = 0; mt < MT2; ++mt)
+                    acc[mt] = FMT == MLA_FMT_E2M1_S16 ? mfma32_f16(qa[mt][s], cur.kb[s], acc[mt])
+                                                      : mfma32_bf16(qa[mt][s], cur.kb[s], acc[mt]);
+        }
         const float mult = cur.mult;
         if (c + 1 < n_dma) fetch(c + 1, cur);
         // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
@@ -1360,7 +1467,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         const int64_t unit32 = (int64_t)kDma32Waves * kDmaRows;
         int64_t d32rpb = (a.capacity + per_seq32 - 1) / per_seq32;
         d32rpb = ((d32rpb + unit32 - 1) / unit32) * unit32;
-        d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), (int64_t)kDmaRowsPerWave * kDma32Waves);
+        const int64_t rpw32 = a.fmt == MLA_FMT_E4M3_S128 ? kDmaRowsPerWave : kDmaRowsPerWave4;
+        d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), rpw32 * kDma32Waves);
         const dim3 d32grid((unsigned)((a.capacity + d32rpb - 1) / d32rpb), a.B);
         // the queue-fed 32x32 scan (MLA_SCAN_QUEUES; at the T = 128K shape it is
         // slower than the static partition): about 64 queues (a sequence's rows
@@ -1385,7 +1493,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
                 if constexpr (M % 2 == 0) {                                                    \
                     if (!dyn && carry && pieces_supported(*append) &&                          \
                         piece_count(*append) <= (int64_t)d32grid.x * kDma32Waves)              \
-                        return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves, true>,    \
+                        return launch_kernel(k_scan_dma32<F, M / 2, F == MLA_FMT_E4M3_S128 ? kDmaNbuf : kDmaNbuf4, kDma32Waves, true>,    \
                                              d32grid, dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, \
                                              a, (int)d32rpb, *append);                         \
                     if (const hipError_t e = unfused(); e != hipSuccess) return e;             \
@@ -1393,7 +1501,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
                         return launch_kernel(k_scan_dyn32<F, M / 2, kDma32Waves>,              \
                                              dim3((unsigned)dyn_nq, (unsigned)dyn_per_queue), dim3(64 * kDma32Waves), \
                                              0, stream, p.start, p.stop, a, dyn_lg);   \
-                    return launch_kernel(k_scan_dma32<F, M / 2, kDmaNbuf, kDma32Waves, false>, d32grid,     \
+                    return launch_kernel(k_scan_dma32<F, M / 2, F == MLA_FMT_E4M3_S128 ? kDmaNbuf : kDmaNbuf4, kDma32Waves, false>, d32grid,     \
                                          dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb, \
                                          AppendArgs{});                                        \
                 }                                                                              \

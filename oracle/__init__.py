@@ -14,7 +14,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, E4M3_S128, E2M1_S16, MXFP4 = 0, 1, 2, 3, 4
+F32, BF16, E4M3_S128, E2M1_S16, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
 
 _lib = None
 
@@ -30,6 +30,7 @@ def lib():
         L.orc_e4m3_value.argtypes, L.orc_e4m3_value.restype = [C.c_uint32], C.c_double
         L.orc_e8m0_value.argtypes, L.orc_e8m0_value.restype = [C.c_uint32], C.c_double
         L.orc_mx_scale.argtypes, L.orc_mx_scale.restype = [C.c_float], C.c_uint32
+        L.orc_mx8_scale.argtypes, L.orc_mx8_scale.restype = [C.c_float], C.c_uint32
         L.orc_e4m3_encode.argtypes, L.orc_e4m3_encode.restype = [f32], C.c_uint32
         L.orc_e2m1_value.argtypes, L.orc_e2m1_value.restype = [C.c_uint32], C.c_double
         L.orc_e2m1_encode.argtypes, L.orc_e2m1_encode.restype = [f32], C.c_uint32
@@ -86,6 +87,11 @@ def e8m0_value(codes):
 def mx_scale(amax):
     """The E8M0 code of an MXFP4 block whose largest magnitude is amax (fp32)."""
     return int(lib().orc_mx_scale(float(np.float32(amax))))
+
+
+def mx8_scale(amax):
+    """The E8M0 code of an MXFP8 (E4M3) block whose largest magnitude is amax (fp32)."""
+    return int(lib().orc_mx8_scale(float(np.float32(amax))))
 
 
 def e2m1_value(nibs):

@@ -182,6 +182,23 @@ uint32_t orc_mx_scale(float amax) {
     return (uint32_t)e;
 }
 
+/* The MXFP8 block scale of V4.1's window entry ([P1] "DeepSeek-V4.1", the
+ * 528-byte window entry: 512 E4M3 values plus 16 E8M0 scales, one per 32
+ * channels).  The same OCP rule with E4M3's largest exponent: X =
+ * 2^(floor(log2(amax)) - 8), 8 being the exponent of 448, clamped to the codes
+ * 0 .. 254; a block of zeros takes code 0.  Elements are E4M3(x / X),
+ * round-to-nearest-even, saturating at 448 (amax / X lies in [256, 512)).
+ * Pins: amax 448 -> code 127, amax 1 -> 119; hand-encoded elements; 528 B. */
+uint32_t orc_mx8_scale(float amax) {
+    int e;
+    if (!(amax > 0.0f)) return 0u;
+    (void)frexpf(amax, &e);                 /* floor(log2 amax) = e - 1 */
+    e = (e - 1) - 8 + 127;
+    if (e < 0) e = 0;
+    if (e > 254) e = 254;
+    return (uint32_t)e;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Row layouts.
  *  F32        : (dim+rope) fp32                                   c1: 320 / 128 B
@@ -195,6 +212,8 @@ uint32_t orc_mx_scale(float amax) {
  *               ([P1] "DeepSeek-V4.1", "Four bits for the main KV": 256 + 32 =
  *               288 B; [P3] section 3: the indexer key in the same format is
  *               72 B)
+ *  MXFP8      : dim E4M3 codes | dim/32 E8M0 scale bytes; no RoPE part (the
+ *               window entry: 512 + 16 = 528 B, [P1] "DeepSeek-V4.1")
  *  MXFP4      : dim/2 bytes of nibbles (as E2M1_S16) | dim/32 E8M0 scale bytes;
  *               no RoPE part ([P1] "DeepSeek-V4", "The indexer in four bits":
  *               64 + 4 = 68 B for the 128-channel indexer key)
@@ -215,6 +234,9 @@ int64_t orc_row_bytes(int fmt, int dim, int rope) {
     case ORC_MXFP4:
         if (dim % 32 || rope != 0) return -1;
         return (int64_t)dim / 2 + dim / 32;
+    case ORC_MXFP8:
+        if (dim % 32 || rope != 0) return -1;
+        return (int64_t)dim + dim / 32;
     default: return -1;
     }
 }
@@ -277,6 +299,20 @@ int orc_quant_row(int fmt, int dim, int rope, const float* x, uint8_t* row) {
             }
         }
         return 0;
+    case ORC_MXFP8:
+        for (b = 0; b < dim / 32; b++) {
+            float a = 0.0f, X;
+            uint32_t sc;
+            for (c = 32 * b; c < 32 * (b + 1); c++) {
+                float m = fabsf(x[c]);
+                if (m > a) a = m;
+            }
+            sc = orc_mx8_scale(a);
+            X = ldexpf(1.0f, (int)sc - 127);         /* exact, 2^-127 as an fp32 subnormal */
+            row[dim + b] = (uint8_t)sc;
+            for (c = 32 * b; c < 32 * (b + 1); c++) row[c] = (uint8_t)((a == 0.0f) ? 0u : orc_e4m3_encode(x[c] / X));
+        }
+        return 0;
     case ORC_MXFP4:
         memset(row, 0, (size_t)nb);
         for (b = 0; b < dim / 32; b++) {
@@ -323,6 +359,9 @@ int orc_dequant_row(int fmt, int dim, int rope, const uint8_t* row, double* out)
             uint32_t nib = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 0xF);
             out[c] = orc_e2m1_value(nib) * orc_e4m3_value(row[dim / 2 + c / 16]);
         }
+        return 0;
+    case ORC_MXFP8:
+        for (c = 0; c < dim; c++) out[c] = orc_e4m3_value(row[c]) * orc_e8m0_value(row[dim + c / 32]);
         return 0;
     case ORC_MXFP4:
         for (c = 0; c < dim; c++) {

@@ -20,7 +20,7 @@ extern "C" {
 #endif
 
 /* Row formats (value of the `fmt` arguments). */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3_S128 = 2, ORC_E2M1_S16 = 3, ORC_MXFP4 = 4 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3_S128 = 2, ORC_E2M1_S16 = 3, ORC_MXFP4 = 4, ORC_MXFP8 = 5 };
 
 /* Scalar codecs. */
 double   orc_e4m3_value(uint32_t code);   /* NaN for 0x7F / 0xFF */
@@ -30,6 +30,7 @@ uint32_t orc_e2m1_encode(float y);        /* RNE on the ladder, saturating at +-
 uint32_t orc_bf16_encode(float x);        /* RNE */
 double   orc_e8m0_value(uint32_t code);   /* 2^(code - 127); NaN for 0xFF */
 uint32_t orc_mx_scale(float amax);        /* shared exponent code of an MXFP4 block */
+uint32_t orc_mx8_scale(float amax);       /* shared exponent code of an MXFP8 (E4M3) block */
 float    orc_bf16_value(uint32_t h);
 
 /* Rows. */

@@ -271,3 +271,41 @@ def test_mxfp4_row_roundtrip_error_bound_and_layout():
     # a block of zeros: scale code 0, codes 0
     z = np.zeros((1, 128), np.float32)
     assert not O.quant_rows(O.MXFP4, 128, 0, z).any()
+
+
+def test_mxfp8_window_entry_size_scale_rule_and_hand_encoded_codes():
+    # the V4.1 window entry: 512 E4M3 values and 16 E8M0 scales, 528 B
+    assert O.quant_rows(O.MXFP8, 512, 0, np.zeros((1, 512), np.float32)).shape == (1, 528)
+    # X = 2^(floor(log2 amax) - 8): the block maximum lands in [256, 512) scale units
+    assert O.mx8_scale(448.0) == 127 and O.mx8_scale(256.0) == 127 and O.mx8_scale(511.9) == 127
+    assert O.mx8_scale(255.9) == 126 and O.mx8_scale(512.0) == 128 and O.mx8_scale(1.0) == 119
+    assert O.mx8_scale(0.0) == 0 and O.mx8_scale(2.0 ** -140) == 0
+    # one block encoded by hand: amax 1 -> X = 2^-8; 1 -> 256 = 2^8 (0 1111 000), -0.3 -> -76.8,
+    # nearest 1.25 * 2^6 (1 1101 010), 0.5 -> 2^7 (0 1110 000), 2^-10 -> 2^-2 (0 0101 000)
+    x = np.zeros((1, 32), np.float32)
+    x[0, :4] = [1.0, -0.3, 0.5, 2.0 ** -10]
+    r = O.quant_rows(O.MXFP8, 32, 0, x)
+    assert list(r[0, :4]) == [0x78, 0xEA, 0x70, 0x28] and not r[0, 4:32].any() and r[0, 32] == 119
+    # saturation: amax 511 -> X = 1, 511 clamps to 448 (0 1111 110)
+    x[0, 0] = 511.0
+    r = O.quant_rows(O.MXFP8, 32, 0, x)
+    assert r[0, 32] == 127 and r[0, 0] == 0x7E
+
+
+def test_mxfp8_row_roundtrip_and_error_bound():
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 0x7F, (40, 128)).astype(np.uint32) | (rng.integers(0, 2, (40, 128)) << 7).astype(np.uint32)
+    codes[:, ::32] = rng.integers(0x78, 0x7F, (40, 4))                   # 256 .. 448 in every block
+    e = rng.integers(100, 150, (40, 4))
+    x = (O.e4m3_value(codes) * np.repeat(2.0 ** (e - 127), 32, axis=1)).astype(np.float32)
+    r = O.quant_rows(O.MXFP8, 128, 0, x)
+    assert np.array_equal(O.dequant_rows(O.MXFP8, 128, 0, r), x)
+    assert np.array_equal(r[:, 128:], e.astype(np.uint8))
+    y = (rng.standard_normal((64, 128)) * rng.uniform(1e-3, 1e3, (64, 1))).astype(np.float32)
+    ry = O.quant_rows(O.MXFP8, 128, 0, y)
+    d = O.dequant_rows(O.MXFP8, 128, 0, ry)
+    Xs = np.repeat(O.e8m0_value(ry[:, 128:]), 32, axis=1)
+    small = np.abs(y) <= 448 * Xs                                        # E4M3 RNE: half an ulp
+    assert np.all(np.abs(d - y)[small] <= np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10 * Xs)[small])
+    assert (~small).any() and np.all(np.abs(d[~small]) == 448 * Xs[~small])   # saturation
+    assert not O.quant_rows(O.MXFP8, 128, 0, np.zeros((1, 128), np.float32)).any()

@@ -80,6 +80,11 @@ typedef enum {
  *                    E2M1 nearest-even of x/X, saturating at 6. As an indexer format it
  *                    makes the query-key product FP4 on both sides: mla_indexer_topk
  *                    rounds each head's query to MXFP4 the same way before scoring.
+ *  MLA_FMT_MXFP8     [dim E4M3 codes | dim/32 E8M0 scale bytes]; dim % 32 == 0, rope == 0;
+ *                    window entries only (win_fmt below): V4.1's 512 + 16 = 528 B window
+ *                    entry ([P1] "DeepSeek-V4.1"). The same OCP rule with E4M3's largest
+ *                    exponent: code floor(log2 amax) - 8 + 127, clamped to 0..254 (0 for a
+ *                    block of zeros); element = E4M3 nearest-even of x/X, saturating at 448.
  * E4M3 is the OCP "fn" variant (max 448, no infinities); E2M1 magnitudes are
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6 ([P1] "A Precision Primer"); an E8M0 code e is 2^(e - 127). */
 typedef enum {
@@ -87,7 +92,8 @@ typedef enum {
     MLA_FMT_BF16 = 1,
     MLA_FMT_E4M3_S128 = 2,
     MLA_FMT_E2M1_S16 = 3,
-    MLA_FMT_MXFP4 = 4
+    MLA_FMT_MXFP4 = 4,
+    MLA_FMT_MXFP8 = 5
 } mla_fmt_t;
 
 /* A row: `dim` quantised (or plain) channels followed by `rope_dim` RoPE channels.
@@ -162,7 +168,10 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
  *  idx_cache          likewise for indexer keys; or NULL
  *  new_win            fp32 [B, Dw] or NULL (no window write)
  *  win_pos            int32 [B] absolute positions (>= 0) of the window entries
- *  win_ring           bf16 [B, W, Dw]
+ *  win_ring           [B, W, entry bytes]: bf16 [B, W, Dw] (win_fmt MLA_FMT_BF16) or
+ *                     MXFP8 entries of Dw + Dw/32 bytes (win_fmt MLA_FMT_MXFP8, Dw % 32 == 0,
+ *                     Dw <= 2048: the 528-byte window entry of V4.1 at Dw = 512)
+ *  win_fmt            MLA_FMT_BF16 or MLA_FMT_MXFP8 (ignored without a window)
  * Errors: MLA_ERR_INVALID_ARG for B < 0, n_new < 0, missing pointers, strides
  * smaller than capacity * row_bytes, W <= 0 or Dw <= 0 with a window;
  * MLA_ERR_UNSUPPORTED for an unsupported row format.
@@ -173,7 +182,7 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
                                  void* main_cache, int64_t main_seq_stride,
                                  void* idx_cache, int64_t idx_seq_stride,
                                  const float* new_win, const int32_t* win_pos,
-                                 void* win_ring, int32_t W, int32_t Dw,
+                                 void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt,
                                  void* stream);
 
 /*
@@ -295,7 +304,7 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
                                      void* main_cache, int64_t main_seq_stride,
                                      void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
                                      const float* new_win, const int32_t* win_pos,
-                                     void* win_ring, int32_t W, int32_t Dw,
+                                     void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt,
                                      const void* q_idx, const float* w, float score_scale,
                                      const int32_t* n_visible, int32_t B, int32_t H_I, int32_t k,
                                      int32_t* out_idx, float* out_scores,
@@ -320,7 +329,10 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
  *  main_cache  rows as in mla_kv_append_quant; capacity rows per sequence
  *  idx         int32 [B, k]: positions in [0, capacity) or -1 (skipped); duplicates
  *              are attended twice
- *  win_ring    optional bf16 [B, W, dim+rope] window entries (K = V), with
+ *  win_ring    optional window entries (K = V) in format win_fmt: bf16 [B, W, dim+rope]
+ *              (16-byte aligned) or MXFP8 [B, W, D + D/32] bytes (D = dim+rope, D % 32 ==
+ *              0), widened exactly to bf16 in the workspace before the decode (exact
+ *              for every block whose scale code is at least 3), with
  *  win_len     int32 [B] in [0, W], the number of valid ring slots (slots 0..len-1)
  *  epilogue    optional (NULL = none):
  *              sinks: fp32 [H] attention-sink logits, one per head, shared by the batch
@@ -348,12 +360,12 @@ typedef struct {
 } mla_decode_epilogue_t;
 
 size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H,
-                                   int32_t k, int32_t W);
+                                   int32_t k, int32_t W, int32_t win_fmt);
 
 mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
                                const void* main_cache, int64_t main_seq_stride, int64_t capacity,
                                const int32_t* idx, int32_t k,
-                               const void* win_ring, const int32_t* win_len, int32_t W,
+                               const void* win_ring, const int32_t* win_len, int32_t W, int32_t win_fmt,
                                float softmax_scale, const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H,
                                float* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);

@@ -15,7 +15,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla.so")
 
-F32, BF16, E4M3_S128, E2M1_S16, MXFP4 = 0, 1, 2, 3, 4
+F32, BF16, E4M3_S128, E2M1_S16, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
 
@@ -56,21 +56,21 @@ def lib():
         L.mla_profile_read.argtypes = [C.c_char_p, C.POINTER(i32), C.POINTER(C.c_double)]
         L.mla_profile_read.restype = i32
         L.mla_kv_append_quant.argtypes = [_CRow, _CRow, P, P, P, i32, i32, i64, P, i64, P, i64,
-                                          P, P, P, i32, i32, P]
+                                          P, P, P, i32, i32, i32, P]
         L.mla_kv_append_quant.restype = i32
         L.mla_indexer_topk_workspace.argtypes, L.mla_indexer_topk_workspace.restype = [i32, i64, i32], sz
         L.mla_indexer_topk.argtypes = [_CRow, P, P, f32, P, i64, i64, P, P, i32, i32, i32, i32,
                                        P, P, P, sz, P]
         L.mla_indexer_topk.restype = i32
         L.mla_append_indexer_topk.argtypes = [_CRow, _CRow, P, P, P, i32, P, i64, P, i64, i64, P, P, P,
-                                              i32, i32, P, P, f32, P, i32, i32, i32, P, P, P, sz, P]
+                                              i32, i32, i32, P, P, f32, P, i32, i32, i32, P, P, P, sz, P]
         L.mla_append_indexer_topk.restype = i32
         L.mla_indexer_pool_workspace.argtypes, L.mla_indexer_pool_workspace.restype = [i32, i64, i32], sz
         L.mla_indexer_pool.argtypes = [P, i64, P, i32, i32, i32, P, P, sz, P]
         L.mla_indexer_pool.restype = i32
-        L.mla_sparse_decode_workspace.argtypes = [_CRow, i32, i32, i32, i32, i32]
+        L.mla_sparse_decode_workspace.argtypes = [_CRow, i32, i32, i32, i32, i32, i32]
         L.mla_sparse_decode_workspace.restype = sz
-        L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, f32, P, i32, i32,
+        L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, i32, f32, P, i32, i32,
                                         P, P, P, sz, P]
         L.mla_sparse_decode.restype = i32
         _lib = L
@@ -151,11 +151,25 @@ def _cache_stride(cache: Optional[torch.Tensor], name: str) -> int:
     return cache.stride(0)
 
 
+def _win_ring(win_ring, B, D, name="win_ring"):
+    """(format, W) of a window ring: bf16 [B, W, D] or MXFP8 uint8 [B, W, D + D/32]."""
+    if win_ring.dtype == torch.uint8:
+        _need(win_ring, name, torch.uint8, 3)
+        if D % 32 != 0 or win_ring.shape[0] != B or win_ring.shape[2] != D + D // 32:
+            raise ValueError(f"{name}: MXFP8 ring [B, W, D + D/32] bytes with D % 32 == 0 expected")
+        return MXFP8, win_ring.shape[1]
+    _need(win_ring, name, torch.bfloat16, 3)
+    if win_ring.shape[0] != B or win_ring.shape[2] != D:
+        raise ValueError(f"{name}: bf16 ring [B, W, D] expected")
+    return BF16, win_ring.shape[1]
+
+
 def mla_kv_append_quant(main_row: Row, idx_row: Row, new_main, new_idx, slots,
                         main_cache, idx_cache, new_win=None, win_pos=None, win_ring=None, stream=None):
     """Quantise-append.  new_main fp32 [B, n, D], new_idx fp32 [B, n, d_I], slots int32 [B, n];
     main_cache / idx_cache uint8 [B, capacity, row_bytes] (either may be None);
-    new_win fp32 [B, Dw], win_pos int32 [B], win_ring bf16 [B, W, Dw] (optional)."""
+    new_win fp32 [B, Dw], win_pos int32 [B], win_ring (optional) bf16 [B, W, Dw] or uint8
+    [B, W, Dw + Dw/32] for MXFP8 window entries."""
     caches = [c for c in (main_cache, idx_cache) if c is not None]
     capacity = caches[0].shape[1] if caches else 0
     if len(caches) == 2 and main_cache.shape[1] != idx_cache.shape[1]:
@@ -177,21 +191,21 @@ def mla_kv_append_quant(main_row: Row, idx_row: Row, new_main, new_idx, slots,
         if idx_cache.shape[2] != row_bytes(idx_row):
             raise ValueError("idx_cache rows do not match the row format")
     W = Dw = 0
+    wfmt = BF16
     if new_win is not None:
         _need(new_win, "new_win", torch.float32, 2)
         _need(win_pos, "win_pos", torch.int32, 1)
-        _need(win_ring, "win_ring", torch.bfloat16, 3)
         if caches and new_win.shape[0] != B:
             raise ValueError("new_win batch differs from the caches'")
-        B = new_win.shape[0]
-        _, W, Dw = win_ring.shape
-        if win_ring.shape[0] != B or new_win.shape[1] != Dw or win_pos.shape[0] != B:
-            raise ValueError("window shapes: new_win [B, Dw], win_pos [B], win_ring [B, W, Dw]")
+        B, Dw = new_win.shape
+        wfmt, W = _win_ring(win_ring, B, Dw)
+        if win_pos.shape[0] != B:
+            raise ValueError("window shapes: new_win [B, Dw], win_pos [B]")
     _check(lib().mla_kv_append_quant(
         _crow(main_row), _crow(idx_row), _ptr(new_main), _ptr(new_idx), _ptr(slots), B, n_new, capacity,
         _ptr(main_cache), _cache_stride(main_cache, "main_cache"),
         _ptr(idx_cache), _cache_stride(idx_cache, "idx_cache"),
-        _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw, _stream(stream)))
+        _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw, wfmt, _stream(stream)))
 
 
 def mla_indexer_topk_workspace(B: int, capacity: int, k: int) -> int:
@@ -278,13 +292,14 @@ def mla_append_indexer_topk(main_row: Row, idx_row: Row, new_main, new_idx, slot
     if tuple(new_idx.shape) != (B, n_new, idx_row.dim) or idx_cache.shape[0] != B:
         raise ValueError("new_idx must be [B, n_new, idx dim] and idx_cache [B, capacity, row_bytes]")
     W = Dw = 0
+    wfmt = BF16
     if new_win is not None:
         _need(new_win, "new_win", torch.float32, 2)
         _need(win_pos, "win_pos", torch.int32, 1)
-        _need(win_ring, "win_ring", torch.bfloat16, 3)
-        _, W, Dw = win_ring.shape
-        if win_ring.shape[0] != B or tuple(new_win.shape) != (B, Dw) or win_pos.shape[0] != B:
-            raise ValueError("window shapes: new_win [B, Dw], win_pos [B], win_ring [B, W, Dw]")
+        Dw = new_win.shape[1]
+        wfmt, W = _win_ring(win_ring, B, Dw)
+        if new_win.shape[0] != B or win_pos.shape[0] != B:
+            raise ValueError("window shapes: new_win [B, Dw], win_pos [B]")
     _need(q_idx, "q_idx", query_dtype(idx_row), 3)
     _need(w, "w", torch.float32, 2)
     _need(n_visible, "n_visible", torch.int32, 1)
@@ -303,13 +318,15 @@ def mla_append_indexer_topk(main_row: Row, idx_row: Row, new_main, new_idx, slot
         _crow(main_row), _crow(idx_row), _ptr(new_main), _ptr(new_idx), _ptr(slots), n_new,
         _ptr(main_cache), _cache_stride(main_cache, "main_cache"),
         _ptr(idx_cache), _cache_stride(idx_cache, "idx_cache"), cap,
-        _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw,
+        _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw, wfmt,
         _ptr(q_idx), _ptr(w), float(score_scale), _ptr(n_visible), B, H_I, k, _ptr(out_idx), _ptr(out_scores),
         _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
-def mla_sparse_decode_workspace(main_row: Row, d_v: int, B: int, H: int, k: int, W: int = 0) -> int:
-    return int(lib().mla_sparse_decode_workspace(_crow(main_row), d_v, B, H, k, W))
+def mla_sparse_decode_workspace(main_row: Row, d_v: int, B: int, H: int, k: int, W: int = 0,
+                                win_fmt: int = 1) -> int:
+    """Workspace bytes of mla_sparse_decode (win_fmt MXFP8 adds the ring's bf16 copy)."""
+    return int(lib().mla_sparse_decode_workspace(_crow(main_row), d_v, B, H, k, W, win_fmt))
 
 
 class _CEpilogue(C.Structure):
@@ -334,12 +351,12 @@ def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale
     if idx.shape[0] != B or tuple(out.shape) != (B, H, d_v) or tuple(lse.shape) != (B, H):
         raise ValueError("idx [B, k], out [B, H, d_v], lse [B, H] expected")
     W = 0
+    wfmt = BF16
     if win_ring is not None:
-        _need(win_ring, "win_ring", torch.bfloat16, 3)
         _need(win_len, "win_len", torch.int32, 1)
-        if win_ring.shape[0] != B or win_ring.shape[2] != D or tuple(win_len.shape) != (B,):
-            raise ValueError("win_ring [B, W, dim + rope] and win_len [B] expected")
-        W = win_ring.shape[1]
+        wfmt, W = _win_ring(win_ring, B, D)
+        if tuple(win_len.shape) != (B,):
+            raise ValueError("win_len [B] expected")
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
     epi = None
@@ -359,5 +376,5 @@ def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale
         epi = C.c_void_p(C.addressof(epi_s))             # (epi_s stays alive through the call)
     _check(lib().mla_sparse_decode(
         _crow(main_row), d_v, _ptr(q), _ptr(main_cache), stride, main_cache.shape[1], _ptr(idx), idx.shape[1],
-        _ptr(win_ring), _ptr(win_len), W, float(softmax_scale), epi, B, H, _ptr(out), _ptr(lse),
+        _ptr(win_ring), _ptr(win_len), W, wfmt, float(softmax_scale), epi, B, H, _ptr(out), _ptr(lse),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))

@@ -90,7 +90,8 @@ TopkLayout topk_layout(int32_t B, int64_t capacity) {
 mla_status_t append_args(mla_row_t main_row, mla_row_t idx_row, const float* new_main, const float* new_idx,
                          const int32_t* slots, int32_t B, int32_t n_new, int64_t capacity, void* main_cache,
                          int64_t main_seq_stride, void* idx_cache, int64_t idx_seq_stride, const float* new_win,
-                         const int32_t* win_pos, void* win_ring, int32_t W, int32_t Dw, mla::AppendArgs* out) {
+                         const int32_t* win_pos, void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt,
+                         mla::AppendArgs* out) {
     if (B < 0 || n_new < 0) return fail(MLA_ERR_INVALID_ARG, "append: B and n_new must be >= 0");
     mla::AppendArgs a{};
     if (main_cache) {
@@ -113,7 +114,12 @@ mla_status_t append_args(mla_row_t main_row, mla_row_t idx_row, const float* new
     if (new_win) {
         if (!win_pos || !win_ring) return fail(MLA_ERR_INVALID_ARG, "append: window needs win_pos and win_ring");
         if (W <= 0 || Dw <= 0) return fail(MLA_ERR_INVALID_ARG, "append: window needs W > 0 and Dw > 0");
-        if (!aligned(win_ring, 2)) return fail(MLA_ERR_INVALID_ARG, "append: misaligned window ring");
+        if (win_fmt != MLA_FMT_BF16 && win_fmt != MLA_FMT_MXFP8)
+            return fail(MLA_ERR_UNSUPPORTED, "append: window entries must be BF16 or MXFP8");
+        if (win_fmt == MLA_FMT_MXFP8 && (Dw % 32 != 0 || Dw > 2048))
+            return fail(MLA_ERR_UNSUPPORTED, "append: an MXFP8 window needs Dw % 32 == 0 and Dw <= 2048");
+        if (win_fmt == MLA_FMT_BF16 && !aligned(win_ring, 2))
+            return fail(MLA_ERR_INVALID_ARG, "append: misaligned window ring");
     }
     a.main_fmt = main_row.fmt;
     a.main_dim = main_row.dim;
@@ -135,6 +141,7 @@ mla_status_t append_args(mla_row_t main_row, mla_row_t idx_row, const float* new
     a.win_ring = new_win ? static_cast<uint16_t*>(win_ring) : nullptr;
     a.W = W;
     a.Dw = Dw;
+    a.win_fmt = win_fmt;
     *out = a;
     return ok();
 }
@@ -243,6 +250,9 @@ int64_t mla_row_bytes(mla_row_t row) {
     case MLA_FMT_MXFP4:
         if (row.dim % 32 != 0 || row.rope_dim != 0 || row.dim > 1024) return -1;
         return (int64_t)row.dim / 2 + row.dim / 32;
+    case MLA_FMT_MXFP8:
+        if (row.dim % 32 != 0 || row.rope_dim != 0 || row.dim > 2048) return -1;
+        return (int64_t)row.dim + row.dim / 32;
     default: return -1;
     }
 }
@@ -278,11 +288,11 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const fl
                                  const float* new_idx, const int32_t* slots, int32_t B, int32_t n_new,
                                  int64_t capacity, void* main_cache, int64_t main_seq_stride, void* idx_cache,
                                  int64_t idx_seq_stride, const float* new_win, const int32_t* win_pos,
-                                 void* win_ring, int32_t W, int32_t Dw, void* stream) {
+                                 void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt, void* stream) {
     mla::AppendArgs a{};
     const mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
                                        main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W,
-                                       Dw, &a);
+                                       Dw, win_fmt, &a);
     if (s != MLA_OK) return s;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     return hip_status(mla::launch_append(a, st), "append launch");
@@ -309,14 +319,16 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, cons
                                      const float* new_idx, const int32_t* slots, int32_t n_new, void* main_cache,
                                      int64_t main_seq_stride, void* idx_cache, int64_t idx_seq_stride,
                                      int64_t capacity, const float* new_win, const int32_t* win_pos,
-                                     void* win_ring, int32_t W, int32_t Dw, const void* q_idx, const float* w,
+                                     void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt, const void* q_idx,
+                                     const float* w,
                                      float score_scale, const int32_t* n_visible, int32_t B, int32_t H_I,
                                      int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
                                      size_t workspace_bytes, void* stream) {
     if (!idx_cache) return fail(MLA_ERR_INVALID_ARG, "append_indexer_topk: idx_cache is NULL");
     mla::AppendArgs ap{};
     mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
-                                 main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W, Dw, &ap);
+                                 main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W, Dw,
+                                 win_fmt, &ap);
     if (s != MLA_OK) return s;
     TopkCall c;
     s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, nullptr, 0, B,
@@ -374,14 +386,23 @@ mla_status_t mla_indexer_pool(const float* scores, int64_t capacity, const int32
     return hip_status(e, "pool select");
 }
 
-size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H, int32_t k, int32_t W) {
+// Bytes of the bf16 copy of an MXFP8 window ring, placed after the decode's own workspace.
+static size_t window_copy_bytes(int32_t win_fmt, int32_t B, int32_t W, int D) {
+    if (win_fmt != MLA_FMT_MXFP8 || W <= 0) return 0;
+    return ((size_t)B * W * D * 2 + 255) & ~(size_t)255;
+}
+
+size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, int32_t H, int32_t k, int32_t W,
+                                   int32_t win_fmt) {
     if (B <= 0 || H <= 0 || k < 0 || W < 0 || mla_row_bytes(main_row) < 0) return 0;
-    return mla::decode_workspace_bytes(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W);
+    return mla::decode_workspace_bytes(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W) +
+           window_copy_bytes(win_fmt, B, W, main_row.dim + main_row.rope_dim);
 }
 
 mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
                                int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
-                               const void* win_ring, const int32_t* win_len, int32_t W, float softmax_scale,
+                               const void* win_ring, const int32_t* win_len, int32_t W, int32_t win_fmt,
+                               float softmax_scale,
                                const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
                                void* workspace,
                                size_t workspace_bytes, void* stream) {
@@ -397,6 +418,11 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: a required pointer is NULL");
     if (win_ring && (!win_len || W <= 0))
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: window needs win_len and W > 0");
+    if (win_ring && win_fmt != MLA_FMT_BF16 && win_fmt != MLA_FMT_MXFP8)
+        return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: window entries must be BF16 or MXFP8");
+    if (win_ring && win_fmt == MLA_FMT_MXFP8 && D % 32 != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: an MXFP8 window needs dim + rope % 32 == 0");
+    const bool win8 = win_ring && win_fmt == MLA_FMT_MXFP8;
     const float* sinks = epilogue ? epilogue->sinks : nullptr;
     const int32_t rope_dim = epilogue ? epilogue->rope_dim : 0;
     const float* rope_cs = epilogue ? epilogue->rope_cs : nullptr;
@@ -405,13 +431,14 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: output RoPE needs rope_dim >= 0 and aligned rope_cs");
     if (rope_dim % 8 != 0 || rope_dim > d_v || rope_dim > 256)
         return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: output RoPE needs rope_dim % 8 == 0, <= min(d_v, 256)");
-    if (!aligned(q, 16) || !aligned(out, 16) || (win_ring && !aligned(win_ring, 16)))
+    if (!aligned(q, 16) || !aligned(out, 16) || (win_ring && !win8 && !aligned(win_ring, 16)))
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: q, out and win_ring must be 16-byte aligned");
     if (!mla::decode_supported(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, H))
         return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: no kernel for this shape");
-    const size_t need = mla::decode_workspace_bytes(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k,
+    const size_t base = mla::decode_workspace_bytes(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k,
                                                     win_ring ? W : 0);
-    if (need == 0 && (k + (win_ring ? W : 0) > 8192 || D > 1024))
+    const size_t need = base + (win8 ? window_copy_bytes(win_fmt, B, W, D) : 0);
+    if (base == 0 && (k + (win_ring ? W : 0) > 8192 || D > 1024))
         return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: generic path limited to k + W <= 8192, width <= 1024");
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return fail(MLA_ERR_WORKSPACE, "sparse_decode: workspace needs %zu bytes, 256-byte aligned", need);
@@ -427,7 +454,8 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
     a.capacity = capacity;
     a.idx = idx;
     a.k = k;
-    a.win = win_ring ? static_cast<const uint16_t*>(win_ring) : nullptr;
+    a.win = (win_ring && !win8) ? static_cast<const uint16_t*>(win_ring) : nullptr;
+    a.win8 = win8 ? static_cast<const uint8_t*>(win_ring) : nullptr;
     a.win_len = win_len;
     a.W = win_ring ? W : 0;
     a.scale = softmax_scale;

@@ -33,7 +33,7 @@ __device__ void quant_row(int fmt, int dim, int rope, const float* __restrict__ 
         for (int c = t; c < dim + rope; c += NT) reinterpret_cast<uint16_t*>(dst)[c] = (uint16_t)bf16_rne(src[c]);
         return;
     }
-    const int blk = (fmt == MLA_FMT_E4M3_S128) ? 128 : (fmt == MLA_FMT_MXFP4 ? 32 : 16);
+    const int blk = (fmt == MLA_FMT_E4M3_S128) ? 128 : ((fmt == MLA_FMT_MXFP4 || fmt == MLA_FMT_MXFP8) ? 32 : 16);
     const int nblk = dim / blk;
     for (int j = t; j < nblk; j += NT) amax_bits[j] = 0u;
     __syncthreads();
@@ -49,6 +49,12 @@ __device__ void quant_row(int fmt, int dim, int rope, const float* __restrict__ 
         for (int j = t; j < nblk; j += NT) scales[j] = u2f(amax_bits[j]) / 448.0f;
         uint16_t* ropep = reinterpret_cast<uint16_t*>(dst + dim + 4 * nblk);
         for (int r = t; r < rope; r += NT) ropep[r] = (uint16_t)bf16_rne(src[dim + r]);
+    } else if (fmt == MLA_FMT_MXFP8) {                     // x / X by an exact power of two
+        for (int c = t; c < dim; c += NT) {
+            const uint32_t ab = amax_bits[c / 32];
+            dst[c] = ab == 0u ? (uint8_t)0 : (uint8_t)e4m3_encode(__builtin_ldexpf(src[c], 127 - (int)mx8_code(ab)));
+        }
+        for (int j = t; j < nblk; j += NT) dst[dim + j] = (uint8_t)mx8_code(amax_bits[j]);
     } else if (fmt == MLA_FMT_MXFP4) {
         for (int p = t; p < dim / 2; p += NT) {
             const int c = 2 * p;
@@ -141,6 +147,7 @@ __host__ inline int64_t piece_count(const AppendArgs& a) {
     return (int64_t)a.B * (a.n_new * m.per_entry + m.win_pieces);
 }
 __host__ inline bool pieces_supported(const AppendArgs& a) {
+    if (a.win_ring && a.win_fmt != MLA_FMT_BF16) return false;
     if (a.main_cache && !((a.main_fmt == MLA_FMT_E4M3_S128 && a.main_rope <= 128) ||
                           (a.main_fmt == MLA_FMT_E2M1_S16 && a.main_rope == 0)))
         return false;
@@ -311,7 +318,15 @@ __device__ void append_store(const AppendArgs& a, int i, int b, const AppendStag
                           a.idx_cache + b * a.idx_stride + slot * a.idx_row_bytes, amax_bits);
     }
     const bool win = a.win_ring && i == 0;
-    if (win && st.pos >= 0) {
+    if (win && st.pos >= 0 && a.win_fmt == MLA_FMT_MXFP8) {   // (Dw <= kStageMain)
+        uint8_t* dst = reinterpret_cast<uint8_t*>(a.win_ring) + ((int64_t)b * a.W + st.pos % a.W) * (a.Dw + a.Dw / 32);
+        __syncthreads();                                   // the rows' quantisers are done with the LDS
+#pragma unroll
+        for (int j = 0; j < kStageMain / NT; ++j)
+            if (t + NT * j < a.Dw) s_main[t + NT * j] = st.vw[j];
+        __syncthreads();
+        quant_row<NT>(MLA_FMT_MXFP8, a.Dw, 0, s_main, dst, amax_bits);
+    } else if (win && st.pos >= 0) {
         const float* wsrc = a.new_win + (int64_t)b * a.Dw;
         uint16_t* dst = a.win_ring + ((int64_t)b * a.W + st.pos % a.W) * a.Dw;
         if (a.Dw <= kStageMain) {

@@ -102,6 +102,12 @@ __device__ __forceinline__ uint32_t mx_encode(float x, uint32_t amax_bits, uint3
     return amax_bits ? e2m1_encode(__builtin_ldexpf(x, 127 - (int)code)) : 0u;
 }
 
+// E8M0 code of an MXFP8 block (E4M3 elements, largest exponent 8) from the fp32
+// bits of its largest magnitude: floor(log2 amax) - 8 + 127, clamped to 0..254.
+__device__ __forceinline__ uint32_t mx8_code(uint32_t amax_bits) {
+    const uint32_t e = amax_bits >> 23;
+    return e >= 8u ? min(e - 8u, 254u) : 0u;
+}
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
     f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false);
     return v.x;

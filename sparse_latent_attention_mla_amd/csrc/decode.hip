@@ -1279,8 +1279,30 @@ static hipError_t launch_layout(const DecodeArgs& a, const Geometry& g, float* o
     return launch_mfma<SRC_MAIN, DQK, 4, 1>(a, g, o_part, lse_part, stream);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-    if (a.B == 0) return hipSuccess;
+// An MXFP8 window ring [B, W, D + D/32 bytes] widened to bf16 rows [B, W, D]:
+// the E4M3 value times its block's power of two, formed in fp32 (exact) and
+// rounded to bf16, exact unless the product lies below bf16's smallest
+// subnormal (blocks with a scale code below 3). One workgroup per ring slot.
+__global__ __launch_bounds__(256) void k_widen_window(const uint8_t* __restrict__ ring, int D,
+                                                      uint16_t* __restrict__ out) {
+    const int64_t row = blockIdx.x;
+    const uint8_t* src = ring + row * (D + D / 32);
+    for (int c = threadIdx.x; c < D; c += 256)
+        out[row * D + c] = (uint16_t)bf16_rne(e4m3_to_f32(src[c]) * e8m0_to_f32(src[D + c / 32]));
+}
+
+hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
+    if (a_in.B == 0) return hipSuccess;
+    DecodeArgs a = a_in;
+    if (a.win8 && a.W > 0) {                               // bf16 copy after the decode's own workspace
+        const size_t base = decode_workspace_bytes(a.fmt, a.dim, a.rope, a.d_v, a.B, a.H, a.k, a.W);
+        uint16_t* wide = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + base);
+        const hipError_t e = launch_kernel(k_widen_window, dim3((unsigned)(a.B * a.W)), dim3(256), 0, stream,
+                                           nullptr, nullptr, a.win8, a.dim + a.rope, wide);
+        if (e != hipSuccess) return e;
+        a.win = wide;
+        a.win8 = nullptr;
+    }
     if (!mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H)) {
         const ProfSlot p = prof_slot(PROF_DECODE);
         return launch_kernel(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, p.start, p.stop, a);

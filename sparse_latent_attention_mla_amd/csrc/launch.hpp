@@ -40,8 +40,9 @@ struct AppendArgs {
     int64_t idx_stride;
     const float* new_win;
     const int32_t* win_pos;
-    uint16_t* win_ring;
+    uint16_t* win_ring;     // bf16 entries, or MXFP8 entries of Dw + Dw/32 bytes (win_fmt)
     int W, Dw;
+    int win_fmt;
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
@@ -114,6 +115,7 @@ struct DecodeArgs {
     const int32_t* idx;
     int k;
     const uint16_t* win;    // [B, W, dim+rope] bf16 or null
+    const uint8_t* win8;    // or [B, W, D + D/32] MXFP8 entries (widened into the workspace first)
     const int32_t* win_len;
     int W;
     float scale;
@@ -127,6 +129,7 @@ struct DecodeArgs {
     size_t workspace_bytes;
 };
 bool decode_supported(int fmt, int dim, int rope, int d_v, int H);
+size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 
 // Opt-in per-kernel event timing (profile.cpp), off unless mla_profile_enable(1).
 enum ProfKernel { PROF_APPEND, PROF_SCAN, PROF_SELECT, PROF_DECODE, PROF_MERGE, PROF_KERNELS };

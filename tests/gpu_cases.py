@@ -156,7 +156,8 @@ def gpu_decode(case: Case, layer: int, idx: np.ndarray, with_window=True, sinks=
     out = torch.empty((B, H, cfg.d_v), dtype=torch.float32, device=DEV)
     lse = torch.empty((B, H), dtype=torch.float32, device=DEV)
     use_w = with_window and cfg.W > 0
-    ws_n = M.mla_sparse_decode_workspace(main_row(cfg), cfg.d_v, B, H, k, cfg.W if use_w else 0)
+    win_fmt = M.MXFP8 if (use_w and case.g_win.dtype == torch.uint8) else M.BF16
+    ws_n = M.mla_sparse_decode_workspace(main_row(cfg), cfg.d_v, B, H, k, cfg.W if use_w else 0, win_fmt)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=DEV)
     M.mla_sparse_decode(main_row(cfg), cfg.d_v, _q_gpu(cfg, case.inp.q[layer]), case.g_main, _t(idx),
                         cfg.softmax_scale, out, lse, ws,

@@ -45,6 +45,7 @@ def test_row_bytes_and_status_strings(M):
     assert M.row_bytes(R(M.E2M1_S16, 512)) == 288
     assert M.row_bytes(R(M.E2M1_S16, 128)) == 72
     assert M.row_bytes(R(M.MXFP4, 128)) == 68 and M.row_bytes(R(M.MXFP4, 48)) == -1
+    assert M.row_bytes(R(M.MXFP8, 512)) == 528 and M.row_bytes(R(M.MXFP8, 40)) == -1
     assert M.row_bytes(R(M.BF16, 512, 64)) == 1152
     assert M.row_bytes(R(M.F32, 64, 16)) == 320
     assert M.row_bytes(R(M.E2M1_S16, 512, 64)) == -1          # no separate RoPE part in FP4 rows
@@ -64,13 +65,26 @@ def test_host_validation_rejects_before_launch(M):
     r_main, r_idx = _row(M, M.E4M3_S128, 512, 64), _row(M, M.E4M3_S128, 128)
     # append: negative batch
     assert L.mla_kv_append_quant(r_main, r_idx, fake, fake, fake, -1, 1, 10, fake, 6560, fake, 1320,
-                                 None, None, None, 0, 0, None) == 1
+                                 None, None, None, 0, 0, 1, None) == 1
     # append: unsupported row format
     assert L.mla_kv_append_quant(_row(M, 9, 512), r_idx, fake, fake, fake, 1, 1, 10, fake, 6560, None, 0,
-                                 None, None, None, 0, 0, None) == 2
+                                 None, None, None, 0, 0, 1, None) == 2
     # append: window without a ring
     assert L.mla_kv_append_quant(r_main, r_idx, None, None, None, 1, 0, 0, None, 0, None, 0,
-                                 fake, fake, None, 128, 512, None) == 1
+                                 fake, fake, None, 128, 512, 1, None) == 1
+    # append: window entries in a format other than BF16 / MXFP8, or an MXFP8 width not a multiple of 32
+    assert L.mla_kv_append_quant(r_main, r_idx, None, None, None, 1, 0, 0, None, 0, None, 0,
+                                 fake, fake, fake, 128, 512, 7, None) == 2
+    assert L.mla_kv_append_quant(r_main, r_idx, None, None, None, 1, 0, 0, None, 0, None, 0,
+                                 fake, fake, fake, 128, 520, M.MXFP8, None) == 2
+    # decode: window entries in an unsupported format
+    assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
+                               fake, fake, 128, 7, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
+                               C.c_void_p(0x100000), 1 << 30, None) == 2
+    # decode: the MXFP8 window's bf16 copy is part of the workspace
+    wb = L.mla_sparse_decode_workspace(r_main, 512, 4, 128, 2048, 128, M.BF16)
+    w8 = L.mla_sparse_decode_workspace(r_main, 512, 4, 128, 2048, 128, M.MXFP8)
+    assert w8 == wb + 4 * 128 * 576 * 2
     # topk: score scale must be positive
     assert L.mla_indexer_topk(r_idx, fake, fake, 0.0, fake, 1408, 10, fake, None, 0, 1, 64, 8,
                               fake, None, fake, 1 << 20, None) == 1
@@ -105,26 +119,26 @@ def test_host_validation_rejects_before_launch(M):
                               1 << 24, None) == 2
     # append + topk: the indexer cache is required
     assert L.mla_append_indexer_topk(r_main, r_idx, fake, fake, fake, 1, fake, 6560, None, 0, 10,
-                                     None, None, None, 0, 0, fake, fake, 0.1, fake, 1, 64, 8,
+                                     None, None, None, 0, 0, 1, fake, fake, 0.1, fake, 1, 64, 8,
                                      fake, None, fake, 1 << 20, None) == 1
     # append + topk: the append half is validated too (unsupported main row format)
     assert L.mla_append_indexer_topk(_row(M, 9, 512), r_idx, fake, fake, fake, 1, fake, 6560, fake, 1408, 10,
-                                     None, None, None, 0, 0, fake, fake, 0.1, fake, 1, 64, 8,
+                                     None, None, None, 0, 0, 1, fake, fake, 0.1, fake, 1, 64, 8,
                                      fake, None, fake, 1 << 20, None) == 2
     # append + topk: and the top-k half (workspace too small)
     assert L.mla_append_indexer_topk(r_main, r_idx, fake, fake, fake, 1, C.c_void_p(0x10000), 6560,
-                                     C.c_void_p(0x10000), 1408, 10, None, None, None, 0, 0, fake, fake, 0.1,
+                                     C.c_void_p(0x10000), 1408, 10, None, None, None, 0, 0, 1, fake, fake, 0.1,
                                      fake, 1, 64, 8, fake, None, C.c_void_p(0x100000), 16, None) == 3
     # decode: d_v larger than the latent
-    assert L.mla_sparse_decode(r_main, 600, fake, fake, 6560, 10, fake, 4, None, None, 0, 0.1, None, 1, 128,
+    assert L.mla_sparse_decode(r_main, 600, fake, fake, 6560, 10, fake, 4, None, None, 0, 1, 0.1, None, 1, 128,
                                fake, fake, fake, 1 << 30, None) == 1
     # decode: workspace too small for the MFMA path
     assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
-                               None, None, 0, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
+                               None, None, 0, 1, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
                                C.c_void_p(0x100000), 64, None) == 3
     # decode: misaligned query
     assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10002), C.c_void_p(0x10000), 6560, 10, fake, 4,
-                               None, None, 0, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
+                               None, None, 0, 1, 0.1, None, 1, 128, C.c_void_p(0x10000), fake,
                                C.c_void_p(0x100000), 1 << 30, None) == 1
     # decode epilogue: misaligned sinks; output RoPE without its table, or of an unsupported width
     def epi(sinks, r, cs):
@@ -134,7 +148,7 @@ def test_host_validation_rejects_before_launch(M):
                               ((None, 12, 0x20000), 2), ((None, 512, 0x20000), 2)):
         keep, ep = epi(sk, r, cs)
         assert L.mla_sparse_decode(r_main, 512, C.c_void_p(0x10000), C.c_void_p(0x10000), 6560, 10, fake, 4,
-                                   None, None, 0, 0.1, ep, 1, 128, C.c_void_p(0x10000), fake,
+                                   None, None, 0, 1, 0.1, ep, 1, 128, C.c_void_p(0x10000), fake,
                                    C.c_void_p(0x100000), 1 << 30, None) == want, (sk, r, cs)
 
 

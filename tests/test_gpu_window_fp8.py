@@ -1,0 +1,73 @@
+"""MXFP8 window entries (E4M3 codes with one E8M0 scale per 32 channels: V4.1's
+528-byte window entry, [P1] "DeepSeek-V4.1"): the append writes the oracle's
+bytes exactly, and the decode over such a ring matches the oracle's attention
+over the dequantised entries (which are exact in bf16 for these inputs)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_latent_attention_mla_amd as M
+import workloads as WL
+from tests import gpu_cases as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _window_values(B, W, D, seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((W, B, D)) * np.exp2(rng.integers(-12, 12, (W, B, 1)))
+    v[0, 0, :32] = 0.0                                  # a block of zeros
+    v[1, 0, 5] = -0.0
+    v[2, 0, 32:64] *= np.exp2(np.arange(32) - 16)      # a wide block: subnormal E4M3 codes
+    v[3, 0, 64] = 1e6                                  # one dominant value per block
+    v[4, 0, 96:128] = 447.9                            # near the top of the E4M3 range
+    return v.astype(np.float32)
+
+
+C = WL.CONFIGS
+SMALL = {                                              # (V3.2's shapes given a window: 576-channel entries)
+    "c3w": C["c3"].with_(name="c3w", cid=123, B=2, N=6001, W=64),
+    "c4s": C["c4"].with_(name="c4s", cid=104, B=2, N=4099),
+    "c5s": C["c5"].with_(name="c5s", cid=105, B=1, N=3001),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_mxfp8_window_append_bytes_and_decode(name):
+    cfg = SMALL[name]
+    if cfg.W == 0:
+        pytest.skip("no window in this configuration")
+    print("mxfp8 window", name, flush=True)
+    case = G.build_case(cfg, seed=3)
+    B, W, D = cfg.B, cfg.W, cfg.dim + cfg.rope
+    vals = _window_values(B, W, D, cfg.cid + 31)
+    ring = torch.zeros((B, W, D + D // 32), dtype=torch.uint8, device=G.DEV)
+    mr, ir = G.main_row(cfg), G.idx_row(cfg)
+    for i in range(W):                                  # slot i <- window entry i
+        M.mla_kv_append_quant(mr, ir, None, None, None, None, None, G._t(vals[i]),
+                              G._t(np.full(B, i, np.int32)), ring)
+    torch.cuda.synchronize()
+    want = O.quant_rows(O.MXFP8, D, 0, vals.transpose(1, 0, 2).reshape(-1, D)).reshape(B, W, -1)
+    got = ring.cpu().numpy()
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:4].tolist()}"
+    # the oracle's attention over the dequantised entries, carried as bf16 (exact here)
+    deq = O.dequant_rows(O.MXFP8, D, 0, want.reshape(-1, D + D // 32))
+    as_bf16 = torch.from_numpy(deq.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(as_bf16.float().numpy().astype(np.float64), deq)
+    o_win = as_bf16.view(torch.int16).numpy().view(np.uint16).reshape(1, B, W, D)
+    case8 = dataclasses.replace(case, o_win=o_win, g_win=ring.unsqueeze(0))
+    rng = np.random.default_rng(cfg.cid + 37)            # any selection will do: distinct visible rows, some -1
+    idx = np.stack([rng.permutation(int(n))[:cfg.k] for n in case8.n_visible]).astype(np.int32)
+    idx[:, ::7] = -1
+    ref_o, ref_l = G.oracle_attention(case8, 0, idx)
+    got_o, got_l = G.gpu_decode(case8, 0, idx)
+    G.check_attention(got_o, got_l, ref_o, ref_l)
+    # the same entries as a bf16 ring give the same decode up to summation order
+    case16 = dataclasses.replace(case, o_win=o_win, g_win=as_bf16.reshape(1, B, W, D).to(G.DEV))
+    got16_o, got16_l = G.gpu_decode(case16, 0, idx)
+    np.testing.assert_allclose(got_o, got16_o, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(got_l, got16_l, rtol=1e-6, atol=1e-6)

@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--pool", type=int, default=0,
                    help="CSA2 group: the Full layer publishes a candidate pool of this many 8-position "
                         "blocks and the Reindex layer scores only the pool (hierarchical sparse indexer)")
+    p.add_argument("--win-fmt", default="bf16", choices=["bf16", "mxfp8"],
+                   help="window entries as bf16 or as MXFP8 (V4.1's 528-byte entry at 512 channels)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="replay each rotated layer's step from a HIP graph captured once (the stamped steps "
@@ -215,6 +217,16 @@ def main():
     n_layers = max(1, args.layers)
     log(f"config {cfg.name}: {cfg.desc}; building {n_layers} layer caches")
     layers = build_layers(cfg, n_layers)
+    win_fmt = M.MXFP8 if (cfg.W and args.win_fmt == "mxfp8") else M.BF16
+    if win_fmt == M.MXFP8:                                 # the same window values as MXFP8 entries
+        for X in layers:
+            ring8 = torch.zeros((X.win.shape[0], B, cfg.W, cfg.D + cfg.D // 32), dtype=torch.uint8, device=dev)
+            for l in range(X.win.shape[0]):
+                for s in range(cfg.W):
+                    M.mla_kv_append_quant(mr, ir, None, None, None, None, None, X.win[l, :, s].float().contiguous(),
+                                          torch.full((B,), s, dtype=torch.int32, device=dev), ring8[l])
+            X.win = ring8
+        torch.cuda.synchronize()
 
     # step buffers
     k = cfg.k
@@ -234,7 +246,7 @@ def main():
         full_scores = torch.empty((B, N), dtype=torch.float32, device=dev)
         pool_pos = torch.empty((B, pool * POOL_BLOCK), dtype=torch.int32, device=dev)
     ws_topk = torch.zeros(ws_size, dtype=torch.uint8, device=dev)
-    ws_dec = torch.empty(max(1, M.mla_sparse_decode_workspace(mr, cfg.d_v, B, H, k, cfg.W)), dtype=torch.uint8,
+    ws_dec = torch.empty(max(1, M.mla_sparse_decode_workspace(mr, cfg.d_v, B, H, k, cfg.W, win_fmt)), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()
 
@@ -366,17 +378,17 @@ def main():
         "breakdown pass (avg us): " +
         ", ".join(f"{k}={v['avg_us']:.2f}" for k, v in per_kernel.items()))
 
-    ab = WL.algorithmic_bytes(cfg, pool)
+    ab = WL.algorithmic_bytes(cfg, pool, win_fmt=win_fmt)
     step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: the first layer's indexer scan, which also carries its
     # quantise-append.  Per launch it must read every visible indexer row of the
     # batch plus the indexer queries and head weights, and read the new entries
     # and write their rows (the step's one entry per sequence: fp32 inputs in,
-    # quantised main row and indexer key out, and the first layer's bf16 window
+    # quantised main row and indexer key out, and the first layer's window
     # entry); the scores it writes for the selection are implementation traffic,
     # not counted.
     n_idx_layers = WL.n_indexers(cfg)
-    carried = B * (M.row_bytes(mr) + M.row_bytes(ir) + 4 * (cfg.D + cfg.d_I)) + (B * cfg.D * 6 if cfg.W else 0)
+    carried = B * (M.row_bytes(mr) + M.row_bytes(ir) + 4 * (cfg.D + cfg.d_I)) + (B * (4 * cfg.D + WL.window_entry_bytes(cfg, win_fmt)) if cfg.W else 0)
     scan_bytes = B * N * M.row_bytes(ir) + ab["q_idx_w"] // n_idx_layers + carried
     scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
     result = {
@@ -397,7 +409,7 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {cfg.desc}",
             "batch": B, "context_rows": N, "tokens": cfg.tokens, "heads": H, "qk_dim": cfg.D, "v_dim": cfg.d_v,
-            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "window": cfg.W, "layers_per_step": len(cfg.layers),
+            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "window": cfg.W, "window_format": args.win_fmt if cfg.W else None, "layers_per_step": len(cfg.layers),
             "main_row_bytes": M.row_bytes(mr), "indexer_row_bytes": M.row_bytes(ir),
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
             "candidate_pool": (f"{pool} blocks of {POOL_BLOCK} published by the Full layer, scored by the "

@@ -124,6 +124,24 @@ __device__ __forceinline__ void quant128_wave<MLA_FMT_MXFP4>(float v0, float v1,
     if ((l & 15) == 0) scales[l >> 4] = (uint8_t)code;
 }
 
+// MXFP8 quantisation of the first n (a multiple of 32, at most 128) channels
+// by one wave: lane l holds channels 2l and 2l + 1, a block of 32 channels is
+// a group of 16 lanes (its maximum by shuffles), codes[2l .. 2l + 1] and
+// scales[j] of block j are written; every byte equals quant_row's. `codes`
+// must be 2-byte aligned.
+__device__ __forceinline__ void quant_mx8_wave(float v0, float v1, int n, uint8_t* codes, uint8_t* scales) {
+    const int l = threadIdx.x & 63;
+    uint32_t m = max(f2u(fabsf(v0)), f2u(fabsf(v1)));
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    const uint32_t code = mx8_code(m);
+    const int sh = 127 - (int)code;
+    const uint32_t c0 = m == 0u ? 0u : e4m3_encode(__builtin_ldexpf(v0, sh));
+    const uint32_t c1 = m == 0u ? 0u : e4m3_encode(__builtin_ldexpf(v1, sh));
+    if (2 * l < n) reinterpret_cast<uint16_t*>(codes)[l] = (uint16_t)(c0 | (c1 << 8));
+    if ((l & 15) == 0 && 2 * l < n) scales[l >> 4] = (uint8_t)code;
+}
+
 // An entry cut into pieces of at most 128 channels that one wave each
 // quantises in registers (no LDS, no barrier): for entry e = (b, i), the main
 // row's 128-channel blocks, its RoPE part (at most 128 channels, bf16), the
@@ -147,7 +165,9 @@ __host__ inline int64_t piece_count(const AppendArgs& a) {
     return (int64_t)a.B * (a.n_new * m.per_entry + m.win_pieces);
 }
 __host__ inline bool pieces_supported(const AppendArgs& a) {
-    if (a.win_ring && a.win_fmt != MLA_FMT_BF16) return false;
+    if (a.win_ring && a.win_fmt == MLA_FMT_MXFP8 &&                 // 2-byte aligned entries
+        (((a.Dw / 32) & 1) != 0 || reinterpret_cast<uintptr_t>(a.win_ring) % 2 != 0))
+        return false;
     if (a.main_cache && !((a.main_fmt == MLA_FMT_E4M3_S128 && a.main_rope <= 128) ||
                           (a.main_fmt == MLA_FMT_E2M1_S16 && a.main_rope == 0)))
         return false;
@@ -209,6 +229,12 @@ __device__ __forceinline__ void piece_load(const AppendArgs& a, int64_t p, Piece
 __device__ __forceinline__ void piece_store(const AppendArgs& a, const Piece& pc) {
     const int l = threadIdx.x & 63;
     if (pc.kind == 0) return;
+    if (pc.kind == 4 && a.win_fmt == MLA_FMT_MXFP8) {      // window slice, MXFP8 (n % 32 == 0)
+        if (pc.slot < 0) return;
+        uint8_t* ent = reinterpret_cast<uint8_t*>(a.win_ring) + ((int64_t)pc.b * a.W + pc.slot % a.W) * (a.Dw + a.Dw / 32);
+        quant_mx8_wave(pc.v0, pc.v1, pc.n, ent + 128 * pc.part, ent + a.Dw + 4 * pc.part);
+        return;
+    }
     if (pc.kind == 4) {                                    // window slice, bf16
         if (pc.slot < 0) return;
         uint16_t* dst = a.win_ring + ((int64_t)pc.b * a.W + pc.slot % a.W) * a.Dw + 128 * pc.part;

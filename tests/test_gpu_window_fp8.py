@@ -71,3 +71,37 @@ def test_mxfp8_window_append_bytes_and_decode(name):
     got16_o, got16_l = G.gpu_decode(case16, 0, idx)
     np.testing.assert_allclose(got_o, got16_o, rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(got_l, got16_l, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["c3w", "c4s"])
+def test_mxfp8_window_in_the_carried_append(name):
+    """mla_append_indexer_topk with an MXFP8 ring: the window entry rides in the
+    scan's launch (one wave per 128-channel slice) and its bytes equal the oracle's."""
+    cfg = SMALL[name]
+    print("mxfp8 carried window", name, flush=True)
+    B, N, D, k = cfg.B, cfg.N, cfg.dim + cfg.rope, cfg.k
+    rng = np.random.default_rng(cfg.cid + 41)
+    mr, ir = G.main_row(cfg), G.idx_row(cfg)
+    main = torch.zeros((B, N, M.row_bytes(mr)), dtype=torch.uint8, device=G.DEV)
+    idx_c = torch.zeros((B, N, M.row_bytes(ir)), dtype=torch.uint8, device=G.DEV)
+    ring = torch.zeros((B, cfg.W, D + D // 32), dtype=torch.uint8, device=G.DEV)
+    vals = _window_values(B, 5, D, cfg.cid + 43)[2]         # entry 2: a wide block in sequence 0
+    vals[-1, :32] = 0.0                                    # and a block of zeros
+    pos = np.array([5 + 3 * b for b in range(B)], np.int32)
+    new_main = G._t(rng.standard_normal((B, 1, D)).astype(np.float32))
+    new_idx = G._t(rng.standard_normal((B, 1, cfg.d_I)).astype(np.float32))
+    slots = G._t(np.full((B, 1), N - 1, np.int32))
+    qi = G._qi_gpu(cfg, rng.standard_normal((B, cfg.H_I, cfg.d_I)).astype(np.float32))
+    w = G._t(rng.standard_normal((B, cfg.H_I)).astype(np.float32))
+    out_idx = torch.empty((B, k), dtype=torch.int32, device=G.DEV)
+    ws = torch.zeros(M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device=G.DEV)
+    M.mla_append_indexer_topk(mr, ir, new_main, new_idx, slots, main, idx_c, qi, w, cfg.sigma,
+                              G._t(np.full(B, N, np.int32)), k, out_idx, ws,
+                              new_win=G._t(vals), win_pos=G._t(pos), win_ring=ring)
+    torch.cuda.synchronize()
+    want = O.quant_rows(O.MXFP8, D, 0, vals)
+    got = ring.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b, pos[b] % cfg.W], want[b]), f"sequence {b}"
+        others = np.delete(got[b], pos[b] % cfg.W, axis=0)
+        assert not others.any(), "only the entry's slot is written"

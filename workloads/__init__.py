@@ -31,7 +31,7 @@ LIB = os.path.join(HERE, "libsynth.so")
 T_MAIN, T_IDX, T_Q, T_QIDX, T_W, T_WIN = 1, 2, 3, 4, 5, 6
 
 # row formats (numbering used by the library and the oracle alike)
-F32, BF16, E4M3_S128, E2M1_S16, MXFP4 = 0, 1, 2, 3, 4
+F32, BF16, E4M3_S128, E2M1_S16, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
 
 
 def build(verbose=False):
@@ -209,7 +209,12 @@ def step_inputs(cfg: Config, seed: int = 0) -> StepInputs:
     return StepInputs(cfg, main, idx, q, q_idx, w.astype(np.float32), win)
 
 
-def algorithmic_bytes(cfg: Config, pool_blocks: int = 0, block: int = 8) -> dict:
+def window_entry_bytes(cfg: Config, win_fmt: int = BF16) -> int:
+    """Bytes of one window entry: bf16, or MXFP8 (E4M3 codes + one E8M0 byte per 32 channels)."""
+    return cfg.D + cfg.D // 32 if win_fmt == MXFP8 else 2 * cfg.D
+
+
+def algorithmic_bytes(cfg: Config, pool_blocks: int = 0, block: int = 8, win_fmt: int = BF16) -> dict:
     """Bytes one decode step (layer group) must move, by part.  Materialised
     scores and split-K partials are excluded: they are implementation traffic.
     With pool_blocks > 0 the first indexer layer publishes a candidate pool of
@@ -227,10 +232,10 @@ def algorithmic_bytes(cfg: Config, pool_blocks: int = 0, block: int = 8) -> dict
         "q_idx_w": LI * B * cfg.H_I * (cfg.d_I * qb + 4),
         "indices": LI * B * cfg.k * 4 + L * B * cfg.k * 4,
         "gather": L * B * k_eff * rb_main,
-        "window": L * B * cfg.W * cfg.D * 2,
+        "window": L * B * cfg.W * window_entry_bytes(cfg, win_fmt),
         "q": L * B * cfg.H * cfg.D * qb,
         "out": L * B * cfg.H * (cfg.d_v + 1) * 4,
-        "append": B * (rb_main + rb_idx + 4 * (cfg.D + cfg.d_I)) + L * B * cfg.D * (4 + 2) * (cfg.W > 0),
+        "append": B * (rb_main + rb_idx + 4 * (cfg.D + cfg.d_I)) + L * B * (4 * cfg.D + window_entry_bytes(cfg, win_fmt)) * (cfg.W > 0),
     }
     if pool_blocks and LI > 1:
         parts["pool"] = B * pool_blocks * block * 4 * LI

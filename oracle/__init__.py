@@ -52,6 +52,8 @@ def lib():
                                     f32, P, i32, P, i32, i32, P, P]
         L.orc_attention.restype = i32
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i32
+        L.orc_compress.argtypes = [i32, i32, P, P, P, C.c_double, i32, P, i32, P]
+        L.orc_compress.restype = i32
         _lib = L
     return _lib
 
@@ -261,3 +263,19 @@ def attention(main_row, d_v, q, main_cache, idx, softmax_scale, win_ring=None, w
                              _p(_c(rope_cs, np.float32)), B, H, _p(out), _p(lse))
     _check(rc, "attention")
     return out, lse
+
+
+def compress(kv, gate, norm_weight=None, eps=1e-6, rope_cs=None):
+    """The CSA2 compressor: kv, gate fp32 [B, m, D] -> normalised, gated-pooled entries fp32 [B, D]
+    (rope_cs [B, r/2, 2] rotates the trailing r channels forward)."""
+    kv = _c(kv, np.float32)
+    gate = _c(gate, np.float32)
+    B, m, D = kv.shape
+    g = None if norm_weight is None else _c(norm_weight, np.float32)
+    cs = None if rope_cs is None else _c(rope_cs, np.float32)
+    r = 0 if cs is None else 2 * cs.shape[1]
+    out = np.empty((B, D), dtype=np.float32)
+    rc = lib().orc_compress(D, m, _p(kv), _p(gate), _p(g), float(eps), r, _p(cs), B, _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_compress failed ({rc})")
+    return out

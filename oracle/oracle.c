@@ -719,3 +719,58 @@ void orc_bf16_encode_n(const float* x, int64_t n, uint16_t* out) {
     int64_t i;
     for (i = 0; i < n; i++) out[i] = (uint16_t)orc_bf16_encode(x[i]);
 }
+
+/* ------------------------------------------------------------------------- */
+/* The CSA2 compressor at append ([P1] "DeepSeek-V4.1", "CSA2: the simplified
+ * compressor": windows of m tokens that do not overlap and no position bias;
+ * [P2] Part 2, the compressor's training-path code: a softmax of the gate over
+ * the window's m tokens per channel, the gated sum of the kv vectors, then the
+ * kv normalisation).  For each sequence b, from the already projected kv[b, i, c]
+ * and gate[b, i, c] (i < m, c < D):
+ *     w[i, c]   = exp(gate[i, c]) / sum_j exp(gate[j, c])
+ *     p[c]      = sum_i w[i, c] kv[i, c]
+ *     y[c]      = p[c] / sqrt(mean_c p[c]^2 + eps) * g[c]       (RMS normalisation)
+ * and, with rope_dim r > 0, the trailing r channels rotated forward at the
+ * window's position in the rotate-half pairing: x1 = y[D-r .. D-r/2),
+ * x2 = y[D-r/2 .. D): (x1 cos - x2 sin, x2 cos + x1 sin), (cos, sin) =
+ * rope_cs[b, i].  The normalisation is read as RMSNorm with a weight (the
+ * pages name kv_norm only); g == NULL means ones.  Output fp32 [B, D] (the
+ * fp64 result rounded).  Pins: m = 1 is the normalised kv; equal gates give
+ * the normalised mean (the mean-of-pairs stand-in at m = 2); a dominant gate
+ * selects its token; the weights sum to one; the rotation keeps pair norms and
+ * the output RoPE inverse undoes it. */
+int orc_compress(int D, int m, const float* kv, const float* gate, const float* g, double eps, int rope_dim,
+                 const float* rope_cs, int B, float* out) {
+    if (D <= 0 || m <= 0 || B < 0 || rope_dim < 0 || rope_dim > D || rope_dim % 2) return -1;
+    double* p = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!p) return -2;
+    for (int b = 0; b < B; b++) {
+        const float* K = kv + (int64_t)b * m * D;
+        const float* G = gate + (int64_t)b * m * D;
+        double ss = 0.0;
+        for (int c = 0; c < D; c++) {
+            double mx = -INFINITY, den = 0.0, num = 0.0;
+            for (int i = 0; i < m; i++)
+                if ((double)G[(int64_t)i * D + c] > mx) mx = G[(int64_t)i * D + c];
+            for (int i = 0; i < m; i++) {
+                double e = exp((double)G[(int64_t)i * D + c] - mx);
+                den += e;
+                num += e * (double)K[(int64_t)i * D + c];
+            }
+            p[c] = num / den;
+            ss += p[c] * p[c];
+        }
+        const double inv = 1.0 / sqrt(ss / D + eps);
+        for (int c = 0; c < D; c++) p[c] = p[c] * inv * (g ? (double)g[c] : 1.0);
+        const int h = rope_dim / 2;
+        for (int i = 0; i < h; i++) {
+            const double cs = rope_cs[((int64_t)b * h + i) * 2], sn = rope_cs[((int64_t)b * h + i) * 2 + 1];
+            const double x1 = p[D - rope_dim + i], x2 = p[D - h + i];
+            p[D - rope_dim + i] = x1 * cs - x2 * sn;
+            p[D - h + i] = x2 * cs + x1 * sn;
+        }
+        for (int c = 0; c < D; c++) out[(int64_t)b * D + c] = (float)p[c];
+    }
+    free(p);
+    return 0;
+}

@@ -58,6 +58,8 @@ int orc_topk(const float* scores, int64_t n_rows, const int32_t* n_visible,
              const int32_t* cand, int n_cand, int B, int k, int32_t* out_idx);
 
 /* Sparse absorbed-MLA attention over the selected rows plus the window. */
+int orc_compress(int D, int m, const float* kv, const float* gate, const float* g, double eps, int rope_dim,
+                 const float* rope_cs, int B, float* out);
 int orc_attention(int main_fmt, int main_dim, int main_rope, int d_v,
                   const float* q, const uint8_t* main_cache, int64_t main_seq_stride, int64_t capacity,
                   const int32_t* idx, int k,

@@ -186,6 +186,39 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
                                  void* stream);
 
 /*
+ * mla_compress_append -- the CSA2 compressor at append, fused with the quantise-append.
+ *
+ * V4.1 pools each window of m tokens into one cache entry, the windows not
+ * overlapping and with no position bias ([P1] "DeepSeek-V4.1", "CSA2: the
+ * simplified compressor"; [P2] Part 2, the compressor's training-path code).
+ * For each sequence b, from the projected kv[b, i, :] and gate[b, i, :] of the
+ * window's tokens i < m (D = main_row.dim + main_row.rope_dim channels):
+ *     w[i, c] = softmax over i of gate[i, c]        p[c] = sum_i w[i, c] kv[i, c]
+ *     y[c]    = p[c] / sqrt(mean_c p[c]^2 + eps) * norm_weight[c]
+ * then, with rope_dim r > 0, the trailing r channels are rotated forward at the
+ * window's position (rotate-half pairing: x1 = y[D-r .. D-r/2), x2 = y[D-r/2 .. D),
+ * pair i becomes (x1 cos - x2 sin, x2 cos + x1 sin), (cos, sin) = rope_cs[b, i]),
+ * and y is quantised into main_cache at row slots[b] exactly as mla_kv_append_quant
+ * quantises an entry. The kv / gate projections and the indexer key's projection
+ * from the entry are the caller's matmuls; out_entry returns y in fp32 for the latter.
+ *
+ *  kv, gate           fp32 [B, m, D], m >= 1
+ *  norm_weight        fp32 [D], or NULL (ones); eps >= 0
+ *  rope_dim, rope_cs  0 / NULL, or r even, r <= D, with fp32 [B, r/2, 2] (cos, sin)
+ *  slots              int32 [B] rows in [0, capacity) (others are skipped); NULL with
+ *                     main_cache NULL (no cache write)
+ *  main_cache         rows as in mla_kv_append_quant, or NULL; main_seq_stride its stride
+ *  out_entry          fp32 [B, D], or NULL
+ * Works in fp32 (the softmax online over the tokens). D <= 2048.
+ * Errors: MLA_ERR_INVALID_ARG for negative sizes, missing pointers, m < 1, eps < 0,
+ * an odd or too large rope_dim; MLA_ERR_UNSUPPORTED for an unsupported row or D > 2048.
+ */
+mla_status_t mla_compress_append(mla_row_t main_row, const float* kv, const float* gate, int32_t m,
+                                 const float* norm_weight, float eps, int32_t rope_dim, const float* rope_cs,
+                                 const int32_t* slots, int32_t B, int64_t capacity,
+                                 void* main_cache, int64_t main_seq_stride, float* out_entry, void* stream);
+
+/*
  * mla_indexer_topk -- lightning-indexer scan, causal mask and top-k.
  *
  * For every sequence b and cached row s < n_visible[b]:

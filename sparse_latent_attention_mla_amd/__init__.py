@@ -59,6 +59,8 @@ def lib():
                                           P, P, P, i32, i32, i32, P]
         L.mla_kv_append_quant.restype = i32
         L.mla_indexer_topk_workspace.argtypes, L.mla_indexer_topk_workspace.restype = [i32, i64, i32], sz
+        L.mla_compress_append.argtypes = [_CRow, P, P, i32, P, f32, i32, P, P, i32, i64, P, i64, P, P]
+        L.mla_compress_append.restype = i32
         L.mla_indexer_topk.argtypes = [_CRow, P, P, f32, P, i64, i64, P, P, i32, i32, i32, i32,
                                        P, P, P, sz, P]
         L.mla_indexer_topk.restype = i32
@@ -206,6 +208,41 @@ def mla_kv_append_quant(main_row: Row, idx_row: Row, new_main, new_idx, slots,
         _ptr(main_cache), _cache_stride(main_cache, "main_cache"),
         _ptr(idx_cache), _cache_stride(idx_cache, "idx_cache"),
         _ptr(new_win), _ptr(win_pos), _ptr(win_ring), W, Dw, wfmt, _stream(stream)))
+
+
+def mla_compress_append(main_row: Row, kv, gate, main_cache=None, slots=None, norm_weight=None, eps=1e-6,
+                        rope_cs=None, out_entry=None, stream=None):
+    """The CSA2 compressor at append: kv, gate fp32 [B, m, D] -> one normalised, gated-pooled entry
+    per sequence, quantised into main_cache uint8 [B, capacity, row_bytes] at slots int32 [B] and/or
+    returned in out_entry fp32 [B, D]; norm_weight fp32 [D]; rope_cs fp32 [B, r/2, 2]."""
+    _need(kv, "kv", torch.float32, 3)
+    _need(gate, "gate", torch.float32, 3)
+    B, m, D = kv.shape
+    if tuple(gate.shape) != (B, m, D) or D != main_row.dim + main_row.rope:
+        raise ValueError("kv and gate [B, m, dim + rope] expected")
+    capacity = stride = 0
+    if main_cache is not None:
+        _need(slots, "slots", torch.int32, 1)
+        if main_cache.shape[0] != B or main_cache.shape[2] != row_bytes(main_row) or tuple(slots.shape) != (B,):
+            raise ValueError("main_cache [B, capacity, row_bytes] and slots [B] expected")
+        capacity, stride = main_cache.shape[1], _cache_stride(main_cache, "main_cache")
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", torch.float32, 1)
+        if tuple(norm_weight.shape) != (D,):
+            raise ValueError("norm_weight [D] expected")
+    r = 0
+    if rope_cs is not None:
+        _need(rope_cs, "rope_cs", torch.float32, 3)
+        if rope_cs.shape[0] != B or rope_cs.shape[2] != 2:
+            raise ValueError("rope_cs [B, r/2, 2] expected")
+        r = 2 * rope_cs.shape[1]
+    if out_entry is not None:
+        _need(out_entry, "out_entry", torch.float32, 2)
+        if tuple(out_entry.shape) != (B, D):
+            raise ValueError("out_entry [B, D] expected")
+    _check(lib().mla_compress_append(_crow(main_row), _ptr(kv), _ptr(gate), m, _ptr(norm_weight), float(eps), r,
+                                     _ptr(rope_cs), _ptr(slots), B, capacity, _ptr(main_cache), stride,
+                                     _ptr(out_entry), _stream(stream)))
 
 
 def mla_indexer_topk_workspace(B: int, capacity: int, k: int) -> int:

@@ -298,6 +298,48 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const fl
     return hip_status(mla::launch_append(a, st), "append launch");
 }
 
+mla_status_t mla_compress_append(mla_row_t main_row, const float* kv, const float* gate, int32_t m,
+                                 const float* norm_weight, float eps, int32_t rope_dim, const float* rope_cs,
+                                 const int32_t* slots, int32_t B, int64_t capacity, void* main_cache,
+                                 int64_t main_seq_stride, float* out_entry, void* stream) {
+    if (B < 0 || m < 1 || !(eps >= 0.0f) || capacity < 0)
+        return fail(MLA_ERR_INVALID_ARG, "compress: need B >= 0, m >= 1, eps >= 0, capacity >= 0");
+    const int64_t rb = mla_row_bytes(main_row);
+    if (rb < 0 || main_row.fmt == MLA_FMT_MXFP8) return fail(MLA_ERR_UNSUPPORTED, "compress: unsupported row format");
+    const int D = main_row.dim + main_row.rope_dim;
+    if (D > 2048) return fail(MLA_ERR_UNSUPPORTED, "compress: more than 2048 channels");
+    if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D || (rope_dim > 0 && !rope_cs))
+        return fail(MLA_ERR_INVALID_ARG, "compress: rope_dim must be even, <= D, with rope_cs");
+    if (B == 0) return ok();
+    if (!kv || !gate) return fail(MLA_ERR_INVALID_ARG, "compress: kv and gate are required");
+    if (main_cache) {
+        int64_t rb2 = 0;
+        const mla_status_t s = check_rows("compress", main_row, main_cache, main_seq_stride, capacity, B, &rb2);
+        if (s != MLA_OK) return s;
+        if (!slots) return fail(MLA_ERR_INVALID_ARG, "compress: slots is NULL");
+    }
+    mla::CompressArgs a{};
+    a.fmt = main_row.fmt;
+    a.dim = main_row.dim;
+    a.rope = main_row.rope_dim;
+    a.row_bytes = rb;
+    a.kv = kv;
+    a.gate = gate;
+    a.g = norm_weight;
+    a.eps = eps;
+    a.m = m;
+    a.D = D;
+    a.rope_dim = rope_dim;
+    a.rope_cs = rope_cs;
+    a.slots = main_cache ? slots : nullptr;
+    a.capacity = capacity;
+    a.cache = static_cast<uint8_t*>(main_cache);
+    a.stride = main_seq_stride;
+    a.out = out_entry;
+    a.B = B;
+    return hip_status(mla::launch_compress(a, static_cast<hipStream_t>(stream)), "compress launch");
+}
+
 size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
     (void)k;
     return topk_layout(B, capacity).total;

@@ -46,6 +46,26 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
+// The CSA2 compressor at append (compress.hip).
+struct CompressArgs {
+    int fmt, dim, rope;     // main row format (D = dim + rope channels)
+    int64_t row_bytes;
+    const float* kv;        // [B, m, D]
+    const float* gate;      // [B, m, D]
+    const float* g;         // [D] normalisation weight, or null (ones)
+    float eps;
+    int m, D;
+    int rope_dim;           // trailing channels rotated forward (0: none)
+    const float* rope_cs;   // [B, rope_dim / 2, 2] (cos, sin)
+    const int32_t* slots;   // [B] row of the entry, or null (no cache write)
+    int64_t capacity;
+    uint8_t* cache;
+    int64_t stride;
+    float* out;             // [B, D] fp32 entries, or null
+    int B;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+
 // Workspace of the indexer + top-k, carved by the host (all 256-byte aligned).
 struct TopkWorkspace {
     float* scores;          // [B, capacity] (used when the caller gives no score buffer)

@@ -27,8 +27,8 @@ def M():
 
 def test_header_declares_the_three_path_calls():
     names = declared_functions()
-    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode", "mla_append_indexer_topk",
-              "mla_indexer_pool"):
+    for n in ("mla_kv_append_quant", "mla_indexer_topk", "mla_sparse_decode", "mla_append_indexer_topk", "mla_compress_append",
+              "mla_indexer_pool", "mla_compress_append"):
         assert n in names
 
 
@@ -85,6 +85,12 @@ def test_host_validation_rejects_before_launch(M):
     wb = L.mla_sparse_decode_workspace(r_main, 512, 4, 128, 2048, 128, M.BF16)
     w8 = L.mla_sparse_decode_workspace(r_main, 512, 4, 128, 2048, 128, M.MXFP8)
     assert w8 == wb + 4 * 128 * 576 * 2
+    # compress: an empty window, negative eps, an odd rotation width, more than 2048 channels
+    assert L.mla_compress_append(r_main, fake, fake, 0, None, 1e-6, 0, None, None, 1, 0, None, 0, fake, None) == 1
+    assert L.mla_compress_append(r_main, fake, fake, 2, None, -1.0, 0, None, None, 1, 0, None, 0, fake, None) == 1
+    assert L.mla_compress_append(r_main, fake, fake, 2, None, 1e-6, 3, fake, None, 1, 0, None, 0, fake, None) == 1
+    assert L.mla_compress_append(_row(M, M.BF16, 4096), fake, fake, 2, None, 1e-6, 0, None, None, 1, 0, None, 0,
+                                 fake, None) == 2
     # topk: score scale must be positive
     assert L.mla_indexer_topk(r_idx, fake, fake, 0.0, fake, 1408, 10, fake, None, 0, 1, 64, 8,
                               fake, None, fake, 1 << 20, None) == 1

@@ -43,6 +43,8 @@ def parse():
                         "blocks and the Reindex layer scores only the pool (hierarchical sparse indexer)")
     p.add_argument("--win-fmt", default="bf16", choices=["bf16", "mxfp8"],
                    help="window entries as bf16 or as MXFP8 (V4.1's 528-byte entry at 512 channels)")
+    p.add_argument("--compress", type=int, default=0, metavar="M",
+                   help="pool the step's main entry from M tokens with the CSA2 compressor (mla_compress_append)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="replay each rotated layer's step from a HIP graph captured once (the stamped steps "
@@ -218,6 +220,11 @@ def main():
     log(f"config {cfg.name}: {cfg.desc}; building {n_layers} layer caches")
     layers = build_layers(cfg, n_layers)
     win_fmt = M.MXFP8 if (cfg.W and args.win_fmt == "mxfp8") else M.BF16
+    if args.compress:                                      # the window's projected kv and gate vectors
+        for i, X in enumerate(layers):
+            X.comp_kv = torch.from_numpy(WL.normal(0, cfg.cid, 200 + 2 * i, (B, args.compress, cfg.D))).to(dev)
+            X.comp_gate = torch.from_numpy(WL.normal(0, cfg.cid, 201 + 2 * i, (B, args.compress, cfg.D))).to(dev)
+        comp_norm = torch.ones(cfg.D, dtype=torch.float32, device=dev)
     if win_fmt == M.MXFP8:                                 # the same window values as MXFP8 entries
         for X in layers:
             ring8 = torch.zeros((X.win.shape[0], B, cfg.W, cfg.D + cfg.D // 32), dtype=torch.uint8, device=dev)
@@ -250,6 +257,7 @@ def main():
                          device=dev)
     stream = torch.cuda.current_stream()
 
+    slots1 = slots[:, 0].contiguous()
     def step(X, stamp=False):
         """One layer-step (or CSA2 group) on layer caches X: the first layer appends the
         step's entry (main row, indexer key) and every layer its window entry; Full and
@@ -263,11 +271,15 @@ def main():
             first = l == 0
             win = (X.new_win[l], win_pos, X.win[l]) if cfg.W else (None, None, None)
             selects = mode in ("full", "reindex")
+            if first and args.compress:                    # the main entry pooled from the window's tokens
+                M.mla_compress_append(mr, X.comp_kv, X.comp_gate, X.main, slots1, comp_norm, 1e-6)
             if first and selects:
                 latest = idx_out[j % 2]
                 if stamp:
                     M.mla_profile_enable(("indexer_scan",))
-                M.mla_append_indexer_topk(mr, ir, X.new_main, X.new_idx, slots, X.main, X.idx, X.q_idx[j],
+                own_main = not args.compress
+                M.mla_append_indexer_topk(mr, ir, X.new_main if own_main else None, X.new_idx, slots,
+                                          X.main if own_main else None, X.idx, X.q_idx[j],
                                           X.w[j], cfg.sigma, nvis, k, latest, ws_topk,
                                           new_win=win[0], win_pos=win[1], win_ring=win[2],
                                           out_scores=full_scores if pool else None)
@@ -379,6 +391,9 @@ def main():
         ", ".join(f"{k}={v['avg_us']:.2f}" for k, v in per_kernel.items()))
 
     ab = WL.algorithmic_bytes(cfg, pool, win_fmt=win_fmt)
+    if args.compress:                                      # m tokens' kv and gate in place of one fp32 entry
+        ab["compress"] = B * args.compress * cfg.D * 8 + cfg.D * 4 - B * cfg.D * 4
+        ab["total"] += ab["compress"]
     step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
     # dominant kernel: the first layer's indexer scan, which also carries its
     # quantise-append.  Per launch it must read every visible indexer row of the
@@ -409,7 +424,7 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {cfg.desc}",
             "batch": B, "context_rows": N, "tokens": cfg.tokens, "heads": H, "qk_dim": cfg.D, "v_dim": cfg.d_v,
-            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "window": cfg.W, "window_format": args.win_fmt if cfg.W else None, "layers_per_step": len(cfg.layers),
+            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "window": cfg.W, "window_format": args.win_fmt if cfg.W else None, "compress_m": args.compress or None, "layers_per_step": len(cfg.layers),
             "main_row_bytes": M.row_bytes(mr), "indexer_row_bytes": M.row_bytes(ir),
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
             "candidate_pool": (f"{pool} blocks of {POOL_BLOCK} published by the Full layer, scored by the "

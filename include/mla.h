@@ -204,7 +204,7 @@ mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row,
  *
  *  kv, gate           fp32 [B, m, D], m >= 1
  *  norm_weight        fp32 [D], or NULL (ones); eps >= 0
- *  rope_dim, rope_cs  0 / NULL, or r even, r <= D, with fp32 [B, r/2, 2] (cos, sin)
+ *  rope_dim, rope_cs  0 / NULL, or r even, r <= min(D, 512), with fp32 [B, r/2, 2] (cos, sin)
  *  slots              int32 [B] rows in [0, capacity) (others are skipped); NULL with
  *                     main_cache NULL (no cache write)
  *  main_cache         rows as in mla_kv_append_quant, or NULL; main_seq_stride its stride

@@ -310,6 +310,7 @@ mla_status_t mla_compress_append(mla_row_t main_row, const float* kv, const floa
     if (D > 2048) return fail(MLA_ERR_UNSUPPORTED, "compress: more than 2048 channels");
     if (rope_dim < 0 || rope_dim % 2 != 0 || rope_dim > D || (rope_dim > 0 && !rope_cs))
         return fail(MLA_ERR_INVALID_ARG, "compress: rope_dim must be even, <= D, with rope_cs");
+    if (rope_dim > 512) return fail(MLA_ERR_UNSUPPORTED, "compress: rope_dim above 512");
     if (B == 0) return ok();
     if (!kv || !gate) return fail(MLA_ERR_INVALID_ARG, "compress: kv and gate are required");
     if (main_cache) {

@@ -91,6 +91,8 @@ def test_host_validation_rejects_before_launch(M):
     assert L.mla_compress_append(r_main, fake, fake, 2, None, 1e-6, 3, fake, None, 1, 0, None, 0, fake, None) == 1
     assert L.mla_compress_append(_row(M, M.BF16, 4096), fake, fake, 2, None, 1e-6, 0, None, None, 1, 0, None, 0,
                                  fake, None) == 2
+    assert L.mla_compress_append(_row(M, M.BF16, 2048), fake, fake, 2, None, 1e-6, 1024, fake, None, 1, 0, None, 0,
+                                 fake, None) == 2
     # topk: score scale must be positive
     assert L.mla_indexer_topk(r_idx, fake, fake, 0.0, fake, 1408, 10, fake, None, 0, 1, 64, 8,
                               fake, None, fake, 1 << 20, None) == 1

@@ -236,7 +236,10 @@ mla_status_t mla_compress_append(mla_row_t main_row, const float* kv, const floa
  *  w            fp32 [B, H_I], the per-head weights already scaled by the caller
  *               (the V3.2 code multiplies them by H_I^-0.5)
  *  score_scale  sigma > 0 applied inside the ReLU (d_I^-0.5 in the V3.2 code)
- *  idx_cache    indexer rows, row s of sequence b at b*idx_seq_stride + s*row_bytes
+ *  idx_cache    indexer rows, row s of sequence b at b*idx_seq_stride + s*row_bytes;
+ *               idx_seq_stride 0 makes every batch row read the same sequence: several
+ *               queries of one sequence in one call (multi-token prediction), each with its
+ *               own q_idx, w and n_visible (its causal limit)
  *  capacity     rows allocated per sequence (the scan covers rows < n_visible[b] <= capacity)
  *  n_visible    int32 [B] on the device, each in [0, capacity]
  *  cand, n_cand NULL and 0: every row is a candidate.  Otherwise a candidate pool
@@ -359,7 +362,9 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
  *
  *  main_row    main row format; d_v <= dim
  *  q           [B, H, dim+rope] bf16 (fp32 when main_row.fmt == MLA_FMT_F32)
- *  main_cache  rows as in mla_kv_append_quant; capacity rows per sequence
+ *  main_cache  rows as in mla_kv_append_quant; capacity rows per sequence; main_seq_stride
+ *              0 makes every batch row read the same sequence (several queries of one
+ *              sequence, each with its own q, idx and window rows)
  *  idx         int32 [B, k]: positions in [0, capacity) or -1 (skipped); duplicates
  *              are attended twice
  *  win_ring    optional window entries (K = V) in format win_fmt: bf16 [B, W, dim+rope]

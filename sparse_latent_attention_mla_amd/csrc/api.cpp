@@ -45,8 +45,10 @@ int64_t row_alignment(int64_t row_bytes) {
     return a;
 }
 
+// shared: a stride of 0 is accepted (every batch row reads the same sequence's
+// rows: several queries of one sequence); only for calls that do not write rows.
 mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int64_t stride, int64_t capacity,
-                        int B, int64_t* row_bytes) {
+                        int B, int64_t* row_bytes, bool shared = false) {
     const int64_t rb = mla_row_bytes(row);
     if (rb < 0)
         return fail(MLA_ERR_UNSUPPORTED, "%s: unsupported row format (fmt %d, dim %d, rope %d)", what, row.fmt,
@@ -54,7 +56,7 @@ mla_status_t check_rows(const char* what, mla_row_t row, const void* cache, int6
     *row_bytes = rb;
     if (!cache) return ok();
     if (capacity < 0) return fail(MLA_ERR_INVALID_ARG, "%s: capacity < 0", what);
-    if (B > 1 && stride < capacity * rb)
+    if (B > 1 && stride < capacity * rb && !(shared && stride == 0))
         return fail(MLA_ERR_INVALID_ARG, "%s: sequence stride %lld < capacity * row bytes %lld", what,
                     (long long)stride, (long long)(capacity * rb));
     const int64_t ra = row_alignment(rb);
@@ -169,7 +171,7 @@ mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, flo
         return ok();
     }
     int64_t rb = 0;
-    mla_status_t s = check_rows("indexer_topk", idx_row, idx_cache, idx_seq_stride, capacity, B, &rb);
+    mla_status_t s = check_rows("indexer_topk", idx_row, idx_cache, idx_seq_stride, capacity, B, &rb, true);
     if (s != MLA_OK) return s;
     if (!q_idx || !w || !idx_cache || !n_visible || !out_idx)
         return fail(MLA_ERR_INVALID_ARG, "indexer_topk: a required pointer is NULL");
@@ -454,7 +456,7 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
     const int D = main_row.dim + main_row.rope_dim;
     if (d_v <= 0 || d_v > main_row.dim) return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need 0 < d_v <= dim");
     int64_t rb = 0;
-    mla_status_t s = check_rows("sparse_decode", main_row, main_cache, main_seq_stride, capacity, B, &rb);
+    mla_status_t s = check_rows("sparse_decode", main_row, main_cache, main_seq_stride, capacity, B, &rb, true);
     if (s != MLA_OK) return s;
     if (B == 0) return ok();
     if (!q || !out || !lse || (k > 0 && (!idx || !main_cache)))

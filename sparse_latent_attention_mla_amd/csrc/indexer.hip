@@ -1444,7 +1444,10 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         rpb = ((rpb + 4 * kChunkRows - 1) / (4 * kChunkRows)) * (4 * kChunkRows);
         const dim3 sgrid((unsigned)((a.capacity + rpb - 1) / rpb), a.B);
         // LDS-DMA scan: 16-byte aligned cache and stride; about kDmaBlocksPerCu blocks per CU
-        const bool dma = (reinterpret_cast<uintptr_t>(a.cache) % 16 == 0) && (a.stride % 16 == 0);
+        // (and a sequence's rows end on a 16-byte boundary: the chunk that holds the last
+        // row loads whole 16-byte pieces up to the sequence's end, none beyond it)
+        const bool dma = (reinterpret_cast<uintptr_t>(a.cache) % 16 == 0) && (a.stride % 16 == 0) &&
+                         (a.capacity * a.row_bytes) % 16 == 0;
         // MLA_SCAN_BLOCKS overrides the target number of blocks (for tuning)
         int64_t dma_target = 256 * kDmaBlocksPerCu;
         if (const char* e = getenv("MLA_SCAN_BLOCKS")) {

@@ -61,8 +61,12 @@ def test_compress_matches_the_oracle(case):
         assert same > 0.98, same
         d_got = O.dequant_rows(ORC_FMT[fmt], dim, rope, rows)
         d_ref = O.dequant_rows(ORC_FMT[fmt], dim, rope, want)
-        step = np.max(np.abs(d_ref)) / 2                # at most one code step apart
-        assert np.max(np.abs(d_got - d_ref)) <= step
+        # at most one rung apart: every format's gap at a value is at most half the
+        # largest magnitude of the 16 channels around it
+        n = (dim // 16) * 16
+        blk = np.abs(d_ref[:, :n]).reshape(B, -1, 16).max(-1, keepdims=True)
+        diff = np.abs(d_got[:, :n] - d_ref[:, :n]).reshape(B, -1, 16)
+        assert np.all(diff <= 0.5 * blk)
 
 
 @pytest.mark.parametrize("fmt", [M.E2M1_S16, M.E4M3_S128, M.BF16, M.MXFP4])

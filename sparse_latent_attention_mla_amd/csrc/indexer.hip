@@ -42,6 +42,8 @@ constexpr int kDmaRowsPerWave4 = MLA_SCAN_RPW4;   // the same for the four-bit k
 #endif
 constexpr int kDmaNbuf4 = MLA_SCAN_NBUF4;          // ring depth of the 32x32 scan for the four-bit keys
 template <int FMT>
+constexpr int dma32_chunk_rows() { return FMT == MLA_FMT_E4M3_S128 ? kDmaRows : 2 * kDmaRows; }
+template <int FMT>
 constexpr int dma32_rows_per_wave() { return FMT == MLA_FMT_E4M3_S128 ? kDmaRowsPerWave : kDmaRowsPerWave4; }
 #ifndef MLA_SCAN_WAVES
 #define MLA_SCAN_WAVES 4                  // waves per block of the 32x32 scan (4 or 8)
@@ -599,7 +601,9 @@ template <int FMT, int MT2, int NBUF, int NW, bool FUSE>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block, AppendArgs ap) {
     constexpr int NT = 64 * NW;                          // threads of the block
     constexpr int RB = idx_rb<FMT>();
-    constexpr int kBytes = kDmaRows * RB;                 // 4224 / 2304
+    constexpr int CR = dma32_chunk_rows<FMT>();            // rows per chunk: 32 (E4M3) or 64 (four-bit rows)
+    constexpr int TPC = CR / 32;                           // 32-row tiles per chunk
+    constexpr int kBytes = CR * RB;                        // 4224 / 4608 / 4352
     constexpr int KI = (kBytes + 1023) / 1024;           // DMA instructions per chunk: 5 / 3
     constexpr int kBuf = (KI * 1024 > 5120) ? KI * 1024 : 5120;   // also one head tile of queries + weights
     static_assert(kBytes % 16 == 0, "chunk of 16-byte pieces");
@@ -635,25 +639,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
                 const int64_t sl = ap.slots[(int64_t)b * ap.n_new + e];
                 const int64_t local = sl - row0;
                 if (sl >= 0 && sl < cap && local >= 0 && local < rows_per_block) {
-                    const int ci = (int)(local >> 5);
+                    const int ci = (int)(local / CR);
                     if (ci % NW == wave) {
                         own_it[e] = ci / NW;
-                        own_r[e] = (int)(local & 31);
+                        own_r[e] = (int)(local % CR);
                     }
                 }
             }
         }
     }
-    const int n_it = rows_per_block / (NW * kDmaRows);
+    const int n_it = rows_per_block / (NW * CR);
     for (int i = threadIdx.x; i < kHistBins / 2; i += NT) hist2[i] = 0u;
     if (threadIdx.x < kCoarseBins) coarse[threadIdx.x] = 0u;
 
     const uint8_t* base = a.cache + b * a.stride;
-    auto chunk_row = [&](int it) { return row0 + (int64_t)(NW * it + wave) * kDmaRows; };
+    auto chunk_row = [&](int it) { return row0 + (int64_t)(NW * it + wave) * CR; };
     auto chunks_below = [&](int64_t lim) {
-        const int64_t d = lim - row0 - (int64_t)wave * kDmaRows;
+        const int64_t d = lim - row0 - (int64_t)wave * CR;
         if (d <= 0) return 0;
-        const int64_t n = (d + NW * kDmaRows - 1) / (NW * kDmaRows);
+        const int64_t n = (d + NW * CR - 1) / (NW * CR);
         return (int)(n < n_it ? n : n_it);
     };
     const int n_dma = chunks_below(nvis);
@@ -784,18 +788,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
         float mult;
         uint32_t ks;                                       // MXFP4: the E8M0 codes of blocks 2h, 2h + 1
     };
-    auto fetch = [&](int c, ChunkIn& in) {
-        if (NBUF == 3 && c + 1 < n_dma) wait_vmcnt<KI>();
-        else wait_vmcnt<0>();
-        if (c + NBUF - 1 < n_dma) issue(c + NBUF - 1);
-        if constexpr (FUSE) {                              // a new entry's row: its bytes over the stale ones
+    // (tile t of chunk t / TPC: the chunk's wait, its successor's issue and the
+    // new entries' rows happen at its first tile)
+    auto fetch = [&](int t, ChunkIn& in) {
+        const int c = t / TPC;
+        if (t % TPC == 0) {
+            if (NBUF == 3 && c + 1 < n_dma) wait_vmcnt<KI>();
+            else wait_vmcnt<0>();
+            if (c + NBUF - 1 < n_dma) issue(c + NBUF - 1);
+            if constexpr (FUSE) {                          // a new entry's row: its bytes over the stale ones
 #pragma unroll
-            for (int e = 0; e < kFuseMaxNew; ++e)
-                if (own_it[e] == c && lane < RB / 4)
-                    reinterpret_cast<uint32_t*>(&ring[wave][c % NBUF][0] + own_r[e] * RB)[lane] =
-                        reinterpret_cast<const uint32_t*>(&fuse_row[e][0])[lane];
+                for (int e = 0; e < kFuseMaxNew; ++e)
+                    if (own_it[e] == c && lane < RB / 4)
+                        reinterpret_cast<uint32_t*>(&ring[wave][c % NBUF][0] + own_r[e] * RB)[lane] =
+                            reinterpret_cast<const uint32_t*>(&fuse_row[e][0])[lane];
+            }
         }
-        const uint8_t* rp = &ring[wave][c % NBUF][0] + n32 * RB;
+        const uint8_t* rp = &ring[wave][c % NBUF][0] + ((t % TPC) * 32 + n32) * RB;
         in.mult = 1.0f;
         if constexpr (FMT == MLA_FMT_E4M3_S128) {
             uint32_t w[16];
@@ -820,8 +829,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
         }
     };
     ChunkIn cur;
-    if (n_dma > 0) fetch(0, cur);
-    for (int c = 0; c < n_dma; ++c) {
+    const int n_tiles = TPC * n_dma;
+    if (n_tiles > 0) fetch(0, cur);
+    for (int tt = 0; tt < n_tiles; ++tt) {
         f32x16 acc[MT2];
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt) {
@@ -843,7 +853,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
                                                       : mfma32_bf16(qa[mt][s], cur.kb[s], acc[mt]);
         }
         const float mult = cur.mult;
-        if (c + 1 < n_dma) fetch(c + 1, cur);
+        if (tt + 1 < n_tiles) fetch(tt + 1, cur);
         // sum_j w_j ReLU(sigma * mult * d_j) = mult * sum_j (w_j sigma) ReLU(d_j)  (sigma, mult >= 0)
         float pm[MT2][4];
 #pragma unroll
@@ -858,7 +868,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt) part += (pm[mt][0] + pm[mt][1]) + (pm[mt][2] + pm[mt][3]);
         const float score = xsum2(part) * mult;
-        const int lrow = (NW * c + wave) * kDmaRows + n32;  // row within the block
+        const int lrow = (NW * (tt / TPC) + wave) * CR + (tt % TPC) * 32 + n32;  // row within the block
         if (h == 0) {
             const bool valid = row0 + lrow < nvis;
             sc[lrow] = valid ? score : -__builtin_inff();
@@ -871,7 +881,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     }
     if constexpr (FUSE) piece_store(ap, pc);               // every load of the wave has landed
     for (int c = n_dma; c < n_cap; ++c)                     // chunks without a visible row
-        if (lane < kDmaRows) sc[(NW * c + wave) * kDmaRows + lane] = -__builtin_inff();
+        if (lane < CR) sc[(NW * c + wave) * CR + lane] = -__builtin_inff();
     __syncthreads();
     float* scores = a.scores + b * cap;
     const int64_t nrows = min((int64_t)rows_per_block, cap - row0);
@@ -1467,7 +1477,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
             if (v >= 1 && v <= 65536) blk32 = v * 4 / kDma32Waves;
         }
         const int64_t per_seq32 = (blk32 + a.B - 1) / a.B;
-        const int64_t unit32 = (int64_t)kDma32Waves * kDmaRows;
+        const int64_t unit32 = (int64_t)kDma32Waves * (a.fmt == MLA_FMT_E4M3_S128 ? kDmaRows : 2 * kDmaRows);
         int64_t d32rpb = (a.capacity + per_seq32 - 1) / per_seq32;
         d32rpb = ((d32rpb + unit32 - 1) / unit32) * unit32;
         const int64_t rpw32 = a.fmt == MLA_FMT_E4M3_S128 ? kDmaRowsPerWave : kDmaRowsPerWave4;

@@ -147,6 +147,36 @@ mla_status_t mla_profile_enable(int32_t kernels);
 mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* total_ms);
 
 /*
+ * Kernel-choice options (process-wide; not part of the computation). Several
+ * calls have more than one kernel that computes the same result; by default
+ * (every option 0) the library picks by shape. An option forces a choice, for
+ * tuning and for tests that must reach a particular kernel. Options are read at
+ * each call, so set them before the calls they should affect and not while
+ * another thread is calling.
+ *   name                     range      meaning of a non-zero value
+ *   "topk_path"              0..2       1: one workgroup selects each sequence;
+ *                                       2: many select workgroups and a final step
+ *   "topk_final"             0..1       1: the 256-thread final of the many-workgroup path
+ *   "scan_queues"            0..1       1: the queue-fed 32x32 indexer scan
+ *   "scan_blocks"            0..65536   target number of 4-wave indexer-scan workgroups
+ *   "decode_rows_per_split"  0..256     selected rows per decode split (32..256, multiple of 32)
+ *   "decode_heads_per_group" 0..32      heads per decode workgroup (16 or 32)
+ *   "decode_waves"           0..8       waves per decode workgroup (4 or 8)
+ * Values in range that a kernel cannot use are ignored. Errors:
+ * MLA_ERR_INVALID_ARG (unknown name, NULL pointer, value out of range).
+ */
+mla_status_t mla_set_option(const char* name, int64_t value);
+mla_status_t mla_get_option(const char* name, int64_t* value);
+
+/*
+ * The kernels that the calling thread's most recent compute call (append,
+ * compress, top-k, pool or decode) launched, as demangled names separated by
+ * ';' ("" if it launched none). Valid until the thread's next call of this
+ * function. For tests and tuning: it shows which kernel served a call.
+ */
+const char* mla_last_kernels(void);
+
+/*
  * mla_kv_append_quant -- quantise-append of one decode step's entries.
  *
  * Writes, for each sequence b and each new entry i < n_new, the quantised main

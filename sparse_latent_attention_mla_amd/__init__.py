@@ -55,6 +55,9 @@ def lib():
         L.mla_profile_enable.argtypes, L.mla_profile_enable.restype = [i32], i32
         L.mla_profile_read.argtypes = [C.c_char_p, C.POINTER(i32), C.POINTER(C.c_double)]
         L.mla_profile_read.restype = i32
+        L.mla_set_option.argtypes, L.mla_set_option.restype = [C.c_char_p, i64], i32
+        L.mla_get_option.argtypes, L.mla_get_option.restype = [C.c_char_p, C.POINTER(i64)], i32
+        L.mla_last_kernels.argtypes, L.mla_last_kernels.restype = [], C.c_char_p
         L.mla_kv_append_quant.argtypes = [_CRow, _CRow, P, P, P, i32, i32, i64, P, i64, P, i64,
                                           P, P, P, i32, i32, i32, P]
         L.mla_kv_append_quant.restype = i32
@@ -116,6 +119,39 @@ def row_bytes(row: Row) -> int:
 
 def version() -> int:
     return int(lib().mla_version())
+
+
+def mla_set_option(name: str, value: int) -> None:
+    """Force a kernel choice (see include/mla.h); 0 restores the library's own choice."""
+    _check(lib().mla_set_option(name.encode(), int(value)))
+
+
+def mla_get_option(name: str) -> int:
+    v = C.c_int64(0)
+    _check(lib().mla_get_option(name.encode(), C.byref(v)))
+    return int(v.value)
+
+
+class option:
+    """Context manager: set an option for the duration of a block, then restore it."""
+
+    def __init__(self, name: str, value: int):
+        self.name, self.value = name, value
+
+    def __enter__(self):
+        self.old = mla_get_option(self.name)
+        mla_set_option(self.name, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        mla_set_option(self.name, self.old)
+        return False
+
+
+def mla_last_kernels() -> list:
+    """Demangled names of the kernels the calling thread's last compute call launched."""
+    s = lib().mla_last_kernels().decode()
+    return s.split(";") if s else []
 
 
 PROFILE_KERNELS = ("kv_append", "indexer_scan", "topk_select", "decode", "decode_merge")

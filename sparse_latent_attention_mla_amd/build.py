@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "mla")
 LIB = os.path.join(HERE, "libmla.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "profile.cpp", "append.hip", "indexer.hip", "topk.hip", "pool.hip", "decode.hip", "compress.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "options.cpp", "append.hip", "indexer.hip", "topk.hip", "pool.hip", "decode.hip", "compress.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

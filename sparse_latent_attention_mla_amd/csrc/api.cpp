@@ -284,13 +284,33 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
     return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
 }
 
-int32_t mla_version(void) { return 102; }
+int32_t mla_version(void) { return 103; }
+
+mla_status_t mla_set_option(const char* name, int64_t value) {
+    if (!name) return fail(MLA_ERR_INVALID_ARG, "mla_set_option: NULL name");
+    const int i = mla::option_index(name);
+    if (i < 0) return fail(MLA_ERR_INVALID_ARG, "mla_set_option: unknown option '%s'", name);
+    if (!mla::option_set(i, value))
+        return fail(MLA_ERR_INVALID_ARG, "mla_set_option: value %lld out of range for '%s'", (long long)value, name);
+    return ok();
+}
+
+mla_status_t mla_get_option(const char* name, int64_t* value) {
+    if (!name || !value) return fail(MLA_ERR_INVALID_ARG, "mla_get_option: NULL argument");
+    const int i = mla::option_index(name);
+    if (i < 0) return fail(MLA_ERR_INVALID_ARG, "mla_get_option: unknown option '%s'", name);
+    *value = mla::option(static_cast<mla::Opt>(i));
+    return ok();
+}
+
+const char* mla_last_kernels(void) { return mla::launched_names(); }
 
 mla_status_t mla_kv_append_quant(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
                                  const float* new_idx, const int32_t* slots, int32_t B, int32_t n_new,
                                  int64_t capacity, void* main_cache, int64_t main_seq_stride, void* idx_cache,
                                  int64_t idx_seq_stride, const float* new_win, const int32_t* win_pos,
                                  void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt, void* stream) {
+    mla::begin_call();
     mla::AppendArgs a{};
     const mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
                                        main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W,
@@ -304,6 +324,7 @@ mla_status_t mla_compress_append(mla_row_t main_row, const float* kv, const floa
                                  const float* norm_weight, float eps, int32_t rope_dim, const float* rope_cs,
                                  const int32_t* slots, int32_t B, int64_t capacity, void* main_cache,
                                  int64_t main_seq_stride, float* out_entry, void* stream) {
+    mla::begin_call();
     if (B < 0 || m < 1 || !(eps >= 0.0f) || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "compress: need B >= 0, m >= 1, eps >= 0, capacity >= 0");
     const int64_t rb = mla_row_bytes(main_row);
@@ -353,6 +374,7 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
                               const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
                               int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
                               size_t workspace_bytes, void* stream) {
+    mla::begin_call();
     TopkCall c;
     const mla_status_t s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
                                      cand, n_cand, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
@@ -369,6 +391,7 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, cons
                                      float score_scale, const int32_t* n_visible, int32_t B, int32_t H_I,
                                      int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
                                      size_t workspace_bytes, void* stream) {
+    mla::begin_call();
     if (!idx_cache) return fail(MLA_ERR_INVALID_ARG, "append_indexer_topk: idx_cache is NULL");
     mla::AppendArgs ap{};
     mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
@@ -398,6 +421,7 @@ size_t mla_indexer_pool_workspace(int32_t B, int64_t capacity, int32_t block) {
 mla_status_t mla_indexer_pool(const float* scores, int64_t capacity, const int32_t* n_visible, int32_t B,
                               int32_t block, int32_t n_blocks, int32_t* out_pos, void* workspace,
                               size_t workspace_bytes, void* stream) {
+    mla::begin_call();
     if (B < 0 || capacity < 0 || n_blocks < 0)
         return fail(MLA_ERR_INVALID_ARG, "indexer_pool: need B >= 0, capacity >= 0, n_blocks >= 0");
     if (block < 1 || block > 64 || (block & (block - 1)) != 0)
@@ -451,6 +475,7 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
                                const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
                                void* workspace,
                                size_t workspace_bytes, void* stream) {
+    mla::begin_call();
     if (B < 0 || H < 1 || k < 0 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need B >= 0, H >= 1, k >= 0, capacity >= 0");
     const int D = main_row.dim + main_row.rope_dim;

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
                     den[j] = den[j] * sc + 1.0f;
                     num[j] = num[j] * sc + xv[u][j];
                     mx[j] = gv[u][j];
-                } else {
-                    const float e = expf(gv[u][j] - mx[j]);
+                } else {                                     // a gate of -inf weighs 0 (also while mx is -inf)
+                    const float e = gv[u][j] == -__builtin_inff() ? 0.0f : expf(gv[u][j] - mx[j]);
                     den[j] += e;
                     num[j] += e * xv[u][j];
                 }

@@ -28,14 +28,12 @@
 //     a low bf16 part.
 //   Layouts: rows staged by DMA use 8 wave-specialised waves (decode_split_ws:
 //   4 waves stage and score chunk c + 1 while 4 run softmax and PV on chunk c,
-//   one barrier per chunk); E2M1 rows, two head tiles per workgroup or
-//   MLA_DECODE_NW=4 use 4 waves that take both roles in turn (decode_split).
+//   one barrier per chunk); E2M1 rows, two head tiles per workgroup or the
+//   decode_waves option 4 use 4 waves that take both roles in turn (decode_split).
 //   The split's normalised output and logsumexp are written as a partial and
 //   k_merge combines the partials by logsumexp.
 // Generic path (any other shape): one workgroup per (b, h), fp32 on the vector
 // ALUs, writes the final output directly.
-#include <cstdlib>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -159,9 +157,10 @@ __device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 w) {
 }
 
 // Entries per split and heads per workgroup. Fewer, longer splits write fewer
-// fp32 partials; more splits keep more workgroups in flight. MLA_DECODE_RPS
-// (32..256, multiple of 32) and MLA_DECODE_HT (1 or 2) override the choice for
-// tuning; the workspace query reads them too.
+// fp32 partials; more splits keep more workgroups in flight. The options
+// decode_rows_per_split (32..256, multiple of 32), decode_heads_per_group (16
+// or 32) and decode_waves (4 or 8) override the choice for tuning; the
+// workspace query reads them too.
 struct Geometry {
     int ht, nw, rps, S_main, S_win, groups;
 };
@@ -169,21 +168,17 @@ struct Geometry {
 Geometry decode_geometry(int B, int H, int k, int W) {
     Geometry g{};
     g.ht = 1;
-    if (const char* e = getenv("MLA_DECODE_HT")) {
-        const int v = atoi(e);
-        if (v == 2 && H % 32 == 0) g.ht = 2;
-    }
+    if (option(OPT_DECODE_HEADS) == 32 && H % 32 == 0) g.ht = 2;
     g.groups = H / (16 * g.ht);
     // waves per workgroup: 8 (wave-specialised: half stage and score chunk c + 1 while
-    // the other half runs softmax and PV on chunk c) unless MLA_DECODE_NW=4; two head
+    // the other half runs softmax and PV on chunk c) unless decode_waves is 4; two head
     // tiles per workgroup, and E2M1 rows (staged through registers), use 4
     g.nw = 8;
-    if (const char* e = getenv("MLA_DECODE_NW"))
-        if (atoi(e) == 4) g.nw = 4;
+    if (option(OPT_DECODE_WAVES) == 4) g.nw = 4;
     if (g.ht == 2) g.nw = 4;
     int rps = 0;
-    if (const char* e = getenv("MLA_DECODE_RPS")) {
-        const int v = atoi(e);
+    {
+        const int v = (int)option(OPT_DECODE_RPS);
         if (v >= kChunk && v <= kMaxRps && v % kChunk == 0) rps = v;
     }
     if (rps == 0) {

@@ -1458,12 +1458,9 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         // row loads whole 16-byte pieces up to the sequence's end, none beyond it)
         const bool dma = (reinterpret_cast<uintptr_t>(a.cache) % 16 == 0) && (a.stride % 16 == 0) &&
                          (a.capacity * a.row_bytes) % 16 == 0;
-        // MLA_SCAN_BLOCKS overrides the target number of blocks (for tuning)
+        // the scan_blocks option overrides the target number of blocks (for tuning)
         int64_t dma_target = 256 * kDmaBlocksPerCu;
-        if (const char* e = getenv("MLA_SCAN_BLOCKS")) {
-            const int64_t v = atoll(e);
-            if (v >= 1 && v <= 65536) dma_target = v;
-        }
+        if (const int64_t v = option(OPT_SCAN_BLOCKS)) dma_target = v;
         const int64_t dma_per_seq = (dma_target + a.B - 1) / a.B;
         int64_t drpb = (a.capacity + dma_per_seq - 1) / dma_per_seq;
         drpb = ((drpb + 4 * kDmaRows - 1) / (4 * kDmaRows)) * (4 * kDmaRows);
@@ -1472,10 +1469,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         // the 32x32 scan: blocks of kDma32Waves waves, as many as the CUs hold at once
         // (two 4-wave blocks per CU, whatever the ring depth)
         int64_t blk32 = 256 * (8 / kDma32Waves);
-        if (const char* e = getenv("MLA_SCAN_BLOCKS")) {
-            const int64_t v = atoll(e);
-            if (v >= 1 && v <= 65536) blk32 = v * 4 / kDma32Waves;
-        }
+        if (const int64_t v = option(OPT_SCAN_BLOCKS)) blk32 = std::max<int64_t>(1, v * 4 / kDma32Waves);
         const int64_t per_seq32 = (blk32 + a.B - 1) / a.B;
         const int64_t unit32 = (int64_t)kDma32Waves * (a.fmt == MLA_FMT_E4M3_S128 ? kDmaRows : 2 * kDmaRows);
         int64_t d32rpb = (a.capacity + per_seq32 - 1) / per_seq32;
@@ -1483,11 +1477,11 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         const int64_t rpw32 = a.fmt == MLA_FMT_E4M3_S128 ? kDmaRowsPerWave : kDmaRowsPerWave4;
         d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), rpw32 * kDma32Waves);
         const dim3 d32grid((unsigned)((a.capacity + d32rpb - 1) / d32rpb), a.B);
-        // the queue-fed 32x32 scan (MLA_SCAN_QUEUES; at the T = 128K shape it is
+        // the queue-fed 32x32 scan (option scan_queues; at the T = 128K shape it is
         // slower than the static partition): about 64 queues (a sequence's rows
         // split into `groups` ranges), 2 blocks per CU in all, at least about 4
         // chunks per wave
-        const bool dyn = a.queues != nullptr && a.B <= kScanQueuesHost && getenv("MLA_SCAN_QUEUES") != nullptr;
+        const bool dyn = a.queues != nullptr && a.B <= kScanQueuesHost && option(OPT_SCAN_QUEUES) != 0;
         int dyn_lg = 0;
         while (a.B << (dyn_lg + 1) <= 64) ++dyn_lg;            // 2^lg queues per sequence, B 2^lg <= 64
         const int64_t dyn_nq = (int64_t)a.B << dyn_lg;

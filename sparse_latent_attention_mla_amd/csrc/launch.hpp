@@ -161,6 +161,19 @@ void prof_enable(uint32_t mask);  // bit k times ProfKernel k
 int prof_index(const char* name);  // -1 for an unknown name
 hipError_t prof_read(int k, int32_t* launches, double* total_ms);
 
+// Kernel-choice options (options.cpp; mla_set_option): 0 = the library's own choice.
+enum Opt {
+    OPT_TOPK_PATH, OPT_TOPK_FINAL, OPT_SCAN_QUEUES, OPT_SCAN_BLOCKS,
+    OPT_DECODE_RPS, OPT_DECODE_HEADS, OPT_DECODE_WAVES, OPT_COUNT
+};
+int64_t option(Opt o);
+int option_index(const char* name);     // -1 for an unknown name
+bool option_set(int i, int64_t v);      // false when out of range
+// The kernels the calling thread's current API call launches (mla_last_kernels).
+void begin_call();
+void note_launch(const void* f);
+const char* launched_names();
+
 // Launch `kernel`.  With events, through hipExtLaunchKernel: the runtime stamps
 // them from the kernel's own dispatch (start, end), so a pair brackets exactly
 // that kernel and no marker packet is added between kernels on the stream.
@@ -175,6 +188,7 @@ hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint3
         ((argv[i++] = static_cast<void*>(&x)), ...);
     }, held);
     const void* f = reinterpret_cast<const void*>(kernel);
+    note_launch(f);
     if (t0 || t1) return hipExtLaunchKernel(f, grid, block, argv, lds, stream, t0, t1, 0);
     return hipLaunchKernel(f, grid, block, argv, lds, stream);
 }

@@ -1031,13 +1031,13 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2_flat(const int32_t
 
 }  // namespace
 
-// MLA_TOPK_PATH=row|multi forces a path, MLA_TOPK_FINAL1 the 256-thread final (for tuning).
+// Options topk_path (1 row, 2 multi) and topk_final (1: the 256-thread final) force a path.
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                          const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream, const SelectMap& map) {
     if (B == 0 || k == 0) return hipSuccess;
     const bool pool = map.cand != nullptr, expand = map.expand != 1;
     bool row = capacity <= kRowPathMax;
-    if (const char* e = getenv("MLA_TOPK_PATH")) row = (e[0] == 'r');
+    if (const int64_t path = option(OPT_TOPK_PATH)) row = path == 1;
     const ProfSlot p = prof_slot(PROF_SELECT);      // spans both kernels of the two-kernel path
     if (row) {
         auto kr = pool ? (expand ? k_topk_row<true, true> : k_topk_row<true, false>)
@@ -1052,7 +1052,7 @@ hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n
                                            scores, capacity, n_visible, k, ws, map);
         if (e != hipSuccess) return e;
     }
-    if (nx <= (unsigned)kF2MaxGroups && !getenv("MLA_TOPK_FINAL1"))
+    if (nx <= (unsigned)kF2MaxGroups && option(OPT_TOPK_FINAL) == 0)
         return launch_kernel(expand ? k_select_final2_flat<true>
                                     : (nx > (unsigned)kSpecGroups ? k_select_final2_flat<false>
                                                                   : k_select_final2<false>),

@@ -184,3 +184,21 @@ def test_profile_hooks_off_by_default_and_reject_unknown_names(M):
         M.mla_profile_read("k_scan")
     n, ms = C.c_int32(), C.c_double()
     assert M.lib().mla_profile_read(None, C.byref(n), C.byref(ms)) == 1
+
+
+def test_options_set_get_and_validation(M):
+    """Kernel-choice options: declared names round-trip, unknown names and values
+    out of range are rejected on the host, and 0 restores the default."""
+    for name, v in (("topk_path", 2), ("topk_final", 1), ("scan_queues", 1), ("scan_blocks", 300),
+                    ("decode_rows_per_split", 128), ("decode_heads_per_group", 32), ("decode_waves", 4)):
+        assert M.mla_get_option(name) == 0
+        with M.option(name, v):
+            assert M.mla_get_option(name) == v
+        assert M.mla_get_option(name) == 0
+    with pytest.raises(M.MLAError, match="unknown option"):
+        M.mla_set_option("no_such_option", 1)
+    with pytest.raises(M.MLAError, match="out of range"):
+        M.mla_set_option("topk_path", 3)
+    with pytest.raises(M.MLAError, match="out of range"):
+        M.mla_set_option("scan_blocks", -1)
+    assert M.mla_last_kernels() == []                          # nothing launched on this thread

@@ -14,6 +14,10 @@ C = WL.CONFIGS
 CFGS = {
     "c3s": C["c3"].with_(name="c3s", cid=103, B=2, N=6001),
     "c4s": C["c4"].with_(name="c4s", cid=104, B=2, N=4099),
+    # sequences ending on a 16-byte boundary: the LDS-DMA scans read the shared rows
+    "c3d": C["c3"].with_(name="c3d", cid=123, B=2, N=6004),
+    "c4d": C["c4"].with_(name="c4d", cid=124, B=2, N=4100),
+    "c4xd": C["c4x"].with_(name="c4xd", cid=126, B=2, N=4100),
 }
 
 
@@ -37,7 +41,10 @@ def test_several_queries_of_one_sequence(name):
     shared_idx = case.g_idx[0:1].expand(Q, -1, -1)
     M.mla_indexer_topk(G.idx_row(cfg), G._qi_gpu(cfg, q_idx), G._t(w), cfg.sigma, shared_idx, G._t(nv), k,
                        out_idx, ws, out_scores=scores)
+    launched = M.mla_last_kernels()
     torch.cuda.synchronize()
+    if name.endswith("d"):
+        assert any("k_scan_dma32" in n for n in launched), launched
     got_idx, got_s = out_idx.cpu().numpy(), scores.cpu().numpy()
     G.check_scores(got_s, ref, nv)
     G.check_topk(got_idx, ref, nv, k)

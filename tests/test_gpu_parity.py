@@ -32,8 +32,19 @@ SMALL = {
     # sizes at which every wave of the queue-fed scan draws several tickets
     "c3m": C["c3"].with_(name="c3m", cid=113, B=3, N=40001),
     "c4m": C["c4"].with_(name="c4m", cid=114, B=1, N=70001),
+    # sequences ending on a 16-byte boundary (N % 4 == 0) but not on a 64-row chunk:
+    # the LDS-DMA scans (and the append they carry), with a ragged last chunk
+    "c3d": C["c3"].with_(name="c3d", cid=123, B=2, N=6004),
+    "c4d": C["c4"].with_(name="c4d", cid=124, B=2, N=4100),
+    "c4xd": C["c4x"].with_(name="c4xd", cid=126, B=2, N=4100),
+    # the queue-fed and static LDS-DMA scans at sizes where every wave draws several tickets
+    "c3q": C["c3"].with_(name="c3q", cid=133, B=3, N=40004),
+    "c4q": C["c4"].with_(name="c4q", cid=134, B=1, N=70004),
 }
+# the cases whose indexer cache the LDS-DMA scans read (16-byte aligned sequence ends)
+DMA_CASES = ("c3d", "c4d", "c4xd")
 FULL = {n: C[n] for n in ("c2", "c3", "c4", "c4x", "c5")}
+TOPK_PATH = {"row": 1, "multi": 2}
 
 
 def say(*a):
@@ -112,8 +123,10 @@ def test_decode_given_oracle_indices(name):
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_step_end_to_end(name):
-    """The GPU's own indices feed the GPU decode; the outputs are compared with
-    the oracle's step wherever the two selected sets coincide exactly."""
+    """The GPU's own indices feed the GPU decode. Every sequence's output is
+    compared with the oracle's attention over the GPU's selected set (which the
+    top-k bar has already tied to the oracle's set), and where the two sets
+    coincide exactly, also with the oracle's whole step."""
     case = case_of(name)
     cfg = case.cfg
     ref_idx = oracle_indices_per_layer(case)
@@ -121,13 +134,19 @@ def test_step_end_to_end(name):
     for layer, mode in enumerate(cfg.layers):
         if mode in ("full", "reindex"):
             latest, _ = G.gpu_topk(case, j, want_scores=False)
+            G.check_topk(latest, G.oracle_scores(case, j), case.n_visible, cfg.k)
             j += 1
         say("step", name, "layer", layer, mode)
         got_o, got_l = G.gpu_decode(case, layer, latest)
+        own_o, own_l = G.oracle_attention(case, layer, latest)
+        G.check_attention(got_o, got_l, own_o, own_l)        # all B sequences
         ref_o, ref_l = G.oracle_attention(case, layer, ref_idx[layer])
+        same = 0
         for b in range(cfg.B):
             if set(latest[b].tolist()) == set(ref_idx[layer][b].tolist()):
                 G.check_attention(got_o[b:b + 1], got_l[b:b + 1], ref_o[b:b + 1], ref_l[b:b + 1])
+                same += 1
+        say(f"  {cfg.B} sequences against the GPU's sets, {same} also against the oracle's step")
 
 
 @pytest.mark.parametrize("name", ["c1", "c3s", "c4s", "c4xs"])
@@ -237,14 +256,13 @@ def test_decode_head_counts(name, H):
 @pytest.mark.parametrize("path", ["row", "multi"])
 @pytest.mark.parametrize("fmt", [G.O.E4M3_S128, G.O.E2M1_S16, G.O.MXFP4, G.O.BF16])
 @pytest.mark.parametrize("k", [1, 37, 2048])
-def test_topk_exact_ties(fmt, k, path, monkeypatch):
+def test_topk_exact_ties(fmt, k, path):
     """Scores that are exact integers on both sides: integer queries and weights, and
     rows whose values the format holds exactly with unit block scales (a 448 in each
     E4M3 block of 128, a 6 in each E2M1 group of 16). Rows repeat, so many share a
     score; the selected set must equal the oracle's exactly, the smaller position
     winning each tie, and the scores must agree bit for bit. Both selection paths:
     one workgroup per sequence, and many with a separate final step."""
-    monkeypatch.setenv("MLA_TOPK_PATH", path)
     rng = np.random.default_rng(1000 + 10 * fmt + k)
     B, N, d, H_I = 2, 5003, 128, 64
     distinct = rng.choice(np.array([-3, -2, -1, 0, 1, 2, 3], np.float32), (B, 997, d))
@@ -269,8 +287,11 @@ def test_topk_exact_ties(fmt, k, path, monkeypatch):
     out_s = torch.empty((B, N), dtype=torch.float32, device="cuda")
     ws = torch.zeros(G.M.mla_indexer_topk_workspace(B, N, k), dtype=torch.uint8, device="cuda")
     say("topk ties", fmt, k, path)
-    G.M.mla_indexer_topk(G.M.Row(fmt, d, 0), G._t(q_idx, torch.bfloat16), G._t(w), 1.0, g_cache, G._t(nv), k,
-                         out_idx, ws, out_scores=out_s)
+    with G.M.option("topk_path", TOPK_PATH[path]):
+        G.M.mla_indexer_topk(G.M.Row(fmt, d, 0), G._t(q_idx, torch.bfloat16), G._t(w), 1.0, g_cache, G._t(nv), k,
+                             out_idx, ws, out_scores=out_s)
+        launched = G.M.mla_last_kernels()
+    assert any(("k_topk_row" in n) == (path == "row") for n in launched), launched
     torch.cuda.synchronize()
     got_s, got_i = out_s.cpu().numpy(), out_idx.cpu().numpy()
     for b in range(B):
@@ -337,7 +358,7 @@ def test_full_size(name):
         say(f"  worst rel err out {wo:.2e} lse {wl:.2e}")
 
 
-def test_topk_workspace_reused_across_shapes(monkeypatch):
+def test_topk_workspace_reused_across_shapes():
     """One workspace, zeroed once, serves calls of different batch sizes,
     capacities, formats and selection paths in a row: each call must leave the
     histogram part zeroed for the next."""
@@ -346,24 +367,22 @@ def test_topk_workspace_reused_across_shapes(monkeypatch):
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
     for name, path in (("c3s", "multi"), ("c2s", "row"), ("c3s", "row"), ("c4s", "multi"), ("c3s", "multi"),
                        ("c2s", "multi")):
-        monkeypatch.setenv("MLA_TOPK_PATH", path)
         case = case_of(name)
         say("workspace reuse", name, path)
-        got_idx, _ = G.gpu_topk(case, 0, ws=ws, want_scores=False)
+        with G.M.option("topk_path", TOPK_PATH[path]):
+            got_idx, _ = G.gpu_topk(case, 0, ws=ws, want_scores=False)
         ref_s = G.oracle_scores(case, 0)
         G.check_topk(got_idx, ref_s, case.n_visible, case.cfg.k)
 
 
 @pytest.mark.parametrize("scan", ["queues", "static"])
-@pytest.mark.parametrize("name", ["c3m", "c4m"])
-def test_scan_work_queues(name, scan, monkeypatch):
+@pytest.mark.parametrize("name", ["c3q", "c4q"])
+def test_scan_work_queues(name, scan):
     """The queue-fed scan (chunks handed out by ticket at run time, 48 and 64
     queues here, several tickets per wave) and the statically partitioned one,
     on ragged visible lengths, with one workspace reused across the calls: the
     scores, the selection, and the zeroed start of the workspace (the queues'
     counters, then the histogram copies) after every call."""
-    if scan == "queues":
-        monkeypatch.setenv("MLA_SCAN_QUEUES", "1")
     case = case_of(name)
     cfg = case.cfg
     B, N, k = cfg.B, cfg.N, cfg.k
@@ -373,15 +392,19 @@ def test_scan_work_queues(name, scan, monkeypatch):
     for nv in ([N] * B, rng.integers(1, N + 1, B).tolist(), [N - 31] + [33] * (B - 1), [0] * B):
         nv = np.array(nv, np.int32)
         say("scan queues", name, scan, nv.tolist())
-        got_idx, got_s = G.gpu_topk(case, 0, n_visible=nv, ws=ws)
+        with G.M.option("scan_queues", int(scan == "queues")):
+            got_idx, got_s = G.gpu_topk(case, 0, n_visible=nv, ws=ws)
+            launched = G.M.mla_last_kernels()
+        want = "k_scan_dyn32" if scan == "queues" else "k_scan_dma32"
+        assert any(want in n for n in launched), launched
         ref_s = G.oracle_scores(case, 0, n_visible=nv)
         G.check_scores(got_s, ref_s, nv)
         G.check_topk(got_idx, ref_s, nv, k)
         assert not bool(ws[:zero_part].any()), "workspace start not zero after the call"
 
 
-@pytest.mark.parametrize("slots_kind", ["step", "spread"])
-@pytest.mark.parametrize("name", ["c3s", "c4s", "c4xs", "c3m", "c2s", "c1"])
+@pytest.mark.parametrize("slots_kind", ["step", "spread", "tiles"])
+@pytest.mark.parametrize("name", ["c3s", "c4s", "c4xs", "c3m", "c2s", "c1", "c3d", "c4d", "c4xd"])
 def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
     """mla_append_indexer_topk against mla_kv_append_quant then mla_indexer_topk on
     copies of the same caches whose new slots hold stale bytes: the caches and the
@@ -389,13 +412,21 @@ def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
     against the oracle (the entries re-appended are the ones the caches were built
     from, so the expected bytes are the case's own). Entries: the step's one (slot
     N - 1), or four spread over the sequence so that several scan workgroups and
-    waves each own one; visible lengths that include and that exclude slot N - 1.
-    E4M3 and E2M1 indexer rows take the fused kernel, bf16 and fp32 the fallback."""
+    waves each own one, or four of which three sit in the second 32-row tile of a
+    64-row chunk; visible lengths that include and that exclude slot N - 1, and a
+    ragged one. Where the sequences end on a 16-byte boundary, E4M3, E2M1 and MXFP4
+    indexer rows take the LDS-DMA scan carrying the append (checked by the kernel the
+    call launched); other shapes and bf16 / fp32 rows the separate append + scan."""
     case = case_of(name)
     cfg = case.cfg
     B, N, k = cfg.B, cfg.N, cfg.k
     mr, ir = G.main_row(cfg), G.idx_row(cfg)
-    slots = [N - 1] if slots_kind == "step" else sorted({N - 1, 5 % N, N // 2, (37 * N) // 41})
+    if slots_kind == "step":
+        slots = [N - 1]
+    elif slots_kind == "spread":
+        slots = sorted({N - 1, 5 % N, N // 2, (37 * N) // 41})
+    else:                                               # rows 32..63 of a 64-row chunk, and the last row
+        slots = sorted({37 % N, 100 % N, (64 * (N // 128) + 50) % N, N - 1})
     sl = np.tile(np.array(slots, np.int32), (B, 1))
     new_main = G._t(case.inp.main[:, slots])
     new_idx = G._t(case.inp.idx[:, slots])
@@ -413,8 +444,8 @@ def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
             wr[:, p % cfg.W] = 7.0
         return m, i, wr
 
-    for nv in ([N] * B, [N - 1] + [N] * (B - 1)):
-        nv = np.array(nv, np.int32)
+    for nv in ([N] * B, [N - 1] + [N] * (B - 1), [N - 70] + [max(1, N // 2 + 13)] * (B - 1)):
+        nv = np.array([max(0, v) for v in nv], np.int32)
         say("append+topk", name, slots_kind, slots, nv.tolist())
         m_a, i_a, w_a = stale()
         m_b, i_b, w_b = stale()
@@ -431,7 +462,15 @@ def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
         G.M.mla_append_indexer_topk(mr, ir, new_main, new_idx, G._t(sl), m_b, i_b, qi, w, cfg.sigma, G._t(nv),
                                     k, out_b, ws_b, new_win=wl0, win_pos=posv if cfg.W else None, win_ring=w_b,
                                     out_scores=s_b)
+        launched = G.M.mla_last_kernels()
         torch.cuda.synchronize()
+        scans = [n for n in launched if "k_scan" in n]
+        assert len(scans) == 1, launched
+        if name in DMA_CASES:                           # one launch before the selection: the DMA scan carrying the append
+            assert not any("k_append" in n for n in launched), launched
+            assert "k_scan_dma32" in scans[0] and "true>(" in scans[0], launched
+        elif name in ("c3s", "c4s", "c4xs", "c3m"):     # odd sequence ends: separate append, staged scan
+            assert any("k_append" in n for n in launched) and "k_scan_staged" in scans[0], launched
         assert torch.equal(m_a, m_b) and torch.equal(i_a, i_b), "caches differ between the paths"
         assert torch.equal(i_b, case.g_idx) and torch.equal(m_b, case.g_main), "caches differ from the case's"
         if cfg.W:

@@ -72,3 +72,17 @@ def test_forward_rope_on_the_trailing_channels():
     n0 = np.hypot(x1, x2)
     n1 = np.hypot(t[:, D - r:D - r // 2], t[:, D - r // 2:])
     np.testing.assert_allclose(n1, n0, rtol=1e-6, atol=1e-7)  # a rotation keeps pair norms
+
+
+def test_masked_gates_drop_their_tokens():
+    """A gate of -inf takes its token out of the channel's softmax: masking tokens
+    gives the same entry as a window without them (per channel)."""
+    kv, gate, g = _data(2, 4, 96, 11)
+    masked = gate.copy()
+    masked[0, 0] = -np.inf                                     # sequence 0: token 0 masked everywhere
+    masked[1, 1:3] = -np.inf                                   # sequence 1: tokens 1 and 2 masked
+    got = O.compress(kv, masked, g, 1e-6)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(got[:1], O.compress(kv[:1, 1:], gate[:1, 1:], g, 1e-6))
+    keep = [0, 3]
+    np.testing.assert_array_equal(got[1:], O.compress(kv[1:, keep], gate[1:, keep], g, 1e-6))

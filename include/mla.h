@@ -438,6 +438,31 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
                                float* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mla_sparse_decode_noalloc -- mla_sparse_decode with the library's own scratch.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * arguments and errors as mla_sparse_decode, without the workspace arguments.
+ * The split partials (and an MXFP8 window's bf16 copy) go to a static array of
+ * MLA_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, held until the
+ * process ends; the call allocates and frees nothing. Its device address is
+ * looked up on the first call on each device, with that device current; the
+ * stream must belong to the current device. Shapes whose workspace
+ * (mla_sparse_decode_workspace) exceeds the array are rejected with
+ * MLA_ERR_WORKSPACE. Every call on a GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or host threads without
+ * ordering) race and give wrong results; order them on one stream.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (32u << 20)
+mla_status_t mla_sparse_decode_noalloc(mla_row_t main_row, int32_t d_v, const void* q,
+                                       const void* main_cache, int64_t main_seq_stride, int64_t capacity,
+                                       const int32_t* idx, int32_t k,
+                                       const void* win_ring, const int32_t* win_len, int32_t W,
+                                       int32_t win_fmt, float softmax_scale,
+                                       const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H,
+                                       float* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

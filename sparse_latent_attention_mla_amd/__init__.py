@@ -78,6 +78,9 @@ def lib():
         L.mla_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, i32, f32, P, i32, i32,
                                         P, P, P, sz, P]
         L.mla_sparse_decode.restype = i32
+        L.mla_sparse_decode_noalloc.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, i32, f32, P, i32,
+                                                i32, P, P, P]
+        L.mla_sparse_decode_noalloc.restype = i32
         _lib = L
     return _lib
 
@@ -406,13 +409,9 @@ class _CEpilogue(C.Structure):
     _fields_ = [("sinks", C.c_void_p), ("rope_dim", C.c_int32), ("rope_cs", C.c_void_p)]
 
 
-def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
-                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None, rope_cs=None):
-    """Sparse absorbed-MLA decode.  q [B, H, D] (bf16; fp32 for F32 rows), main_cache uint8
-    [B, capacity, row_bytes], idx int32 [B, k], out fp32 [B, H, d_v], lse fp32 [B, H];
-    win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch; sinks fp32 [H]
-    attention-sink logits (optional); rope_cs fp32 [B, r/2, 2] (cos, sin) un-rotating the
-    trailing r output channels (optional)."""
+def _decode_args(main_row, d_v, q, main_cache, idx, softmax_scale, out, lse, win_ring, win_len, sinks, rope_cs):
+    """Checked argument tuple of the decode calls (up to the workspace), and the epilogue struct
+    it points to (keep it alive through the call)."""
     _need(q, "q", query_dtype(main_row), 3)
     _need(idx, "idx", torch.int32, 2)
     _need(out, "out", torch.float32, 3)
@@ -430,9 +429,7 @@ def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale
         wfmt, W = _win_ring(win_ring, B, D)
         if tuple(win_len.shape) != (B,):
             raise ValueError("win_len [B] expected")
-    if workspace is not None:
-        _need(workspace, "workspace", torch.uint8)
-    epi = None
+    epi_s, epi = None, None
     if sinks is not None or rope_cs is not None:
         if sinks is not None:
             _need(sinks, "sinks", torch.float32, 1)
@@ -446,8 +443,33 @@ def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale
             r = 2 * rope_cs.shape[1]
         epi_s = _CEpilogue(None if sinks is None else sinks.data_ptr(), r,
                            None if rope_cs is None else rope_cs.data_ptr())
-        epi = C.c_void_p(C.addressof(epi_s))             # (epi_s stays alive through the call)
-    _check(lib().mla_sparse_decode(
-        _crow(main_row), d_v, _ptr(q), _ptr(main_cache), stride, main_cache.shape[1], _ptr(idx), idx.shape[1],
-        _ptr(win_ring), _ptr(win_len), W, wfmt, float(softmax_scale), epi, B, H, _ptr(out), _ptr(lse),
-        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+        epi = C.c_void_p(C.addressof(epi_s))
+    args = (_crow(main_row), d_v, _ptr(q), _ptr(main_cache), stride, main_cache.shape[1], _ptr(idx), idx.shape[1],
+            _ptr(win_ring), _ptr(win_len), W, wfmt, float(softmax_scale), epi, B, H, _ptr(out), _ptr(lse))
+    return args, epi_s
+
+
+def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
+                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None, rope_cs=None):
+    """Sparse absorbed-MLA decode.  q [B, H, D] (bf16; fp32 for F32 rows), main_cache uint8
+    [B, capacity, row_bytes], idx int32 [B, k], out fp32 [B, H, d_v], lse fp32 [B, H];
+    win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch; sinks fp32 [H]
+    attention-sink logits (optional); rope_cs fp32 [B, r/2, 2] (cos, sin) un-rotating the
+    trailing r output channels (optional)."""
+    args, keep = _decode_args(main_row, d_v, q, main_cache, idx, softmax_scale, out, lse, win_ring, win_len, sinks,
+                              rope_cs)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    _check(lib().mla_sparse_decode(*args, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                   _stream(stream)))
+    del keep
+
+
+def mla_sparse_decode_noalloc(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
+                              win_ring=None, win_len=None, stream=None, sinks=None, rope_cs=None):
+    """mla_sparse_decode with the library's static per-GPU scratch instead of a workspace
+    (for callers that cannot allocate); calls that overlap on one GPU race."""
+    args, keep = _decode_args(main_row, d_v, q, main_cache, idx, softmax_scale, out, lse, win_ring, win_len, sinks,
+                              rope_cs)
+    _check(lib().mla_sparse_decode_noalloc(*args, _stream(stream)))
+    del keep

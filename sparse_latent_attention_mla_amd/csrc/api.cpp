@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.hpp"
 #include "mla.h"
@@ -232,6 +234,38 @@ mla_status_t topk_launch(const TopkCall& c, const mla::AppendArgs* append, hipSt
         e = mla::launch_select(a.scores, a.capacity, a.n_visible, a.B, a.k, c.ws, c.out_idx, st);
     }
     return hip_status(e, "top-k select");
+}
+
+// Scratch of mla_sparse_decode_noalloc: one array per GPU, kept until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it only stands in for the symbol); the device address of each GPU's copy
+// is looked up once, with that GPU current, and kept.
+constexpr size_t kScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The calling thread's current device's scratch address, or null (error set).
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        fail(MLA_ERR_HIP, "sparse_decode_noalloc: no current device (or device index >= %d)", kMaxDevices);
+        return nullptr;
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            fail(MLA_ERR_HIP, "sparse_decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
 }
 
 }  // namespace
@@ -539,6 +573,24 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
     return hip_status(mla::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse decode");
+}
+
+mla_status_t mla_sparse_decode_noalloc(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
+                                       int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
+                                       const void* win_ring, const int32_t* win_len, int32_t W, int32_t win_fmt,
+                                       float softmax_scale, const mla_decode_epilogue_t* epilogue, int32_t B,
+                                       int32_t H, float* out, float* lse, void* stream) {
+    mla::begin_call();
+    const size_t need = (B > 0 && H > 0 && k >= 0 && W >= 0)
+                            ? mla_sparse_decode_workspace(main_row, d_v, B, H, k, win_ring ? W : 0, win_fmt)
+                            : 0;
+    if (need > kScratchBytes)
+        return fail(MLA_ERR_WORKSPACE, "sparse_decode_noalloc: this shape needs %zu bytes of scratch, above the "
+                    "library's %zu", need, kScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && !(ws = device_scratch())) return MLA_ERR_HIP;
+    return mla_sparse_decode(main_row, d_v, q, main_cache, main_seq_stride, capacity, idx, k, win_ring, win_len, W,
+                             win_fmt, softmax_scale, epilogue, B, H, out, lse, ws, ws ? kScratchBytes : 0, stream);
 }
 
 }  // extern "C"

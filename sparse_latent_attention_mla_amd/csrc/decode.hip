@@ -52,6 +52,7 @@ constexpr int kZs = 36;                    // floats per (head) score row in LDS
 constexpr int kMergeThreads = kDv / 4;
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxRows = 8192;
+constexpr int kMergeFast = 16;             // splits the merge loads in one round
 
 enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2 };
 
@@ -163,6 +164,7 @@ __device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 w) {
 // workspace query reads them too.
 struct Geometry {
     int ht, nw, rps, S_main, S_win, groups;
+    int rps_win;
 };
 
 Geometry decode_geometry(int B, int H, int k, int W) {
@@ -565,30 +567,31 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem,
 }
 
 // Wave-specialised split (8 waves, one head tile of 16, rows staged by LDS DMA):
-// waves 0 .. 3 stage the chunks and compute the scores of chunk c + 1 (2 row
-// tiles x 2 K halves) while waves 4 .. 7 run the softmax and the PV product of
-// chunk c (128 value channels each), so the two halves of a chunk's work
-// overlap and there is one barrier per chunk. Before that barrier the QK waves
-// wait for their own loads of chunk c + 2, which the barrier then makes visible
-// to all. Four chunk buffers: c (PV), c + 1 (QK), c + 2 (landed), c + 3 (in flight).
+// waves 0 .. 3 compute the scores of chunk c + 1 (2 row tiles x 2 K halves)
+// while waves 4 .. 7 run the softmax and the PV product of chunk c (128 value
+// channels each), so the two halves of a chunk's work overlap and there is one
+// barrier per chunk. Before that barrier every wave waits for its own loads of
+// chunk c + 2, which the barrier then makes visible to all. Four chunk buffers:
+// c (PV), c + 1 (QK), c + 2 (landed), c + 3 (in flight).
 // With SMQK (E4M3 rows) the softmax moves to the QK waves and runs once per
-// chunk instead of once in every PV wave, and the PV waves take over the row
-// gathers: in step c the QK waves score chunk c + 1 and turn chunk c's scores
-// into P (wave q: heads 4q .. 4q + 3, two rows per lane, the lazy reference
-// per head), writing P and the reference's factor to LDS, while the PV waves
-// issue chunk c + 3, rescale and accumulate chunk c - 1 and wait for their
-// loads of chunk c + 2; five chunk buffers (c - 1 for PV, c idle, c + 1 .. c + 3),
-// one barrier per step.
+// chunk instead of once in every PV wave: in step c the QK waves score chunk
+// c + 1 and turn chunk c's scores into P (wave q: heads 4q .. 4q + 3, two rows
+// per lane, the lazy reference per head), writing P and the reference's factor
+// to LDS, while the PV waves rescale and accumulate chunk c - 1; five chunk
+// buffers (c - 1 for PV, c idle, c + 1 .. c + 3), one barrier per step.
+// Every wave issues an eighth of each chunk's gathers (a wave stalls while the
+// CU's memory pipeline accepts its loads, so the stall is shared by all).
 template <int SRC, int DQK, bool SMQK>
 __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
-                                                bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
+                                                int groups, bool is_win, int64_t first, int n, float* o_part,
+                                                float* lse_part) {
     using G = Stage<SRC, DQK>;
     using V = Waves<4, 1>;                                  // score layout of the 4 QK waves
     static_assert(G::kDirect, "rows staged by DMA");
     constexpr int NB = SMQK ? 5 : 4;
     static_assert(!SMQK || SRC == SRC_E4M3, "P in LDS: E4M3 rows");
-    constexpr int kHi = (G::kInstr + 3) / 4;              // loads per QK wave, waves q < kInstr % 4
-    constexpr int kLo = G::kInstr / 4;
+    constexpr int kHi = (G::kInstr + 7) / 8;              // loads per wave and chunk, waves w < kInstr % 8
+    constexpr int kLo = G::kInstr / 8;
     constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
     constexpr int NMAIN_W = 8;                            // main k-steps per QK wave
     constexpr int NROPE_W = NROPE / 2;
@@ -636,21 +639,23 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
                                      : a.cache + b * a.stride;
     const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;   // at most 2 KiB
     const uint32_t buf_m0 = __builtin_amdgcn_readfirstlane(lds_addr(bufs));
-    // QK waves' DMA slots: slot (i) = 64 (q + 4 i) + lane, the same in every chunk
+    // every wave gathers its share of each chunk: slot (i) = 64 (w + 8 i) + lane, the same in every chunk
+    // (a wave stalls while the CU's memory pipeline takes its loads; shared, the stall is spread)
     int slot_row[kHi];
     uint32_t slot_off[kHi];
     bool slot_data[kHi];
 #pragma unroll
     for (int i = 0; i < kHi; ++i) {
-        const int s = 64 * (q + 4 * i) + lane;
+        const int s = 64 * (w + 8 * i) + lane;
         const int u = s / G::kPieces, p = s - u * G::kPieces;
         slot_row[i] = u < kChunk ? u : kChunk;
         slot_off[i] = 16u * (uint32_t)p;
         slot_data[i] = u < kChunk && p < G::kDataPieces;
     }
-    auto issue = [&](int c) -> uint32_t {                   // returns the slots whose row has no bytes
+    // issue chunk c into buffer `into` (by default its own, c % NB); returns the slots whose row has no bytes
+    auto issue = [&](int c, int into = -1) -> uint32_t {
         uint32_t zm = 0;
-        const uint32_t m0 = buf_m0 + (uint32_t)((c % NB) * G::kBytes);
+        const uint32_t m0 = buf_m0 + (uint32_t)(((into < 0 ? c : into) % NB) * G::kBytes);
         int32_t rr[kHi];
 #pragma unroll
         for (int i = 0; i < kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
@@ -666,13 +671,13 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
         }
 #pragma unroll
         for (int i = 0; i < kHi; ++i)
-            if (q + 4 * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(q + 4 * i));
+            if (w + 8 * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(w + 8 * i));
         return zm;
     };
     // wait for chunk c (the `later` chunks issued after it, 0 .. 2, may stay in flight)
     // and zero its slots without row bytes (their P is 0; stand-in bytes could decode to NaN)
     auto land = [&](int c, int later, uint32_t zm) {
-        const bool hi = q < (G::kInstr & 3) || (G::kInstr & 3) == 0;
+        const bool hi = w < (G::kInstr & 7) || (G::kInstr & 7) == 0;
         if (later >= 2) {
             if (hi) wait_vmcnt<2 * kHi>();
             else wait_vmcnt<2 * kLo>();
@@ -687,7 +692,7 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
 #pragma unroll
             for (int i = 0; i < kHi; ++i)
                 if (zm & (1u << i))
-                    *reinterpret_cast<u32x4*>(buf + 16 * (64 * (q + 4 * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4*>(buf + 16 * (64 * (w + 8 * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
         }
     };
     // scores of chunk c (rows 16 rt .. +15, the wave's K half) into parity c & 1
@@ -857,38 +862,42 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
         }
     };
 
+    // ---- L2 warm-up: the head groups of a split run on one XCD and gather the same rows, so
+    // each pulls its share of the chunks past the first three (chunk c goes to head group
+    // c mod groups) from HBM at once; the chunk loads that follow then find those rows in the
+    // XCD's L2. The bytes land in buffer NB - 1, which no chunk uses before the prologue's
+    // waits (issued before chunk 0, these loads are counted first).
+    auto prefetch = [&]() {
+        for (int c = 3 + ((hg - 3) % groups + groups) % groups; c < nc; c += groups) (void)issue(c, NB - 1);
+    };
     // ---- prologue: chunks 0 .. 2 in flight, chunk 0 landed and scored, chunk 1 landed
-    uint32_t zm0 = 0, zm1 = 0, zm2 = 0;                     // zero masks of chunks c + 1, c + 2, c + 3
-    if (SMQK) {                                            // QK waves gather chunks 0, 1; PV waves from 2 on
-        if (qk_role) {
-            uint32_t z0 = 0;
-            if (nc > 0) z0 = issue(0);
-            if (nc > 1) zm0 = issue(1);
-            if (nc > 0) land(0, nc > 1 ? 1 : 0, z0);
-        } else if (nc > 2) {
-            zm1 = issue(2);
-        }
-    } else if (qk_role) {
-        uint32_t z0 = 0;
+    uint32_t zm1 = 0, zm2 = 0;                              // zero masks of chunks c + 2, c + 3
+    {
+        prefetch();
+        uint32_t z0 = 0, z1 = 0;
         if (nc > 0) z0 = issue(0);
-        if (nc > 1) zm0 = issue(1);
+        if (nc > 1) z1 = issue(1);
         if (nc > 2) zm1 = issue(2);
         if (nc > 0) land(0, min(2, nc - 1), z0);
+        __syncthreads();
+        if (qk_role && nc > 0) qk(0);
+        if (nc > 1) land(1, nc > 2 ? 1 : 0, z1);
+        __syncthreads();
     }
-    __syncthreads();
-    if (qk_role) {
-        if (nc > 0) qk(0);
-        if (nc > 1) land(1, (!SMQK && nc > 2) ? 1 : 0, zm0);   // with SMQK chunk 2 is the PV waves' load
-    }
-    __syncthreads();
 
     // each role in a loop of its own, one barrier per chunk in both (the output tile
-    // then lives in the PV loop alone; a shared loop made the compiler copy it per chunk)
+    // then lives in the PV loop alone; a shared loop made the compiler copy it per chunk);
+    // in step c every wave issues its share of chunk c + 3 (into the buffer chunk c - NB + 3
+    // left, consumed before the previous barrier) and waits for its share of chunk c + 2
     if constexpr (SMQK) {                                  // step c: scores c + 1, P of c, PV of c - 1
         if (qk_role) {
             for (int c = 0; c <= nc; ++c) {
+                if (c + 3 < nc) zm2 = issue(c + 3);
                 if (c + 1 < nc) qk(c + 1);
                 if (c < nc) softmax_qk(c);
+                if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
+                zm1 = zm2;
+                zm2 = 0;
                 __syncthreads();
             }
             const float l = row16_sum(l_q);                // the head's sum over its 16 lanes
@@ -898,7 +907,7 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
             }
         } else {
             for (int c = 0; c <= nc; ++c) {
-                if (c + 3 < nc) zm2 = issue(c + 3);        // into chunk c - 2's buffer (read before the barrier)
+                if (c + 3 < nc) zm2 = issue(c + 3);
                 if (c >= 1) pv(c - 1);
                 if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
                 zm1 = zm2;
@@ -907,9 +916,9 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
             }
         }
         __syncthreads();                                   // l and the reference of every head
-    } else if (qk_role) {
+    } else if (qk_role) {                                  // step c: scores c + 1 (QK), PV of c
         for (int c = 0; c < nc; ++c) {
-            if (c + 3 < nc) zm2 = issue(c + 3);            // into chunk c - 1's buffer (read before the barrier)
+            if (c + 3 < nc) zm2 = issue(c + 3);
             if (c + 1 < nc) qk(c + 1);
             if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
             zm1 = zm2;
@@ -918,7 +927,11 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
         }
     } else {
         for (int c = 0; c < nc; ++c) {
+            if (c + 3 < nc) zm2 = issue(c + 3);
             pv(c);
+            if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
+            zm1 = zm2;
+            zm2 = 0;
             __syncthreads();
         }
     }
@@ -937,6 +950,362 @@ __device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* sm
         if (q == 0 && g == 0)
             lse_part[prow] = (l > 0.0f) ? (mref + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
                                         : -__builtin_inff();
+    }
+}
+
+// ------------------------------------------------------------------------
+// Gather-all split (8 waves, one head tile of 16 heads, up to R rows).
+//
+// A split's rows are gathered into LDS at once, as the value region: E4M3 rows
+// as stored up to their RoPE part (512 codes | 4 fp32 block scales = 528 B,
+// by LDS DMA, so the region is one contiguous image of 33 16-byte pieces per
+// row); bf16 rows (and window entries) as their leading 512 channels (DMA, one
+// row per load instruction, 1056-byte stride); E2M1 rows through registers,
+// widened exactly to bf16 (E2M1 value times its E4M3 scale) in the same
+// 1056-byte layout. RoPE channels (576-channel rows) are loaded per lane
+// straight into the QK operand registers. The queries of the 16 heads sit in
+// LDS. Then, with no per-chunk chain:
+//   A  QK: wave w scores row tiles w, w + 8 (16 rows x 16 heads each) over the
+//      whole K width (bf16 MFMA; E4M3 codes widened exactly, one accumulator per
+//      128-channel block times the row's scale);
+//   B  softmax over the split's rows, exact: the heads' maxima meet in LDS, P =
+//      2^(z - max) goes to LDS (over the queries, no longer needed);
+//   C  PV: wave w owns value channels 64 w .. 64 w + 63 for all 16 heads and
+//      every row (V^T through the transposing LDS reads; P, times the E4M3 row's
+//      block scale, as a high and a low bf16 term).
+// The split's normalised output and logsumexp are its partial, merged by
+// k_merge. One DMA wait and three barriers per workgroup; each CU gathers a
+// split's rows once per head tile, at the rate its memory pipeline accepts them.
+namespace gd {
+constexpr int kQStride = 1168;                             // bytes per head of the staged queries (576 bf16 + 16 B)
+template <int SRC>
+struct VRow {
+    static constexpr int kStride = SRC == SRC_E4M3 ? 528 : 1056;
+    static constexpr int kRopeOff = SRC == SRC_E4M3 ? 528 : 1024;   // byte offset of a 576-channel row's RoPE part
+};
+template <int SRC, int R>
+struct Lay {
+    static constexpr int kVBytes = R * VRow<SRC>::kStride;
+    static constexpr int kQ = kVBytes;                     // queries [16][kQStride], later P [16][R + 4] fp32
+    static constexpr int kPStride = R + 4;
+    static constexpr int kQBytes = (16 * kQStride > 16 * kPStride * 4) ? 16 * kQStride : 16 * kPStride * 4;
+    static constexpr int kIdx = kQ + kQBytes;              // row indices [R]
+    static constexpr int kRed = kIdx + R * 4;              // [2][8 waves][16 heads]: maxima, sums
+    static constexpr int kBytes = kRed + 2 * 8 * 16 * 4;
+};
+template <int SRC_MAIN, int DQK>
+constexpr int lds_bytes() {
+    constexpr int m = Lay<SRC_MAIN, SRC_MAIN == SRC_E4M3 ? 256 : 128>::kBytes;
+    constexpr int w = Lay<SRC_BF16, 128>::kBytes;
+    return m > w ? m : w;
+}
+}  // namespace gd
+
+template <int SRC, int DQK, int R>
+__device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
+                                               bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
+    using L = gd::Lay<SRC, R>;
+    constexpr int VS = gd::VRow<SRC>::kStride;
+    constexpr int NT = (R / 16 + 7) / 8;                   // row tiles per wave (waves w < R / 16 have them)
+    constexpr bool kRope = DQK == 576;
+    constexpr int NMAIN = 16;                              // k-steps of 32 channels in the value region
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, g = lane >> 4;
+    uint8_t* V = smem;
+    uint8_t* Q = smem + L::kQ;
+    float* P = reinterpret_cast<float*>(smem + L::kQ);
+    int32_t* ridx = reinterpret_cast<int32_t*>(smem + L::kIdx);
+    float* red = reinterpret_cast<float*>(smem + L::kRed);
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float zscale = a.scale * kLog2e;
+    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
+                                     : a.cache + b * a.stride;
+    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;
+
+    // ---- row indices (-1: no row) and the 16 heads' queries
+    if (tid < R) {
+        int32_t r = -1;
+        if (tid < n) {
+            if (is_win) r = (int32_t)(first + tid);
+            else {
+                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
+                if (s >= 0 && s < a.capacity) r = s;
+            }
+        }
+        ridx[tid] = r;
+    }
+    {
+        constexpr int kPer = DQK / 8;                      // 16-byte pieces per head
+        constexpr int kIt = (16 * kPer + 511) / 512;
+        const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + 16 * hg) * DQK;
+        u32x4 qv[kIt];
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {                    // every load issued before the first store
+            const int it = tid + 512 * i, h = it / kPer, pc = it - h * kPer;
+            if (it < 16 * kPer) qv[i] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)h * DQK + 8 * pc);
+        }
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int it = tid + 512 * i, h = it / kPer, pc = it - h * kPer;
+            if (it < 16 * kPer) *reinterpret_cast<u32x4*>(Q + h * gd::kQStride + 16 * pc) = qv[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- gather the value region; slots without a row load a stand-in and are zeroed once landed
+    const uint32_t v_m0 = __builtin_amdgcn_readfirstlane(lds_addr(V));
+    uint32_t zmask = 0;
+    if constexpr (SRC == SRC_E4M3) {
+        constexpr int NI = R * 33 / 64;                   // load instructions: 33 pieces per row, 64 per load
+        constexpr int PW = (NI + 7) / 8;
+        // the head groups of a split (one XCD) gather the same rows: each starts at a different
+        // eighth of them, so that a row's first request (from HBM) is spread over the group and
+        // the others find it in L2
+        const int rot = ((hg & 7) * (NI / 8)) & ~7;
+#pragma unroll
+        for (int i = 0; i < PW; ++i) {
+            // the group's own eighth first, landed before the rest is requested: by then the
+            // other head groups' eighths are in flight or in L2, not all eight missing at once
+            if (i == (PW + 7) / 8) wait_vmcnt<0>();
+            int I = w + 8 * i;
+            if (I < NI) {
+                I = (I + rot) % NI;                        // (rot % 8 == 0: a wave's loads stay its own slots)
+                const int P16 = 64 * I + lane;
+                const int u = P16 / 33, pc = P16 - 33 * u;
+                const int32_t r = ridx[u];
+                zmask |= r < 0 ? (1u << i) : 0u;
+                const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * pc
+                                            : reinterpret_cast<const uint8_t*>(a.q);
+                dma16(src, __builtin_amdgcn_readfirstlane(v_m0 + 1024u * (uint32_t)I));
+            }
+        }
+    } else if constexpr (SRC == SRC_BF16) {
+        constexpr int PW = R / 8;                          // one row per load instruction
+        const int rot = (hg & 7) * (R / 8);                // (a multiple of 8: a wave keeps its rows)
+#pragma unroll 4
+        for (int i = 0; i < PW; ++i) {
+            if (i == (PW + 7) / 8) wait_vmcnt<0>();       // the group's own eighth first (as above)
+            const int u = (w + 8 * i + rot) % R;
+            const int32_t r = ridx[u];
+            zmask |= r < 0 ? (1u << i) : 0u;
+            const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * lane
+                                        : reinterpret_cast<const uint8_t*>(a.q);
+            dma16(src, __builtin_amdgcn_readfirstlane(v_m0 + (uint32_t)(VS * u)));
+        }
+    } else {                                               // E2M1 rows: 16 pieces of 32 channels per row
+        constexpr int kPer = R * 16 / 512;
+        u32x4 nib[kPer];
+        uint32_t scb[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int item = tid + 512 * i, u = item >> 4, pc = item & 15;
+            const int32_t r = ridx[u];
+            const uint8_t* rp = row_base + (uint64_t)(uint32_t)(r < 0 ? 0 : r) * row_bytes;
+            nib[i] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 16 * pc) : u32x4{0u, 0u, 0u, 0u};
+            scb[i] = r >= 0 ? *reinterpret_cast<const uint16_t*>(rp + 256 + 2 * pc) : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int item = tid + 512 * i, u = item >> 4, pc = item & 15;
+            u32x4* d = reinterpret_cast<u32x4*>(V + u * VS + 64 * pc);
+            const float s0 = e4m3_to_f32(scb[i] & 0xFFu), s1 = e4m3_to_f32((scb[i] >> 8) & 0xFFu);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float sc = q4 < 2 ? s0 : s1;
+                const uint32_t wv = nib[i][q4];
+                const f32x2 v0 = e2m1x2_to_f32<0>(wv), v1 = e2m1x2_to_f32<1>(wv);
+                const f32x2 v2 = e2m1x2_to_f32<2>(wv), v3 = e2m1x2_to_f32<3>(wv);
+                d[q4] = u32x4{pack_bf16_trunc(v0.x * sc, v0.y * sc), pack_bf16_trunc(v1.x * sc, v1.y * sc),
+                              pack_bf16_trunc(v2.x * sc, v2.y * sc), pack_bf16_trunc(v3.x * sc, v3.y * sc)};
+            }
+        }
+    }
+    // RoPE channels of the wave's row tiles, straight into QK operand registers (A layout:
+    // lane (row j, k-group g) holds channels 512 + 32 s + 8 g .. + 7 of its row)
+    u32x4 rope[NT][2];
+    if constexpr (kRope) {
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+            const int tt = w + 8 * m;
+            const int32_t r = (16 * tt < R) ? ridx[16 * tt + j] : -1;
+            const uint8_t* rp = row_base + (uint64_t)(uint32_t)(r < 0 ? 0 : r) * row_bytes + gd::VRow<SRC>::kRopeOff;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                rope[m][s2] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 2 * (32 * s2 + 8 * g))
+                                     : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    wait_vmcnt<0>();
+    if constexpr (SRC == SRC_E4M3) {
+        constexpr int NI = R * 33 / 64;
+        constexpr int PW = (NI + 7) / 8;
+        const int rot = ((hg & 7) * (NI / 8)) & ~7;
+        if (__builtin_amdgcn_ballot_w64(zmask != 0u)) {
+#pragma unroll
+            for (int i = 0; i < PW; ++i)
+                if ((zmask >> i) & 1u)
+                    *reinterpret_cast<u32x4*>(V + 16 * (64 * ((w + 8 * i + rot) % NI) + lane)) = u32x4{0u, 0u, 0u, 0u};
+        }
+    } else if constexpr (SRC == SRC_BF16) {
+        const int rot = (hg & 7) * (R / 8);
+        if (__builtin_amdgcn_ballot_w64(zmask != 0u)) {
+            for (int i = 0; i < R / 8; ++i)
+                if ((zmask >> i) & 1u)
+                    *reinterpret_cast<u32x4*>(V + VS * ((w + 8 * i + rot) % R) + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __syncthreads();
+
+    // ---- A: scores of the wave's row tiles; lane (head j, g) ends with rows 4 g .. 4 g + 3 of each tile
+    constexpr int NQ = DQK / 32;                           // k-steps over the K width
+    u32x4 qv[NQ];                                          // B operands: channels 32 s + 8 g .. of head j
+    {
+        const uint8_t* qh = Q + j * gd::kQStride + 16 * g;
+#pragma unroll
+        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
+    }
+    float z[NT][4];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+        const int tt = w + 8 * m;
+        const bool live = 16 * tt < n;                     // (wave-uniform) a tile with a row of the split
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            const uint8_t* krow = V + (16 * tt + j) * VS;
+            if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk) {
+                    f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int st = 4 * blk + s4;
+                        const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * st + 8 * g);
+                        t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[st], t4);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[r] += t4[r] * *reinterpret_cast<const float*>(V + (16 * tt + 4 * g + r) * VS + 512 + 4 * blk);
+                }
+            } else {
+#pragma unroll
+                for (int st = 0; st < NMAIN; ++st)
+                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * st + 8 * g)), qv[st], acc);
+            }
+            if constexpr (kRope) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    acc = mfma_bf16(rope[m][s2], qv[NMAIN + s2], acc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * tt + 4 * g + r;
+            z[m][r] = (live && ridx[row] >= 0) ? acc[r] * zscale : -__builtin_inff();
+        }
+    }
+
+    // ---- B: exact softmax over the split's rows (base 2)
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, z[m][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    if (g == 0) red[16 * w + j] = mloc;
+    __syncthreads();                                       // maxima in; every wave is past its query reads
+    float M = red[j];
+#pragma unroll
+    for (int ww = 1; ww < 8; ++ww) M = fmaxf(M, red[16 * ww + j]);
+    float sloc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+        const int tt = w + 8 * m;
+        f32x4 pv4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pv4[r] = (z[m][r] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[m][r] - M);
+            sloc += pv4[r];
+        }
+        if (16 * tt < R) *reinterpret_cast<f32x4*>(P + j * L::kPStride + 16 * tt + 4 * g) = pv4;
+    }
+    sloc += __shfl_xor(sloc, 16, 64);
+    sloc += __shfl_xor(sloc, 32, 64);
+    if (g == 0) red[128 + 16 * w + j] = sloc;
+    __syncthreads();                                       // P and the sums in
+
+    // ---- C: PV over every row for value channels 64 w .. 64 w + 63
+    f32x4 o[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int blk = w >> 1;                                // the E4M3 block of the wave's channels
+    for (int st = 0; st < R / 32; ++st) {
+        if (32 * st >= n) break;
+        const float* pr = P + j * L::kPStride + 32 * st + 8 * g;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+        float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] *= *reinterpret_cast<const float*>(V + (32 * st + 8 * g + e) * VS + 512 + 4 * blk);
+        }
+        u32x4 pa, pb;
+        split_bf16x8(p, pa, pb);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int c0 = 64 * w + 16 * mt;
+            u32x4 av;
+            if constexpr (SRC == SRC_E4M3) {
+                av = e4m3x8_to_bf16(ds_tr8(V + (32 * st + 8 * g + (j >> 1)) * VS + c0 + 8 * (j & 1)));
+            } else {
+                const uint8_t* vp = V + (32 * st + 8 * g + (j >> 2)) * VS + 2 * (c0 + 4 * (j & 3));
+                const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * VS);
+                av = u32x4{r0.x, r0.y, r1.x, r1.y};
+            }
+            o[mt] = mfma_bf16(av, pa, o[mt]);
+            o[mt] = mfma_bf16(av, pb, o[mt]);
+        }
+    }
+
+    // ---- the split's partial: normalised output (channels 64 w ..) and logsumexp (natural log)
+    float l = red[128 + j];
+#pragma unroll
+    for (int ww = 1; ww < 8; ++ww) l += red[128 + 16 * ww + j];
+    const int head = 16 * hg + j;
+    const int64_t prow = ((int64_t)b * S + split) * a.H + head;
+    const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        *reinterpret_cast<float4*>(o_part + prow * kDv + 64 * w + 16 * mt + 4 * g) =
+            make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
+    if (w == 0 && g == 0)
+        lse_part[prow] = (l > 0.0f) ? (M + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
+}
+
+template <int SRC_MAIN, int DQK>
+__global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int S_win, int rps, int rps_win,
+                                                  int groups, int n_items, float* o_part, float* lse_part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int L = blockIdx.x;
+    const int per = gridDim.x >> 3;
+    const int item = (L & 7) * per + (L >> 3);
+    if (item >= n_items) return;
+    const int S = S_main + S_win;
+    const int hg = item % groups;
+    const int rest = item / groups;
+    const int split = rest % S;
+    const int b = rest / S;
+    constexpr int RM = SRC_MAIN == SRC_E4M3 ? 256 : 128;
+    if (split < S_main) {
+        const int64_t first = (int64_t)split * rps;
+        const int n = (int)((a.k - first < rps) ? a.k - first : rps);
+        decode_split_g<SRC_MAIN, DQK, RM>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
+    } else {
+        const int64_t first = (int64_t)(split - S_main) * rps_win;
+        const int wl = (int)clamp_visible(a.win_len[b], a.W);
+        int n = (int)(wl - first);
+        n = n < 0 ? 0 : (n > rps_win ? rps_win : n);
+        decode_split_g<SRC_BF16, DQK, 128>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
     }
 }
 
@@ -959,8 +1328,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
         const int64_t first = (int64_t)split * rps;
         const int n = (int)((a.k - first < rps) ? a.k - first : rps);
         if constexpr (NW == 8)
-            decode_split_ws<SRC_MAIN, DQK, SRC_MAIN == SRC_E4M3>(a, smem, b, split, S, hg, false, first, n, o_part,
-                                                                  lse_part);
+            decode_split_ws<SRC_MAIN, DQK, SRC_MAIN == SRC_E4M3>(a, smem, b, split, S, hg, groups, false, first, n,
+                                                                  o_part, lse_part);
         else
             decode_split<SRC_MAIN, DQK, NW, HT>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
     } else {
@@ -969,7 +1338,8 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
         int n = (int)(wl - first);
         n = n < 0 ? 0 : (n > rps ? rps : n);
         if constexpr (NW == 8)
-            decode_split_ws<SRC_BF16, DQK, false>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+            decode_split_ws<SRC_BF16, DQK, false>(a, smem, b, split, S, hg, groups, true, first, n, o_part,
+                                                  lse_part);
         else
             decode_split<SRC_BF16, DQK, NW, HT>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
     }
@@ -978,7 +1348,6 @@ __global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_mai
 // Combine the splits of one (b, h) by their logsumexp; thread t owns channels 4t .. 4t+3.
 // Up to kMergeFast splits, every load (logsumexps and partials) is issued at
 // once, from clamped in-bounds addresses, so the block pays one memory round trip.
-constexpr int kMergeFast = 16;
 // With attention sinks the head's sink logit joins the normaliser (no value
 // vector): out scales by exp(lse_U - lse) and lse = logaddexp(lse_U, sink).
 // The output's RoPE inverse on thread t's four channels 4t .. 4t + 3 (the
@@ -1235,9 +1604,42 @@ bool decode_supported(int fmt, int dim, int rope, int d_v, int H) {
     return dim + rope <= 1024 && d_v <= dim + rope && d_v > 0;
 }
 
+// Splits of the gather-all decode: R = 256 rows for E4M3 rows, 128 otherwise (and for
+// the window), halved (down to 32) while the chip is short of a workgroup per CU, the
+// halved splits still fit one round of workgroups (one per CU: the LDS holds one) and
+// the merge still takes every split's partial in one round of loads (kMergeFast);
+// the option decode_rows_per_split (32 .. R, a multiple of 32) overrides the main rows' R.
+Geometry gather_geometry(int fmt, int B, int H, int k, int W) {
+    Geometry g{};
+    g.ht = 1;
+    g.nw = 8;
+    g.groups = H / 16;
+    const int R = fmt == MLA_FMT_E4M3_S128 ? 256 : 128;
+    int rps = R, rpw = 128;
+    const int v = (int)option(OPT_DECODE_RPS);
+    if (v >= 32 && v <= R && v % 32 == 0) {
+        rps = v;
+    } else {
+        auto blocks = [&](int r, int rw) {
+            return (int64_t)B * g.groups * ((k + r - 1) / r + (W + rw - 1) / rw);
+        };
+        auto splits = [&](int r, int rw) { return (k + r - 1) / r + (W + rw - 1) / rw; };
+        while (rps > 32 && blocks(rps, rpw) < 256 && blocks(rps / 2, rpw > 32 ? rpw / 2 : rpw) <= 256 &&
+               splits(rps / 2, rpw > 32 ? rpw / 2 : rpw) <= kMergeFast) {
+            rps /= 2;
+            if (rpw > 32) rpw /= 2;
+        }
+    }
+    g.rps = rps;
+    g.rps_win = rpw;
+    g.S_main = (k + rps - 1) / rps;
+    g.S_win = (W + rpw - 1) / rpw;
+    return g;
+}
+
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W) {
     if (!mfma_shape(fmt, dim, rope, d_v, H)) return 0;
-    const Geometry g = decode_geometry(B, H, k, W);
+    const Geometry g = gather_geometry(fmt, B, H, k, W);
     const size_t S = (size_t)(g.S_main + g.S_win);
     const size_t o = (size_t)B * S * H * kDv * sizeof(float);
     const size_t l = (size_t)B * S * H * sizeof(float);
@@ -1274,6 +1676,26 @@ static hipError_t launch_layout(const DecodeArgs& a, const Geometry& g, float* o
     return launch_mfma<SRC_MAIN, DQK, 4, 1>(a, g, o_part, lse_part, stream);
 }
 
+template <int SRC_MAIN, int DQK>
+static hipError_t launch_gather(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
+                                hipStream_t stream) {
+    const int S = g.S_main + g.S_win;
+    const int n_items = a.B * S * g.groups;
+    const int grid = (n_items + 7) / 8 * 8;
+    constexpr int lds = gd::lds_bytes<SRC_MAIN, DQK>();
+    auto kern = k_decode_g<SRC_MAIN, DQK>;
+    static bool attr_set = false;                          // dynamic LDS above 64 KiB, once per kernel
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const ProfSlot p = prof_slot(PROF_DECODE);
+    return launch_kernel(kern, dim3(grid), dim3(512), lds, stream, p.start, p.stop, a, g.S_main, g.S_win, g.rps,
+                         g.rps_win, g.groups, n_items, o_part, lse_part);
+}
+
 // An MXFP8 window ring [B, W, D + D/32 bytes] widened to bf16 rows [B, W, D]:
 // the E4M3 value times its block's power of two, formed in fp32 (exact) and
 // rounded to bf16, exact unless the product lies below bf16's smallest
@@ -1302,17 +1724,17 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
         const ProfSlot p = prof_slot(PROF_DECODE);
         return launch_kernel(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, p.start, p.stop, a);
     }
-    const Geometry g = decode_geometry(a.B, a.H, a.k, a.win ? a.W : 0);
+    const Geometry g = gather_geometry(a.fmt, a.B, a.H, a.k, a.win ? a.W : 0);
     const int S = g.S_main + g.S_win;
     const size_t o_bytes = (((size_t)a.B * S * a.H * kDv * sizeof(float)) + 255) & ~(size_t)255;
     float* o_part = reinterpret_cast<float*>(a.workspace);
     float* lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + o_bytes);
     if (S > 0) {
         hipError_t e = hipSuccess;
-        if (a.fmt == MLA_FMT_E4M3_S128) e = launch_layout<SRC_E4M3, 576>(a, g, o_part, lse_part, stream);
-        else if (a.fmt == MLA_FMT_E2M1_S16) e = launch_layout<SRC_FP4, 512>(a, g, o_part, lse_part, stream);
-        else if (a.rope == 64) e = launch_layout<SRC_BF16, 576>(a, g, o_part, lse_part, stream);
-        else e = launch_layout<SRC_BF16, 512>(a, g, o_part, lse_part, stream);
+        if (a.fmt == MLA_FMT_E4M3_S128) e = launch_gather<SRC_E4M3, 576>(a, g, o_part, lse_part, stream);
+        else if (a.fmt == MLA_FMT_E2M1_S16) e = launch_gather<SRC_FP4, 512>(a, g, o_part, lse_part, stream);
+        else if (a.rope == 64) e = launch_gather<SRC_BF16, 576>(a, g, o_part, lse_part, stream);
+        else e = launch_gather<SRC_BF16, 512>(a, g, o_part, lse_part, stream);
         if (e != hipSuccess) return e;
     }
     const ProfSlot p = prof_slot(PROF_MERGE);

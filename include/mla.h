@@ -159,9 +159,8 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
  *   "topk_final"             0..1       1: the 256-thread final of the many-workgroup path
  *   "scan_queues"            0..1       1: the queue-fed 32x32 indexer scan
  *   "scan_blocks"            0..65536   target number of 4-wave indexer-scan workgroups
- *   "decode_rows_per_split"  0..256     selected rows per decode split (32..256, multiple of 32)
- *   "decode_heads_per_group" 0..32      heads per decode workgroup (16 or 32)
- *   "decode_waves"           0..8       waves per decode workgroup (4 or 8)
+ *   "decode_rows_per_split"  0..256     selected rows per decode split (a multiple of 32 up to
+ *                                       256 for E4M3 rows, 128 for bf16 and E2M1 rows)
  * Values in range that a kernel cannot use are ignored. Errors:
  * MLA_ERR_INVALID_ARG (unknown name, NULL pointer, value out of range).
  */

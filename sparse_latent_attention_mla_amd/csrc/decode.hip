@@ -6,30 +6,19 @@
 // ([P1] "DeepSeek's Attention and KV Cache - From MLA to CSA2", "DeepSeek-V2",
 // "Why RoPE breaks the trick" and "Check it in numpy"; [P2] "From MLA to DSA
 // to HCA/CSA", Part 2 "What replaced MLA"; each selected latent is read once
-// per head group, [P1] "DeepSeek-V3.2", "The lightning indexer").
+// per head group of 16, [P1] "DeepSeek-V3.2", "The lightning indexer").
 //
 // MFMA path (H a multiple of 16 up to 128, d_v = 512, K width 576 = 512 + 64 or 512):
-//   one workgroup per (b, split, group of 16 heads); a split is `rps` <= 256
-//   consecutive entries of idx[b] (or of the window ring). Work items are laid
-//   out so that the head groups of one split run on the same XCD and share its
-//   L2. The split's rows stream through LDS in 32-row chunks:
-//   * E4M3 and bf16 rows are gathered straight from HBM into LDS
-//     (global_load_lds_dwordx4, several chunks in flight); E2M1 rows pass
-//     through registers and are staged dequantised to bf16 (exact).
-//   * QK: a wave takes rows 16 rt .. +15 of the chunk and one part of the K
-//     width; K comes from the staged rows (E4M3 codes widened exactly to bf16,
-//     one accumulator per 128-channel block times the row's fp32 scale),
-//     queries sit in registers, bf16 MFMA. Partial scores meet in LDS.
-//   * Softmax: online, with a lazily raised reference maximum, on every PV wave.
-//   * PV: a wave owns a slice of the 512 value channels for all 16 heads. V^T
-//     operands come from the staged rows through the transposing LDS reads
-//     (ds_read_b64_tr_b8 for E4M3 codes, ds_read_b64_tr_b16 for bf16); bf16
-//     MFMA with P (times the row's block scale for E4M3) split into a high and
-//     a low bf16 part.
-//   Layouts: rows staged by DMA use 8 wave-specialised waves (decode_split_ws:
-//   4 waves stage and score chunk c + 1 while 4 run softmax and PV on chunk c,
-//   one barrier per chunk); E2M1 rows, two head tiles per workgroup or the
-//   decode_waves option 4 use 4 waves that take both roles in turn (decode_split).
+//   one workgroup of 8 waves per (b, split, group of 16 heads); a split is up
+//   to 256 consecutive entries of idx[b] (E4M3 rows; 128 for bf16 and E2M1 rows
+//   and for the window ring). Work items are laid out so that the head groups
+//   of one split run on the same XCD and share its L2. The split's rows are
+//   gathered into LDS at once (LDS DMA for E4M3 and bf16 rows; E2M1 rows
+//   widened exactly to bf16 through registers), then QK (bf16 MFMA, E4M3 codes
+//   widened exactly, one accumulator per 128-channel block times the row's
+//   fp32 scale), an exact softmax over the split, and PV with each wave owning
+//   64 value channels (V^T through ds_read_b64_tr_b8 / _b16, P times the E4M3
+//   row's block scale as a high and a low bf16 term) -- see decode_split_g.
 //   The split's normalised output and logsumexp are written as a partial and
 //   k_merge combines the partials by logsumexp.
 // Generic path (any other shape): one workgroup per (b, h), fp32 on the vector
@@ -41,52 +30,13 @@ namespace mla {
 
 namespace {
 
-#ifndef MLA_E4M3_BUFS
-#define MLA_E4M3_BUFS 3                    // E4M3 chunk buffers in LDS (2 or 3)
-#endif
-constexpr int kChunk = 32;                 // rows per pipeline step
 constexpr int kDv = 512;
-constexpr int kMaxWaves = 8;             // waves of a workgroup: 4 or 8
-constexpr int kMaxRps = 256;               // rows per split: one row index per thread
-constexpr int kZs = 36;                    // floats per (head) score row in LDS: 32 rows + pad
 constexpr int kMergeThreads = kDv / 4;
 constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxRows = 8192;
 constexpr int kMergeFast = 16;             // splits the merge loads in one round
 
 enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2 };
-
-// Geometry of one staged 32-row chunk. E4M3 rows are staged as stored
-// (512 codes | 4 fp32 scales | 64 bf16 RoPE = 656 B), bf16 rows as stored and
-// E2M1 rows dequantised to bf16; bf16 rows get 32 bytes of padding so that
-// consecutive rows start 8 LDS banks apart.
-template <int SRC, int DQK>
-struct Stage {
-    static constexpr int kRowBytes = SRC == SRC_E4M3 ? 656 : (SRC == SRC_FP4 ? 288 : 2 * DQK);
-    static constexpr int kStride = SRC == SRC_E4M3 ? 656 : 2 * (SRC == SRC_FP4 ? 512 : DQK) + 32;
-    static constexpr bool kDirect = SRC != SRC_FP4;
-    static constexpr int kPieces = kStride / 16;                  // 16-byte slots per staged row
-    static constexpr int kDataPieces = kRowBytes / 16;            // of which hold row bytes (direct)
-    static constexpr int kInstr = (kChunk * kPieces + 63) / 64;   // direct loads per chunk, 64 slots each
-    static constexpr int kBytes = kDirect ? kInstr * 1024 : kChunk * kStride;
-    static constexpr int kBufs = SRC == SRC_E4M3 ? MLA_E4M3_BUFS : 2;  // chunk buffers
-    static constexpr int kLds = kBufs * kBytes;
-};
-
-// Dynamic LDS: row indices of the split | scores [2 parities][KP][16 HT heads][kZs] | chunk buffers.
-// The waves of a workgroup are 2 row tiles x HT head tiles x KP parts of the K
-// width for QK, and NW slices of the 512 value channels for PV.
-constexpr int kLdsIdx = 0;
-constexpr int kLdsZ = kMaxRps * 4;
-template <int NW, int HT>
-struct Waves {
-    static constexpr int KP = NW / (2 * HT);               // K parts
-    static constexpr int kZBytes = 2 * KP * HT * 16 * kZs * 4;
-    static constexpr int kBuf = kLdsZ + kZBytes;            // offset of the chunk buffers
-    static constexpr int CPW = kDv / NW;                    // value channels per wave
-    static constexpr int MTW = CPW / 16;                    // 16-channel output tiles per wave
-};
-
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -103,26 +53,6 @@ __device__ __forceinline__ u32x2 ds_tr16(const uint8_t* p) {
                  (uint32_t)(uint16_t)r.z | ((uint32_t)(uint16_t)r.w << 16)};
 }
 
-// One DPP lane permutation of a float (compile-time control word).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), CTRL, 0xf, 0xf, false));
-}
-// Max / sum over each row of 16 lanes, on the VALU: swaps within pairs and quads
-// (quad_perm 1,0,3,2 and 2,3,0,1), then the two quads of each half row
-// (row_half_mirror) and the two halves (row_mirror).
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));
-    v = fmaxf(v, dpp_f<0x4E>(v));
-    v = fmaxf(v, dpp_f<0x141>(v));
-    return fmaxf(v, dpp_f<0x140>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-    v += dpp_f<0xB1>(v);
-    v += dpp_f<0x4E>(v);
-    v += dpp_f<0x141>(v);
-    return v + dpp_f<0x140>(v);
-}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // two floats -> two bf16 (round to nearest even, hardware convert), low half first
@@ -140,817 +70,11 @@ __device__ __forceinline__ void split_bf16x8(const float* p, u32x4& hi, u32x4& l
     }
 }
 
-__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
-}
 
 // 8 E4M3 codes -> 8 exact bf16 / fp16 values (two per u32)
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 w) {
     const u32x2 a = e4m3x4_to_bf16(w.x), b = e4m3x4_to_bf16(w.y);
     return u32x4{a.x, a.y, b.x, b.y};
-}
-__device__ __forceinline__ u32x4 e4m3x8_to_f16(u32x2 w) {
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true))};
-}
-
-// Entries per split and heads per workgroup. Fewer, longer splits write fewer
-// fp32 partials; more splits keep more workgroups in flight. The options
-// decode_rows_per_split (32..256, multiple of 32), decode_heads_per_group (16
-// or 32) and decode_waves (4 or 8) override the choice for tuning; the
-// workspace query reads them too.
-struct Geometry {
-    int ht, nw, rps, S_main, S_win, groups;
-    int rps_win;
-};
-
-Geometry decode_geometry(int B, int H, int k, int W) {
-    Geometry g{};
-    g.ht = 1;
-    if (option(OPT_DECODE_HEADS) == 32 && H % 32 == 0) g.ht = 2;
-    g.groups = H / (16 * g.ht);
-    // waves per workgroup: 8 (wave-specialised: half stage and score chunk c + 1 while
-    // the other half runs softmax and PV on chunk c) unless decode_waves is 4; two head
-    // tiles per workgroup, and E2M1 rows (staged through registers), use 4
-    g.nw = 8;
-    if (option(OPT_DECODE_WAVES) == 4) g.nw = 4;
-    if (g.ht == 2) g.nw = 4;
-    int rps = 0;
-    {
-        const int v = (int)option(OPT_DECODE_RPS);
-        if (v >= kChunk && v <= kMaxRps && v % kChunk == 0) rps = v;
-    }
-    if (rps == 0) {
-        // the longest split that still gives every CU a workgroup; at least two chunks
-        constexpr int kTargetBlocks = 256;
-        constexpr int kMinRps = 2 * kChunk;
-        rps = kMinRps;
-        for (int r = kMaxRps; r >= kMinRps; r /= 2) {
-            const int64_t blocks = (int64_t)B * g.groups * ((k + r - 1) / r + (W + r - 1) / r);
-            if (blocks >= kTargetBlocks) { rps = r; break; }
-        }
-    }
-    g.rps = rps;
-    g.S_main = (k + rps - 1) / rps;
-    g.S_win = (W + rps - 1) / rps;
-    return g;
-}
-
-template <int SRC_MAIN, int DQK, int NW, int HT>
-constexpr int decode_lds_bytes(bool window) {
-    if constexpr (NW == 8) {                               // wave-specialised: four chunk buffers (E4M3: five + P)
-        constexpr int m = SRC_MAIN == SRC_E4M3 ? 5 * Stage<SRC_MAIN, DQK>::kBytes + (2 * 16 * kZs + 4 * 16) * 4
-                                               : 4 * Stage<SRC_MAIN, DQK>::kBytes;
-        constexpr int w = 4 * Stage<SRC_BF16, DQK>::kBytes;
-        return Waves<4, 1>::kBuf + ((window && w > m) ? w : m);
-    } else {
-        constexpr int m = Stage<SRC_MAIN, DQK>::kLds, w = Stage<SRC_BF16, DQK>::kLds;
-        return Waves<NW, HT>::kBuf + ((window && w > m) ? w : m);
-    }
-}
-
-// E2M1 rows through registers: 32 rows x 16 pieces (32 channels each) per chunk.
-struct Fp4Slot {
-    u32x4 v;
-    uint32_t sc;
-    int ok;
-};
-
-// One split of one workgroup. SRC is the kind of the rows (the window is bf16).
-template <int SRC, int DQK, int NW, int HT>
-__device__ __forceinline__ void decode_split(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
-                                             bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
-    using G = Stage<SRC, DQK>;
-    using V = Waves<NW, HT>;
-    constexpr int NT = 64 * NW;
-    constexpr int NB = G::kBufs;
-    constexpr int KP = V::KP;                             // K parts split over waves
-    constexpr int kHi = (G::kInstr + NW - 1) / NW;        // per-wave load count, waves w < kInstr % NW
-    constexpr int kLo = G::kInstr / NW;                   // the other waves
-    constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
-    constexpr int NMAIN_W = 16 / KP;                      // main k-steps per wave
-    // RoPE k-steps per wave: all of them with one K part, else step kp for the parts kp < NROPE
-    constexpr int NROPE_W = (KP == 1) ? NROPE : (NROPE > 0 ? 1 : 0);
-    constexpr int NQ = NMAIN_W + NROPE_W;
-    static_assert(KP >= 1 && 16 % KP == 0 && (KP == 1 || NROPE <= KP), "wave layout");
-    constexpr float kLazy = 8.0f;                         // P <= 2^8 before the reference max moves
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = lane & 15, g = lane >> 4;
-    const int rt = w & 1;                                   // QK row tile
-    const int kp = (w >> 1) % KP;                           // QK K part
-    const int qt = (w >> 1) / KP;                           // QK head tile
-    const bool rope_here = (KP == 1) || kp < NROPE;         // the wave's RoPE step exists
-    const int nc = (n + kChunk - 1) / kChunk;
-    int32_t* ridx = reinterpret_cast<int32_t*>(smem + kLdsIdx);
-    float* zs = reinterpret_cast<float*>(smem + kLdsZ);
-    uint8_t* bufs = smem + V::kBuf;
-    constexpr float kLog2e = 1.4426950408889634f;
-    const float zscale = a.scale * kLog2e;
-
-    // ---- queries of the wave's QK head tile and K range: k-step t covers channels 32 t .. 32 t + 31
-    u32x4 qv[NQ];
-    {
-        const int head = 16 * (HT * hg + qt) + j;
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head) * DQK + 8 * g;
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int rs = (KP == 1) ? (i - NMAIN_W) : kp;     // RoPE step of slot i >= NMAIN_W
-            const int t = (i < NMAIN_W) ? (NMAIN_W * kp + i) : (16 + (rope_here ? rs : 0));
-            qv[i] = *reinterpret_cast<const u32x4*>(qp + 32 * t);
-        }
-    }
-    // ---- row indices of the split (-1: no row)
-    if (tid < kMaxRps) {
-        int32_t r = -1;
-        if (tid < n) {
-            if (is_win) r = (int32_t)(first + tid);
-            else {
-                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
-                if (s >= 0 && s < a.capacity) r = s;
-            }
-        }
-        ridx[tid] = r;
-    }
-    __syncthreads();
-
-    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
-                                     : a.cache + b * a.stride;
-    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;   // at most 2 KiB
-    const uint32_t buf_m0 = __builtin_amdgcn_readfirstlane(lds_addr(bufs));
-    // direct path: the lane's slots are the same in every chunk; slot (i) = 64 (w + NW i) + lane
-    // row in chunk (kChunk: none), byte offset in the row, whether the slot holds row bytes
-    int slot_row[kHi];
-    uint32_t slot_off[kHi];
-    bool slot_data[kHi];
-#pragma unroll
-    for (int i = 0; i < kHi; ++i) {
-        const int s = 64 * (w + NW * i) + lane;
-        const int u = s / G::kPieces, p = s - u * G::kPieces;
-        slot_row[i] = u < kChunk ? u : kChunk;
-        slot_off[i] = 16u * (uint32_t)p;
-        slot_data[i] = u < kChunk && p < G::kDataPieces;
-    }
-    // issue chunk c into buffer c % NB; returns the lane's slots whose row has no bytes (to be zeroed)
-    auto issue = [&](int c) -> uint32_t {
-        uint32_t zm = 0;
-        const uint32_t m0 = buf_m0 + (uint32_t)((c % NB) * G::kBytes);
-        int32_t rr[kHi];
-#pragma unroll
-        for (int i = 0; i < kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
-        const void* src[kHi];
-#pragma unroll
-        for (int i = 0; i < kHi; ++i) {
-            const bool row_ok = slot_row[i] < kChunk && rr[i] >= 0;
-            zm |= (slot_row[i] < kChunk && rr[i] < 0) ? (1u << i) : 0u;
-            // computed for every slot and selected without branching; slots without row
-            // bytes load a 16-byte-aligned stand-in (the queries)
-            const uint64_t row = reinterpret_cast<uint64_t>(row_base + slot_off[i]) +
-                                 (uint64_t)(uint32_t)(rr[i] < 0 ? 0 : rr[i]) * row_bytes;
-            const bool use = row_ok && slot_data[i];
-            src[i] = reinterpret_cast<const void*>(use ? row : reinterpret_cast<uint64_t>(a.q));
-        }
-#pragma unroll
-        for (int i = 0; i < kHi; ++i)
-            if (w + NW * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(w + NW * i));
-        return zm;
-    };
-    // register path (E2M1): 512 pieces of 32 channels per chunk, 512 / NT per thread
-    constexpr int kFp4Per = 512 / NT;
-    Fp4Slot fs[kFp4Per];
-    auto fp4_load = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < kFp4Per; ++i) {
-            const int item = tid + NT * i;
-            const int u = item >> 4, p = item & 15;
-            const int32_t r = ridx[kChunk * c + u];
-            fs[i].ok = r >= 0;
-            if (r >= 0) {
-                const uint8_t* rp = row_base + (uint64_t)(uint32_t)r * row_bytes;
-                fs[i].v = *reinterpret_cast<const u32x4*>(rp + 16 * p);
-                fs[i].sc = *reinterpret_cast<const uint16_t*>(rp + 256 + 2 * p);
-            }
-        }
-    };
-    auto fp4_store = [&](int c) {
-        uint8_t* buf = bufs + (c % NB) * G::kBytes;
-#pragma unroll
-        for (int i = 0; i < kFp4Per; ++i) {
-            const int item = tid + NT * i;
-            const int u = item >> 4, p = item & 15;
-            u32x4* d = reinterpret_cast<u32x4*>(buf + u * G::kStride + 64 * p);
-            const float s0 = fs[i].ok ? e4m3_to_f32(fs[i].sc & 0xFFu) : 0.0f;
-            const float s1 = fs[i].ok ? e4m3_to_f32((fs[i].sc >> 8) & 0xFFu) : 0.0f;
-            const u32x4 v = fs[i].ok ? fs[i].v : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float sc = (q < 2) ? s0 : s1;
-                const uint32_t wv = v[q];
-                const f32x2 v0 = e2m1x2_to_f32<0>(wv), v1 = e2m1x2_to_f32<1>(wv);
-                const f32x2 v2 = e2m1x2_to_f32<2>(wv), v3 = e2m1x2_to_f32<3>(wv);
-                d[q] = u32x4{pack_bf16_trunc(v0.x * sc, v0.y * sc), pack_bf16_trunc(v1.x * sc, v1.y * sc),
-                             pack_bf16_trunc(v2.x * sc, v2.y * sc), pack_bf16_trunc(v3.x * sc, v3.y * sc)};
-            }
-        }
-    };
-
-    // ---- running state: reference max (base 2, lazily raised), per-lane partial sums, output tile
-    f32x4 o[HT][V::MTW];
-#pragma unroll
-    for (int h = 0; h < HT; ++h)
-#pragma unroll
-        for (int mt = 0; mt < V::MTW; ++mt) o[h][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref[HT], l_run[HT];
-#pragma unroll
-    for (int h = 0; h < HT; ++h) {
-        m_ref[h] = -__builtin_inff();
-        l_run[h] = 0.0f;
-    }
-
-    uint32_t zm0 = 0, zm1 = 0;                              // zero masks of the chunks in flight
-    if constexpr (G::kDirect) {
-        if (nc > 0) zm0 = issue(0);
-        if (NB > 2 && nc > 1) zm1 = issue(1);
-    } else {
-        if (nc > 0) fp4_load(0);
-    }
-
-    for (int c = 0; c < nc; ++c) {
-        uint8_t* buf = bufs + (c % NB) * G::kBytes;
-        if constexpr (G::kDirect) {
-            // chunk c has landed once at most the later chunk's loads are outstanding
-            if ((NB > 2) && (c + 1 < nc)) {
-                if (w < (G::kInstr % NW) || (G::kInstr % NW) == 0) wait_vmcnt<kHi>();
-                else wait_vmcnt<kLo>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            // rows without bytes read as zeros (their P is 0; stand-in bytes could decode to NaN)
-            if (__builtin_amdgcn_ballot_w64(zm0 != 0u)) {
-#pragma unroll
-                for (int i = 0; i < kHi; ++i)
-                    if (zm0 & (1u << i))
-                        *reinterpret_cast<u32x4*>(buf + 16 * (64 * (w + NW * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
-            }
-        } else {
-            fp4_store(c);
-        }
-        __syncthreads();                                    // chunk c staged; chunk c - 1 consumed
-        if constexpr (G::kDirect) {
-            zm0 = zm1;
-            zm1 = 0;
-            if (c + NB - 1 < nc) {
-                if (NB > 2) zm1 = issue(c + NB - 1);
-                else zm0 = issue(c + NB - 1);
-            }
-        } else {
-            if (c + 1 < nc) fp4_load(c + 1);
-        }
-
-        // ---- QK: rows 16 rt .. +15, K range of the wave, head tile qt
-        {
-            const uint8_t* krow = buf + (16 * rt + j) * G::kStride;
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-                for (int bb = 0; bb < NMAIN_W / 4; ++bb) {
-                    const int blk = (NMAIN_W / 4) * kp + bb;
-                    f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const int t = 4 * blk + s4;
-                        const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * t + 8 * g);
-                        t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[4 * bb + s4], t4);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[r] += t4[r] * *reinterpret_cast<const float*>(buf + (16 * rt + 4 * g + r) * G::kStride +
-                                                                        512 + 4 * blk);
-                }
-#pragma unroll
-                for (int i = 0; i < NROPE_W; ++i) {
-                    const int t = (KP == 1) ? i : kp;          // RoPE k-step within the 64 RoPE channels
-                    if (rope_here)
-                        acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 528 + 2 * (32 * t + 8 * g)),
-                                        qv[NMAIN_W + i], acc);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < NQ; ++i) {
-                    const int rs = (KP == 1) ? (i - NMAIN_W) : kp;
-                    const int t = (i < NMAIN_W) ? (NMAIN_W * kp + i) : (16 + rs);
-                    if (i < NMAIN_W || rope_here)
-                        acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * t + 8 * g)), qv[i], acc);
-                }
-            }
-            float* zd = zs + (((c & 1) * KP + kp) * 16 * HT + 16 * qt + j) * kZs + 16 * rt + 4 * g;
-            *reinterpret_cast<f32x4*>(zd) = acc;
-        }
-        __syncthreads();                                    // scores of chunk c complete
-
-        // ---- softmax on the chunk; lane (j, g) holds rows 8 g .. 8 g + 7 of head j
-        bool vld[8];
-        {
-            const int32_t* rp = ridx + kChunk * c + 8 * g;
-            const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp), r1 = *reinterpret_cast<const u32x4*>(rp + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vld[e] = (int32_t)r0[e] >= 0;
-                vld[4 + e] = (int32_t)r1[e] >= 0;
-            }
-        }
-        float sc[8];                                        // E4M3: the rows' scale of block w (0 for rows without bytes)
-        if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 +
-                                                        4 * ((V::CPW * w) / 128));
-        }
-        float z[HT][8], alpha[HT];
-        bool grow = false;
-#pragma unroll
-        for (int h = 0; h < HT; ++h) {
-            const float* zr = zs + (((c & 1) * KP) * 16 * HT + 16 * h + j) * kZs + 8 * g;
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(zr), a1 = *reinterpret_cast<const f32x4*>(zr + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                z[h][e] = a0[e];
-                z[h][4 + e] = a1[e];
-            }
-#pragma unroll
-            for (int p = 1; p < KP; ++p) {                  // the other K parts' partial scores
-                const float* zr2 = zr + p * 16 * HT * kZs;
-                const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr2), b1 = *reinterpret_cast<const f32x4*>(zr2 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    z[h][e] += b0[e];
-                    z[h][4 + e] += b1[e];
-                }
-            }
-            float cm = -__builtin_inff();
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                z[h][e] = vld[e] ? z[h][e] * zscale : -__builtin_inff();
-                cm = fmaxf(cm, z[h][e]);
-            }
-            cm = xmax4(cm);
-            // the reference moves only when the chunk exceeds it by more than 2^kLazy (and on
-            // the first chunk with a visible row, where the factor is exp2(-inf) = 0 on empty state)
-            const bool up = cm > m_ref[h] + kLazy;
-            alpha[h] = up ? __builtin_amdgcn_exp2f(m_ref[h] - cm) : 1.0f;
-            m_ref[h] = up ? cm : m_ref[h];
-            grow |= up;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int h = 0; h < HT; ++h) {
-                l_run[h] *= alpha[h];
-#pragma unroll
-                for (int mt = 0; mt < V::MTW; ++mt) o[h][mt] = o[h][mt] * alpha[h];
-            }
-        }
-        u32x4 pa[HT], pb[HT];                               // PV B operands: P (times the E4M3 scale) as bf16 hi, lo
-#pragma unroll
-        for (int h = 0; h < HT; ++h) {
-            float ls = 0.0f;
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = (z[h][e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[h][e] - m_ref[h]);
-                ls += p[e];
-                if constexpr (SRC == SRC_E4M3) p[e] *= sc[e];
-            }
-            l_run[h] += ls;
-            split_bf16x8(p, pa[h], pb[h]);
-        }
-
-        // ---- PV: O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels CPW w .. + CPW - 1
-#pragma unroll
-        for (int mt = 0; mt < V::MTW; ++mt) {
-            const int c0 = V::CPW * w + 16 * mt;
-            u32x4 av;
-            if constexpr (SRC == SRC_E4M3) {
-                // lane (G, m) names row 8 G + m / 2, channels c0 + 8 (m & 1) ..; receives channel c0 + m of rows 8 G ..
-                av = e4m3x8_to_bf16(ds_tr8(buf + (8 * g + (j >> 1)) * G::kStride + c0 + 8 * (j & 1)));
-            } else {
-                // lane (G, m) names row 8 G + m / 4 (+4), channels c0 + 4 (m & 3) ..
-                const uint8_t* vp = buf + (8 * g + (j >> 2)) * G::kStride + 2 * (c0 + 4 * (j & 3));
-                const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * G::kStride);
-                av = u32x4{r0.x, r0.y, r1.x, r1.y};
-            }
-#pragma unroll
-            for (int h = 0; h < HT; ++h) {
-                o[h][mt] = mfma_bf16(av, pa[h], o[h][mt]);
-                o[h][mt] = mfma_bf16(av, pb[h], o[h][mt]);
-            }
-        }
-    }
-
-    // ---- partial: normalised output (channels CPW w ..) and logsumexp of the split
-#pragma unroll
-    for (int h = 0; h < HT; ++h) {
-        const float l = xsum4(l_run[h]);
-        const int head = 16 * (HT * hg + h) + j;
-        const int64_t prow = ((int64_t)b * S + split) * a.H + head;
-        const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < V::MTW; ++mt)
-            *reinterpret_cast<float4*>(o_part + prow * kDv + V::CPW * w + 16 * mt + 4 * g) =
-                make_float4(o[h][mt][0] * f, o[h][mt][1] * f, o[h][mt][2] * f, o[h][mt][3] * f);
-        if (w == 0 && g == 0)
-            lse_part[prow] = (l > 0.0f) ? (m_ref[h] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
-                                        : -__builtin_inff();
-    }
-}
-
-// Wave-specialised split (8 waves, one head tile of 16, rows staged by LDS DMA):
-// waves 0 .. 3 compute the scores of chunk c + 1 (2 row tiles x 2 K halves)
-// while waves 4 .. 7 run the softmax and the PV product of chunk c (128 value
-// channels each), so the two halves of a chunk's work overlap and there is one
-// barrier per chunk. Before that barrier every wave waits for its own loads of
-// chunk c + 2, which the barrier then makes visible to all. Four chunk buffers:
-// c (PV), c + 1 (QK), c + 2 (landed), c + 3 (in flight).
-// With SMQK (E4M3 rows) the softmax moves to the QK waves and runs once per
-// chunk instead of once in every PV wave: in step c the QK waves score chunk
-// c + 1 and turn chunk c's scores into P (wave q: heads 4q .. 4q + 3, two rows
-// per lane, the lazy reference per head), writing P and the reference's factor
-// to LDS, while the PV waves rescale and accumulate chunk c - 1; five chunk
-// buffers (c - 1 for PV, c idle, c + 1 .. c + 3), one barrier per step.
-// Every wave issues an eighth of each chunk's gathers (a wave stalls while the
-// CU's memory pipeline accepts its loads, so the stall is shared by all).
-template <int SRC, int DQK, bool SMQK>
-__device__ __forceinline__ void decode_split_ws(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
-                                                int groups, bool is_win, int64_t first, int n, float* o_part,
-                                                float* lse_part) {
-    using G = Stage<SRC, DQK>;
-    using V = Waves<4, 1>;                                  // score layout of the 4 QK waves
-    static_assert(G::kDirect, "rows staged by DMA");
-    constexpr int NB = SMQK ? 5 : 4;
-    static_assert(!SMQK || SRC == SRC_E4M3, "P in LDS: E4M3 rows");
-    constexpr int kHi = (G::kInstr + 7) / 8;              // loads per wave and chunk, waves w < kInstr % 8
-    constexpr int kLo = G::kInstr / 8;
-    constexpr int NROPE = (DQK - kDv) / 32;               // RoPE k-steps (0 or 2)
-    constexpr int NMAIN_W = 8;                            // main k-steps per QK wave
-    constexpr int NROPE_W = NROPE / 2;
-    constexpr int NQ = NMAIN_W + NROPE_W;
-    constexpr float kLazy = 8.0f;                         // P <= 2^8 before the reference max moves
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool qk_role = w < 4;
-    const int q = w & 3;                                    // the wave's index within its role
-    const int j = lane & 15, g = lane >> 4;
-    const int rt = q & 1, kh = q >> 1;                      // QK row tile, K half
-    const int nc = (n + kChunk - 1) / kChunk;
-    int32_t* ridx = reinterpret_cast<int32_t*>(smem + kLdsIdx);
-    float* zs = reinterpret_cast<float*>(smem + kLdsZ);
-    uint8_t* bufs = smem + V::kBuf;
-    constexpr float kLog2e = 1.4426950408889634f;
-    const float zscale = a.scale * kLog2e;
-
-    // ---- QK waves: queries of their K half; k-step t covers channels 32 t .. 32 t + 31
-    u32x4 qv[NQ];
-    if (qk_role) {
-        const int head = 16 * hg + j;
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + head) * DQK + 8 * g;
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
-            qv[i] = *reinterpret_cast<const u32x4*>(qp + 32 * t);
-        }
-    }
-    // ---- row indices of the split (-1: no row)
-    if (tid < kMaxRps) {
-        int32_t r = -1;
-        if (tid < n) {
-            if (is_win) r = (int32_t)(first + tid);
-            else {
-                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
-                if (s >= 0 && s < a.capacity) r = s;
-            }
-        }
-        ridx[tid] = r;
-    }
-    __syncthreads();
-
-    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
-                                     : a.cache + b * a.stride;
-    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;   // at most 2 KiB
-    const uint32_t buf_m0 = __builtin_amdgcn_readfirstlane(lds_addr(bufs));
-    // every wave gathers its share of each chunk: slot (i) = 64 (w + 8 i) + lane, the same in every chunk
-    // (a wave stalls while the CU's memory pipeline takes its loads; shared, the stall is spread)
-    int slot_row[kHi];
-    uint32_t slot_off[kHi];
-    bool slot_data[kHi];
-#pragma unroll
-    for (int i = 0; i < kHi; ++i) {
-        const int s = 64 * (w + 8 * i) + lane;
-        const int u = s / G::kPieces, p = s - u * G::kPieces;
-        slot_row[i] = u < kChunk ? u : kChunk;
-        slot_off[i] = 16u * (uint32_t)p;
-        slot_data[i] = u < kChunk && p < G::kDataPieces;
-    }
-    // issue chunk c into buffer `into` (by default its own, c % NB); returns the slots whose row has no bytes
-    auto issue = [&](int c, int into = -1) -> uint32_t {
-        uint32_t zm = 0;
-        const uint32_t m0 = buf_m0 + (uint32_t)(((into < 0 ? c : into) % NB) * G::kBytes);
-        int32_t rr[kHi];
-#pragma unroll
-        for (int i = 0; i < kHi; ++i) rr[i] = ridx[kChunk * c + (slot_row[i] & (kChunk - 1))];
-        const void* src[kHi];
-#pragma unroll
-        for (int i = 0; i < kHi; ++i) {
-            const bool row_ok = slot_row[i] < kChunk && rr[i] >= 0;
-            zm |= (slot_row[i] < kChunk && rr[i] < 0) ? (1u << i) : 0u;
-            const uint64_t row = reinterpret_cast<uint64_t>(row_base + slot_off[i]) +
-                                 (uint64_t)(uint32_t)(rr[i] < 0 ? 0 : rr[i]) * row_bytes;
-            const bool use = row_ok && slot_data[i];
-            src[i] = reinterpret_cast<const void*>(use ? row : reinterpret_cast<uint64_t>(a.q));
-        }
-#pragma unroll
-        for (int i = 0; i < kHi; ++i)
-            if (w + 8 * i < G::kInstr) dma16(src[i], m0 + 1024u * (uint32_t)(w + 8 * i));
-        return zm;
-    };
-    // wait for chunk c (the `later` chunks issued after it, 0 .. 2, may stay in flight)
-    // and zero its slots without row bytes (their P is 0; stand-in bytes could decode to NaN)
-    auto land = [&](int c, int later, uint32_t zm) {
-        const bool hi = w < (G::kInstr & 7) || (G::kInstr & 7) == 0;
-        if (later >= 2) {
-            if (hi) wait_vmcnt<2 * kHi>();
-            else wait_vmcnt<2 * kLo>();
-        } else if (later == 1) {
-            if (hi) wait_vmcnt<kHi>();
-            else wait_vmcnt<kLo>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        if (__builtin_amdgcn_ballot_w64(zm != 0u)) {
-            uint8_t* buf = bufs + (c % NB) * G::kBytes;
-#pragma unroll
-            for (int i = 0; i < kHi; ++i)
-                if (zm & (1u << i))
-                    *reinterpret_cast<u32x4*>(buf + 16 * (64 * (w + 8 * i) + lane)) = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    // scores of chunk c (rows 16 rt .. +15, the wave's K half) into parity c & 1
-    auto qk = [&](int c) {
-        const uint8_t* buf = bufs + (c % NB) * G::kBytes;
-        const uint8_t* krow = buf + (16 * rt + j) * G::kStride;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-            for (int bb = 0; bb < NMAIN_W / 4; ++bb) {
-                const int blk = (NMAIN_W / 4) * kh + bb;
-                f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) {
-                    const int t = 4 * blk + s4;
-                    const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * t + 8 * g);
-                    t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[4 * bb + s4], t4);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[r] += t4[r] * *reinterpret_cast<const float*>(buf + (16 * rt + 4 * g + r) * G::kStride +
-                                                                    512 + 4 * blk);
-            }
-#pragma unroll
-            for (int i = 0; i < NROPE_W; ++i) {
-                const int t = NROPE_W * kh + i;
-                acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 528 + 2 * (32 * t + 8 * g)), qv[NMAIN_W + i],
-                                acc);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int t = (i < NMAIN_W) ? (NMAIN_W * kh + i) : (16 + NROPE_W * kh + (i - NMAIN_W));
-                acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * t + 8 * g)), qv[i], acc);
-            }
-        }
-        float* zd = zs + (((c & 1) * 2 + kh) * 16 + j) * kZs + 16 * rt + 4 * g;
-        *reinterpret_cast<f32x4*>(zd) = acc;
-    };
-
-    // ---- SMQK: P [2 parities][16 heads][kZs], the reference's factor [2][16], final l, m [2][16]
-    float* pbuf = reinterpret_cast<float*>(bufs + NB * G::kBytes);
-    float* abuf = pbuf + 2 * 16 * kZs;
-    float* lmbuf = abuf + 2 * 16;
-    float m_q = -__builtin_inff(), l_q = 0.0f;              // QK lane's head 4q + lane / 16
-    auto softmax_qk = [&](int c) {
-        const int hh = 4 * q + (lane >> 4), r0 = 2 * (lane & 15);
-        const f32x2 za = *reinterpret_cast<const f32x2*>(zs + (((c & 1) * 2) * 16 + hh) * kZs + r0);
-        const f32x2 zb = *reinterpret_cast<const f32x2*>(zs + (((c & 1) * 2 + 1) * 16 + hh) * kZs + r0);
-        const u32x2 iv = *reinterpret_cast<const u32x2*>(ridx + kChunk * c + r0);
-        const float z0 = ((int32_t)iv.x >= 0) ? (za.x + zb.x) * zscale : -__builtin_inff();
-        const float z1 = ((int32_t)iv.y >= 0) ? (za.y + zb.y) * zscale : -__builtin_inff();
-        const float cm = row16_max(fmaxf(z0, z1));        // the head's 16 lanes
-        // the reference moves only when the chunk exceeds it by more than 2^kLazy (and on
-        // the first chunk with a visible row, where the factor is exp2(-inf) = 0 on empty state)
-        const bool up = cm > m_q + kLazy;
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_q - cm) : 1.0f;
-        m_q = up ? cm : m_q;
-        const float p0 = (z0 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z0 - m_q);
-        const float p1 = (z1 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z1 - m_q);
-        l_q = l_q * alpha + (p0 + p1);
-        *reinterpret_cast<f32x2*>(pbuf + ((c & 1) * 16 + hh) * kZs + r0) = f32x2{p0, p1};
-        if ((lane & 15) == 0) abuf[(c & 1) * 16 + hh] = alpha;
-    };
-
-    // ---- PV waves' running state: reference max (base 2, lazily raised), partial sums, output tile
-    f32x4 o[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -__builtin_inff(), l_run = 0.0f;
-    auto pv = [&](int c) {
-        const uint8_t* buf = bufs + (c % NB) * G::kBytes;
-        u32x4 pa, pb;                                       // PV B operands: P (times the E4M3 scale), bf16 hi + lo
-        if constexpr (SMQK) {
-            float sc[8];                                    // the rows' scale of block q
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 + 4 * q);
-            const float alpha = abuf[(c & 1) * 16 + j];
-            const float* pr = pbuf + ((c & 1) * 16 + j) * kZs + 8 * g;
-            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int mt = 0; mt < 8; ++mt) o[mt] = o[mt] * alpha;
-            }
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p[e] = p0[e] * sc[e];
-                p[4 + e] = p1[e] * sc[4 + e];
-            }
-            split_bf16x8(p, pa, pb);
-        } else {
-        // softmax on the chunk; lane (j, g) holds rows 8 g .. 8 g + 7 of head j
-        bool vld[8];
-        {
-            const int32_t* rp = ridx + kChunk * c + 8 * g;
-            const u32x4 r0 = *reinterpret_cast<const u32x4*>(rp), r1 = *reinterpret_cast<const u32x4*>(rp + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vld[e] = (int32_t)r0[e] >= 0;
-                vld[4 + e] = (int32_t)r1[e] >= 0;
-            }
-        }
-        float sc[8];                                        // E4M3: the rows' scale of block q
-        if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                sc[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * G::kStride + 512 + 4 * q);
-        }
-        float z[8];
-        {
-            const float* zr = zs + (((c & 1) * 2) * 16 + j) * kZs + 8 * g;
-            const float* zr2 = zr + 16 * kZs;
-            const f32x4 a0 = *reinterpret_cast<const f32x4*>(zr), a1 = *reinterpret_cast<const f32x4*>(zr + 4);
-            const f32x4 b0 = *reinterpret_cast<const f32x4*>(zr2), b1 = *reinterpret_cast<const f32x4*>(zr2 + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                z[e] = a0[e] + b0[e];
-                z[4 + e] = a1[e] + b1[e];
-            }
-        }
-        float cm = -__builtin_inff();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            z[e] = vld[e] ? z[e] * zscale : -__builtin_inff();
-            cm = fmaxf(cm, z[e]);
-        }
-        cm = xmax4(cm);
-        // the reference moves only when the chunk exceeds it by more than 2^kLazy (and on
-        // the first chunk with a visible row, where the factor is exp2(-inf) = 0 on empty state)
-        const bool up = cm > m_ref + kLazy;
-        const float alpha = up ? __builtin_amdgcn_exp2f(m_ref - cm) : 1.0f;
-        m_ref = up ? cm : m_ref;
-        if (__builtin_amdgcn_ballot_w64(up)) {
-            l_run *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) o[mt] = o[mt] * alpha;
-        }
-        {
-            float ls = 0.0f;
-            float p[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                p[e] = (z[e] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[e] - m_ref);
-                ls += p[e];
-                if constexpr (SRC == SRC_E4M3) p[e] *= sc[e];
-            }
-            l_run += ls;
-            split_bf16x8(p, pa, pb);
-        }
-        }
-        // O^T[c][h] += V^T[c][rows] P^T[rows][h] over channels 128 q .. +127
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int c0 = 128 * q + 16 * mt;
-            u32x4 av;
-            if constexpr (SRC == SRC_E4M3) {
-                av = e4m3x8_to_bf16(ds_tr8(buf + (8 * g + (j >> 1)) * G::kStride + c0 + 8 * (j & 1)));
-            } else {
-                const uint8_t* vp = buf + (8 * g + (j >> 2)) * G::kStride + 2 * (c0 + 4 * (j & 3));
-                const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * G::kStride);
-                av = u32x4{r0.x, r0.y, r1.x, r1.y};
-            }
-            o[mt] = mfma_bf16(av, pa, o[mt]);
-            o[mt] = mfma_bf16(av, pb, o[mt]);
-        }
-    };
-
-    // ---- L2 warm-up: the head groups of a split run on one XCD and gather the same rows, so
-    // each pulls its share of the chunks past the first three (chunk c goes to head group
-    // c mod groups) from HBM at once; the chunk loads that follow then find those rows in the
-    // XCD's L2. The bytes land in buffer NB - 1, which no chunk uses before the prologue's
-    // waits (issued before chunk 0, these loads are counted first).
-    auto prefetch = [&]() {
-        for (int c = 3 + ((hg - 3) % groups + groups) % groups; c < nc; c += groups) (void)issue(c, NB - 1);
-    };
-    // ---- prologue: chunks 0 .. 2 in flight, chunk 0 landed and scored, chunk 1 landed
-    uint32_t zm1 = 0, zm2 = 0;                              // zero masks of chunks c + 2, c + 3
-    {
-        prefetch();
-        uint32_t z0 = 0, z1 = 0;
-        if (nc > 0) z0 = issue(0);
-        if (nc > 1) z1 = issue(1);
-        if (nc > 2) zm1 = issue(2);
-        if (nc > 0) land(0, min(2, nc - 1), z0);
-        __syncthreads();
-        if (qk_role && nc > 0) qk(0);
-        if (nc > 1) land(1, nc > 2 ? 1 : 0, z1);
-        __syncthreads();
-    }
-
-    // each role in a loop of its own, one barrier per chunk in both (the output tile
-    // then lives in the PV loop alone; a shared loop made the compiler copy it per chunk);
-    // in step c every wave issues its share of chunk c + 3 (into the buffer chunk c - NB + 3
-    // left, consumed before the previous barrier) and waits for its share of chunk c + 2
-    if constexpr (SMQK) {                                  // step c: scores c + 1, P of c, PV of c - 1
-        if (qk_role) {
-            for (int c = 0; c <= nc; ++c) {
-                if (c + 3 < nc) zm2 = issue(c + 3);
-                if (c + 1 < nc) qk(c + 1);
-                if (c < nc) softmax_qk(c);
-                if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
-                zm1 = zm2;
-                zm2 = 0;
-                __syncthreads();
-            }
-            const float l = row16_sum(l_q);                // the head's sum over its 16 lanes
-            if ((lane & 15) == 0) {
-                lmbuf[4 * q + (lane >> 4)] = l;
-                lmbuf[16 + 4 * q + (lane >> 4)] = m_q;
-            }
-        } else {
-            for (int c = 0; c <= nc; ++c) {
-                if (c + 3 < nc) zm2 = issue(c + 3);
-                if (c >= 1) pv(c - 1);
-                if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
-                zm1 = zm2;
-                zm2 = 0;
-                __syncthreads();
-            }
-        }
-        __syncthreads();                                   // l and the reference of every head
-    } else if (qk_role) {                                  // step c: scores c + 1 (QK), PV of c
-        for (int c = 0; c < nc; ++c) {
-            if (c + 3 < nc) zm2 = issue(c + 3);
-            if (c + 1 < nc) qk(c + 1);
-            if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
-            zm1 = zm2;
-            zm2 = 0;
-            __syncthreads();
-        }
-    } else {
-        for (int c = 0; c < nc; ++c) {
-            if (c + 3 < nc) zm2 = issue(c + 3);
-            pv(c);
-            if (c + 2 < nc) land(c + 2, c + 3 < nc ? 1 : 0, zm1);
-            zm1 = zm2;
-            zm2 = 0;
-            __syncthreads();
-        }
-    }
-
-    // ---- partial: normalised output (channels 128 q ..) and logsumexp of the split
-    if (!qk_role) {
-        const float l = SMQK ? lmbuf[j] : xsum4(l_run);
-        const float mref = SMQK ? lmbuf[16 + j] : m_ref;
-        const int head = 16 * hg + j;
-        const int64_t prow = ((int64_t)b * S + split) * a.H + head;
-        const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * q + 16 * mt + 4 * g) =
-                make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
-        if (q == 0 && g == 0)
-            lse_part[prow] = (l > 0.0f) ? (mref + __builtin_amdgcn_logf(l)) * 0.6931471805599453f
-                                        : -__builtin_inff();
-    }
 }
 
 // ------------------------------------------------------------------------
@@ -1309,42 +433,6 @@ __global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int 
     }
 }
 
-// Work item order: consecutive items are the head groups of one split; items
-// [x * per, (x + 1) * per) run on XCD x (workgroups go to XCDs round-robin).
-template <int SRC_MAIN, int DQK, int NW, int HT>
-__global__ __launch_bounds__(64 * NW) void k_decode_mfma(DecodeArgs a, int S_main, int S_win, int rps, int groups,
-                                                         int n_items, float* o_part, float* lse_part) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int L = blockIdx.x;
-    const int per = gridDim.x >> 3;
-    const int item = (L & 7) * per + (L >> 3);
-    if (item >= n_items) return;
-    const int S = S_main + S_win;
-    const int hg = item % groups;
-    const int rest = item / groups;
-    const int split = rest % S;
-    const int b = rest / S;
-    if (split < S_main) {
-        const int64_t first = (int64_t)split * rps;
-        const int n = (int)((a.k - first < rps) ? a.k - first : rps);
-        if constexpr (NW == 8)
-            decode_split_ws<SRC_MAIN, DQK, SRC_MAIN == SRC_E4M3>(a, smem, b, split, S, hg, groups, false, first, n,
-                                                                  o_part, lse_part);
-        else
-            decode_split<SRC_MAIN, DQK, NW, HT>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
-    } else {
-        const int64_t first = (int64_t)(split - S_main) * rps;
-        const int wl = (int)clamp_visible(a.win_len[b], a.W);
-        int n = (int)(wl - first);
-        n = n < 0 ? 0 : (n > rps ? rps : n);
-        if constexpr (NW == 8)
-            decode_split_ws<SRC_BF16, DQK, false>(a, smem, b, split, S, hg, groups, true, first, n, o_part,
-                                                  lse_part);
-        else
-            decode_split<SRC_BF16, DQK, NW, HT>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
-    }
-}
-
 // Combine the splits of one (b, h) by their logsumexp; thread t owns channels 4t .. 4t+3.
 // Up to kMergeFast splits, every load (logsumexps and partials) is issued at
 // once, from clamped in-bounds addresses, so the block pays one memory round trip.
@@ -1604,6 +692,10 @@ bool decode_supported(int fmt, int dim, int rope, int d_v, int H) {
     return dim + rope <= 1024 && d_v <= dim + rope && d_v > 0;
 }
 
+struct Geometry {
+    int groups, rps, rps_win, S_main, S_win;
+};
+
 // Splits of the gather-all decode: R = 256 rows for E4M3 rows, 128 otherwise (and for
 // the window), halved (down to 32) while the chip is short of a workgroup per CU, the
 // halved splits still fit one round of workgroups (one per CU: the LDS holds one) and
@@ -1611,8 +703,6 @@ bool decode_supported(int fmt, int dim, int rope, int d_v, int H) {
 // the option decode_rows_per_split (32 .. R, a multiple of 32) overrides the main rows' R.
 Geometry gather_geometry(int fmt, int B, int H, int k, int W) {
     Geometry g{};
-    g.ht = 1;
-    g.nw = 8;
     g.groups = H / 16;
     const int R = fmt == MLA_FMT_E4M3_S128 ? 256 : 128;
     int rps = R, rpw = 128;
@@ -1644,36 +734,6 @@ size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H,
     const size_t o = (size_t)B * S * H * kDv * sizeof(float);
     const size_t l = (size_t)B * S * H * sizeof(float);
     return ((o + 255) & ~(size_t)255) + ((l + 255) & ~(size_t)255);
-}
-
-template <int SRC_MAIN, int DQK, int NW, int HT>
-static hipError_t launch_mfma(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
-                              hipStream_t stream) {
-    const int S = g.S_main + g.S_win;
-    const int n_items = a.B * S * g.groups;
-    const int grid = (n_items + 7) / 8 * 8;
-    const int lds = decode_lds_bytes<SRC_MAIN, DQK, NW, HT>(g.S_win > 0);
-    auto kern = k_decode_mfma<SRC_MAIN, DQK, NW, HT>;
-    static bool attr_set = false;                          // dynamic LDS above 64 KiB, once per kernel
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 decode_lds_bytes<SRC_MAIN, DQK, NW, HT>(true));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const ProfSlot p = prof_slot(PROF_DECODE);
-    return launch_kernel(kern, dim3(grid), dim3(64 * NW), lds, stream, p.start, p.stop, a, g.S_main, g.S_win,
-                         g.rps, g.groups, n_items, o_part, lse_part);
-}
-
-template <int SRC_MAIN, int DQK>
-static hipError_t launch_layout(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
-                                hipStream_t stream) {
-    if (g.ht == 2) return launch_mfma<SRC_MAIN, DQK, 4, 2>(a, g, o_part, lse_part, stream);
-    if constexpr (SRC_MAIN != SRC_FP4)                     // rows staged by DMA: wave-specialised
-        if (g.nw == 8) return launch_mfma<SRC_MAIN, DQK, 8, 1>(a, g, o_part, lse_part, stream);
-    return launch_mfma<SRC_MAIN, DQK, 4, 1>(a, g, o_part, lse_part, stream);
 }
 
 template <int SRC_MAIN, int DQK>

@@ -164,7 +164,7 @@ hipError_t prof_read(int k, int32_t* launches, double* total_ms);
 // Kernel-choice options (options.cpp; mla_set_option): 0 = the library's own choice.
 enum Opt {
     OPT_TOPK_PATH, OPT_TOPK_FINAL, OPT_SCAN_QUEUES, OPT_SCAN_BLOCKS,
-    OPT_DECODE_RPS, OPT_DECODE_HEADS, OPT_DECODE_WAVES, OPT_COUNT
+    OPT_DECODE_RPS, OPT_COUNT
 };
 int64_t option(Opt o);
 int option_index(const char* name);     // -1 for an unknown name

@@ -28,9 +28,8 @@ const OptDef kOpts[OPT_COUNT] = {
     {"topk_final", 0, 1},         // 0 by workgroup count, 1 the 256-thread final of the many-workgroup path
     {"scan_queues", 0, 1},        // 1: the queue-fed 32x32 scan instead of the static partition
     {"scan_blocks", 0, 65536},    // target number of 4-wave scan workgroups (0: two per CU)
-    {"decode_rows_per_split", 0, 256},   // selected rows per decode split (0: by shape; else 32 .. 256, multiple of 32)
-    {"decode_heads_per_group", 0, 32},   // heads per decode workgroup (0: by shape; 16 or 32)
-    {"decode_waves", 0, 8},       // waves per decode workgroup (0: by shape; 4 or 8)
+    {"decode_rows_per_split", 0, 256},   // selected rows per decode split (0: by shape; else 32 .. 256 (128 for
+                                         // rows other than E4M3), a multiple of 32)
 };
 std::atomic<int64_t> g_opt[OPT_COUNT];
 

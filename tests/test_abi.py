@@ -190,7 +190,7 @@ def test_options_set_get_and_validation(M):
     """Kernel-choice options: declared names round-trip, unknown names and values
     out of range are rejected on the host, and 0 restores the default."""
     for name, v in (("topk_path", 2), ("topk_final", 1), ("scan_queues", 1), ("scan_blocks", 300),
-                    ("decode_rows_per_split", 128), ("decode_heads_per_group", 32), ("decode_waves", 4)):
+                    ("decode_rows_per_split", 128)):
         assert M.mla_get_option(name) == 0
         with M.option(name, v):
             assert M.mla_get_option(name) == v

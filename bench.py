@@ -45,6 +45,8 @@ def parse():
                    help="window entries as bf16 or as MXFP8 (V4.1's 528-byte entry at 512 channels)")
     p.add_argument("--compress", type=int, default=0, metavar="M",
                    help="pool the step's main entry from M tokens with the CSA2 compressor (mla_compress_append)")
+    p.add_argument("--score-bf16", action="store_true",
+                   help="the bf16-score top-k: index scores rounded to bf16 before they are selected")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="replay each rotated layer's step from a HIP graph captured once (the stamped steps "
@@ -282,7 +284,7 @@ def main():
                                           X.main if own_main else None, X.idx, X.q_idx[j],
                                           X.w[j], cfg.sigma, nvis, k, latest, ws_topk,
                                           new_win=win[0], win_pos=win[1], win_ring=win[2],
-                                          out_scores=full_scores if pool else None)
+                                          out_scores=full_scores if pool else None, score_bf16=args.score_bf16)
                 if stamp:
                     M.mla_profile_enable(())
                 if pool:
@@ -295,7 +297,7 @@ def main():
                 if selects:
                     latest = idx_out[j % 2]
                     M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk,
-                                       cand=pool_pos if pool else None)
+                                       cand=pool_pos if pool else None, score_bf16=args.score_bf16)
                     j += 1
             M.mla_sparse_decode(mr, cfg.d_v, X.q[l], X.main, latest, cfg.softmax_scale, out, lse, ws_dec,
                                 X.win[l] if cfg.W else None, win_len if cfg.W else None)
@@ -424,7 +426,7 @@ def main():
         "config": {
             "workload": f"{cfg.name}: {cfg.desc}",
             "batch": B, "context_rows": N, "tokens": cfg.tokens, "heads": H, "qk_dim": cfg.D, "v_dim": cfg.d_v,
-            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "window": cfg.W, "window_format": args.win_fmt if cfg.W else None, "compress_m": args.compress or None, "layers_per_step": len(cfg.layers),
+            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "index_scores": "bf16" if args.score_bf16 else "fp32", "window": cfg.W, "window_format": args.win_fmt if cfg.W else None, "compress_m": args.compress or None, "layers_per_step": len(cfg.layers),
             "main_row_bytes": M.row_bytes(mr), "indexer_row_bytes": M.row_bytes(ir),
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
             "candidate_pool": (f"{pool} blocks of {POOL_BLOCK} published by the Full layer, scored by the "

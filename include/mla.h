@@ -309,6 +309,26 @@ mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float*
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_indexer_topk_bf16 -- the bf16-score top-k.
+ *
+ * mla_indexer_topk with every score rounded to bf16 (round to nearest even;
+ * -inf stays -inf) before it is stored, counted and selected: the selection
+ * is the k visible rows of largest bf16 score, ties -- now frequent: bf16 keeps
+ * 8 significant bits -- going to the smaller position ([P1] "DeepSeek-V4", "The
+ * indexer in four bits": index scores in bf16 instead of fp32). out_scores, if
+ * given, receives the rounded scores as fp32 values (each exactly a bf16 value).
+ * Same arguments, workspace and errors as mla_indexer_topk.
+ */
+mla_status_t mla_indexer_topk_bf16(mla_row_t idx_row, const void* q_idx, const float* w,
+                                   float score_scale,
+                                   const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                   const int32_t* n_visible,
+                                   const int32_t* cand, int32_t n_cand,
+                                   int32_t B, int32_t H_I, int32_t k,
+                                   int32_t* out_idx, float* out_scores,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_indexer_pool -- the candidate pool of the hierarchical sparse indexer.
  *
  * From one layer's indexer scores ([P4] "The Hierarchical Sparse Indexer:
@@ -374,6 +394,20 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row,
                                      const int32_t* n_visible, int32_t B, int32_t H_I, int32_t k,
                                      int32_t* out_idx, float* out_scores,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* mla_append_indexer_topk_bf16 -- mla_append_indexer_topk whose top-k is the bf16-score
+ * top-k of mla_indexer_topk_bf16 (same arguments and errors). */
+mla_status_t mla_append_indexer_topk_bf16(mla_row_t main_row, mla_row_t idx_row,
+                                          const float* new_main, const float* new_idx,
+                                          const int32_t* slots, int32_t n_new,
+                                          void* main_cache, int64_t main_seq_stride,
+                                          void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                          const float* new_win, const int32_t* win_pos,
+                                          void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt,
+                                          const void* q_idx, const float* w, float score_scale,
+                                          const int32_t* n_visible, int32_t B, int32_t H_I, int32_t k,
+                                          int32_t* out_idx, float* out_scores,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * mla_sparse_decode -- absorbed MLA as shared-KV MQA over the selected entries.

@@ -216,6 +216,20 @@ def topk(scores, n_visible, k, n_rows=None, cand=None):
     return out
 
 
+def bf16_scores(scores):
+    """Index scores as the bf16-score top-k keeps them ([P1] "DeepSeek-V4", "The indexer in
+    four bits": scores in bf16 instead of fp32): each fp32 score rounded to the nearest bf16
+    value, ties to even (-inf stays -inf), returned as fp32 values."""
+    s = _c(scores, np.float32)
+    return bf16_value(bf16_encode(s)).reshape(s.shape)
+
+
+def topk_bf16(scores, n_visible, k, cand=None):
+    """The bf16-score top-k: the selection of topk() over bf16_scores(scores) -- the k visible
+    rows of largest bf16 score, ties going to the smaller position."""
+    return topk(bf16_scores(scores), n_visible, k, cand=cand)
+
+
 def pool(scores, n_visible, n_blocks, block=8):
     """Candidate pool of the hierarchical sparse indexer: the block indices
     [B, n_blocks] of the n_blocks blocks (of `block` consecutive positions) with

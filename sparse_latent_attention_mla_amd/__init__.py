@@ -67,9 +67,12 @@ def lib():
         L.mla_indexer_topk.argtypes = [_CRow, P, P, f32, P, i64, i64, P, P, i32, i32, i32, i32,
                                        P, P, P, sz, P]
         L.mla_indexer_topk.restype = i32
+        L.mla_indexer_topk_bf16.argtypes, L.mla_indexer_topk_bf16.restype = L.mla_indexer_topk.argtypes, i32
         L.mla_append_indexer_topk.argtypes = [_CRow, _CRow, P, P, P, i32, P, i64, P, i64, i64, P, P, P,
                                               i32, i32, i32, P, P, f32, P, i32, i32, i32, P, P, P, sz, P]
         L.mla_append_indexer_topk.restype = i32
+        L.mla_append_indexer_topk_bf16.argtypes = L.mla_append_indexer_topk.argtypes
+        L.mla_append_indexer_topk_bf16.restype = i32
         L.mla_indexer_pool_workspace.argtypes, L.mla_indexer_pool_workspace.restype = [i32, i64, i32], sz
         L.mla_indexer_pool.argtypes = [P, i64, P, i32, i32, i32, P, P, sz, P]
         L.mla_indexer_pool.restype = i32
@@ -289,13 +292,14 @@ def mla_indexer_topk_workspace(B: int, capacity: int, k: int) -> int:
 
 
 def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_visible, k: int,
-                     out_idx, workspace, out_scores=None, stream=None, cand=None):
+                     out_idx, workspace, out_scores=None, stream=None, cand=None, score_bf16=False):
     """Indexer scan + mask + top-k.  q_idx [B, H_I, d_I] (bf16; fp32 for F32 rows), w fp32 [B, H_I],
     idx_cache uint8 [B, capacity, row_bytes], n_visible int32 [B], out_idx int32 [B, k],
     workspace uint8 of mla_indexer_topk_workspace bytes, zeroed before its first use (every
     successful call leaves it ready for the next), out_scores fp32 [B, capacity] (optional).
     cand: optional int32 [B, n_cand] candidate pool (positions); only those are scored, and
-    out_scores is then [B, n_cand]."""
+    out_scores is then [B, n_cand].  score_bf16: the bf16-score top-k (mla_indexer_topk_bf16: scores
+    rounded to bf16 before they are stored and selected)."""
     _need(q_idx, "q_idx", query_dtype(idx_row), 3)
     _need(w, "w", torch.float32, 2)
     _need(n_visible, "n_visible", torch.int32, 1)
@@ -321,7 +325,8 @@ def mla_indexer_topk(idx_row: Row, q_idx, w, score_scale: float, idx_cache, n_vi
     # an empty pool is still a pool: the C ABI takes it as a non-NULL cand with n_cand 0
     # (never read), so an empty tensor's null data pointer is replaced by out_idx's
     cand_p = None if cand is None else (_ptr(cand) if n_cand > 0 else _ptr(out_idx))
-    _check(lib().mla_indexer_topk(
+    fn = lib().mla_indexer_topk_bf16 if score_bf16 else lib().mla_indexer_topk
+    _check(fn(
         _crow(idx_row), _ptr(q_idx), _ptr(w), float(score_scale), _ptr(idx_cache), stride,
         idx_cache.shape[1], _ptr(n_visible), cand_p, n_cand, B, H_I, k, _ptr(out_idx), _ptr(out_scores),
         _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -349,7 +354,8 @@ def mla_indexer_pool(scores, n_visible, n_blocks: int, out_pos, workspace, block
 
 def mla_append_indexer_topk(main_row: Row, idx_row: Row, new_main, new_idx, slots, main_cache, idx_cache,
                             q_idx, w, score_scale: float, n_visible, k: int, out_idx, workspace,
-                            new_win=None, win_pos=None, win_ring=None, out_scores=None, stream=None):
+                            new_win=None, win_pos=None, win_ring=None, out_scores=None, stream=None,
+                            score_bf16=False):
     """mla_kv_append_quant then mla_indexer_topk in one call (the append rides in the
     scan's launch where the scan kernel can carry it).  Arguments as for those two;
     idx_cache is required, main_cache may be None."""
@@ -390,7 +396,8 @@ def mla_append_indexer_topk(main_row: Row, idx_row: Row, new_main, new_idx, slot
         _need(out_scores, "out_scores", torch.float32, 2)
         if tuple(out_scores.shape) != (B, cap):
             raise ValueError("out_scores must be [B, capacity]")
-    _check(lib().mla_append_indexer_topk(
+    fn = lib().mla_append_indexer_topk_bf16 if score_bf16 else lib().mla_append_indexer_topk
+    _check(fn(
         _crow(main_row), _crow(idx_row), _ptr(new_main), _ptr(new_idx), _ptr(slots), n_new,
         _ptr(main_cache), _cache_stride(main_cache, "main_cache"),
         _ptr(idx_cache), _cache_stride(idx_cache, "idx_cache"), cap,

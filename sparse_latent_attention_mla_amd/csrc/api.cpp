@@ -161,7 +161,8 @@ struct TopkCall {
 mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
                        const void* idx_cache, int64_t idx_seq_stride, int64_t capacity, const int32_t* n_visible,
                        const int32_t* cand, int32_t n_cand, int32_t B, int32_t H_I, int32_t k, int32_t* out_idx,
-                       float* out_scores, void* workspace, size_t workspace_bytes, TopkCall* out) {
+                       float* out_scores, void* workspace, size_t workspace_bytes, TopkCall* out,
+                       bool score_bf16 = false) {
     if (B < 0 || k < 0 || H_I < 1 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "indexer_topk: need B >= 0, k >= 0, H_I >= 1, capacity >= 0");
     if (n_cand < 0 || (!cand && n_cand != 0))
@@ -215,6 +216,7 @@ mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, flo
     a.queues = reinterpret_cast<uint32_t*>(ws + L.queues);
     a.cand = cand;
     a.n_cand = cand ? n_cand : 0;
+    a.score_bf16 = score_bf16 ? 1 : 0;
     out->out_idx = out_idx;
     return ok();
 }
@@ -403,17 +405,65 @@ size_t mla_indexer_topk_workspace(int32_t B, int64_t capacity, int32_t k) {
     return topk_layout(B, capacity).total;
 }
 
+static mla_status_t indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
+                                 const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                 const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
+                                 int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
+                                 size_t workspace_bytes, void* stream, bool score_bf16) {
+    mla::begin_call();
+    TopkCall c;
+    const mla_status_t s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
+                                     cand, n_cand, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c,
+                                     score_bf16);
+    if (s != MLA_OK || c.empty) return s;
+    return topk_launch(c, nullptr, static_cast<hipStream_t>(stream));
+}
+
 mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
                               const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
                               const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
                               int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
                               size_t workspace_bytes, void* stream) {
+    return indexer_topk(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, cand, n_cand,
+                        B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, stream, false);
+}
+
+mla_status_t mla_indexer_topk_bf16(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
+                                   const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                   const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
+                                   int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    return indexer_topk(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, cand, n_cand,
+                        B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, stream, true);
+}
+
+static mla_status_t append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
+                                        const float* new_idx, const int32_t* slots, int32_t n_new, void* main_cache,
+                                        int64_t main_seq_stride, void* idx_cache, int64_t idx_seq_stride,
+                                        int64_t capacity, const float* new_win, const int32_t* win_pos,
+                                        void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt, const void* q_idx,
+                                        const float* w, float score_scale, const int32_t* n_visible, int32_t B,
+                                        int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores,
+                                        void* workspace, size_t workspace_bytes, void* stream, bool score_bf16) {
     mla::begin_call();
+    if (!idx_cache) return fail(MLA_ERR_INVALID_ARG, "append_indexer_topk: idx_cache is NULL");
+    mla::AppendArgs ap{};
+    mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
+                                 main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W, Dw,
+                                 win_fmt, &ap);
+    if (s != MLA_OK) return s;
     TopkCall c;
-    const mla_status_t s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
-                                     cand, n_cand, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
-    if (s != MLA_OK || c.empty) return s;
-    return topk_launch(c, nullptr, static_cast<hipStream_t>(stream));
+    s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, nullptr, 0, B,
+                  H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c, score_bf16);
+    if (s != MLA_OK) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c.empty) return hip_status(mla::launch_append(ap, st), "append launch");
+    if (n_new == 0) {                                      // at most a window entry: nothing to carry
+        const mla_status_t sa = hip_status(mla::launch_append(ap, st), "append launch");
+        if (sa != MLA_OK) return sa;
+        return topk_launch(c, nullptr, st);
+    }
+    return topk_launch(c, &ap, st);
 }
 
 mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
@@ -425,25 +475,25 @@ mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, cons
                                      float score_scale, const int32_t* n_visible, int32_t B, int32_t H_I,
                                      int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-    mla::begin_call();
-    if (!idx_cache) return fail(MLA_ERR_INVALID_ARG, "append_indexer_topk: idx_cache is NULL");
-    mla::AppendArgs ap{};
-    mla_status_t s = append_args(main_row, idx_row, new_main, new_idx, slots, B, n_new, capacity, main_cache,
-                                 main_seq_stride, idx_cache, idx_seq_stride, new_win, win_pos, win_ring, W, Dw,
-                                 win_fmt, &ap);
-    if (s != MLA_OK) return s;
-    TopkCall c;
-    s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible, nullptr, 0, B,
-                  H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c);
-    if (s != MLA_OK) return s;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (c.empty) return hip_status(mla::launch_append(ap, st), "append launch");
-    if (n_new == 0) {                                      // at most a window entry: nothing to carry
-        const mla_status_t sa = hip_status(mla::launch_append(ap, st), "append launch");
-        if (sa != MLA_OK) return sa;
-        return topk_launch(c, nullptr, st);
-    }
-    return topk_launch(c, &ap, st);
+    return append_indexer_topk(main_row, idx_row, new_main, new_idx, slots, n_new, main_cache, main_seq_stride,
+                               idx_cache, idx_seq_stride, capacity, new_win, win_pos, win_ring, W, Dw, win_fmt, q_idx,
+                               w, score_scale, n_visible, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes,
+                               stream, false);
+}
+
+mla_status_t mla_append_indexer_topk_bf16(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
+                                          const float* new_idx, const int32_t* slots, int32_t n_new,
+                                          void* main_cache, int64_t main_seq_stride, void* idx_cache,
+                                          int64_t idx_seq_stride, int64_t capacity, const float* new_win,
+                                          const int32_t* win_pos, void* win_ring, int32_t W, int32_t Dw,
+                                          int32_t win_fmt, const void* q_idx, const float* w, float score_scale,
+                                          const int32_t* n_visible, int32_t B, int32_t H_I, int32_t k,
+                                          int32_t* out_idx, float* out_scores, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+    return append_indexer_topk(main_row, idx_row, new_main, new_idx, slots, n_new, main_cache, main_seq_stride,
+                               idx_cache, idx_seq_stride, capacity, new_win, win_pos, win_ring, W, Dw, win_fmt, q_idx,
+                               w, score_scale, n_visible, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes,
+                               stream, true);
 }
 
 size_t mla_indexer_pool_workspace(int32_t B, int64_t capacity, int32_t block) {

@@ -25,6 +25,12 @@ namespace mla {
 
 namespace {
 
+// A row's score as the selection sees it: the fp32 score, or (the bf16-score top-k,
+// [P1] "DeepSeek-V4", "The indexer in four bits") that score rounded to bf16, round to
+// nearest even; -inf stays -inf.
+__device__ __forceinline__ float sel_score(float s, int bf16) { return bf16 ? u2f(bf16_rne(s) << 16) : s; }
+
+
 constexpr int kScanThreads = 256;         // 4 waves
 constexpr int kTilesPerWave = 8;          // 16-row tiles per wave (direct-load path)
 constexpr int kRowsPerBlock = 4 * kTilesPerWave * 16;
@@ -232,8 +238,8 @@ __device__ __forceinline__ float tile_epilogue(const ScanCtx<MT>& C, const f32x4
 template <int MT>
 __device__ __forceinline__ void tile_scores(const ScanCtx<MT>& C, const u32x4 kb[4], float mult, int64_t s,
                                             bool valid, int g, float sigma, int64_t capacity, float* scores,
-                                            uint32_t* hist) {
-    const float part = tile_dot<MT>(C, kb, mult);
+                                            uint32_t* hist, int round16) {
+    const float part = sel_score(tile_dot<MT>(C, kb, mult), round16);
     if (g == 0 && s < capacity) {
         scores[s] = valid ? part : -__builtin_inff();
         if (valid) atomicAdd(&hist[score_key(part) >> (32 - kHistBits)], 1u);
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_staged(ScanArgs a, int ro
             u32x4 kb[4];
             dequant_key<FMT>(w, sw, kb);
             if (!valid) mult = 0.0f;
-            tile_scores<MT>(C, kb, mult, s, valid, g, a.sigma, a.capacity, scores, hist);
+            tile_scores<MT>(C, kb, mult, s, valid, g, a.sigma, a.capacity, scores, hist, a.score_bf16);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -542,7 +548,7 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
             for (int m = 0; m < MT; ++m) acc[m] = mfma_bf16(C.qa[m][t], cur.kb[t], acc[m]);
         const float mult = cur.mult;
         if (n + 1 < n_tiles) fetch((n + 1) >> 1, (n + 1) & 1, cur);
-        const float score = tile_epilogue<MT>(C, acc, mult);
+        const float score = sel_score(tile_epilogue<MT>(C, acc, mult), a.score_bf16);
         const int rr = tile * 16 + col;
         const int lrow = (4 * c + wave) * kDmaRows + rr;   // row within the block
         if (g == tile) {                                   // one lane group per tile writes
@@ -867,7 +873,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
         float part = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt) part += (pm[mt][0] + pm[mt][1]) + (pm[mt][2] + pm[mt][3]);
-        const float score = xsum2(part) * mult;
+        const float score = sel_score(xsum2(part) * mult, a.score_bf16);
         const int lrow = (NW * (tt / TPC) + wave) * CR + (tt % TPC) * 32 + n32;  // row within the block
         if (h == 0) {
             const bool valid = row0 + lrow < nvis;
@@ -1142,7 +1148,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
         float part = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < MT2; ++mt) part += (pm[mt][0] + pm[mt][1]) + (pm[mt][2] + pm[mt][3]);
-        const float score = xsum2(part) * mult;
+        const float score = sel_score(xsum2(part) * mult, a.score_bf16);
         if (h == 0 && row < cap) {                         // row 0 of the chunk is visible: one store
             const bool valid = row < nvis;
             scores[row] = valid ? score : -__builtin_inff();
@@ -1215,7 +1221,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) kb[t] = u32x4{0u, 0u, 0u, 0u};
         }
-        tile_scores<MT>(C, kb, valid ? 1.0f : 0.0f, s, valid, g, a.sigma, a.capacity, scores, hist);
+        tile_scores<MT>(C, kb, valid ? 1.0f : 0.0f, s, valid, g, a.sigma, a.capacity, scores, hist,
+                        a.score_bf16);
     }
     __syncthreads();
     flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
@@ -1310,7 +1317,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_cand(ScanArgs a) {
             dequant_key<FMT>(w[t], sw[t], kb);
             if constexpr (FMT == MLA_FMT_E4M3_S128) mult = valid[t] ? __builtin_bit_cast(float, sw[t]) : 0.0f;
         }
-        const float part = tile_dot<MT>(C, kb, mult);
+        const float part = sel_score(tile_dot<MT>(C, kb, mult), a.score_bf16);
         if (g == 0 && ent[t] < n) {
             const float sc = valid[t] ? part : -__builtin_inff();
             scores[ent[t]] = sc;
@@ -1389,6 +1396,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_generic(ScanArgs a) {
                 score += a.w[(int64_t)b * a.H_I + j] * fmaxf(a.sigma * d, 0.0f);
             }
         }
+        score = sel_score(score, a.score_bf16);
         if (a.cand || pos < nvis) atomicAdd(&hist[score_key(score) >> (32 - kHistBits)], 1u);
         a.scores[b * n_out + s] = score;
     }

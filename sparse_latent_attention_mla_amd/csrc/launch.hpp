@@ -95,6 +95,8 @@ struct ScanArgs {
     const int32_t* cand;    // [B, n_cand] positions of a candidate pool, or null: every row
     int64_t n_cand;         // pool entries per sequence; with a pool the scores are [B, n_cand] and
                             // the histogram counts every entry (those not visible as -inf)
+    int score_bf16;         // 1: scores rounded to bf16 (round to nearest even) before they are
+                            // stored, counted and selected (the bf16-score top-k)
 };
 // Entries of a step's append that the indexer scan can carry in the same launch.
 constexpr int kFuseMaxNew = 4;

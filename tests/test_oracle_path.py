@@ -452,3 +452,26 @@ def test_output_rope_undoes_the_rotation_at_the_query_position():
         outs.append(O.attention((O.F32, D, 0), D, qz, O.quant_rows(O.F32, D, 0, xr.astype(np.float32)), idx, 0.1,
                                 rope_cs=cst)[0])
     np.testing.assert_allclose(outs[0], outs[1], rtol=1e-4, atol=1e-5)
+
+
+def test_bf16_score_topk_matches_the_library_cast_and_lexsort():
+    """The bf16-score top-k is the fp32 scores rounded by the library bf16 cast (round to
+    nearest even) and ordered by (score desc, position asc): checked on scores full of
+    bf16 ties, with masking and k above the visible count."""
+    import torch
+    rng = np.random.default_rng(21)
+    B, N = 3, 5000
+    s = (rng.standard_normal((B, N)) * 3).astype(np.float32)
+    s[:, ::7] = np.float32(1.0) + np.float32(2.0 ** -9) * rng.integers(0, 3, (B, (N + 6) // 7))  # bf16 midpoints/ties
+    nv = np.array([N, 4321, 17], np.int32)
+    ref16 = torch.from_numpy(s).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.bf16_scores(s), ref16)
+    for k in (1, 64, 2048, 4400):
+        got = O.topk_bf16(s, nv, k)
+        for b in range(B):
+            n = int(nv[b])
+            order = np.lexsort((np.arange(n), -ref16[b, :n].astype(np.float64)))[:min(k, n)]
+            assert np.array_equal(np.sort(got[b][got[b] >= 0]), np.sort(order))
+            assert np.sum(got[b] < 0) == k - min(k, n)
+    # the rounding creates ties that the fp32 order would break: the two selections differ
+    assert not np.array_equal(np.sort(O.topk_bf16(s, nv, 64), 1), np.sort(O.topk(s, nv, 64), 1))

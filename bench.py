@@ -45,6 +45,10 @@ def parse():
                    help="window entries as bf16 or as MXFP8 (V4.1's 528-byte entry at 512 channels)")
     p.add_argument("--compress", type=int, default=0, metavar="M",
                    help="pool the step's main entry from M tokens with the CSA2 compressor (mla_compress_append)")
+    p.add_argument("--queries", type=int, default=0, metavar="G",
+                   help="G positions of one sequence per step (a prefill chunk / multi-token prediction): "
+                        "the step appends G entries, then one indexer call and one decode call serve the G "
+                        "queries over the shared cache (each with its own causal limit)")
     p.add_argument("--score-bf16", action="store_true",
                    help="the bf16-score top-k: index scores rounded to bf16 before they are selected")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -213,6 +217,8 @@ def main():
     import workloads as WL
 
     cfg = WL.CONFIGS[args.config]
+    if args.queries:
+        return multi_query(args, cfg)
     dev = "cuda"
     torch.cuda.set_device(0)
     B, N, H = cfg.B, cfg.N, cfg.H
@@ -453,6 +459,92 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(result), flush=True)
+
+
+def multi_query(args, cfg):
+    """G positions of one sequence per step: append the G entries, score and select for
+    the G queries in one mla_indexer_topk call over the shared cache (stride 0; query i
+    sees rows < N - G + 1 + i), then one mla_sparse_decode call for the G queries."""
+    import numpy as np
+    import torch
+
+    import sparse_latent_attention_mla_amd as M
+    import workloads as WL
+
+    G = args.queries
+    if cfg.W or len(cfg.layers) > 1:
+        raise SystemExit("--queries: single-layer configurations without a window (c2, c3, c4x)")
+    cfg1 = cfg.with_(B=1)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    n_layers = max(1, args.layers)
+    log(f"multi-query {cfg.name}: one sequence of {cfg.N} rows, {G} queries per step; {n_layers} layer caches")
+    layers = build_layers(cfg1, n_layers)
+    N, H, k = cfg.N, cfg.H, cfg.k
+    mr = M.Row(cfg.main_fmt, cfg.dim, cfg.rope)
+    ir = M.Row(cfg.idx_fmt, cfg.d_I, 0)
+    qdt = torch.float32 if cfg.main_fmt == WL.F32 else torch.bfloat16
+    for l, X in enumerate(layers):                       # G queries, G new entries
+        off = 16 * l
+        X.qg = torch.from_numpy(WL.normal(0, cfg.cid, 300 + off, (G, H, cfg.D))).to(dev).to(qdt)
+        X.qig = torch.from_numpy(WL.normal(0, cfg.cid, 301 + off, (G, cfg.H_I, cfg.d_I))).to(dev).to(qdt)
+        X.wg = torch.from_numpy(WL.normal(0, cfg.cid, 302 + off, (G, cfg.H_I)) * np.float32(cfg.w_scale)).to(dev)
+        X.newg = torch.from_numpy(WL.normal(0, cfg.cid, 303 + off, (1, G, cfg.D))).to(dev)
+        X.newig = torch.from_numpy(WL.normal(0, cfg.cid, 304 + off, (1, G, cfg.d_I))).to(dev)
+    slots = torch.arange(N - G, N, dtype=torch.int32, device=dev)[None].contiguous()
+    nvis = torch.arange(N - G + 1, N + 1, dtype=torch.int32, device=dev)
+    idx = torch.empty((G, k), dtype=torch.int32, device=dev)
+    out = torch.empty((G, H, cfg.d_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((G, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(M.mla_indexer_topk_workspace(G, N, k), dtype=torch.uint8, device=dev)
+    wsd = torch.empty(max(1, M.mla_sparse_decode_workspace(mr, cfg.d_v, G, H, k, 0)), dtype=torch.uint8,
+                      device=dev)
+
+    def step(X):
+        M.mla_kv_append_quant(mr, ir, X.newg, X.newig, slots, X.main, X.idx)
+        M.mla_indexer_topk(ir, X.qig, X.wg, cfg.sigma, X.idx.expand(G, -1, -1), nvis, k, idx, ws,
+                           score_bf16=args.score_bf16)
+        M.mla_sparse_decode(mr, cfg.d_v, X.qg, X.main.expand(G, -1, -1), idx, cfg.softmax_scale, out, lse, wsd)
+
+    for i in range(args.warmup):
+        step(layers[i % n_layers])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(layers[i % n_layers])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    M.mla_profile_enable(M.PROFILE_KERNELS)
+    for i in range(min(args.steps, 50)):
+        step(layers[i % n_layers])
+    torch.cuda.synchronize()
+    M.mla_profile_enable(())
+    per_kernel = {}
+    for name in M.PROFILE_KERNELS:
+        n, tot = M.mla_profile_read(name)
+        if n:
+            per_kernel[name] = {"launches": n, "avg_us": tot * 1e3 / n}
+    key_bytes = N * M.row_bytes(ir)
+    scan_us = per_kernel.get("indexer_scan", {}).get("avg_us")
+    log(f"{ms * 1e3:.2f} us/step for {G} queries; breakdown (avg us): " +
+        ", ".join(f"{kk}={v['avg_us']:.2f}" for kk, v in per_kernel.items()))
+    result = {
+        "metric": METRIC + " (several queries of one sequence per step)",
+        "value": 1e3 / ms, "unit": f"steps/s ({G} queries each)", "queries_per_s": G * 1e3 / ms,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} with one sequence and {G} queries per step (stride-0 shared cache)",
+                   "queries": G, "context_rows": N, "heads": H, "top_k": k, "rotated_layer_caches": n_layers,
+                   "index_scores": "bf16" if args.score_bf16 else "fp32"},
+        "scan": {"key_bytes_per_launch": key_bytes, "avg_launch_us": scan_us,
+                 "key_gbps_once": key_bytes / (scan_us * 1e-6) / 1e9 if scan_us else None},
+        "per_kernel_breakdown": per_kernel,
+    }
     print(json.dumps(result), flush=True)
 
 

@@ -603,8 +603,22 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
 // the queries, quantises it (quant128_wave, byte for byte quant_row's) and
 // writes the bytes over the chunk's row in LDS before it dequantises the chunk,
 // so the row is scored from the bytes the append writes, whatever the load saw.
+// Several queries of one sequence (a shared cache, stride 0: the batch rows are the
+// queries): the grid is padded to a multiple of 8 row ranges, and the block index is
+// read so that, on each XCD, the G blocks of one row range (one per query) go out
+// one after another: they run together and read the range's keys from HBM once,
+// the others finding them in that XCD's L2. Blocks past the last range do nothing.
+__device__ __forceinline__ bool shared_cache_block(int G, int X, int* bx, int* by) {
+    const int L = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+    const int j = L >> 3;                                  // the block's place on its XCD (L mod 8)
+    *by = j % G;
+    *bx = (j / G) * 8 + (L & 7);
+    return *bx < X;
+}
+
 template <int FMT, int MT2, int NBUF, int NW, bool FUSE>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block, AppendArgs ap) {
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int rows_per_block, AppendArgs ap,
+                                                                int shared_x) {
     constexpr int NT = 64 * NW;                          // threads of the block
     constexpr int RB = idx_rb<FMT>();
     constexpr int CR = dma32_chunk_rows<FMT>();            // rows per chunk: 32 (E4M3) or 64 (four-bit rows)
@@ -621,18 +635,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     __shared__ __attribute__((aligned(16))) float fuse_src[FUSE ? kFuseMaxNew : 1][128];
     __shared__ __attribute__((aligned(16))) uint8_t fuse_row[FUSE ? kFuseMaxNew : 1][144];
     static_assert(NW * NBUF * kBuf >= kAppendLdsBytes, "append scratch in the ring");
-    const int b = blockIdx.y;
+    int bx = (int)blockIdx.x, b = (int)blockIdx.y;
+    if (!FUSE && shared_x > 0 && !shared_cache_block(a.B, shared_x, &bx, &b)) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Piece pc;                                              // the carried piece, in registers meanwhile
     if constexpr (FUSE) {
         pc.kind = 0;
-        if (blockIdx.y == 0) piece_load(ap, (int64_t)blockIdx.x * NW + wave, pc);
+        if (b == 0) piece_load(ap, (int64_t)bx * NW + wave, pc);
     }
     const int n32 = lane & 31, h = lane >> 5;
     const int64_t cap = a.capacity;
     const int64_t nvis = clamp_visible(a.n_visible[b], cap);
-    const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+    const int64_t row0 = (int64_t)bx * rows_per_block;
     // new entries whose slot lies in one of this wave's chunks: own_it[e] is that
     // chunk's iteration (-1: not this wave's), own_r[e] the row in the chunk
     int own_it[FUSE ? kFuseMaxNew : 1], own_r[FUSE ? kFuseMaxNew : 1];
@@ -1485,6 +1500,10 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         const int64_t rpw32 = a.fmt == MLA_FMT_E4M3_S128 ? kDmaRowsPerWave : kDmaRowsPerWave4;
         d32rpb = std::min<int64_t>(std::max<int64_t>(d32rpb, unit32), rpw32 * kDma32Waves);
         const dim3 d32grid((unsigned)((a.capacity + d32rpb - 1) / d32rpb), a.B);
+        // several queries of one shared cache: row ranges padded to a multiple of 8 (see
+        // shared_cache_block), the same rows per block as for one sequence
+        const bool shared = a.stride == 0 && a.B > 1 && !carry;
+        const dim3 d32grid_sh((d32grid.x + 7) / 8 * 8, a.B);
         // the queue-fed 32x32 scan (option scan_queues; at the T = 128K shape it is
         // slower than the static partition): about 64 queues (a sequence's rows
         // split into `groups` ranges), 2 blocks per CU in all, at least about 4
@@ -1510,15 +1529,15 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
                         piece_count(*append) <= (int64_t)d32grid.x * kDma32Waves)              \
                         return launch_kernel(k_scan_dma32<F, M / 2, F == MLA_FMT_E4M3_S128 ? kDmaNbuf : kDmaNbuf4, kDma32Waves, true>,    \
                                              d32grid, dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, \
-                                             a, (int)d32rpb, *append);                         \
+                                             a, (int)d32rpb, *append, 0);                      \
                     if (const hipError_t e = unfused(); e != hipSuccess) return e;             \
                     if (dyn)                                                                   \
                         return launch_kernel(k_scan_dyn32<F, M / 2, kDma32Waves>,              \
                                              dim3((unsigned)dyn_nq, (unsigned)dyn_per_queue), dim3(64 * kDma32Waves), \
                                              0, stream, p.start, p.stop, a, dyn_lg);   \
-                    return launch_kernel(k_scan_dma32<F, M / 2, F == MLA_FMT_E4M3_S128 ? kDmaNbuf : kDmaNbuf4, kDma32Waves, false>, d32grid,     \
-                                         dim3(64 * kDma32Waves), 0, stream, p.start, p.stop, a, (int)d32rpb, \
-                                         AppendArgs{});                                        \
+                    return launch_kernel(k_scan_dma32<F, M / 2, F == MLA_FMT_E4M3_S128 ? kDmaNbuf : kDmaNbuf4, kDma32Waves, false>, \
+                                         shared ? d32grid_sh : d32grid, dim3(64 * kDma32Waves), 0, stream, p.start, \
+                                         p.stop, a, (int)d32rpb, AppendArgs{}, shared ? (int)d32grid.x : 0); \
                 }                                                                              \
                 else {                                                                         \
                     if (const hipError_t e = unfused(); e != hipSuccess) return e;             \

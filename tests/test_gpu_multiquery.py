@@ -21,15 +21,21 @@ CFGS = {
 }
 
 
+@pytest.mark.parametrize("Q", [2, 3, 4, 16])
 @pytest.mark.parametrize("name", sorted(CFGS))
-def test_several_queries_of_one_sequence(name):
+def test_several_queries_of_one_sequence(name, Q):
+    """Q positions of one sequence in one call (a prefill chunk or the drafts of
+    multi-token prediction): the last Q positions, each with its causal limit, and
+    for Q = 16 some much shorter limits too (ragged)."""
     cfg = CFGS[name]
-    print("multi-query", name, flush=True)
+    print("multi-query", name, Q, flush=True)
     case = G.build_case(cfg, seed=5)
     M, O = G.M, G.O
-    Q, N, k = 3, cfg.N, cfg.k
-    rng = np.random.default_rng(cfg.cid + 51)
-    nv = np.array([N - 2, N - 1, N], np.int32)            # the step's three positions: their causal limits
+    N, k = cfg.N, cfg.k
+    rng = np.random.default_rng(cfg.cid + 51 + Q)
+    nv = np.arange(N - Q + 1, N + 1, dtype=np.int32)      # the step's positions: their causal limits
+    if Q == 16:
+        nv[:4] = [1, k // 3, k + 1, N // 2]
     bf = lambda x: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).float().numpy()   # as handed over
     q_idx = bf(rng.standard_normal((Q, cfg.H_I, cfg.d_I)))
     w = (rng.standard_normal((Q, cfg.H_I)) * cfg.w_scale).astype(np.float32)
@@ -45,6 +51,7 @@ def test_several_queries_of_one_sequence(name):
     torch.cuda.synchronize()
     if name.endswith("d"):
         assert any("k_scan_dma32" in n for n in launched), launched
+        assert sum("k_scan" in n for n in launched) == 1, launched     # every query in one launch
     got_idx, got_s = out_idx.cpu().numpy(), scores.cpu().numpy()
     G.check_scores(got_s, ref, nv)
     G.check_topk(got_idx, ref, nv, k)

@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--score-bf16", action="store_true",
                    help="the bf16-score top-k: index scores rounded to bf16 before they are selected")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-side-configs", action="store_true",
+                   help="skip the short runs of c2, c4, c4x and c5 that the default c3 invocation reports")
     p.add_argument("--graph", action="store_true",
                    help="replay each rotated layer's step from a HIP graph captured once (the stamped steps "
                         "still run eagerly); default: every step's kernels are launched from the host")
@@ -134,7 +136,6 @@ def build_layers(cfg, n_layers, seed=0):
     return layers
 
 
-SAMPLE_EVERY = 25
 SCAN_SOURCES = ("csrc/indexer.hip", "csrc/append.hpp", "csrc/common.hpp", "csrc/launch.hpp", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_c3_hbm_traffic.md")
 
@@ -201,6 +202,9 @@ def calibrate_copy(args):
 COPY_BYTES = 1 << 30
 
 
+SIDE_CONFIGS = ("c2", "c4", "c4x", "c5")      # reported beside the headline in the same run
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -210,113 +214,139 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args)
         return
+    import torch
+
+    import workloads as WL
+
+    cfg = WL.CONFIGS[args.config]
+    if args.queries:
+        return multi_query(args, cfg)
+    torch.cuda.set_device(0)
+    head = run_config(args, cfg, max(1, args.layers), args.steps, args.warmup, headline=True)
+    result = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "launch": head["launch"],
+        "ms_per_step_eager": head["ms_per_step_eager"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "step_roofline": head["step_roofline"],
+        "per_kernel_breakdown": head["per_kernel_breakdown"],
+    }
+    if "csa2_flushed" in head:
+        result["csa2_flushed"] = head["csa2_flushed"]
+    # the other configurations, shortly, in the same run (default invocation only)
+    if args.config == "c3" and not (args.pool or args.compress or args.graph or args.score_bf16 or
+                                    args.win_fmt != "bf16" or args.no_side_configs):
+        side = {}
+        for name in SIDE_CONFIGS:
+            torch.cuda.empty_cache()
+            r = run_config(args, WL.CONFIGS[name], 4, max(20, min(args.steps, 50)), 5, headline=False)
+            side[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "launch")}
+            side[name]["step_frac"] = r["step_roofline"]["frac"]
+            side[name]["scan_frac"] = r["roofline"]["frac"]
+            side[name]["scan_avg_launch_us"] = r["roofline"]["avg_launch_us"]
+            side[name]["per_kernel_breakdown"] = r["per_kernel_breakdown"]
+            if "csa2_flushed" in r:
+                side[name]["csa2_flushed"] = r["csa2_flushed"]
+            log(f"{name}: {r['ms_per_step'] * 1e3:.2f} us/step, step {100 * side[name]['step_frac']:.1f} % of "
+                f"8 TB/s, scan {100 * side[name]['scan_frac']:.1f} %")
+        result["configs"] = side
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(result), flush=True)
+
+
+def run_config(args, cfg, n_layers, steps, warmup, headline):
+    """Build rotated layer caches for cfg, time `steps` steps (the group helper's calls),
+    then the roofline pass (every indexer scan stamped, outside the timed steps) and the
+    per-kernel breakdown pass. Returns the figures."""
     import numpy as np
     import torch
 
     import sparse_latent_attention_mla_amd as M
     import workloads as WL
 
-    cfg = WL.CONFIGS[args.config]
-    if args.queries:
-        return multi_query(args, cfg)
     dev = "cuda"
-    torch.cuda.set_device(0)
     B, N, H = cfg.B, cfg.N, cfg.H
     mr = M.Row(cfg.main_fmt, cfg.dim, cfg.rope)
     ir = M.Row(cfg.idx_fmt, cfg.d_I, 0)
-    n_layers = max(1, args.layers)
+    L_grp = len(cfg.layers)
     log(f"config {cfg.name}: {cfg.desc}; building {n_layers} layer caches")
     layers = build_layers(cfg, n_layers)
-    win_fmt = M.MXFP8 if (cfg.W and args.win_fmt == "mxfp8") else M.BF16
-    if args.compress:                                      # the window's projected kv and gate vectors
+    opt = args if headline else argparse.Namespace(pool=0, compress=0, win_fmt="bf16", graph=cfg.name == "c5",
+                                                   score_bf16=False)
+    win_fmt = M.MXFP8 if (cfg.W and opt.win_fmt == "mxfp8") else M.BF16
+    if opt.compress:                                       # the window's projected kv and gate vectors
         for i, X in enumerate(layers):
-            X.comp_kv = torch.from_numpy(WL.normal(0, cfg.cid, 200 + 2 * i, (B, args.compress, cfg.D))).to(dev)
-            X.comp_gate = torch.from_numpy(WL.normal(0, cfg.cid, 201 + 2 * i, (B, args.compress, cfg.D))).to(dev)
+            X.comp_kv = torch.from_numpy(WL.normal(0, cfg.cid, 200 + 2 * i, (B, opt.compress, cfg.D))).to(dev)
+            X.comp_gate = torch.from_numpy(WL.normal(0, cfg.cid, 201 + 2 * i, (B, opt.compress, cfg.D))).to(dev)
         comp_norm = torch.ones(cfg.D, dtype=torch.float32, device=dev)
     if win_fmt == M.MXFP8:                                 # the same window values as MXFP8 entries
         for X in layers:
             ring8 = torch.zeros((X.win.shape[0], B, cfg.W, cfg.D + cfg.D // 32), dtype=torch.uint8, device=dev)
             for l in range(X.win.shape[0]):
-                for s in range(cfg.W):
-                    M.mla_kv_append_quant(mr, ir, None, None, None, None, None, X.win[l, :, s].float().contiguous(),
-                                          torch.full((B,), s, dtype=torch.int32, device=dev), ring8[l])
+                for s_ in range(cfg.W):
+                    M.mla_kv_append_quant(mr, ir, None, None, None, None, None, X.win[l, :, s_].float().contiguous(),
+                                          torch.full((B,), s_, dtype=torch.int32, device=dev), ring8[l])
             X.win = ring8
         torch.cuda.synchronize()
 
-    # step buffers
     k = cfg.k
     nvis = torch.full((B,), N, dtype=torch.int32, device=dev)
     slots = torch.full((B, 1), N - 1, dtype=torch.int32, device=dev)
-    p = cfg.tokens - 1
-    win_pos = torch.full((B,), p, dtype=torch.int32, device=dev)
-    win_len = torch.full((B,), min(cfg.W, p + 1), dtype=torch.int32, device=dev)
+    p_ = cfg.tokens - 1
+    win_pos = torch.full((B,), p_, dtype=torch.int32, device=dev)
+    win_len = torch.full((B,), min(cfg.W, p_ + 1), dtype=torch.int32, device=dev)
     idx_out = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(2)]
-    out = torch.empty((B, H, cfg.d_v), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    pool = args.pool if WL.n_indexers(cfg) > 1 else 0
+    out = torch.empty((L_grp, B, H, cfg.d_v), dtype=torch.float32, device=dev)
+    lse = torch.empty((L_grp, B, H), dtype=torch.float32, device=dev)
+    pool = opt.pool if WL.n_indexers(cfg) > 1 else 0
     POOL_BLOCK = 8
     ws_size = M.mla_indexer_topk_workspace(B, N, k)
+    pool_args = None
     if pool:
         ws_size = max(ws_size, M.mla_indexer_pool_workspace(B, N, POOL_BLOCK))
-        full_scores = torch.empty((B, N), dtype=torch.float32, device=dev)
-        pool_pos = torch.empty((B, pool * POOL_BLOCK), dtype=torch.int32, device=dev)
+        pool_args = (pool, POOL_BLOCK, torch.empty((B, N), dtype=torch.float32, device=dev),
+                     torch.empty((B, pool * POOL_BLOCK), dtype=torch.int32, device=dev))
     ws_topk = torch.zeros(ws_size, dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(max(1, M.mla_sparse_decode_workspace(mr, cfg.d_v, B, H, k, cfg.W, win_fmt)), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()
-
     slots1 = slots[:, 0].contiguous()
-    def step(X, stamp=False):
-        """One layer-step (or CSA2 group) on layer caches X: the first layer appends the
-        step's entry (main row, indexer key) and every layer its window entry; Full and
-        Reindex layers select, every layer attends. The first layer's append rides
-        with its indexer scan (mla_append_indexer_topk). With a pool, the Full layer
-        also publishes the candidate pool and the Reindex layer scores only the pool.
-        stamp: time the first layer's scan (the full scan carrying the append)."""
-        j = 0
-        latest = None
-        for l, mode in enumerate(cfg.layers):
-            first = l == 0
-            win = (X.new_win[l], win_pos, X.win[l]) if cfg.W else (None, None, None)
-            selects = mode in ("full", "reindex")
-            if first and args.compress:                    # the main entry pooled from the window's tokens
-                M.mla_compress_append(mr, X.comp_kv, X.comp_gate, X.main, slots1, comp_norm, 1e-6)
-            if first and selects:
-                latest = idx_out[j % 2]
-                if stamp:
-                    M.mla_profile_enable(("indexer_scan",))
-                own_main = not args.compress
-                M.mla_append_indexer_topk(mr, ir, X.new_main if own_main else None, X.new_idx, slots,
-                                          X.main if own_main else None, X.idx, X.q_idx[j],
-                                          X.w[j], cfg.sigma, nvis, k, latest, ws_topk,
-                                          new_win=win[0], win_pos=win[1], win_ring=win[2],
-                                          out_scores=full_scores if pool else None, score_bf16=args.score_bf16)
-                if stamp:
-                    M.mla_profile_enable(())
-                if pool:
-                    M.mla_indexer_pool(full_scores, nvis, pool, pool_pos, ws_topk, block=POOL_BLOCK)
-                j += 1
-            else:
-                M.mla_kv_append_quant(mr, ir, X.new_main if first else None, X.new_idx if first else None,
-                                      slots if first else None, X.main if first else None,
-                                      X.idx if first else None, *win)
-                if selects:
-                    latest = idx_out[j % 2]
-                    M.mla_indexer_topk(ir, X.q_idx[j], X.w[j], cfg.sigma, X.idx, nvis, k, latest, ws_topk,
-                                       cand=pool_pos if pool else None, score_bf16=args.score_bf16)
-                    j += 1
-            M.mla_sparse_decode(mr, cfg.d_v, X.q[l], X.main, latest, cfg.softmax_scale, out, lse, ws_dec,
-                                X.win[l] if cfg.W else None, win_len if cfg.W else None)
 
-    log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
+    def step(X, between=None):
+        """One layer-step (or CSA2 group) on layer caches X, through the group helper: the
+        first layer appends the step's entry in its scan's launch (with --compress the main
+        entry is pooled by mla_compress_append first), every layer its window entry."""
+        if opt.compress:
+            M.mla_compress_append(mr, X.comp_kv, X.comp_gate, X.main, slots1, comp_norm, 1e-6)
+        M.csa2_group_step(mr, ir, cfg.layers, X.main, X.idx, nvis, k, cfg.sigma, cfg.softmax_scale, X.q, X.q_idx,
+                          X.w, out, lse, ws_topk, ws_dec, idx_out,
+                          new_main=None if opt.compress else X.new_main, new_idx=X.new_idx, slots=slots,
+                          win_rings=X.win if cfg.W else None, new_win=X.new_win if cfg.W else None,
+                          win_pos=win_pos if cfg.W else None, win_len=win_len if cfg.W else None,
+                          pool=pool_args, score_bf16=opt.score_bf16, between_layers=between)
+
+    log(f"warmup {warmup} steps")
+    for i in range(warmup):
         step(layers[i % n_layers])
     torch.cuda.synchronize()
 
     # one HIP graph per rotated layer cache, captured from the same calls (the
     # library only enqueues kernels: no allocation, no memset, no host sync)
     graphs = None
-    if args.graph:
+    if opt.graph:
         graphs = []
         for l in range(n_layers):
             g = torch.cuda.CUDAGraph()
@@ -341,48 +371,50 @@ def main():
                 raise RuntimeError("graph replay differs from the eager step")
         log(f"captured {n_layers} step graphs; replays match the eager step")
 
-    def run_step(i, stamp=False):
-        if graphs is None or stamp:
-            step(layers[i % n_layers], stamp=stamp)
+    def run_step(i):
+        if graphs is None:
+            step(layers[i % n_layers])
         else:
             graphs[i % n_layers].replay()
 
-    # timed region: exactly K steps.  On every SAMPLE_EVERY-th step the library
-    # stamps a pair of events from the scan kernel's own dispatch on the launch
-    # stream (mla_profile_*), so the scan's duration is measured inside the timed
-    # steps.  A stamped launch costs extra time around it, hence the sampling;
-    # SAMPLE_EVERY is coprime with the number of rotated caches, so the samples
-    # visit every layer cache.
+    # timed region: exactly `steps` steps, nothing stamped
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    for name in M.PROFILE_KERNELS:
-        M.mla_profile_read(name)          # discard anything recorded before
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
-        run_step(i, stamp=i % SAMPLE_EVERY == 0)
+    for i in range(steps):
+        run_step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    n_scan, scan_ms = M.mla_profile_read("indexer_scan")
-    scan_us = scan_ms * 1e3 / n_scan
+    ms_per_step = t_start.elapsed_time(t_end) / steps
 
-    # the same K steps all launched from the host, for comparison (not the result)
+    # the same steps all launched from the host, for comparison (not the result)
     eager_ms = None
     if graphs is not None:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(steps):
             step(layers[i % n_layers])
         e1.record(stream)
         torch.cuda.synchronize()
-        eager_ms = e0.elapsed_time(e1) / args.steps
+        eager_ms = e0.elapsed_time(e1) / steps
 
-    # per-kernel breakdown: a separate, untimed pass with every kernel stamped
-    # (stamped launches cost host time, so this pass is not the step time)
-    n_brk = min(args.steps, 100)
+    # roofline pass (outside the timed steps): whole eager steps with every indexer scan
+    # stamped from its own dispatch, two per rotated cache (at least 16 launches)
+    for name in M.PROFILE_KERNELS:
+        M.mla_profile_read(name)          # discard anything recorded before
+    n_roof = max(16, 2 * n_layers)
+    M.mla_profile_enable(("indexer_scan",))
+    for i in range(n_roof):
+        step(layers[i % n_layers])
+    torch.cuda.synchronize()
+    M.mla_profile_enable(())
+    n_scan, scan_ms = M.mla_profile_read("indexer_scan")
+    scan_us = scan_ms * 1e3 / n_scan
+
+    # per-kernel breakdown: a separate pass with every kernel stamped
+    n_brk = min(steps, 100)
     M.mla_profile_enable(M.PROFILE_KERNELS)
     for i in range(n_brk):
         step(layers[i % n_layers])
@@ -393,62 +425,85 @@ def main():
         n, ms = M.mla_profile_read(name)
         if n:
             per_kernel[name] = {"launches": n, "avg_us": ms * 1e3 / n}
+
+    res = {}
+    if L_grp > 1:
+        # the CSA2 group with a 512 MB scratch write between its layers (outside the timed
+        # events; MoE layers intervene in the model): each layer timed on its own, the
+        # Reindex layer no longer finding the keys the Full layer pulled through the caches
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L_grp)]
+        per_layer = np.zeros(L_grp)
+        n_fl = min(steps, 20)
+        for i in range(n_fl):
+            def between(l):
+                ev[l - 1][1].record(stream)
+                scratch.fill_(l)
+                ev[l][0].record(stream)
+            scratch.fill_(0)
+            ev[0][0].record(stream)
+            step(layers[i % n_layers], between=between)
+            ev[L_grp - 1][1].record(stream)
+            torch.cuda.synchronize()
+            per_layer += [ev[l][0].elapsed_time(ev[l][1]) for l in range(L_grp)]
+        per_layer /= n_fl
+        res["csa2_flushed"] = {
+            "ms_per_group": float(per_layer.sum()),
+            "ms_per_layer": {f"{l}:{m}": float(per_layer[l]) for l, m in enumerate(cfg.layers)},
+            "groups": n_fl,
+            "note": "eager launches, a 512 MB scratch write between layers outside the timed events; "
+                    "value / ms_per_step are the back-to-back group",
+        }
     log(f"{ms_per_step * 1e3:.2f} us/step" + (f" (eager {eager_ms * 1e3:.2f})" if eager_ms else "") +
-        f"; scan {scan_us:.2f} us live ({n_scan} stamped launches); "
-        "breakdown pass (avg us): " +
-        ", ".join(f"{k}={v['avg_us']:.2f}" for k, v in per_kernel.items()))
+        f"; scan {scan_us:.2f} us ({n_scan} stamped launches); breakdown pass (avg us): " +
+        ", ".join(f"{kk}={v['avg_us']:.2f}" for kk, v in per_kernel.items()))
 
     ab = WL.algorithmic_bytes(cfg, pool, win_fmt=win_fmt)
-    if args.compress:                                      # m tokens' kv and gate in place of one fp32 entry
-        ab["compress"] = B * args.compress * cfg.D * 8 + cfg.D * 4 - B * cfg.D * 4
+    if opt.compress:                                       # m tokens' kv and gate in place of one fp32 entry
+        ab["compress"] = B * opt.compress * cfg.D * 8 + cfg.D * 4 - B * cfg.D * 4
         ab["total"] += ab["compress"]
     step_gbps = ab["total"] / (ms_per_step * 1e-3) / 1e9
-    # dominant kernel: the first layer's indexer scan, which also carries its
-    # quantise-append.  Per launch it must read every visible indexer row of the
-    # batch plus the indexer queries and head weights, and read the new entries
-    # and write their rows (the step's one entry per sequence: fp32 inputs in,
-    # quantised main row and indexer key out, and the first layer's window
-    # entry); the scores it writes for the selection are implementation traffic,
-    # not counted.
+    # dominant kernel: the indexer scan (the first layer's carries the step's append).
+    # Per launch it must read every visible indexer row of the batch plus the indexer
+    # queries and head weights; the carried append's inputs and rows (entry and window)
+    # are averaged over the group's scans; the scores it writes for the selection are
+    # implementation traffic, not counted.
     n_idx_layers = WL.n_indexers(cfg)
-    carried = B * (M.row_bytes(mr) + M.row_bytes(ir) + 4 * (cfg.D + cfg.d_I)) + (B * (4 * cfg.D + WL.window_entry_bytes(cfg, win_fmt)) if cfg.W else 0)
-    scan_bytes = B * N * M.row_bytes(ir) + ab["q_idx_w"] // n_idx_layers + carried
-    scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9
-    result = {
-        "metric": METRIC,
+    carried = B * (M.row_bytes(mr) + M.row_bytes(ir) + 4 * (cfg.D + cfg.d_I)) + (
+        B * (4 * cfg.D + WL.window_entry_bytes(cfg, win_fmt)) if cfg.W else 0)
+    scan_bytes = B * N * M.row_bytes(ir) + ab["q_idx_w"] // n_idx_layers + carried / n_idx_layers
+    if pool:
+        scan_bytes = None                                  # full and pool scans differ: no single figure
+    scan_gbps = scan_bytes / (scan_us * 1e-6) / 1e9 if scan_bytes else None
+    res.update({
         "value": 1e3 / ms_per_step,
-        "unit": "layer-steps/s" if len(cfg.layers) == 1 else "layer-groups/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "unit": "layer-steps/s" if L_grp == 1 else "layer-groups/s",
         "ms_per_step": ms_per_step,
-        "launch": "eager" if graphs is None else "HIP graph per layer cache (every 25th step eager, scan-stamped)",
+        "launch": "eager" if graphs is None else "HIP graph per layer cache",
         "ms_per_step_eager": eager_ms if graphs is not None else ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.desc}",
             "batch": B, "context_rows": N, "tokens": cfg.tokens, "heads": H, "qk_dim": cfg.D, "v_dim": cfg.d_v,
-            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "index_scores": "bf16" if args.score_bf16 else "fp32", "window": cfg.W, "window_format": args.win_fmt if cfg.W else None, "compress_m": args.compress or None, "layers_per_step": len(cfg.layers),
+            "indexer": f"{cfg.H_I}x{cfg.d_I}", "top_k": k, "index_scores": "bf16" if opt.score_bf16 else "fp32",
+            "window": cfg.W, "window_format": opt.win_fmt if cfg.W else None, "compress_m": opt.compress or None,
+            "layers_per_step": L_grp,
             "main_row_bytes": M.row_bytes(mr), "indexer_row_bytes": M.row_bytes(ir),
             "rotated_layer_caches": n_layers, "parallelism": "single GPU",
             "candidate_pool": (f"{pool} blocks of {POOL_BLOCK} published by the Full layer, scored by the "
                                "Reindex layer") if pool else None,
         },
         "roofline": {
-            "kernel": "indexer scan carrying the step's append (k_scan_dma32)",
+            "kernel": "indexer scan (k_scan_dma32; the first layer's carries the step's append)",
             "bound": "hbm",
             "achieved": scan_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": scan_gbps / HBM_PEAK_GBPS,
-            "traffic": scan_traffic(cfg),
+            "frac": scan_gbps / HBM_PEAK_GBPS if scan_gbps else None,
+            "traffic": scan_traffic(cfg) if headline and not opt.score_bf16 else None,
             "algorithmic_bytes_per_launch": scan_bytes,
             "avg_launch_us": scan_us,
             "launches_timed": n_scan,
+            "timed_in": "a pass of whole steps after the timed region, every scan stamped",
         },
         "step_roofline": {
             "algorithmic_bytes_per_step": ab["total"],
@@ -456,10 +511,9 @@ def main():
             "frac": step_gbps / HBM_PEAK_GBPS,
         },
         "per_kernel_breakdown": per_kernel,
-    }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg)
-    print(json.dumps(result), flush=True)
+    })
+    del layers, graphs
+    return res
 
 
 def multi_query(args, cfg):
@@ -550,7 +604,8 @@ def multi_query(args, cfg):
 
 def cpu_baseline(cfg):
     """Time the CPU oracle, as it stands, on one layer-step of the same workload
-    (all sequences), on the host's cores.  Reported beside the GPU, not a target."""
+    (all sequences), on all the host's cores and on one thread.  Reported beside
+    the GPU, not a target."""
     import numpy as np
 
     import oracle as O
@@ -570,22 +625,38 @@ def cpu_baseline(cfg):
              inp.idx[:, :N - 1], pre, o_main, o_idx)
     last = np.full((B, 1), N - 1, np.int32)
     nvis = np.full(B, N, np.int32)
-    times = []
-    for rep in range(3):
-        t0 = time.perf_counter()
-        O.append((cfg.main_fmt, cfg.dim, cfg.rope), (cfg.idx_fmt, cfg.d_I, 0), inp.main[:, N - 1:],
-                 inp.idx[:, N - 1:], last, o_main, o_idx)
-        s = O.indexer_scores((cfg.idx_fmt, cfg.d_I, 0), inp.q_idx[0], inp.w[0], cfg.sigma, o_idx, nvis)
-        idx = O.topk(s, nvis, cfg.k)
-        O.attention((cfg.main_fmt, cfg.dim, cfg.rope), cfg.d_v, inp.q[0], o_main, idx, cfg.softmax_scale)
-        times.append(time.perf_counter() - t0)
-        log(f"cpu baseline rep {rep}: {times[-1]:.2f}s")
-        if sum(times) > 30:
-            break
+
+    def timed(budget_s, max_reps):
+        times = []
+        for rep in range(max_reps):
+            t0 = time.perf_counter()
+            O.append((cfg.main_fmt, cfg.dim, cfg.rope), (cfg.idx_fmt, cfg.d_I, 0), inp.main[:, N - 1:],
+                     inp.idx[:, N - 1:], last, o_main, o_idx)
+            s = O.indexer_scores((cfg.idx_fmt, cfg.d_I, 0), inp.q_idx[0], inp.w[0], cfg.sigma, o_idx, nvis)
+            idx = O.topk(s, nvis, cfg.k)
+            O.attention((cfg.main_fmt, cfg.dim, cfg.rope), cfg.d_v, inp.q[0], o_main, idx, cfg.softmax_scale)
+            times.append(time.perf_counter() - t0)
+            log(f"cpu baseline ({O.num_threads()} threads) rep {rep}: {times[-1]:.2f}s")
+            if sum(times) > budget_s:
+                break
+        return times
+
+    what = (f"full layer-steps of {cfg.name} (append + fp64 indexer scores over all {B}x{N} rows + "
+            f"top-{cfg.k} + attention)")
+    all_cores = O.num_threads()
+    times = timed(20, 3)
     t = statistics.median(times)
-    return {"value": 1.0 / t, "unit": "layer-steps/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{len(times)} full layer-steps of {cfg.name} (append + fp64 indexer scores over all "
-                      f"{B}x{N} rows + top-{cfg.k} + attention), median {t:.3f}s"}
+    res = {"value": 1.0 / t, "unit": "layer-steps/s", "cores": all_cores, "kind": "oracle",
+           "sample": f"{len(times)} {what}, median {t:.3f}s"}
+    O.set_num_threads(1)
+    try:
+        times1 = timed(15, 2)
+    finally:
+        O.set_num_threads(all_cores)
+    t1 = statistics.median(times1)
+    res["one_thread"] = {"value": 1.0 / t1, "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+                         "sample": f"{len(times1)} {what}, median {t1:.3f}s"}
+    return res
 
 
 if __name__ == "__main__":

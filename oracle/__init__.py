@@ -52,6 +52,7 @@ def lib():
                                     f32, P, i32, P, i32, i32, P, P]
         L.orc_attention.restype = i32
         L.orc_num_threads.argtypes, L.orc_num_threads.restype = [], i32
+        L.orc_set_threads.argtypes, L.orc_set_threads.restype = [i32], None
         L.orc_compress.argtypes = [i32, i32, P, P, P, C.c_double, i32, P, i32, P]
         L.orc_compress.restype = i32
         _lib = L
@@ -69,6 +70,11 @@ def _c(a, dt):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 def num_threads() -> int:

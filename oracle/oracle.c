@@ -29,6 +29,11 @@
 #include <omp.h>
 #endif
 
+/* Threads the OpenMP loops use from now on (n >= 1); for timing the oracle on one core. */
+void orc_set_threads(int n) {
+    if (n >= 1) omp_set_num_threads(n);
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -480,3 +480,72 @@ def mla_sparse_decode_noalloc(main_row: Row, d_v: int, q, main_cache, idx, softm
                               rope_cs)
     _check(lib().mla_sparse_decode_noalloc(*args, _stream(stream)))
     del keep
+
+
+def csa2_group_step(main_row: Row, idx_row: Row, modes, main_cache, idx_cache, n_visible, k: int,
+                    score_scale: float, softmax_scale: float, q, q_idx, w, out, lse, topk_workspace,
+                    decode_workspace, idx_out, new_main=None, new_idx=None, slots=None, win_rings=None,
+                    new_win=None, win_pos=None, win_len=None, pool=None, score_bf16=False, stream=None,
+                    between_layers=None):
+    """One decode step of a layer group over one shared cache, as compositions of the
+    C-ABI calls ([P1] "DeepSeek-V4.1", "Three modes"; [P4] "CSA2: four layers keep their
+    own copy"). modes[l] is "full", "reindex" or "reuse":
+      full     the step's append (main row and indexer key, carried in the scan's launch)
+               + indexer top-k with the layer's own indexer query + decode;
+      reindex  indexer top-k with its own indexer query over the shared indexer keys
+               (with `pool`, over the Full layer's candidate pool only) + decode;
+      reuse    decode with the latest Full / Reindex layer's indices.
+    Every layer attends over the shared main cache with its own query and window.
+
+      q            [L, B, H, D] absorbed queries, one per layer
+      q_idx, w     [n, B, H_I, d_I] and [n, B, H_I] for the n Full / Reindex layers, in order
+      out, lse     [L, B, H, d_v] and [L, B, H]
+      idx_out      list of two int32 [B, k] buffers, used in turn by the selecting layers
+      new_main, new_idx, slots   the step's entry (first layer only; new_main None: the main
+                   row was appended by other means, e.g. mla_compress_append)
+      win_rings    [L, B, W, ...] window rings (bf16 or MXFP8 bytes), new_win [L, B, D] the
+                   step's window entries, win_pos [B], win_len [B]; or None (no window)
+      pool         None, or (n_blocks, block, full_scores [B, N] fp32, pool_pos int32
+                   [B, n_blocks * block]): the Full layer publishes a candidate pool
+    The workspaces are one top-k workspace (large enough for the pool too, when used)
+    and one decode workspace, each used by one call at a time. between_layers(l), if
+    given, is called before layer l > 0 is enqueued (e.g. to time layers apart).
+    Returns, per layer, the index tensor it attended."""
+    L = len(modes)
+    attended, latest, j = [], None, 0
+    for l, mode in enumerate(modes):
+        if mode not in ("full", "reindex", "reuse"):
+            raise ValueError(f"unknown layer mode {mode!r}")
+        if l > 0 and between_layers is not None:
+            between_layers(l)
+        win = (new_win[l], win_pos, win_rings[l]) if win_rings is not None else (None, None, None)
+        if mode == "full" or mode == "reindex":
+            latest = idx_out[j % 2]
+            if l == 0:
+                mla_append_indexer_topk(main_row, idx_row, new_main, new_idx, slots,
+                                        main_cache if new_main is not None else None, idx_cache, q_idx[j], w[j],
+                                        score_scale, n_visible, k, latest, topk_workspace, new_win=win[0],
+                                        win_pos=win[1], win_ring=win[2],
+                                        out_scores=pool[2] if (pool is not None and mode == "full") else None,
+                                        score_bf16=score_bf16, stream=stream)
+            else:
+                if win[0] is not None:
+                    mla_kv_append_quant(main_row, idx_row, None, None, None, None, None, *win, stream=stream)
+                use_pool = pool is not None and mode == "reindex"
+                mla_indexer_topk(idx_row, q_idx[j], w[j], score_scale, idx_cache, n_visible, k, latest,
+                                 topk_workspace, out_scores=pool[2] if (pool is not None and mode == "full") else None,
+                                 cand=pool[3] if use_pool else None, score_bf16=score_bf16, stream=stream)
+            if pool is not None and mode == "full":
+                mla_indexer_pool(pool[2], n_visible, pool[0], pool[3], topk_workspace, block=pool[1],
+                                 stream=stream)
+            j += 1
+        else:
+            if latest is None:
+                raise ValueError("a reuse layer needs a preceding full or reindex layer")
+            if win[0] is not None:
+                mla_kv_append_quant(main_row, idx_row, None, None, None, None, None, *win, stream=stream)
+        mla_sparse_decode(main_row, out.shape[-1], q[l], main_cache, latest, softmax_scale, out[l], lse[l],
+                          decode_workspace, win_rings[l] if win_rings is not None else None,
+                          win_len if win_rings is not None else None, stream=stream)
+        attended.append(latest)
+    return attended

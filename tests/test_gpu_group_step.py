@@ -1,0 +1,177 @@
+"""The layer-group helper (csa2_group_step, a composition of the C-ABI calls only)
+against the same calls made one by one, and against the oracle's step: Full /
+Reindex layers select with their own indexer query over the shared keys, Reuse
+layers take the latest selection, every layer attends with its own query and
+window ("DeepSeek-V4.1", "Three modes"; "CSA2: four layers keep their own copy").
+
+The cases' caches already hold the step's entry (position N-1, and the window
+entries of position p); the helper appends the same values to the same slots
+again, which leaves every cache byte unchanged."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from tests import gpu_cases as G
+from tests.test_gpu_pool import check_pool_near, check_pool_topk
+
+pytestmark = pytest.mark.gpu
+C = WL.CONFIGS
+CFGS = {
+    "c1": C["c1"],
+    "c3d": C["c3"].with_(name="c3d", cid=123, B=2, N=6004),
+    "c4d": C["c4"].with_(name="c4d", cid=124, B=2, N=4100),
+    "c5s": C["c5"].with_(name="c5s", cid=105, B=1, N=3001),
+    "c5d": C["c5"].with_(name="c5d", cid=125, B=2, N=4100),
+}
+POOL_BLOCK = 8
+
+
+def say(*a):
+    print("[group-step]", *a, file=sys.stderr, flush=True)
+
+
+def _inputs(case, pool_blocks):
+    cfg = case.cfg
+    M, dev = G.M, G.DEV
+    B, N, L, k = cfg.B, cfg.N, len(cfg.layers), cfg.k
+    n_idx = WL.n_indexers(cfg)
+    inp = case.inp
+    x = dict(
+        q=torch.stack([G._q_gpu(cfg, inp.q[l]) for l in range(L)]),
+        q_idx=torch.stack([G._qi_gpu(cfg, inp.q_idx[j]) for j in range(n_idx)]),
+        w=G._t(inp.w),
+        nvis=G._t(case.n_visible),
+        new_main=G._t(inp.main[:, N - 1:]), new_idx=G._t(inp.idx[:, N - 1:]),
+        slots=torch.full((B, 1), N - 1, dtype=torch.int32, device=dev),
+    )
+    ws = M.mla_indexer_topk_workspace(B, N, k)
+    if pool_blocks:
+        ws = max(ws, M.mla_indexer_pool_workspace(B, N, POOL_BLOCK))
+        x["pool"] = (pool_blocks, POOL_BLOCK, torch.empty((B, N), dtype=torch.float32, device=dev),
+                     torch.empty((B, pool_blocks * POOL_BLOCK), dtype=torch.int32, device=dev))
+    else:
+        x["pool"] = None
+    x["ws"] = torch.zeros(ws, dtype=torch.uint8, device=dev)
+    x["wsd"] = torch.empty(max(1, M.mla_sparse_decode_workspace(G.main_row(cfg), cfg.d_v, B, cfg.H, k, cfg.W)),
+                           dtype=torch.uint8, device=dev)
+    if cfg.W:
+        p = cfg.tokens - 1
+        x["new_win"] = G._t(inp.win[:, :, cfg.W - 1])
+        x["win_pos"] = torch.full((B,), p, dtype=torch.int32, device=dev)
+        x["win_len"] = G._t(case.win_len)
+    return x
+
+
+def _outs(cfg):
+    L, B, H = len(cfg.layers), cfg.B, cfg.H
+    return (torch.full((L, B, H, cfg.d_v), float("nan"), device=G.DEV),
+            torch.full((L, B, H), float("nan"), device=G.DEV),
+            [torch.full((B, cfg.k), -7, dtype=torch.int32, device=G.DEV) for _ in range(2)])
+
+
+def _by_hand(case, x, main, idx, win):
+    """The same step as individual calls, in the group's order."""
+    cfg = case.cfg
+    M = G.M
+    mr, ir = G.main_row(cfg), G.idx_row(cfg)
+    out, lse, bufs = _outs(cfg)
+    pool = x["pool"]
+    latest, j, attended = None, 0, []
+    for l, mode in enumerate(cfg.layers):
+        wargs = (x["new_win"][l], x["win_pos"], win[l]) if cfg.W else (None, None, None)
+        if mode in ("full", "reindex"):
+            latest = bufs[j % 2]
+            scores = pool[2] if (pool is not None and mode == "full") else None
+            if l == 0:
+                M.mla_kv_append_quant(mr, ir, x["new_main"], x["new_idx"], x["slots"], main, idx, *wargs)
+            elif cfg.W:
+                M.mla_kv_append_quant(mr, ir, None, None, None, None, None, *wargs)
+            M.mla_indexer_topk(ir, x["q_idx"][j], x["w"][j], cfg.sigma, idx, x["nvis"], cfg.k, latest, x["ws"],
+                               out_scores=scores, cand=pool[3] if (pool is not None and mode == "reindex") else None)
+            if scores is not None:
+                M.mla_indexer_pool(scores, x["nvis"], pool[0], pool[3], x["ws"], block=pool[1])
+            j += 1
+        elif cfg.W:
+            M.mla_kv_append_quant(mr, ir, None, None, None, None, None, *wargs)
+        M.mla_sparse_decode(mr, cfg.d_v, x["q"][l], main, latest, cfg.softmax_scale, out[l], lse[l], x["wsd"],
+                            win[l] if cfg.W else None, x["win_len"] if cfg.W else None)
+        attended.append(latest.clone())
+    return out, lse, attended
+
+
+def _helper(case, x, main, idx, win, calls):
+    cfg = case.cfg
+    out, lse, bufs = _outs(cfg)
+    att = G.M.csa2_group_step(G.main_row(cfg), G.idx_row(cfg), cfg.layers, main, idx, x["nvis"], cfg.k, cfg.sigma,
+                              cfg.softmax_scale, x["q"], x["q_idx"], x["w"], out, lse, x["ws"], x["wsd"], bufs,
+                              new_main=x["new_main"], new_idx=x["new_idx"], slots=x["slots"],
+                              win_rings=win, new_win=x.get("new_win"), win_pos=x.get("win_pos"),
+                              win_len=x.get("win_len"), pool=x["pool"], between_layers=calls.append)
+    # each selecting layer's buffer is overwritten two selections later: keep copies
+    # of what each layer attended as soon as the group is done (two buffers suffice
+    # for any group with at most two selecting layers)
+    return out, lse, [a.clone() for a in att]
+
+
+@pytest.mark.parametrize("name,pool", [("c1", 0), ("c3d", 0), ("c4d", 0), ("c5s", 0), ("c5d", 0), ("c5d", 96)])
+def test_group_helper_matches_calls_and_oracle(name, pool):
+    cfg = CFGS[name]
+    say(name, "pool", pool)
+    case = G.build_case(cfg, seed=3)
+    x = _inputs(case, pool)
+    L = len(cfg.layers)
+    cache = lambda: (case.g_main.clone(), case.g_idx.clone(), case.g_win.clone() if cfg.W else None)
+    main_h, idx_h, win_h = cache()
+    calls = []
+    out_h, lse_h, att_h = _helper(case, x, main_h, idx_h, win_h, calls)
+    torch.cuda.synchronize()
+    pool_pos = x["pool"][3].cpu().numpy() if pool else None      # the Full layer's pool, as the helper left it
+    main_m, idx_m, win_m = cache()
+    out_m, lse_m, att_m = _by_hand(case, x, main_m, idx_m, win_m)
+    torch.cuda.synchronize()
+    assert calls == list(range(1, L)), calls
+    # re-appending the step's entry leaves the caches as built
+    assert torch.equal(main_h, case.g_main) and torch.equal(idx_h, case.g_idx)
+    if cfg.W:
+        assert torch.equal(win_h, case.g_win)
+    for l in range(L):
+        a, b = att_h[l].cpu().numpy(), att_m[l].cpu().numpy()
+        assert np.array_equal(np.sort(a, 1), np.sort(b, 1)), l      # the same sets (order may differ)
+    # the same kernels on the same sets: outputs agree to summation order
+    G.check_attention(out_h.cpu().numpy().reshape(-1, cfg.H, cfg.d_v), lse_h.cpu().numpy().reshape(-1, cfg.H),
+                      out_m.cpu().numpy().reshape(-1, cfg.H, cfg.d_v), lse_m.cpu().numpy().reshape(-1, cfg.H),
+                      rel=1e-5)
+    if pool:                                    # the pool itself, to the scores' bar
+        check_pool_near(pool_pos, G.oracle_scores(case, 0), case.n_visible, pool, POOL_BLOCK)
+    # against the oracle: selections of the selecting layers, attention of every layer
+    j = 0
+    for l, mode in enumerate(cfg.layers):
+        got = att_h[l].cpu().numpy()
+        if mode in ("full", "reindex"):
+            if pool and mode == "reindex":       # scored over the pool the Full layer published
+                check_pool_topk(got, G.oracle_scores(case, j, cand=pool_pos), pool_pos, case.n_visible, cfg.k)
+            else:
+                G.check_topk(got, G.oracle_scores(case, j), case.n_visible, cfg.k)
+            j += 1
+        else:
+            assert np.array_equal(got, att_h[l - 1].cpu().numpy())
+        ref_o, ref_l = G.oracle_attention(case, l, got)
+        G.check_attention(out_h[l].cpu().numpy(), lse_h[l].cpu().numpy(), ref_o, ref_l)
+
+
+def test_group_helper_rejects_unknown_and_leading_reuse():
+    cfg = CFGS["c5s"]
+    case = G.build_case(cfg, seed=3)
+    x = _inputs(case, 0)
+    for modes in (("full", "bogus"), ("reuse", "full")):
+        out, lse, bufs = _outs(cfg.with_(layers=modes))
+        with pytest.raises(ValueError):
+            G.M.csa2_group_step(G.main_row(cfg), G.idx_row(cfg), modes, case.g_main.clone(), case.g_idx.clone(),
+                                x["nvis"], cfg.k, cfg.sigma, cfg.softmax_scale, x["q"], x["q_idx"], x["w"], out,
+                                lse, x["ws"], x["wsd"], bufs, new_main=x["new_main"], new_idx=x["new_idx"],
+                                slots=x["slots"], win_rings=case.g_win.clone(), new_win=x["new_win"],
+                                win_pos=x["win_pos"], win_len=x["win_len"])
+    torch.cuda.synchronize()

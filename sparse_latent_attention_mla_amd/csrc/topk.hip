@@ -544,19 +544,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
     }
     lds_barrier();
     const int T = T_s;
-    // this workgroup's share of zeroing the fine histogram for the next call: every
-    // workgroup of the sequence finds the same threshold, so only the 64 fine bins of
-    // the threshold's coarse bin (which the others may still be reading, and which
-    // k_select_final clears) are skipped
-    {
-        uint32_t* fine0 = hist_fine(ws.hist + (int64_t)b * kHistWordsHost, 0);
-        constexpr int kFineWords = kHistCopies * kHistBins;
-        const int per = (kFineWords / 4 + gridDim.x - 1) / gridDim.x;   // u32x4 per workgroup
-        const int cb = T >= 0 ? T / kFinePerCoarse : -1;
-        for (int i = blockIdx.x * per + t; i < (int)(blockIdx.x + 1) * per && i < kFineWords / 4; i += kSelThreads)
-            if (((4 * i) % kHistBins) / kFinePerCoarse != cb)
-                reinterpret_cast<u32x4*>(fine0)[i] = u32x4{0u, 0u, 0u, 0u};
-    }
     uint32_t key[kPer];
     uint64_t mt[kPer], mc[kPer];
     uint32_t nt = 0, nc = 0;
@@ -589,6 +576,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* __restrict_
         }
     }
     lds_barrier();
+    // this workgroup's share of zeroing the fine histogram for the next call: every
+    // workgroup of the sequence finds the same threshold, so only the 64 fine bins of
+    // the threshold's coarse bin (which the others may still be reading, and which
+    // k_select_final clears) are skipped. (Issued after the classification: a load
+    // waited for behind a store waits for that store too.)
+    {
+        uint32_t* fine0 = hist_fine(ws.hist + (int64_t)b * kHistWordsHost, 0);
+        constexpr int kFineWords = kHistCopies * kHistBins;
+        const int per = (kFineWords / 4 + gridDim.x - 1) / gridDim.x;   // u32x4 per workgroup
+        const int cb = T >= 0 ? T / kFinePerCoarse : -1;
+        for (int i = blockIdx.x * per + t; i < (int)(blockIdx.x + 1) * per && i < kFineWords / 4; i += kSelThreads)
+            if (((4 * i) % kHistBins) / kFinePerCoarse != cb)
+                reinterpret_cast<u32x4*>(fine0)[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     // the workgroup's own slots: counts, then its lists at r0 (at most kSelRows rows each)
     if (t == 0) {
         uint32_t* cnt = ws.counts + ((int64_t)b * gridDim.x + blockIdx.x) * 2;
@@ -768,6 +769,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     __shared__ uint32_t cursor;
     __shared__ uint32_t g_cnt[kF2MaxGroups][2], g_off[kF2MaxGroups][2];
     __shared__ uint32_t wtot[kF2Waves][2];
+    __shared__ uint32_t has_rest;
     const int b = blockIdx.x;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t nvis = visible_of(n_visible, b, capacity);
@@ -804,7 +806,8 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
         wtot[wv][0] = is;
         wtot[wv][1] = ic;
     }
-    __syncthreads();
+    if (t == 0) has_rest = groups > kSpecGroups ? 1u : 0u;
+    lds_barrier();
     uint32_t bs = 0, bc = 0, nsel = 0, ncand = 0;
 #pragma unroll
     for (int i = 0; i < kF2Waves; ++i) {
@@ -821,8 +824,9 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
         g_off[t][1] = bc + ic - cc;
         g_cnt[t][0] = cs;
         g_cnt[t][1] = cc;
+        if (cs > 64u || cc > 64u) has_rest = 1u;
     }
-    __syncthreads();
+    lds_barrier();
     // placement: entry i of workgroup j's lists goes to the output (selected) or to
     // the candidate list (LDS, then cand2 past kFinalLds)
     auto place_sel = [&](int j, uint32_t i, int32_t v) {
@@ -843,25 +847,32 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
         }
     }
     // the rest: workgroups past the speculated ones, and entries past the first 64
-    for (int j = wv; j < groups; j += kF2Waves) {
-        const uint32_t i0 = (j < wv + kF2Waves * kF2Spec) ? 64u : 0u;
-        const uint32_t ns = g_cnt[j][0], nc = g_cnt[j][1];
-        for (uint32_t i = i0 + lane; i < ns; i += 64) place_sel(j, i, gsel[(int64_t)j * kSelRows + i]);
-        for (uint32_t i = i0 + lane; i < nc; i += 64) place_cnd(j, i, gcnd[(int64_t)j * kSelRows + i]);
+    // (skipped as a whole when there is none: its loads, issued behind the output's
+    // stores, would wait for them)
+    if (has_rest) {
+        for (int j = wv; j < groups; j += kF2Waves) {
+            const uint32_t i0 = (j < wv + kF2Waves * kF2Spec) ? 64u : 0u;
+            const uint32_t ns = g_cnt[j][0], nc = g_cnt[j][1];
+            for (uint32_t i = i0 + lane; i < ns; i += 64) place_sel(j, i, gsel[(int64_t)j * kSelRows + i]);
+            for (uint32_t i = i0 + lane; i < nc; i += 64) place_cnd(j, i, gcnd[(int64_t)j * kSelRows + i]);
+        }
     }
-    __syncthreads();
+    // the barriers below order LDS only (the output's stores need no ordering here);
+    // a candidate list that overflows LDS is also read from global memory, so then
+    // every store of it has landed first
+    if (ncand > (uint32_t)kFinalLds) __threadfence_block();
+    lds_barrier();
     if (ncand > (uint32_t)kFinalLds) {                   // the radix passes then read one contiguous list
         for (uint32_t i = t; i < (uint32_t)kFinalLds; i += kF2Threads) gc2[i] = L.lc[i];
         __threadfence_block();                             // (only then: it waits for every store)
     }
     if (t == 0) cursor = nsel;
     for (int i = t; i < kMaxDigitBins; i += kF2Threads) L.h[0][i] = 0u;
-    __syncthreads();
+    lds_barrier();
     const uint32_t need = (want > nsel) ? want - nsel : 0u;
     zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k, csum);   // the stores drain during the radix
     radix_take_any<kF2Threads>(L, gc2, ncand, need, want, out, &cursor);
-    __syncthreads();
-    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);   // slots the take leaves alone
 }
 
 
@@ -1025,8 +1036,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2_flat(const int32_t
     const uint32_t need = (want > nsel) ? want - nsel : 0u;
     zero_hist_rest(ws.hist + (int64_t)b * kHistWordsHost, (uint32_t)k, csum);   // the stores drain during the radix
     radix_take_any<kF2Threads>(L, gc2, ncand, need, want, out, &cursor);
-    __syncthreads();
-    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);
+    for (uint32_t i = want + t; i < (uint32_t)k; i += kF2Threads) out.put(i, -1);   // slots the take leaves alone
 }
 
 }  // namespace

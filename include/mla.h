@@ -432,8 +432,9 @@ mla_status_t mla_append_indexer_topk_bf16(mla_row_t main_row, mla_row_t idx_row,
  *              are attended twice
  *  win_ring    optional window entries (K = V) in format win_fmt: bf16 [B, W, dim+rope]
  *              (16-byte aligned) or MXFP8 [B, W, D + D/32] bytes (D = dim+rope, D % 32 ==
- *              0), widened exactly to bf16 in the workspace before the decode (exact
- *              for every block whose scale code is at least 3), with
+ *              0), widened to bf16 (exact for every block whose scale code is at least 3):
+ *              512-channel entries in a 16-byte aligned ring as the decode stages them,
+ *              others into the workspace by a launch of their own first, with
  *  win_len     int32 [B] in [0, W], the number of valid ring slots (slots 0..len-1)
  *  epilogue    optional (NULL = none):
  *              sinks: fp32 [H] attention-sink logits, one per head, shared by the batch

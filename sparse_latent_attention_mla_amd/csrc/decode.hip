@@ -36,7 +36,7 @@ constexpr int kGenericThreads = 256;
 constexpr int kGenericMaxRows = 8192;
 constexpr int kMergeFast = 16;             // splits the merge loads in one round
 
-enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2 };
+enum SrcKind { SRC_E4M3 = 0, SRC_FP4 = 1, SRC_BF16 = 2, SRC_MX8 = 3 };   // SRC_MX8: MXFP8 window entries
 
 typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -143,9 +143,12 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
     float* red = reinterpret_cast<float*>(smem + L::kRed);
     constexpr float kLog2e = 1.4426950408889634f;
     const float zscale = a.scale * kLog2e;
-    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
-                                     : a.cache + b * a.stride;
-    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;
+    static_assert(SRC != SRC_MX8 || DQK == 512, "MXFP8 window entries of 512 channels");
+    constexpr uint32_t kMx8Bytes = DQK + DQK / 32;        // an MXFP8 entry: codes, then one E8M0 byte per 32
+    const uint8_t* row_base = SRC == SRC_MX8 ? a.win8 + (int64_t)b * a.W * kMx8Bytes
+                              : is_win       ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
+                                             : a.cache + b * a.stride;
+    const uint32_t row_bytes = SRC == SRC_MX8 ? kMx8Bytes : is_win ? 2 * DQK : (uint32_t)a.row_bytes;
 
     // ---- row indices (-1: no row) and the 16 heads' queries
     if (tid < R) {
@@ -216,6 +219,41 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
             const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * lane
                                         : reinterpret_cast<const uint8_t*>(a.q);
             dma16(src, __builtin_amdgcn_readfirstlane(v_m0 + (uint32_t)(VS * u)));
+        }
+    } else if constexpr (SRC == SRC_MX8) {                 // MXFP8 entries: 16 blocks of 32 channels per entry
+        // (one E8M0 scale per block: the converter applies the power of two given as an
+        // fp32 scale, whose exponent field is the E8M0 code; E4M3 times 2^k is exact in
+        // bf16 down to bf16's subnormals, as with the entry widened on its own)
+        constexpr int kPer = R * 16 / 512;
+        u32x4 c0[kPer], c1[kPer];
+        uint32_t scb[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int item = tid + 512 * i, u = item >> 4, pc = item & 15;
+            const int32_t r = ridx[u];
+            const uint8_t* rp = row_base + (uint64_t)(uint32_t)(r < 0 ? 0 : r) * row_bytes;
+            c0[i] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 32 * pc) : u32x4{0u, 0u, 0u, 0u};
+            c1[i] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 32 * pc + 16) : u32x4{0u, 0u, 0u, 0u};
+            scb[i] = r >= 0 ? (uint32_t)rp[DQK + pc] : 127u;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int item = tid + 512 * i, u = item >> 4, pc = item & 15;
+            u32x4* d = reinterpret_cast<u32x4*>(V + u * VS + 64 * pc);
+            const float sc = u2f(scb[i] << 23);            // exponent field = the E8M0 code
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const u32x4 c = h2 ? c1[i] : c0[i];
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const uint32_t w0 = c[2 * q2], w1 = c[2 * q2 + 1];
+                    d[2 * h2 + q2] = u32x4{
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true))};
+                }
+            }
         }
     } else {                                               // E2M1 rows: 16 pieces of 32 channels per row
         constexpr int kPer = R * 16 / 512;
@@ -429,6 +467,12 @@ __global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int 
         const int wl = (int)clamp_visible(a.win_len[b], a.W);
         int n = (int)(wl - first);
         n = n < 0 ? 0 : (n > rps_win ? rps_win : n);
+        if constexpr (DQK == 512) {
+            if (a.win8) {                                  // MXFP8 entries, widened as they are staged
+                decode_split_g<SRC_MX8, DQK, 128>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+                return;
+            }
+        }
         decode_split_g<SRC_BF16, DQK, 128>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
     }
 }
@@ -771,7 +815,11 @@ __global__ __launch_bounds__(256) void k_widen_window(const uint8_t* __restrict_
 hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
     if (a_in.B == 0) return hipSuccess;
     DecodeArgs a = a_in;
-    if (a.win8 && a.W > 0) {                               // bf16 copy after the decode's own workspace
+    // MXFP8 window entries of 512 channels (16-byte aligned) are widened inside the gather
+    // decode's staging; others are first widened to a bf16 copy after the decode's own workspace
+    const bool mfma = mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H);
+    const bool win8_inline = a.win8 && mfma && a.dim + a.rope == 512 && reinterpret_cast<uintptr_t>(a.win8) % 16 == 0;
+    if (a.win8 && a.W > 0 && !win8_inline) {
         const size_t base = decode_workspace_bytes(a.fmt, a.dim, a.rope, a.d_v, a.B, a.H, a.k, a.W);
         uint16_t* wide = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + base);
         const hipError_t e = launch_kernel(k_widen_window, dim3((unsigned)(a.B * a.W)), dim3(256), 0, stream,
@@ -780,11 +828,11 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
         a.win = wide;
         a.win8 = nullptr;
     }
-    if (!mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H)) {
+    if (!mfma) {
         const ProfSlot p = prof_slot(PROF_DECODE);
         return launch_kernel(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, p.start, p.stop, a);
     }
-    const Geometry g = gather_geometry(a.fmt, a.B, a.H, a.k, a.win ? a.W : 0);
+    const Geometry g = gather_geometry(a.fmt, a.B, a.H, a.k, (a.win || a.win8) ? a.W : 0);
     const int S = g.S_main + g.S_win;
     const size_t o_bytes = (((size_t)a.B * S * a.H * kDv * sizeof(float)) + 255) & ~(size_t)255;
     float* o_part = reinterpret_cast<float*>(a.workspace);

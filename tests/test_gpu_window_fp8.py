@@ -65,6 +65,10 @@ def test_mxfp8_window_append_bytes_and_decode(name):
     idx[:, ::7] = -1
     ref_o, ref_l = G.oracle_attention(case8, 0, idx)
     got_o, got_l = G.gpu_decode(case8, 0, idx)
+    launched = M.mla_last_kernels()
+    # 512-channel entries are widened as the decode stages them; 576-channel ones (594 bytes,
+    # not 16-byte aligned) by a widening launch first
+    assert any("k_widen_window" in k for k in launched) == (D != 512), launched
     G.check_attention(got_o, got_l, ref_o, ref_l)
     # the same entries as a bf16 ring give the same decode up to summation order
     case16 = dataclasses.replace(case, o_win=o_win, g_win=as_bf16.reshape(1, B, W, D).to(G.DEV))

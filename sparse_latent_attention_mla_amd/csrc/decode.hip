@@ -444,6 +444,219 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         lse_part[prow] = (l > 0.0f) ? (M + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
 }
 
+// Gather-all split for bf16 rows (and bf16 window entries), two head tiles of 16 heads
+// per workgroup: waves 0-3 serve heads 32 hp .. + 15, waves 4-7 heads 32 hp + 16 .. + 31,
+// over the same 128 staged rows, so each row crosses into a CU once per 32 heads. The
+// queries go from memory straight into each wave's operand registers (LDS holds the
+// rows, P and the reductions); otherwise the phases are decode_split_g's: QK on the
+// wave's two row tiles, an exact softmax per head tile, PV with the wave owning 128
+// value channels of its head tile.
+namespace gd2 {
+constexpr int kR = 128;
+constexpr int kVS = 1056;                                  // bytes per staged row (512 bf16 + 32)
+constexpr int kPStride = kR + 4;                           // fp32 per head in P
+constexpr int kP = kR * kVS;                               // P [32 heads][kPStride]
+constexpr int kIdx = kP + 32 * kPStride * 4;               // row indices [kR]
+constexpr int kRed = kIdx + kR * 4;                        // [2][8 waves][16 heads]
+constexpr int kBytes = kRed + 2 * 8 * 16 * 4;
+}  // namespace gd2
+
+template <int DQK>
+__device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* smem, int b, int split, int S,
+                                                  int hp, bool is_win, int64_t first, int n, float* o_part,
+                                                  float* lse_part) {
+    constexpr int R = gd2::kR, VS = gd2::kVS;
+    constexpr bool kRope = DQK == 576;
+    constexpr int NMAIN = 16, NQ = DQK / 32, NT = 2;      // row tiles per wave: wq and wq + 4
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hs = w >> 2, wq = w & 3;                     // the wave's head tile in the pair, its place there
+    const int j = lane & 15, g = lane >> 4;
+    uint8_t* V = smem;
+    float* P = reinterpret_cast<float*>(smem + gd2::kP);
+    int32_t* ridx = reinterpret_cast<int32_t*>(smem + gd2::kIdx);
+    float* red = reinterpret_cast<float*>(smem + gd2::kRed);
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float zscale = a.scale * kLog2e;
+    const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
+                                     : a.cache + b * a.stride;
+    const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;
+
+    if (tid < R) {
+        int32_t r = -1;
+        if (tid < n) {
+            if (is_win) r = (int32_t)(first + tid);
+            else {
+                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
+                if (s >= 0 && s < a.capacity) r = s;
+            }
+        }
+        ridx[tid] = r;
+    }
+    // B operands of the wave's 16 heads (channels 32 st + 8 g .. of head j), used after the gather
+    u32x4 qv[NQ];
+    {
+        const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + 32 * hp + 16 * hs + j) * DQK;
+#pragma unroll
+        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 32 * st + 8 * g);
+    }
+    __syncthreads();                                       // the row indices
+
+    // ---- gather: one row per load instruction; the pairs of a split (one XCD) start at
+    // different quarters of its rows, each landing its own quarter before requesting the rest
+    const uint32_t v_m0 = __builtin_amdgcn_readfirstlane(lds_addr(V));
+    uint32_t zmask = 0;
+    constexpr int PW = R / 8;
+    const int rot = (hp & 3) * (R / 4);                    // (a multiple of 8: a wave keeps its rows)
+#pragma unroll 4
+    for (int i = 0; i < PW; ++i) {
+        if (i == PW / 4) wait_vmcnt<0>();
+        const int u = (w + 8 * i + rot) % R;
+        const int32_t r = ridx[u];
+        zmask |= r < 0 ? (1u << i) : 0u;
+        const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * lane
+                                    : reinterpret_cast<const uint8_t*>(a.q);
+        dma16(src, __builtin_amdgcn_readfirstlane(v_m0 + (uint32_t)(VS * u)));
+    }
+    u32x4 rope[NT][2];
+    if constexpr (kRope) {
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+            const int tt = wq + 4 * m;
+            const int32_t r = ridx[16 * tt + j];
+            const uint8_t* rp = row_base + (uint64_t)(uint32_t)(r < 0 ? 0 : r) * row_bytes + 1024;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                rope[m][s2] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 2 * (32 * s2 + 8 * g))
+                                     : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    wait_vmcnt<0>();
+    if (__builtin_amdgcn_ballot_w64(zmask != 0u)) {
+        for (int i = 0; i < PW; ++i)
+            if ((zmask >> i) & 1u)
+                *reinterpret_cast<u32x4*>(V + VS * ((w + 8 * i + rot) % R) + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+
+    // ---- A: scores of the wave's two row tiles for its 16 heads
+    float z[NT][4];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+        const int tt = wq + 4 * m;
+        const bool live = 16 * tt < n;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            const uint8_t* krow = V + (16 * tt + j) * VS;
+#pragma unroll
+            for (int st = 0; st < NMAIN; ++st)
+                acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * st + 8 * g)), qv[st], acc);
+            if constexpr (kRope) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) acc = mfma_bf16(rope[m][s2], qv[NMAIN + s2], acc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * tt + 4 * g + r;
+            z[m][r] = (live && ridx[row] >= 0) ? acc[r] * zscale : -__builtin_inff();
+        }
+    }
+
+    // ---- B: exact softmax over the split's rows per head tile (base 2)
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int m = 0; m < NT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, z[m][r]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    if (g == 0) red[16 * w + j] = mloc;
+    __syncthreads();
+    float M = red[16 * (4 * hs) + j];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, red[16 * (4 * hs + ww) + j]);
+    float* Ph = P + (16 * hs + j) * gd2::kPStride;
+    float sloc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NT; ++m) {
+        const int tt = wq + 4 * m;
+        f32x4 pv4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pv4[r] = (z[m][r] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[m][r] - M);
+            sloc += pv4[r];
+        }
+        *reinterpret_cast<f32x4*>(Ph + 16 * tt + 4 * g) = pv4;
+    }
+    sloc += __shfl_xor(sloc, 16, 64);
+    sloc += __shfl_xor(sloc, 32, 64);
+    if (g == 0) red[128 + 16 * w + j] = sloc;
+    __syncthreads();
+
+    // ---- C: PV over every row for value channels 128 wq .. 128 wq + 127 of the head tile
+    f32x4 o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < R / 32; ++st) {
+        if (32 * st >= n) break;
+        const float* pr = Ph + 32 * st + 8 * g;
+        const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+        const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        u32x4 pa, pb;
+        split_bf16x8(p, pa, pb);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const int c0 = 128 * wq + 16 * mt;
+            const uint8_t* vp = V + (32 * st + 8 * g + (j >> 2)) * VS + 2 * (c0 + 4 * (j & 3));
+            const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * VS);
+            const u32x4 av = u32x4{r0.x, r0.y, r1.x, r1.y};
+            o[mt] = mfma_bf16(av, pa, o[mt]);
+            o[mt] = mfma_bf16(av, pb, o[mt]);
+        }
+    }
+
+    // ---- the split's partial for the wave's head tile
+    float l = red[128 + 16 * (4 * hs) + j];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) l += red[128 + 16 * (4 * hs + ww) + j];
+    const int head = 32 * hp + 16 * hs + j;
+    const int64_t prow = ((int64_t)b * S + split) * a.H + head;
+    const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * wq + 16 * mt + 4 * g) =
+            make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
+    if (wq == 0 && g == 0)
+        lse_part[prow] = (l > 0.0f) ? (M + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
+}
+
+template <int DQK>
+__global__ __launch_bounds__(512) void k_decode_pair(DecodeArgs a, int S_main, int S_win, int rps, int rps_win,
+                                                     int pairs, int n_items, float* o_part, float* lse_part) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int L = blockIdx.x;
+    const int per = gridDim.x >> 3;
+    const int item = (L & 7) * per + (L >> 3);
+    if (item >= n_items) return;
+    const int S = S_main + S_win;
+    const int hp = item % pairs;
+    const int rest = item / pairs;
+    const int split = rest % S;
+    const int b = rest / S;
+    if (split < S_main) {
+        const int64_t first = (int64_t)split * rps;
+        const int n = (int)((a.k - first < rps) ? a.k - first : rps);
+        decode_split_pair<DQK>(a, smem, b, split, S, hp, false, first, n, o_part, lse_part);
+    } else {
+        const int64_t first = (int64_t)(split - S_main) * rps_win;
+        const int wl = (int)clamp_visible(a.win_len[b], a.W);
+        int n = (int)(wl - first);
+        n = n < 0 ? 0 : (n > rps_win ? rps_win : n);
+        decode_split_pair<DQK>(a, smem, b, split, S, hp, true, first, n, o_part, lse_part);
+    }
+}
+
 template <int SRC_MAIN, int DQK>
 __global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int S_win, int rps, int rps_win,
                                                   int groups, int n_items, float* o_part, float* lse_part) {
@@ -800,6 +1013,32 @@ static hipError_t launch_gather(const DecodeArgs& a, const Geometry& g, float* o
                          g.rps_win, g.groups, n_items, o_part, lse_part);
 }
 
+template <int DQK>
+static hipError_t launch_pair(const DecodeArgs& a, const Geometry& g, float* o_part, float* lse_part,
+                              hipStream_t stream) {
+    const int S = g.S_main + g.S_win;
+    const int pairs = a.H / 32;
+    const int n_items = a.B * S * pairs;
+    const int grid = (n_items + 7) / 8 * 8;
+    auto kern = k_decode_pair<DQK>;
+    static bool attr_set = false;                          // dynamic LDS above 64 KiB, once per kernel
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, gd2::kBytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const ProfSlot p = prof_slot(PROF_DECODE);
+    return launch_kernel(kern, dim3(grid), dim3(512), gd2::kBytes, stream, p.start, p.stop, a, g.S_main, g.S_win,
+                         g.rps, g.rps_win, pairs, n_items, o_part, lse_part);
+}
+
+// Two head tiles per workgroup for bf16 rows when one head tile per workgroup would
+// take more than one round of the CUs: each row is then staged once per 32 heads.
+static bool use_pairs(int fmt, int B, int H, const Geometry& g) {
+    return fmt == MLA_FMT_BF16 && H % 32 == 0 && (int64_t)B * (g.S_main + g.S_win) * g.groups > 256;
+}
+
 // An MXFP8 window ring [B, W, D + D/32 bytes] widened to bf16 rows [B, W, D]:
 // the E4M3 value times its block's power of two, formed in fp32 (exact) and
 // rounded to bf16, exact unless the product lies below bf16's smallest
@@ -818,7 +1057,10 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
     // MXFP8 window entries of 512 channels (16-byte aligned) are widened inside the gather
     // decode's staging; others are first widened to a bf16 copy after the decode's own workspace
     const bool mfma = mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H);
-    const bool win8_inline = a.win8 && mfma && a.dim + a.rope == 512 && reinterpret_cast<uintptr_t>(a.win8) % 16 == 0;
+    const Geometry g = gather_geometry(a.fmt, a.B, a.H, a.k, (a.win || a.win8) ? a.W : 0);
+    const bool pairs = mfma && use_pairs(a.fmt, a.B, a.H, g);
+    const bool win8_inline = a.win8 && mfma && !pairs && a.dim + a.rope == 512 &&
+                             reinterpret_cast<uintptr_t>(a.win8) % 16 == 0;
     if (a.win8 && a.W > 0 && !win8_inline) {
         const size_t base = decode_workspace_bytes(a.fmt, a.dim, a.rope, a.d_v, a.B, a.H, a.k, a.W);
         uint16_t* wide = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + base);
@@ -832,7 +1074,6 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
         const ProfSlot p = prof_slot(PROF_DECODE);
         return launch_kernel(k_decode_generic, dim3(a.H, a.B), dim3(kGenericThreads), 0, stream, p.start, p.stop, a);
     }
-    const Geometry g = gather_geometry(a.fmt, a.B, a.H, a.k, (a.win || a.win8) ? a.W : 0);
     const int S = g.S_main + g.S_win;
     const size_t o_bytes = (((size_t)a.B * S * a.H * kDv * sizeof(float)) + 255) & ~(size_t)255;
     float* o_part = reinterpret_cast<float*>(a.workspace);
@@ -841,6 +1082,8 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
         hipError_t e = hipSuccess;
         if (a.fmt == MLA_FMT_E4M3_S128) e = launch_gather<SRC_E4M3, 576>(a, g, o_part, lse_part, stream);
         else if (a.fmt == MLA_FMT_E2M1_S16) e = launch_gather<SRC_FP4, 512>(a, g, o_part, lse_part, stream);
+        else if (pairs) e = a.rope == 64 ? launch_pair<576>(a, g, o_part, lse_part, stream)
+                                         : launch_pair<512>(a, g, o_part, lse_part, stream);
         else if (a.rope == 64) e = launch_gather<SRC_BF16, 576>(a, g, o_part, lse_part, stream);
         else e = launch_gather<SRC_BF16, 512>(a, g, o_part, lse_part, stream);
         if (e != hipSuccess) return e;

@@ -473,6 +473,33 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_append_sparse_decode -- the step's window entry appended, then the decode, in
+ * one call ([P1] "DeepSeek-V4", "A window in every layer": every layer writes the
+ * step's own entry into its window, then attends over the window and its selected
+ * rows; [P1] "DeepSeek-V4.1", "Three modes": a Reuse layer's step is exactly this).
+ *
+ * Exactly mla_kv_append_quant(window entry only: new_win, win_pos, win_ring, W, Dw =
+ * dim + rope, win_fmt) followed by mla_sparse_decode with the same ring, on the same
+ * stream: afterwards the ring holds the entry's bytes in slot win_pos[b] mod W
+ * (win_pos[b] < 0: sequence b appends nothing), and the decode attends over them.
+ * With 512-channel bf16 or MXFP8 entries (16-byte aligned ring and new_win) on the
+ * gather decode, the decode's window split writes the entry itself and stages it from
+ * new_win, with no launch of its own; otherwise the append is launched first.
+ *  new_win   fp32 [B, dim + rope], device
+ *  win_pos   int32 [B] positions, device
+ *  win_ring  the ring, writable; the other arguments, the workspace and the errors as
+ *            for mla_sparse_decode (win_ring, win_len and W > 0 are required).
+ */
+mla_status_t mla_append_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q,
+                                      const void* main_cache, int64_t main_seq_stride, int64_t capacity,
+                                      const int32_t* idx, int32_t k, const float* new_win,
+                                      const int32_t* win_pos, void* win_ring, const int32_t* win_len,
+                                      int32_t W, int32_t win_fmt, float softmax_scale,
+                                      const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H,
+                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * mla_sparse_decode_noalloc -- mla_sparse_decode with the library's own scratch.
  *
  * For callers that cannot allocate device memory (code under HIP graph capture,

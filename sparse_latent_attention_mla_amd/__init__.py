@@ -84,6 +84,9 @@ def lib():
         L.mla_sparse_decode_noalloc.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, i32, i32, f32, P, i32,
                                                 i32, P, P, P]
         L.mla_sparse_decode_noalloc.restype = i32
+        L.mla_append_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, P, P, i32, i32, f32, P, i32,
+                                               i32, P, P, P, sz, P]
+        L.mla_append_sparse_decode.restype = i32
         _lib = L
     return _lib
 
@@ -457,18 +460,31 @@ def _decode_args(main_row, d_v, q, main_cache, idx, softmax_scale, out, lse, win
 
 
 def mla_sparse_decode(main_row: Row, d_v: int, q, main_cache, idx, softmax_scale: float, out, lse,
-                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None, rope_cs=None):
+                      workspace=None, win_ring=None, win_len=None, stream=None, sinks=None, rope_cs=None,
+                      new_win=None, win_pos=None):
     """Sparse absorbed-MLA decode.  q [B, H, D] (bf16; fp32 for F32 rows), main_cache uint8
     [B, capacity, row_bytes], idx int32 [B, k], out fp32 [B, H, d_v], lse fp32 [B, H];
     win_ring bf16 [B, W, D] and win_len int32 [B] for the window branch; sinks fp32 [H]
     attention-sink logits (optional); rope_cs fp32 [B, r/2, 2] (cos, sin) un-rotating the
-    trailing r output channels (optional)."""
+    trailing r output channels (optional). With new_win fp32 [B, D] and win_pos int32 [B]
+    the step's window entry is appended to the ring first, in the same call
+    (mla_append_sparse_decode)."""
     args, keep = _decode_args(main_row, d_v, q, main_cache, idx, softmax_scale, out, lse, win_ring, win_len, sinks,
                               rope_cs)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    _check(lib().mla_sparse_decode(*args, _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                                   _stream(stream)))
+    ws = (_ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
+    if new_win is None:
+        _check(lib().mla_sparse_decode(*args, *ws))
+    else:
+        B, D = q.shape[0], q.shape[2]
+        if win_ring is None:
+            raise ValueError("new_win needs win_ring")
+        _need(new_win, "new_win", torch.float32, 2)
+        _need(win_pos, "win_pos", torch.int32, 1)
+        if tuple(new_win.shape) != (B, D) or tuple(win_pos.shape) != (B,):
+            raise ValueError("new_win [B, D] and win_pos [B] expected")
+        _check(lib().mla_append_sparse_decode(*args[:8], _ptr(new_win), _ptr(win_pos), *args[8:], *ws))
     del keep
 
 
@@ -529,8 +545,6 @@ def csa2_group_step(main_row: Row, idx_row: Row, modes, main_cache, idx_cache, n
                                         out_scores=pool[2] if (pool is not None and mode == "full") else None,
                                         score_bf16=score_bf16, stream=stream)
             else:
-                if win[0] is not None:
-                    mla_kv_append_quant(main_row, idx_row, None, None, None, None, None, *win, stream=stream)
                 use_pool = pool is not None and mode == "reindex"
                 mla_indexer_topk(idx_row, q_idx[j], w[j], score_scale, idx_cache, n_visible, k, latest,
                                  topk_workspace, out_scores=pool[2] if (pool is not None and mode == "full") else None,
@@ -539,13 +553,13 @@ def csa2_group_step(main_row: Row, idx_row: Row, modes, main_cache, idx_cache, n
                 mla_indexer_pool(pool[2], n_visible, pool[0], pool[3], topk_workspace, block=pool[1],
                                  stream=stream)
             j += 1
-        else:
-            if latest is None:
-                raise ValueError("a reuse layer needs a preceding full or reindex layer")
-            if win[0] is not None:
-                mla_kv_append_quant(main_row, idx_row, None, None, None, None, None, *win, stream=stream)
+        elif latest is None:
+            raise ValueError("a reuse layer needs a preceding full or reindex layer")
+        # layers after the first append their window entry in the decode's call
+        fused_win = l > 0 and win[0] is not None
         mla_sparse_decode(main_row, out.shape[-1], q[l], main_cache, latest, softmax_scale, out[l], lse[l],
                           decode_workspace, win_rings[l] if win_rings is not None else None,
-                          win_len if win_rings is not None else None, stream=stream)
+                          win_len if win_rings is not None else None, stream=stream,
+                          new_win=win[0] if fused_win else None, win_pos=win[1] if fused_win else None)
         attended.append(latest)
     return attended

@@ -320,7 +320,7 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
     return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
 }
 
-int32_t mla_version(void) { return 103; }
+int32_t mla_version(void) { return 104; }
 
 mla_status_t mla_set_option(const char* name, int64_t value) {
     if (!name) return fail(MLA_ERR_INVALID_ARG, "mla_set_option: NULL name");
@@ -552,14 +552,12 @@ size_t mla_sparse_decode_workspace(mla_row_t main_row, int32_t d_v, int32_t B, i
            window_copy_bytes(win_fmt, B, W, main_row.dim + main_row.rope_dim);
 }
 
-mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
-                               int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
-                               const void* win_ring, const int32_t* win_len, int32_t W, int32_t win_fmt,
-                               float softmax_scale,
-                               const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
-                               void* workspace,
-                               size_t workspace_bytes, void* stream) {
-    mla::begin_call();
+static mla_status_t decode_impl(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
+                                int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
+                                const float* new_win, const int32_t* win_pos, const void* win_ring,
+                                const int32_t* win_len, int32_t W, int32_t win_fmt, float softmax_scale,
+                                const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || H < 1 || k < 0 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need B >= 0, H >= 1, k >= 0, capacity >= 0");
     const int D = main_row.dim + main_row.rope_dim;
@@ -622,7 +620,52 @@ mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, c
     a.lse = lse;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
-    return hip_status(mla::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse decode");
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (new_win) {                                         // the step's window entry first
+        a.new_win = new_win;
+        a.win_pos = win_pos;
+        if (!mla::decode_fuses_window_append(a)) {
+            mla::AppendArgs ap{};
+            const mla_status_t sa = append_args(main_row, mla_row_t{MLA_FMT_F32, 0, 0}, nullptr, nullptr, nullptr, B,
+                                                0, capacity, nullptr, 0, nullptr, 0, new_win, win_pos,
+                                                const_cast<void*>(win_ring), W, D, win_fmt, &ap);
+            if (sa != MLA_OK) return sa;
+            const hipError_t e = mla::launch_append(ap, st);
+            if (e != hipSuccess) return hip_status(e, "window append launch");
+            a.new_win = nullptr;
+            a.win_pos = nullptr;
+        }
+    }
+    return hip_status(mla::launch_decode(a, st), "sparse decode");
+}
+
+mla_status_t mla_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
+                               int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
+                               const void* win_ring, const int32_t* win_len, int32_t W, int32_t win_fmt,
+                               float softmax_scale,
+                               const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
+                               void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    mla::begin_call();
+    return decode_impl(main_row, d_v, q, main_cache, main_seq_stride, capacity, idx, k, nullptr, nullptr, win_ring,
+                       win_len, W, win_fmt, softmax_scale, epilogue, B, H, out, lse, workspace, workspace_bytes,
+                       stream);
+}
+
+mla_status_t mla_append_sparse_decode(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,
+                                      int64_t main_seq_stride, int64_t capacity, const int32_t* idx, int32_t k,
+                                      const float* new_win, const int32_t* win_pos, void* win_ring,
+                                      const int32_t* win_len, int32_t W, int32_t win_fmt, float softmax_scale,
+                                      const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out,
+                                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    mla::begin_call();
+    if (!new_win || !win_pos || !win_ring)
+        return fail(MLA_ERR_INVALID_ARG, "append_sparse_decode: needs new_win, win_pos and win_ring");
+    if (!aligned(new_win, 4) || !aligned(win_pos, 4))
+        return fail(MLA_ERR_INVALID_ARG, "append_sparse_decode: misaligned new_win or win_pos");
+    return decode_impl(main_row, d_v, q, main_cache, main_seq_stride, capacity, idx, k, new_win, win_pos, win_ring,
+                       win_len, W, win_fmt, softmax_scale, epilogue, B, H, out, lse, workspace, workspace_bytes,
+                       stream);
 }
 
 mla_status_t mla_sparse_decode_noalloc(mla_row_t main_row, int32_t d_v, const void* q, const void* main_cache,

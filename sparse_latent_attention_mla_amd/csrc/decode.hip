@@ -127,7 +127,8 @@ constexpr int lds_bytes() {
 
 template <int SRC, int DQK, int R>
 __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
-                                               bool is_win, int64_t first, int n, float* o_part, float* lse_part) {
+                                               bool is_win, int64_t first, int n, int span, float* o_part,
+                                               float* lse_part) {
     using L = gd::Lay<SRC, R>;
     constexpr int VS = gd::VRow<SRC>::kStride;
     constexpr int NT = (R / 16 + 7) / 8;                   // row tiles per wave (waves w < R / 16 have them)
@@ -149,6 +150,20 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
                               : is_win       ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
                                              : a.cache + b * a.stride;
     const uint32_t row_bytes = SRC == SRC_MX8 ? kMx8Bytes : is_win ? 2 * DQK : (uint32_t)a.row_bytes;
+
+    // the step's window entry, when its ring slot lies in this window split's span of slots:
+    // row u_new of the split is staged from it (attended when u_new < n) and, by head group
+    // 0, written into the ring, instead of read
+    int u_new = -1;
+    int64_t s_new = 0;
+    f32x4 nw0 = f32x4{0.f, 0.f, 0.f, 0.f}, nw1 = nw0;     // bf16 windows: this lane's 8 channels of the entry
+    if constexpr ((SRC == SRC_BF16 || SRC == SRC_MX8) && DQK == 512) {
+        if (is_win && a.new_win) {
+            const int64_t pos = a.win_pos[b];
+            s_new = pos >= 0 ? pos % a.W : -1;
+            if (s_new >= first && s_new < first + span) u_new = (int)(s_new - first);
+        }
+    }
 
     // ---- row indices (-1: no row) and the 16 heads' queries
     if (tid < R) {
@@ -210,11 +225,18 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
     } else if constexpr (SRC == SRC_BF16) {
         constexpr int PW = R / 8;                          // one row per load instruction
         const int rot = (hg & 7) * (R / 8);                // (a multiple of 8: a wave keeps its rows)
+        if constexpr (DQK == 512) {                        // the wave whose rows hold u_new loads the entry now
+            if (u_new >= 0 && (u_new & 7) == w) {
+                const float* src = a.new_win + (int64_t)b * DQK + 8 * lane;
+                nw0 = *reinterpret_cast<const f32x4*>(src);
+                nw1 = *reinterpret_cast<const f32x4*>(src + 4);
+            }
+        }
 #pragma unroll 4
         for (int i = 0; i < PW; ++i) {
             if (i == (PW + 7) / 8) wait_vmcnt<0>();       // the group's own eighth first (as above)
             const int u = (w + 8 * i + rot) % R;
-            const int32_t r = ridx[u];
+            const int32_t r = u == u_new ? -1 : ridx[u];   // (the new entry's row: a stand-in, then overwritten)
             zmask |= r < 0 ? (1u << i) : 0u;
             const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * lane
                                         : reinterpret_cast<const uint8_t*>(a.q);
@@ -227,6 +249,14 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         constexpr int kPer = R * 16 / 512;
         u32x4 c0[kPer], c1[kPer];
         uint32_t scb[kPer];
+        // the wave that stages the new entry's row (16 threads of it) quantises the whole
+        // entry afterwards, 8 channels per lane, and writes it over that row: load them now
+        const int w_new = u_new >= 0 ? ((16 * u_new) & 511) >> 6 : -1;
+        if (w == w_new) {
+            const float* src = a.new_win + (int64_t)b * DQK + 8 * lane;
+            nw0 = *reinterpret_cast<const f32x4*>(src);
+            nw1 = *reinterpret_cast<const f32x4*>(src + 4);
+        }
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int item = tid + 512 * i, u = item >> 4, pc = item & 15;
@@ -253,6 +283,31 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false)),
                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true))};
                 }
+            }
+        }
+        if (w == w_new) {                                  // the entry, quantised as the append quantises it
+            const float x[8] = {nw0[0], nw0[1], nw0[2], nw0[3], nw1[0], nw1[1], nw1[2], nw1[3]};
+            uint32_t m = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = max(m, f2u(fabsf(x[e])));
+            m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));           // the 4 lanes of a 32-channel block
+            m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+            const uint32_t code = mx8_code(m);
+            const int sh = 127 - (int)code;
+            uint32_t wd[2] = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                wd[e >> 2] |= (m == 0u ? 0u : e4m3_encode(__builtin_ldexpf(x[e], sh))) << (8 * (e & 3));
+            const float sc = u2f(code << 23);
+            *reinterpret_cast<u32x4*>(V + u_new * VS + 16 * lane) = u32x4{
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[0], sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[0], sc, true)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[1], sc, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[1], sc, true))};
+            if (hg == 0) {
+                uint8_t* ent = const_cast<uint8_t*>(a.win8) + ((int64_t)b * a.W + s_new) * kMx8Bytes;
+                *reinterpret_cast<u32x2*>(ent + 8 * lane) = u32x2{wd[0], wd[1]};
+                if ((lane & 3) == 0) ent[DQK + (lane >> 2)] = (uint8_t)code;
             }
         }
     } else {                                               // E2M1 rows: 16 pieces of 32 channels per row
@@ -315,6 +370,15 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
             for (int i = 0; i < R / 8; ++i)
                 if ((zmask >> i) & 1u)
                     *reinterpret_cast<u32x4*>(V + VS * ((w + 8 * i + rot) % R) + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        }
+        if constexpr (DQK == 512) {
+            if (u_new >= 0 && (u_new & 7) == w) {          // the step's entry, rounded to bf16 as the append does
+                const u32x4 v = u32x4{bf16_rne(nw0[0]) | (bf16_rne(nw0[1]) << 16), bf16_rne(nw0[2]) | (bf16_rne(nw0[3]) << 16),
+                                      bf16_rne(nw1[0]) | (bf16_rne(nw1[1]) << 16), bf16_rne(nw1[2]) | (bf16_rne(nw1[3]) << 16)};
+                *reinterpret_cast<u32x4*>(V + VS * u_new + 16 * lane) = v;
+                if (hg == 0)
+                    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(a.win) + ((int64_t)b * a.W + s_new) * DQK + 8 * lane) = v;
+            }
         }
     }
     __syncthreads();
@@ -674,7 +738,7 @@ __global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int 
     if (split < S_main) {
         const int64_t first = (int64_t)split * rps;
         const int n = (int)((a.k - first < rps) ? a.k - first : rps);
-        decode_split_g<SRC_MAIN, DQK, RM>(a, smem, b, split, S, hg, false, first, n, o_part, lse_part);
+        decode_split_g<SRC_MAIN, DQK, RM>(a, smem, b, split, S, hg, false, first, n, rps, o_part, lse_part);
     } else {
         const int64_t first = (int64_t)(split - S_main) * rps_win;
         const int wl = (int)clamp_visible(a.win_len[b], a.W);
@@ -682,11 +746,12 @@ __global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int 
         n = n < 0 ? 0 : (n > rps_win ? rps_win : n);
         if constexpr (DQK == 512) {
             if (a.win8) {                                  // MXFP8 entries, widened as they are staged
-                decode_split_g<SRC_MX8, DQK, 128>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+                decode_split_g<SRC_MX8, DQK, 128>(a, smem, b, split, S, hg, true, first, n, rps_win, o_part,
+                                                  lse_part);
                 return;
             }
         }
-        decode_split_g<SRC_BF16, DQK, 128>(a, smem, b, split, S, hg, true, first, n, o_part, lse_part);
+        decode_split_g<SRC_BF16, DQK, 128>(a, smem, b, split, S, hg, true, first, n, rps_win, o_part, lse_part);
     }
 }
 
@@ -1049,6 +1114,14 @@ __global__ __launch_bounds__(256) void k_widen_window(const uint8_t* __restrict_
     const uint8_t* src = ring + row * (D + D / 32);
     for (int c = threadIdx.x; c < D; c += 256)
         out[row * D + c] = (uint16_t)bf16_rne(e4m3_to_f32(src[c]) * e8m0_to_f32(src[D + c / 32]));
+}
+
+bool decode_fuses_window_append(const DecodeArgs& a) {
+    if (!a.new_win || !a.win_pos || a.W <= 0 || (!a.win && !a.win8) || a.B <= 0) return false;
+    if (!mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H) || a.dim + a.rope != 512) return false;
+    if (reinterpret_cast<uintptr_t>(a.new_win) % 16 != 0) return false;
+    if (use_pairs(a.fmt, a.B, a.H, gather_geometry(a.fmt, a.B, a.H, a.k, a.W))) return false;
+    return reinterpret_cast<uintptr_t>(a.win8 ? static_cast<const void*>(a.win8) : a.win) % 16 == 0;
 }
 
 hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {

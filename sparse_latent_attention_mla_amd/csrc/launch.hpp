@@ -140,6 +140,8 @@ struct DecodeArgs {
     const uint8_t* win8;    // or [B, W, D + D/32] MXFP8 entries (widened into the workspace first)
     const int32_t* win_len;
     int W;
+    const float* new_win;   // [B, dim+rope] fp32: the step's window entry, written into ring slot
+    const int32_t* win_pos; // win_pos[b] mod W by the decode itself (null: the ring is as given)
     float scale;
     const float* sinks;     // [H] attention-sink logits, or null
     int rope_dim;           // trailing output channels un-rotated (0: none)
@@ -196,5 +198,8 @@ hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint3
 }
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Whether launch_decode writes a.new_win into the window ring itself (512-channel bf16 or
+// MXFP8 entries on the gather decode); otherwise the caller appends it first.
+bool decode_fuses_window_append(const DecodeArgs& a);
 
 }  // namespace mla

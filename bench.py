@@ -92,31 +92,32 @@ def build_layers(cfg, n_layers, seed=0):
         X.main = torch.empty((B, N, M.row_bytes(mr)), dtype=torch.uint8, device=dev)
         X.idx = torch.empty((B, N, M.row_bytes(ir)), dtype=torch.uint8, device=dev)
         slots_all = torch.arange(N, dtype=torch.int32, device=dev).expand(B, N).contiguous()
-        chunk = max(1, (1 << 26) // (N * D))          # sequences per generation chunk
-        for b0 in range(0, B, chunk):
-            b1 = min(B, b0 + chunk)
-            # positions of sequences b0..b1 in the [B, N(, m), D] streams
-            if cfg.m == 1:
+        if cfg.m == 1:
+            chunk = max(1, (1 << 26) // (N * D))      # sequences per generation chunk
+            for b0 in range(0, B, chunk):
+                b1 = min(B, b0 + chunk)
+                # positions of sequences b0..b1 in the [B, N, D] streams
                 main = WL.normal(seed, cfg.cid, WL.T_MAIN + off, (b1 - b0, N, D), offset=b0 * N * D)
                 idx = WL.normal(seed, cfg.cid, WL.T_IDX + off, (b1 - b0, N, cfg.d_I), offset=b0 * N * cfg.d_I)
-            else:
-                tok = WL.normal(seed, cfg.cid, WL.T_MAIN + off, (b1 - b0, N, cfg.m, D), offset=b0 * N * cfg.m * D)
-                main = tok[:, :, 0].copy()
-                for jj in range(1, cfg.m):
-                    main += tok[:, :, jj]
-                main *= np.float32(1.0 / cfg.m)
-                del tok
-                tok = WL.normal(seed, cfg.cid, WL.T_IDX + off, (b1 - b0, N, cfg.m, cfg.d_I),
-                                offset=b0 * N * cfg.m * cfg.d_I)
-                idx = tok[:, :, 0].copy()
-                for jj in range(1, cfg.m):
-                    idx += tok[:, :, jj]
-                idx *= np.float32(1.0 / cfg.m)
-                del tok
-            M.mla_kv_append_quant(mr, ir, torch.from_numpy(np.ascontiguousarray(main)).to(dev),
-                                  torch.from_numpy(np.ascontiguousarray(idx)).to(dev),
-                                  slots_all[b0:b1].contiguous(), X.main[b0:b1], X.idx[b0:b1])
-            del main, idx
+                M.mla_kv_append_quant(mr, ir, torch.from_numpy(main).to(dev), torch.from_numpy(idx).to(dev),
+                                      slots_all[b0:b1].contiguous(), X.main[b0:b1], X.idx[b0:b1])
+                del main, idx
+        else:
+            # m tokens per entry: each entry pooled by the CSA2 compressor on the GPU (unit norm
+            # weight, no rotation) straight into its row; the indexer key appended on its own
+            slot0 = torch.zeros(N, dtype=torch.int32, device=dev)    # each entry is its own one-row "sequence"
+            ce = 1 << 15
+            for b in range(B):
+                for n0 in range(0, N, ce):
+                    n1 = min(N, n0 + ce)
+                    kv, gate = WL.compressor_tokens(cfg, seed, b, n0, n1, tensor_offset=off)
+                    M.mla_compress_append(mr, torch.from_numpy(kv).to(dev), torch.from_numpy(gate).to(dev),
+                                          X.main[b, n0:n1].unsqueeze(1), slot0[:n1 - n0], None, 1e-6)
+                    del kv, gate
+                idx = WL.normal(seed, cfg.cid, WL.T_IDX + off, (1, N, cfg.d_I), offset=b * N * cfg.d_I)
+                M.mla_kv_append_quant(mr, ir, None, torch.from_numpy(idx).to(dev), slots_all[b:b + 1].contiguous(),
+                                      None, X.idx[b:b + 1])
+                del idx
         # the entry appended by each step (position N-1), and the step's queries
         X.new_main = torch.from_numpy(WL.normal(seed, cfg.cid, 100 + off, (B, 1, D))).to(dev)
         X.new_idx = torch.from_numpy(WL.normal(seed, cfg.cid, 101 + off, (B, 1, cfg.d_I))).to(dev)

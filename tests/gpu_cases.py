@@ -60,11 +60,31 @@ class Case:
         return np.full(self.cfg.B, self.cfg.N, np.int32)
 
 
+COMPRESS_EPS = 1e-6
+
+
+def pooled_inputs(cfg: WL.Config, seed: int = 0) -> WL.StepInputs:
+    """The step inputs, with m > 1 the main entries pooled from the workload's tokens by the
+    oracle's CSA2 compressor (unit norm weight, no rotation); both sides then append the
+    same fp32 entries."""
+    inp = WL.step_inputs(cfg, seed)
+    if inp.main is not None:
+        return inp
+    main = np.empty((cfg.B, cfg.N, cfg.D), np.float32)
+    chunk = 16384
+    for b in range(cfg.B):
+        for n0 in range(0, cfg.N, chunk):
+            n1 = min(cfg.N, n0 + chunk)
+            kv, gate = WL.compressor_tokens(cfg, seed, b, n0, n1)
+            main[b, n0:n1] = O.compress(kv, gate, None, COMPRESS_EPS)
+    return dataclasses.replace(inp, main=main)
+
+
 def build_case(cfg: WL.Config, seed: int = 0) -> Case:
     """Caches hold positions 0..N-2 (bulk append), then the step appends
     position N-1 (n_new = 1) on each side; window rings hold the W most recent
     window entries, the last one written by the step's append."""
-    inp = WL.step_inputs(cfg, seed)
+    inp = pooled_inputs(cfg, seed)
     B, N, D = cfg.B, cfg.N, cfg.D
     mr, ir = main_row(cfg), idx_row(cfg)
     rb, rbi = O.row_bytes(cfg.main_fmt, cfg.dim, cfg.rope), O.row_bytes(cfg.idx_fmt, cfg.d_I, 0)

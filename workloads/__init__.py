@@ -29,6 +29,7 @@ LIB = os.path.join(HERE, "libsynth.so")
 
 # tensor ids of the generator streams
 T_MAIN, T_IDX, T_Q, T_QIDX, T_W, T_WIN = 1, 2, 3, 4, 5, 6
+T_GATE = 7            # gate logits of the CSA2 compressor's tokens
 
 # row formats (numbering used by the library and the oracle alike)
 F32, BF16, E4M3_S128, E2M1_S16, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
@@ -161,7 +162,8 @@ CONFIGS = {
 class StepInputs:
     """fp32 inputs of one decode step (layer group) of a configuration."""
     cfg: Config
-    main: np.ndarray      # [B, N, D]   entry vectors of positions 0..N-1 (last one is appended)
+    main: np.ndarray      # [B, N, D]   entry vectors of positions 0..N-1 (last one is appended);
+                          #             None when m > 1 (pooled by the compressor, see compressor_tokens)
     idx: np.ndarray       # [B, N, d_I] indexer keys
     q: np.ndarray         # [L, B, H, D]      (bf16-rounded unless fp32 config)
     q_idx: np.ndarray     # [L_I, B, H_I, d_I] (bf16-rounded unless fp32 config)
@@ -181,23 +183,10 @@ def step_inputs(cfg: Config, seed: int = 0) -> StepInputs:
     B, N, D, L = cfg.B, cfg.N, cfg.D, len(cfg.layers)
     LI = n_indexers(cfg)
     cid = cfg.cid
-    if cfg.m == 1:
-        main = normal(seed, cid, T_MAIN, (B, N, D))
-        idx = normal(seed, cid, T_IDX, (B, N, cfg.d_I))
-    else:
-        # tokens, then fp32 mean of each run of m consecutive tokens
-        tok = normal(seed, cid, T_MAIN, (B, N, cfg.m, D))
-        main = tok[:, :, 0, :].copy()
-        for j in range(1, cfg.m):
-            main += tok[:, :, j, :]
-        main *= np.float32(1.0 / cfg.m)
-        del tok
-        tok = normal(seed, cid, T_IDX, (B, N, cfg.m, cfg.d_I))
-        idx = tok[:, :, 0, :].copy()
-        for j in range(1, cfg.m):
-            idx += tok[:, :, j, :]
-        idx *= np.float32(1.0 / cfg.m)
-        del tok
+    # with m > 1 tokens per entry the main entries come from the CSA2 compressor over
+    # compressor_tokens(); the caller pools them (main is None here)
+    main = normal(seed, cid, T_MAIN, (B, N, D)) if cfg.m == 1 else None
+    idx = normal(seed, cid, T_IDX, (B, N, cfg.d_I))
     lowp = cfg.main_fmt != F32
     q = normal(seed, cid, T_Q, (L, B, cfg.H, D))
     q_idx = normal(seed, cid, T_QIDX, (LI, B, cfg.H_I, cfg.d_I))
@@ -207,6 +196,16 @@ def step_inputs(cfg: Config, seed: int = 0) -> StepInputs:
     w = normal(seed, cid, T_W, (LI, B, cfg.H_I)) * np.float32(cfg.w_scale)
     win = normal(seed, cid, T_WIN, (L, B, cfg.W, D)) if cfg.W else None
     return StepInputs(cfg, main, idx, q, q_idx, w.astype(np.float32), win)
+
+
+def compressor_tokens(cfg: Config, seed: int, b: int, n0: int, n1: int, tensor_offset: int = 0):
+    """The compressor inputs of entries n0 .. n1-1 of sequence b: kv and gate logits fp32
+    [n1 - n0, m, D], i.i.d. N(0, 1), m tokens per entry."""
+    D, m, N = cfg.D, cfg.m, cfg.N
+    off = (b * N + n0) * m * D
+    kv = normal(seed, cfg.cid, T_MAIN + tensor_offset, (n1 - n0, m, D), offset=off)
+    gate = normal(seed, cfg.cid, T_GATE + tensor_offset, (n1 - n0, m, D), offset=off)
+    return kv, gate
 
 
 def window_entry_bytes(cfg: Config, win_fmt: int = BF16) -> int:

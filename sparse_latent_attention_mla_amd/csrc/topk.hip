@@ -753,15 +753,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select_final(const int32_t* __r
 constexpr int kF2Threads = 1024;
 constexpr int kF2Waves = kF2Threads / 64;
 constexpr int kF2MaxGroups = 1024;
-constexpr int kF2Spec = 4;                // workgroups per wave whose first 64 entries load early
+constexpr int kF2Spec = 8;                // workgroups per wave whose first 64 entries load early (flat final)
 constexpr int kF2Flat = 4;                // rest entries per thread per batch
 constexpr int kSpecGroups = kF2Waves * kF2Spec;
-// The final for up to kSpecGroups (64) select workgroups, where every list's
+// The final for up to 16 SPEC select workgroups (SPEC = 4 or 8), where every list's
 // first 64 entries are loaded speculatively: wave w places the lists of
-// workgroups w, w + 16, w + 32, w + 48 (the counts are loaded first, and the
+// workgroups w, w + 16, .., w + 16 (SPEC - 1) (the counts are loaded first, and the
 // prefix sums wait only for them); entries past the first 64 of a list, which
 // the selections here rarely have, are placed afterwards, 64 at a time.
-template <bool EXPAND>
+template <bool EXPAND, int SPEC>
 __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __restrict__ n_visible, int k,
                                                               int64_t capacity, int groups, TopkWorkspace ws,
                                                               int32_t* __restrict__ out_idx, SelectMap map) {
@@ -785,10 +785,10 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     const uint32_t csum = (t < 64) ? coarse_sum_of_lane(ws.hist + (int64_t)b * kHistWordsHost) : 0u;
     const bool has_cnt = t < groups;
     const u32x2 c2 = *reinterpret_cast<const u32x2*>(ws.counts + ((int64_t)b * groups + (has_cnt ? t : 0)) * 2);
-    int32_t vs[kF2Spec];
-    uint64_t vc[kF2Spec];
+    int32_t vs[SPEC];
+    uint64_t vc[SPEC];
 #pragma unroll
-    for (int u = 0; u < kF2Spec; ++u) {
+    for (int u = 0; u < SPEC; ++u) {
         const int j = wv + kF2Waves * u;
         const int64_t off = (int64_t)j * kSelRows + lane;
         const bool ok = j < groups && off < capacity;
@@ -806,7 +806,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
         wtot[wv][0] = is;
         wtot[wv][1] = ic;
     }
-    if (t == 0) has_rest = groups > kSpecGroups ? 1u : 0u;
+    if (t == 0) has_rest = groups > (kF2Waves * SPEC) ? 1u : 0u;
     lds_barrier();
     uint32_t bs = 0, bc = 0, nsel = 0, ncand = 0;
 #pragma unroll
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
         else gc2[o] = v;                                   // o < capacity: every row is in at most one list
     };
 #pragma unroll
-    for (int u = 0; u < kF2Spec; ++u) {
+    for (int u = 0; u < SPEC; ++u) {
         const int j = wv + kF2Waves * u;
         if (j < groups) {
             if ((uint32_t)lane < g_cnt[j][0]) place_sel(j, lane, vs[u]);
@@ -851,7 +851,7 @@ __global__ __launch_bounds__(kF2Threads) void k_select_final2(const int32_t* __r
     // stores, would wait for them)
     if (has_rest) {
         for (int j = wv; j < groups; j += kF2Waves) {
-            const uint32_t i0 = (j < wv + kF2Waves * kF2Spec) ? 64u : 0u;
+            const uint32_t i0 = (j < wv + kF2Waves * SPEC) ? 64u : 0u;
             const uint32_t ns = g_cnt[j][0], nc = g_cnt[j][1];
             for (uint32_t i = i0 + lane; i < ns; i += 64) place_sel(j, i, gsel[(int64_t)j * kSelRows + i]);
             for (uint32_t i = i0 + lane; i < nc; i += 64) place_cnd(j, i, gcnd[(int64_t)j * kSelRows + i]);
@@ -1065,7 +1065,8 @@ hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n
     if (nx <= (unsigned)kF2MaxGroups && option(OPT_TOPK_FINAL) == 0)
         return launch_kernel(expand ? k_select_final2_flat<true>
                                     : (nx > (unsigned)kSpecGroups ? k_select_final2_flat<false>
-                                                                  : k_select_final2<false>),
+                                       : nx > (unsigned)(kF2Waves * 4) ? k_select_final2<false, 8>
+                                                                       : k_select_final2<false, 4>),
                              dim3(B), dim3(kF2Threads), 0, stream, nx > 0 ? nullptr : p.start,
                              p.stop, n_visible, k, capacity, (int)nx, ws, out_idx, map);
     return launch_kernel(expand ? k_select_final<true> : k_select_final<false>, dim3(B), dim3(kSelThreads), 0,

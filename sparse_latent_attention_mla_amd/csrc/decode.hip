@@ -194,6 +194,15 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         }
     }
     __syncthreads();
+    // B operands of the contraction (lane (head j, g): channels 32 s + 8 g .. of head j), read
+    // from LDS now so that the reads overlap the gather
+    constexpr int NQ = DQK / 32;                           // k-steps over the K width
+    u32x4 qv[NQ];
+    {
+        const uint8_t* qh = Q + j * gd::kQStride + 16 * g;
+#pragma unroll
+        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
+    }
 
     // ---- gather the value region; slots without a row load a stand-in and are zeroed once landed
     const uint32_t v_m0 = __builtin_amdgcn_readfirstlane(lds_addr(V));
@@ -384,13 +393,6 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
     __syncthreads();
 
     // ---- A: scores of the wave's row tiles; lane (head j, g) ends with rows 4 g .. 4 g + 3 of each tile
-    constexpr int NQ = DQK / 32;                           // k-steps over the K width
-    u32x4 qv[NQ];                                          // B operands: channels 32 s + 8 g .. of head j
-    {
-        const uint8_t* qh = Q + j * gd::kQStride + 16 * g;
-#pragma unroll
-        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
-    }
     float z[NT][4];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {

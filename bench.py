@@ -402,10 +402,11 @@ def run_config(args, cfg, n_layers, steps, warmup, headline):
         eager_ms = e0.elapsed_time(e1) / steps
 
     # roofline pass (outside the timed steps): whole eager steps with every indexer scan
-    # stamped from its own dispatch, two per rotated cache (at least 16 launches)
+    # stamped from its own dispatch: 96 steps, at least two per rotated cache, so that the
+    # first launches after the idle gap do not weigh on the average
     for name in M.PROFILE_KERNELS:
         M.mla_profile_read(name)          # discard anything recorded before
-    n_roof = max(16, 2 * n_layers)
+    n_roof = max(96, 2 * n_layers)
     M.mla_profile_enable(("indexer_scan",))
     for i in range(n_roof):
         step(layers[i % n_layers])

@@ -134,6 +134,9 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
     constexpr int NT = (R / 16 + 7) / 8;                   // row tiles per wave (waves w < R / 16 have them)
     constexpr bool kRope = DQK == 576;
     constexpr int NMAIN = 16;                              // k-steps of 32 channels in the value region
+    // E4M3 splits of 256 rows are gathered in two halves (rows 0 .. 127, then 128 .. 255), and
+    // the first row tile of every wave (in the first half) is contracted while the second lands
+    constexpr int NPART = (SRC == SRC_E4M3 && NT == 2 && R == 256) ? 2 : 1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, g = lane >> 4;
@@ -209,23 +212,25 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
     uint32_t zmask = 0;
     if constexpr (SRC == SRC_E4M3) {
         constexpr int NI = R * 33 / 64;                   // load instructions: 33 pieces per row, 64 per load
-        constexpr int PW = (NI + 7) / 8;
+        constexpr int NH = NI / NPART;                    // per part (a half: 66 loads = 128 rows)
+        constexpr int PW = (NH + 7) / 8;
+        static_assert(NH * NPART == NI && (NPART == 1 || (NH * 64) % 33 == 0), "parts of whole rows");
         // the head groups of a split (one XCD) gather the same rows: each starts at a different
-        // eighth of them, so that a row's first request (from HBM) is spread over the group and
-        // the others find it in L2
-        const int rot = ((hg & 7) * (NI / 8)) & ~7;
+        // eighth of each part, so that a row's first requests come from different head groups
+        // and the L2 merges the others into them; every load is issued at once (waiting for the
+        // group's own eighth before requesting the rest cost a memory round trip)
+        const int rot = ((hg & 7) * (NH / 8)) & ~7;
+#pragma unroll
+        for (int part = 0; part < NPART; ++part)
 #pragma unroll
         for (int i = 0; i < PW; ++i) {
-            // the group's own eighth first, landed before the rest is requested: by then the
-            // other head groups' eighths are in flight or in L2, not all eight missing at once
-            if (i == (PW + 7) / 8) wait_vmcnt<0>();
             int I = w + 8 * i;
-            if (I < NI) {
-                I = (I + rot) % NI;                        // (rot % 8 == 0: a wave's loads stay its own slots)
+            if (I < NH) {
+                I = part * NH + (I + rot) % NH;
                 const int P16 = 64 * I + lane;
                 const int u = P16 / 33, pc = P16 - 33 * u;
                 const int32_t r = ridx[u];
-                zmask |= r < 0 ? (1u << i) : 0u;
+                zmask |= r < 0 ? (1u << (part * PW + i)) : 0u;
                 const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * pc
                                             : reinterpret_cast<const uint8_t*>(a.q);
                 dma16(src, __builtin_amdgcn_readfirstlane(v_m0 + 1024u * (uint32_t)I));
@@ -243,7 +248,7 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         }
 #pragma unroll 4
         for (int i = 0; i < PW; ++i) {
-            if (i == (PW + 7) / 8) wait_vmcnt<0>();       // the group's own eighth first (as above)
+            if (i == (PW + 7) / 8) wait_vmcnt<0>();       // the group's own eighth first, landed before the rest
             const int u = (w + 8 * i + rot) % R;
             const int32_t r = u == u_new ? -1 : ridx[u];   // (the new entry's row: a stand-in, then overwritten)
             zmask |= r < 0 ? (1u << i) : 0u;
@@ -362,16 +367,59 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
                                      : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    // ---- A: scores of the wave's row tiles; lane (head j, g) ends with rows 4 g .. 4 g + 3 of each tile.
+    // The value-region part of tile m (main), then its RoPE part (rope), in this order for every tile
+    f32x4 acc[NT];
+#pragma unroll
+    for (int m = 0; m < NT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto live = [&](int m) { return 16 * (w + 8 * m) < n; };   // (wave-uniform) a tile with a row of the split
+    auto qk_main = [&](int m) {
+        const int tt = w + 8 * m;
+        const uint8_t* krow = V + (16 * tt + j) * VS;
+        if constexpr (SRC == SRC_E4M3) {
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int st = 4 * blk + s4;
+                    const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * st + 8 * g);
+                    t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[st], t4);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[m][r] += t4[r] * *reinterpret_cast<const float*>(V + (16 * tt + 4 * g + r) * VS + 512 + 4 * blk);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < NMAIN; ++st)
+                acc[m] = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * st + 8 * g)), qv[st], acc[m]);
+        }
+    };
+    if constexpr (NPART == 2) {
+        // this wave's first half has landed once at most the second half's loads are
+        // outstanding (wave 7 issues the fewest of them); the whole first half after the barrier
+        constexpr int kSecond = (R * 33 / 64 / 2 - 1 - 7) / 8 + 1;
+        wait_vmcnt<kSecond>();
+        lds_barrier();
+        if (live(0)) qk_main(0);
+    }
     wait_vmcnt<0>();
     if constexpr (SRC == SRC_E4M3) {
+        // slots without a row: zeroed for PV (their scores are masked below, so the
+        // first half's contraction may have read them before or after)
         constexpr int NI = R * 33 / 64;
-        constexpr int PW = (NI + 7) / 8;
-        const int rot = ((hg & 7) * (NI / 8)) & ~7;
+        constexpr int NH = NI / NPART;
+        constexpr int PW = (NH + 7) / 8;
+        const int rot = ((hg & 7) * (NH / 8)) & ~7;
         if (__builtin_amdgcn_ballot_w64(zmask != 0u)) {
 #pragma unroll
-            for (int i = 0; i < PW; ++i)
-                if ((zmask >> i) & 1u)
-                    *reinterpret_cast<u32x4*>(V + 16 * (64 * ((w + 8 * i + rot) % NI) + lane)) = u32x4{0u, 0u, 0u, 0u};
+            for (int part = 0; part < NPART; ++part)
+#pragma unroll
+                for (int i = 0; i < PW; ++i)
+                    if ((zmask >> (part * PW + i)) & 1u)
+                        *reinterpret_cast<u32x4*>(V + 16 * (64 * (part * NH + (w + 8 * i + rot) % NH) + lane)) =
+                            u32x4{0u, 0u, 0u, 0u};
         }
     } else if constexpr (SRC == SRC_BF16) {
         const int rot = (hg & 7) * (R / 8);
@@ -392,44 +440,22 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
     }
     __syncthreads();
 
-    // ---- A: scores of the wave's row tiles; lane (head j, g) ends with rows 4 g .. 4 g + 3 of each tile
     float z[NT][4];
 #pragma unroll
     for (int m = 0; m < NT; ++m) {
         const int tt = w + 8 * m;
-        const bool live = 16 * tt < n;                     // (wave-uniform) a tile with a row of the split
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (live) {
-            const uint8_t* krow = V + (16 * tt + j) * VS;
-            if constexpr (SRC == SRC_E4M3) {
-#pragma unroll
-                for (int blk = 0; blk < 4; ++blk) {
-                    f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const int st = 4 * blk + s4;
-                        const u32x2 codes = *reinterpret_cast<const u32x2*>(krow + 32 * st + 8 * g);
-                        t4 = mfma_bf16(e4m3x8_to_bf16(codes), qv[st], t4);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[r] += t4[r] * *reinterpret_cast<const float*>(V + (16 * tt + 4 * g + r) * VS + 512 + 4 * blk);
-                }
-            } else {
-#pragma unroll
-                for (int st = 0; st < NMAIN; ++st)
-                    acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * st + 8 * g)), qv[st], acc);
-            }
+        if (live(m)) {
+            if (NPART == 1 || m > 0) qk_main(m);
             if constexpr (kRope) {
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
-                    acc = mfma_bf16(rope[m][s2], qv[NMAIN + s2], acc);
+                    acc[m] = mfma_bf16(rope[m][s2], qv[NMAIN + s2], acc[m]);
             }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * tt + 4 * g + r;
-            z[m][r] = (live && ridx[row] >= 0) ? acc[r] * zscale : -__builtin_inff();
+            z[m][r] = (live(m) && ridx[row] >= 0) ? acc[m][r] * zscale : -__builtin_inff();
         }
     }
 

@@ -585,14 +585,34 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
         }
         ridx[tid] = r;
     }
-    // B operands of the wave's 16 heads (channels 32 st + 8 g .. of head j), used after the gather
+    // the pair's 32 heads' queries, staged once in the value region (every load issued before
+    // the first store), then read by each wave into the B operands of its 16 heads (channels
+    // 32 st + 8 g .. of head j); the gather overwrites the region only after every wave's reads
+    {
+        constexpr int kPer = DQK / 8;                      // 16-byte pieces per head
+        constexpr int kIt = (32 * kPer + 511) / 512;
+        static_assert(32 * gd::kQStride <= R * VS, "the staged queries fit the value region");
+        const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + 32 * hp) * DQK;
+        u32x4 qs[kIt];
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
+            if (it < 32 * kPer) qs[i] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)hh * DQK + 8 * pc);
+        }
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
+            if (it < 32 * kPer) *reinterpret_cast<u32x4*>(V + hh * gd::kQStride + 16 * pc) = qs[i];
+        }
+    }
+    __syncthreads();                                       // the row indices and the queries
     u32x4 qv[NQ];
     {
-        const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + 32 * hp + 16 * hs + j) * DQK;
+        const uint8_t* qh = V + (16 * hs + j) * gd::kQStride + 16 * g;
 #pragma unroll
-        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 32 * st + 8 * g);
+        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
     }
-    __syncthreads();                                       // the row indices
+    lds_barrier();                                         // every wave's query reads done: the region is free
 
     // ---- gather: one row per load instruction; the pairs of a split (one XCD) start at
     // different quarters of its rows, each landing its own quarter before requesting the rest

@@ -614,15 +614,15 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
     }
     lds_barrier();                                         // every wave's query reads done: the region is free
 
-    // ---- gather: one row per load instruction; the pairs of a split (one XCD) start at
-    // different quarters of its rows, each landing its own quarter before requesting the rest
+    // ---- gather: one row per load instruction, every load issued at once; the pairs of a
+    // split (one XCD) start at different quarters of its rows, so that a row's first requests
+    // come from different pairs and the L2 merges the others into them
     const uint32_t v_m0 = __builtin_amdgcn_readfirstlane(lds_addr(V));
     uint32_t zmask = 0;
     constexpr int PW = R / 8;
     const int rot = (hp & 3) * (R / 4);                    // (a multiple of 8: a wave keeps its rows)
 #pragma unroll 4
     for (int i = 0; i < PW; ++i) {
-        if (i == PW / 4) wait_vmcnt<0>();
         const int u = (w + 8 * i + rot) % R;
         const int32_t r = ridx[u];
         zmask |= r < 0 ? (1u << i) : 0u;

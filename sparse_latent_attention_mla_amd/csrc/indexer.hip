@@ -576,7 +576,6 @@ __global__ __launch_bounds__(kScanThreads, kDmaBlocksPerCu) void k_scan_dma(Scan
     // instruction covers 64 consecutive bins
     uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
     const int copy = hist_copy_of_block();
-    uint32_t* fine = hist_fine(hb, copy);
     uint32_t cnt[kHistBins / kScanThreads];
 #pragma unroll
     for (int i = 0; i < kHistBins / kScanThreads; ++i) {
@@ -914,7 +913,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dma32(ScanArgs a, int 
     }
     uint32_t* hb = a.hist + (int64_t)b * kHistWordsHost;
     const int copy = hist_copy_of_block();
-    uint32_t* fine = hist_fine(hb, copy);
     uint32_t cnt[kHistBins / NT];
 #pragma unroll
     for (int i = 0; i < kHistBins / NT; ++i) {
@@ -1205,30 +1203,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
 
 // MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
 template <int MT>
-__global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
+__global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a, int rows_per_block) {
     __shared__ uint32_t hist[kHistBins];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
     const int64_t nvis = clamp_visible(a.n_visible[b], a.capacity);
-    const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock;
-    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
-    ScanCtx<MT> C;
-    load_ctx<MT>(C, a, b, col, g);
-    __syncthreads();
+    const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+    const int n_it = rows_per_block / 64;                  // 16-row tiles per wave
     const uint8_t* base = a.cache + b * a.stride;
     float* scores = a.scores + b * a.capacity;
-    for (int it = 0; it < kTilesPerWave; ++it) {
-        const int64_t tile0 = row0 + (int64_t)(it * 4 + wave) * 16;
-        if (tile0 >= a.capacity) break;
-        const int64_t s = tile0 + col;
-        const bool valid = s < nvis;
-        if (tile0 >= nvis) {
-            if (g == 0 && s < a.capacity) scores[s] = -__builtin_inff();
-            continue;
-        }
-        u32x4 kb[4];
-        if (valid) {
+    // the tile's B operands (zero past the visible rows); the next tile's loads are issued
+    // before the current tile is contracted
+    auto load_tile = [&](int it, u32x4* kb) {
+        const int64_t s = row0 + (int64_t)(it * 4 + wave) * 16 + col;
+        if (s < nvis) {
             const u32x4* p = reinterpret_cast<const u32x4*>(base + s * 256 + g * 64);
 #pragma unroll
             for (int t = 0; t < 4; ++t) kb[t] = __builtin_nontemporal_load(p + t);
@@ -1236,8 +1225,44 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) kb[t] = u32x4{0u, 0u, 0u, 0u};
         }
-        tile_scores<MT>(C, kb, valid ? 1.0f : 0.0f, s, valid, g, a.sigma, a.capacity, scores, hist,
-                        a.score_bf16);
+    };
+    // the sequence's queries staged once per workgroup (272-byte head stride: the 16 lanes
+    // reading one piece of 16 heads hit distinct banks), then read into every wave's operands
+    __shared__ __attribute__((aligned(16))) uint8_t qs[16 * MT * 272];
+    u32x4 kb[4], kn[4];
+    load_tile(0, kb);
+    {
+        const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q_idx) + (int64_t)b * a.H_I * 256;
+        for (int i = threadIdx.x; i < 16 * MT * 16; i += kScanThreads)
+            *reinterpret_cast<u32x4*>(qs + (i >> 4) * 272 + 16 * (i & 15)) =
+                *reinterpret_cast<const u32x4*>(qb + 16 * i);
+    }
+    for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
+    ScanCtx<MT> C;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) C.wv[m][r] = a.w[(int64_t)b * a.H_I + 16 * m + 4 * g + r] * a.sigma;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            C.qa[m][t] = *reinterpret_cast<const u32x4*>(qs + (16 * m + col) * 272 + 2 * (g * 32 + t * 8));
+    for (int it = 0; it < n_it; ++it) {
+        const int64_t tile0 = row0 + (int64_t)(it * 4 + wave) * 16;
+        if (tile0 >= a.capacity) break;
+        if (it + 1 < n_it) load_tile(it + 1, kn);
+        const int64_t s = tile0 + col;
+        const bool valid = s < nvis;
+        if (tile0 >= nvis) {
+            if (g == 0 && s < a.capacity) scores[s] = -__builtin_inff();
+        } else {
+            tile_scores<MT>(C, kb, valid ? 1.0f : 0.0f, s, valid, g, a.sigma, a.capacity, scores, hist,
+                            a.score_bf16);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) kb[t] = kn[t];
     }
     __syncthreads();
     flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
@@ -1470,7 +1495,15 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
     }
     if (a.B == 0 || a.capacity == 0) return unfused();
     if (mfma) {
-        const dim3 grid((unsigned)((a.capacity + kRowsPerBlock - 1) / kRowsPerBlock), a.B);
+        // bf16 keys: rows per block (a multiple of 64, at most kRowsPerBlock) for about one
+        // block per CU, so that short caches still fill the chip (c2, 8 x 8192 rows: 256
+        // blocks measured 0.3 us per step ahead of 384, 512 and 768)
+        int64_t bblocks = 256;
+        if (const int64_t v = option(OPT_SCAN_BLOCKS)) bblocks = v;
+        const int64_t bper_seq = std::max<int64_t>(1, bblocks / a.B);
+        int64_t brpb = (a.capacity + bper_seq - 1) / bper_seq;
+        brpb = std::min<int64_t>(std::max<int64_t>((brpb + 63) / 64 * 64, 64), kRowsPerBlock);
+        const dim3 bgrid((unsigned)((a.capacity + brpb - 1) / brpb), a.B);
         // staged scan: ~kStagedBlocks long-lived workgroups, each wave streaming many chunks
         const int64_t per_seq = (kStagedBlocks + a.B - 1) / a.B;
         int64_t rpb = (a.capacity + per_seq - 1) / per_seq;
@@ -1520,7 +1553,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
         if constexpr (F == MLA_FMT_BF16) {                                                     \
             if (const hipError_t e = unfused(); e != hipSuccess) return e;                     \
             const ProfSlot p = prof_slot(PROF_SCAN);                                           \
-            return launch_kernel(k_scan_bf16<M>, grid, dim3(kScanThreads), 0, stream, p.start, p.stop, a); \
+            return launch_kernel(k_scan_bf16<M>, bgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, a, \
+                                 (int)brpb);                                                   \
         } else {                                                                               \
             const ProfSlot p = prof_slot(PROF_SCAN);                                           \
             if (dma) {                                                                         \

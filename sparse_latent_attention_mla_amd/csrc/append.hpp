@@ -169,11 +169,19 @@ __host__ inline bool pieces_supported(const AppendArgs& a) {
         (((a.Dw / 32) & 1) != 0 || reinterpret_cast<uintptr_t>(a.win_ring) % 2 != 0))
         return false;
     if (a.main_cache && !((a.main_fmt == MLA_FMT_E4M3_S128 && a.main_rope <= 128) ||
-                          (a.main_fmt == MLA_FMT_E2M1_S16 && a.main_rope == 0)))
+                          (a.main_fmt == MLA_FMT_E2M1_S16 && a.main_rope == 0) ||
+                          (a.main_fmt == MLA_FMT_BF16 && a.main_rope <= 128)))
         return false;
     if (a.main_cache && a.main_dim % 128 != 0) return false;
     if (a.idx_cache && !((a.idx_fmt == MLA_FMT_E4M3_S128 || a.idx_fmt == MLA_FMT_E2M1_S16 ||
-                          a.idx_fmt == MLA_FMT_MXFP4) && a.idx_dim == 128))
+                          a.idx_fmt == MLA_FMT_MXFP4 || a.idx_fmt == MLA_FMT_BF16) && a.idx_dim == 128))
+        return false;
+    // bf16 rows are written two channels (4 bytes) per lane
+    if (a.main_cache && a.main_fmt == MLA_FMT_BF16 &&
+        (reinterpret_cast<uintptr_t>(a.main_cache) % 4 != 0 || a.main_stride % 4 != 0 || a.main_row_bytes % 4 != 0))
+        return false;
+    if (a.idx_cache && a.idx_fmt == MLA_FMT_BF16 &&
+        (reinterpret_cast<uintptr_t>(a.idx_cache) % 4 != 0 || a.idx_stride % 4 != 0 || a.idx_row_bytes % 4 != 0))
         return false;
     return reinterpret_cast<uintptr_t>(a.new_main) % 8 == 0 && reinterpret_cast<uintptr_t>(a.new_idx) % 8 == 0 &&
            reinterpret_cast<uintptr_t>(a.new_win) % 8 == 0 && (a.main_dim + a.main_rope) % 2 == 0 &&
@@ -244,12 +252,21 @@ __device__ __forceinline__ void piece_store(const AppendArgs& a, const Piece& pc
     if (pc.slot < 0 || pc.slot >= a.capacity) return;
     if (pc.kind == 3) {                                    // indexer key
         uint8_t* row = a.idx_cache + pc.b * a.idx_stride + pc.slot * a.idx_row_bytes;
+        if (a.idx_fmt == MLA_FMT_BF16) {                   // (2 l < 128 for every lane)
+            reinterpret_cast<uint32_t*>(row)[l] = bf16_rne(pc.v0) | (bf16_rne(pc.v1) << 16);
+            return;
+        }
         if (a.idx_fmt == MLA_FMT_E4M3_S128) quant128_wave<MLA_FMT_E4M3_S128>(pc.v0, pc.v1, row, row + 128);
         else if (a.idx_fmt == MLA_FMT_MXFP4) quant128_wave<MLA_FMT_MXFP4>(pc.v0, pc.v1, row, row + 64);
         else quant128_wave<MLA_FMT_E2M1_S16>(pc.v0, pc.v1, row, row + 64);
         return;
     }
     uint8_t* row = a.main_cache + pc.b * a.main_stride + pc.slot * a.main_row_bytes;
+    if (a.main_fmt == MLA_FMT_BF16) {                      // bf16 row: block `part`, or the RoPE part
+        uint8_t* dst = row + 2 * (pc.kind == 2 ? a.main_dim : 128 * pc.part);
+        if (2 * l < pc.n) reinterpret_cast<uint32_t*>(dst)[l] = bf16_rne(pc.v0) | (bf16_rne(pc.v1) << 16);
+        return;
+    }
     if (pc.kind == 2) {                                    // RoPE part of an E4M3 row, bf16
         uint8_t* rp = row + a.main_dim + 4 * (a.main_dim / 128);
         if (2 * l < pc.n) {

@@ -1202,12 +1202,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_scan_dyn32(ScanArgs a, int 
 }
 
 // MFMA scan, 256-byte bf16 rows (16-byte aligned): direct 16-byte loads.
-template <int MT>
-__global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a, int rows_per_block) {
+// bf16 indexer keys (256-byte rows): each wave contracts 16-row tiles loaded straight
+// into its B operands, the next tile's loads issued before the current tile is
+// contracted; the queries are staged once per workgroup in LDS.
+// With FUSE the kernel also carries its step's append (ap, at most kFuseMaxNew entries
+// per sequence) as the 32x32 scan does: wave w of block (x, 0) loads piece 4 x + w
+// as it starts and stores it after its tiles, and a row that is one of the new slots
+// is scored from the new key rounded to bf16 (staged in LDS), the bytes the append
+// writes, whatever its load saw.
+template <int MT, bool FUSE>
+__global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a, int rows_per_block, AppendArgs ap) {
     __shared__ uint32_t hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint16_t new_key[FUSE ? kFuseMaxNew : 1][128];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
+    Piece pc;                                              // the carried piece, in registers meanwhile
+    if constexpr (FUSE) {
+        pc.kind = 0;
+        if (b == 0) piece_load(ap, (int64_t)blockIdx.x * 4 + wave, pc);
+    }
     const int64_t nvis = clamp_visible(a.n_visible[b], a.capacity);
     const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
     const int n_it = rows_per_block / 64;                  // 16-row tiles per wave
@@ -1237,6 +1251,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a, int rows
             *reinterpret_cast<u32x4*>(qs + (i >> 4) * 272 + 16 * (i & 15)) =
                 *reinterpret_cast<const u32x4*>(qb + 16 * i);
     }
+    int64_t slot[FUSE ? kFuseMaxNew : 1];                  // the new slots of the sequence (-1: none)
+    if constexpr (FUSE) {
+#pragma unroll
+        for (int e = 0; e < kFuseMaxNew; ++e) {
+            slot[e] = -1;
+            if (e < ap.n_new) {
+                const int64_t sl = ap.slots[(int64_t)b * ap.n_new + e];
+                if (sl >= 0 && sl < a.capacity) slot[e] = sl;
+            }
+        }
+        const int e = threadIdx.x >> 6;                    // wave e stages new key e, 2 channels per lane
+        if (e < ap.n_new) {
+            const f32x2 v = *reinterpret_cast<const f32x2*>(ap.new_idx + ((int64_t)b * ap.n_new + e) * 128 + 2 * lane);
+            reinterpret_cast<uint32_t*>(&new_key[e][0])[lane] = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+        }
+    }
     for (int i = threadIdx.x; i < kHistBins; i += kScanThreads) hist[i] = 0u;
     ScanCtx<MT> C;
 #pragma unroll
@@ -1255,6 +1285,16 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a, int rows
         if (it + 1 < n_it) load_tile(it + 1, kn);
         const int64_t s = tile0 + col;
         const bool valid = s < nvis;
+        if constexpr (FUSE) {                              // a new slot's row: the new key's bytes
+#pragma unroll
+            for (int e = 0; e < kFuseMaxNew; ++e)
+                if (s == slot[e]) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        kb[t] = valid ? *reinterpret_cast<const u32x4*>(&new_key[e][g * 32 + t * 8])
+                                      : u32x4{0u, 0u, 0u, 0u};
+                }
+        }
         if (tile0 >= nvis) {
             if (g == 0 && s < a.capacity) scores[s] = -__builtin_inff();
         } else {
@@ -1264,6 +1304,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_bf16(ScanArgs a, int rows
 #pragma unroll
         for (int t = 0; t < 4; ++t) kb[t] = kn[t];
     }
+    if constexpr (FUSE) piece_store(ap, pc);
     __syncthreads();
     flush_hist(hist, a.hist + (int64_t)b * kHistWordsHost);
 }
@@ -1551,10 +1592,15 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream, const AppendArgs* 
 #define MLA_SCAN_CASE(F, M)                                                                    \
     if (a.fmt == F && a.H_I == 16 * M) {                                                       \
         if constexpr (F == MLA_FMT_BF16) {                                                     \
+            if (carry && pieces_supported(*append) && piece_count(*append) <= (int64_t)bgrid.x * 4) { \
+                const ProfSlot p = prof_slot(PROF_SCAN);                                       \
+                return launch_kernel(k_scan_bf16<M, true>, bgrid, dim3(kScanThreads), 0, stream, p.start, \
+                                     p.stop, a, (int)brpb, *append);                           \
+            }                                                                                  \
             if (const hipError_t e = unfused(); e != hipSuccess) return e;                     \
             const ProfSlot p = prof_slot(PROF_SCAN);                                           \
-            return launch_kernel(k_scan_bf16<M>, bgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, a, \
-                                 (int)brpb);                                                   \
+            return launch_kernel(k_scan_bf16<M, false>, bgrid, dim3(kScanThreads), 0, stream, p.start, p.stop, a, \
+                                 (int)brpb, AppendArgs{});                                     \
         } else {                                                                               \
             const ProfSlot p = prof_slot(PROF_SCAN);                                           \
             if (dma) {                                                                         \

@@ -415,8 +415,9 @@ def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
     waves each own one, or four of which three sit in the second 32-row tile of a
     64-row chunk; visible lengths that include and that exclude slot N - 1, and a
     ragged one. Where the sequences end on a 16-byte boundary, E4M3, E2M1 and MXFP4
-    indexer rows take the LDS-DMA scan carrying the append (checked by the kernel the
-    call launched); other shapes and bf16 / fp32 rows the separate append + scan."""
+    indexer rows take the LDS-DMA scan carrying the append, and bf16 rows the bf16 scan
+    carrying it (checked by the kernel the call launched); other shapes and fp32 rows
+    the separate append + scan."""
     case = case_of(name)
     cfg = case.cfg
     B, N, k = cfg.B, cfg.N, cfg.k
@@ -471,6 +472,9 @@ def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
             assert "k_scan_dma32" in scans[0] and "true>(" in scans[0], launched
         elif name in ("c3s", "c4s", "c4xs", "c3m"):     # odd sequence ends: separate append, staged scan
             assert any("k_append" in n for n in launched) and "k_scan_staged" in scans[0], launched
+        elif name == "c2s":                             # bf16 rows: the bf16 scan carrying the append
+            assert not any("k_append" in n for n in launched), launched
+            assert "k_scan_bf16" in scans[0] and "true>(" in scans[0], launched
         assert torch.equal(m_a, m_b) and torch.equal(i_a, i_b), "caches differ between the paths"
         assert torch.equal(i_b, case.g_idx) and torch.equal(m_b, case.g_main), "caches differ from the case's"
         if cfg.W:

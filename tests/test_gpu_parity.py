@@ -25,6 +25,8 @@ C = WL.CONFIGS
 SMALL = {
     "c1": C["c1"],
     "c2s": C["c2"].with_(name="c2s", cid=102, B=2, N=5003),
+    # bf16 rows and keys with a bf16 window ring: the bf16 scan carrying the append, window included
+    "c2sw": C["c2"].with_(name="c2sw", cid=107, B=3, N=4100, W=64),
     "c3s": C["c3"].with_(name="c3s", cid=103, B=2, N=6001),
     "c4s": C["c4"].with_(name="c4s", cid=104, B=2, N=4099),
     "c4xs": C["c4x"].with_(name="c4xs", cid=106, B=2, N=5021),
@@ -404,7 +406,7 @@ def test_scan_work_queues(name, scan):
 
 
 @pytest.mark.parametrize("slots_kind", ["step", "spread", "tiles"])
-@pytest.mark.parametrize("name", ["c3s", "c4s", "c4xs", "c3m", "c2s", "c1", "c3d", "c4d", "c4xd"])
+@pytest.mark.parametrize("name", ["c3s", "c4s", "c4xs", "c3m", "c2s", "c2sw", "c1", "c3d", "c4d", "c4xd"])
 def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
     """mla_append_indexer_topk against mla_kv_append_quant then mla_indexer_topk on
     copies of the same caches whose new slots hold stale bytes: the caches and the
@@ -472,7 +474,7 @@ def test_append_indexer_topk_equals_the_two_calls(name, slots_kind):
             assert "k_scan_dma32" in scans[0] and "true>(" in scans[0], launched
         elif name in ("c3s", "c4s", "c4xs", "c3m"):     # odd sequence ends: separate append, staged scan
             assert any("k_append" in n for n in launched) and "k_scan_staged" in scans[0], launched
-        elif name == "c2s":                             # bf16 rows: the bf16 scan carrying the append
+        elif name in ("c2s", "c2sw"):                   # bf16 rows: the bf16 scan carrying the append
             assert not any("k_append" in n for n in launched), launched
             assert "k_scan_bf16" in scans[0] and "true>(" in scans[0], launched
         assert torch.equal(m_a, m_b) and torch.equal(i_a, i_b), "caches differ between the paths"

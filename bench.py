@@ -16,6 +16,8 @@ caches.
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
+import contextlib
+import gc
 import hashlib
 import json
 import math
@@ -57,6 +59,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="replay each rotated layer's step from a HIP graph captured once (the stamped steps "
                         "still run eagerly); default: every step's kernels are launched from the host")
+    p.add_argument("--python-group", action="store_true",
+                   help="enqueue each step through csa2_group_step (one Python call per layer and kernel) "
+                        "instead of mla_csa2_group_step (one C call per step)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="time only torch's device copy of a known size (scales HBM byte counters)")
     return p.parse_args()
@@ -139,6 +144,40 @@ def build_layers(cfg, n_layers, seed=0):
 
 SCAN_SOURCES = ("csrc/indexer.hip", "csrc/append.hpp", "csrc/common.hpp", "csrc/launch.hpp", "build.py")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_scan_c3_hbm_traffic.md")
+
+
+PACE_EVERY, PACE_AHEAD = 8, 16
+
+
+@contextlib.contextmanager
+def gc_paused():
+    """Python's cyclic garbage collector paused (after one full collection): a collection
+    of the whole heap takes tens of ms, during which a host that keeps the GPU only a few
+    steps ahead leaves it idle (a serving loop runs the same way)."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
+def paced_loop(run_step, steps, stream):
+    """run_step(i) for i < steps, the host at most PACE_AHEAD + PACE_EVERY steps ahead of
+    the GPU (an event every PACE_EVERY steps; before recording one, the host waits for the
+    one recorded that many steps earlier). The GPU stays fed; without the bound, a host that enqueues faster than the GPU
+    runs piles up thousands of launches, and the runtime then stalls while it recycles
+    their resources, leaving the GPU idle between kernels (a c5 group: 288 instead of
+    130 us on some runs)."""
+    import torch
+    marks = [torch.cuda.Event() for _ in range(PACE_AHEAD // PACE_EVERY + 1)]
+    for i in range(steps):
+        if i % PACE_EVERY == 0:
+            m = (i // PACE_EVERY) % len(marks)
+            if i >= PACE_AHEAD + PACE_EVERY:
+                marks[m].synchronize()                 # recorded PACE_AHEAD + PACE_EVERY steps ago
+            marks[m].record(stream)
+        run_step(i)
 
 
 def scan_source_digest():
@@ -285,8 +324,8 @@ def run_config(args, cfg, n_layers, steps, warmup, headline):
     L_grp = len(cfg.layers)
     log(f"config {cfg.name}: {cfg.desc}; building {n_layers} layer caches")
     layers = build_layers(cfg, n_layers)
-    opt = args if headline else argparse.Namespace(pool=0, compress=0, win_fmt="bf16", graph=cfg.name == "c5",
-                                                   score_bf16=False)
+    opt = args if headline else argparse.Namespace(pool=0, compress=0, win_fmt="bf16", graph=False,
+                                                   score_bf16=False, python_group=False)
     win_fmt = M.MXFP8 if (cfg.W and opt.win_fmt == "mxfp8") else M.BF16
     if opt.compress:                                       # the window's projected kv and gate vectors
         for i, X in enumerate(layers):
@@ -327,17 +366,22 @@ def run_config(args, cfg, n_layers, steps, warmup, headline):
     slots1 = slots[:, 0].contiguous()
 
     def step(X, between=None):
-        """One layer-step (or CSA2 group) on layer caches X, through the group helper: the
+        """One layer-step (or CSA2 group) on layer caches X, as one mla_csa2_group_step call
+        (or, with --python-group or a hook between layers, through csa2_group_step): the
         first layer appends the step's entry in its scan's launch (with --compress the main
         entry is pooled by mla_compress_append first), every layer its window entry."""
         if opt.compress:
             M.mla_compress_append(mr, X.comp_kv, X.comp_gate, X.main, slots1, comp_norm, 1e-6)
-        M.csa2_group_step(mr, ir, cfg.layers, X.main, X.idx, nvis, k, cfg.sigma, cfg.softmax_scale, X.q, X.q_idx,
-                          X.w, out, lse, ws_topk, ws_dec, idx_out,
-                          new_main=None if opt.compress else X.new_main, new_idx=X.new_idx, slots=slots,
-                          win_rings=X.win if cfg.W else None, new_win=X.new_win if cfg.W else None,
-                          win_pos=win_pos if cfg.W else None, win_len=win_len if cfg.W else None,
-                          pool=pool_args, score_bf16=opt.score_bf16, between_layers=between)
+        kw = dict(new_main=None if opt.compress else X.new_main, new_idx=X.new_idx, slots=slots,
+                  win_rings=X.win if cfg.W else None, new_win=X.new_win if cfg.W else None,
+                  win_pos=win_pos if cfg.W else None, win_len=win_len if cfg.W else None,
+                  pool=pool_args, score_bf16=opt.score_bf16)
+        if between is not None or opt.python_group:
+            M.csa2_group_step(mr, ir, cfg.layers, X.main, X.idx, nvis, k, cfg.sigma, cfg.softmax_scale, X.q,
+                              X.q_idx, X.w, out, lse, ws_topk, ws_dec, idx_out, between_layers=between, **kw)
+        else:                                              # the whole step in one C call
+            M.mla_csa2_group_step(mr, ir, cfg.layers, X.main, X.idx, nvis, k, cfg.sigma, cfg.softmax_scale, X.q,
+                                  X.q_idx, X.w, out, lse, ws_topk, ws_dec, idx_out, **kw)
 
     log(f"warmup {warmup} steps")
     for i in range(warmup):
@@ -382,11 +426,11 @@ def run_config(args, cfg, n_layers, steps, warmup, headline):
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(steps):
-        run_step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
+    with gc_paused():
+        t_start.record(stream)
+        paced_loop(run_step, steps, stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / steps
 
     # the same steps all launched from the host, for comparison (not the result)
@@ -394,11 +438,11 @@ def run_config(args, cfg, n_layers, steps, warmup, headline):
     if graphs is not None:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            step(layers[i % n_layers])
-        e1.record(stream)
-        torch.cuda.synchronize()
+        with gc_paused():
+            e0.record(stream)
+            paced_loop(lambda i: step(layers[i % n_layers]), steps, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / steps
 
     # roofline pass (outside the timed steps): whole eager steps with every indexer scan
@@ -481,7 +525,9 @@ def run_config(args, cfg, n_layers, steps, warmup, headline):
         "value": 1e3 / ms_per_step,
         "unit": "layer-steps/s" if L_grp == 1 else "layer-groups/s",
         "ms_per_step": ms_per_step,
-        "launch": "eager" if graphs is None else "HIP graph per layer cache",
+        "launch": ("HIP graph per layer cache" if graphs is not None else
+                   "eager, one Python call per layer and kernel" if opt.python_group else
+                   "eager, one C call per step"),
         "ms_per_step_eager": eager_ms if graphs is not None else ms_per_step,
         "config": {
             "workload": f"{cfg.name}: {cfg.desc}",

@@ -14,9 +14,10 @@
  * one layer's scores into the candidate pool of the hierarchical sparse indexer,
  * which deeper layers' mla_indexer_topk calls then score instead of every row.
  * The cross-layer sharing modes of CSA2 are compositions of these calls over
- * shared pointers (no mode enum): Full = append + topk + decode; Reindex = topk
- * with its own indexer query over another layer's indexer cache + decode over
- * the shared main cache; Reuse = decode with the shared indices.
+ * shared pointers: Full = append + topk + decode; Reindex = topk with its own
+ * indexer query over another layer's indexer cache + decode over the shared main
+ * cache; Reuse = decode with the shared indices.  mla_csa2_group_step enqueues a
+ * whole group's calls in one call from C.
  *
  * Sources (web pages, cited by title and section):
  *  [P1] "DeepSeek's Attention and KV Cache - From MLA to CSA2, From First Principles"
@@ -498,6 +499,69 @@ mla_status_t mla_append_sparse_decode(mla_row_t main_row, int32_t d_v, const voi
                                       const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H,
                                       float* out, float* lse, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/*
+ * mla_csa2_group_step -- one decode step of a layer group over one shared cache, in one call.
+ *
+ * The layers of a CSA2 group ([P1] "DeepSeek-V4.1", "Three modes"; [P4] "CSA2: four layers
+ * keep their own copy") enqueued in order on `stream`, each exactly as the calls it is
+ * made of (same kernels, same results):
+ *   MLA_LAYER_FULL, MLA_LAYER_REINDEX  the layer selects with its own indexer query over the
+ *        shared indexer keys: for layer 0, mla_append_indexer_topk (the step's entry: main
+ *        row, indexer key and layer 0's window entry, carried in the scan's launch where it
+ *        can be); for a later layer, mla_indexer_topk (a Reindex layer scores only the pool
+ *        when pool_blocks > 0); a Full layer with pool_blocks > 0 also writes its scores to
+ *        pool_scores and publishes the pool (mla_indexer_pool) into pool_pos;
+ *   MLA_LAYER_REUSE  the indices of the latest selecting layer;
+ * then every layer's decode over the shared main cache with its own query and window:
+ * mla_sparse_decode for layer 0, mla_append_sparse_decode (the layer's window entry
+ * appended in the decode's call) for the others when W > 0. Selecting layers write their
+ * indices to idx_a and idx_b in turn (the first to idx_a): with more than two selecting
+ * layers, a buffer is overwritten by the selection two layers later. The bf16-score top-k
+ * (mla_indexer_topk_bf16) when score_bf16 != 0.
+ *
+ * One call instead of one per layer and kernel, for callers whose host loop would
+ * otherwise set the pace: the launches are enqueued back to back from C.
+ *
+ *  layers        host array of n_layers descriptors (below); layer 0 must select
+ *  new_main, new_idx, slots, n_new   the step's entry as for mla_append_indexer_topk
+ *                (new_main NULL: the main row was appended by other means)
+ *  main_cache, idx_cache, strides, capacity, n_visible, B, H, H_I, k, d_v   shared by the layers,
+ *                as for the calls above
+ *  win_pos, win_len, W, win_fmt   the layers' windows (W = 0: none); Dw = dim + rope
+ *  pool_blocks, pool_block, pool_scores (fp32 [B, capacity]), pool_pos (int32
+ *                [B, pool_blocks * pool_block])   the candidate pool, or pool_blocks = 0
+ *  idx_a, idx_b  int32 [B, k] each
+ *  topk_workspace   at least mla_indexer_topk_workspace (and mla_indexer_pool_workspace with
+ *                a pool) bytes, under their zeroing contract; decode_workspace at least
+ *                mla_sparse_decode_workspace(main_row, d_v, B, H, k, W, win_fmt) bytes
+ * Errors: those of the calls above; and, before any launch, MLA_ERR_INVALID_ARG for an
+ * unknown mode, a leading Reuse layer, a missing or misaligned per-layer pointer (q, out:
+ * 16 bytes; q_idx 16, w 4 for selecting layers; win_ring 16 (MXFP8: 2), new_win 16 when
+ * W > 0), missing index buffers or pool arrays, and MLA_ERR_WORKSPACE for a short workspace.
+ */
+enum { MLA_LAYER_FULL = 0, MLA_LAYER_REINDEX = 1, MLA_LAYER_REUSE = 2 };
+typedef struct {
+    int32_t mode;            /* MLA_LAYER_FULL, MLA_LAYER_REINDEX or MLA_LAYER_REUSE */
+    const void* q;           /* [B, H, dim + rope] bf16: the layer's absorbed query */
+    const void* q_idx;       /* [B, H_I, d_I] bf16: selecting layers (NULL for Reuse) */
+    const float* w;          /* [B, H_I] indexer head weights: selecting layers */
+    float* out;              /* [B, H, d_v] */
+    float* lse;              /* [B, H] */
+    void* win_ring;          /* the layer's window ring (bf16 or MXFP8 bytes), when W > 0 */
+    const float* new_win;    /* [B, dim + rope] the step's window entry of the layer, when W > 0 */
+} mla_group_layer_t;
+
+mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t d_v, int32_t n_layers,
+                                 const mla_group_layer_t* layers, const float* new_main, const float* new_idx,
+                                 const int32_t* slots, int32_t n_new, void* main_cache, int64_t main_seq_stride,
+                                 void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                 const int32_t* n_visible, int32_t B, int32_t H, int32_t H_I, int32_t k,
+                                 float score_scale, float softmax_scale, const int32_t* win_pos,
+                                 const int32_t* win_len, int32_t W, int32_t win_fmt, int32_t score_bf16,
+                                 int32_t pool_blocks, int32_t pool_block, float* pool_scores, int32_t* pool_pos,
+                                 int32_t* idx_a, int32_t* idx_b, void* topk_workspace, size_t topk_workspace_bytes,
+                                 void* decode_workspace, size_t decode_workspace_bytes, void* stream);
 
 /*
  * mla_sparse_decode_noalloc -- mla_sparse_decode with the library's own scratch.

@@ -87,6 +87,10 @@ def lib():
         L.mla_append_sparse_decode.argtypes = [_CRow, i32, P, P, i64, i64, P, i32, P, P, P, P, i32, i32, f32, P, i32,
                                                i32, P, P, P, sz, P]
         L.mla_append_sparse_decode.restype = i32
+        L.mla_csa2_group_step.argtypes = [_CRow, _CRow, i32, i32, P, P, P, P, i32, P, i64, P, i64, i64, P, i32, i32,
+                                          i32, i32, f32, f32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P,
+                                          sz, P]
+        L.mla_csa2_group_step.restype = i32
         _lib = L
     return _lib
 
@@ -561,5 +565,100 @@ def csa2_group_step(main_row: Row, idx_row: Row, modes, main_cache, idx_cache, n
                           decode_workspace, win_rings[l] if win_rings is not None else None,
                           win_len if win_rings is not None else None, stream=stream,
                           new_win=win[0] if fused_win else None, win_pos=win[1] if fused_win else None)
+        attended.append(latest)
+    return attended
+
+
+class _CLayer(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("q", C.c_void_p), ("q_idx", C.c_void_p), ("w", C.c_void_p),
+                ("out", C.c_void_p), ("lse", C.c_void_p), ("win_ring", C.c_void_p), ("new_win", C.c_void_p)]
+
+
+_LAYER_MODE = {"full": 0, "reindex": 1, "reuse": 2}
+
+
+def mla_csa2_group_step(main_row: Row, idx_row: Row, modes, main_cache, idx_cache, n_visible, k: int,
+                        score_scale: float, softmax_scale: float, q, q_idx, w, out, lse, topk_workspace,
+                        decode_workspace, idx_out, new_main=None, new_idx=None, slots=None, win_rings=None,
+                        new_win=None, win_pos=None, win_len=None, pool=None, score_bf16=False, stream=None):
+    """csa2_group_step as one C call (mla_csa2_group_step): the same layers, kernels and
+    results, enqueued back to back from C instead of one Python call per layer and kernel.
+    Same arguments as csa2_group_step (every layer's tensors stacked on a leading layer
+    axis; q_idx and w one entry per selecting layer, in order); no between_layers. Returns,
+    per layer, the index tensor it attended."""
+    L = len(modes)
+    if L < 1 or any(m not in _LAYER_MODE for m in modes):
+        raise ValueError(f"modes must be 'full', 'reindex' or 'reuse', got {modes!r}")
+    _need(q, "q", query_dtype(main_row), 4)
+    _need(out, "out", torch.float32, 4)
+    _need(lse, "lse", torch.float32, 3)
+    _need(n_visible, "n_visible", torch.int32, 1)
+    _need(topk_workspace, "topk_workspace", torch.uint8)
+    _need(decode_workspace, "decode_workspace", torch.uint8)
+    if len(idx_out) != 2:
+        raise ValueError("idx_out: two int32 [B, k] buffers")
+    for i, t in enumerate(idx_out):
+        _need(t, f"idx_out[{i}]", torch.int32, 2)
+    Lq, B, H, D = q.shape
+    n_sel = sum(m != "reuse" for m in modes)
+    if Lq != L or out.shape[:3] != (L, B, H) or tuple(lse.shape) != (L, B, H):
+        raise ValueError("q [L, B, H, D], out [L, B, H, d_v] and lse [L, B, H] expected")
+    if D != main_row.dim + main_row.rope or main_cache.shape[0] != B or main_cache.shape[2] != row_bytes(main_row):
+        raise ValueError("q and main_cache must match the main row format")
+    if idx_cache.shape[0] != B or idx_cache.shape[2] != row_bytes(idx_row) or idx_cache.shape[1] != main_cache.shape[1]:
+        raise ValueError("idx_cache [B, capacity, row_bytes] of the indexer row format, the main cache's capacity")
+    _need(q_idx, "q_idx", query_dtype(idx_row), 4)
+    _need(w, "w", torch.float32, 3)
+    if q_idx.shape[0] < n_sel or w.shape[0] < n_sel or q_idx.shape[1] != B or q_idx.shape[3] != idx_row.dim:
+        raise ValueError("q_idx [n, B, H_I, dim] and w [n, B, H_I] for the n selecting layers expected")
+    H_I = q_idx.shape[2]
+    if tuple(w.shape[1:]) != (B, H_I):
+        raise ValueError("w [n, B, H_I] expected")
+    n_new = 0
+    if new_idx is not None:
+        _need(new_idx, "new_idx", torch.float32, 3)
+        _need(slots, "slots", torch.int32, 2)
+        n_new = slots.shape[1]
+        if tuple(slots.shape) != (B, n_new) or tuple(new_idx.shape) != (B, n_new, idx_row.dim):
+            raise ValueError("slots [B, n_new] and new_idx [B, n_new, idx dim] expected")
+    if new_main is not None:
+        _need(new_main, "new_main", torch.float32, 3)
+        if tuple(new_main.shape) != (B, n_new, D):
+            raise ValueError("new_main [B, n_new, dim + rope] expected")
+    W, wfmt = 0, BF16
+    if win_rings is not None:
+        _need(new_win, "new_win", torch.float32, 3)
+        _need(win_pos, "win_pos", torch.int32, 1)
+        _need(win_len, "win_len", torch.int32, 1)
+        if win_rings.shape[0] != L or tuple(new_win.shape) != (L, B, D):
+            raise ValueError("win_rings [L, B, W, ...] and new_win [L, B, dim + rope] expected")
+        wfmt, W = _win_ring(win_rings[0], B, D)
+    pool_blocks = pool_block = 0
+    pool_scores = pool_pos = None
+    if pool is not None:
+        pool_blocks, pool_block, pool_scores, pool_pos = pool
+        _need(pool_scores, "pool scores", torch.float32, 2)
+        _need(pool_pos, "pool positions", torch.int32, 2)
+    layers = (_CLayer * L)()
+    j = 0
+    for l, m in enumerate(modes):
+        sel = m != "reuse"
+        layers[l] = _CLayer(_LAYER_MODE[m], q[l].data_ptr(), q_idx[j].data_ptr() if sel else None,
+                            w[j].data_ptr() if sel else None, out[l].data_ptr(), lse[l].data_ptr(),
+                            win_rings[l].data_ptr() if W else None, new_win[l].data_ptr() if W else None)
+        j += sel
+    _check(lib().mla_csa2_group_step(
+        _crow(main_row), _crow(idx_row), out.shape[-1], L, C.c_void_p(C.addressof(layers)), _ptr(new_main), _ptr(new_idx), _ptr(slots), n_new,
+        _ptr(main_cache), _cache_stride(main_cache, "main_cache"), _ptr(idx_cache),
+        _cache_stride(idx_cache, "idx_cache"), idx_cache.shape[1], _ptr(n_visible), B, H, H_I, k,
+        float(score_scale), float(softmax_scale), _ptr(win_pos), _ptr(win_len), W, wfmt, int(bool(score_bf16)),
+        pool_blocks, pool_block, _ptr(pool_scores), _ptr(pool_pos), _ptr(idx_out[0]), _ptr(idx_out[1]),
+        _ptr(topk_workspace), topk_workspace.numel(), _ptr(decode_workspace), decode_workspace.numel(),
+        _stream(stream)))
+    attended, j = [], 0
+    for m in modes:
+        if m != "reuse":
+            latest = idx_out[j % 2]
+            j += 1
         attended.append(latest)
     return attended

@@ -320,7 +320,7 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
     return hip_status(mla::prof_read(k, launches, total_ms), "mla_profile_read");
 }
 
-int32_t mla_version(void) { return 104; }
+int32_t mla_version(void) { return 105; }
 
 mla_status_t mla_set_option(const char* name, int64_t value) {
     if (!name) return fail(MLA_ERR_INVALID_ARG, "mla_set_option: NULL name");
@@ -684,6 +684,103 @@ mla_status_t mla_sparse_decode_noalloc(mla_row_t main_row, int32_t d_v, const vo
     if (need > 0 && !(ws = device_scratch())) return MLA_ERR_HIP;
     return mla_sparse_decode(main_row, d_v, q, main_cache, main_seq_stride, capacity, idx, k, win_ring, win_len, W,
                              win_fmt, softmax_scale, epilogue, B, H, out, lse, ws, ws ? kScratchBytes : 0, stream);
+}
+
+
+mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t d_v, int32_t n_layers,
+                                 const mla_group_layer_t* layers, const float* new_main, const float* new_idx,
+                                 const int32_t* slots, int32_t n_new, void* main_cache, int64_t main_seq_stride,
+                                 void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
+                                 const int32_t* n_visible, int32_t B, int32_t H, int32_t H_I, int32_t k,
+                                 float score_scale, float softmax_scale, const int32_t* win_pos,
+                                 const int32_t* win_len, int32_t W, int32_t win_fmt, int32_t score_bf16,
+                                 int32_t pool_blocks, int32_t pool_block, float* pool_scores, int32_t* pool_pos,
+                                 int32_t* idx_a, int32_t* idx_b, void* topk_workspace, size_t topk_workspace_bytes,
+                                 void* decode_workspace, size_t decode_workspace_bytes, void* stream) {
+    mla::begin_call();
+    // the group's own arguments, every layer's, and the workspace sizes: checked before the
+    // first launch (the calls below check the shared arguments again, identically each time)
+    if (n_layers < 1 || !layers) return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: needs at least one layer");
+    if (!idx_a || !idx_b || !aligned(idx_a, 4) || !aligned(idx_b, 4))
+        return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: needs two 4-byte aligned index buffers");
+    if (pool_blocks < 0 || (pool_blocks > 0 && (!pool_scores || !pool_pos)))
+        return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: a pool needs pool_scores and pool_pos");
+    bool selected = false;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const mla_group_layer_t& y = layers[l];
+        if (y.mode != MLA_LAYER_FULL && y.mode != MLA_LAYER_REINDEX && y.mode != MLA_LAYER_REUSE)
+            return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: layer %d has an unknown mode %d", l, y.mode);
+        if (y.mode == MLA_LAYER_REUSE && !selected)
+            return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: layer %d reuses indices no earlier layer selected", l);
+        selected = true;
+        if (!y.q || !y.out || !y.lse || !aligned(y.q, 16) || !aligned(y.out, 16) || !aligned(y.lse, 4))
+            return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: layer %d needs q, out (16-byte aligned) and lse", l);
+        if (y.mode != MLA_LAYER_REUSE && (!y.q_idx || !y.w || !aligned(y.q_idx, 16) || !aligned(y.w, 4)))
+            return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: selecting layer %d needs q_idx (16-byte aligned) and w",
+                        l);
+        if (W > 0 && (!y.win_ring || !y.new_win || !aligned(y.win_ring, win_fmt == MLA_FMT_MXFP8 ? 2 : 16) ||
+                      !aligned(y.new_win, 16)))
+            return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: layer %d needs its window ring and entry (aligned)", l);
+    }
+    if (B < 0 || H < 1 || k < 0 || capacity < 0 || W < 0)
+        return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: B, H, k, capacity or W out of range");
+    const size_t need_topk = std::max(mla_indexer_topk_workspace(B, capacity, k),
+                                      pool_blocks > 0 ? mla_indexer_pool_workspace(B, capacity, pool_block) : 0);
+    if (!topk_workspace || topk_workspace_bytes < need_topk)
+        return fail(MLA_ERR_WORKSPACE, "csa2_group_step: top-k workspace %zu bytes, needs %zu", topk_workspace_bytes,
+                    need_topk);
+    const size_t need_dec = mla_sparse_decode_workspace(main_row, d_v, B, H, k, W, win_fmt);
+    if (need_dec > 0 && (!decode_workspace || decode_workspace_bytes < need_dec))
+        return fail(MLA_ERR_WORKSPACE, "csa2_group_step: decode workspace %zu bytes, needs %zu",
+                    decode_workspace_bytes, need_dec);
+
+    struct Scope {                                         // one kernel record for the whole group
+        Scope() { mla::group_begin(); }
+        ~Scope() { mla::group_end(); }
+    } scope;
+    const int32_t Dw = main_row.dim + main_row.rope_dim;
+    int32_t* bufs[2] = {idx_a, idx_b};
+    int32_t* latest = nullptr;
+    int j = 0;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const mla_group_layer_t& y = layers[l];
+        mla_status_t st = MLA_OK;
+        if (y.mode != MLA_LAYER_REUSE) {                   // full / reindex: select with the layer's own query
+            latest = bufs[j % 2];
+            float* scores = (pool_blocks > 0 && y.mode == MLA_LAYER_FULL) ? pool_scores : nullptr;
+            if (l == 0) {                                  // carrying the step's append (and window entry)
+                st = (score_bf16 ? mla_append_indexer_topk_bf16 : mla_append_indexer_topk)(
+                    main_row, idx_row, new_main, new_idx, slots, n_new, new_main ? main_cache : nullptr,
+                    main_seq_stride, idx_cache, idx_seq_stride, capacity, W > 0 ? y.new_win : nullptr,
+                    W > 0 ? win_pos : nullptr, W > 0 ? y.win_ring : nullptr, W > 0 ? W : 0, W > 0 ? Dw : 0, win_fmt,
+                    y.q_idx, y.w, score_scale, n_visible, B, H_I, k, latest, scores, topk_workspace,
+                    topk_workspace_bytes, stream);
+            } else {                                       // a Reindex layer with a pool scores the pool only
+                const bool use_pool = pool_blocks > 0 && y.mode == MLA_LAYER_REINDEX;
+                st = (score_bf16 ? mla_indexer_topk_bf16 : mla_indexer_topk)(
+                    idx_row, y.q_idx, y.w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
+                    use_pool ? pool_pos : nullptr, use_pool ? pool_blocks * pool_block : 0, B, H_I, k, latest, scores,
+                    topk_workspace, topk_workspace_bytes, stream);
+            }
+            if (st == MLA_OK && scores)                    // the Full layer publishes the candidate pool
+                st = mla_indexer_pool(scores, capacity, n_visible, B, pool_block, pool_blocks, pool_pos,
+                                      topk_workspace, topk_workspace_bytes, stream);
+            if (st != MLA_OK) return st;
+            ++j;
+        }
+        if (l > 0 && W > 0)                                // the layer's window entry in its decode's call
+            st = mla_append_sparse_decode(main_row, d_v, y.q, main_cache, main_seq_stride, capacity, latest, k,
+                                          y.new_win, win_pos, y.win_ring, win_len, W, win_fmt, softmax_scale,
+                                          nullptr, B, H, y.out, y.lse, decode_workspace, decode_workspace_bytes,
+                                          stream);
+        else
+            st = mla_sparse_decode(main_row, d_v, y.q, main_cache, main_seq_stride, capacity, latest, k,
+                                   W > 0 ? y.win_ring : nullptr, W > 0 ? win_len : nullptr, W > 0 ? W : 0, win_fmt,
+                                   softmax_scale, nullptr, B, H, y.out, y.lse, decode_workspace,
+                                   decode_workspace_bytes, stream);
+        if (st != MLA_OK) return st;
+    }
+    return ok();
 }
 
 }  // extern "C"

@@ -175,6 +175,9 @@ int option_index(const char* name);     // -1 for an unknown name
 bool option_set(int i, int64_t v);      // false when out of range
 // The kernels the calling thread's current API call launches (mla_last_kernels).
 void begin_call();
+// Between these, the calls a group call makes add to one record (begin_call does not reset it).
+void group_begin();
+void group_end();
 void note_launch(const void* f);
 const char* launched_names();
 

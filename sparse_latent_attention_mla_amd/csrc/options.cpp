@@ -33,7 +33,7 @@ const OptDef kOpts[OPT_COUNT] = {
 };
 std::atomic<int64_t> g_opt[OPT_COUNT];
 
-constexpr int kMaxNoted = 16;
+constexpr int kMaxNoted = 64;
 thread_local const void* t_launched[kMaxNoted];
 thread_local int t_n = 0;
 thread_local std::string t_names;
@@ -54,7 +54,16 @@ bool option_set(int i, int64_t v) {
     return true;
 }
 
-void begin_call() { t_n = 0; }
+thread_local bool t_group = false;                      // inside mla_csa2_group_step
+
+void begin_call() {
+    if (!t_group) t_n = 0;
+}
+void group_begin() {
+    t_n = 0;
+    t_group = true;
+}
+void group_end() { t_group = false; }
 
 void note_launch(const void* f) {
     if (t_n < kMaxNoted) t_launched[t_n++] = f;

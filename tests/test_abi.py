@@ -160,6 +160,35 @@ def test_host_validation_rejects_before_launch(M):
                                    C.c_void_p(0x100000), 1 << 30, None) == want, (sk, r, cs)
 
 
+def test_group_step_rejects_before_launch(M):
+    """mla_csa2_group_step checks the group and every layer before its first launch."""
+    L = M.lib()
+    r_main, r_idx = _row(M, M.E2M1_S16, 512), _row(M, M.E2M1_S16, 128)
+    a, fake = 0x10000, C.c_void_p(0x10000)
+
+    def layer(mode, q=a, win=None):
+        return M._CLayer(mode, q, a, a, a, a, win, a if win else None)
+
+    def call(layers, W=0, topk_bytes=1 << 30, dec_bytes=1 << 30, idx_b=fake, pool=(0, 8, None, None)):
+        arr = (M._CLayer * len(layers))(*layers)
+        return L.mla_csa2_group_step(r_main, r_idx, 512, len(layers), C.cast(arr, C.c_void_p), fake, fake, fake, 1,
+                                     fake, 288 * 1000, fake, 72 * 1000, 1000, fake, 2, 64, 64, 512, 0.1, 0.04,
+                                     fake, fake, W, M.BF16, 0, *pool, fake, idx_b, C.c_void_p(0x100000), topk_bytes,
+                                     C.c_void_p(0x200000), dec_bytes, None)
+    full, reuse = 0, 2
+    assert call([layer(full), layer(7)]) == 1                       # unknown mode
+    assert b"mode" in L.mla_last_error()
+    assert call([layer(reuse), layer(full)]) == 1                   # nothing selected yet
+    assert call([layer(full), layer(reuse, q=a + 2)]) == 1          # misaligned query
+    assert call([layer(full), layer(reuse)], W=128) == 1            # a window without rings
+    assert call([layer(full)], idx_b=None) == 1                     # one index buffer
+    assert call([layer(full)], pool=(16, 8, None, None)) == 1       # a pool without its arrays
+    assert call([], W=0) == 1                                       # no layers
+    assert call([layer(full), layer(reuse)], topk_bytes=64) == 3    # short workspaces
+    assert call([layer(full), layer(reuse)], dec_bytes=64) == 3
+    assert b"decode workspace" in L.mla_last_error()
+
+
 def test_workspace_queries(M):
     assert M.mla_indexer_topk_workspace(4, 131072, 2048) >= 4 * 131072 * (4 + 8)
     # the pool's selection runs over capacity / block block scores

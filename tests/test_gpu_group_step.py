@@ -175,3 +175,47 @@ def test_group_helper_rejects_unknown_and_leading_reuse():
                                 slots=x["slots"], win_rings=case.g_win.clone(), new_win=x["new_win"],
                                 win_pos=x["win_pos"], win_len=x["win_len"])
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,pool,score_bf16", [("c1", 0, False), ("c3d", 0, False), ("c4d", 0, False),
+                                                  ("c5s", 0, False), ("c5d", 0, False), ("c5d", 96, False),
+                                                  ("c5d", 0, True), ("c3d", 0, True)])
+def test_native_group_step_equals_the_helper(name, pool, score_bf16):
+    """mla_csa2_group_step (one C call) against csa2_group_step (the same calls from Python):
+    the caches and window rings byte for byte, the selected sets, the pool's positions, and
+    the outputs (the same kernels; the order of a selection's positions, and with it the
+    decode's summation order, may differ); every layer's decode in the call's kernel record."""
+    cfg = CFGS[name]
+    say("native", name, "pool", pool, "bf16 scores", score_bf16)
+    case = G.build_case(cfg, seed=3)
+    L = len(cfg.layers)
+    runs = []
+    for native in (False, True):
+        x = _inputs(case, pool)
+        main, idx = case.g_main.clone(), case.g_idx.clone()
+        win = case.g_win.clone() if cfg.W else None
+        out, lse, bufs = _outs(cfg)
+        fn = G.M.mla_csa2_group_step if native else G.M.csa2_group_step
+        att = fn(G.main_row(cfg), G.idx_row(cfg), cfg.layers, main, idx, x["nvis"], cfg.k, cfg.sigma,
+                 cfg.softmax_scale, x["q"], x["q_idx"], x["w"], out, lse, x["ws"], x["wsd"], bufs,
+                 new_main=x["new_main"], new_idx=x["new_idx"], slots=x["slots"], win_rings=win,
+                 new_win=x.get("new_win"), win_pos=x.get("win_pos"), win_len=x.get("win_len"), pool=x["pool"],
+                 score_bf16=score_bf16)
+        launched = G.M.mla_last_kernels()
+        att = [a.clone() for a in att]
+        torch.cuda.synchronize()
+        runs.append((main, idx, win, out, lse, att, x["pool"][3].clone() if pool else None, launched))
+    (m0, i0, w0, o0, l0, a0, p0, _), (m1, i1, w1, o1, l1, a1, p1, launched) = runs
+    assert sum("k_decode" in n for n in launched) == L, launched       # one record for the whole group
+    assert torch.equal(m0, m1) and torch.equal(i0, i1)
+    if cfg.W:
+        assert torch.equal(w0.view(torch.uint8), w1.view(torch.uint8))
+    for l in range(L):
+        assert np.array_equal(np.sort(a0[l].cpu().numpy(), 1), np.sort(a1[l].cpu().numpy(), 1)), l
+    if pool:
+        pa, pb = p0.cpu().numpy(), p1.cpu().numpy()
+        for b in range(cfg.B):                   # the same blocks (block order unspecified)
+            blocks = lambda p: sorted(map(tuple, p[b].reshape(-1, POOL_BLOCK).tolist()))
+            assert blocks(pa) == blocks(pb), b
+    G.check_attention(o1.cpu().numpy().reshape(-1, cfg.H, cfg.d_v), l1.cpu().numpy().reshape(-1, cfg.H),
+                      o0.cpu().numpy().reshape(-1, cfg.H, cfg.d_v), l0.cpu().numpy().reshape(-1, cfg.H), rel=1e-5)

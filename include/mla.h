@@ -161,7 +161,9 @@ mla_status_t mla_profile_read(const char* kernel, int32_t* launches, double* tot
  *   "scan_queues"            0..1       1: the queue-fed 32x32 indexer scan
  *   "scan_blocks"            0..65536   target number of 4-wave indexer-scan workgroups
  *   "decode_rows_per_split"  0..256     selected rows per decode split (a multiple of 32 up to
- *                                       256 for E4M3 rows, 128 for bf16 and E2M1 rows)
+ *                                       256 for E4M3 rows, 128 for E2M1 rows and bf16 rows
+ *                                       decoded 16 heads per workgroup; a multiple of 64 from
+ *                                       64 for bf16 rows decoded 32 heads per workgroup)
  * Values in range that a kernel cannot use are ignored. Errors:
  * MLA_ERR_INVALID_ARG (unknown name, NULL pointer, value out of range).
  */

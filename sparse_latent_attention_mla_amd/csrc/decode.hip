@@ -536,20 +536,27 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         lse_part[prow] = (l > 0.0f) ? (M + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
 }
 
-// Gather-all split for bf16 rows (and bf16 window entries), two head tiles of 16 heads
-// per workgroup: waves 0-3 serve heads 32 hp .. + 15, waves 4-7 heads 32 hp + 16 .. + 31,
-// over the same 128 staged rows, so each row crosses into a CU once per 32 heads. The
-// queries go from memory straight into each wave's operand registers (LDS holds the
-// rows, P and the reductions); otherwise the phases are decode_split_g's: QK on the
-// wave's two row tiles, an exact softmax per head tile, PV with the wave owning 128
-// value channels of its head tile.
+// Split for bf16 rows (and bf16 window entries), two head tiles of 16 heads per
+// workgroup: waves 0-3 serve heads 32 hp .. + 15, waves 4-7 heads 32 hp + 16 .. + 31,
+// over the same staged rows, so each row crosses into a CU once per 32 heads. A split
+// of up to kMaxRows rows streams through two LDS buffers of kC rows: the next chunk's
+// rows are gathered while the current one is contracted, and the softmax runs online
+// over the chunks (running maximum per head; the output and the running sum rescaled
+// when it grows), so one workgroup per CU covers as many rows as one round of the CUs
+// needs and the split's partial is written once. The queries go from memory straight
+// into each wave's operand registers. Per chunk: QK on the wave's row tile, the chunk's
+// maximum per head tile, P for the chunk, PV with the wave owning 128 value channels of
+// its head tile. The pairs of a split (one XCD) take its chunks in rotated order, so
+// that a chunk's rows come from HBM for one pair and from the L2 for the others.
 namespace gd2 {
-constexpr int kR = 128;
+constexpr int kC = 64;                                     // rows per chunk
+constexpr int kMaxRows = 512;                              // rows per split at most
 constexpr int kVS = 1056;                                  // bytes per staged row (512 bf16 + 32)
-constexpr int kPStride = kR + 4;                           // fp32 per head in P
-constexpr int kP = kR * kVS;                               // P [32 heads][kPStride]
-constexpr int kIdx = kP + 32 * kPStride * 4;               // row indices [kR]
-constexpr int kRed = kIdx + kR * 4;                        // [2][8 waves][16 heads]
+constexpr int kBuf = kC * kVS;                             // one chunk's rows
+constexpr int kPStride = kC + 4;                           // fp32 per head in P
+constexpr int kP = 2 * kBuf;                               // P [32 heads][kPStride]
+constexpr int kIdx = kP + 32 * kPStride * 4;               // row indices [kMaxRows]
+constexpr int kRed = kIdx + kMaxRows * 4;                  // [2][8 waves][16 heads]
 constexpr int kBytes = kRed + 2 * 8 * 16 * 4;
 }  // namespace gd2
 
@@ -557,24 +564,41 @@ template <int DQK>
 __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* smem, int b, int split, int S,
                                                   int hp, bool is_win, int64_t first, int n, float* o_part,
                                                   float* lse_part) {
-    constexpr int R = gd2::kR, VS = gd2::kVS;
+    constexpr int C = gd2::kC, VS = gd2::kVS;
     constexpr bool kRope = DQK == 576;
-    constexpr int NMAIN = 16, NQ = DQK / 32, NT = 2;      // row tiles per wave: wq and wq + 4
+    constexpr int NMAIN = 16, NQ = DQK / 32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hs = w >> 2, wq = w & 3;                     // the wave's head tile in the pair, its place there
+    const int hs = w >> 2, wq = w & 3;                     // the wave's head tile in the pair, its row tile
     const int j = lane & 15, g = lane >> 4;
     uint8_t* V = smem;
     float* P = reinterpret_cast<float*>(smem + gd2::kP);
     int32_t* ridx = reinterpret_cast<int32_t*>(smem + gd2::kIdx);
     float* red = reinterpret_cast<float*>(smem + gd2::kRed);
     constexpr float kLog2e = 1.4426950408889634f;
+    constexpr float kNegInf = -__builtin_inff();
     const float zscale = a.scale * kLog2e;
     const uint8_t* row_base = is_win ? reinterpret_cast<const uint8_t*>(a.win + (int64_t)b * a.W * DQK)
                                      : a.cache + b * a.stride;
     const uint32_t row_bytes = is_win ? 2 * DQK : (uint32_t)a.row_bytes;
+    const int nch = (n + C - 1) / C;                       // n <= kMaxRows (the launcher's split)
 
-    if (tid < R) {
+    // the pair's 32 heads' queries (registers, then LDS in the second row buffer) and the
+    // row indices (thread u: row u of the split; -1 past n, negative or out of range),
+    // every load issued before the first store
+    constexpr int kPer = DQK / 8;                          // 16-byte pieces per head
+    constexpr int kIt = (32 * kPer + 511) / 512;
+    static_assert(gd2::kBuf + 32 * gd::kQStride <= 2 * gd2::kBuf, "the staged queries fit the second buffer");
+    static_assert(gd2::kMaxRows <= 512, "one row index per thread");
+    uint8_t* Q = V + gd2::kBuf;
+    {
+        const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + 32 * hp) * DQK;
+        u32x4 qs[kIt];
+#pragma unroll
+        for (int i = 0; i < kIt; ++i) {
+            const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
+            if (it < 32 * kPer) qs[i] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)hh * DQK + 8 * pc);
+        }
         int32_t r = -1;
         if (tid < n) {
             if (is_win) r = (int32_t)(first + tid);
@@ -583,152 +607,153 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
                 if (s >= 0 && s < a.capacity) r = s;
             }
         }
-        ridx[tid] = r;
-    }
-    // the pair's 32 heads' queries, staged once in the value region (every load issued before
-    // the first store), then read by each wave into the B operands of its 16 heads (channels
-    // 32 st + 8 g .. of head j); the gather overwrites the region only after every wave's reads
-    {
-        constexpr int kPer = DQK / 8;                      // 16-byte pieces per head
-        constexpr int kIt = (32 * kPer + 511) / 512;
-        static_assert(32 * gd::kQStride <= R * VS, "the staged queries fit the value region");
-        const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.H + 32 * hp) * DQK;
-        u32x4 qs[kIt];
+        if (tid < nch * C) ridx[tid] = r;
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
             const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
-            if (it < 32 * kPer) qs[i] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)hh * DQK + 8 * pc);
-        }
-#pragma unroll
-        for (int i = 0; i < kIt; ++i) {
-            const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
-            if (it < 32 * kPer) *reinterpret_cast<u32x4*>(V + hh * gd::kQStride + 16 * pc) = qs[i];
+            if (it < 32 * kPer) *reinterpret_cast<u32x4*>(Q + hh * gd::kQStride + 16 * pc) = qs[i];
         }
     }
     __syncthreads();                                       // the row indices and the queries
-    u32x4 qv[NQ];
-    {
-        const uint8_t* qh = V + (16 * hs + j) * gd::kQStride + 16 * g;
-#pragma unroll
-        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
-    }
-    lds_barrier();                                         // every wave's query reads done: the region is free
 
-    // ---- gather: one row per load instruction, every load issued at once; the pairs of a
-    // split (one XCD) start at different quarters of its rows, so that a row's first requests
-    // come from different pairs and the L2 merges the others into them
     const uint32_t v_m0 = __builtin_amdgcn_readfirstlane(lds_addr(V));
-    uint32_t zmask = 0;
-    constexpr int PW = R / 8;
-    const int rot = (hp & 3) * (R / 4);                    // (a multiple of 8: a wave keeps its rows)
-#pragma unroll 4
-    for (int i = 0; i < PW; ++i) {
-        const int u = (w + 8 * i + rot) % R;
-        const int32_t r = ridx[u];
-        zmask |= r < 0 ? (1u << i) : 0u;
-        const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * lane
-                                    : reinterpret_cast<const uint8_t*>(a.q);
-        dma16(src, __builtin_amdgcn_readfirstlane(v_m0 + (uint32_t)(VS * u)));
-    }
-    u32x4 rope[NT][2];
-    if constexpr (kRope) {
+    const int rot = nch > 0 ? hp % nch : 0;
+    auto chunk_of = [&](int c) { const int cc = c + rot; return cc >= nch ? cc - nch : cc; };
+    // gather chunk c into buffer c & 1: one row per load instruction (wave w: rows w + 8 i),
+    // rows with no entry loaded from the queries (any readable bytes) and zeroed once landed;
+    // the RoPE part of the wave's row tile straight into registers
+    u32x4 rope_c[2], rope_n[2];
+    uint32_t zm_c = 0, zm_n = 0;
+    auto issue = [&](int c) {
+        const int base = C * chunk_of(c);
+        const uint32_t m0 = v_m0 + (uint32_t)((c & 1) * gd2::kBuf);
+        uint32_t zm = 0;
+        const int32_t rv = ridx[base + w + 8 * (lane & 7)];  // lane i < 8: the entry of row w + 8 i
 #pragma unroll
-        for (int m = 0; m < NT; ++m) {
-            const int tt = wq + 4 * m;
-            const int32_t r = ridx[16 * tt + j];
+        for (int i = 0; i < C / 8; ++i) {
+            const int u = w + 8 * i;
+            const int32_t r = __builtin_amdgcn_readlane(rv, i);
+            zm |= r < 0 ? (1u << i) : 0u;
+            const uint8_t* src = r >= 0 ? row_base + (uint64_t)(uint32_t)r * row_bytes + 16 * lane
+                                        : reinterpret_cast<const uint8_t*>(a.q);
+            dma16(src, __builtin_amdgcn_readfirstlane(m0 + (uint32_t)(VS * u)));
+        }
+        zm_n = zm;
+        if constexpr (kRope) {
+            const int32_t r = ridx[base + 16 * wq + j];
             const uint8_t* rp = row_base + (uint64_t)(uint32_t)(r < 0 ? 0 : r) * row_bytes + 1024;
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-                rope[m][s2] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 2 * (32 * s2 + 8 * g))
-                                     : u32x4{0u, 0u, 0u, 0u};
+                rope_n[s2] = r >= 0 ? *reinterpret_cast<const u32x4*>(rp + 2 * (32 * s2 + 8 * g))
+                                    : u32x4{0u, 0u, 0u, 0u};
         }
-    }
-    wait_vmcnt<0>();
-    if (__builtin_amdgcn_ballot_w64(zmask != 0u)) {
-        for (int i = 0; i < PW; ++i)
-            if ((zmask >> i) & 1u)
-                *reinterpret_cast<u32x4*>(V + VS * ((w + 8 * i + rot) % R) + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
+    };
 
-    // ---- A: scores of the wave's two row tiles for its 16 heads
-    float z[NT][4];
+    // chunk 0 into the first buffer while each wave reads its 16 heads' queries into the
+    // B operands (channels 32 st + 8 g .. of head j) from the second, which chunk 1
+    // overwrites only after the barrier that every wave reaches after these reads
+    if (nch > 0) issue(0);
+    u32x4 qv[NQ];
+    {
+        const uint8_t* qh = Q + (16 * hs + j) * gd::kQStride + 16 * g;
 #pragma unroll
-    for (int m = 0; m < NT; ++m) {
-        const int tt = wq + 4 * m;
-        const bool live = 16 * tt < n;
+        for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
+    }
+    f32x4 o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float M = kNegInf, sloc = 0.0f;                        // running maximum (head j, base 2), the lane's sum
+    float* Ph = P + (16 * hs + j) * gd2::kPStride;
+    for (int c = 0; c < nch; ++c) {
+        zm_c = zm_n;
+        if constexpr (kRope) {
+            rope_c[0] = rope_n[0];
+            rope_c[1] = rope_n[1];
+        }
+        uint8_t* Vb = V + (c & 1) * gd2::kBuf;
+        wait_vmcnt<0>();                                   // chunk c landed
+        if (__builtin_amdgcn_ballot_w64(zm_c != 0u)) {
+            for (int i = 0; i < C / 8; ++i)
+                if ((zm_c >> i) & 1u) *reinterpret_cast<u32x4*>(Vb + VS * (w + 8 * i) + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();                                   // its rows; every wave is done with chunk c - 1
+        if (c + 1 < nch) issue(c + 1);                     // into chunk c - 1's buffer
+
+        // ---- QK: the wave's row tile of the chunk for its 16 heads
+        const int base = C * chunk_of(c);
+        const int nc = (n - base < C) ? n - base : C;
+        const bool live = 16 * wq < nc;
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
         if (live) {
-            const uint8_t* krow = V + (16 * tt + j) * VS;
+            const uint8_t* krow = Vb + (16 * wq + j) * VS;
 #pragma unroll
             for (int st = 0; st < NMAIN; ++st)
                 acc = mfma_bf16(*reinterpret_cast<const u32x4*>(krow + 2 * (32 * st + 8 * g)), qv[st], acc);
             if constexpr (kRope) {
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) acc = mfma_bf16(rope[m][s2], qv[NMAIN + s2], acc);
+                for (int s2 = 0; s2 < 2; ++s2) acc = mfma_bf16(rope_c[s2], qv[NMAIN + s2], acc);
             }
         }
+        float z[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * tt + 4 * g + r;
-            z[m][r] = (live && ridx[row] >= 0) ? acc[r] * zscale : -__builtin_inff();
+            const int row = 16 * wq + 4 * g + r;
+            z[r] = (live && ridx[base + row] >= 0) ? acc[r] * zscale : kNegInf;
         }
-    }
 
-    // ---- B: exact softmax over the split's rows per head tile (base 2)
-    float mloc = -__builtin_inff();
+        // ---- the chunk's maximum per head across the head tile's four waves, then P
+        float mloc = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        if (g == 0) red[16 * w + j] = mloc;
+        lds_barrier();
+        float Mn = M;
 #pragma unroll
-    for (int m = 0; m < NT; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, z[m][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    if (g == 0) red[16 * w + j] = mloc;
-    __syncthreads();
-    float M = red[16 * (4 * hs) + j];
-#pragma unroll
-    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, red[16 * (4 * hs + ww) + j]);
-    float* Ph = P + (16 * hs + j) * gd2::kPStride;
-    float sloc = 0.0f;
-#pragma unroll
-    for (int m = 0; m < NT; ++m) {
-        const int tt = wq + 4 * m;
+        for (int ww = 0; ww < 4; ++ww) Mn = fmaxf(Mn, red[16 * (4 * hs + ww) + j]);
+        // what has been accumulated, rescaled to the new maximum (nothing yet while it is -inf)
+        const float alpha = (Mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+        M = Mn;
         f32x4 pv4;
+        float s4 = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pv4[r] = (z[m][r] == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(z[m][r] - M);
-            sloc += pv4[r];
+            pv4[r] = (z[r] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(z[r] - M);
+            s4 += pv4[r];
         }
-        *reinterpret_cast<f32x4*>(Ph + 16 * tt + 4 * g) = pv4;
-    }
-    sloc += __shfl_xor(sloc, 16, 64);
-    sloc += __shfl_xor(sloc, 32, 64);
-    if (g == 0) red[128 + 16 * w + j] = sloc;
-    __syncthreads();
+        *reinterpret_cast<f32x4*>(Ph + 16 * wq + 4 * g) = pv4;
+        sloc = sloc * alpha + s4;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[mt][r] *= alpha;
+        lds_barrier();                                     // the chunk's P
 
-    // ---- C: PV over every row for value channels 128 wq .. 128 wq + 127 of the head tile
-    f32x4 o[8];
+        // ---- PV over the chunk's rows for value channels 128 wq .. 128 wq + 127 of the head tile
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int st = 0; st < R / 32; ++st) {
-        if (32 * st >= n) break;
-        const float* pr = Ph + 32 * st + 8 * g;
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
-        const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-        u32x4 pa, pb;
-        split_bf16x8(p, pa, pb);
+        for (int st = 0; st < C / 32; ++st) {
+            if (32 * st >= nc) break;
+            const float* pr = Ph + 32 * st + 8 * g;
+            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+            const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            u32x4 pa, pb;
+            split_bf16x8(p, pa, pb);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int c0 = 128 * wq + 16 * mt;
-            const uint8_t* vp = V + (32 * st + 8 * g + (j >> 2)) * VS + 2 * (c0 + 4 * (j & 3));
-            const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * VS);
-            const u32x4 av = u32x4{r0.x, r0.y, r1.x, r1.y};
-            o[mt] = mfma_bf16(av, pa, o[mt]);
-            o[mt] = mfma_bf16(av, pb, o[mt]);
+            for (int mt = 0; mt < 8; ++mt) {
+                const int c0 = 128 * wq + 16 * mt;
+                const uint8_t* vp = Vb + (32 * st + 8 * g + (j >> 2)) * VS + 2 * (c0 + 4 * (j & 3));
+                const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * VS);
+                const u32x4 av = u32x4{r0.x, r0.y, r1.x, r1.y};
+                o[mt] = mfma_bf16(av, pa, o[mt]);
+                o[mt] = mfma_bf16(av, pb, o[mt]);
+            }
         }
     }
 
     // ---- the split's partial for the wave's head tile
+    sloc += __shfl_xor(sloc, 16, 64);
+    sloc += __shfl_xor(sloc, 32, 64);
+    if (g == 0) red[128 + 16 * w + j] = sloc;
+    lds_barrier();
     float l = red[128 + 16 * (4 * hs) + j];
 #pragma unroll
     for (int ww = 1; ww < 4; ++ww) l += red[128 + 16 * (4 * hs + ww) + j];
@@ -1097,9 +1122,46 @@ Geometry gather_geometry(int fmt, int B, int H, int k, int W) {
     return g;
 }
 
+// Two head tiles per workgroup for bf16 rows when one head tile per workgroup would
+// take more than one round of the CUs: each row is then staged once per 32 heads.
+static bool use_pairs(int fmt, int B, int H, const Geometry& g) {
+    return fmt == MLA_FMT_BF16 && H % 32 == 0 && (int64_t)B * (g.S_main + g.S_win) * g.groups > 256;
+}
+
+// Splits of the paired decode, which streams its rows in chunks of 64: the fewest
+// rows per split (64 .. 512, doubling) that keep the grid within one round of
+// workgroups (one per CU), else 512; 128 window slots per split. The option
+// decode_rows_per_split, when a multiple of 64, overrides the main rows per split.
+static Geometry pair_geometry(int B, int H, int k, int W) {
+    Geometry g{};
+    g.groups = H / 32;
+    int rps = 64;
+    const int rpw = 128;
+    const int v = (int)option(OPT_DECODE_RPS);
+    const int64_t S_win = (W + rpw - 1) / rpw;
+    if (v >= 64 && v <= 512 && v % 64 == 0) {
+        rps = v;
+    } else {
+        while (rps < 512 && (int64_t)B * g.groups * ((k + rps - 1) / rps + S_win) > 256) rps *= 2;
+    }
+    g.rps = rps;
+    g.rps_win = rpw;
+    g.S_main = (k + rps - 1) / rps;
+    g.S_win = (int)S_win;
+    return g;
+}
+
+// The splits the MFMA decode runs with (pairs: whether it pairs head tiles).
+static Geometry decode_geometry(int fmt, int B, int H, int k, int W, bool* pairs) {
+    const Geometry g = gather_geometry(fmt, B, H, k, W);
+    *pairs = use_pairs(fmt, B, H, g);
+    return *pairs ? pair_geometry(B, H, k, W) : g;
+}
+
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W) {
     if (!mfma_shape(fmt, dim, rope, d_v, H)) return 0;
-    const Geometry g = gather_geometry(fmt, B, H, k, W);
+    bool pairs = false;
+    const Geometry g = decode_geometry(fmt, B, H, k, W, &pairs);
     const size_t S = (size_t)(g.S_main + g.S_win);
     const size_t o = (size_t)B * S * H * kDv * sizeof(float);
     const size_t l = (size_t)B * S * H * sizeof(float);
@@ -1146,12 +1208,6 @@ static hipError_t launch_pair(const DecodeArgs& a, const Geometry& g, float* o_p
                          g.rps, g.rps_win, pairs, n_items, o_part, lse_part);
 }
 
-// Two head tiles per workgroup for bf16 rows when one head tile per workgroup would
-// take more than one round of the CUs: each row is then staged once per 32 heads.
-static bool use_pairs(int fmt, int B, int H, const Geometry& g) {
-    return fmt == MLA_FMT_BF16 && H % 32 == 0 && (int64_t)B * (g.S_main + g.S_win) * g.groups > 256;
-}
-
 // An MXFP8 window ring [B, W, D + D/32 bytes] widened to bf16 rows [B, W, D]:
 // the E4M3 value times its block's power of two, formed in fp32 (exact) and
 // rounded to bf16, exact unless the product lies below bf16's smallest
@@ -1178,8 +1234,9 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
     // MXFP8 window entries of 512 channels (16-byte aligned) are widened inside the gather
     // decode's staging; others are first widened to a bf16 copy after the decode's own workspace
     const bool mfma = mfma_shape(a.fmt, a.dim, a.rope, a.d_v, a.H);
-    const Geometry g = gather_geometry(a.fmt, a.B, a.H, a.k, (a.win || a.win8) ? a.W : 0);
-    const bool pairs = mfma && use_pairs(a.fmt, a.B, a.H, g);
+    bool pairs = false;
+    const Geometry g = decode_geometry(a.fmt, a.B, a.H, a.k, (a.win || a.win8) ? a.W : 0, &pairs);
+    pairs = pairs && mfma;
     const bool win8_inline = a.win8 && mfma && !pairs && a.dim + a.rope == 512 &&
                              reinterpret_cast<uintptr_t>(a.win8) % 16 == 0;
     if (a.win8 && a.W > 0 && !win8_inline) {

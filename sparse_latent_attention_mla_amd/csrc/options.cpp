@@ -29,7 +29,8 @@ const OptDef kOpts[OPT_COUNT] = {
     {"scan_queues", 0, 1},        // 1: the queue-fed 32x32 scan instead of the static partition
     {"scan_blocks", 0, 65536},    // target number of 4-wave scan workgroups (0: two per CU)
     {"decode_rows_per_split", 0, 256},   // selected rows per decode split (0: by shape; else 32 .. 256 (128 for
-                                         // rows other than E4M3), a multiple of 32)
+                                         // E2M1 and unpaired bf16 rows), a multiple of 32; a multiple of 64
+                                         // for the paired bf16 decode)
 };
 std::atomic<int64_t> g_opt[OPT_COUNT];
 

@@ -1,7 +1,10 @@
 """The sparse decode over bf16 rows when one workgroup serves two head tiles (32
 heads) of a split: the launch picks it when one head tile per workgroup would take
-more than one round of the CUs. Against the oracle's attention over the same
-rows and index sets, at the spec bar; the test asserts the kernel that ran."""
+more than one round of the CUs. A split streams its rows through LDS in chunks of
+64 with the softmax carried online from chunk to chunk, the fewest rows per split
+(64 .. 512) that keep one round of workgroups. Against the oracle's attention over
+the same rows and index sets, at the spec bar; the test asserts the kernel
+that ran."""
 import dataclasses
 
 import numpy as np
@@ -54,6 +57,29 @@ def test_paired_decode_matches_the_oracle(name):
     sinks = (rng.standard_normal(cfg.H) * 3).astype(np.float32)
     ref_o, ref_l = G.oracle_attention(case, 0, idx, sinks=sinks)
     got_o, got_l = _decode(case, idx, sinks=sinks)
+    G.check_attention(got_o, got_l, ref_o, ref_l)
+
+
+def _ragged_idx(rng, N, k, B):
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(B)]).astype(np.int32)
+    idx[1, rng.random(k) < 0.4] = -1                     # scattered gaps
+    idx[2, -300:] = -1                                   # the last splits without a row
+    idx[3, :k // 2] = -1                                 # the first half without a row
+    idx[4, :] = -1                                       # nothing selected: out = 0, lse = -inf
+    return idx
+
+
+@pytest.mark.parametrize("B,k", [(6, 1000), (16, 2048)])
+def test_paired_decode_chunking(B, k):
+    """Splits of 128 rows ending in a 40-row chunk (k = 1000: 7 x 128 + 104), and
+    splits of 512 rows streamed as 8 chunks (B = 16); sequences whose splits hold
+    no row, or only some rows, and one with none selected."""
+    cfg = C["c2"].with_(name=f"c2c{B}", cid=160 + B, B=B, N=2300, k=k)
+    case = G.build_case(cfg, seed=5)
+    rng = np.random.default_rng(B)
+    idx = _ragged_idx(rng, cfg.N, k, B)
+    ref_o, ref_l = G.oracle_attention(case, 0, idx)
+    got_o, got_l = _decode(case, idx)
     G.check_attention(got_o, got_l, ref_o, ref_l)
 
 

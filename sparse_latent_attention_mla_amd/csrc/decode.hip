@@ -545,8 +545,8 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
 // when it grows), so one workgroup per CU covers as many rows as one round of the CUs
 // needs and the split's partial is written once. The queries go from memory straight
 // into each wave's operand registers. Per chunk: QK on the wave's row tile, the chunk's
-// maximum per head tile, P for the chunk, PV with the wave owning 128 value channels of
-// its head tile. The pairs of a split (one XCD) take its chunks in rotated order, so
+// maximum per head tile, P for the chunk, PV with the wave owning 64 value channels of
+// both head tiles (each V^T operand read from LDS once for the 32 heads). The pairs of a split (one XCD) take its chunks in rotated order, so
 // that a chunk's rows come from HBM for one pair and from the L2 for the others.
 namespace gd2 {
 constexpr int kC = 64;                                     // rows per chunk
@@ -659,10 +659,13 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
 #pragma unroll
         for (int st = 0; st < NQ; ++st) qv[st] = *reinterpret_cast<const u32x4*>(qh + 64 * st);
     }
-    f32x4 o[8];
+    f32x4 o[2][4];                                         // head tile t, value channels 64 w + 16 mt ..
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float M = kNegInf, sloc = 0.0f;                        // running maximum (head j, base 2), the lane's sum
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) o[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float M[2] = {kNegInf, kNegInf};                       // running maxima of head j of each tile (base 2)
+    float sloc = 0.0f;                                     // the lane's sum over its QK rows (head tile hs)
     float* Ph = P + (16 * hs + j) * gd2::kPStride;
     for (int c = 0; c < nch; ++c) {
         zm_c = zm_n;
@@ -707,65 +710,83 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
         if (g == 0) red[16 * w + j] = mloc;
         lds_barrier();
-        float Mn = M;
+        // both head tiles' new maxima (every wave accumulates both in PV); what has been
+        // accumulated is rescaled to them (nothing yet while a maximum is -inf)
+        float alpha[2];
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) Mn = fmaxf(Mn, red[16 * (4 * hs + ww) + j]);
-        // what has been accumulated, rescaled to the new maximum (nothing yet while it is -inf)
-        const float alpha = (Mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
-        M = Mn;
+        for (int t = 0; t < 2; ++t) {
+            float Mn = M[t];
+#pragma unroll
+            for (int ww = 0; ww < 4; ++ww) Mn = fmaxf(Mn, red[16 * (4 * t + ww) + j]);
+            alpha[t] = (Mn == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(M[t] - Mn);
+            M[t] = Mn;
+        }
+        const float Mh = hs ? M[1] : M[0];
         f32x4 pv4;
         float s4 = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pv4[r] = (z[r] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(z[r] - M);
+            pv4[r] = (z[r] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(z[r] - Mh);
             s4 += pv4[r];
         }
         *reinterpret_cast<f32x4*>(Ph + 16 * wq + 4 * g) = pv4;
-        sloc = sloc * alpha + s4;
+        sloc = sloc * (hs ? alpha[1] : alpha[0]) + s4;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[mt][r] *= alpha;
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[t][mt][r] *= alpha[t];
         lds_barrier();                                     // the chunk's P
 
-        // ---- PV over the chunk's rows for value channels 128 wq .. 128 wq + 127 of the head tile
+        // ---- PV over the chunk's rows for value channels 64 w .. 64 w + 63 of both head tiles
+        // (each V^T operand read once for the pair's 32 heads)
 #pragma unroll
         for (int st = 0; st < C / 32; ++st) {
             if (32 * st >= nc) break;
-            const float* pr = Ph + 32 * st + 8 * g;
-            const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
-            const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-            u32x4 pa, pb;
-            split_bf16x8(p, pa, pb);
+            u32x4 pa[2], pb[2];
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const int c0 = 128 * wq + 16 * mt;
+            for (int t = 0; t < 2; ++t) {
+                const float* pr = P + (16 * t + j) * gd2::kPStride + 32 * st + 8 * g;
+                const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr), p1 = *reinterpret_cast<const f32x4*>(pr + 4);
+                const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                split_bf16x8(p, pa[t], pb[t]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int c0 = 64 * w + 16 * mt;
                 const uint8_t* vp = Vb + (32 * st + 8 * g + (j >> 2)) * VS + 2 * (c0 + 4 * (j & 3));
                 const u32x2 r0 = ds_tr16(vp), r1 = ds_tr16(vp + 4 * VS);
                 const u32x4 av = u32x4{r0.x, r0.y, r1.x, r1.y};
-                o[mt] = mfma_bf16(av, pa, o[mt]);
-                o[mt] = mfma_bf16(av, pb, o[mt]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    o[t][mt] = mfma_bf16(av, pa[t], o[t][mt]);
+                    o[t][mt] = mfma_bf16(av, pb[t], o[t][mt]);
+                }
             }
         }
     }
 
-    // ---- the split's partial for the wave's head tile
+    // ---- the split's partials: the wave's value channels of both head tiles
     sloc += __shfl_xor(sloc, 16, 64);
     sloc += __shfl_xor(sloc, 32, 64);
     if (g == 0) red[128 + 16 * w + j] = sloc;
     lds_barrier();
-    float l = red[128 + 16 * (4 * hs) + j];
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) l += red[128 + 16 * (4 * hs + ww) + j];
-    const int head = 32 * hp + 16 * hs + j;
-    const int64_t prow = ((int64_t)b * S + split) * a.H + head;
-    const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
+    for (int t = 0; t < 2; ++t) {
+        float l = red[128 + 16 * (4 * t) + j];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<float4*>(o_part + prow * kDv + 128 * wq + 16 * mt + 4 * g) =
-            make_float4(o[mt][0] * f, o[mt][1] * f, o[mt][2] * f, o[mt][3] * f);
-    if (wq == 0 && g == 0)
-        lse_part[prow] = (l > 0.0f) ? (M + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
+        for (int ww = 1; ww < 4; ++ww) l += red[128 + 16 * (4 * t + ww) + j];
+        const int head = 32 * hp + 16 * t + j;
+        const int64_t prow = ((int64_t)b * S + split) * a.H + head;
+        const float f = (l > 0.0f) ? __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            *reinterpret_cast<float4*>(o_part + prow * kDv + 64 * w + 16 * mt + 4 * g) =
+                make_float4(o[t][mt][0] * f, o[t][mt][1] * f, o[t][mt][2] * f, o[t][mt][3] * f);
+        if (w == 0 && g == 0)
+            lse_part[prow] = (l > 0.0f) ? (M[t] + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -__builtin_inff();
+    }
 }
 
 template <int DQK>

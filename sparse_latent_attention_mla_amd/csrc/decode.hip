@@ -850,8 +850,9 @@ __global__ __launch_bounds__(512) void k_decode_g(DecodeArgs a, int S_main, int 
 }
 
 // Combine the splits of one (b, h) by their logsumexp; thread t owns channels 4t .. 4t+3.
-// Up to kMergeFast splits, every load (logsumexps and partials) is issued at
-// once, from clamped in-bounds addresses, so the block pays one memory round trip.
+// Up to NF splits (4, 8, 12 or kMergeFast: the launcher's fewest that cover S), every
+// load (logsumexps and partials) is issued at once, from clamped in-bounds
+// addresses, so the block pays one memory round trip.
 // With attention sinks the head's sink logit joins the normaliser (no value
 // vector): out scales by exp(lse_U - lse) and lse = logaddexp(lse_U, sink).
 // The output's RoPE inverse on thread t's four channels 4t .. 4t + 3 (the
@@ -903,30 +904,32 @@ __device__ __forceinline__ void merge_finish(float m, float tot, float4 acc, con
     if (t == 0) *lse_out = m + __logf(tot);
 }
 
+template <int NF>
 __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const float* __restrict__ o_part,
                                                          const float* __restrict__ lse_part, float* __restrict__ out,
                                                          float* __restrict__ lse, const float* __restrict__ sinks,
                                                          int rope_dim, const float* __restrict__ rope_cs) {
+    static_assert(NF >= 1 && NF <= kMergeFast, "splits loaded in one round");
     const int h = blockIdx.x, b = blockIdx.y;
     const int t = threadIdx.x;
     const float* lp = lse_part + (int64_t)b * S * H + h;
     // an empty set: all mass on the sink (lse = the sink's logit, -inf without one)
     const float empty_lse = sinks ? sinks[h] : -__builtin_inff();
     const float* cs = rope_dim > 0 ? rope_cs + (int64_t)b * rope_dim : nullptr;   // [r / 2][2] of sequence b
-    if (S <= kMergeFast) {
+    if (S <= NF) {
         const float4* op = reinterpret_cast<const float4*>(o_part + ((int64_t)b * S * H + h) * kDv) + t;
         const int64_t step = (int64_t)H * (kDv / 4);
-        float lv[kMergeFast];
-        float4 pv[kMergeFast];
+        float lv[NF];
+        float4 pv[NF];
 #pragma unroll
-        for (int s = 0; s < kMergeFast; ++s) {
+        for (int s = 0; s < NF; ++s) {
             const int sc = (s < S) ? s : 0;
             lv[s] = lp[(int64_t)sc * H];
             pv[s] = op[sc * step];
         }
         float m = -__builtin_inff();
 #pragma unroll
-        for (int s = 0; s < kMergeFast; ++s)
+        for (int s = 0; s < NF; ++s)
             if (s < S) m = fmaxf(m, lv[s]);
         float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * H + h) * kDv) + t;
         if (m == -__builtin_inff()) {
@@ -937,7 +940,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge(int S, int H, const flo
         float tot = 0.0f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int s = 0; s < kMergeFast; ++s) {
+        for (int s = 0; s < NF; ++s) {
             const float wv = (s < S) ? __expf(lv[s] - m) : 0.0f;
             tot += wv;
             acc.x += wv * pv[s].x;
@@ -1287,8 +1290,10 @@ hipError_t launch_decode(const DecodeArgs& a_in, hipStream_t stream) {
         else e = launch_gather<SRC_BF16, 512>(a, g, o_part, lse_part, stream);
         if (e != hipSuccess) return e;
     }
+    // the merge's one-round path loads the fewest splits (4, 8, 12 or 16) that cover S
     const ProfSlot p = prof_slot(PROF_MERGE);
-    return launch_kernel(k_merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, p.start, p.stop, S, a.H, o_part,
+    auto merge = S <= 4 ? k_merge<4> : S <= 8 ? k_merge<8> : S <= 12 ? k_merge<12> : k_merge<kMergeFast>;
+    return launch_kernel(merge, dim3(a.H, a.B), dim3(kMergeThreads), 0, stream, p.start, p.stop, S, a.H, o_part,
                          lse_part, a.out, a.lse, a.sinks, a.rope_dim, a.rope_cs);
 }
 

@@ -506,8 +506,8 @@ mla_status_t mla_append_sparse_decode(mla_row_t main_row, int32_t d_v, const voi
  * mla_csa2_group_step -- one decode step of a layer group over one shared cache, in one call.
  *
  * The layers of a CSA2 group ([P1] "DeepSeek-V4.1", "Three modes"; [P4] "CSA2: four layers
- * keep their own copy") enqueued in order on `stream`, each exactly as the calls it is
- * made of (same kernels, same results):
+ * keep their own copy") enqueued in order on `stream`, each as the calls it is made of
+ * (the same selections and outputs; see below for the one fused step):
  *   MLA_LAYER_FULL, MLA_LAYER_REINDEX  the layer selects with its own indexer query over the
  *        shared indexer keys: for layer 0, mla_append_indexer_topk (the step's entry: main
  *        row, indexer key and layer 0's window entry, carried in the scan's launch where it
@@ -521,6 +521,14 @@ mla_status_t mla_append_sparse_decode(mla_row_t main_row, int32_t d_v, const voi
  * indices to idx_a and idx_b in turn (the first to idx_a): with more than two selecting
  * layers, a buffer is overwritten by the selection two layers later. The bf16-score top-k
  * (mla_indexer_topk_bf16) when score_bf16 != 0.
+ * One difference in how, not in what: without a pool, when a selection takes the
+ * many-workgroup path (capacity above the one-workgroup selection's 16,384 rows) and the
+ * decode is the gather decode of 16 heads per workgroup, the selection's final step runs
+ * inside that layer's decode instead of as its own kernel: the decode takes its rows from
+ * the per-workgroup lists of the selection's first kernel and writes the index set to
+ * idx_a or idx_b itself. The set is the one the separate calls select (an unordered set,
+ * -1 in the same trailing slots); the order of its entries, and with it the decode's
+ * summation order, may differ.
  *
  * One call instead of one per layer and kernel, for callers whose host loop would
  * otherwise set the pace: the launches are enqueued back to back from C.

@@ -221,11 +221,33 @@ mla_status_t topk_args(mla_row_t idx_row, const void* q_idx, const float* w, flo
     return ok();
 }
 
-// The scan (carrying `append` when given) and the selection.
-mla_status_t topk_launch(const TopkCall& c, const mla::AppendArgs* append, hipStream_t st) {
+// A selection whose final is left to the decode that follows (groups > 0: k_select ran
+// alone, its lists and counts in ws).
+struct Deferred {
+    int groups = 0;
+    mla::TopkWorkspace ws{};
+    const int32_t* n_visible = nullptr;
+    int64_t capacity = 0;
+};
+
+// The scan (carrying `append` when given) and the selection; with `defer`, only
+// k_select when the selection takes its many-workgroup path over every entry.
+mla_status_t topk_launch(const TopkCall& c, const mla::AppendArgs* append, hipStream_t st,
+                         Deferred* defer = nullptr) {
     hipError_t e = mla::launch_scan(c.scan, st, append);
     if (e != hipSuccess) return hip_status(e, "indexer scan");
     const mla::ScanArgs& a = c.scan;
+    if (defer && !a.cand) {
+        defer->groups = 0;
+        e = mla::launch_select_lists(a.scores, a.capacity, a.n_visible, a.B, a.k, c.ws, st, &defer->groups);
+        if (e != hipSuccess) return hip_status(e, "top-k select");
+        if (defer->groups > 0) {
+            defer->ws = c.ws;
+            defer->n_visible = a.n_visible;
+            defer->capacity = a.capacity;
+            return ok();
+        }
+    }
     if (a.cand) {       // the pool's n_cand entries, reported as their positions
         mla::SelectMap map;
         map.cand = a.cand;
@@ -409,14 +431,14 @@ static mla_status_t indexer_topk(mla_row_t idx_row, const void* q_idx, const flo
                                  const void* idx_cache, int64_t idx_seq_stride, int64_t capacity,
                                  const int32_t* n_visible, const int32_t* cand, int32_t n_cand, int32_t B,
                                  int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores, void* workspace,
-                                 size_t workspace_bytes, void* stream, bool score_bf16) {
+                                 size_t workspace_bytes, void* stream, bool score_bf16, Deferred* defer = nullptr) {
     mla::begin_call();
     TopkCall c;
     const mla_status_t s = topk_args(idx_row, q_idx, w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
                                      cand, n_cand, B, H_I, k, out_idx, out_scores, workspace, workspace_bytes, &c,
                                      score_bf16);
     if (s != MLA_OK || c.empty) return s;
-    return topk_launch(c, nullptr, static_cast<hipStream_t>(stream));
+    return topk_launch(c, nullptr, static_cast<hipStream_t>(stream), defer);
 }
 
 mla_status_t mla_indexer_topk(mla_row_t idx_row, const void* q_idx, const float* w, float score_scale,
@@ -444,7 +466,8 @@ static mla_status_t append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, c
                                         void* win_ring, int32_t W, int32_t Dw, int32_t win_fmt, const void* q_idx,
                                         const float* w, float score_scale, const int32_t* n_visible, int32_t B,
                                         int32_t H_I, int32_t k, int32_t* out_idx, float* out_scores,
-                                        void* workspace, size_t workspace_bytes, void* stream, bool score_bf16) {
+                                        void* workspace, size_t workspace_bytes, void* stream, bool score_bf16,
+                                        Deferred* defer = nullptr) {
     mla::begin_call();
     if (!idx_cache) return fail(MLA_ERR_INVALID_ARG, "append_indexer_topk: idx_cache is NULL");
     mla::AppendArgs ap{};
@@ -461,9 +484,9 @@ static mla_status_t append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, c
     if (n_new == 0) {                                      // at most a window entry: nothing to carry
         const mla_status_t sa = hip_status(mla::launch_append(ap, st), "append launch");
         if (sa != MLA_OK) return sa;
-        return topk_launch(c, nullptr, st);
+        return topk_launch(c, nullptr, st, defer);
     }
-    return topk_launch(c, &ap, st);
+    return topk_launch(c, &ap, st, defer);
 }
 
 mla_status_t mla_append_indexer_topk(mla_row_t main_row, mla_row_t idx_row, const float* new_main,
@@ -557,7 +580,8 @@ static mla_status_t decode_impl(mla_row_t main_row, int32_t d_v, const void* q, 
                                 const float* new_win, const int32_t* win_pos, const void* win_ring,
                                 const int32_t* win_len, int32_t W, int32_t win_fmt, float softmax_scale,
                                 const mla_decode_epilogue_t* epilogue, int32_t B, int32_t H, float* out, float* lse,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                const Deferred* sel = nullptr, int32_t* idx_out = nullptr) {
     if (B < 0 || H < 1 || k < 0 || capacity < 0)
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: need B >= 0, H >= 1, k >= 0, capacity >= 0");
     const int D = main_row.dim + main_row.rope_dim;
@@ -566,7 +590,8 @@ static mla_status_t decode_impl(mla_row_t main_row, int32_t d_v, const void* q, 
     mla_status_t s = check_rows("sparse_decode", main_row, main_cache, main_seq_stride, capacity, B, &rb, true);
     if (s != MLA_OK) return s;
     if (B == 0) return ok();
-    if (!q || !out || !lse || (k > 0 && (!idx || !main_cache)))
+    const bool finish = sel && sel->groups > 0;            // the rows come from the selection's lists
+    if (!q || !out || !lse || (k > 0 && ((!idx && !finish) || !main_cache)) || (finish && !idx_out))
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: a required pointer is NULL");
     if (win_ring && (!win_len || W <= 0))
         return fail(MLA_ERR_INVALID_ARG, "sparse_decode: window needs win_len and W > 0");
@@ -620,6 +645,19 @@ static mla_status_t decode_impl(mla_row_t main_row, int32_t d_v, const void* q, 
     a.lse = lse;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
+    if (finish) {
+        if (!mla::decode_takes_select_lists(a.fmt, a.dim, a.rope, a.d_v, B, H, k, a.W))
+            return fail(MLA_ERR_UNSUPPORTED, "sparse_decode: this shape cannot finish a selection");
+        a.idx = nullptr;
+        a.sel_counts = sel->ws.counts;
+        a.sel_lists = sel->ws.sel;
+        a.cand_lists = sel->ws.cand;
+        a.sel_hist = sel->ws.hist;
+        a.sel_visible = sel->n_visible;
+        a.sel_capacity = sel->capacity;
+        a.sel_groups = sel->groups;
+        a.idx_out = idx_out;
+    }
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (new_win) {                                         // the step's window entry first
         a.new_win = new_win;
@@ -739,28 +777,35 @@ mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t 
         ~Scope() { mla::group_end(); }
     } scope;
     const int32_t Dw = main_row.dim + main_row.rope_dim;
+    // a selecting layer's final folded into its decode: the many-workgroup selection over
+    // every row (none with a pool, whose kernels reuse the top-k workspace), on the gather decode
+    const bool fold = pool_blocks == 0 &&
+                      mla::decode_takes_select_lists(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W);
+    if (W > 0 && n_layers > 1 && (!win_pos || !aligned(win_pos, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: the window entries need win_pos (4-byte aligned)");
     int32_t* bufs[2] = {idx_a, idx_b};
     int32_t* latest = nullptr;
     int j = 0;
     for (int32_t l = 0; l < n_layers; ++l) {
         const mla_group_layer_t& y = layers[l];
         mla_status_t st = MLA_OK;
+        Deferred dfr;
         if (y.mode != MLA_LAYER_REUSE) {                   // full / reindex: select with the layer's own query
             latest = bufs[j % 2];
             float* scores = (pool_blocks > 0 && y.mode == MLA_LAYER_FULL) ? pool_scores : nullptr;
             if (l == 0) {                                  // carrying the step's append (and window entry)
-                st = (score_bf16 ? mla_append_indexer_topk_bf16 : mla_append_indexer_topk)(
+                st = append_indexer_topk(
                     main_row, idx_row, new_main, new_idx, slots, n_new, new_main ? main_cache : nullptr,
                     main_seq_stride, idx_cache, idx_seq_stride, capacity, W > 0 ? y.new_win : nullptr,
                     W > 0 ? win_pos : nullptr, W > 0 ? y.win_ring : nullptr, W > 0 ? W : 0, W > 0 ? Dw : 0, win_fmt,
                     y.q_idx, y.w, score_scale, n_visible, B, H_I, k, latest, scores, topk_workspace,
-                    topk_workspace_bytes, stream);
+                    topk_workspace_bytes, stream, score_bf16 != 0, fold ? &dfr : nullptr);
             } else {                                       // a Reindex layer with a pool scores the pool only
                 const bool use_pool = pool_blocks > 0 && y.mode == MLA_LAYER_REINDEX;
-                st = (score_bf16 ? mla_indexer_topk_bf16 : mla_indexer_topk)(
-                    idx_row, y.q_idx, y.w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
-                    use_pool ? pool_pos : nullptr, use_pool ? pool_blocks * pool_block : 0, B, H_I, k, latest, scores,
-                    topk_workspace, topk_workspace_bytes, stream);
+                st = indexer_topk(idx_row, y.q_idx, y.w, score_scale, idx_cache, idx_seq_stride, capacity, n_visible,
+                                  use_pool ? pool_pos : nullptr, use_pool ? pool_blocks * pool_block : 0, B, H_I, k,
+                                  latest, scores, topk_workspace, topk_workspace_bytes, stream, score_bf16 != 0,
+                                  fold ? &dfr : nullptr);
             }
             if (st == MLA_OK && scores)                    // the Full layer publishes the candidate pool
                 st = mla_indexer_pool(scores, capacity, n_visible, B, pool_block, pool_blocks, pool_pos,
@@ -768,16 +813,17 @@ mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t 
             if (st != MLA_OK) return st;
             ++j;
         }
+        // (a deferred selection: the decode finishes it and writes the index set to `latest`)
+        const Deferred* sel = dfr.groups > 0 ? &dfr : nullptr;
         if (l > 0 && W > 0)                                // the layer's window entry in its decode's call
-            st = mla_append_sparse_decode(main_row, d_v, y.q, main_cache, main_seq_stride, capacity, latest, k,
-                                          y.new_win, win_pos, y.win_ring, win_len, W, win_fmt, softmax_scale,
-                                          nullptr, B, H, y.out, y.lse, decode_workspace, decode_workspace_bytes,
-                                          stream);
+            st = decode_impl(main_row, d_v, y.q, main_cache, main_seq_stride, capacity, latest, k, y.new_win, win_pos,
+                             y.win_ring, win_len, W, win_fmt, softmax_scale, nullptr, B, H, y.out, y.lse,
+                             decode_workspace, decode_workspace_bytes, stream, sel, latest);
         else
-            st = mla_sparse_decode(main_row, d_v, y.q, main_cache, main_seq_stride, capacity, latest, k,
-                                   W > 0 ? y.win_ring : nullptr, W > 0 ? win_len : nullptr, W > 0 ? W : 0, win_fmt,
-                                   softmax_scale, nullptr, B, H, y.out, y.lse, decode_workspace,
-                                   decode_workspace_bytes, stream);
+            st = decode_impl(main_row, d_v, y.q, main_cache, main_seq_stride, capacity, latest, k, nullptr, nullptr,
+                             W > 0 ? y.win_ring : nullptr, W > 0 ? win_len : nullptr, W > 0 ? W : 0, win_fmt,
+                             softmax_scale, nullptr, B, H, y.out, y.lse, decode_workspace, decode_workspace_bytes,
+                             stream, sel, latest);
         if (st != MLA_OK) return st;
     }
     return ok();

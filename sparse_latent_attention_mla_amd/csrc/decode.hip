@@ -25,6 +25,7 @@
 // ALUs, writes the final output directly.
 #include "common.hpp"
 #include "launch.hpp"
+#include "select.hpp"
 
 namespace mla {
 
@@ -125,6 +126,225 @@ constexpr int lds_bytes() {
 }
 }  // namespace gd
 
+// ---- finishing a many-workgroup selection inside the decode
+// Slot o of sequence b's index set, placed as the selection's final places it: the rows
+// above the threshold bin first, in the order of k_select's workgroups and of their lists;
+// then the candidates of the threshold bin that the exact threshold takes (the composite
+// key << 32 | ~position, so that equal scores go to the smaller position), in the same
+// list order; -1 from min(n_visible, k) on ([P2] "CSA: two changes to HCA" for the -1
+// slots). The workgroup of (b, split, head group) fills its split's slots first ..
+// first + n - 1 into ridx (-1 for a position outside the cache); the splits that reach
+// into the threshold bin run the radix over its candidates themselves (each head group
+// of such a split, redundantly: the result is one function of the lists). scratch is
+// the row buffers, free until the gather (candidates past its room are read from the
+// lists in global memory). Called by every thread of the workgroup.
+namespace fs {
+constexpr uint32_t kOffS = 0;                              // [kFusedSelectGroups + 1] selected offsets
+constexpr uint32_t kOffC = 4160;                           // candidate offsets
+constexpr uint32_t kHist = 8320;                           // [2][kMaxDigitBins] digit histograms
+constexpr uint32_t kRes = 16512;                           // digit result
+constexpr uint32_t kWsum = 16576;                          // [8 waves][2] scan totals
+constexpr uint32_t kCand = 16640;                          // candidates
+}  // namespace fs
+
+__device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t scratch_bytes, int32_t* ridx,
+                                 int R, int b, bool zero_rest, int64_t first, int n) {
+    static_assert(kFusedSelectGroups <= 2 * 512, "two workgroups' counts per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    uint32_t* offs_s = reinterpret_cast<uint32_t*>(scratch + fs::kOffS);
+    uint32_t* offs_c = reinterpret_cast<uint32_t*>(scratch + fs::kOffC);
+    uint32_t(*h)[kMaxDigitBins] = reinterpret_cast<uint32_t(*)[kMaxDigitBins]>(scratch + fs::kHist);
+    uint32_t* res = reinterpret_cast<uint32_t*>(scratch + fs::kRes);
+    uint32_t* wsum = reinterpret_cast<uint32_t*>(scratch + fs::kWsum);
+    uint64_t* lc = reinterpret_cast<uint64_t*>(scratch + fs::kCand);
+    const uint32_t cand_room = (scratch_bytes - fs::kCand) / 8;
+    const int G = a.sel_groups;
+    const int64_t cap = a.sel_capacity;
+    const int64_t nvis = clamp_visible(a.sel_visible[b], cap);
+    const uint32_t want = (uint32_t)(nvis < a.k ? nvis : a.k);
+    uint32_t* hb = a.sel_hist + (int64_t)b * kHistWordsHost;
+    const int32_t* sl = a.sel_lists + b * cap;
+    const uint64_t* cl = a.cand_lists + b * cap;
+
+    // the workgroups' counts (thread t: workgroups 2t, 2t + 1), exclusive prefix sums
+    const uint32_t csum = (zero_rest && tid < 64) ? coarse_sum_of_lane(hb) : 0u;
+    uint32_t cs[2], cc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = 2 * tid + i;
+        const bool ok = j < G;
+        const u32x2 c2 = *reinterpret_cast<const u32x2*>(a.sel_counts + ((int64_t)b * G + (ok ? j : 0)) * 2);
+        cs[i] = ok ? c2.x : 0u;
+        cc[i] = ok ? c2.y : 0u;
+    }
+    const uint32_t ts = cs[0] + cs[1], tc = cc[0] + cc[1];
+    const uint32_t is = wave_incl_scan(ts), ic = wave_incl_scan(tc);
+    if (lane == 63) {
+        wsum[2 * wv] = is;
+        wsum[2 * wv + 1] = ic;
+    }
+    lds_barrier();
+    uint32_t bs = 0, bc = 0, nsel = 0, ncand = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t s_ = wsum[2 * i], c_ = wsum[2 * i + 1];
+        if (i < wv) {
+            bs += s_;
+            bc += c_;
+        }
+        nsel += s_;
+        ncand += c_;
+    }
+    const uint32_t es = bs + is - ts, ec = bc + ic - tc;
+    if (2 * tid < G) {
+        offs_s[2 * tid] = es;
+        offs_c[2 * tid] = ec;
+    }
+    if (2 * tid + 1 < G) {
+        offs_s[2 * tid + 1] = es + cs[0];
+        offs_c[2 * tid + 1] = ec + cc[0];
+    }
+    lds_barrier();
+    // the workgroup holding entry i of the concatenated lists: the last whose offset is <= i
+    auto owner = [&](const uint32_t* offs, uint32_t i) {
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (offs[mid] <= i) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    };
+    const int64_t o = first + tid;
+    const uint32_t need = want > nsel ? want - nsel : 0u;
+    const bool tail = need > 0 && first < (int64_t)want && first + n > (int64_t)nsel;
+    auto cand_at = [&](uint32_t i) {
+        const int j = owner(offs_c, i);
+        return cl[(int64_t)j * kSelRowsHost + (i - offs_c[j])];
+    };
+    const bool in_lds = ncand <= cand_room;
+    // the split's selected slots and (in a split that reaches the threshold bin) the first
+    // 2048 candidates: every load issued before the first store
+    constexpr int kCB = 4;                                 // candidates per thread per batch
+    int32_t r = -1;
+    if (tid < n && o < (int64_t)nsel) {
+        const int j = owner(offs_s, (uint32_t)o);
+        r = sl[(int64_t)j * kSelRowsHost + ((uint32_t)o - offs_s[j])];
+    }
+    uint64_t cv0[kCB];
+    if (tail && in_lds) {
+#pragma unroll
+        for (int u = 0; u < kCB; ++u) {
+            const uint32_t i = u * 512 + tid;
+            cv0[u] = i < ncand ? cand_at(i) : 0ull;
+        }
+    }
+    if (tid < R) ridx[tid] = (r >= 0 && r < a.capacity) ? r : -1;
+    if (tail) {
+        if (in_lds) {
+#pragma unroll
+            for (int u = 0; u < kCB; ++u) {
+                const uint32_t i = u * 512 + tid;
+                if (i < ncand) lc[i] = cv0[u];
+            }
+            for (uint32_t i0 = kCB * 512; i0 < ncand; i0 += kCB * 512) {
+                uint64_t v[kCB];
+#pragma unroll
+                for (int u = 0; u < kCB; ++u) {
+                    const uint32_t i = i0 + u * 512 + tid;
+                    v[u] = i < ncand ? cand_at(i) : 0ull;
+                }
+#pragma unroll
+                for (int u = 0; u < kCB; ++u) {
+                    const uint32_t i = i0 + u * 512 + tid;
+                    if (i < ncand) lc[i] = v[u];
+                }
+            }
+        }
+        for (int i = tid; i < 2 * kMaxDigitBins; i += 512) h[0][i] = 0u;
+        lds_barrier();
+        // the radix and the ranking, over the candidates in LDS or (past its room) in the lists
+        auto finish = [&](auto cv) {
+            // the radix over the candidates' composites, most significant digit first: two
+            // 10-bit digits fix the threshold score (the bin fixed its top 12 bits), and four
+            // 8-bit digits of the inverted position follow when more candidates share that
+            // score than are still needed; `prefix` ends as the need-th largest composite
+            const bool radix = need < ncand;
+            uint64_t mask = 0xFFFull << 52, prefix = radix ? (cv(0) & mask) : 0ull;
+            uint32_t rem = need;
+            int par = 0;
+            auto pass = [&](int shift, int bits) {
+                const int nb = 1 << bits;
+                uint32_t* hc = h[par];
+                for (uint32_t i = tid; i < ncand; i += 512) {
+                    const uint64_t v = cv(i);
+                    if ((v & mask) == prefix) atomicAdd(&hc[(v >> shift) & (uint64_t)(nb - 1)], 1u);
+                }
+                lds_barrier();
+                if (tid < 64) {
+                    const DigitResult d = wave_find_digit(hc, nb, rem);
+                    if (lane == 0) {
+                        res[0] = (uint32_t)d.digit;
+                        res[1] = d.above;
+                        res[2] = d.count;
+                    }
+                } else {
+                    for (int i = tid - 64; i < kMaxDigitBins; i += 512 - 64) h[par ^ 1][i] = 0u;
+                }
+                lds_barrier();
+                prefix |= (uint64_t)res[0] << shift;
+                mask |= (uint64_t)(nb - 1) << shift;
+                rem -= res[1];
+                par ^= 1;
+                return res[2];
+            };
+            if (radix) {
+                pass(42, 10);
+                const uint32_t eq = pass(32, 10);
+                if (rem < eq) {
+                    pass(24, 8);
+                    pass(16, 8);
+                    pass(8, 8);
+                    pass(0, 8);
+                }
+            }
+            // the taken candidates (every one at or above `prefix`: exactly `need`), ranked in list
+            // order; rank q fills slot nsel + q, and this split keeps the ranks of its own slots
+            const uint32_t q_lo = (uint32_t)((first > (int64_t)nsel ? first : (int64_t)nsel) - nsel);
+            const uint32_t q_hi = (uint32_t)((first + n < (int64_t)want ? first + n : (int64_t)want) - nsel);
+            uint32_t base = 0;
+            int it = 0;
+            for (uint32_t i0 = 0; i0 < ncand && base < q_hi; i0 += 512, ++it) {
+                const uint32_t i = i0 + tid;
+                const uint64_t v = i < ncand ? cv(i) : 0ull;
+                const bool take = i < ncand && (!radix || v >= prefix);
+                const uint64_t m = __ballot(take);
+                uint32_t* ws2 = wsum + 8 * (it & 1);           // two sets: one barrier per round
+                if (lane == 0) ws2[wv] = (uint32_t)__popcll(m);
+                lds_barrier();
+                uint32_t before = 0, tot = 0;
+    #pragma unroll
+                for (int w2 = 0; w2 < 8; ++w2) {
+                    const uint32_t c_ = ws2[w2];
+                    if (w2 < wv) before += c_;
+                    tot += c_;
+                }
+                if (take) {
+                    const uint32_t q = base + before + lanes_below(m);
+                    if (q >= q_lo && q < q_hi) {
+                        const int32_t pos = (int32_t)~(uint32_t)(v & 0xFFFFFFFFull);
+                        ridx[(int64_t)nsel + q - first] = (pos >= 0 && pos < a.capacity) ? pos : -1;
+                    }
+                }
+                base += tot;
+            }
+        };
+        if (in_lds) finish([&](uint32_t i) { return lc[i]; });
+        else finish(cand_at);
+    }
+    if (zero_rest) zero_hist_rest(hb, (uint32_t)a.k, csum);
+}
+
 template <int SRC, int DQK, int R>
 __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* smem, int b, int split, int S, int hg,
                                                bool is_win, int64_t first, int n, int span, float* o_part,
@@ -168,18 +388,7 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         }
     }
 
-    // ---- row indices (-1: no row) and the 16 heads' queries
-    if (tid < R) {
-        int32_t r = -1;
-        if (tid < n) {
-            if (is_win) r = (int32_t)(first + tid);
-            else {
-                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
-                if (s >= 0 && s < a.capacity) r = s;
-            }
-        }
-        ridx[tid] = r;
-    }
+    // ---- row indices (-1: no row) and the 16 heads' queries (their loads issued first)
     {
         constexpr int kPer = DQK / 8;                      // 16-byte pieces per head
         constexpr int kIt = (16 * kPer + 511) / 512;
@@ -190,6 +399,19 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
             const int it = tid + 512 * i, h = it / kPer, pc = it - h * kPer;
             if (it < 16 * kPer) qv[i] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)h * DQK + 8 * pc);
         }
+        if (!is_win && a.sel_counts) {                     // the rows of a selection this decode finishes
+            finish_selection(a, V, (uint32_t)L::kVBytes, ridx, R, b, split == 0 && hg == 0, first, n);
+        } else if (tid < R) {
+            int32_t r = -1;
+            if (tid < n) {
+                if (is_win) r = (int32_t)(first + tid);
+                else {
+                    const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
+                    if (s >= 0 && s < a.capacity) r = s;
+                }
+            }
+            ridx[tid] = r;
+        }
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
             const int it = tid + 512 * i, h = it / kPer, pc = it - h * kPer;
@@ -197,6 +419,8 @@ __device__ __forceinline__ void decode_split_g(const DecodeArgs& a, uint8_t* sme
         }
     }
     __syncthreads();
+    if (!is_win && a.sel_counts && hg == 0 && tid < n)    // the finished index set, once per split
+        a.idx_out[(int64_t)b * a.k + first + tid] = ridx[tid];
     // B operands of the contraction (lane (head j, g): channels 32 s + 8 g .. of head j), read
     // from LDS now so that the reads overlap the gather
     constexpr int NQ = DQK / 32;                           // k-steps over the K width
@@ -1242,6 +1466,13 @@ __global__ __launch_bounds__(256) void k_widen_window(const uint8_t* __restrict_
     const uint8_t* src = ring + row * (D + D / 32);
     for (int c = threadIdx.x; c < D; c += 256)
         out[row * D + c] = (uint16_t)bf16_rne(e4m3_to_f32(src[c]) * e8m0_to_f32(src[D + c / 32]));
+}
+
+bool decode_takes_select_lists(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W) {
+    if (!mfma_shape(fmt, dim, rope, d_v, H) || k <= 0) return false;
+    bool pairs = false;
+    decode_geometry(fmt, B, H, k, W, &pairs);
+    return !pairs;
 }
 
 bool decode_fuses_window_append(const DecodeArgs& a) {

@@ -121,6 +121,13 @@ struct SelectMap {
 hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                          const TopkWorkspace& ws, int32_t* out_idx, hipStream_t stream,
                          const SelectMap& map = SelectMap{});
+// k_select alone, when launch_select would take its many-workgroup path over every
+// entry (no pool, no expansion) with at most kFusedSelectGroups workgroups per sequence:
+// *groups = those workgroups, and the decode that follows finishes the selection from
+// their lists (DecodeArgs.sel_*). Otherwise nothing is launched and *groups = 0.
+constexpr int kFusedSelectGroups = 1024;
+hipError_t launch_select_lists(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
+                               const TopkWorkspace& ws, hipStream_t stream, int* groups);
 // Block maxima of a layer's scores ([B, capacity]): bmax[b, i] = the largest
 // score among the visible positions block*i .. block*i + block - 1, the
 // histogram of their keys into hist (as the scan builds it), and nvb[b] = the
@@ -151,6 +158,19 @@ struct DecodeArgs {
     float* lse;             // [B, H]
     void* workspace;
     size_t workspace_bytes;
+    // A selection to finish (sel_counts null: the rows come from idx): k_select's lists of a
+    // many-workgroup selection over scores [B, sel_capacity] (sel_groups workgroups per
+    // sequence, each with its counts, selected positions and candidates), the histogram whose
+    // rest is zeroed for the next call, and idx_out [B, k], where the decode writes the index
+    // set the final would have written.
+    const uint32_t* sel_counts = nullptr;
+    const int32_t* sel_lists = nullptr;
+    const uint64_t* cand_lists = nullptr;
+    uint32_t* sel_hist = nullptr;
+    const int32_t* sel_visible = nullptr;
+    int64_t sel_capacity = 0;
+    int sel_groups = 0;
+    int32_t* idx_out = nullptr;
 };
 bool decode_supported(int fmt, int dim, int rope, int d_v, int H);
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
@@ -201,6 +221,9 @@ hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint3
 }
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Whether launch_decode can finish a selection from k_select's lists for this shape
+// (the gather decode of 16 heads per workgroup; W: window slots, 0 without a window).
+bool decode_takes_select_lists(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 // Whether launch_decode writes a.new_win into the window ring itself (512-channel bf16 or
 // MXFP8 entries on the gather decode); otherwise the caller appends it first.
 bool decode_fuses_window_append(const DecodeArgs& a);

@@ -25,6 +25,11 @@ CFGS = {
     "c4d": C["c4"].with_(name="c4d", cid=124, B=2, N=4100),
     "c5s": C["c5"].with_(name="c5s", cid=105, B=1, N=3001),
     "c5d": C["c5"].with_(name="c5d", cid=125, B=2, N=4100),
+    # more rows than the one-workgroup selection takes: the many-workgroup selection, whose
+    # final the group call folds into the decode
+    "c3f": C["c3"].with_(name="c3f", cid=173, B=3, N=40004),
+    "c4f": C["c4"].with_(name="c4f", cid=174, B=2, N=40004),
+    "c5f": C["c5"].with_(name="c5f", cid=175, B=1, N=40004),
 }
 POOL_BLOCK = 8
 
@@ -179,15 +184,22 @@ def test_group_helper_rejects_unknown_and_leading_reuse():
 
 @pytest.mark.parametrize("name,pool,score_bf16", [("c1", 0, False), ("c3d", 0, False), ("c4d", 0, False),
                                                   ("c5s", 0, False), ("c5d", 0, False), ("c5d", 96, False),
-                                                  ("c5d", 0, True), ("c3d", 0, True)])
-def test_native_group_step_equals_the_helper(name, pool, score_bf16):
+                                                  ("c5d", 0, True), ("c3d", 0, True),
+                                                  ("c3f", 0, False), ("c3f", 0, True), ("c4f", 0, False),
+                                                  ("c5f", 0, False), ("c5f", 0, True), ("c5f", 96, False)])
+def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=False):
     """mla_csa2_group_step (one C call) against csa2_group_step (the same calls from Python):
     the caches and window rings byte for byte, the selected sets, the pool's positions, and
-    the outputs (the same kernels; the order of a selection's positions, and with it the
-    decode's summation order, may differ); every layer's decode in the call's kernel record."""
+    the outputs (the order of a selection's positions, and with it the decode's summation
+    order, may differ); every layer's decode in the call's kernel record. Where the
+    selection takes its many-workgroup path (c3f, c4f, c5f without a pool), the group call
+    folds the selection's final into the decode, which then writes the index set: the
+    sets must still equal the final's exactly."""
     cfg = CFGS[name]
-    say("native", name, "pool", pool, "bf16 scores", score_bf16)
+    say("native", name, "pool", pool, "bf16 scores", score_bf16, "zero keys", zero_keys)
     case = G.build_case(cfg, seed=3)
+    if zero_keys:                                        # every stored key zero: every score ties
+        case.g_idx.zero_()
     L = len(cfg.layers)
     runs = []
     for native in (False, True):
@@ -207,6 +219,9 @@ def test_native_group_step_equals_the_helper(name, pool, score_bf16):
         runs.append((main, idx, win, out, lse, att, x["pool"][3].clone() if pool else None, launched))
     (m0, i0, w0, o0, l0, a0, p0, _), (m1, i1, w1, o1, l1, a1, p1, launched) = runs
     assert sum("k_decode" in n for n in launched) == L, launched       # one record for the whole group
+    if name.endswith("f") and not pool:                  # folded: k_select, then the decode finishes
+        assert not any("k_select_final" in n for n in launched), launched
+        assert any("k_select<" in n for n in launched), launched
     assert torch.equal(m0, m1) and torch.equal(i0, i1)
     if cfg.W:
         assert torch.equal(w0.view(torch.uint8), w1.view(torch.uint8))
@@ -219,3 +234,11 @@ def test_native_group_step_equals_the_helper(name, pool, score_bf16):
             assert blocks(pa) == blocks(pb), b
     G.check_attention(o1.cpu().numpy().reshape(-1, cfg.H, cfg.d_v), l1.cpu().numpy().reshape(-1, cfg.H),
                       o0.cpu().numpy().reshape(-1, cfg.H, cfg.d_v), l0.cpu().numpy().reshape(-1, cfg.H), rel=1e-5)
+
+
+def test_native_group_step_with_tied_scores():
+    """Every stored indexer key zero, so every visible row but the step's own scores 0: the
+    threshold bin holds tens of thousands of candidates (more than the decode keeps in LDS,
+    so it reads them from the selection's lists) and the exact selection goes by position.
+    The folded selection must still take the final's set."""
+    test_native_group_step_equals_the_helper("c3f", 0, False, zero_keys=True)

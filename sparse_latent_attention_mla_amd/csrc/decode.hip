@@ -224,39 +224,42 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
     };
     const bool in_lds = ncand <= cand_room;
     // the split's selected slots and (in a split that reaches the threshold bin) the first
-    // 2048 candidates: every load issued before the first store
+    // 2048 candidates, kCB consecutive ones per thread (one owner search, then a step to
+    // the next list where one ends): every load issued before the first store
     constexpr int kCB = 4;                                 // candidates per thread per batch
+    auto load_run = [&](uint32_t i0, uint64_t* v) {
+        int j = i0 < ncand ? owner(offs_c, i0) : 0;
+#pragma unroll
+        for (int u = 0; u < kCB; ++u) {
+            const uint32_t i = i0 + u;
+            v[u] = 0ull;
+            if (i < ncand) {
+                while (j + 1 < G && offs_c[j + 1] <= i) ++j;
+                v[u] = cl[(int64_t)j * kSelRowsHost + (i - offs_c[j])];
+            }
+        }
+    };
     int32_t r = -1;
     if (tid < n && o < (int64_t)nsel) {
         const int j = owner(offs_s, (uint32_t)o);
         r = sl[(int64_t)j * kSelRowsHost + ((uint32_t)o - offs_s[j])];
     }
     uint64_t cv0[kCB];
-    if (tail && in_lds) {
-#pragma unroll
-        for (int u = 0; u < kCB; ++u) {
-            const uint32_t i = u * 512 + tid;
-            cv0[u] = i < ncand ? cand_at(i) : 0ull;
-        }
-    }
+    if (tail && in_lds) load_run(kCB * tid, cv0);
     if (tid < R) ridx[tid] = (r >= 0 && r < a.capacity) ? r : -1;
     if (tail) {
         if (in_lds) {
 #pragma unroll
             for (int u = 0; u < kCB; ++u) {
-                const uint32_t i = u * 512 + tid;
+                const uint32_t i = kCB * tid + u;
                 if (i < ncand) lc[i] = cv0[u];
             }
-            for (uint32_t i0 = kCB * 512; i0 < ncand; i0 += kCB * 512) {
+            for (uint32_t b0 = kCB * 512; b0 < ncand; b0 += kCB * 512) {
                 uint64_t v[kCB];
+                load_run(b0 + kCB * tid, v);
 #pragma unroll
                 for (int u = 0; u < kCB; ++u) {
-                    const uint32_t i = i0 + u * 512 + tid;
-                    v[u] = i < ncand ? cand_at(i) : 0ull;
-                }
-#pragma unroll
-                for (int u = 0; u < kCB; ++u) {
-                    const uint32_t i = i0 + u * 512 + tid;
+                    const uint32_t i = b0 + kCB * tid + u;
                     if (i < ncand) lc[i] = v[u];
                 }
             }
@@ -266,7 +269,8 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
         // the radix and the ranking, over the candidates in LDS or (past its room) in the lists
         auto finish = [&](auto cv) {
             // the radix over the candidates' composites, most significant digit first: two
-            // 10-bit digits fix the threshold score (the bin fixed its top 12 bits), and four
+            // 10-bit digits fix the threshold score (the bin fixed its top 12 bits; the second
+            // only when the first leaves more candidates than are still needed), and four
             // 8-bit digits of the inverted position follow when more candidates share that
             // score than are still needed; `prefix` ends as the need-th largest composite
             const bool radix = need < ncand;
@@ -299,13 +303,15 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
                 return res[2];
             };
             if (radix) {
-                pass(42, 10);
-                const uint32_t eq = pass(32, 10);
-                if (rem < eq) {
-                    pass(24, 8);
-                    pass(16, 8);
-                    pass(8, 8);
-                    pass(0, 8);
+                const uint32_t c1 = pass(42, 10);
+                if (rem < c1) {                            // (every candidate of the digit needed: done)
+                    const uint32_t eq = pass(32, 10);
+                    if (rem < eq) {
+                        pass(24, 8);
+                        pass(16, 8);
+                        pass(8, 8);
+                        pass(0, 8);
+                    }
                 }
             }
             // the taken candidates (every one at or above `prefix`: exactly `need`), ranked in list

@@ -30,6 +30,9 @@ CFGS = {
     "c3f": C["c3"].with_(name="c3f", cid=173, B=3, N=40004),
     "c4f": C["c4"].with_(name="c4f", cid=174, B=2, N=40004),
     "c5f": C["c5"].with_(name="c5f", cid=175, B=1, N=40004),
+    # the bench's c3 step at full size (64 select workgroups per sequence, two splits per
+    # sequence reaching the threshold bin)
+    "c3full": C["c3"],
 }
 POOL_BLOCK = 8
 
@@ -186,7 +189,8 @@ def test_group_helper_rejects_unknown_and_leading_reuse():
                                                   ("c5s", 0, False), ("c5d", 0, False), ("c5d", 96, False),
                                                   ("c5d", 0, True), ("c3d", 0, True),
                                                   ("c3f", 0, False), ("c3f", 0, True), ("c4f", 0, False),
-                                                  ("c5f", 0, False), ("c5f", 0, True), ("c5f", 96, False)])
+                                                  ("c5f", 0, False), ("c5f", 0, True), ("c5f", 96, False),
+                                                  ("c3full", 0, False)])
 def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=False):
     """mla_csa2_group_step (one C call) against csa2_group_step (the same calls from Python):
     the caches and window rings byte for byte, the selected sets, the pool's positions, and
@@ -219,7 +223,7 @@ def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=F
         runs.append((main, idx, win, out, lse, att, x["pool"][3].clone() if pool else None, launched))
     (m0, i0, w0, o0, l0, a0, p0, _), (m1, i1, w1, o1, l1, a1, p1, launched) = runs
     assert sum("k_decode" in n for n in launched) == L, launched       # one record for the whole group
-    if name.endswith("f") and not pool:                  # folded: k_select, then the decode finishes
+    if name.endswith(("f", "full")) and not pool:        # folded: k_select, then the decode finishes
         assert not any("k_select_final" in n for n in launched), launched
         assert any("k_select<" in n for n in launched), launched
     assert torch.equal(m0, m1) and torch.equal(i0, i1)

@@ -191,7 +191,7 @@ def test_group_helper_rejects_unknown_and_leading_reuse():
                                                   ("c3f", 0, False), ("c3f", 0, True), ("c4f", 0, False),
                                                   ("c5f", 0, False), ("c5f", 0, True), ("c5f", 96, False),
                                                   ("c3full", 0, False)])
-def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=False):
+def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=False, visible=None):
     """mla_csa2_group_step (one C call) against csa2_group_step (the same calls from Python):
     the caches and window rings byte for byte, the selected sets, the pool's positions, and
     the outputs (the order of a selection's positions, and with it the decode's summation
@@ -208,6 +208,8 @@ def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=F
     runs = []
     for native in (False, True):
         x = _inputs(case, pool)
+        if visible is not None:                          # per-sequence causal limits below N
+            x["nvis"] = torch.tensor(visible, dtype=torch.int32, device=G.DEV)
         main, idx = case.g_main.clone(), case.g_idx.clone()
         win = case.g_win.clone() if cfg.W else None
         out, lse, bufs = _outs(cfg)
@@ -246,3 +248,10 @@ def test_native_group_step_with_tied_scores():
     so it reads them from the selection's lists) and the exact selection goes by position.
     The folded selection must still take the final's set."""
     test_native_group_step_equals_the_helper("c3f", 0, False, zero_keys=True)
+
+
+def test_native_group_step_with_ragged_visibility():
+    """Causal limits below the cache's rows: one sequence with fewer visible rows than k
+    (every visible row selected, -1 after them), one whose limit ends inside a select
+    workgroup's slice, one at full length; the finished selection against the final's."""
+    test_native_group_step_equals_the_helper("c3f", 0, False, visible=[40004, 1500, 23001])

@@ -270,9 +270,9 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
         auto finish = [&](auto cv) {
             // the radix over the candidates' composites, most significant digit first: two
             // 10-bit digits fix the threshold score (the bin fixed its top 12 bits; the second
-            // only when the first leaves more candidates than are still needed), and four
-            // 8-bit digits of the inverted position follow when more candidates share that
-            // score than are still needed; `prefix` ends as the need-th largest composite
+            // only when the first leaves more candidates than are still needed), and digits of
+            // the inverted position follow when more candidates share that score than are
+            // still needed; `prefix` ends as the need-th largest composite
             const bool radix = need < ncand;
             uint64_t mask = 0xFFFull << 52, prefix = radix ? (cv(0) & mask) : 0ull;
             uint32_t rem = need;
@@ -307,10 +307,20 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
                 if (rem < c1) {                            // (every candidate of the digit needed: done)
                     const uint32_t eq = pass(32, 10);
                     if (rem < eq) {
-                        pass(24, 8);
-                        pass(16, 8);
-                        pass(8, 8);
-                        pass(0, 8);
+                        // ties at the threshold score: the inverted position's digits. Positions
+                        // lie below the capacity, so its bits from pb up are ones in every
+                        // candidate; the digits cover bits pb - 1 .. 0 from the top, 10 at a time
+                        // (the last of 8 or 10 bits, reaching below 0 into bits already fixed)
+                        const int pb = 32 - __builtin_clz((uint32_t)(cap > 1 ? cap - 1 : 1));
+                        const uint64_t ones = pb < 32 ? (uint64_t)(0xFFFFFFFFu >> pb << pb) : 0ull;
+                        prefix |= ones;
+                        mask |= ones;
+                        for (int hi = pb; hi > 0;) {
+                            const int bits = hi >= 10 ? 10 : (hi > 8 ? 10 : 8);
+                            const int lo = hi - bits > 0 ? hi - bits : 0;
+                            pass(lo, bits);
+                            hi = lo;
+                        }
                     }
                 }
             }

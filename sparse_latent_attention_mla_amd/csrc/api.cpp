@@ -783,6 +783,19 @@ mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t 
                       mla::decode_takes_select_lists(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W);
     if (W > 0 && n_layers > 1 && (!win_pos || !aligned(win_pos, 4)))
         return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: the window entries need win_pos (4-byte aligned)");
+    if (W > 0 && (!win_len || !aligned(win_len, 4)))
+        return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: a window needs win_len (4-byte aligned)");
+    if (W > 0 && win_fmt != MLA_FMT_BF16 && win_fmt != MLA_FMT_MXFP8)
+        return fail(MLA_ERR_UNSUPPORTED, "csa2_group_step: window entries must be BF16 or MXFP8");
+    if (W > 0 && win_fmt == MLA_FMT_MXFP8 && Dw % 32 != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "csa2_group_step: an MXFP8 window needs dim + rope % 32 == 0");
+    if (fold && B > 0 && k > 0) {                          // a decode that finishes a selection must not fail
+        int64_t rb = 0;                                    // after it: its cache is checked first
+        if (!main_cache) return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: main_cache is NULL");
+        const mla_status_t sc = check_rows("csa2_group_step", main_row, main_cache, main_seq_stride, capacity, B,
+                                           &rb, true);
+        if (sc != MLA_OK) return sc;
+    }
     int32_t* bufs[2] = {idx_a, idx_b};
     int32_t* latest = nullptr;
     int j = 0;

@@ -225,7 +225,8 @@ def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=F
         runs.append((main, idx, win, out, lse, att, x["pool"][3].clone() if pool else None, launched))
     (m0, i0, w0, o0, l0, a0, p0, _), (m1, i1, w1, o1, l1, a1, p1, launched) = runs
     assert sum("k_decode" in n for n in launched) == L, launched       # one record for the whole group
-    if name.endswith(("f", "full")) and not pool:        # folded: k_select, then the decode finishes
+    many = name.endswith(("f", "full")) or G.M.mla_get_option("topk_path") == 2
+    if many and not pool:                                # folded: k_select, then the decode finishes
         assert not any("k_select_final" in n for n in launched), launched
         assert any("k_select<" in n for n in launched), launched
     assert torch.equal(m0, m1) and torch.equal(i0, i1)
@@ -255,3 +256,12 @@ def test_native_group_step_with_ragged_visibility():
     (every visible row selected, -1 after them), one whose limit ends inside a select
     workgroup's slice, one at full length; the finished selection against the final's."""
     test_native_group_step_equals_the_helper("c3f", 0, False, visible=[40004, 1500, 23001])
+
+
+@pytest.mark.parametrize("name", ["c3d", "c5d"])
+def test_native_group_step_finishes_a_forced_many_workgroup_selection(name):
+    """Short sequences with the many-workgroup selection forced (topk_path = 2): a few
+    select workgroups per sequence, the decode finishing their lists; against the helper,
+    which runs the same selection with its final kernel."""
+    with G.M.option("topk_path", 2):
+        test_native_group_step_equals_the_helper(name, 0, False)

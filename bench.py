@@ -291,7 +291,8 @@ def main():
         side = {}
         for name in SIDE_CONFIGS:
             torch.cuda.empty_cache()
-            r = run_config(args, WL.CONFIGS[name], 4, max(20, min(args.steps, 50)), 5, headline=False)
+            r = run_config(args, WL.CONFIGS[name], 4, max(20, min(args.steps, 200)), max(5, min(args.warmup, 20)),
+                           headline=False)
             side[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "launch")}
             side[name]["step_frac"] = r["step_roofline"]["frac"]
             side[name]["scan_frac"] = r["roofline"]["frac"]

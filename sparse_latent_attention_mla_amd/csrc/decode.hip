@@ -839,15 +839,20 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
             const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
             if (it < 32 * kPer) qs[i] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)hh * DQK + 8 * pc);
         }
-        int32_t r = -1;
-        if (tid < n) {
-            if (is_win) r = (int32_t)(first + tid);
-            else {
-                const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
-                if (s >= 0 && s < a.capacity) r = s;
+        if (!is_win && a.sel_counts) {                     // the rows of a selection this decode finishes
+            finish_selection(a, V, 2 * gd2::kBuf, ridx, nch * C, b, split == 0 && hp == 0, first, n);
+            lds_barrier();                                 // (the row buffers were its scratch)
+        } else {
+            int32_t r = -1;
+            if (tid < n) {
+                if (is_win) r = (int32_t)(first + tid);
+                else {
+                    const int32_t s = a.idx[(int64_t)b * a.k + first + tid];
+                    if (s >= 0 && s < a.capacity) r = s;
+                }
             }
+            if (tid < nch * C) ridx[tid] = r;
         }
-        if (tid < nch * C) ridx[tid] = r;
 #pragma unroll
         for (int i = 0; i < kIt; ++i) {
             const int it = tid + 512 * i, hh = it / kPer, pc = it - hh * kPer;
@@ -855,6 +860,8 @@ __device__ __forceinline__ void decode_split_pair(const DecodeArgs& a, uint8_t* 
         }
     }
     __syncthreads();                                       // the row indices and the queries
+    if (!is_win && a.sel_counts && hp == 0 && tid < n)    // the finished index set, once per split
+        a.idx_out[(int64_t)b * a.k + first + tid] = ridx[tid];
 
     const uint32_t v_m0 = __builtin_amdgcn_readfirstlane(lds_addr(V));
     const int rot = nch > 0 ? hp % nch : 0;
@@ -1485,10 +1492,9 @@ __global__ __launch_bounds__(256) void k_widen_window(const uint8_t* __restrict_
 }
 
 bool decode_takes_select_lists(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W) {
-    if (!mfma_shape(fmt, dim, rope, d_v, H) || k <= 0) return false;
-    bool pairs = false;
-    decode_geometry(fmt, B, H, k, W, &pairs);
-    return !pairs;
+    (void)B;
+    (void)W;
+    return mfma_shape(fmt, dim, rope, d_v, H) && k > 0;
 }
 
 bool decode_fuses_window_append(const DecodeArgs& a) {

@@ -128,6 +128,9 @@ hipError_t launch_select(const float* scores, int64_t capacity, const int32_t* n
 constexpr int kFusedSelectGroups = 1024;
 hipError_t launch_select_lists(const float* scores, int64_t capacity, const int32_t* n_visible, int B, int k,
                                const TopkWorkspace& ws, hipStream_t stream, int* groups);
+// (the same from kFoldManyMin rows on, where the many-workgroup path with its final in the
+// decode is ahead of the one-workgroup selection)
+constexpr int64_t kFoldManyMin = 4096;
 // Block maxima of a layer's scores ([B, capacity]): bmax[b, i] = the largest
 // score among the visible positions block*i .. block*i + block - 1, the
 // histogram of their keys into hist (as the scan builds it), and nvb[b] = the
@@ -222,7 +225,7 @@ hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint3
 size_t decode_workspace_bytes(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Whether launch_decode can finish a selection from k_select's lists for this shape
-// (the gather decode of 16 heads per workgroup; W: window slots, 0 without a window).
+// (the MFMA decodes; W: window slots, 0 without a window).
 bool decode_takes_select_lists(int fmt, int dim, int rope, int d_v, int B, int H, int k, int W);
 // Whether launch_decode writes a.new_win into the window ring itself (512-channel bf16 or
 // MXFP8 entries on the gather decode); otherwise the caller appends it first.

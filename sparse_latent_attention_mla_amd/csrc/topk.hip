@@ -923,7 +923,7 @@ hipError_t launch_select_lists(const float* scores, int64_t capacity, const int3
                                const TopkWorkspace& ws, hipStream_t stream, int* groups) {
     *groups = 0;
     if (B == 0 || k == 0) return hipSuccess;
-    bool row = capacity <= kRowPathMax;
+    bool row = capacity < kFoldManyMin;
     if (const int64_t path = option(OPT_TOPK_PATH)) row = path == 1;
     const int64_t nx = (capacity + kSelRows - 1) / kSelRows;
     if (row || nx < 1 || nx > kFusedSelectGroups) return hipSuccess;

@@ -33,6 +33,8 @@ CFGS = {
     # the bench's c3 step at full size (64 select workgroups per sequence, two splits per
     # sequence reaching the threshold bin)
     "c3full": C["c3"],
+    # bf16 rows decoded 32 heads per workgroup (the paired decode finishing the selection)
+    "c2full": C["c2"],
 }
 POOL_BLOCK = 8
 
@@ -190,7 +192,7 @@ def test_group_helper_rejects_unknown_and_leading_reuse():
                                                   ("c5d", 0, True), ("c3d", 0, True),
                                                   ("c3f", 0, False), ("c3f", 0, True), ("c4f", 0, False),
                                                   ("c5f", 0, False), ("c5f", 0, True), ("c5f", 96, False),
-                                                  ("c3full", 0, False)])
+                                                  ("c3full", 0, False), ("c2full", 0, False)])
 def test_native_group_step_equals_the_helper(name, pool, score_bf16, zero_keys=False, visible=None):
     """mla_csa2_group_step (one C call) against csa2_group_step (the same calls from Python):
     the caches and window rings byte for byte, the selected sets, the pool's positions, and

@@ -779,8 +779,9 @@ mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t 
     const int32_t Dw = main_row.dim + main_row.rope_dim;
     // a selecting layer's final folded into its decode: the many-workgroup selection over
     // every row (none with a pool, whose kernels reuse the top-k workspace), on the gather decode
-    const bool fold = pool_blocks == 0 &&
-                      mla::decode_takes_select_lists(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W);
+    // (a Reindex layer scoring a pool keeps the final: its selection maps pool entries to positions;
+    // a Full layer that publishes the pool does so after its decode, which reads the lists first)
+    const bool fold = mla::decode_takes_select_lists(main_row.fmt, main_row.dim, main_row.rope_dim, d_v, B, H, k, W);
     if (W > 0 && n_layers > 1 && (!win_pos || !aligned(win_pos, 4)))
         return fail(MLA_ERR_INVALID_ARG, "csa2_group_step: the window entries need win_pos (4-byte aligned)");
     if (W > 0 && (!win_len || !aligned(win_len, 4)))
@@ -820,7 +821,7 @@ mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t 
                                   latest, scores, topk_workspace, topk_workspace_bytes, stream, score_bf16 != 0,
                                   fold ? &dfr : nullptr);
             }
-            if (st == MLA_OK && scores)                    // the Full layer publishes the candidate pool
+            if (st == MLA_OK && scores && dfr.groups == 0)  // the Full layer publishes the candidate pool
                 st = mla_indexer_pool(scores, capacity, n_visible, B, pool_block, pool_blocks, pool_pos,
                                       topk_workspace, topk_workspace_bytes, stream);
             if (st != MLA_OK) return st;
@@ -837,6 +838,10 @@ mla_status_t mla_csa2_group_step(mla_row_t main_row, mla_row_t idx_row, int32_t 
                              W > 0 ? y.win_ring : nullptr, W > 0 ? win_len : nullptr, W > 0 ? W : 0, win_fmt,
                              softmax_scale, nullptr, B, H, y.out, y.lse, decode_workspace, decode_workspace_bytes,
                              stream, sel, latest);
+        if (st != MLA_OK) return st;
+        if (sel && y.mode == MLA_LAYER_FULL && pool_blocks > 0)   // the pool, once the lists are read
+            st = mla_indexer_pool(pool_scores, capacity, n_visible, B, pool_block, pool_blocks, pool_pos,
+                                  topk_workspace, topk_workspace_bytes, stream);
         if (st != MLA_OK) return st;
     }
     return ok();

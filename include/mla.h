@@ -521,10 +521,11 @@ mla_status_t mla_append_sparse_decode(mla_row_t main_row, int32_t d_v, const voi
  * indices to idx_a and idx_b in turn (the first to idx_a): with more than two selecting
  * layers, a buffer is overwritten by the selection two layers later. The bf16-score top-k
  * (mla_indexer_topk_bf16) when score_bf16 != 0.
- * One difference in how, not in what: without a pool, for a capacity of 4096 rows or more
- * and a decode on the MFMA path (fmt E4M3_S128, E2M1_S16 or BF16 at 512 value channels),
- * a selecting layer runs the many-workgroup selection and its final step runs inside that
- * layer's decode instead of as its own kernel: the decode takes its rows from
+ * One difference in how, not in what: for a capacity of 4096 rows or more and a decode on
+ * the MFMA path (fmt E4M3_S128, E2M1_S16 or BF16 at 512 value channels), a selecting layer
+ * (other than a Reindex layer scoring the pool) runs the many-workgroup selection and its
+ * final step runs inside that layer's decode instead of as its own kernel (a Full layer that
+ * publishes the pool then does so after its decode): the decode takes its rows from
  * the per-workgroup lists of the selection's first kernel and writes the index set to
  * idx_a or idx_b itself. The set is the one the separate calls select (an unordered set,
  * -1 in the same trailing slots); the order of its entries, and with it the decode's

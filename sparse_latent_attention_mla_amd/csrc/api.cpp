@@ -652,6 +652,7 @@ static mla_status_t decode_impl(mla_row_t main_row, int32_t d_v, const void* q, 
         a.sel_counts = sel->ws.counts;
         a.sel_lists = sel->ws.sel;
         a.cand_lists = sel->ws.cand;
+        a.cand_flat = sel->ws.cand2;
         a.sel_hist = sel->ws.hist;
         a.sel_visible = sel->n_visible;
         a.sel_capacity = sel->capacity;

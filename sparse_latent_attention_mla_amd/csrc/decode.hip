@@ -136,8 +136,8 @@ constexpr int lds_bytes() {
 // first + n - 1 into ridx (-1 for a position outside the cache); the splits that reach
 // into the threshold bin run the radix over its candidates themselves (each head group
 // of such a split, redundantly: the result is one function of the lists). scratch is
-// the row buffers, free until the gather (candidates past its room are read from the
-// lists in global memory). Called by every thread of the workgroup.
+// the row buffers, free until the gather (candidates past its room go to one contiguous
+// list in the workspace). Called by every thread of the workgroup.
 namespace fs {
 constexpr uint32_t kOffS = 0;                              // [kFusedSelectGroups + 1] selected offsets
 constexpr uint32_t kOffC = 4160;                           // candidate offsets
@@ -218,10 +218,6 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
     const int64_t o = first + tid;
     const uint32_t need = want > nsel ? want - nsel : 0u;
     const bool tail = need > 0 && first < (int64_t)want && first + n > (int64_t)nsel;
-    auto cand_at = [&](uint32_t i) {
-        const int j = owner(offs_c, i);
-        return cl[(int64_t)j * kSelRowsHost + (i - offs_c[j])];
-    };
     const bool in_lds = ncand <= cand_room;
     // the split's selected slots and (in a split that reaches the threshold bin) the first
     // 2048 candidates, kCB consecutive ones per thread (one owner search, then a step to
@@ -263,9 +259,23 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
                     if (i < ncand) lc[i] = v[u];
                 }
             }
+        } else {
+            // past the room: one contiguous copy in the workspace, written alike by every workgroup
+            // that finishes this sequence (the same bytes), read back by this one after its fence
+            uint64_t* cf = a.cand_flat + b * cap;
+            for (uint32_t b0 = 0; b0 < ncand; b0 += kCB * 512) {
+                uint64_t v[kCB];
+                load_run(b0 + kCB * tid, v);
+#pragma unroll
+                for (int u = 0; u < kCB; ++u) {
+                    const uint32_t i = b0 + kCB * tid + u;
+                    if (i < ncand) cf[i] = v[u];
+                }
+            }
+            __threadfence_block();
         }
         for (int i = tid; i < 2 * kMaxDigitBins; i += 512) h[0][i] = 0u;
-        lds_barrier();
+        __syncthreads();
         // the radix and the ranking, over the candidates in LDS or (past its room) in the lists
         auto finish = [&](auto cv) {
             // the radix over the candidates' composites, most significant digit first: two
@@ -356,7 +366,7 @@ __device__ void finish_selection(const DecodeArgs& a, uint8_t* scratch, uint32_t
             }
         };
         if (in_lds) finish([&](uint32_t i) { return lc[i]; });
-        else finish(cand_at);
+        else finish([&](uint32_t i) { return a.cand_flat[b * cap + i]; });
     }
     if (zero_rest) zero_hist_rest(hb, (uint32_t)a.k, csum);
 }

@@ -169,6 +169,7 @@ struct DecodeArgs {
     const uint32_t* sel_counts = nullptr;
     const int32_t* sel_lists = nullptr;
     const uint64_t* cand_lists = nullptr;
+    uint64_t* cand_flat = nullptr;          // [B, sel_capacity]: the candidates in one list, past LDS
     uint32_t* sel_hist = nullptr;
     const int32_t* sel_visible = nullptr;
     int64_t sel_capacity = 0;
